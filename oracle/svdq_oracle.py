@@ -1,0 +1,421 @@
+"""CPU oracle of the SVDQuant linear layer.  TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import, call or execute anything under ``oracle/``.  The product
+(the C-ABI library and its Python binding) never does, and this module imports
+nothing from the product.
+
+What it is: a plain, slow, readable restatement of the method in numpy, in
+float64 except at the rounding points the method fixes in float32 / fp16 / bf16.
+Sources, cited by section and equation:
+
+  [Review]  "SVDQuant: How a Small High-Precision Branch Makes 4-Bit Diffusion
+            Practical" (Zhou's technical review of arXiv:2411.05007v4):
+            sec. 2.2 Eq.(1) quantizer; sec. 3.1 Eq.(3)-(4) smoothing;
+            sec. 4.1 Eq.(5)-(6) error split and bound; sec. 4.2 Eq.(7)-(8)
+            two-branch output; sec. 4.3 Eq.(9) residual bound; sec. 5 Eq.(10)
+            and Algorithm 1 (protected-layer construction); sec. 6.1 Eq.(11)
+            and Algorithm 2 (fused execution); sec. 6.2 Eq.(12); sec. 7 Eq.(13)
+            LoRA; sec. 8 (INT4: group 64 on both operands, 16-bit scales).
+  [Nunchaku article] "SVDQuant: 4-bit Quantization Enables Efficient Diffusion
+            Model Inference on Consumer GPUs", section "Nunchaku": two 4-bit
+            values per byte.
+
+Readings taken where the pages are silent (each also listed in the design doc):
+  R1  ties in round() go to even (IEEE default).
+  R2  codes are emitted in [-7, 7]: the review's symmetric grid (sec. 2.2).
+  R3  16-bit scale = fp16(fl32(amax / 7)), saturated at 65504.
+  R4  a group whose fp16 scale is 0 (all-zero or underflowing group) gets code 0
+      everywhere (sec. 2.2 sets the all-zero group aside without defining it).
+  R5  lambda_k = 1 where the activation or weight statistic of channel k is 0
+      (sec. 3.1 declines to pick a safeguard).
+  R6  the smoothing scale multiplies W on the left, W~ = diag(lambda) W (sec. 3.1
+      notes the paper's W diag(lambda) is dimensionally inconsistent).
+  R7  X~ = X diag(lambda)^-1 is computed as x * fl32(1/lambda32) in float32 and
+      materialised once as bf16; both branches use that bf16 X~ (Algorithm 2
+      steps 1-3 read one 16-bit smoothed tile and feed it to both branches).
+  R8  Sigma goes into L1 (Eq.10); the stored factors are bf16; the residual
+      R = W~ - L1 L2 uses the STORED (rounded) factors, so W~ = L1 L2 + R holds
+      exactly with respect to what runs.
+  R9  the up-projection operand Z is rounded to bf16 before Z L2 (the branch is
+      a bf16 matrix product).
+  R10 the LoRA scale is absorbed into B (sec. 7 allows either factor).
+  R11 quantization groups run along the input channels for both operands
+      (sec. 8: group quantization on both operands, group 64).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+GROUP = 64
+QMAX = 7           # [Review] sec. 2.2: symmetric INT4 grid spans -7..7
+FP16_MAX = 65504.0
+
+# --------------------------------------------------------------------------
+# Rounding primitives (the method's fixed rounding points).
+# --------------------------------------------------------------------------
+
+
+def f32(a) -> np.ndarray:
+    """Round to IEEE float32, nearest-even."""
+    return np.asarray(a, dtype=np.float64).astype(np.float32)
+
+
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_from_f32(a32) -> np.ndarray:
+    """float32 -> nearest bf16 value (ties to even), returned as float32.
+
+    bf16 keeps the top 16 bits of the float32 encoding; rounding adds
+    0x7FFF + (bit 16) before truncating, the usual integer form of RNE.
+    """
+    u = np.ascontiguousarray(a32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    u = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
+    return u.astype(np.uint32).view(np.float32)
+
+
+def bf16_bits_from_f32(a32) -> np.ndarray:
+    return (bf16_from_f32(a32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_from_f64(a) -> np.ndarray:
+    """float64 -> nearest bf16 value (ties to even) in ONE rounding, as float32.
+
+    bf16 has 8 significant bits and the float32 exponent range; the grid
+    spacing for |x| in [2^e, 2^(e+1)) is 2^(e-7), never below 2^-133.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    out = np.zeros_like(a)
+    nz = a != 0
+    e = np.floor(np.log2(np.abs(a[nz])))
+    # guard the log2 floor against off-by-one at exact powers of two
+    av = np.abs(a[nz])
+    e = np.where(2.0 ** e > av, e - 1, e)
+    e = np.where(2.0 ** (e + 1) <= av, e + 1, e)
+    q = 2.0 ** (np.maximum(e, -126.0) - 7.0)
+    out[nz] = np.rint(a[nz] / q) * q     # a/q is exact (power-of-two scaling)
+    big = np.abs(out) > 3.3895313892515355e38   # beyond the largest finite bf16
+    out[big] = np.sign(out[big]) * np.inf
+    return out.astype(np.float32)
+
+
+def fp16_from_f32_sat(a32) -> np.ndarray:
+    """float32 -> nearest fp16 (ties to even), saturated at +-65504 (reading R3).
+
+    Returned as float32 holding the fp16 value.
+    """
+    a32 = np.asarray(a32, dtype=np.float32)
+    with np.errstate(over="ignore"):
+        h = a32.astype(np.float16)
+    h = np.where(np.isinf(h) & np.isfinite(a32), np.sign(a32) * np.float16(FP16_MAX), h)
+    return h.astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Quantizer: [Review] sec. 2.2, Eq.(1)  s = max|Z| / 7,  Q(Z) = s * round(Z / s)
+# --------------------------------------------------------------------------
+
+
+def quantize_groups(v32: np.ndarray, group: int = GROUP):
+    """Symmetric per-group INT4 round-to-nearest along the LAST axis.
+
+    v32: float32 array [..., K] with K % group == 0.
+    Returns (codes int8 [..., K] in [-7, 7], scales float32 [..., K/group]
+    holding fp16 values).
+
+    Steps per group (Eq.1 with readings R1-R4):
+      amax = max|v| (exact);  s = fp16(fl32(amax / 7));
+      q = clamp(round_half_even(fl32(v / s)), -7, 7);  q = 0 where s == 0.
+    """
+    v32 = np.asarray(v32, dtype=np.float32)
+    K = v32.shape[-1]
+    assert K % group == 0
+    g = v32.reshape(v32.shape[:-1] + (K // group, group))
+    amax = np.max(np.abs(g), axis=-1)                      # exact in float32
+    s = fp16_from_f32_sat(np.float32(amax) / np.float32(QMAX))   # fl32 divide, then fp16
+    s_b = s[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        quot = np.where(s_b > 0, g / np.where(s_b > 0, s_b, np.float32(1)), np.float32(0))
+    quot = quot.astype(np.float32)                         # fl32(v / s)
+    q = np.clip(np.rint(quot), -QMAX, QMAX)                # rint: ties to even
+    q = np.where(s_b > 0, q, 0).astype(np.int8)
+    return q.reshape(v32.shape), s.astype(np.float32)
+
+
+def dequantize_groups(codes: np.ndarray, scales: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """Q(v) = s * q, in float64 (exact: a 4-bit integer times an fp16 value)."""
+    K = codes.shape[-1]
+    c = codes.astype(np.float64).reshape(codes.shape[:-1] + (K // group, group))
+    return (c * scales.astype(np.float64)[..., None]).reshape(codes.shape)
+
+
+# --------------------------------------------------------------------------
+# Calibration and smoothing: [Review] sec. 3.1, Eq.(3)-(4)
+# --------------------------------------------------------------------------
+
+
+def act_amax(x32: np.ndarray) -> np.ndarray:
+    """Calibration statistic a_k = max_i |X_ik| (exact), float32 [m]."""
+    return np.max(np.abs(np.asarray(x32, dtype=np.float32)), axis=0)
+
+
+def smoothing_lambda(a: np.ndarray, w32: np.ndarray, alpha: float = 0.5):
+    """lambda_k = a_k^alpha / w_k^(1-alpha), w_k = max_j |W_kj|  (Eq.4).
+
+    Computed in float64; lambda_k = 1 where a_k or w_k is 0 (reading R5).
+    Returns (lam64, lam32, inv32) with lam32 = fl32(lam64) and
+    inv32 = fl32(1 / lam32) (the smoothing multiply of reading R7).
+    """
+    a = np.asarray(a, dtype=np.float64)
+    wmax = np.max(np.abs(np.asarray(w32, dtype=np.float64)), axis=1)
+    ok = (a > 0) & (wmax > 0)
+    lam = np.ones_like(a)
+    lam[ok] = np.power(a[ok], alpha) / np.power(wmax[ok], 1.0 - alpha)
+    lam32 = lam.astype(np.float32)
+    inv32 = (1.0 / lam32.astype(np.float64)).astype(np.float32)
+    return lam, lam32, inv32
+
+
+def smooth_weight(w32: np.ndarray, lam32: np.ndarray) -> np.ndarray:
+    """W~ = diag(lambda) W in float64 (Eq.3, reading R6); products are exact."""
+    return np.asarray(w32, dtype=np.float64) * lam32.astype(np.float64)[:, None]
+
+
+def smooth_activation(x32: np.ndarray, inv32: Optional[np.ndarray]) -> np.ndarray:
+    """X~ = bf16(fl32(x * inv32))  (Eq.3 with reading R7); None = no smoothing."""
+    x32 = np.asarray(x32, dtype=np.float32)
+    if inv32 is None:
+        return bf16_from_f32(x32)
+    return bf16_from_f32(x32 * np.asarray(inv32, dtype=np.float32)[None, :])
+
+
+# --------------------------------------------------------------------------
+# Low-rank decomposition: [Review] sec. 5, Eq.(10), Algorithm 1 steps 3-5
+# --------------------------------------------------------------------------
+
+
+def truncated_svd(wt: np.ndarray, rank: int):
+    """L1 = U_r Sigma_r, L2 = V_r^T of the smoothed weight (Eq.10), float64.
+
+    Uses LAPACK's SVD (numpy) as the textbook routine.  Sign convention for
+    reproducible dumps: the largest-magnitude entry of each U column is made
+    positive (a sign flip of a singular pair leaves L1 L2 unchanged).
+    Returns (L1 [m][r], L2 [r][n], sigma [min(m, n)]).
+    """
+    U, S, Vt = np.linalg.svd(wt, full_matrices=False)
+    U = U[:, :rank].copy()
+    Vt = Vt[:rank].copy()
+    if rank:
+        idx = np.argmax(np.abs(U), axis=0)
+        sgn = np.sign(U[idx, np.arange(rank)])
+        sgn[sgn == 0] = 1
+        U *= sgn[None, :]
+        Vt *= sgn[:, None]
+    return U * S[None, :rank], Vt, S
+
+
+def residual(wt: np.ndarray, l1b: np.ndarray, l2b: np.ndarray) -> np.ndarray:
+    """R = W~ - L1 L2 with the stored bf16 factors, in float64 (reading R8)."""
+    return np.asarray(wt, dtype=np.float64) - l1b.astype(np.float64) @ l2b.astype(np.float64)
+
+
+def quantize_weight_residual(r32: np.ndarray, group: int = GROUP):
+    """INT4 group quantization of the residual (Algorithm 1 step 5).
+
+    r32: float32 [m][n].  Groups of 64 consecutive rows k per column j
+    (reading R11).  Returns (codes int8 [m][n], scales float32 [m/64][n]).
+    """
+    codes_t, s_t = quantize_groups(np.ascontiguousarray(np.asarray(r32, np.float32).T), group)
+    return np.ascontiguousarray(codes_t.T), np.ascontiguousarray(s_t.T)
+
+
+def prepare_weights(w32: np.ndarray, a: Optional[np.ndarray], rank: int,
+                    group: int = GROUP, alpha: float = 0.5) -> dict:
+    """Offline preparation of one protected layer (Algorithm 1 steps 2-5, 9).
+
+    w32: float32 [m][n]; a: float32 [m] calibration maxima, or None (no smoothing).
+    Returns a dict with lam32, inv32, wt (float64 W~), l1 (float32 holding bf16,
+    [m][r]), l2 ([r][n]), r32 (float32 residual), qw (int8 codes [m][n]),
+    sw (fp16 values as float32 [m/64][n]), sigma.
+    """
+    w32 = np.asarray(w32, dtype=np.float32)
+    m, n = w32.shape
+    if a is None:
+        lam32 = np.ones(m, np.float32)
+        inv32 = None
+    else:
+        _, lam32, inv32 = smoothing_lambda(a, w32, alpha)
+    wt = smooth_weight(w32, lam32)
+    l1, l2, sigma = truncated_svd(wt, rank)
+    l1b = bf16_from_f64(l1)
+    l2b = bf16_from_f64(l2)
+    r64 = residual(wt, l1b, l2b)
+    r32 = r64.astype(np.float32)
+    qw, sw = quantize_weight_residual(r32, group)
+    return {"lam32": lam32, "inv32": inv32, "wt": wt, "l1": l1b, "l2": l2b,
+            "r64": r64, "r32": r32, "qw": qw, "sw": sw, "sigma": sigma,
+            "rank": rank, "group": group, "alpha": alpha}
+
+
+def append_lora(l1b: np.ndarray, l2b: np.ndarray, lam32: Optional[np.ndarray],
+                lora_a: np.ndarray, lora_b: np.ndarray, scale: float):
+    """Widen the protected branch with an adapter W += scale * A B  (Eq.13).
+
+    In smoothed coordinates the adapter becomes (D A) B (sec. 7), so
+    L1' = [L1 | bf16(diag(lambda) A)], L2' = [L2 ; bf16(scale * B)] (reading
+    R10); the quantized residual is untouched.
+    """
+    a64 = np.asarray(lora_a, dtype=np.float64)
+    if lam32 is not None:
+        a64 = a64 * np.asarray(lam32, dtype=np.float64)[:, None]
+    b64 = float(scale) * np.asarray(lora_b, dtype=np.float64)
+    return (np.concatenate([l1b, bf16_from_f64(a64)], axis=1),
+            np.concatenate([l2b, bf16_from_f64(b64)], axis=0))
+
+
+# --------------------------------------------------------------------------
+# Runtime: [Review] sec. 4.2 Eq.(7) and sec. 6.1 Algorithm 2
+# --------------------------------------------------------------------------
+
+
+def quantize_activation(x32: np.ndarray, inv32: Optional[np.ndarray], group: int = GROUP):
+    """Algorithm 2 steps 1 and 3: smooth, round to bf16, group-quantize per row.
+
+    Returns (xt float32 [b][m] bf16 values, qx int8 [b][m], sx float32 [b][m/64]).
+    """
+    xt = smooth_activation(x32, inv32)
+    qx, sx = quantize_groups(xt, group)
+    return xt, qx, sx
+
+
+def lowrank_down(xt: np.ndarray, l1b: np.ndarray) -> np.ndarray:
+    """Algorithm 2 step 2: Z = X~ L1, accumulated in float64."""
+    return np.asarray(xt, dtype=np.float64) @ np.asarray(l1b, dtype=np.float64)
+
+
+def group_isums(qx: np.ndarray, qw: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """isum[i, j, g] = sum_{k in group g} qx[i, k] * qw[k, j], exact int64.
+
+    Brute-force reference for small shapes (sum of integer products)."""
+    b, m = qx.shape
+    G = m // group
+    out = np.zeros((b, qw.shape[1], G), dtype=np.int64)
+    for g in range(G):
+        ks = slice(g * group, (g + 1) * group)
+        out[:, :, g] = qx[:, ks].astype(np.int64) @ qw[ks, :].astype(np.int64)
+    return out
+
+
+def gemm_main(qx, sx, qw, sw, group: int = GROUP) -> np.ndarray:
+    """Low-bit main branch Q(X~) Q(R) = sum_g sx[i,g] sw[g,j] isum[i,j,g]  (Eq.7).
+
+    Evaluated as one float64 product of the dequantized matrices; every
+    dequantized entry is exact in float64.
+    """
+    xq = dequantize_groups(qx, sx, group)                          # [b][m]
+    wq = dequantize_groups(np.ascontiguousarray(qw.T), np.ascontiguousarray(sw.T), group).T
+    return xq @ wq
+
+
+def lowrank_up(z64: np.ndarray, l2b: np.ndarray) -> np.ndarray:
+    """Algorithm 2 step 6: bf16(Z) L2 in float64 (reading R9)."""
+    return bf16_from_f64(z64).astype(np.float64) @ np.asarray(l2b, dtype=np.float64)
+
+
+def linear(x32: np.ndarray, layer: dict, bias: Optional[np.ndarray] = None,
+           group: int = GROUP) -> dict:
+    """Whole fused layer, Algorithm 2 steps 1-8:  Y = Q(X~)Q(R) + bf16(X~ L1) L2 (+ bias).
+
+    layer: dict with inv32 (or None), l1 [m][r], l2 [r][n], qw [m][n], sw [m/64][n].
+    Returns dict(y=float64 [b][n], xt, qx, sx, z).
+    """
+    xt, qx, sx = quantize_activation(x32, layer.get("inv32"), group)
+    y = gemm_main(qx, sx, layer["qw"], layer["sw"], group)
+    r = layer["l1"].shape[1]
+    z = lowrank_down(xt, layer["l1"]) if r else np.zeros((x32.shape[0], 0))
+    if r:
+        y = y + lowrank_up(z, layer["l2"])
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)[None, :]
+    return {"y": y, "xt": xt, "qx": qx, "sx": sx, "z": z}
+
+
+def linear_rows(x32_rows: np.ndarray, layer: dict, cols: Optional[np.ndarray] = None,
+                bias: Optional[np.ndarray] = None, group: int = GROUP) -> np.ndarray:
+    """Y for a subset of rows (and optionally columns), for sampled full-size checks.
+
+    Rows are independent in every step (quantization groups run along a row),
+    so this equals the corresponding slice of ``linear``."""
+    qw, sw, l2 = layer["qw"], layer["sw"], layer["l2"]
+    if cols is not None:
+        qw, sw, l2 = qw[:, cols], sw[:, cols], l2[:, cols]
+        bias = None if bias is None else np.asarray(bias)[cols]
+    sub = dict(layer, qw=qw, sw=sw, l2=l2)
+    return linear(x32_rows, sub, bias, group)["y"]
+
+
+# --------------------------------------------------------------------------
+# Analysis: [Review] sec. 4.1 Eq.(5)-(6), sec. 4.3 Eq.(9), sec. 6.1-6.2 Eq.(11)-(12)
+# --------------------------------------------------------------------------
+
+
+def prop41_bound(x, w, qx_deq, qw_deq) -> float:
+    """Right-hand side of Eq.(6): ||X||F ||dW||F + ||dX||F (||W||F + ||dW||F)."""
+    dW = np.linalg.norm(w - qw_deq)
+    dX = np.linalg.norm(x - qx_deq)
+    return float(np.linalg.norm(x) * dW + dX * (np.linalg.norm(w) + dW))
+
+
+def eq9_group_bound(v: np.ndarray, qmax: int = QMAX) -> float:
+    """Eq.(9) for one group of N values: sqrt(N) / (2 qmax) * max|v|."""
+    v = np.asarray(v, dtype=np.float64)
+    return math.sqrt(v.size) / (2 * qmax) * float(np.max(np.abs(v)))
+
+
+def mac_ratio(m: int, n: int, r: int) -> float:
+    """Eq.(11): low-rank MACs over dense MACs, r/m + r/n."""
+    return r / m + r / n
+
+
+def storage_ratio(m: int, n: int, r: int) -> float:
+    """Eq.(12): (mn/2 + 2r(m+n)) bytes over 2mn BF16 bytes = 1/4 + r/m + r/n."""
+    return (m * n / 2 + 2 * r * (m + n)) / (2 * m * n)
+
+
+def lowrank_fix_of_quant_error(x32, w32, a, rank: int, alpha: float = 0.5,
+                               group: int = GROUP) -> np.ndarray:
+    """Negative control discussed in sec. 5: quantize W~ first, then protect a
+    rank-r SVD of the rounding error E = W~ - Q(W~) in a bf16 branch.
+
+    Returns Y_hat = Q(X~) Q(W~) + X~ L1e L2e in float64.
+    """
+    _, lam32, inv32 = smoothing_lambda(a, w32, alpha)
+    wt = smooth_weight(w32, lam32)
+    qw, sw = quantize_weight_residual(wt.astype(np.float32), group)
+    wq = dequantize_groups(np.ascontiguousarray(qw.T), np.ascontiguousarray(sw.T), group).T
+    l1, l2, _ = truncated_svd(wt - wq, rank)
+    xt, qx, sx = quantize_activation(x32, inv32, group)
+    return gemm_main(qx, sx, qw, sw, group) + lowrank_up(lowrank_down(xt, bf16_from_f64(l1)),
+                                                         bf16_from_f64(l2))
+
+
+def smoothed_w4a4_no_branch(x32, w32, a, alpha: float = 0.5, group: int = GROUP) -> np.ndarray:
+    """Q(X~) Q(W~): smoothing alone, no protected branch (rank 0)."""
+    _, lam32, inv32 = smoothing_lambda(a, w32, alpha)
+    wt = smooth_weight(w32, lam32)
+    qw, sw = quantize_weight_residual(wt.astype(np.float32), group)
+    _, qx, sx = quantize_activation(x32, inv32, group)
+    return gemm_main(qx, sx, qw, sw, group)
+
+
+def naive_w4a4(x32, w32, group: int = GROUP) -> np.ndarray:
+    """Q(X) Q(W): no smoothing, no branch."""
+    qw, sw = quantize_weight_residual(np.asarray(w32, np.float32), group)
+    _, qx, sx = quantize_activation(x32, None, group)
+    return gemm_main(qx, sx, qw, sw, group)
