@@ -1,0 +1,202 @@
+/*
+ * svdq.h -- C ABI of the SVDQuant linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer computes, for X (b x m) and a prepared weight W (m x n),
+ *
+ *     Y = Q(X diag(lambda)^-1) Q(R) + (X diag(lambda)^-1 L1) L2  (+ bias)
+ *
+ * Sources (cited by section / equation / algorithm; no text is quoted):
+ *   [Review]   "SVDQuant: How a Small High-Precision Branch Makes 4-Bit
+ *              Diffusion Practical" -- technical review of arXiv:2411.05007v4.
+ *   [Nunchaku] "SVDQuant: 4-bit Quantization Enables Efficient Diffusion Model
+ *              Inference on Consumer GPUs", section "Nunchaku".
+ *
+ * Conventions shared by every entry point
+ *   - All matrices are row-major; dimensions are int32; b >= 0, m, n >= 1.
+ *   - The quantization group is 64 input channels (argument `group` must be
+ *     SVDQ_GROUP) and m must be a multiple of 64 ([Review] sec. 8: INT4 uses
+ *     group 64 on both operands with 16-bit scales).
+ *   - INT4 codes are symmetric in [-7, 7] ([Review] sec. 2.2, Eq.(1)); two codes
+ *     per byte, even channel in the low nibble ([Nunchaku]).
+ *   - Packed code tensors are GROUP-MAJOR: for group g (channels 64g..64g+63)
+ *     and row (or column) r, one 32-byte record holds the 64 codes; byte t of
+ *     the record = code[64g+2t] | code[64g+2t+1] << 4.  A tensor of R rows is
+ *     laid out [m/64][R][32].
+ *   - Scales are IEEE fp16 bit patterns, bf16 tensors are bf16 bit patterns
+ *     (uint16_t); fp32 is IEEE float.
+ *   - "HOST" entry points take host pointers and run synchronously on the CPU
+ *     (offline preparation, [Review] sec. 5 Algorithm 1).  "DEVICE" entry points
+ *     take device pointers, validate on the host, then enqueue HIP kernels on
+ *     `stream` (a hipStream_t; NULL = default stream) and return without
+ *     synchronising ([Review] sec. 6.1 Algorithm 2).
+ *   - Ownership: the caller allocates and frees every buffer.  The library
+ *     never allocates device memory and keeps no pointer after a call returns.
+ *   - Errors: every argument is checked BEFORE any HIP call or any write; on an
+ *     error nothing is launched, no output is touched, and a nonzero
+ *     svdq_status is returned.  svdq_last_error() gives a message (per
+ *     thread).  Faults inside a kernel surface at the caller's next
+ *     synchronisation, as usual for HIP.
+ *   - Device pointers must be 16-byte aligned unless stated otherwise.
+ *   - Every entry point is reentrant; the only library state is the per-thread
+ *     error message.
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum svdq_status {
+  SVDQ_OK = 0,
+  SVDQ_ERR_INVALID_ARG = 1,    /* null pointer, bad dimension, alpha outside [0, 1] */
+  SVDQ_ERR_UNSUPPORTED = 2,    /* group != 64, m % 64 != 0, rank above the limit */
+  SVDQ_ERR_ALIGNMENT = 3,      /* device pointer not 16-byte aligned */
+  SVDQ_ERR_NONFINITE = 4,      /* NaN / Inf in a preparation input */
+  SVDQ_ERR_NO_CONVERGENCE = 5, /* truncated SVD did not converge */
+  SVDQ_ERR_WORKSPACE = 6,      /* workspace missing or too small */
+  SVDQ_ERR_HIP = 7             /* a HIP launch or runtime call failed */
+} svdq_status;
+
+enum { SVDQ_OUT_BF16 = 0, SVDQ_OUT_F32 = 1 };
+
+#define SVDQ_GROUP 64
+#define SVDQ_MAX_RANK 256
+
+/*
+ * A prepared layer on the device ([Review] sec. 5 Algorithm 1, step 9: the
+ * stored factors, quantized residual, scales and transform).  Every pointer is
+ * DEVICE memory owned by the caller.
+ *   m, n        input / output features; m % 64 == 0.
+ *   rank        width r of the protected branch, 0 <= r <= SVDQ_MAX_RANK.
+ *   group       must be 64.
+ *   smooth_inv  fp32 [m]: 1/lambda (the runtime half of Eq.(3), X~ = X D^-1),
+ *               or NULL for no smoothing.
+ *   qw          INT4 codes of the residual R, group-major [m/64][n][32].
+ *   wscale      fp16 [m/64][n]: one scale per (group, output column).
+ *   l1          bf16 [rank][m]: L1 TRANSPOSED (each of the r columns of L1 is
+ *               contiguous).  NULL iff rank == 0.
+ *   l2          bf16 [n][rank]: L2 TRANSPOSED (the r coefficients of each output
+ *               column are contiguous; any alignment).  NULL iff rank == 0.
+ *   bias        bf16 [n] added before the store ([Review] Algorithm 2 step 8),
+ *               or NULL (any alignment).
+ */
+typedef struct svdq_layer {
+  int32_t m, n, rank, group;
+  const float* smooth_inv;
+  const uint8_t* qw;
+  const uint16_t* wscale;
+  const uint16_t* l1;
+  const uint16_t* l2;
+  const uint16_t* bias;
+} svdq_layer;
+
+/* ---------------------------------------------------------------------------
+ * HOST: offline preparation of one layer  ([Review] sec. 3.1 Eq.(3)-(4),
+ * sec. 5 Eq.(10) and Algorithm 1 steps 2-5).
+ *
+ *   W         fp32 [m][n], the original weight (finite).
+ *   act_amax  fp32 [m] calibration maxima max_i |X_ik| (finite, >= 0), or NULL
+ *             for no smoothing (lambda = 1).
+ *   alpha     migration strength in [0, 1] (0.5 in the configurations here).
+ *   Computes lambda_k = a_k^alpha / w_k^(1-alpha) with w_k = max_j |W_kj| in
+ *   fp64 (lambda_k = 1 where a_k or w_k is 0), W~ = diag(lambda) W, a rank-r
+ *   truncated SVD W~ ~ L1 L2 with Sigma folded into L1, bf16 factors, the
+ *   residual R = W~ - L1 L2 in fp64 using the bf16 factors, and its INT4 group
+ *   quantization with fp16 scales s = fp16(fl32(amax / 7)).
+ *   Outputs (HOST buffers, caller-allocated, sizes as in svdq_layer):
+ *     qw [m/64][n][32], wscale [m/64][n], l1 [rank][m], l2 [n][rank],
+ *     lambda fp32 [m], smooth_inv fp32 [m] (= fl32(1 / lambda)),
+ *     residual fp32 [m][n] (nullable: the fp32 R that was quantized).
+ *   l1 / l2 may be NULL iff rank == 0.  1 <= rank <= min(m, n, SVDQ_MAX_RANK)
+ *   or rank == 0.  Uses fp64 and all host cores; returns
+ *   SVDQ_ERR_NO_CONVERGENCE if the SVD iteration fails.
+ * ------------------------------------------------------------------------- */
+int svdq_prepare_weights(const float* W, const float* act_amax, int m, int n, int rank,
+                         int group, float alpha, uint8_t* qw, uint16_t* wscale, uint16_t* l1,
+                         uint16_t* l2, float* lambda, float* smooth_inv, float* residual);
+
+/* HOST: the INT4 group quantization step alone ([Review] Algorithm 1 step 5 with
+ * Eq.(1)): R fp32 [m][n] -> qw [m/64][n][32], wscale fp16 [m/64][n]. */
+int svdq_quantize_residual(const float* R, int m, int n, int group, uint8_t* qw,
+                           uint16_t* wscale);
+
+/* HOST: attach an additive adapter W += scale * A B without re-quantizing
+ * ([Review] sec. 7, Eq.(13)).  In smoothed coordinates the adapter is (D A) B,
+ * so the branch widens to
+ *     L1' = [L1 | bf16(diag(lambda) A)],   L2' = [L2 ; bf16(scale B)],
+ * rank' = rank + k; qw and wscale are untouched.
+ *   l1 bf16 [rank][m], l2 bf16 [n][rank] (may be NULL iff rank == 0),
+ *   lambda fp32 [m] or NULL (= 1), A fp32 [m][k], B fp32 [k][n], k >= 1,
+ *   rank + k <= SVDQ_MAX_RANK.
+ *   Outputs: l1_out bf16 [rank+k][m], l2_out bf16 [n][rank+k]. */
+int svdq_append_lora(const uint16_t* l1, const uint16_t* l2, int m, int n, int rank,
+                     const float* lambda, const float* A, const float* B, int k, float scale,
+                     uint16_t* l1_out, uint16_t* l2_out);
+
+/* DEVICE: calibration statistic a_k = max_i |X_ik| over one batch of layer
+ * inputs ([Review] sec. 3.1 Eq.(4) statistics; Algorithm 1 step 1).
+ *   x bf16 [b][m]; amax fp32 [m].  accumulate != 0 folds the batch into the
+ *   existing amax (max of both), otherwise amax is overwritten.  m % 8 == 0. */
+int svdq_calibrate_act_amax(const uint16_t* x, int b, int m, float* amax, int accumulate,
+                            void* stream);
+
+/* Bytes of scratch svdq_quantize_act_lowrank_down needs for split-channel
+ * partial sums of Z (0 when the split count for this shape is 1). */
+size_t svdq_act_workspace_size(int b, int m, int rank);
+
+/* DEVICE: fused activation quantization + low-rank down-projection
+ * ([Review] sec. 6.1 Algorithm 2 steps 1-3; Fig. 4 first fused pair).
+ * Each 64-channel group of every row is read once:
+ *     x~ = bf16(fl32(x * smooth_inv))             (Eq.(3), X~ = X D^-1)
+ *     ascale = fp16(fl32(max|x~| / 7)),  qx = clamp(round(x~ / ascale), -7, 7)  (Eq.(1))
+ *     z = x~ L1 (fp32 accumulation)
+ *   x bf16 [b][m]; smooth_inv fp32 [m] or NULL; l1 bf16 [rank][m] (NULL iff
+ *   rank == 0).  Outputs: qx group-major [m/64][b][32], ascale fp16 [m/64][b]
+ *   (any alignment), z fp32 [b][rank] (NULL iff rank == 0).
+ *   workspace: device, >= svdq_act_workspace_size(b, m, rank) bytes (may be
+ *   NULL when that is 0). */
+int svdq_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int rank, int group,
+                                   const float* smooth_inv, const uint16_t* l1, uint8_t* qx,
+                                   uint16_t* ascale, float* z, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* DEVICE: fused W4A4 GEMM + low-rank up-projection ([Review] sec. 6.1
+ * Algorithm 2 steps 4-8; Eq.(7)):
+ *     isum[i,j,g] = sum_{k in g} qx[i,k] qw[k,j]          (exact integer)
+ *     Y[i,j] = sum_g ascale[g,i] wscale[g,j] isum[i,j,g] + (bf16(z) L2)[i,j] + bias[j]
+ *   qx, ascale, z as produced by svdq_quantize_act_lowrank_down (z NULL iff
+ *   layer->rank == 0; z any 4-byte alignment); y [b][n] in y_dtype
+ *   (SVDQ_OUT_BF16, round-to-nearest-even, or SVDQ_OUT_F32); y needs only
+ *   element alignment.  layer->smooth_inv and layer->l1 are not used. */
+int svdq_gemm_w4a4_lowrank_up(const uint8_t* qx, const uint16_t* ascale, const float* z,
+                              const svdq_layer* layer, int b, void* y, int y_dtype,
+                              void* stream);
+
+/* Bytes of device workspace svdq_linear needs (qx, ascale and Z partials). */
+size_t svdq_linear_workspace_size(int b, int m, int rank, int group);
+
+/* DEVICE: the whole layer = the two fused kernels back to back on `stream`
+ * ([Review] sec. 6.1 Algorithm 2 steps 1-8).  x bf16 [b][m]; y [b][n] in
+ * y_dtype; workspace >= svdq_linear_workspace_size(b, m, rank, group) bytes,
+ * 256-byte aligned.  Z is bit-identical to the standalone kernels' Z. */
+int svdq_linear(const uint16_t* x, const svdq_layer* layer, int b, void* y, int y_dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* svdq_status_string(int status);
+
+/* Message describing the last error raised on the calling thread ("" if none). */
+const char* svdq_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int svdq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H */

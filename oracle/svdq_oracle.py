@@ -200,15 +200,23 @@ def smooth_activation(x32: np.ndarray, inv32: Optional[np.ndarray]) -> np.ndarra
 # --------------------------------------------------------------------------
 
 
-def truncated_svd(wt: np.ndarray, rank: int):
+def truncated_svd(wt: np.ndarray, rank: int, method: str = "lapack"):
     """L1 = U_r Sigma_r, L2 = V_r^T of the smoothed weight (Eq.10), float64.
 
-    Uses LAPACK's SVD (numpy) as the textbook routine.  Sign convention for
-    reproducible dumps: the largest-magnitude entry of each U column is made
-    positive (a sign flip of a singular pair leaves L1 L2 unchanged).
-    Returns (L1 [m][r], L2 [r][n], sigma [min(m, n)]).
+    method "lapack": numpy's full SVD, the textbook routine (returns every
+    singular value).  method "arpack": scipy's truncated SVD (ARPACK, tol 0)
+    for large layers; returns only the top `rank` singular values.  Sign
+    convention for reproducible dumps: the largest-magnitude entry of each U
+    column is made positive (a sign flip of a singular pair leaves L1 L2
+    unchanged).  Returns (L1 [m][r], L2 [r][n], sigma).
     """
-    U, S, Vt = np.linalg.svd(wt, full_matrices=False)
+    if method == "arpack" and 0 < rank < min(wt.shape) - 1:
+        from scipy.sparse.linalg import svds
+        U, S, Vt = svds(wt, k=rank, tol=0, random_state=0)
+        order = np.argsort(S)[::-1]
+        U, S, Vt = U[:, order], S[order], Vt[order]
+    else:
+        U, S, Vt = np.linalg.svd(wt, full_matrices=False)
     U = U[:, :rank].copy()
     Vt = Vt[:rank].copy()
     if rank:
@@ -236,7 +244,7 @@ def quantize_weight_residual(r32: np.ndarray, group: int = GROUP):
 
 
 def prepare_weights(w32: np.ndarray, a: Optional[np.ndarray], rank: int,
-                    group: int = GROUP, alpha: float = 0.5) -> dict:
+                    group: int = GROUP, alpha: float = 0.5, svd: str = "lapack") -> dict:
     """Offline preparation of one protected layer (Algorithm 1 steps 2-5, 9).
 
     w32: float32 [m][n]; a: float32 [m] calibration maxima, or None (no smoothing).
@@ -252,7 +260,7 @@ def prepare_weights(w32: np.ndarray, a: Optional[np.ndarray], rank: int,
     else:
         _, lam32, inv32 = smoothing_lambda(a, w32, alpha)
     wt = smooth_weight(w32, lam32)
-    l1, l2, sigma = truncated_svd(wt, rank)
+    l1, l2, sigma = truncated_svd(wt, rank, svd)
     l1b = bf16_from_f64(l1)
     l2b = bf16_from_f64(l2)
     r64 = residual(wt, l1b, l2b)

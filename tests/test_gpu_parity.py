@@ -1,0 +1,348 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bars (from the layer's contract):
+  * INT4 codes, fp16 scales, calibration maxima: bit-exact.
+  * per-group integer sums: exact (checked through fp32 outputs that carry them
+    exactly).
+  * Z: ||Z - Z_ref||_F / ||Z_ref||_F <= 1e-4 (fp32 MFMA accumulation vs fp64).
+  * Y: ||Y - Y_ref||_F / ||Y_ref||_F <= 2e-3 for fp32 and bf16 outputs.
+Inputs are seeded synthetic tensors; layers are prepared by the oracle, so no
+oracle input or expected value comes from the product.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import svdq_oracle as O
+from tests import layout as LY
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+Y_TOL = 2e-3
+Z_TOL = 1e-4
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def S():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import w4a4_rank_corrected_amd as S
+    S.lib()  # raises if the library is missing: no fallback
+    return S
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def dev_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def device_layer(S, lay, bias_bits=None, smoothing=True):
+    host = LY.oracle_layer_to_host_abi(lay)
+    return S.DeviceLayer(host, bias=bias_bits, smoothing=smoothing and lay.get("inv32") is not None)
+
+
+def y_to_np(y):
+    if y.dtype == torch.bfloat16:
+        return LY.bf16_bits_to_f32(y.view(torch.int16).cpu().numpy().view(np.uint16))
+    return y.cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# inputs
+# ---------------------------------------------------------------------------
+
+def adversarial_x(rng, b, m):
+    """bf16 activations exercising ties, zero / underflowing / saturating groups."""
+    x = rng.standard_normal((b, m)).astype(np.float32)
+    G = m // 64
+    for i in range(b):
+        g = i % G
+        kind = i % 7
+        seg = slice(64 * g, 64 * g + 64)
+        if kind == 0:
+            x[i, seg] = rng.integers(-7, 8, 64)
+            x[i, 64 * g] = 7.0                           # s = 1: exact integer codes
+        elif kind == 1:
+            x[i, seg] = rng.integers(-7, 8, 64) + 0.5    # many exact .5 ties
+            x[i, 64 * g] = 7.0
+        elif kind == 2:
+            x[i, seg] = 0.0                              # all-zero group
+        elif kind == 3:
+            x[i, seg] *= 1e-30                           # fp16 scale underflows to 0
+        elif kind == 4:
+            x[i, seg] *= 1e7                             # scale saturates at 65504
+        elif kind == 5:
+            x[i, seg] = rng.integers(-14, 15, 64) * 0.25  # ties against s = 0.5
+            x[i, 64 * g] = 3.5
+        elif kind == 6:
+            x[i, seg] *= 2.0 ** -133                     # bf16 subnormals
+    return workloads.bf16_bits_of(x)
+
+
+# ---------------------------------------------------------------------------
+# calibration statistic
+# ---------------------------------------------------------------------------
+
+def test_calibrate_amax_bit_exact(S):
+    rng = np.random.default_rng(0)
+    for (b, m) in [(64, 256), (37, 192), (1, 64), (300, 1024)]:
+        _say(f"calibrate b={b} m={m}")
+        xb = workloads.random_bf16_bits(rng, (b, m), 3.0)
+        xd = dev_bf16(xb)
+        am = S.svdq_calibrate_act_amax(xd)
+        torch.cuda.synchronize()
+        assert np.array_equal(am.cpu().numpy(), O.act_amax(LY.bf16_bits_to_f32(xb)))
+        # accumulate a second batch
+        xb2 = workloads.random_bf16_bits(rng, (b, m), 5.0)
+        S.svdq_calibrate_act_amax(dev_bf16(xb2), am, accumulate=True)
+        torch.cuda.synchronize()
+        both = np.concatenate([LY.bf16_bits_to_f32(xb), LY.bf16_bits_to_f32(xb2)])
+        assert np.array_equal(am.cpu().numpy(), O.act_amax(both))
+
+
+# ---------------------------------------------------------------------------
+# fused activation quantization + down-projection
+# ---------------------------------------------------------------------------
+
+ACT_CASES = [
+    # (b, m, rank, smoothing, adversarial)
+    (64, 256, 16, True, False),
+    (37, 192, 20, True, False),
+    (1, 64, 8, False, False),
+    (17, 128, 0, True, False),
+    (200, 512, 48, True, True),
+    (33, 320, 33, False, True),
+    (16, 4096, 32, True, False),     # many groups per split
+    (5, 64, 256, True, False),       # maximum rank
+]
+
+
+@pytest.mark.parametrize("b,m,rank,smooth,adv", ACT_CASES)
+def test_act_quant_down_parity(S, b, m, rank, smooth, adv):
+    _say(f"act_quant_down b={b} m={m} rank={rank} smooth={smooth} adv={adv}")
+    rng = np.random.default_rng(b * 1000 + m + rank)
+    xb = adversarial_x(rng, b, m) if adv else workloads.random_bf16_bits(rng, (b, m), 2.0)
+    x = LY.bf16_bits_to_f32(xb)
+    inv = None
+    if smooth:
+        inv = (1.0 / np.exp(rng.uniform(-2, 2, m))).astype(np.float32)
+    l1 = O.bf16_from_f32((rng.standard_normal((m, rank)) / np.sqrt(m)).astype(np.float32))
+    xt, qx, sx = O.quantize_activation(x, inv)
+    z_ref = O.lowrank_down(xt, l1)
+    qd, asd, zd = S.svdq_quantize_act_lowrank_down(
+        dev_bf16(xb), None if inv is None else dev_f32(inv),
+        dev_bf16(np.ascontiguousarray(LY.f32_to_bf16_bits(l1).T)) if rank else None, rank)
+    torch.cuda.synchronize()
+    assert np.array_equal(LY.unpack_codes(qd.cpu().numpy()), qx)
+    assert np.array_equal(asd.cpu().numpy().view(np.uint16), LY.f32_to_fp16_bits(sx.T))
+    if rank:
+        assert rel(zd.cpu().numpy(), z_ref) <= Z_TOL
+
+
+# ---------------------------------------------------------------------------
+# fused W4A4 GEMM + up-projection
+# ---------------------------------------------------------------------------
+
+def _oracle_layer(rng, m, n, rank, x32):
+    w = (rng.standard_normal((m, n)) / np.sqrt(m)).astype(np.float32)
+    w[rng.choice(m, max(1, m // 64), replace=False)] *= 8
+    return O.prepare_weights(w, O.act_amax(x32), rank)
+
+
+GEMM_CASES = [
+    # (b, m, n, rank, bias)
+    (64, 256, 256, 16, False),
+    (37, 192, 100, 20, True),     # ragged b, n (n % 4 != 0), rank not a multiple of 8
+    (130, 128, 260, 0, True),     # rank 0 = plain W4A4
+    (1, 64, 7, 3, False),
+    (256, 512, 384, 48, True),
+]
+
+
+@pytest.mark.parametrize("b,m,n,rank,bias", GEMM_CASES)
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemm_up_parity(S, b, m, n, rank, bias, out):
+    _say(f"gemm_up b={b} m={m} n={n} rank={rank} bias={bias} out={out}")
+    rng = np.random.default_rng(b + m + n + rank)
+    xb = workloads.random_bf16_bits(rng, (b, m), 1.5)
+    x = LY.bf16_bits_to_f32(xb)
+    lay = _oracle_layer(rng, m, n, rank, x)
+    bias_v = O.bf16_from_f32(rng.standard_normal(n).astype(np.float32)) if bias else None
+    xt, qx, sx = O.quantize_activation(x, lay["inv32"])
+    z = O.lowrank_down(xt, lay["l1"])
+    y_ref = O.gemm_main(qx, sx, lay["qw"], lay["sw"])
+    if rank:
+        y_ref = y_ref + O.lowrank_up(z.astype(np.float32).astype(np.float64), lay["l2"])
+    if bias:
+        y_ref = y_ref + bias_v[None, :]
+    dl = device_layer(S, lay, LY.f32_to_bf16_bits(bias_v) if bias else None)
+    qd = torch.from_numpy(LY.pack_codes(qx)).cuda()
+    asd = torch.from_numpy(LY.f32_to_fp16_bits(np.ascontiguousarray(sx.T)).view(np.int16)).cuda().view(torch.float16)
+    zd = dev_f32(z) if rank else None
+    y = S.svdq_gemm_w4a4_lowrank_up(qd, asd, zd, dl, b, torch.float32 if out == "f32" else torch.bfloat16)
+    torch.cuda.synchronize()
+    yn = y_to_np(y)
+    err = rel(yn, y_ref)
+    _say(f"  rel err {err:.3e}")
+    assert err <= (1e-5 if out == "f32" else Y_TOL)
+    if out == "bf16":
+        # only rare one-ulp flips against the correctly rounded reference
+        yr = O.bf16_from_f64(y_ref)
+        assert np.mean(yn != yr) < 0.01
+
+
+def test_gemm_exact_group_sums(S):
+    """All scales 1, rank 0, fp32 output: Y = sum_g isum exactly; isolating one
+    group at a time (other groups' activation scales 0) yields each isum."""
+    rng = np.random.default_rng(7)
+    b, m, n = 50, 256, 72
+    G = m // 64
+    qx = rng.integers(-7, 8, (b, m)).astype(np.int8)
+    qw = rng.integers(-7, 8, (m, n)).astype(np.int8)
+    qx[:3] = 7
+    qw[:, :2] = -7                                      # extreme sums 64*49
+    isum = O.group_isums(qx, qw)
+    host = {"m": m, "n": n, "rank": 0, "qw": LY.pack_codes(np.ascontiguousarray(qw.T)),
+            "wscale": LY.f32_to_fp16_bits(np.ones((G, n), np.float32)),
+            "l1": np.zeros((0, m), np.uint16), "l2": np.zeros((n, 0), np.uint16),
+            "smooth_inv": np.ones(m, np.float32)}
+    dl = S.DeviceLayer(host, smoothing=False)
+    qd = torch.from_numpy(LY.pack_codes(qx)).cuda()
+    ones = np.ones((G, b), np.float32)
+    for g in [None] + list(range(G)):
+        sc = ones.copy()
+        if g is not None:
+            sc[:] = 0.0
+            sc[g] = 1.0
+        asd = torch.from_numpy(LY.f32_to_fp16_bits(sc).view(np.int16)).cuda().view(torch.float16)
+        y = S.svdq_gemm_w4a4_lowrank_up(qd, asd, None, dl, b, torch.float32)
+        torch.cuda.synchronize()
+        expect = isum.sum(axis=2) if g is None else isum[:, :, g]
+        assert np.array_equal(y.cpu().numpy(), expect.astype(np.float32)), f"group {g}"
+
+
+# ---------------------------------------------------------------------------
+# whole layer
+# ---------------------------------------------------------------------------
+
+LINEAR_CASES = [
+    ("tiny", None),
+    ("tiny_ragged", None),
+    ("tiny_lora", None),
+]
+
+
+def _linear_case(name):
+    rng = np.random.default_rng(11)
+    if name.startswith("tiny"):
+        inp = workloads.make_inputs("tiny")
+        xb, x, w = inp["x_bits"], inp["x"], inp["w"]
+        if name == "tiny_ragged":
+            xb, x, w = xb[:45], x[:45], w[:, :200]
+        lay = O.prepare_weights(w, O.act_amax(x), 16)
+        if name == "tiny_lora":
+            A = (rng.standard_normal((w.shape[0], 16)) * np.sqrt(0.02)).astype(np.float32)
+            Bm = (rng.standard_normal((16, w.shape[1])) * np.sqrt(0.02)).astype(np.float32)
+            l1p, l2p = O.append_lora(lay["l1"], lay["l2"], lay["lam32"], A, Bm, 1.0)
+            lay = dict(lay, l1=l1p, l2=l2p)
+        return xb, x, lay
+
+
+@pytest.mark.parametrize("name", [c[0] for c in LINEAR_CASES])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_linear_parity(S, name, out):
+    _say(f"linear {name} out={out}")
+    xb, x, lay = _linear_case(name)
+    rng = np.random.default_rng(5)
+    n = lay["qw"].shape[1]
+    bias_v = O.bf16_from_f32(rng.standard_normal(n).astype(np.float32) * 0.1)
+    ref = O.linear(x, lay, bias=bias_v)
+    dl = device_layer(S, lay, LY.f32_to_bf16_bits(bias_v))
+    y = S.svdq_linear(dev_bf16(xb), dl, torch.float32 if out == "f32" else torch.bfloat16)
+    torch.cuda.synchronize()
+    err = rel(y_to_np(y), ref["y"])
+    _say(f"  rel err {err:.3e}")
+    assert err <= Y_TOL
+    if out == "f32":
+        assert err <= 1e-4
+
+
+def test_linear_equals_standalone_kernels_bitwise(S):
+    """svdq_linear = act kernel then GEMM kernel; Z partials are summed in the
+    same order in both routes, so the outputs agree bit for bit."""
+    xb, x, lay = _linear_case("tiny_lora")
+    dl = device_layer(S, lay)
+    xd = dev_bf16(xb)
+    y1 = S.svdq_linear(xd, dl, torch.float32)
+    qd, asd, zd = S.svdq_quantize_act_lowrank_down(xd, dl.smooth_inv, dl.l1, dl.rank)
+    y2 = S.svdq_gemm_w4a4_lowrank_up(qd, asd, zd, dl, xd.shape[0], torch.float32)
+    y3 = S.svdq_linear(xd, dl, torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert torch.equal(y1, y3)  # deterministic across calls
+
+
+def test_linear_empty_batch(S):
+    xb, x, lay = _linear_case("tiny")
+    dl = device_layer(S, lay)
+    y = S.svdq_linear(torch.empty((0, 256), dtype=torch.bfloat16, device="cuda"), dl)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 256)
+
+
+# ---------------------------------------------------------------------------
+# full-size layers, sampled rows (the configurations the benchmark times)
+# ---------------------------------------------------------------------------
+
+FULL = ["pixart_fc1", "flux_qkv", "flux_fc2", "flux_single_fc", "flux_single_out",
+        "flux_single_fc_b256", "flux_single_out_b256"]
+
+
+@pytest.mark.parametrize("cfg", FULL)
+def test_full_size_sampled(S, cfg):
+    _say(f"full-size {cfg}: generating inputs and oracle layer")
+    inp = workloads.make_inputs(cfg)
+    c = inp["cfg"]
+    x, xb = inp["x"], inp["x_bits"]
+    b = x.shape[0]
+    lay = O.prepare_weights(inp["w"], O.act_amax(x), c.rank, svd="arpack")
+    if c.lora_rank:
+        l1p, l2p = O.append_lora(lay["l1"], lay["l2"], lay["lam32"], inp["lora_a"], inp["lora_b"],
+                                 inp["lora_scale"])
+        lay = dict(lay, l1=l1p, l2=l2p)
+    del inp
+    dl = device_layer(S, lay)
+    xd = dev_bf16(xb)
+    _say(f"full-size {cfg}: running svdq_linear b={b} m={c.m} n={c.n} rank={lay['l1'].shape[1]}")
+    y = S.svdq_linear(xd, dl, torch.bfloat16)
+    qd, asd, zd = S.svdq_quantize_act_lowrank_down(xd, dl.smooth_inv, dl.l1, dl.rank)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, b, max(1, b // 40)), [b - 1]]))
+    y_ref = O.linear_rows(x[rows], lay)
+    err = rel(y_to_np(y)[rows], y_ref)
+    _say(f"  sampled rows {len(rows)}: rel err {err:.3e}")
+    assert err <= Y_TOL
+    xt, qx, sx = O.quantize_activation(x[rows], lay["inv32"])
+    qx_dev = LY.unpack_codes(qd[:, torch.from_numpy(rows).cuda(), :].cpu().numpy())
+    assert np.array_equal(qx_dev, qx)
+    assert np.array_equal(asd[:, torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint16),
+                          LY.f32_to_fp16_bits(np.ascontiguousarray(sx.T)))
+    assert rel(zd.cpu().numpy()[rows], O.lowrank_down(xt, lay["l1"])) <= Z_TOL

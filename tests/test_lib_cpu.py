@@ -1,0 +1,262 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol, its
+host preparation matches the oracle, and every validation error is raised on
+the host before any HIP call.  No test here launches a kernel."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import svdq_oracle as O
+from tests import layout as LY
+
+S = pytest.importorskip("w4a4_rank_corrected_amd")
+from w4a4_rank_corrected_amd import _binding as B  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib_or_skip():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libsvdq.so not built")
+    return B.lib()
+
+
+def test_exports_every_symbol_declared_in_header():
+    L = _lib_or_skip()
+    hdr = open(os.path.join(ROOT, "include", "svdq.h")).read()
+    names = set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(svdq_\w+)\s*\(", hdr, re.M))
+    assert len(names) >= 12
+    for nm in names:
+        assert hasattr(L, nm), nm
+    assert {s[0] for s in B.SIGNATURES} == names
+    assert L.svdq_abi_version() == 100
+
+
+def test_status_strings():
+    L = _lib_or_skip()
+    for st in range(0, 8):
+        assert L.svdq_status_string(st)
+    assert L.svdq_status_string(99) == b"unknown status"
+
+
+# ---------------------------------------------------------------------------
+# host preparation vs oracle
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def tiny():
+    inp = workloads.make_inputs("tiny")
+    a = O.act_amax(inp["x"])
+    return inp, a, O.prepare_weights(inp["w"], a, 16)
+
+
+def test_prepare_lambda_bit_exact(tiny):
+    _lib_or_skip()
+    inp, a, ref = tiny
+    p = S.svdq_prepare_weights(inp["w"], a, 16)
+    assert np.array_equal(p["lambda"], ref["lam32"])
+    assert np.array_equal(p["smooth_inv"], ref["inv32"])
+
+
+def test_prepare_svd_near_optimal_and_decomposition_exact(tiny):
+    _lib_or_skip()
+    inp, a, ref = tiny
+    p = S.svdq_prepare_weights(inp["w"], a, 16, want_residual=True)
+    l1 = LY.bf16_bits_to_f32(p["l1"]).T.astype(np.float64)   # [m][r]
+    l2 = LY.bf16_bits_to_f32(p["l2"]).T.astype(np.float64)   # [r][n]
+    wt = ref["wt"]
+    r_lib = wt - l1 @ l2
+    # the stored residual is exactly W~ - L1 L2 (up to its fp32 rounding)
+    assert np.linalg.norm(r_lib - p["residual"]) <= 2 ** -23 * np.linalg.norm(r_lib)
+    # truncated-SVD optimality (Eq.10): tail energy within 1e-3 of the oracle's
+    assert np.linalg.norm(r_lib) ** 2 <= (1 + 1e-3) * np.linalg.norm(ref["r64"]) ** 2
+    # the quantized residual is the library's own quantization of that residual
+    qw2, ws2 = S.svdq_quantize_residual(p["residual"])
+    assert np.array_equal(qw2, p["qw"]) and np.array_equal(ws2, p["wscale"])
+
+
+def test_quantize_residual_bit_exact_given_same_R(tiny):
+    _lib_or_skip()
+    _, _, ref = tiny
+    qw, ws = S.svdq_quantize_residual(ref["r32"])
+    assert np.array_equal(LY.unpack_codes(qw), np.ascontiguousarray(ref["qw"].T))
+    assert np.array_equal(ws, LY.f32_to_fp16_bits(ref["sw"]))
+
+
+def test_quantize_residual_adversarial_groups():
+    _lib_or_skip()
+    rng = np.random.default_rng(3)
+    R = (rng.standard_normal((256, 40)) * np.exp(rng.uniform(-6, 6, (1, 40)))).astype(np.float32)
+    R[:64, 0] = 0.0                                   # all-zero group
+    R[64:128, 1] = 1e-9                               # underflowing scale
+    R[128:192, 2] = np.tile([7.0, 2.5, 3.5, -2.5, 0.5, 1.5, -7.0, 0.0], 8)  # exact ties
+    R[192:, 3] = 1e6                                  # saturating scale
+    R[0, 4] = -3e5
+    qw, ws = S.svdq_quantize_residual(R)
+    codes, sw = O.quantize_weight_residual(R)
+    assert np.array_equal(LY.unpack_codes(qw), np.ascontiguousarray(codes.T))
+    assert np.array_equal(ws, LY.f32_to_fp16_bits(sw))
+
+
+def test_prepare_rank0_and_no_smoothing():
+    _lib_or_skip()
+    rng = np.random.default_rng(4)
+    w = (rng.standard_normal((128, 48)) / 11).astype(np.float32)
+    p = S.svdq_prepare_weights(w, None, 0, want_residual=True)
+    assert np.all(p["lambda"] == 1) and np.all(p["smooth_inv"] == 1)
+    assert np.array_equal(p["residual"], w)
+    ref = O.prepare_weights(w, None, 0)
+    assert np.array_equal(LY.unpack_codes(p["qw"]), np.ascontiguousarray(ref["qw"].T))
+
+
+def test_prepare_full_rank_residual_small():
+    _lib_or_skip()
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((64, 40)) / 8).astype(np.float32)
+    p = S.svdq_prepare_weights(w, None, 40, want_residual=True)
+    assert np.linalg.norm(p["residual"]) < 1e-2 * np.linalg.norm(w)
+
+
+def test_append_lora_matches_oracle_bits(tiny):
+    _lib_or_skip()
+    inp, a, ref = tiny
+    rng = np.random.default_rng(6)
+    A = (rng.standard_normal((256, 4)) * 0.14).astype(np.float32)
+    Bm = (rng.standard_normal((4, 256)) * 0.14).astype(np.float32)
+    host = LY.oracle_layer_to_host_abi(ref)
+    l1o, l2o = S.svdq_append_lora(host["l1"], host["l2"], 256, 256, 16, ref["lam32"], A, Bm, 0.5)
+    e1, e2 = O.append_lora(ref["l1"], ref["l2"], ref["lam32"], A, Bm, np.float32(0.5))
+    assert np.array_equal(l1o, LY.f32_to_bf16_bits(e1).T)
+    assert np.array_equal(l2o, LY.f32_to_bf16_bits(e2).T)
+    # rank-0 base: the adapter alone
+    l1z, l2z = S.svdq_append_lora(None, None, 256, 256, 0, None, A, Bm, 1.0)
+    e1, e2 = O.append_lora(np.zeros((256, 0), np.float32), np.zeros((0, 256), np.float32), None, A, Bm, 1.0)
+    assert np.array_equal(l1z, LY.f32_to_bf16_bits(e1).T) and np.array_equal(l2z, LY.f32_to_bf16_bits(e2).T)
+
+
+def test_host_bf16_rounding_matches_oracle_on_ties():
+    """The library's fp64->bf16 rounding (used for factors) against the oracle's."""
+    _lib_or_skip()
+    vals = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 1 + 2 ** -8 + 2 ** -40,
+                     3.0e38, 3.4e38, 1e-40, -2.5e-39, 0.0], np.float64)
+    # route through append_lora with lambda = 1 and A = the values (fp32-exact ones only)
+    v32 = vals.astype(np.float32)
+    A = v32.reshape(-1, 1)
+    m = len(vals)
+    l1o, _ = S.svdq_append_lora(None, None, m, 1, 0, None, A, np.ones((1, 1), np.float32), 1.0)
+    assert np.array_equal(l1o[0], LY.f32_to_bf16_bits(O.bf16_from_f64(v32.astype(np.float64))))
+
+
+# ---------------------------------------------------------------------------
+# validation errors: raised on the host, nothing launched, outputs untouched
+# ---------------------------------------------------------------------------
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address that is never dereferenced
+
+
+def _layer(**kw):
+    d = dict(m=128, n=64, rank=8, group=64, smooth_inv=None, qw=FAKE, wscale=FAKE, l1=FAKE, l2=FAKE,
+             bias=None)
+    d.update(kw)
+    return B.svdq_layer(d["m"], d["n"], d["rank"], d["group"], d["smooth_inv"], d["qw"], d["wscale"],
+                        d["l1"], d["l2"], d["bias"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(group=32), B.SVDQ_ERR_UNSUPPORTED),
+    (dict(m=100), B.SVDQ_ERR_UNSUPPORTED),
+    (dict(n=0), B.SVDQ_ERR_INVALID_ARG),
+    (dict(rank=300), B.SVDQ_ERR_UNSUPPORTED),
+    (dict(rank=-1), B.SVDQ_ERR_UNSUPPORTED),
+    (dict(qw=None), B.SVDQ_ERR_INVALID_ARG),
+    (dict(qw=FAKE + 4), B.SVDQ_ERR_ALIGNMENT),
+    (dict(l2=None), B.SVDQ_ERR_INVALID_ARG),
+    (dict(l1=None), B.SVDQ_ERR_INVALID_ARG),
+])
+def test_linear_validation_errors(kw, code):
+    L = _lib_or_skip()
+    lay = _layer(**kw)
+    st = L.svdq_linear(FAKE, ctypes.byref(lay), 16, FAKE, B.SVDQ_OUT_BF16, FAKE, 1 << 30, None)
+    assert st == code, L.svdq_last_error()
+    assert L.svdq_last_error()
+
+
+def test_linear_workspace_and_dtype_errors():
+    L = _lib_or_skip()
+    lay = _layer()
+    need = L.svdq_linear_workspace_size(16, 128, 8, 64)
+    assert need > 0
+    assert L.svdq_linear(FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE, need - 1, None) == B.SVDQ_ERR_WORKSPACE
+    assert L.svdq_linear(FAKE, ctypes.byref(lay), 16, FAKE, 0, None, need, None) == B.SVDQ_ERR_WORKSPACE
+    assert L.svdq_linear(FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE + 16, need, None) == B.SVDQ_ERR_ALIGNMENT
+    assert L.svdq_linear(FAKE, ctypes.byref(lay), 16, FAKE, 7, FAKE, need, None) == B.SVDQ_ERR_INVALID_ARG
+    assert L.svdq_linear(FAKE + 2, ctypes.byref(lay), 16, FAKE, 0, FAKE, need, None) == B.SVDQ_ERR_ALIGNMENT
+    assert L.svdq_linear(None, ctypes.byref(lay), 16, FAKE, 0, FAKE, need, None) == B.SVDQ_ERR_INVALID_ARG
+    assert L.svdq_linear(FAKE, None, 16, FAKE, 0, FAKE, need, None) == B.SVDQ_ERR_INVALID_ARG
+    assert L.svdq_linear(FAKE, ctypes.byref(lay), -1, FAKE, 0, FAKE, need, None) == B.SVDQ_ERR_INVALID_ARG
+    # empty batch: valid, nothing to do, no workspace needed
+    assert L.svdq_linear(FAKE, ctypes.byref(lay), 0, None, 0, None, 0, None) == B.SVDQ_OK
+
+
+def test_act_and_gemm_validation_errors():
+    L = _lib_or_skip()
+    f = L.svdq_quantize_act_lowrank_down
+    assert f(FAKE, 16, 128, 8, 32, None, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.SVDQ_ERR_UNSUPPORTED
+    assert f(FAKE, 16, 96, 8, 64, None, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.SVDQ_ERR_UNSUPPORTED
+    assert f(FAKE, 16, 128, 8, 64, None, None, FAKE, FAKE, FAKE, None, 0, None) == B.SVDQ_ERR_INVALID_ARG
+    assert f(FAKE, 16, 128, 8, 64, None, FAKE, FAKE, FAKE, None, None, 0, None) == B.SVDQ_ERR_INVALID_ARG
+    assert f(FAKE + 8, 16, 128, 8, 64, None, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.SVDQ_ERR_ALIGNMENT
+    assert f(FAKE, 16, 128, 0, 64, FAKE + 4, None, FAKE, FAKE, None, None, 0, None) == B.SVDQ_ERR_ALIGNMENT
+    assert f(FAKE, 0, 128, 8, 64, None, None, None, None, None, None, 0, None) == B.SVDQ_OK
+    # a shape that splits the channel groups needs a workspace
+    need = L.svdq_act_workspace_size(64, 4096, 32)
+    assert need > 0
+    assert f(FAKE, 64, 4096, 32, 64, None, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.SVDQ_ERR_WORKSPACE
+    g = L.svdq_gemm_w4a4_lowrank_up
+    lay = _layer()
+    assert g(FAKE, FAKE, None, ctypes.byref(lay), 16, FAKE, 0, None) == B.SVDQ_ERR_INVALID_ARG
+    assert g(None, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, None) == B.SVDQ_ERR_INVALID_ARG
+    assert g(FAKE + 1, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, None) == B.SVDQ_ERR_ALIGNMENT
+    assert g(FAKE, FAKE, FAKE, ctypes.byref(lay), 16, FAKE + 2, 1, None) == B.SVDQ_ERR_ALIGNMENT
+    c = L.svdq_calibrate_act_amax
+    assert c(FAKE, 16, 100, FAKE, 0, None) == B.SVDQ_ERR_UNSUPPORTED
+    assert c(FAKE, 16, 128, None, 0, None) == B.SVDQ_ERR_INVALID_ARG
+
+
+def test_prepare_validation_errors():
+    _lib_or_skip()
+    w = np.ones((128, 32), np.float32)
+    with pytest.raises(B.SvdqError) as e:
+        S.svdq_prepare_weights(w, None, 64)              # rank > min(m, n)
+    assert e.value.status == B.SVDQ_ERR_INVALID_ARG
+    w2 = w.copy()
+    w2[3, 4] = np.nan
+    with pytest.raises(B.SvdqError) as e:
+        S.svdq_prepare_weights(w2, None, 4)
+    assert e.value.status == B.SVDQ_ERR_NONFINITE
+    with pytest.raises(B.SvdqError) as e:
+        S.svdq_prepare_weights(w, -np.ones(128, np.float32), 4)
+    assert e.value.status == B.SVDQ_ERR_INVALID_ARG
+    with pytest.raises(B.SvdqError) as e:
+        S.svdq_prepare_weights(w, None, 4, alpha=1.5)
+    assert e.value.status == B.SVDQ_ERR_INVALID_ARG
+    with pytest.raises(B.SvdqError) as e:
+        S.svdq_prepare_weights(np.ones((100, 32), np.float32), None, 4)
+    assert e.value.status == B.SVDQ_ERR_UNSUPPORTED
+    with pytest.raises(B.SvdqError) as e:
+        S.svdq_append_lora(None, None, 128, 32, 250, None, np.ones((128, 8), np.float32),
+                           np.ones((8, 32), np.float32), 1.0)
+    assert e.value.status == B.SVDQ_ERR_UNSUPPORTED
+
+
+def test_workspace_sizes_cover_layout():
+    L = _lib_or_skip()
+    for (b, m, r) in [(1, 64, 0), (37, 256, 16), (4608, 3072, 32), (256, 15360, 48)]:
+        w = L.svdq_linear_workspace_size(b, m, r, 64)
+        G = m // 64
+        assert w >= G * b * 32 + G * b * 2 + b * r * 4
+        assert w % 256 == 0
+    assert L.svdq_linear_workspace_size(16, 100, 8, 64) == 0

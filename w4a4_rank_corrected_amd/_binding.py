@@ -1,0 +1,277 @@
+"""ctypes binding of the C ABI in include/svdq.h (argument marshalling only).
+
+Every computation runs in ``libsvdq.so``: the host entry points in its C++
+preparation code, the device entry points in its HIP kernels.  PyTorch is used
+only to own device memory and to name the current HIP stream.  If the library
+has not been built, every call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+SVDQ_OK = 0
+SVDQ_ERR_INVALID_ARG = 1
+SVDQ_ERR_UNSUPPORTED = 2
+SVDQ_ERR_ALIGNMENT = 3
+SVDQ_ERR_NONFINITE = 4
+SVDQ_ERR_NO_CONVERGENCE = 5
+SVDQ_ERR_WORKSPACE = 6
+SVDQ_ERR_HIP = 7
+SVDQ_OUT_BF16 = 0
+SVDQ_OUT_F32 = 1
+SVDQ_GROUP = 64
+SVDQ_MAX_RANK = 256
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsvdq.so")
+
+_c_int = ctypes.c_int
+_vp = ctypes.c_void_p
+_size = ctypes.c_size_t
+
+
+class svdq_layer(ctypes.Structure):
+    """Mirror of ``struct svdq_layer`` (all pointers are device addresses)."""
+    _fields_ = [("m", ctypes.c_int32), ("n", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("smooth_inv", _vp), ("qw", _vp), ("wscale", _vp),
+                ("l1", _vp), ("l2", _vp), ("bias", _vp)]
+
+
+# (name, restype, argtypes) for every exported symbol of include/svdq.h
+SIGNATURES = [
+    ("svdq_prepare_weights", _c_int,
+     [_vp, _vp, _c_int, _c_int, _c_int, _c_int, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    ("svdq_quantize_residual", _c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp]),
+    ("svdq_append_lora", _c_int,
+     [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_int, ctypes.c_float, _vp, _vp]),
+    ("svdq_calibrate_act_amax", _c_int, [_vp, _c_int, _c_int, _vp, _c_int, _vp]),
+    ("svdq_act_workspace_size", _size, [_c_int, _c_int, _c_int]),
+    ("svdq_quantize_act_lowrank_down", _c_int,
+     [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _size, _vp]),
+    ("svdq_gemm_w4a4_lowrank_up", _c_int,
+     [_vp, _vp, _vp, ctypes.POINTER(svdq_layer), _c_int, _vp, _c_int, _vp]),
+    ("svdq_linear_workspace_size", _size, [_c_int, _c_int, _c_int, _c_int]),
+    ("svdq_linear", _c_int,
+     [_vp, ctypes.POINTER(svdq_layer), _c_int, _vp, _c_int, _vp, _size, _vp]),
+    ("svdq_status_string", ctypes.c_char_p, [_c_int]),
+    ("svdq_last_error", ctypes.c_char_p, []),
+    ("svdq_abi_version", _c_int, []),
+]
+
+_lib = None
+
+
+class SvdqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"svdq status {status}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C-ABI library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, res, args in SIGNATURES:
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != SVDQ_OK:
+        L = lib()
+        msg = L.svdq_last_error().decode() or L.svdq_status_string(status).decode()
+        raise SvdqError(status, msg)
+
+
+def _ptr(a) -> Optional[int]:
+    """Address of a numpy array / torch tensor (None passes through as NULL)."""
+    if a is None:
+        return None
+    if isinstance(a, np.ndarray):
+        assert a.flags["C_CONTIGUOUS"], "host arrays must be C-contiguous"
+        return a.ctypes.data
+    assert a.is_contiguous(), "tensors must be contiguous"
+    return a.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# host entry points (offline preparation)
+# ---------------------------------------------------------------------------
+
+def svdq_prepare_weights(W: np.ndarray, act_amax: Optional[np.ndarray], rank: int,
+                         group: int = SVDQ_GROUP, alpha: float = 0.5,
+                         want_residual: bool = False) -> dict:
+    """Host preparation of one layer; returns the host arrays of the layer bundle.
+
+    Keys: qw uint8 [m/64][n][32], wscale uint16 (fp16 bits) [m/64][n],
+    l1 uint16 (bf16 bits) [rank][m], l2 uint16 [n][rank], lambda / smooth_inv
+    float32 [m], residual float32 [m][n] (if requested), m, n, rank.
+    """
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    m, n = W.shape
+    a = None if act_amax is None else np.ascontiguousarray(act_amax, dtype=np.float32)
+    G = max(m // SVDQ_GROUP, 0)
+    out = {
+        "qw": np.zeros((G, n, 32), np.uint8),
+        "wscale": np.zeros((G, n), np.uint16),
+        "l1": np.zeros((rank, m), np.uint16),
+        "l2": np.zeros((n, rank), np.uint16),
+        "lambda": np.zeros(m, np.float32),
+        "smooth_inv": np.zeros(m, np.float32),
+        "m": m, "n": n, "rank": rank,
+    }
+    res = np.zeros((m, n), np.float32) if want_residual else None
+    _check(lib().svdq_prepare_weights(
+        _ptr(W), _ptr(a), m, n, rank, group, alpha, _ptr(out["qw"]), _ptr(out["wscale"]),
+        _ptr(out["l1"]) if rank else None, _ptr(out["l2"]) if rank else None,
+        _ptr(out["lambda"]), _ptr(out["smooth_inv"]), _ptr(res)))
+    if want_residual:
+        out["residual"] = res
+    return out
+
+
+def svdq_quantize_residual(R: np.ndarray, group: int = SVDQ_GROUP):
+    R = np.ascontiguousarray(R, dtype=np.float32)
+    m, n = R.shape
+    qw = np.zeros((max(m // SVDQ_GROUP, 0), n, 32), np.uint8)
+    ws = np.zeros((max(m // SVDQ_GROUP, 0), n), np.uint16)
+    _check(lib().svdq_quantize_residual(_ptr(R), m, n, group, _ptr(qw), _ptr(ws)))
+    return qw, ws
+
+
+def svdq_append_lora(l1: Optional[np.ndarray], l2: Optional[np.ndarray], m: int, n: int, rank: int,
+                     lam: Optional[np.ndarray], A: np.ndarray, B: np.ndarray, scale: float):
+    A = np.ascontiguousarray(A, dtype=np.float32)
+    B = np.ascontiguousarray(B, dtype=np.float32)
+    k = A.shape[1]
+    l1o = np.zeros((rank + k, m), np.uint16)
+    l2o = np.zeros((n, rank + k), np.uint16)
+    lam = None if lam is None else np.ascontiguousarray(lam, dtype=np.float32)
+    l1 = None if (l1 is None or rank == 0) else np.ascontiguousarray(l1, dtype=np.uint16)
+    l2 = None if (l2 is None or rank == 0) else np.ascontiguousarray(l2, dtype=np.uint16)
+    _check(lib().svdq_append_lora(_ptr(l1), _ptr(l2), m, n, rank, _ptr(lam), _ptr(A), _ptr(B), k,
+                                  float(scale), _ptr(l1o), _ptr(l2o)))
+    return l1o, l2o
+
+
+# ---------------------------------------------------------------------------
+# device entry points
+# ---------------------------------------------------------------------------
+
+def svdq_calibrate_act_amax(x, amax=None, accumulate: bool = False, stream=None):
+    """x: bf16 CUDA tensor [b][m]; returns fp32 amax [m] (allocated if None)."""
+    import torch
+    b, m = x.shape
+    if amax is None:
+        amax = torch.empty(m, dtype=torch.float32, device=x.device)
+    _check(lib().svdq_calibrate_act_amax(_ptr(x), b, m, _ptr(amax), int(accumulate), _stream(stream)))
+    return amax
+
+
+def svdq_act_workspace_size(b: int, m: int, rank: int) -> int:
+    return int(lib().svdq_act_workspace_size(b, m, rank))
+
+
+def svdq_quantize_act_lowrank_down(x, smooth_inv, l1, rank: int, group: int = SVDQ_GROUP,
+                                   qx=None, ascale=None, z=None, workspace=None, stream=None):
+    """Returns (qx uint8 [m/64][b][32], ascale fp16 [m/64][b], z fp32 [b][rank] or None)."""
+    import torch
+    b, m = x.shape
+    dev = x.device
+    G = m // SVDQ_GROUP
+    if qx is None:
+        qx = torch.empty((G, b, 32), dtype=torch.uint8, device=dev)
+    if ascale is None:
+        ascale = torch.empty((G, b), dtype=torch.float16, device=dev)
+    if z is None and rank > 0:
+        z = torch.empty((b, rank), dtype=torch.float32, device=dev)
+    need = svdq_act_workspace_size(b, m, rank)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().svdq_quantize_act_lowrank_down(
+        _ptr(x), b, m, rank, group, _ptr(smooth_inv), _ptr(l1), _ptr(qx), _ptr(ascale), _ptr(z),
+        _ptr(workspace), wsb, _stream(stream)))
+    return qx, ascale, z
+
+
+class DeviceLayer:
+    """A prepared layer resident in device memory plus its ``svdq_layer`` struct."""
+
+    def __init__(self, host: dict, device="cuda", bias: Optional[np.ndarray] = None,
+                 smoothing: bool = True):
+        import torch
+        self.m, self.n, self.rank = int(host["m"]), int(host["n"]), int(host["rank"])
+        t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(device=device).view(dt)
+        self.qw = t(host["qw"], torch.uint8)
+        self.wscale = t(host["wscale"].view(np.int16), torch.float16)
+        self.smooth_inv = t(host["smooth_inv"], torch.float32) if smoothing else None
+        self.l1 = t(host["l1"].view(np.int16), torch.bfloat16) if self.rank else None
+        self.l2 = t(host["l2"].view(np.int16), torch.bfloat16) if self.rank else None
+        self.bias = None if bias is None else t(np.asarray(bias, np.uint16).view(np.int16), torch.bfloat16)
+        self.struct = svdq_layer(self.m, self.n, self.rank, SVDQ_GROUP, _ptr(self.smooth_inv),
+                                 _ptr(self.qw), _ptr(self.wscale), _ptr(self.l1), _ptr(self.l2),
+                                 _ptr(self.bias))
+
+    @classmethod
+    def from_tensors(cls, m, n, rank, qw, wscale, l1=None, l2=None, smooth_inv=None, bias=None):
+        self = cls.__new__(cls)
+        self.m, self.n, self.rank = m, n, rank
+        self.qw, self.wscale, self.l1, self.l2 = qw, wscale, l1, l2
+        self.smooth_inv, self.bias = smooth_inv, bias
+        self.struct = svdq_layer(m, n, rank, SVDQ_GROUP, _ptr(smooth_inv), _ptr(qw), _ptr(wscale),
+                                 _ptr(l1), _ptr(l2), _ptr(bias))
+        return self
+
+
+def svdq_gemm_w4a4_lowrank_up(qx, ascale, z, layer: DeviceLayer, b: Optional[int] = None,
+                              out_dtype=None, y=None, stream=None):
+    import torch
+    if b is None:
+        b = qx.shape[1]
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    code = SVDQ_OUT_BF16 if out_dtype == torch.bfloat16 else SVDQ_OUT_F32
+    if y is None:
+        y = torch.empty((b, layer.n), dtype=out_dtype, device=qx.device)
+    _check(lib().svdq_gemm_w4a4_lowrank_up(_ptr(qx), _ptr(ascale), _ptr(z), ctypes.byref(layer.struct),
+                                           b, _ptr(y), code, _stream(stream)))
+    return y
+
+
+def svdq_linear_workspace_size(b: int, m: int, rank: int, group: int = SVDQ_GROUP) -> int:
+    return int(lib().svdq_linear_workspace_size(b, m, rank, group))
+
+
+def svdq_linear(x, layer: DeviceLayer, out_dtype=None, y=None, workspace=None, stream=None):
+    import torch
+    b, m = x.shape
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    code = SVDQ_OUT_BF16 if out_dtype == torch.bfloat16 else SVDQ_OUT_F32
+    if y is None:
+        y = torch.empty((b, layer.n), dtype=out_dtype, device=x.device)
+    if workspace is None:
+        need = svdq_linear_workspace_size(b, m, layer.rank)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    wsb = workspace.numel() * workspace.element_size()
+    _check(lib().svdq_linear(_ptr(x), ctypes.byref(layer.struct), b, _ptr(y), code, _ptr(workspace),
+                             wsb, _stream(stream)))
+    return y

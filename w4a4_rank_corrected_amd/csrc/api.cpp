@@ -1,0 +1,394 @@
+// C-ABI entry points of the SVDQuant linear-layer library (declared in
+// include/svdq.h).  Every argument is validated here, on the host, before any
+// HIP call or any write to an output; then the work is handed to the host
+// preparation code (prep.cpp) or the HIP kernel launchers.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "internal.h"
+
+namespace svdq {
+
+static thread_local char g_err[512];
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+void clear_error() { g_err[0] = 0; }
+
+// Split plan of the act-quant kernel: enough workgroups to spread the rows'
+// channel groups over the whole chip (about 1024), never more splits than
+// groups.  Depends only on the shape, so the standalone kernel and the fused
+// layer sum Z in the same order.
+ActPlan act_plan(int b, int m, int rank) {
+  ActPlan p;
+  p.strips = (b + 15) / 16;
+  const int G = m / SVDQ_GROUP;
+  int splits = 1;
+  if (p.strips > 0) {
+    splits = (1024 + p.strips - 1) / p.strips;
+    splits = std::max(1, std::min(splits, std::min(G, 32)));
+  }
+  if (rank == 0) splits = std::max(1, splits);
+  p.groups_per_split = (G + splits - 1) / splits;
+  p.splits = (G + p.groups_per_split - 1) / p.groups_per_split;
+  return p;
+}
+
+}  // namespace svdq
+
+using namespace svdq;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE(cond, code, ...)  \
+  do {                            \
+    if (!(cond)) {                \
+      set_error(__VA_ARGS__);     \
+      return (code);              \
+    }                             \
+  } while (0)
+
+int check_group(int m, int group) {
+  REQUIRE(group == SVDQ_GROUP, SVDQ_ERR_UNSUPPORTED, "group must be %d (got %d)", SVDQ_GROUP, group);
+  REQUIRE(m >= SVDQ_GROUP && m % SVDQ_GROUP == 0, SVDQ_ERR_UNSUPPORTED,
+          "m must be a positive multiple of %d (got %d)", SVDQ_GROUP, m);
+  return SVDQ_OK;
+}
+
+int hip_status(int err, const char* what) {
+  if (err == 0) return SVDQ_OK;
+  set_error("%s: HIP error %d (%s)", what, err, hip_error_name(err));
+  return SVDQ_ERR_HIP;
+}
+
+struct LinearWorkspace {
+  size_t qx_off, as_off, z_off, zpart_off, total;
+};
+
+LinearWorkspace linear_ws_layout(int b, int m, int rank) {
+  LinearWorkspace w;
+  const size_t G = (size_t)(m / SVDQ_GROUP);
+  ActPlan p = act_plan(b, m, rank);
+  w.qx_off = 0;
+  w.as_off = round_up(w.qx_off + G * (size_t)b * 32, kAlign);
+  w.z_off = round_up(w.as_off + G * (size_t)b * 2, kAlign);
+  w.zpart_off = round_up(w.z_off + (size_t)b * (size_t)rank * 4, kAlign);
+  const size_t zpart = (rank > 0 && p.splits > 1) ? (size_t)p.splits * (size_t)b * (size_t)rank * 4 : 0;
+  w.total = round_up(w.zpart_off + zpart, kAlign);
+  if (b == 0) w.total = 0;
+  return w;
+}
+
+int check_layer(const svdq_layer* L) {
+  REQUIRE(L != nullptr, SVDQ_ERR_INVALID_ARG, "layer is NULL");
+  int st = check_group(L->m, L->group);
+  if (st) return st;
+  REQUIRE(L->n >= 1, SVDQ_ERR_INVALID_ARG, "n must be >= 1 (got %d)", L->n);
+  REQUIRE(L->rank >= 0 && L->rank <= SVDQ_MAX_RANK, SVDQ_ERR_UNSUPPORTED,
+          "rank must be in [0, %d] (got %d)", SVDQ_MAX_RANK, L->rank);
+  REQUIRE(L->qw && L->wscale, SVDQ_ERR_INVALID_ARG, "layer qw / wscale must not be NULL");
+  REQUIRE(aligned16(L->qw), SVDQ_ERR_ALIGNMENT, "layer qw must be 16-byte aligned");
+  REQUIRE(((uintptr_t)L->wscale & 1u) == 0, SVDQ_ERR_ALIGNMENT, "layer wscale must be 2-byte aligned");
+  if (L->rank > 0) {
+    REQUIRE(L->l2 != nullptr, SVDQ_ERR_INVALID_ARG, "layer l2 must not be NULL when rank > 0");
+    REQUIRE(((uintptr_t)L->l2 & 1u) == 0, SVDQ_ERR_ALIGNMENT, "layer l2 must be 2-byte aligned");
+  }
+  if (L->bias) REQUIRE(((uintptr_t)L->bias & 1u) == 0, SVDQ_ERR_ALIGNMENT, "bias must be 2-byte aligned");
+  return SVDQ_OK;
+}
+
+int check_y(void* y, int y_dtype, int b) {
+  REQUIRE(y_dtype == SVDQ_OUT_BF16 || y_dtype == SVDQ_OUT_F32, SVDQ_ERR_INVALID_ARG,
+          "y_dtype must be SVDQ_OUT_BF16 or SVDQ_OUT_F32 (got %d)", y_dtype);
+  if (b > 0) {
+    REQUIRE(y != nullptr, SVDQ_ERR_INVALID_ARG, "y must not be NULL");
+    REQUIRE(((uintptr_t)y & (y_dtype == SVDQ_OUT_F32 ? 3u : 1u)) == 0, SVDQ_ERR_ALIGNMENT,
+            "y must be element-aligned");
+  }
+  return SVDQ_OK;
+}
+
+bool all_finite(const float* p, size_t count) {
+  for (size_t i = 0; i < count; ++i)
+    if (!std::isfinite(p[i])) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int svdq_abi_version(void) { return 100; }
+
+const char* svdq_last_error(void) { return g_err; }
+
+const char* svdq_status_string(int status) {
+  switch (status) {
+    case SVDQ_OK: return "ok";
+    case SVDQ_ERR_INVALID_ARG: return "invalid argument";
+    case SVDQ_ERR_UNSUPPORTED: return "unsupported shape or parameter";
+    case SVDQ_ERR_ALIGNMENT: return "misaligned pointer";
+    case SVDQ_ERR_NONFINITE: return "non-finite input";
+    case SVDQ_ERR_NO_CONVERGENCE: return "SVD did not converge";
+    case SVDQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case SVDQ_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int svdq_quantize_residual(const float* R, int m, int n, int group, uint8_t* qw, uint16_t* wscale) {
+  clear_error();
+  int st = check_group(m, group);
+  if (st) return st;
+  REQUIRE(n >= 1, SVDQ_ERR_INVALID_ARG, "n must be >= 1 (got %d)", n);
+  REQUIRE(R && qw && wscale, SVDQ_ERR_INVALID_ARG, "R, qw and wscale must not be NULL");
+  REQUIRE(all_finite(R, (size_t)m * n), SVDQ_ERR_NONFINITE, "R holds NaN or Inf");
+  quantize_residual(R, m, n, qw, wscale);
+  return SVDQ_OK;
+}
+
+int svdq_prepare_weights(const float* W, const float* act_amax, int m, int n, int rank, int group,
+                         float alpha, uint8_t* qw, uint16_t* wscale, uint16_t* l1, uint16_t* l2,
+                         float* lambda, float* smooth_inv, float* residual) {
+  clear_error();
+  int st = check_group(m, group);
+  if (st) return st;
+  REQUIRE(n >= 1, SVDQ_ERR_INVALID_ARG, "n must be >= 1 (got %d)", n);
+  REQUIRE(W && qw && wscale && lambda && smooth_inv, SVDQ_ERR_INVALID_ARG,
+          "W, qw, wscale, lambda and smooth_inv must not be NULL");
+  REQUIRE(rank >= 0 && rank <= SVDQ_MAX_RANK, SVDQ_ERR_UNSUPPORTED, "rank must be in [0, %d] (got %d)",
+          SVDQ_MAX_RANK, rank);
+  REQUIRE(rank <= std::min(m, n), SVDQ_ERR_INVALID_ARG, "rank %d exceeds min(m, n) = %d", rank,
+          std::min(m, n));
+  REQUIRE(rank == 0 || (l1 && l2), SVDQ_ERR_INVALID_ARG, "l1 / l2 must not be NULL when rank > 0");
+  REQUIRE(alpha >= 0.0f && alpha <= 1.0f, SVDQ_ERR_INVALID_ARG, "alpha must be in [0, 1] (got %g)",
+          (double)alpha);
+  REQUIRE(all_finite(W, (size_t)m * n), SVDQ_ERR_NONFINITE, "W holds NaN or Inf");
+  if (act_amax) {
+    REQUIRE(all_finite(act_amax, (size_t)m), SVDQ_ERR_NONFINITE, "act_amax holds NaN or Inf");
+    for (int k = 0; k < m; ++k)
+      REQUIRE(act_amax[k] >= 0.0f, SVDQ_ERR_INVALID_ARG, "act_amax[%d] is negative", k);
+  }
+
+  std::vector<float> lam32(m), inv32(m);
+  smoothing_lambda(W, act_amax, m, n, (double)alpha, lam32.data(), inv32.data());
+
+  // W~ = diag(lambda) W in fp64 (Eq.(3); products of two fp32 are exact)
+  std::vector<double> wt((size_t)m * n);
+  for (int k = 0; k < m; ++k) {
+    const double lk = lam32[k];
+    for (int j = 0; j < n; ++j) wt[(size_t)k * n + j] = lk * (double)W[(size_t)k * n + j];
+  }
+
+  std::vector<double> L1((size_t)m * rank), L2((size_t)rank * n);
+  if (!truncated_svd(wt.data(), m, n, rank, L1.data(), L2.data())) {
+    set_error("truncated SVD did not converge (m=%d n=%d rank=%d)", m, n, rank);
+    return SVDQ_ERR_NO_CONVERGENCE;
+  }
+  // stored bf16 factors; the residual is formed with these rounded values
+  std::vector<uint16_t> l1b((size_t)m * rank), l2b((size_t)rank * n);
+  for (size_t i = 0; i < L1.size(); ++i) l1b[i] = f64_to_bf16(L1[i]);
+  for (size_t i = 0; i < L2.size(); ++i) l2b[i] = f64_to_bf16(L2[i]);
+  std::vector<float> r32((size_t)m * n);
+  {
+    std::vector<double> l2d((size_t)rank * n);
+    for (size_t i = 0; i < l2d.size(); ++i) l2d[i] = bf16_to_f32(l2b[i]);
+    std::vector<double> acc(n);
+    for (int i = 0; i < m; ++i) {
+      std::fill(acc.begin(), acc.end(), 0.0);
+      for (int t = 0; t < rank; ++t) {
+        const double a = bf16_to_f32(l1b[(size_t)i * rank + t]);
+        const double* l2row = &l2d[(size_t)t * n];
+        for (int j = 0; j < n; ++j) acc[j] += a * l2row[j];
+      }
+      for (int j = 0; j < n; ++j) r32[(size_t)i * n + j] = (float)(wt[(size_t)i * n + j] - acc[j]);
+    }
+  }
+  quantize_residual(r32.data(), m, n, qw, wscale);
+
+  std::memcpy(lambda, lam32.data(), sizeof(float) * m);
+  std::memcpy(smooth_inv, inv32.data(), sizeof(float) * m);
+  if (rank > 0) {
+    // l1 is stored transposed [rank][m]; l2 transposed [n][rank]
+    for (int i = 0; i < m; ++i)
+      for (int t = 0; t < rank; ++t) l1[(size_t)t * m + i] = l1b[(size_t)i * rank + t];
+    for (int t = 0; t < rank; ++t)
+      for (int j = 0; j < n; ++j) l2[(size_t)j * rank + t] = l2b[(size_t)t * n + j];
+  }
+  if (residual) std::memcpy(residual, r32.data(), sizeof(float) * r32.size());
+  return SVDQ_OK;
+}
+
+int svdq_append_lora(const uint16_t* l1, const uint16_t* l2, int m, int n, int rank,
+                     const float* lambda, const float* A, const float* B, int k, float scale,
+                     uint16_t* l1_out, uint16_t* l2_out) {
+  clear_error();
+  REQUIRE(m >= 1 && n >= 1, SVDQ_ERR_INVALID_ARG, "m, n must be >= 1");
+  REQUIRE(k >= 1, SVDQ_ERR_INVALID_ARG, "adapter rank k must be >= 1 (got %d)", k);
+  REQUIRE(rank >= 0 && rank + k <= SVDQ_MAX_RANK, SVDQ_ERR_UNSUPPORTED,
+          "rank + k must be <= %d (got %d + %d)", SVDQ_MAX_RANK, rank, k);
+  REQUIRE(rank == 0 || (l1 && l2), SVDQ_ERR_INVALID_ARG, "l1 / l2 must not be NULL when rank > 0");
+  REQUIRE(A && B && l1_out && l2_out, SVDQ_ERR_INVALID_ARG, "A, B, l1_out, l2_out must not be NULL");
+  REQUIRE(std::isfinite(scale), SVDQ_ERR_NONFINITE, "scale is not finite");
+  REQUIRE(all_finite(A, (size_t)m * k) && all_finite(B, (size_t)k * n), SVDQ_ERR_NONFINITE,
+          "A or B holds NaN or Inf");
+  if (lambda) REQUIRE(all_finite(lambda, (size_t)m), SVDQ_ERR_NONFINITE, "lambda holds NaN or Inf");
+  const int r2 = rank + k;
+  // L1' = [L1 | bf16(diag(lambda) A)] stored transposed [r2][m]
+  if (rank > 0) std::memmove(l1_out, l1, sizeof(uint16_t) * (size_t)rank * m);
+  for (int t = 0; t < k; ++t)
+    for (int i = 0; i < m; ++i) {
+      double lam = lambda ? (double)lambda[i] : 1.0;
+      l1_out[(size_t)(rank + t) * m + i] = f64_to_bf16(lam * (double)A[(size_t)i * k + t]);
+    }
+  // L2' = [L2 ; bf16(scale B)] stored transposed [n][r2]; walk rows backwards so
+  // l2_out may alias l2 only if the caller wants in-place widening of a buffer
+  // that already has room (not required)
+  std::vector<uint16_t> row(r2);
+  for (int j = 0; j < n; ++j) {
+    for (int t = 0; t < rank; ++t) row[t] = l2[(size_t)j * rank + t];
+    for (int t = 0; t < k; ++t) row[rank + t] = f64_to_bf16((double)scale * (double)B[(size_t)t * n + j]);
+    std::memcpy(l2_out + (size_t)j * r2, row.data(), sizeof(uint16_t) * r2);
+  }
+  return SVDQ_OK;
+}
+
+int svdq_calibrate_act_amax(const uint16_t* x, int b, int m, float* amax, int accumulate,
+                            void* stream) {
+  clear_error();
+  REQUIRE(b >= 0 && m >= 1, SVDQ_ERR_INVALID_ARG, "need b >= 0 and m >= 1 (got b=%d m=%d)", b, m);
+  REQUIRE(m % 8 == 0, SVDQ_ERR_UNSUPPORTED, "m must be a multiple of 8 (got %d)", m);
+  REQUIRE(amax != nullptr, SVDQ_ERR_INVALID_ARG, "amax must not be NULL");
+  REQUIRE(((uintptr_t)amax & 3u) == 0, SVDQ_ERR_ALIGNMENT, "amax must be 4-byte aligned");
+  if (b > 0) {
+    REQUIRE(x != nullptr, SVDQ_ERR_INVALID_ARG, "x must not be NULL");
+    REQUIRE(aligned16(x), SVDQ_ERR_ALIGNMENT, "x must be 16-byte aligned");
+  }
+  return hip_status(launch_calibrate(x, b, m, amax, accumulate, stream), "calibrate_act_amax");
+}
+
+size_t svdq_act_workspace_size(int b, int m, int rank) {
+  if (b <= 0 || m < SVDQ_GROUP || m % SVDQ_GROUP || rank <= 0 || rank > SVDQ_MAX_RANK) return 0;
+  ActPlan p = act_plan(b, m, rank);
+  if (p.splits <= 1) return 0;
+  return round_up((size_t)p.splits * (size_t)b * (size_t)rank * 4, kAlign);
+}
+
+int svdq_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int rank, int group,
+                                   const float* smooth_inv, const uint16_t* l1, uint8_t* qx,
+                                   uint16_t* ascale, float* z, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  clear_error();
+  int st = check_group(m, group);
+  if (st) return st;
+  REQUIRE(b >= 0, SVDQ_ERR_INVALID_ARG, "b must be >= 0 (got %d)", b);
+  REQUIRE(rank >= 0 && rank <= SVDQ_MAX_RANK, SVDQ_ERR_UNSUPPORTED, "rank must be in [0, %d] (got %d)",
+          SVDQ_MAX_RANK, rank);
+  if (b == 0) return SVDQ_OK;
+  REQUIRE(x && qx && ascale, SVDQ_ERR_INVALID_ARG, "x, qx and ascale must not be NULL");
+  REQUIRE(aligned16(x) && aligned16(qx), SVDQ_ERR_ALIGNMENT, "x and qx must be 16-byte aligned");
+  REQUIRE(((uintptr_t)ascale & 1u) == 0, SVDQ_ERR_ALIGNMENT, "ascale must be 2-byte aligned");
+  if (smooth_inv) REQUIRE(aligned16(smooth_inv), SVDQ_ERR_ALIGNMENT, "smooth_inv must be 16-byte aligned");
+  if (rank > 0) {
+    REQUIRE(l1 && z, SVDQ_ERR_INVALID_ARG, "l1 and z must not be NULL when rank > 0");
+    REQUIRE(aligned16(l1), SVDQ_ERR_ALIGNMENT, "l1 must be 16-byte aligned");
+    REQUIRE(((uintptr_t)z & 3u) == 0, SVDQ_ERR_ALIGNMENT, "z must be 4-byte aligned");
+  }
+  ActPlan p = act_plan(b, m, rank);
+  const size_t need = svdq_act_workspace_size(b, m, rank);
+  if (need > 0) {
+    REQUIRE(workspace != nullptr && workspace_bytes >= need, SVDQ_ERR_WORKSPACE,
+            "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
+    REQUIRE(((uintptr_t)workspace & 15u) == 0, SVDQ_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  }
+  float* zpart = (rank > 0 && p.splits > 1) ? (float*)workspace : z;
+  st = hip_status(launch_act_quant_down(x, b, m, rank, smooth_inv, l1, qx, ascale, zpart, p, stream),
+                  "act_quant_lowrank_down");
+  if (st) return st;
+  if (rank > 0 && p.splits > 1)
+    st = hip_status(launch_z_reduce(zpart, p.splits, b, rank, z, stream), "z_reduce");
+  return st;
+}
+
+int svdq_gemm_w4a4_lowrank_up(const uint8_t* qx, const uint16_t* ascale, const float* z,
+                              const svdq_layer* layer, int b, void* y, int y_dtype, void* stream) {
+  clear_error();
+  int st = check_layer(layer);
+  if (st) return st;
+  REQUIRE(b >= 0, SVDQ_ERR_INVALID_ARG, "b must be >= 0 (got %d)", b);
+  st = check_y(y, y_dtype, b);
+  if (st) return st;
+  if (b == 0) return SVDQ_OK;
+  REQUIRE(qx && ascale, SVDQ_ERR_INVALID_ARG, "qx and ascale must not be NULL");
+  REQUIRE(aligned16(qx), SVDQ_ERR_ALIGNMENT, "qx must be 16-byte aligned");
+  REQUIRE(((uintptr_t)ascale & 1u) == 0, SVDQ_ERR_ALIGNMENT, "ascale must be 2-byte aligned");
+  if (layer->rank > 0) {
+    REQUIRE(z != nullptr, SVDQ_ERR_INVALID_ARG, "z must not be NULL when rank > 0");
+    REQUIRE(((uintptr_t)z & 3u) == 0, SVDQ_ERR_ALIGNMENT, "z must be 4-byte aligned");
+  }
+  return hip_status(launch_gemm_up(qx, ascale, z, *layer, b, y, y_dtype, stream), "gemm_w4a4_lowrank_up");
+}
+
+size_t svdq_linear_workspace_size(int b, int m, int rank, int group) {
+  if (group != SVDQ_GROUP || m < SVDQ_GROUP || m % SVDQ_GROUP || b <= 0 || rank < 0 ||
+      rank > SVDQ_MAX_RANK)
+    return 0;
+  return linear_ws_layout(b, m, rank).total;
+}
+
+int svdq_linear(const uint16_t* x, const svdq_layer* layer, int b, void* y, int y_dtype,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  int st = check_layer(layer);
+  if (st) return st;
+  REQUIRE(b >= 0, SVDQ_ERR_INVALID_ARG, "b must be >= 0 (got %d)", b);
+  st = check_y(y, y_dtype, b);
+  if (st) return st;
+  if (b == 0) return SVDQ_OK;
+  const int m = layer->m, rank = layer->rank;
+  REQUIRE(x != nullptr, SVDQ_ERR_INVALID_ARG, "x must not be NULL");
+  REQUIRE(aligned16(x), SVDQ_ERR_ALIGNMENT, "x must be 16-byte aligned");
+  if (layer->smooth_inv)
+    REQUIRE(aligned16(layer->smooth_inv), SVDQ_ERR_ALIGNMENT, "smooth_inv must be 16-byte aligned");
+  if (rank > 0) {
+    REQUIRE(layer->l1 != nullptr, SVDQ_ERR_INVALID_ARG, "layer l1 must not be NULL when rank > 0");
+    REQUIRE(aligned16(layer->l1), SVDQ_ERR_ALIGNMENT, "layer l1 must be 16-byte aligned");
+  }
+  LinearWorkspace w = linear_ws_layout(b, m, rank);
+  REQUIRE(workspace != nullptr && workspace_bytes >= w.total, SVDQ_ERR_WORKSPACE,
+          "workspace of %zu bytes needed (got %zu)", w.total, workspace ? workspace_bytes : (size_t)0);
+  REQUIRE(((uintptr_t)workspace & (kAlign - 1)) == 0, SVDQ_ERR_ALIGNMENT,
+          "workspace must be %zu-byte aligned", kAlign);
+  // exactly the standalone route: act kernel (+ ordered Z reduction when the
+  // channel groups are split), then the GEMM kernel
+  char* ws = (char*)workspace;
+  uint8_t* qx = (uint8_t*)(ws + w.qx_off);
+  uint16_t* as = (uint16_t*)(ws + w.as_off);
+  float* z = rank > 0 ? (float*)(ws + w.z_off) : nullptr;
+  ActPlan p = act_plan(b, m, rank);
+  float* zpart = (rank > 0 && p.splits > 1) ? (float*)(ws + w.zpart_off) : z;
+  st = hip_status(launch_act_quant_down(x, b, m, rank, layer->smooth_inv, layer->l1, qx, as, zpart, p,
+                                        stream),
+                  "act_quant_lowrank_down");
+  if (st) return st;
+  if (rank > 0 && p.splits > 1) {
+    st = hip_status(launch_z_reduce(zpart, p.splits, b, rank, z, stream), "z_reduce");
+    if (st) return st;
+  }
+  return hip_status(launch_gemm_up(qx, as, z, *layer, b, y, y_dtype, stream), "gemm_w4a4_lowrank_up");
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Internal declarations shared by the C-ABI layer, the host preparation code and
+// the HIP kernel launchers.  Not part of the public ABI (include/svdq.h is).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "svdq.h"
+
+namespace svdq {
+
+// ---- per-thread error message (svdq_last_error) -------------------------------
+void set_error(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+void clear_error();
+
+// ---- scalar format conversions on the host (round to nearest, ties to even) ----
+uint16_t f32_to_f16_sat(float f);   // fp16, saturated at +-65504
+float f16_to_f32(uint16_t h);
+uint16_t f64_to_bf16(double x);     // one rounding straight from fp64
+float bf16_to_f32(uint16_t b);
+
+// ---- host preparation (prep.cpp) ----------------------------------------------
+// Smoothing scales of Eq.(4); lam32 / inv32 as fp32.  act_amax may be NULL.
+void smoothing_lambda(const float* W, const float* act_amax, int m, int n, double alpha,
+                      float* lam32, float* inv32);
+// Rank-r truncated SVD of Wt (m x n, row-major fp64): L1 = U_r Sigma_r (m x r,
+// row-major), L2 = V_r^T (r x n, row-major).  Returns false if it failed.
+bool truncated_svd(const double* Wt, int m, int n, int r, double* L1, double* L2);
+// INT4 group quantization of R (fp32 [m][n]) into group-major records.
+void quantize_residual(const float* R, int m, int n, uint8_t* qw, uint16_t* wscale);
+// Number of worker threads used by the preparation loops.
+int host_threads();
+
+// ---- device launch plan --------------------------------------------------------
+// The act-quant kernel covers the rows in strips of 16 and may split the channel
+// groups of a strip over `splits` workgroups; each split writes its own partial
+// Z, summed in split order afterwards (deterministic).
+struct ActPlan {
+  int strips;            // ceil(b / 16)
+  int splits;            // workgroups per strip along the channel groups
+  int groups_per_split;  // channel groups handled by one workgroup
+};
+ActPlan act_plan(int b, int m, int rank);
+
+// ---- kernel launchers (HIP; return a hipError_t value, 0 = success) ------------
+int launch_calibrate(const uint16_t* x, int b, int m, float* amax, int accumulate, void* stream);
+int launch_act_quant_down(const uint16_t* x, int b, int m, int rank, const float* smooth_inv,
+                          const uint16_t* l1, uint8_t* qx, uint16_t* ascale, float* zpart,
+                          const ActPlan& plan, void* stream);
+int launch_z_reduce(const float* zpart, int splits, int b, int rank, float* z, void* stream);
+int launch_gemm_up(const uint8_t* qx, const uint16_t* ascale, const float* z, const svdq_layer& L,
+                   int b, void* y, int y_dtype, void* stream);
+const char* hip_error_name(int err);
+
+}  // namespace svdq

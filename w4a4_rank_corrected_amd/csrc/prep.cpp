@@ -1,0 +1,382 @@
+// Offline preparation of an SVDQuant layer on the host, in fp64.
+//
+// [Review] = "SVDQuant: How a Small High-Precision Branch Makes 4-Bit Diffusion
+// Practical" (technical review of arXiv:2411.05007v4).
+//   smoothing scales           sec. 3.1, Eq.(3)-(4)
+//   truncated SVD / residual   sec. 5, Eq.(10), Algorithm 1 steps 3-4
+//   residual INT4 quantization sec. 2.2 Eq.(1), Algorithm 1 step 5, sec. 8
+//   LoRA concatenation         sec. 7, Eq.(13)
+//
+// The SVD is our own: randomized subspace iteration (Halko, Martinsson & Tropp,
+// SIAM Review 2011, Alg. 4.4) with twice-repeated modified Gram-Schmidt, then a
+// one-sided (Hestenes) Jacobi SVD of the small projected factor.  No LAPACK.
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <functional>
+#include <thread>
+#include <vector>
+
+#include "internal.h"
+
+namespace svdq {
+
+// ---------------------------------------------------------------------------
+// threading
+// ---------------------------------------------------------------------------
+int host_threads() {
+  unsigned hc = std::thread::hardware_concurrency();
+  if (hc == 0) hc = 1;
+  return (int)std::min(hc, 64u);
+}
+
+// Runs fn(lo, hi) over [0, count) split into contiguous chunks, one per worker.
+static void parallel_for(int64_t count, const std::function<void(int64_t, int64_t)>& fn,
+                         int64_t min_chunk = 1) {
+  int nt = host_threads();
+  int64_t chunks = std::max<int64_t>(1, std::min<int64_t>(nt, count / std::max<int64_t>(1, min_chunk)));
+  if (chunks <= 1) {
+    fn(0, count);
+    return;
+  }
+  std::vector<std::thread> th;
+  th.reserve(chunks);
+  for (int64_t c = 0; c < chunks; ++c) {
+    int64_t lo = count * c / chunks, hi = count * (c + 1) / chunks;
+    th.emplace_back([&fn, lo, hi] { fn(lo, hi); });
+  }
+  for (auto& t : th) t.join();
+}
+
+// ---------------------------------------------------------------------------
+// scalar conversions (round to nearest, ties to even)
+// ---------------------------------------------------------------------------
+uint16_t f32_to_f16_sat(float f) {
+  uint32_t x;
+  std::memcpy(&x, &f, 4);
+  uint32_t sign = (x >> 16) & 0x8000u;
+  uint32_t ax = x & 0x7FFFFFFFu;
+  if (ax > 0x7F800000u) return (uint16_t)(sign | 0x7E00u);  // NaN
+  if (ax >= 0x477FF000u) return (uint16_t)(sign | 0x7BFFu);  // rounds to inf: saturate at 65504
+  if (ax >= 0x38800000u) {                                     // fp16 normal range, >= 2^-14
+    uint32_t mant = ax & 0x7FFFFFu;
+    uint32_t h = ((((ax >> 23) - 127u + 15u)) << 10) | (mant >> 13);
+    uint32_t rem = mant & 0x1FFFu;
+    if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1;  // carry may bump the exponent
+    return (uint16_t)(sign | h);
+  }
+  // fp16 subnormal (or zero): value = k * 2^-24, k = nearest-even(|f| * 2^24)
+  float af;
+  std::memcpy(&af, &ax, 4);
+  float k = std::nearbyint(af * 16777216.0f);  // exact scaling by a power of two
+  return (uint16_t)(sign | (uint32_t)k);       // k == 1024 encodes 2^-14 correctly
+}
+
+float f16_to_f32(uint16_t h) {
+  uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+  uint32_t e = (h >> 10) & 0x1Fu, mant = h & 0x3FFu;
+  float v;
+  if (e == 0) {
+    v = std::ldexp((float)mant, -24);
+  } else if (e == 31) {
+    v = mant ? NAN : INFINITY;
+  } else {
+    v = std::ldexp((float)(mant | 0x400u), (int)e - 25);
+  }
+  uint32_t bits;
+  std::memcpy(&bits, &v, 4);
+  bits |= sign;
+  std::memcpy(&v, &bits, 4);
+  return v;
+}
+
+uint16_t f64_to_bf16(double x) {
+  if (std::isnan(x)) return 0x7FC0u;
+  uint16_t sign = std::signbit(x) ? 0x8000u : 0u;
+  double a = std::fabs(x);
+  if (a == 0.0) return sign;
+  int e;
+  std::frexp(a, &e);            // a in [2^(e-1), 2^e)
+  int eb = std::max(e - 1, -126);
+  double q = std::ldexp(1.0, eb - 7);  // bf16 spacing in this binade (8 significant bits)
+  double v = std::nearbyint(a / q) * q;
+  if (v > 3.3895313892515355e38) return (uint16_t)(sign | 0x7F80u);
+  float vf = (float)v;          // exact: v is a bf16 value
+  uint32_t b;
+  std::memcpy(&b, &vf, 4);
+  return (uint16_t)(sign | (b >> 16));
+}
+
+float bf16_to_f32(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// ---------------------------------------------------------------------------
+// smoothing, Eq.(4): lambda_k = a_k^alpha / w_k^(1-alpha); 1 when a statistic is 0
+// ---------------------------------------------------------------------------
+void smoothing_lambda(const float* W, const float* act_amax, int m, int n, double alpha,
+                      float* lam32, float* inv32) {
+  parallel_for(m, [&](int64_t lo, int64_t hi) {
+    for (int64_t k = lo; k < hi; ++k) {
+      double lam = 1.0;
+      if (act_amax) {
+        double wmax = 0.0;
+        const float* row = W + k * (int64_t)n;
+        for (int j = 0; j < n; ++j) wmax = std::max(wmax, std::fabs((double)row[j]));
+        double a = act_amax[k];
+        if (a > 0.0 && wmax > 0.0) lam = std::pow(a, alpha) / std::pow(wmax, 1.0 - alpha);
+      }
+      float l32 = (float)lam;
+      lam32[k] = l32;
+      inv32[k] = (float)(1.0 / (double)l32);
+    }
+  }, 64);
+}
+
+// ---------------------------------------------------------------------------
+// dense helpers for the SVD (row-major fp64)
+// ---------------------------------------------------------------------------
+// Y (m x k) = A (m x n) * X (n x k)
+static void mat_mul_ax(const double* A, int m, int n, const double* X, int k, double* Y) {
+  const int JB = 256;
+  parallel_for(m, [&](int64_t lo, int64_t hi) {
+    const int IB = 32;
+    for (int64_t i0 = lo; i0 < hi; i0 += IB) {
+      int64_t i1 = std::min<int64_t>(hi, i0 + IB);
+      for (int64_t i = i0; i < i1; ++i) std::fill(Y + i * k, Y + (i + 1) * k, 0.0);
+      for (int j0 = 0; j0 < n; j0 += JB) {
+        int j1 = std::min(n, j0 + JB);
+        for (int64_t i = i0; i < i1; ++i) {
+          double* y = Y + i * k;
+          const double* a = A + i * (int64_t)n;
+          for (int j = j0; j < j1; ++j) {
+            double w = a[j];
+            const double* x = X + (int64_t)j * k;
+            for (int c = 0; c < k; ++c) y[c] += w * x[c];
+          }
+        }
+      }
+    }
+  }, 16);
+}
+
+// Z (n x k) = A^T (n x m) * Q (m x k), A is m x n
+static void mat_mul_atx(const double* A, int m, int n, const double* Q, int k, double* Z) {
+  parallel_for(n, [&](int64_t lo, int64_t hi) {
+    const int64_t JB = 128;
+    for (int64_t j0 = lo; j0 < hi; j0 += JB) {
+      int64_t j1 = std::min<int64_t>(hi, j0 + JB);
+      for (int64_t j = j0; j < j1; ++j) std::fill(Z + j * k, Z + (j + 1) * k, 0.0);
+      for (int i = 0; i < m; ++i) {
+        const double* a = A + (int64_t)i * n;
+        const double* q = Q + (int64_t)i * k;
+        for (int64_t j = j0; j < j1; ++j) {
+          double w = a[j];
+          double* z = Z + j * k;
+          for (int c = 0; c < k; ++c) z[c] += w * q[c];
+        }
+      }
+    }
+  }, 64);
+}
+
+// Orthonormalise the k columns of Y (rows x k, row-major) in place with
+// modified Gram-Schmidt applied twice.  If R is given, Y_in = Q R with R upper
+// triangular (k x k, row-major).
+static void orthonormalize(double* Y, int64_t rows, int k, double* R) {
+  std::vector<double> col(rows), qi(rows);
+  if (R) std::fill(R, R + (int64_t)k * k, 0.0);
+  for (int j = 0; j < k; ++j) {
+    for (int64_t r = 0; r < rows; ++r) col[r] = Y[r * k + j];
+    double norm0 = 0.0;
+    for (int64_t r = 0; r < rows; ++r) norm0 += col[r] * col[r];
+    norm0 = std::sqrt(norm0);
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int i = 0; i < j; ++i) {
+        double c = 0.0;
+        for (int64_t r = 0; r < rows; ++r) c += Y[r * k + i] * col[r];
+        for (int64_t r = 0; r < rows; ++r) col[r] -= c * Y[r * k + i];
+        if (R) R[(int64_t)i * k + j] += c;
+      }
+    }
+    double norm = 0.0;
+    for (int64_t r = 0; r < rows; ++r) norm += col[r] * col[r];
+    norm = std::sqrt(norm);
+    if (!(norm > 1e-13 * norm0) || norm == 0.0) {
+      // numerically dependent column: replace by a unit vector orthogonal to the
+      // previous ones (keeps the basis orthonormal; R gets a zero diagonal)
+      for (int64_t start = 0; start < rows; ++start) {
+        std::fill(col.begin(), col.end(), 0.0);
+        col[(start + j) % rows] = 1.0;
+        for (int pass = 0; pass < 2; ++pass)
+          for (int i = 0; i < j; ++i) {
+            double c = 0.0;
+            for (int64_t r = 0; r < rows; ++r) c += Y[r * k + i] * col[r];
+            for (int64_t r = 0; r < rows; ++r) col[r] -= c * Y[r * k + i];
+          }
+        norm = 0.0;
+        for (int64_t r = 0; r < rows; ++r) norm += col[r] * col[r];
+        norm = std::sqrt(norm);
+        if (norm > 0.5) break;
+      }
+      if (R) R[(int64_t)j * k + j] = 0.0;
+    } else if (R) {
+      R[(int64_t)j * k + j] = norm;
+    }
+    for (int64_t r = 0; r < rows; ++r) Y[r * k + j] = col[r] / norm;
+  }
+}
+
+// One-sided Jacobi SVD of a square k x k matrix A (row-major, overwritten):
+// A V = U Sigma.  On return A holds U Sigma column-wise, V the rotations.
+static bool jacobi_svd(double* A, int k, double* V) {
+  for (int i = 0; i < k; ++i)
+    for (int j = 0; j < k; ++j) V[(int64_t)i * k + j] = (i == j) ? 1.0 : 0.0;
+  const double eps = 1e-15;
+  for (int sweep = 0; sweep < 80; ++sweep) {
+    bool rotated = false;
+    for (int p = 0; p < k - 1; ++p) {
+      for (int q = p + 1; q < k; ++q) {
+        double alpha = 0, beta = 0, gamma = 0;
+        for (int r = 0; r < k; ++r) {
+          double ap = A[(int64_t)r * k + p], aq = A[(int64_t)r * k + q];
+          alpha += ap * ap;
+          beta += aq * aq;
+          gamma += ap * aq;
+        }
+        if (gamma == 0.0 || std::fabs(gamma) <= eps * std::sqrt(alpha * beta)) continue;
+        rotated = true;
+        double zeta = (beta - alpha) / (2.0 * gamma);
+        double t = (zeta >= 0 ? 1.0 : -1.0) / (std::fabs(zeta) + std::sqrt(1.0 + zeta * zeta));
+        double c = 1.0 / std::sqrt(1.0 + t * t), s = c * t;
+        for (int r = 0; r < k; ++r) {
+          double ap = A[(int64_t)r * k + p], aq = A[(int64_t)r * k + q];
+          A[(int64_t)r * k + p] = c * ap - s * aq;
+          A[(int64_t)r * k + q] = s * ap + c * aq;
+          double vp = V[(int64_t)r * k + p], vq = V[(int64_t)r * k + q];
+          V[(int64_t)r * k + p] = c * vp - s * vq;
+          V[(int64_t)r * k + q] = s * vp + c * vq;
+        }
+      }
+    }
+    if (!rotated) return true;
+  }
+  return false;
+}
+
+static uint64_t splitmix64(uint64_t& s) {
+  uint64_t z = (s += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+bool truncated_svd(const double* Wt, int m, int n, int r, double* L1, double* L2) {
+  if (r == 0) return true;
+  const int mn = std::min(m, n);
+  // Oversampled width and power iterations sized for flat (Marchenko-Pastur)
+  // spectra, where sigma_r and sigma_{r+1} nearly coincide: the rank-r tail
+  // energy comes within ~1e-5 of the optimum on such matrices.
+  const int k = std::min(mn, r + std::max(32, r));
+  const int power_iters = 8;
+
+  // Gaussian test matrix Omega (n x k), Box-Muller on a fixed-seed splitmix64 stream
+  std::vector<double> omega((int64_t)n * k);
+  uint64_t state = 0x5EED5EEDull;
+  for (int64_t i = 0; i < (int64_t)n * k; i += 2) {
+    double u1 = ((splitmix64(state) >> 11) + 1) * (1.0 / 9007199254740993.0);
+    double u2 = (splitmix64(state) >> 11) * (1.0 / 9007199254740992.0);
+    double rad = std::sqrt(-2.0 * std::log(u1));
+    omega[i] = rad * std::cos(2.0 * M_PI * u2);
+    if (i + 1 < (int64_t)n * k) omega[i + 1] = rad * std::sin(2.0 * M_PI * u2);
+  }
+  std::vector<double> Y((int64_t)m * k), Zn((int64_t)n * k);
+  mat_mul_ax(Wt, m, n, omega.data(), k, Y.data());
+  orthonormalize(Y.data(), m, k, nullptr);
+  for (int it = 0; it < power_iters; ++it) {
+    mat_mul_atx(Wt, m, n, Y.data(), k, Zn.data());
+    orthonormalize(Zn.data(), n, k, nullptr);
+    mat_mul_ax(Wt, m, n, Zn.data(), k, Y.data());
+    orthonormalize(Y.data(), m, k, nullptr);
+  }
+  // B^T = W^T Q (n x k) = Q2 R2;  R2 = U_R Sigma V_R^T  =>  W ~ (Q V_R) Sigma (Q2 U_R)^T
+  mat_mul_atx(Wt, m, n, Y.data(), k, Zn.data());
+  std::vector<double> R2((int64_t)k * k), VR((int64_t)k * k);
+  orthonormalize(Zn.data(), n, k, R2.data());
+  if (!jacobi_svd(R2.data(), k, VR.data())) return false;
+  std::vector<double> sig(k);
+  for (int c = 0; c < k; ++c) {
+    double s = 0;
+    for (int rr = 0; rr < k; ++rr) s += R2[(int64_t)rr * k + c] * R2[(int64_t)rr * k + c];
+    sig[c] = std::sqrt(s);
+  }
+  std::vector<int> order(k);
+  for (int c = 0; c < k; ++c) order[c] = c;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return sig[a] > sig[b]; });
+
+  for (int t = 0; t < r; ++t) {
+    int c = order[t];
+    double s = sig[c];
+    // left vector u = Q * VR[:, c]; right vector v = Q2 * (R2[:, c] / s)
+    std::vector<double> u(m), v(n);
+    for (int i = 0; i < m; ++i) {
+      double acc = 0;
+      for (int j = 0; j < k; ++j) acc += Y[(int64_t)i * k + j] * VR[(int64_t)j * k + c];
+      u[i] = acc;
+    }
+    for (int j = 0; j < n; ++j) {
+      double acc = 0;
+      if (s > 0)
+        for (int q = 0; q < k; ++q) acc += Zn[(int64_t)j * k + q] * (R2[(int64_t)q * k + c] / s);
+      v[j] = acc;
+    }
+    // sign convention: the largest-magnitude entry of u is positive
+    int imax = 0;
+    for (int i = 1; i < m; ++i)
+      if (std::fabs(u[i]) > std::fabs(u[imax])) imax = i;
+    double sgn = u[imax] < 0 ? -1.0 : 1.0;
+    for (int i = 0; i < m; ++i) L1[(int64_t)i * r + t] = sgn * u[i] * s;
+    for (int j = 0; j < n; ++j) L2[(int64_t)t * n + j] = sgn * v[j];
+  }
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// residual INT4 quantization: per output column j, per 64-row group g,
+// s = fp16(fl32(amax / 7)), q = clamp(rint(fl32(v / s)), -7, 7), q = 0 if s == 0
+// ---------------------------------------------------------------------------
+void quantize_residual(const float* R, int m, int n, uint8_t* qw, uint16_t* wscale) {
+  const int G = m / SVDQ_GROUP;
+  parallel_for((int64_t)G * n, [&](int64_t lo, int64_t hi) {
+    for (int64_t idx = lo; idx < hi; ++idx) {
+      int g = (int)(idx / n), j = (int)(idx % n);
+      float amax = 0.0f;
+      for (int kk = 0; kk < SVDQ_GROUP; ++kk)
+        amax = std::max(amax, std::fabs(R[(int64_t)(g * SVDQ_GROUP + kk) * n + j]));
+      uint16_t s16 = f32_to_f16_sat(amax / 7.0f);
+      float s = f16_to_f32(s16);
+      wscale[(int64_t)g * n + j] = s16;
+      uint8_t* rec = qw + ((int64_t)g * n + j) * 32;
+      for (int t = 0; t < 32; ++t) {
+        int q2[2];
+        for (int h = 0; h < 2; ++h) {
+          float v = R[(int64_t)(g * SVDQ_GROUP + 2 * t + h) * n + j];
+          float q = 0.0f;
+          if (s > 0.0f) {
+            float quot = v / s;
+            q = std::nearbyint(quot);
+            q = std::min(7.0f, std::max(-7.0f, q));
+          }
+          q2[h] = (int)q;
+        }
+        rec[t] = (uint8_t)((q2[0] & 0xF) | ((q2[1] & 0xF) << 4));
+      }
+    }
+  }, 256);
+}
+
+}  // namespace svdq
