@@ -29,8 +29,11 @@ HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math
               "-Wall", "-Wextra", "-Wno-unused-parameter", f"-I{INCLUDE}", f"-I{CSRC}"]
 # -packed-fp32-ops: no v_pk_*_f32 in any kernel (the host pass warns that it does
 # not know the feature; that is harmless).
+# -amdgpu-mfma-vgpr-form: MFMA results land in arch VGPRs, where the fp32 scale
+# epilogue reads them without v_accvgpr_read copies.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-Wno-unused-parameter", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

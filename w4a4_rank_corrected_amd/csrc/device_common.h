@@ -35,6 +35,13 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builti
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Raw buffer resource over [base, base + bytes): loads whose offset falls
+// outside read 0 without touching memory (the hardware range check), so edge
+// tiles need no clamping or masking.  Word 3 is the gfx9 raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // Wave-wide max over the four lanes l, l^16, l^32, l^48 (one row of an MFMA
 // operand): ds_swizzle for the xor-16 partner, permlane32_swap for xor-32.
 __device__ __forceinline__ float max4_rows(float v) {
