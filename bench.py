@@ -126,6 +126,7 @@ def main():
     wsz = S.svdq_act_workspace_size(b, m, r)
     ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=dev)
     y = torch.empty((b, n), dtype=out_dtype, device=dev)
+    gws = torch.empty(max(S.svdq_gemm_workspace_size(b, n, m), 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
@@ -135,7 +136,7 @@ def main():
                                          workspace=ws, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        S.svdq_gemm_w4a4_lowrank_up(qx, asc, z, layer, b, out_dtype, y=y, stream=stream)
+        S.svdq_gemm_w4a4_lowrank_up(qx, asc, z, layer, b, out_dtype, y=y, workspace=gws, stream=stream)
         if ev is not None:
             ev[2].record(stream)
 
@@ -155,7 +156,7 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
 
     # the same work through the one-call entry point, for reference
-    ws_lin = torch.empty(max(S.svdq_linear_workspace_size(b, m, r), 1), dtype=torch.uint8, device=dev)
+    ws_lin = torch.empty(max(S.svdq_linear_workspace_size(b, m, n, r), 1), dtype=torch.uint8, device=dev)
     for _ in range(3):
         S.svdq_linear(x, layer, out_dtype, y=y, workspace=ws_lin, stream=stream)
     torch.cuda.synchronize()

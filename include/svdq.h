@@ -164,6 +164,11 @@ int svdq_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int rank, in
                                    uint16_t* ascale, float* z, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace svdq_gemm_w4a4_lowrank_up may need for an output
+ * of b x n with m input channels: fp32 partial tiles and publication flags of
+ * its stream-K schedule (an upper bound valid on every gfx950 device). */
+size_t svdq_gemm_workspace_size(int b, int n, int m);
+
 /* DEVICE: fused W4A4 GEMM + low-rank up-projection ([Review] sec. 6.1
  * Algorithm 2 steps 4-8; Eq.(7)):
  *     isum[i,j,g] = sum_{k in g} qx[i,k] qw[k,j]          (exact integer)
@@ -171,18 +176,26 @@ int svdq_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int rank, in
  *   qx, ascale, z as produced by svdq_quantize_act_lowrank_down (z NULL iff
  *   layer->rank == 0; z any 4-byte alignment); y [b][n] in y_dtype
  *   (SVDQ_OUT_BF16, round-to-nearest-even, or SVDQ_OUT_F32); y needs only
- *   element alignment.  layer->smooth_inv and layer->l1 are not used. */
+ *   element alignment.  layer->smooth_inv and layer->l1 are not used.
+ *   workspace: device, 16-byte aligned, >= svdq_gemm_workspace_size(b, n, m)
+ *   bytes.  Its contents need no initialisation, and calls that overlap in time
+ *   must not share it.  Per-group sums are accumulated in a fixed order that
+ *   depends only on the shape and the device's CU count, so results are
+ *   deterministic. */
 int svdq_gemm_w4a4_lowrank_up(const uint8_t* qx, const uint16_t* ascale, const float* z,
-                              const svdq_layer* layer, int b, void* y, int y_dtype,
-                              void* stream);
+                              const svdq_layer* layer, int b, void* y, int y_dtype, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace svdq_linear needs (qx, ascale and Z partials). */
-size_t svdq_linear_workspace_size(int b, int m, int rank, int group);
+/* Bytes of device workspace svdq_linear needs (qx, ascale, Z and its split
+ * partial sums, and the GEMM's workspace). */
+size_t svdq_linear_workspace_size(int b, int m, int n, int rank, int group);
 
 /* DEVICE: the whole layer = the two fused kernels back to back on `stream`
  * ([Review] sec. 6.1 Algorithm 2 steps 1-8).  x bf16 [b][m]; y [b][n] in
- * y_dtype; workspace >= svdq_linear_workspace_size(b, m, rank, group) bytes,
- * 256-byte aligned.  Z is bit-identical to the standalone kernels' Z. */
+ * y_dtype; workspace >= svdq_linear_workspace_size(b, m, n, rank, group)
+ * bytes, 256-byte aligned, not shared by calls that overlap in time.  Runs
+ * exactly the kernels of the two entry points above, so its output is
+ * bit-identical to theirs. */
 int svdq_linear(const uint16_t* x, const svdq_layer* layer, int b, void* y, int y_dtype,
                 void* workspace, size_t workspace_bytes, void* stream);
 

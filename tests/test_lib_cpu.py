@@ -187,7 +187,7 @@ def test_linear_validation_errors(kw, code):
 def test_linear_workspace_and_dtype_errors():
     L = _lib_or_skip()
     lay = _layer()
-    need = L.svdq_linear_workspace_size(16, 128, 8, 64)
+    need = L.svdq_linear_workspace_size(16, 128, 64, 8, 64)
     assert need > 0
     assert L.svdq_linear(FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE, need - 1, None) == B.SVDQ_ERR_WORKSPACE
     assert L.svdq_linear(FAKE, ctypes.byref(lay), 16, FAKE, 0, None, need, None) == B.SVDQ_ERR_WORKSPACE
@@ -217,10 +217,16 @@ def test_act_and_gemm_validation_errors():
     assert f(FAKE, 64, 4096, 32, 64, None, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.SVDQ_ERR_WORKSPACE
     g = L.svdq_gemm_w4a4_lowrank_up
     lay = _layer()
-    assert g(FAKE, FAKE, None, ctypes.byref(lay), 16, FAKE, 0, None) == B.SVDQ_ERR_INVALID_ARG
-    assert g(None, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, None) == B.SVDQ_ERR_INVALID_ARG
-    assert g(FAKE + 1, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, None) == B.SVDQ_ERR_ALIGNMENT
-    assert g(FAKE, FAKE, FAKE, ctypes.byref(lay), 16, FAKE + 2, 1, None) == B.SVDQ_ERR_ALIGNMENT
+    W = 1 << 30
+    assert g(FAKE, FAKE, None, ctypes.byref(lay), 16, FAKE, 0, FAKE, W, None) == B.SVDQ_ERR_INVALID_ARG
+    assert g(None, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE, W, None) == B.SVDQ_ERR_INVALID_ARG
+    assert g(FAKE + 1, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE, W, None) == B.SVDQ_ERR_ALIGNMENT
+    assert g(FAKE, FAKE, FAKE, ctypes.byref(lay), 16, FAKE + 2, 1, FAKE, W, None) == B.SVDQ_ERR_ALIGNMENT
+    gneed = L.svdq_gemm_workspace_size(16, 64, 128)
+    assert gneed > 0
+    assert g(FAKE, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE, gneed - 1, None) == B.SVDQ_ERR_WORKSPACE
+    assert g(FAKE, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, None, gneed, None) == B.SVDQ_ERR_WORKSPACE
+    assert g(FAKE, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE + 8, gneed, None) == B.SVDQ_ERR_ALIGNMENT
     c = L.svdq_calibrate_act_amax
     assert c(FAKE, 16, 100, FAKE, 0, None) == B.SVDQ_ERR_UNSUPPORTED
     assert c(FAKE, 16, 128, None, 0, None) == B.SVDQ_ERR_INVALID_ARG
@@ -254,9 +260,11 @@ def test_prepare_validation_errors():
 
 def test_workspace_sizes_cover_layout():
     L = _lib_or_skip()
-    for (b, m, r) in [(1, 64, 0), (37, 256, 16), (4608, 3072, 32), (256, 15360, 48)]:
-        w = L.svdq_linear_workspace_size(b, m, r, 64)
+    for (b, m, n, r) in [(1, 64, 8, 0), (37, 256, 200, 16), (4608, 3072, 9216, 32), (256, 15360, 3072, 48)]:
+        w = L.svdq_linear_workspace_size(b, m, n, r, 64)
         G = m // 64
-        assert w >= G * b * 32 + G * b * 2 + b * r * 4
-        assert w % 256 == 0
-    assert L.svdq_linear_workspace_size(16, 100, 8, 64) == 0
+        gw = L.svdq_gemm_workspace_size(b, n, m)
+        assert w >= G * b * 32 + G * b * 2 + b * r * 4 + gw
+        assert w % 256 == 0 and gw % 256 == 0
+    assert L.svdq_linear_workspace_size(16, 100, 8, 8, 64) == 0
+    assert L.svdq_gemm_workspace_size(16, 8, 100) == 0

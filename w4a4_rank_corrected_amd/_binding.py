@@ -51,9 +51,10 @@ SIGNATURES = [
     ("svdq_act_workspace_size", _size, [_c_int, _c_int, _c_int]),
     ("svdq_quantize_act_lowrank_down", _c_int,
      [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _size, _vp]),
+    ("svdq_gemm_workspace_size", _size, [_c_int, _c_int, _c_int]),
     ("svdq_gemm_w4a4_lowrank_up", _c_int,
-     [_vp, _vp, _vp, ctypes.POINTER(svdq_layer), _c_int, _vp, _c_int, _vp]),
-    ("svdq_linear_workspace_size", _size, [_c_int, _c_int, _c_int, _c_int]),
+     [_vp, _vp, _vp, ctypes.POINTER(svdq_layer), _c_int, _vp, _c_int, _vp, _size, _vp]),
+    ("svdq_linear_workspace_size", _size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     ("svdq_linear", _c_int,
      [_vp, ctypes.POINTER(svdq_layer), _c_int, _vp, _c_int, _vp, _size, _vp]),
     ("svdq_status_string", ctypes.c_char_p, [_c_int]),
@@ -243,8 +244,12 @@ class DeviceLayer:
         return self
 
 
+def svdq_gemm_workspace_size(b: int, n: int, m: int) -> int:
+    return int(lib().svdq_gemm_workspace_size(b, n, m))
+
+
 def svdq_gemm_w4a4_lowrank_up(qx, ascale, z, layer: DeviceLayer, b: Optional[int] = None,
-                              out_dtype=None, y=None, stream=None):
+                              out_dtype=None, y=None, workspace=None, stream=None):
     import torch
     if b is None:
         b = qx.shape[1]
@@ -252,13 +257,17 @@ def svdq_gemm_w4a4_lowrank_up(qx, ascale, z, layer: DeviceLayer, b: Optional[int
     code = SVDQ_OUT_BF16 if out_dtype == torch.bfloat16 else SVDQ_OUT_F32
     if y is None:
         y = torch.empty((b, layer.n), dtype=out_dtype, device=qx.device)
+    if workspace is None:
+        need = svdq_gemm_workspace_size(b, layer.n, layer.m)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=qx.device)
+    wsb = workspace.numel() * workspace.element_size()
     _check(lib().svdq_gemm_w4a4_lowrank_up(_ptr(qx), _ptr(ascale), _ptr(z), ctypes.byref(layer.struct),
-                                           b, _ptr(y), code, _stream(stream)))
+                                           b, _ptr(y), code, _ptr(workspace), wsb, _stream(stream)))
     return y
 
 
-def svdq_linear_workspace_size(b: int, m: int, rank: int, group: int = SVDQ_GROUP) -> int:
-    return int(lib().svdq_linear_workspace_size(b, m, rank, group))
+def svdq_linear_workspace_size(b: int, m: int, n: int, rank: int, group: int = SVDQ_GROUP) -> int:
+    return int(lib().svdq_linear_workspace_size(b, m, n, rank, group))
 
 
 def svdq_linear(x, layer: DeviceLayer, out_dtype=None, y=None, workspace=None, stream=None):
@@ -269,7 +278,7 @@ def svdq_linear(x, layer: DeviceLayer, out_dtype=None, y=None, workspace=None, s
     if y is None:
         y = torch.empty((b, layer.n), dtype=out_dtype, device=x.device)
     if workspace is None:
-        need = svdq_linear_workspace_size(b, m, layer.rank)
+        need = svdq_linear_workspace_size(b, m, layer.n, layer.rank)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     wsb = workspace.numel() * workspace.element_size()
     _check(lib().svdq_linear(_ptr(x), ctypes.byref(layer.struct), b, _ptr(y), code, _ptr(workspace),

@@ -75,10 +75,15 @@ int hip_status(int err, const char* what) {
 }
 
 struct LinearWorkspace {
-  size_t qx_off, as_off, z_off, zpart_off, total;
+  size_t qx_off, as_off, z_off, zpart_off, gemm_off, total;
 };
 
-LinearWorkspace linear_ws_layout(int b, int m, int rank) {
+// device-independent upper bound of the GEMM kernel's workspace
+size_t gemm_ws_bytes(int b, int n, int m) {
+  return b > 0 ? round_up(gemm_plan(b, n, m, 0).ws_bytes, kAlign) : 0;
+}
+
+LinearWorkspace linear_ws_layout(int b, int m, int n, int rank) {
   LinearWorkspace w;
   const size_t G = (size_t)(m / SVDQ_GROUP);
   ActPlan p = act_plan(b, m, rank);
@@ -87,7 +92,8 @@ LinearWorkspace linear_ws_layout(int b, int m, int rank) {
   w.z_off = round_up(w.as_off + G * (size_t)b * 2, kAlign);
   w.zpart_off = round_up(w.z_off + (size_t)b * (size_t)rank * 4, kAlign);
   const size_t zpart = (rank > 0 && p.splits > 1) ? (size_t)p.splits * (size_t)b * (size_t)rank * 4 : 0;
-  w.total = round_up(w.zpart_off + zpart, kAlign);
+  w.gemm_off = round_up(w.zpart_off + zpart, kAlign);
+  w.total = round_up(w.gemm_off + gemm_ws_bytes(b, n, m), kAlign);
   if (b == 0) w.total = 0;
   return w;
 }
@@ -323,8 +329,14 @@ int svdq_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int rank, in
   return st;
 }
 
+size_t svdq_gemm_workspace_size(int b, int n, int m) {
+  if (b <= 0 || n <= 0 || m < SVDQ_GROUP || m % SVDQ_GROUP) return 0;
+  return gemm_ws_bytes(b, n, m);
+}
+
 int svdq_gemm_w4a4_lowrank_up(const uint8_t* qx, const uint16_t* ascale, const float* z,
-                              const svdq_layer* layer, int b, void* y, int y_dtype, void* stream) {
+                              const svdq_layer* layer, int b, void* y, int y_dtype, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   clear_error();
   int st = check_layer(layer);
   if (st) return st;
@@ -339,14 +351,21 @@ int svdq_gemm_w4a4_lowrank_up(const uint8_t* qx, const uint16_t* ascale, const f
     REQUIRE(z != nullptr, SVDQ_ERR_INVALID_ARG, "z must not be NULL when rank > 0");
     REQUIRE(((uintptr_t)z & 3u) == 0, SVDQ_ERR_ALIGNMENT, "z must be 4-byte aligned");
   }
-  return hip_status(launch_gemm_up(qx, ascale, z, *layer, b, y, y_dtype, stream), "gemm_w4a4_lowrank_up");
+  const size_t need = gemm_ws_bytes(b, layer->n, layer->m);
+  if (need > 0) {
+    REQUIRE(workspace != nullptr && workspace_bytes >= need, SVDQ_ERR_WORKSPACE,
+            "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
+    REQUIRE(((uintptr_t)workspace & 15u) == 0, SVDQ_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  }
+  return hip_status(launch_gemm_up(qx, ascale, z, *layer, b, y, y_dtype, workspace, stream),
+                    "gemm_w4a4_lowrank_up");
 }
 
-size_t svdq_linear_workspace_size(int b, int m, int rank, int group) {
-  if (group != SVDQ_GROUP || m < SVDQ_GROUP || m % SVDQ_GROUP || b <= 0 || rank < 0 ||
+size_t svdq_linear_workspace_size(int b, int m, int n, int rank, int group) {
+  if (group != SVDQ_GROUP || m < SVDQ_GROUP || m % SVDQ_GROUP || b <= 0 || n <= 0 || rank < 0 ||
       rank > SVDQ_MAX_RANK)
     return 0;
-  return linear_ws_layout(b, m, rank).total;
+  return linear_ws_layout(b, m, n, rank).total;
 }
 
 int svdq_linear(const uint16_t* x, const svdq_layer* layer, int b, void* y, int y_dtype,
@@ -367,7 +386,7 @@ int svdq_linear(const uint16_t* x, const svdq_layer* layer, int b, void* y, int 
     REQUIRE(layer->l1 != nullptr, SVDQ_ERR_INVALID_ARG, "layer l1 must not be NULL when rank > 0");
     REQUIRE(aligned16(layer->l1), SVDQ_ERR_ALIGNMENT, "layer l1 must be 16-byte aligned");
   }
-  LinearWorkspace w = linear_ws_layout(b, m, rank);
+  LinearWorkspace w = linear_ws_layout(b, m, layer->n, rank);
   REQUIRE(workspace != nullptr && workspace_bytes >= w.total, SVDQ_ERR_WORKSPACE,
           "workspace of %zu bytes needed (got %zu)", w.total, workspace ? workspace_bytes : (size_t)0);
   REQUIRE(((uintptr_t)workspace & (kAlign - 1)) == 0, SVDQ_ERR_ALIGNMENT,
@@ -388,7 +407,8 @@ int svdq_linear(const uint16_t* x, const svdq_layer* layer, int b, void* y, int 
     st = hip_status(launch_z_reduce(zpart, p.splits, b, rank, z, stream), "z_reduce");
     if (st) return st;
   }
-  return hip_status(launch_gemm_up(qx, as, z, *layer, b, y, y_dtype, stream), "gemm_w4a4_lowrank_up");
+  return hip_status(launch_gemm_up(qx, as, z, *layer, b, y, y_dtype, ws + w.gemm_off, stream),
+                    "gemm_w4a4_lowrank_up");
 }
 
 }  // extern "C"

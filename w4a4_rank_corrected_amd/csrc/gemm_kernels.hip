@@ -27,13 +27,31 @@
 //
 // Work decomposition (gfx950: 256 CUs in 8 XCDs, 4 SIMDs per CU, wave64),
 // parameterised by GemmCfg:
-//   a workgroup computes a TM x TN tile of Y (rows x columns) with
+//   a workgroup computes TM x TN tiles of Y (rows x columns) with
 //   (TM/WM) x (TN/WN) waves, each owning a WM x WN sub-tile of 16x16 MFMA
-//   blocks.  Per stage of KG channel groups it loads the packed activation and
-//   weight records (contiguous in the group-major layout) with buffer loads,
-//   unpacks them once into LDS (double-buffered), and every wave reads its MFMA
-//   operands from there.  Global loads run two stages ahead in registers.
+//   blocks.  Per 64-channel group it loads the packed activation and weight
+//   records (contiguous in the group-major layout) with buffer loads, unpacks
+//   them once into LDS (double-buffered), and every wave reads its MFMA
+//   operands from there.  Global loads run DEPTH groups ahead in registers.
+//
+// Schedules (tile = TM x TN outputs over all G groups; slots = two resident
+// workgroups per CU):
+//   * one tile per workgroup, when the tiles fill whole rounds of slots;
+//   * otherwise a hybrid: the tiles of the last one or two rounds are shared
+//     out by stream-K among `slots` persistent workgroups (equal (tile, group)
+//     iteration ranges), which are dispatched first; the remaining full rounds
+//     run one tile per workgroup after them.  A stream-K workgroup walks its
+//     range in descending order, so a tile's earlier groups are finished first
+//     (as the first work item of a lower-numbered, earlier-dispatched
+//     workgroup), stored as an fp32 partial and published with a flag.  The
+//     workgroup holding the tile's last groups adds the low-rank branch, waits
+//     for all of the tile's flags (bounded spin), adds the partials in a fixed
+//     order and stores Y.  Results are deterministic for a shape and CU count.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <chrono>
 
 #include "device_common.h"
 #include "internal.h"
@@ -44,24 +62,6 @@ namespace svdq {
 namespace {
 
 using namespace dev;
-
-template <int TM_, int TN_, int WM_, int WN_, int KG_, int WPE_>
-struct GemmCfg {
-  static constexpr int TM = TM_, TN = TN_;  // workgroup tile: rows (tokens) x output columns
-  static constexpr int WM = WM_, WN = WN_;  // wave tile
-  static constexpr int KG = KG_;            // channel groups per LDS stage
-  static constexpr int WPE = WPE_;          // waves per SIMD the register budget must allow
-  static constexpr int WAVES_N = TN / WN;
-  static constexpr int NT = 64 * (TM / WM) * WAVES_N;
-  static constexpr int BI = WM / 16, BJ = WN / 16;
-  static constexpr int A_BYTES = TM * 32 / NT;  // packed activation bytes staged per thread per group
-  static constexpr int B_BYTES = TN * 32 / NT;  // packed weight bytes staged per thread per group
-  static constexpr int ROWB = 64 + 16;          // LDS bytes per unpacked 64-channel row (+16 pad)
-  static constexpr int STAGE_A = KG * TM * ROWB, STAGE_B = KG * TN * ROWB;
-  static_assert(A_BYTES == 4 || A_BYTES == 8 || A_BYTES == 16, "activation staging piece");
-  static_assert(B_BYTES == 4 || B_BYTES == 8 || B_BYTES == 16, "weight staging piece");
-  static_assert(NT >= TM + TN && TM % 64 == 0 && (TM + TN) % 64 == 0, "scale staging");
-};
 
 template <int BYTES>
 struct Piece;  // packed code piece: BYTES/4 words of one 32-byte record
@@ -120,15 +120,10 @@ __device__ __forceinline__ void unpack_piece(uint8_t* row, int w0, const Piece<B
   }
 }
 
-// Workgroup -> tile.  Workgroups are dealt round-robin to the 8 XCDs, so give
-// each XCD a contiguous range of tiles, ordered in bands of 4 tile-rows
-// (column-major inside a band) so that concurrently running workgroups of one
-// XCD share activation and weight tiles in its L2.
-__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& ti, int& tj) {
-  const int T = tiles_m * tiles_n;
-  const int xcd = bid & 7, k = bid >> 3;
-  const int per = T >> 3, extra = T & 7;
-  const int t = xcd < extra ? xcd * (per + 1) + k : extra * (per + 1) + (xcd - extra) * per + k;
+// Linear tile index -> (tile row, tile column), in bands of 4 tile-rows
+// (column-major inside a band), so that tiles with nearby indices share
+// activation and weight records.
+__device__ __forceinline__ void band_tile(int t, int tiles_m, int tiles_n, int& ti, int& tj) {
   constexpr int GM = 4;
   const int band = t / (GM * tiles_n);
   const int first = band * GM;
@@ -138,116 +133,155 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   tj = in_band / gm;
 }
 
+// Workgroup d of `count` one-tile workgroups -> linear tile base + t.
+// Workgroups are dealt round-robin to the 8 XCDs, so each XCD gets a contiguous
+// range of linear tiles, whose workgroups then share records in its L2.
+__device__ __forceinline__ int dp_tile(int d, int count, int base) {
+  const int xcd = d & 7, k = d >> 3;
+  const int per = count >> 3, extra = count & 7;
+  return base + (xcd < extra ? xcd * (per + 1) + k : extra * (per + 1) + (xcd - extra) * per + k);
+}
+
+template <int TM_, int TN_, int WM_, int WN_, int WPE_, int DEPTH_>
+struct GemmCfg {
+  static constexpr int TM = TM_, TN = TN_;  // workgroup tile: rows (tokens) x output columns
+  static constexpr int WM = WM_, WN = WN_;  // wave tile
+  static constexpr int WPE = WPE_;          // waves per SIMD the register budget must allow
+  static constexpr int DEPTH = DEPTH_;      // groups of global loads in flight (even)
+  static constexpr int WAVES_N = TN / WN;
+  static constexpr int NT = 64 * (TM / WM) * WAVES_N;
+  static constexpr int BI = WM / 16, BJ = WN / 16;
+  static constexpr int A_BYTES = TM * 32 / NT;  // packed activation bytes staged per thread per group
+  static constexpr int B_BYTES = TN * 32 / NT;  // packed weight bytes staged per thread per group
+  static constexpr int ROWB = 64 + 16;          // LDS bytes per unpacked 64-channel row (+16 pad)
+  static_assert(DEPTH % 2 == 0, "the register ring alternates with the two LDS buffers");
+  static_assert(A_BYTES == 4 || A_BYTES == 8 || A_BYTES == 16, "activation staging piece");
+  static_assert(B_BYTES == 4 || B_BYTES == 8 || B_BYTES == 16, "weight staging piece");
+  static_assert(NT >= TM + TN && TM % 64 == 0 && (TM + TN) % 64 == 0, "scale staging");
+};
+
+// 128 x 128 tile, 4 waves of 64 x 64; two workgroups share a CU, so one
+// workgroup's barrier and LDS-latency phases overlap the other's compute.
+using Cfg = GemmCfg<128, 128, 64, 64, 2, 2>;
+
+// Cache policy of the stream-K partials: sc1 = device-coherent.
+constexpr int kCoherent = 16;
+// s_waitcnt immediate that waits for vmcnt 0 only (expcnt 7, lgkmcnt 15).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+struct StreamK {
+  int P;                          // stream-K workgroups: blockIdx < P (0 = none)
+  int T;                          // stream-K tiles: linear tiles [0, T)
+  long long U;                    // their (tile, group) iterations: T * G
+  float* partials;                // [P][TM*TN] fp32, in accumulator order
+  unsigned long long* flags;      // [P] publication epochs
+  unsigned long long epoch;       // this launch's epoch
+};
+
 template <class C, bool OUT_BF16>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void gemm_w4a4_up_kernel(
     const uint8_t* __restrict__ qx, const uint16_t* __restrict__ ascale,
     const float* __restrict__ z, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, int b, int n, int G, int rank, int tiles_m, int tiles_n,
-    void* __restrict__ yout) {
-  constexpr int TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN, KG = C::KG;
+    void* __restrict__ yout, StreamK sk) {
+  constexpr int TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN, NT = C::NT;
   constexpr int BI = C::BI, BJ = C::BJ, ROWB = C::ROWB;
-  __shared__ __align__(16) uint8_t As[2][C::STAGE_A];
-  __shared__ __align__(16) uint8_t Bs[2][C::STAGE_B];
-  __shared__ __align__(16) float Sxq[2][KG][TM];  // sx / 256
-  __shared__ __align__(16) float Sng[2][KG][TM];  // -1.5*2^23 * sx / 256
-  __shared__ __align__(16) float Sw[2][KG][TN];
+  __shared__ __align__(16) uint8_t As[2][TM * ROWB];
+  __shared__ __align__(16) uint8_t Bs[2][TN * ROWB];
+  __shared__ __align__(16) float Sxq[2][TM];  // sx / 256
+  __shared__ __align__(16) float Sng[2][TM];  // -1.5*2^23 * sx / 256
+  __shared__ __align__(16) float Sw[2][TN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int r = lane & 15, c = lane >> 4;
-  int ti, tj;
-  tile_of(blockIdx.x, tiles_m, tiles_n, ti, tj);
-  const int i0 = ti * TM, j0 = tj * TN;
+  constexpr int AB = C::A_BYTES, BB = C::B_BYTES;
+  const int a_row = tid * AB / 32, a_w0 = (tid * AB % 32) / 4;
+  const int b_col = tid * BB / 32, b_w0 = (tid * BB % 32) / 4;
+  const uint32_t a_bytes = (uint32_t)b * 32u, b_bytes = (uint32_t)n * 32u;
+  const i32x4 magic = {kMagicBits, kMagicBits, kMagicBits, kMagicBits};
 
   f32x4 acc[BI][BJ];
-#pragma unroll
-  for (int bi = 0; bi < BI; ++bi)
-#pragma unroll
-    for (int bj = 0; bj < BJ; ++bj) acc[bi][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // ---- low-rank branch: acc = bf16(Z) L2 over K = rank in chunks of 32 -------
   // 16-byte loads when every row of l2 / z starts 16-byte aligned
   const bool l2_vec = (rank % 8) == 0 && ((uintptr_t)l2t & 15u) == 0;
   const bool z_vec = (rank % 4) == 0 && ((uintptr_t)z & 15u) == 0;
-  for (int kc = 0; kc < rank; kc += 32) {
-    const int t0 = kc + 8 * c;  // this lane's 8 entries of the rank dimension
-    bf16x8 P[BJ];
+  auto lowrank = [&](int i0, int j0) {
+    for (int kc = 0; kc < rank; kc += 32) {
+      const int t0 = kc + 8 * c;  // this lane's 8 entries of the rank dimension
+      bf16x8 P[BJ];
 #pragma unroll
-    for (int bj = 0; bj < BJ; ++bj) {
-      const int j = j0 + WN * wn + 16 * bj + r;
-      u32x4 wv = {0u, 0u, 0u, 0u};
-      if (j < n) {
-        if (l2_vec && t0 + 8 <= rank) {
-          wv = ldg16(l2t + (size_t)j * rank + t0);
-        } else {
+      for (int bj = 0; bj < BJ; ++bj) {
+        const int j = j0 + WN * wn + 16 * bj + r;
+        u32x4 wv = {0u, 0u, 0u, 0u};
+        if (j < n) {
+          if (l2_vec && t0 + 8 <= rank) {
+            wv = ldg16(l2t + (size_t)j * rank + t0);
+          } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int t = t0 + 2 * e;
-            const uint32_t lo = t < rank ? l2t[(size_t)j * rank + t] : 0u;
-            const uint32_t hi = t + 1 < rank ? l2t[(size_t)j * rank + t + 1] : 0u;
-            wv[e] = lo | (hi << 16);
+            for (int e = 0; e < 4; ++e) {
+              const int t = t0 + 2 * e;
+              const uint32_t lo = t < rank ? l2t[(size_t)j * rank + t] : 0u;
+              const uint32_t hi = t + 1 < rank ? l2t[(size_t)j * rank + t + 1] : 0u;
+              wv[e] = lo | (hi << 16);
+            }
           }
         }
+        P[bj] = __builtin_bit_cast(bf16x8, wv);
       }
-      P[bj] = __builtin_bit_cast(bf16x8, wv);
-    }
 #pragma unroll
-    for (int bi = 0; bi < BI; ++bi) {
-      const int i = i0 + WM * wm + 16 * bi + r;
-      float zv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (i < b) {
-        const float* zr = z + (size_t)i * rank + t0;
-        if (z_vec && t0 + 8 <= rank) {
-          const f32x4 z0 = *reinterpret_cast<const f32x4*>(zr);
-          const f32x4 z1 = *reinterpret_cast<const f32x4*>(zr + 4);
+      for (int bi = 0; bi < BI; ++bi) {
+        const int i = i0 + WM * wm + 16 * bi + r;
+        float zv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (i < b) {
+          const float* zr = z + (size_t)i * rank + t0;
+          if (z_vec && t0 + 8 <= rank) {
+            const f32x4 z0 = *reinterpret_cast<const f32x4*>(zr);
+            const f32x4 z1 = *reinterpret_cast<const f32x4*>(zr + 4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            zv[e] = z0[e];
-            zv[4 + e] = z1[e];
+            for (int e = 0; e < 4; ++e) {
+              zv[e] = z0[e];
+              zv[4 + e] = z1[e];
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) zv[e] = t0 + e < rank ? zr[e] : 0.0f;
           }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) zv[e] = t0 + e < rank ? zr[e] : 0.0f;
         }
-      }
-      const bf16x8 Q = __builtin_bit_cast(
-          bf16x8, u32x4{pack_bf16x2(zv[0], zv[1]), pack_bf16x2(zv[2], zv[3]),
-                        pack_bf16x2(zv[4], zv[5]), pack_bf16x2(zv[6], zv[7])});
+        const bf16x8 Q = __builtin_bit_cast(
+            bf16x8, u32x4{pack_bf16x2(zv[0], zv[1]), pack_bf16x2(zv[2], zv[3]),
+                          pack_bf16x2(zv[4], zv[5]), pack_bf16x2(zv[6], zv[7])});
 #pragma unroll
-      for (int bj = 0; bj < BJ; ++bj)
-        acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(P[bj], Q, acc[bi][bj], 0, 0, 0);
+        for (int bj = 0; bj < BJ; ++bj)
+          acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(P[bj], Q, acc[bi][bj], 0, 0, 0);
+      }
     }
-  }
+  };
 
-  // ---- main branch: exact per-group i8 MFMA + fp32 scale epilogue ----------
+  // ---- main branch over groups [g0, g1) of the tile at (i0, j0) --------------
   // Staging: per group every thread issues the same three buffer loads: one
   // piece of an activation record, one piece of a weight record, one fp16
   // scale.  The per-group base lives in the (scalar) buffer descriptor, whose
   // size bound makes rows >= b and columns >= n read as zero.
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy
-  constexpr int AB = C::A_BYTES, BB = C::B_BYTES;
-  const int a_row = tid * AB / 32, a_w0 = (tid * AB % 32) / 4;
-  const int b_col = tid * BB / 32, b_w0 = (tid * BB % 32) / 4;
-  const uint32_t a_voff = (uint32_t)(i0 + a_row) * 32u + 4u * a_w0;
-  const uint32_t b_voff = (uint32_t)(j0 + b_col) * 32u + 4u * b_w0;
-  // activation scale of row i0+tid, weight scale of column j0+tid-TM, or an
-  // out-of-range offset (reads 0) for the threads that stage no scale
-  const uint32_t s_voff = tid < TM ? (uint32_t)(i0 + tid) * 2u
-                                   : (tid < TM + TN ? (uint32_t)(j0 + tid - TM) * 2u : 0x7FFFFFF0u);
-  const uint32_t a_bytes = (uint32_t)b * 32u, b_bytes = (uint32_t)n * 32u;
-
   struct Stage {
-    Piece<AB> a[KG];
-    Piece<BB> w[KG];
-    uint32_t s[KG];
+    Piece<AB> a;
+    Piece<BB> w;
+    uint32_t s;
   };
-  const int S = (G + KG - 1) / KG;  // stages
-  auto load_stage = [&](int st_idx, Stage& st) {
-#pragma unroll
-    for (int kg = 0; kg < KG; ++kg) {
-      const int g = min(st_idx * KG + kg, G - 1);
+  auto main_branch = [&](int i0, int j0, int g0, int g1) {
+    const uint32_t a_voff = (uint32_t)(i0 + a_row) * 32u + 4u * a_w0;
+    const uint32_t b_voff = (uint32_t)(j0 + b_col) * 32u + 4u * b_w0;
+    // activation scale of row i0+tid, weight scale of column j0+tid-TM, or an
+    // out-of-range offset (reads 0) for the threads that stage no scale
+    const uint32_t s_voff = tid < TM ? (uint32_t)(i0 + tid) * 2u
+                                     : (tid < TM + TN ? (uint32_t)(j0 + tid - TM) * 2u : 0x7FFFFFF0u);
+    const int S = g1 - g0;  // groups in this segment
+    auto load_stage = [&](int k, Stage& st) {
+      const int g = g0 + min(k, S - 1);
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(qx + (size_t)g * a_bytes, a_bytes);
       const __amdgpu_buffer_rsrc_t rb = make_rsrc(qw + (size_t)g * b_bytes, b_bytes);
       // wave-uniform choice (waves 0 .. TM/64-1 stage activation scales), so the
@@ -255,176 +289,316 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
       const __amdgpu_buffer_rsrc_t rs =
           wave_u < TM / 64 ? make_rsrc(ascale + (size_t)g * b, (uint32_t)b * 2u)
                            : make_rsrc(wscale + (size_t)g * n, (uint32_t)n * 2u);
-      st.a[kg] = buffer_piece<AB>(ra, a_voff);
-      st.w[kg] = buffer_piece<BB>(rb, b_voff);
-      st.s[kg] = __builtin_amdgcn_raw_buffer_load_b16(rs, s_voff, 0, 0);
-    }
-  };
-  auto store_stage = [&](int buf, const Stage& st) {
-#pragma unroll
-    for (int kg = 0; kg < KG; ++kg) {
-      unpack_piece<AB>(&As[buf][(kg * TM + a_row) * ROWB], a_w0, st.a[kg]);
-      unpack_piece<BB>(&Bs[buf][(kg * TN + b_col) * ROWB], b_w0, st.w[kg]);
-      const float sv = f16_to_f32((uint16_t)st.s[kg]);
+      st.a = buffer_piece<AB>(ra, a_voff);
+      st.w = buffer_piece<BB>(rb, b_voff);
+      st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, s_voff, 0, 0);
+    };
+    auto store_stage = [&](int buf, const Stage& st) {
+      unpack_piece<AB>(&As[buf][a_row * ROWB], a_w0, st.a);
+      unpack_piece<BB>(&Bs[buf][b_col * ROWB], b_w0, st.w);
+      const float sv = f16_to_f32((uint16_t)st.s);
       if (wave_u < TM / 64) {
         const float q = sv * 0.00390625f;  // sx / 256 (exact)
-        Sxq[buf][kg][tid] = q;
-        Sng[buf][kg][tid] = -kMagic * q;   // exact: 3 * 2^14 * sx
+        Sxq[buf][tid] = q;
+        Sng[buf][tid] = -kMagic * q;       // exact: 3 * 2^14 * sx
       } else if (wave_u < (TM + TN) / 64) {
-        Sw[buf][kg][tid - TM] = sv;
+        Sw[buf][tid - TM] = sv;
       }
-    }
-  };
-
-  const i32x4 magic = {kMagicBits, kMagicBits, kMagicBits, kMagicBits};
-  // One group: for each 16-row block bi, BJ MFMAs (one per 16-column block) and
-  // 8*BJ FMAs.  The MFMAs of block bi are issued next to the FMAs of block bi-1
-  // (software pipeline).  The empty asm statements take the updated
-  // accumulators as operands: they emit nothing but pin each block's FMAs in
-  // place, so the compiler cannot sink them past later MFMAs (which would keep
-  // every MFMA result live at once).
-  auto compute_group = [&](const uint8_t* Ab, const uint8_t* Bb, const float* sxq_s,
-                           const float* sng_s, const float* sw_s) {
-    u32x4 Pb[BJ];
-    f32x4 sw4[BJ];
+    };
+    // One group: for each 16-row block bi, BJ MFMAs (one per 16-column block)
+    // and 8*BJ FMAs.  The MFMAs of block bi are issued next to the FMAs of block
+    // bi-1 (software pipeline).  The empty asm statements take the updated
+    // accumulators as operands: they emit nothing but pin each block's FMAs in
+    // place, so the compiler cannot sink them past later MFMAs (which would keep
+    // every MFMA result live at once).
+    auto compute = [&](int buf) {
+      u32x4 Pb[BJ];
+      f32x4 sw4[BJ];
 #pragma unroll
-    for (int bj = 0; bj < BJ; ++bj) {
-      const int cc = WN * wn + 16 * bj;
-      Pb[bj] = *reinterpret_cast<const u32x4*>(&Bb[(cc + r) * ROWB + 16 * c]);
-      sw4[bj] = *reinterpret_cast<const f32x4*>(&sw_s[cc + 4 * c]);
-    }
-    const int rbase = WM * wm + r;
-    u32x4 Qa = *reinterpret_cast<const u32x4*>(&Ab[rbase * ROWB + 16 * c]);
-    i32x4 d[2][BJ];
-    float sxq[2], sng[2];
-#pragma unroll
-    for (int bi = 0; bi <= BI; ++bi) {
-      const int cur = bi & 1, prev = cur ^ 1;
-      u32x4 Qn = Qa;
-      if (bi < BI) {
-        const int rr = rbase + 16 * bi;
-        sxq[cur] = sxq_s[rr];
-        sng[cur] = sng_s[rr];
-        if (bi + 1 < BI) Qn = *reinterpret_cast<const u32x4*>(&Ab[(rr + 16) * ROWB + 16 * c]);
-#pragma unroll
-        for (int bj = 0; bj < BJ; ++bj)
-          d[cur][bj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-              __builtin_bit_cast(i32x4, Pb[bj]), __builtin_bit_cast(i32x4, Qa), magic, 0, 0, 0);
+      for (int bj = 0; bj < BJ; ++bj) {
+        const int cc = WN * wn + 16 * bj;
+        Pb[bj] = *reinterpret_cast<const u32x4*>(&Bs[buf][(cc + r) * ROWB + 16 * c]);
+        sw4[bj] = *reinterpret_cast<const f32x4*>(&Sw[buf][cc + 4 * c]);
       }
-      if (bi > 0) {
+      const int rbase = WM * wm + r;
+      u32x4 Qa = *reinterpret_cast<const u32x4*>(&As[buf][rbase * ROWB + 16 * c]);
+      i32x4 d[2][BJ];
+      float sxq[2], sng[2];
 #pragma unroll
-        for (int bj = 0; bj < BJ; ++bj) {
+      for (int bi = 0; bi <= BI; ++bi) {
+        const int cur = bi & 1, prev = cur ^ 1;
+        u32x4 Qn = Qa;
+        if (bi < BI) {
+          const int rr = rbase + 16 * bi;
+          sxq[cur] = Sxq[buf][rr];
+          sng[cur] = Sng[buf][rr];
+          if (bi + 1 < BI) Qn = *reinterpret_cast<const u32x4*>(&As[buf][(rr + 16) * ROWB + 16 * c]);
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float t = __builtin_fmaf(__int_as_float(d[prev][bj][v]), sxq[prev], sng[prev]);
-            acc[bi - 1][bj][v] = __builtin_fmaf(t, sw4[bj][v], acc[bi - 1][bj][v]);
-          }
-          asm volatile("" : "+v"(acc[bi - 1][bj]));
+          for (int bj = 0; bj < BJ; ++bj)
+            d[cur][bj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                __builtin_bit_cast(i32x4, Pb[bj]), __builtin_bit_cast(i32x4, Qa), magic, 0, 0, 0);
         }
-      }
-      Qa = Qn;
-    }
-  };
-  auto compute = [&](int buf, int st_idx) {
+        if (bi > 0) {
 #pragma unroll
-    for (int kg = 0; kg < KG; ++kg) {
-      if (KG == 1 || st_idx * KG + kg < G)
-        compute_group(&As[buf][kg * TM * ROWB], &Bs[buf][kg * TN * ROWB], Sxq[buf][kg], Sng[buf][kg],
-                      Sw[buf][kg]);
+          for (int bj = 0; bj < BJ; ++bj) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float t = __builtin_fmaf(__int_as_float(d[prev][bj][v]), sxq[prev], sng[prev]);
+              acc[bi - 1][bj][v] = __builtin_fmaf(t, sw4[bj][v], acc[bi - 1][bj][v]);
+            }
+            asm volatile("" : "+v"(acc[bi - 1][bj]));
+          }
+        }
+        Qa = Qn;
+      }
+    };
+
+    // Pipeline: LDS[k & 1] holds group g0+k while it is computed; a ring of D
+    // register stages holds groups k+1 .. k+D (the later ones still loading).
+    // After computing group k, group k+1 moves from its register slot into the
+    // other LDS buffer and the freed slot starts loading group k+1+D.  Loads
+    // and stores are unconditional (past the end they re-read the last group
+    // into a buffer nobody reads), so no branch sits between a load and its use
+    // and each wait covers exactly one group.  The trailing barrier also makes
+    // the LDS buffers free for the next segment.
+    constexpr int D = C::DEPTH;
+    Stage st[D];
+#pragma unroll
+    for (int k = 0; k < D; ++k) load_stage(k, st[k]);
+    store_stage(0, st[0]);
+    load_stage(D, st[0]);
+    __syncthreads();
+    for (int k0 = 0; k0 < S; k0 += D) {
+#pragma unroll
+      for (int k = 0; k < D; ++k) {
+        if (k0 + k < S) compute(k & 1);
+        store_stage((k + 1) & 1, st[(k + 1) % D]);
+        load_stage(k0 + k + 1 + D, st[(k + 1) % D]);
+        __syncthreads();
+      }
     }
   };
-
-  // pipeline: LDS[s & 1] holds stage s; register stage st[(s + 1) & 1] holds
-  // stage s + 1; stage st[s & 1] has stage s + 2 in flight.  Loads and stores
-  // in the loop are unconditional (past the end they re-read the last group
-  // into a buffer nobody reads), so no branch sits between a load and its use
-  // and each wait covers exactly one stage.
-  Stage st0, st1;
-  load_stage(0, st0);
-  load_stage(min(1, S - 1), st1);
-  store_stage(0, st0);
-  load_stage(min(2, S - 1), st0);
-  __syncthreads();
-  int s = 0;
-  for (; s + 1 < S; s += 2) {
-    compute(0, s);
-    store_stage(1, st1);
-    load_stage(min(s + 3, S - 1), st1);
-    __syncthreads();
-    compute(1, s + 1);
-    store_stage(0, st0);
-    load_stage(min(s + 4, S - 1), st0);
-    __syncthreads();
-  }
-  if (s < S) compute(0, s);
 
   // ---- epilogue: bias, cast, one store of Y ---------------------------------
   // lane holds Y[i][j..j+3]: i = row (l & 15) of block bi, j = 4 (l >> 4) of block bj
-  const bool vec_ok = (n & 3) == 0 && ((uintptr_t)yout & (OUT_BF16 ? 7u : 15u)) == 0;
+  auto store_tile = [&](int i0, int j0) {
+    const bool vec_ok = (n & 3) == 0 && ((uintptr_t)yout & (OUT_BF16 ? 7u : 15u)) == 0;
 #pragma unroll
-  for (int bj = 0; bj < BJ; ++bj) {
-    const int j = j0 + WN * wn + 16 * bj + 4 * c;
-    float bv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (bias) {
+    for (int bj = 0; bj < BJ; ++bj) {
+      const int j = j0 + WN * wn + 16 * bj + 4 * c;
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (bias) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (j + v < n) bv[v] = __uint_as_float((uint32_t)bias[j + v] << 16);
-    }
+        for (int v = 0; v < 4; ++v)
+          if (j + v < n) bv[v] = __uint_as_float((uint32_t)bias[j + v] << 16);
+      }
 #pragma unroll
-    for (int bi = 0; bi < BI; ++bi) {
-      const int i = i0 + WM * wm + 16 * bi + r;
-      if (i >= b) continue;
-      f32x4 o = acc[bi][bj];
+      for (int bi = 0; bi < BI; ++bi) {
+        const int i = i0 + WM * wm + 16 * bi + r;
+        if (i >= b) continue;
+        f32x4 o = acc[bi][bj];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) o[v] += bv[v];
-      if (OUT_BF16) {
-        uint16_t* y = reinterpret_cast<uint16_t*>(yout) + (size_t)i * n + j;
-        if (vec_ok && j + 3 < n) {
-          *reinterpret_cast<uint2*>(y) = uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        for (int v = 0; v < 4; ++v) o[v] += bv[v];
+        if (OUT_BF16) {
+          uint16_t* y = reinterpret_cast<uint16_t*>(yout) + (size_t)i * n + j;
+          if (vec_ok && j + 3 < n) {
+            *reinterpret_cast<uint2*>(y) = uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (j + v < n) y[v] = bf16_bits(o[v]);
+          }
         } else {
+          float* y = reinterpret_cast<float*>(yout) + (size_t)i * n + j;
+          if (vec_ok && j + 3 < n) {
+            *reinterpret_cast<f32x4*>(y) = o;
+          } else {
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (j + v < n) y[v] = bf16_bits(o[v]);
-        }
-      } else {
-        float* y = reinterpret_cast<float*>(yout) + (size_t)i * n + j;
-        if (vec_ok && j + 3 < n) {
-          *reinterpret_cast<f32x4*>(y) = o;
-        } else {
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (j + v < n) y[v] = o[v];
+            for (int v = 0; v < 4; ++v)
+              if (j + v < n) y[v] = o[v];
+          }
         }
       }
     }
+  };
+
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < BJ; ++bj) acc[bi][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  if ((int)blockIdx.x >= sk.P) {  // one tile per workgroup
+    const int T = tiles_m * tiles_n;
+    int ti, tj;
+    band_tile(dp_tile((int)blockIdx.x - sk.P, T - sk.T, sk.T), tiles_m, tiles_n, ti, tj);
+    zero_acc();
+    lowrank(ti * TM, tj * TN);
+    main_branch(ti * TM, tj * TN, 0, G);
+    store_tile(ti * TM, tj * TN);
+    return;
+  }
+
+  // ---- stream-K: iterations [u0, u1) of this workgroup, descending ----------
+  const int p = blockIdx.x;
+  const long long u0 = (long long)p * sk.U / sk.P, u1 = (long long)(p + 1) * sk.U / sk.P;
+  long long u = u1;
+  while (u > u0) {
+    const long long t = (u - 1) / G, ts = t * G;
+    const long long lo = u0 > ts ? u0 : ts;
+    const int g0 = (int)(lo - ts), g1 = (int)(u - ts);
+    int ti, tj;
+    band_tile((int)t, tiles_m, tiles_n, ti, tj);
+    const int i0 = ti * TM, j0 = tj * TN;
+    zero_acc();
+    if (g1 == G) lowrank(i0, j0);  // the tile's last groups carry the low-rank branch
+    main_branch(i0, j0, g0, g1);
+    if (g1 < G) {
+      // Publish this partial (this workgroup's first work item) for the
+      // finisher.  Partials are written and read only with device-coherent
+      // (sc1) buffer accesses, the cache policy of device-scope atomics, so
+      // no L2 writeback or invalidate is needed: each wave waits for its
+      // stores to complete (vmcnt 0) before the barrier after which the flag
+      // (a device-scope atomic) is raised.
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc(sk.partials + (size_t)p * (TM * TN), TM * TN * 4);
+#pragma unroll
+      for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < BJ; ++bj)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[bi][bj]), rp,
+                                                 (uint32_t)(((bi * BJ + bj) * NT + tid) * 16), 0, kCoherent);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      if (tid == 0) __hip_atomic_store(&sk.flags[p], sk.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      // finisher: the tile's earlier groups were published by workgroups
+      // qlo .. p-1 (lower-numbered, dispatched earlier, and each running that
+      // piece as its first work item, which waits on nothing)
+      int qlo = p;
+      while (qlo > 0 && (long long)qlo * sk.U / sk.P > ts) --qlo;
+      if (qlo < p) {
+        if (tid == 0) {
+          for (int q = p - 1; q >= qlo; --q)
+            for (int spin = 0; spin < (1 << 24); ++spin) {  // bound: guards misuse of the workspace
+              if (__hip_atomic_load(&sk.flags[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == sk.epoch) break;
+              __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        // the flag loads have completed before the barrier; the partials are
+        // then read with device-coherent loads, in the fixed order p-1 .. qlo
+        __syncthreads();
+        for (int q = p - 1; q >= qlo; --q) {
+          const __amdgpu_buffer_rsrc_t rq = make_rsrc(sk.partials + (size_t)q * (TM * TN), TM * TN * 4);
+#pragma unroll
+          for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < BJ; ++bj)
+              acc[bi][bj] += __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)(((bi * BJ + bj) * NT + tid) * 16), 0,
+                                                               kCoherent));
+        }
+      }
+      store_tile(i0, j0);
+    }
+    u = lo;
   }
 }
 
-template <class C>
-int launch_cfg(const uint8_t* qx, const uint16_t* ascale, const float* z, const svdq_layer& L, int b,
-               void* y, int y_dtype, hipStream_t st) {
-  const int G = L.m / 64;
-  const int tiles_n = (L.n + C::TN - 1) / C::TN;
-  const int tiles_m = (b + C::TM - 1) / C::TM;
-  dim3 grid((unsigned)(tiles_n * tiles_m));
-  if (y_dtype == SVDQ_OUT_BF16)
-    hipLaunchKernelGGL((gemm_w4a4_up_kernel<C, true>), grid, dim3(C::NT), 0, st, qx, ascale, z, L.qw,
-                       L.wscale, L.l2, L.bias, b, L.n, G, L.rank, tiles_m, tiles_n, y);
-  else
-    hipLaunchKernelGGL((gemm_w4a4_up_kernel<C, false>), grid, dim3(C::NT), 0, st, qx, ascale, z, L.qw,
-                       L.wscale, L.l2, L.bias, b, L.n, G, L.rank, tiles_m, tiles_n, y);
+int g_num_cus = 0;
+std::atomic<unsigned long long> g_epoch_counter{0};  // one sequence for every launch
+
+// Base of the stream-K publication epochs: distinct per process (time and
+// address entropy), so flags left in reused memory by another process never
+// match an epoch of this one.
+unsigned long long epoch_base() {
+  static const unsigned long long base = [] {
+    const unsigned long long t =
+        (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+    const unsigned long long a = (unsigned long long)(uintptr_t)&g_num_cus;
+    unsigned long long x = t ^ (a << 17) ^ 0x9E3779B97F4A7C15ull;
+    x ^= x >> 31;
+    x *= 0xBF58476D1CE4E5B9ull;
+    x ^= x >> 29;
+    return (x | 1ull) << 20;  // low bits left for the per-launch counter
+  }();
+  return base;
+}
+
+template <bool OUT_BF16>
+int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, const svdq_layer& L, int b,
+                 void* y, const GemmPlan& plan, void* ws, hipStream_t st) {
+  StreamK sk{0, 0, 0, nullptr, nullptr, 0};
+  if (plan.streamk) {
+    sk.P = plan.sk_grid;
+    sk.T = plan.sk_tiles;
+    sk.U = (long long)plan.sk_tiles * plan.G;
+    sk.partials = reinterpret_cast<float*>(ws);
+    sk.flags = reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(ws) + plan.partial_bytes);
+    sk.epoch = epoch_base() + g_epoch_counter.fetch_add(1);
+  }
+  hipLaunchKernelGGL((gemm_w4a4_up_kernel<Cfg, OUT_BF16>), dim3((unsigned)plan.grid), dim3(Cfg::NT), 0, st,
+                     qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
+                     plan.tiles_n, y, sk);
   return (int)hipGetLastError();
 }
 
-// 128 x 128 tile, 4 waves of 64 x 64; two workgroups share a CU, so one
-// workgroup's barrier and LDS-latency phases overlap the others' compute.
-using CfgBig = GemmCfg<128, 128, 64, 64, 1, 2>;
-
 }  // namespace
 
+// Plan of the GEMM launch.  With T tiles of G groups and S = 2 * CUs
+// resident slots, one tile per workgroup leaves each slot idle for
+// (ceil(T / S) - T / S) * G group-iterations on average.  When that idle
+// time is at least 16 group-iterations (the measured cost of splitting a
+// tile is a few), the tiles beyond the first floor(T / S) - 1 full rounds
+// (between S and 2S of them, or all T when T < 2S) go to min(S, their
+// iterations / 8) stream-K workgroups, dispatched first, and the full rounds
+// follow one tile per workgroup.  The workspace bound assumes the largest
+// gfx950 part (256 CUs), so it does not depend on the device.
+GemmPlan gemm_plan(int b, int n, int m, int cus) {
+  GemmPlan p;
+  p.G = m / 64;
+  p.tiles_m = (b + Cfg::TM - 1) / Cfg::TM;
+  p.tiles_n = (n + Cfg::TN - 1) / Cfg::TN;
+  const long long T = (long long)p.tiles_m * p.tiles_n;
+  const long long slots = 2LL * (cus > 0 ? cus : kMaxCUs);
+  const long long rounds = (T + slots - 1) / slots;
+  const double idle = ((double)rounds - (double)T / (double)slots) * p.G;
+  p.streamk = idle >= 16.0 && T * p.G >= 16;
+  p.sk_tiles = 0;
+  p.sk_grid = 0;
+  if (p.streamk) {
+    const long long full = T / slots;
+    const long long dp = full >= 2 ? (full - 1) * slots : 0;
+    p.sk_tiles = (int)(T - dp);
+    p.sk_grid = (int)std::max(1LL, std::min(slots, (long long)p.sk_tiles * p.G / 8));
+    p.grid = (int)(p.sk_grid + dp);
+  } else {
+    p.grid = (int)T;
+  }
+  const long long max_sk = std::max(1LL, std::min(2LL * kMaxCUs, T * p.G / 8));
+  p.partial_bytes = (size_t)max_sk * Cfg::TM * Cfg::TN * 4;
+  p.ws_bytes = p.streamk || cus <= 0 ? p.partial_bytes + (size_t)max_sk * 8 : 0;
+  return p;
+}
+
+int device_cus() {
+  if (g_num_cus == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      g_num_cus = std::min(v, kMaxCUs);
+    else
+      g_num_cus = kMaxCUs;
+  }
+  return g_num_cus;
+}
+
 int launch_gemm_up(const uint8_t* qx, const uint16_t* ascale, const float* z, const svdq_layer& L,
-                   int b, void* y, int y_dtype, void* stream) {
-  return launch_cfg<CfgBig>(qx, ascale, z, L, b, y, y_dtype, (hipStream_t)stream);
+                   int b, void* y, int y_dtype, void* ws, void* stream) {
+  const GemmPlan plan = gemm_plan(b, L.n, L.m, device_cus());
+  hipStream_t st = (hipStream_t)stream;
+  if (y_dtype == SVDQ_OUT_BF16) return launch_typed<true>(qx, ascale, z, L, b, y, plan, ws, st);
+  return launch_typed<false>(qx, ascale, z, L, b, y, plan, ws, st);
 }
 
 }  // namespace svdq

@@ -48,8 +48,24 @@ int launch_act_quant_down(const uint16_t* x, int b, int m, int rank, const float
                           const uint16_t* l1, uint8_t* qx, uint16_t* ascale, float* zpart,
                           const ActPlan& plan, void* stream);
 int launch_z_reduce(const float* zpart, int splits, int b, int rank, float* z, void* stream);
+// GEMM launch plan (gemm_kernels.hip): one tile per workgroup, or stream-K
+// over a persistent grid with fp32 partials and publication flags in the
+// workspace.
+constexpr int kMaxCUs = 256;  // largest gfx950 part
+struct GemmPlan {
+  int tiles_m, tiles_n, G;
+  int grid;             // workgroups launched
+  int streamk;          // 1 = hybrid schedule with a stream-K part
+  int sk_tiles;         // tiles shared out by stream-K (linear tiles [0, sk_tiles))
+  int sk_grid;          // stream-K workgroups (dispatched first)
+  size_t partial_bytes; // partial-sum area at the start of the workspace
+  size_t ws_bytes;      // workspace this launch needs (0 for one tile per workgroup)
+};
+// cus <= 0 gives the device-independent upper bound used to size workspaces.
+GemmPlan gemm_plan(int b, int n, int m, int cus);
+int device_cus();
 int launch_gemm_up(const uint8_t* qx, const uint16_t* ascale, const float* z, const svdq_layer& L,
-                   int b, void* y, int y_dtype, void* stream);
+                   int b, void* y, int y_dtype, void* ws, void* stream);
 const char* hip_error_name(int err);
 
 }  // namespace svdq
