@@ -9,13 +9,34 @@ that HIP events on the launch stream can bracket the GEMM kernel inside the
 timed region.  Offline preparation (smoothing, SVD, residual quantization) is
 done before timing and is not part of a step.
 
-Prints ONE JSON line (see the keys below).  Default workload: the FLUX-shaped
-fused QKV projection (b=4608 tokens, m=3072, n=9216, rank 32, group 64).
+Timed region ("cold"): the steps rotate over several independently seeded
+input + weight sets whose footprint exceeds the 256 MB last-level cache, so a
+step does not find its layer's weights or activations cached by the previous
+step.  Also reported: the same steps on one set ("warm"), the low-rank
+overhead t(rank r) / t(rank 0, same codes and scales) - 1, and the one-call
+``svdq_linear`` entry point.
+
+Prints ONE JSON line.  Default workload: the FLUX-shaped fused QKV projection
+(b=4608 tokens, m=3072, n=9216, rank 32, group 64).
+
+Extra modes (used with rocprofv3 runs):
+  --copy-check               also run a plain device copy of known size, which
+                             calibrates the FETCH_SIZE / WRITE_SIZE counters;
+  --traffic-summary F W      turn two counter-collection directories (a
+                             FETCH_SIZE run and a WRITE_SIZE run of the same
+                             command) into the per-launch HBM traffic summary
+                             read by the JSON line's roofline.traffic;
+  --trace-summary DIR        summarize a --kernel-trace --stats run of this
+                             script (same --workload/--steps/--warmup).
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import csv
+import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -28,10 +49,29 @@ sys.path.insert(0, ROOT)
 I8_PEAK_TOPS = 5000.0      # MI355X dense i8 MFMA, TOP/s
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 METRIC = "fused W4A4+low-rank linear TOPS (2·b·m·n/s), FLUX shapes; % of i8 MFMA peak"
+GEMM_KERNEL = "gemm_w4a4_up_kernel"
+# sources whose text defines the GEMM kernel and its launch plan
+GEMM_SOURCES = ["w4a4_rank_corrected_amd/csrc/gemm_kernels.hip",
+                "w4a4_rank_corrected_amd/csrc/device_common.h",
+                "w4a4_rank_corrected_amd/csrc/internal.h"]
+COPY_BYTES = 256 << 20     # plain copy used to calibrate the byte counters
+COLD_BYTES = 512 << 20     # rotated footprint of the cold measurement
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{GEMM_KERNEL}_{workload}.json")
 
 
 def algorithmic_bytes(b, m, n, r):
@@ -42,6 +82,135 @@ def algorithmic_bytes(b, m, n, r):
     k2 = b * m // 2 + 2 * b * G + 4 * b * r + m * n // 2 + 2 * G * n + 2 * n * r + 2 * b * n
     return k1, k2
 
+
+def set_plan(cfg, rank, out):
+    """(bytes of one input+weight set, number of sets rotated by the cold timing)."""
+    b, m, n = cfg.rows or cfg.b, cfg.m, cfg.n
+    per_set = 2 * b * m + m * n // 2 + 2 * (m // 64) * n + 2 * rank * (m + n) + 4 * m + \
+        (2 if out == "bf16" else 4) * b * n
+    return per_set, max(3, math.ceil(COLD_BYTES / per_set))
+
+
+# ---------------------------------------------------------------------------
+# profile summaries (no GPU needed)
+# ---------------------------------------------------------------------------
+
+def trace_summary(prof_dir, cfg, args, rank):
+    """Markdown summary of a ``rocprofv3 --kernel-trace --stats`` run of this
+    script: per-kernel totals, and the mean duration of each kernel over the
+    cold timed region (the dispatches after the warm-up, in launch order)."""
+    import re
+    import sqlite3
+    dbs = glob.glob(os.path.join(prof_dir, "**", "*.db"), recursive=True)
+    if not dbs:
+        raise SystemExit(f"no rocpd database under {prof_dir}")
+    c = sqlite3.connect(dbs[0])
+    _, n_sets = set_plan(cfg, rank, args.out)
+    skip = max(args.warmup, n_sets)
+    short = lambda nm: re.sub(r"\(.*", "", nm.replace("svdq::(anonymous namespace)::", "")
+                              .replace("void ", "").replace("svdq::", ""))
+    rows = list(c.execute("select name, start, end, grid_x, workgroup_x, vgpr_count, accum_vgpr_count, "
+                          "lds_size, scratch_size from kernels order by start"))
+    by = {}
+    for nm, st, en, gx, wx, vg, ag, lds, scr in rows:
+        by.setdefault(nm, []).append(((en - st) / 1e3, gx // max(wx, 1), wx, vg, ag, lds, scr))
+    cmd = (f"rocprofv3 --kernel-trace --stats -d {prof_dir} -o run -- python3 bench.py --workload {cfg.name} "
+           f"--steps {args.steps} --warmup {args.warmup} --no-cpu-baseline")
+    out = [f"# Kernel trace: {cfg.name} (b={cfg.rows or cfg.b}, m={cfg.m}, n={cfg.n}, rank {rank})", "",
+           "Command (repository root, one MI355X), then the summary:", "", "```", cmd,
+           f"python bench.py --trace-summary {prof_dir} --workload {cfg.name} --steps {args.steps} "
+           f"--warmup {args.warmup}", "```", "",
+           f"Timed region: {args.steps} steps after {skip} untimed ones, rotating over {n_sets} "
+           f"input+weight sets; the script then times warm steps, rank-0 steps and the one-call entry "
+           f"point, which the all-dispatch columns include.", "",
+           "| kernel | dispatches | mean, timed region (us) | mean, all (us) | total (ms) | workgroups | "
+           "threads | LDS (B) | scratch (B) |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    total = sum(d[0] for v in by.values() for d in v)
+    for nm, v in sorted(by.items(), key=lambda kv: -sum(d[0] for d in kv[1])):
+        durs = [d[0] for d in v]
+        # kernels launched once per step: the timed region is dispatches [skip, skip + steps)
+        per_step = [d for d in durs[skip: skip + args.steps]] if len(durs) >= skip + args.steps else []
+        t = f"{np.mean(per_step):.2f}" if per_step else "-"
+        d0 = v[0]
+        out.append(f"| `{short(nm)}` | {len(v)} | {t} | {np.mean(durs):.2f} | {sum(durs) / 1e3:.3f} | "
+                   f"{d0[1]} | {d0[2]} | {d0[5]} | {d0[6]} |")
+    out += ["", f"All kernels: {total / 1e3:.3f} ms of GPU time.", ""]
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{cfg.name}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out))
+    print("\n".join(out))
+    log(f"wrote {path}")
+
+
+def _counter_rows(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch(rows, counter, name_pred):
+    vals = {}
+    for r in rows:
+        if r["Counter_Name"] == counter and name_pred(r["Kernel_Name"]):
+            vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return list(vals.values())
+
+
+def traffic_summary(fetch_dir, write_dir, workload, commands):
+    """Per-launch HBM bytes of the GEMM kernel from a FETCH_SIZE run and a
+    WRITE_SIZE run (KiB per dispatch), each scaled by what the same counter
+    reads for the plain copy of COPY_BYTES."""
+    is_copy = lambda k: "elementwise" in k or "copy" in k.lower()
+    is_gemm = lambda k: GEMM_KERNEL in k
+    fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    # the copy is the largest elementwise dispatch of the run
+    cf = max(_per_dispatch(fr, "FETCH_SIZE", is_copy))
+    cw = max(_per_dispatch(wr, "WRITE_SIZE", is_copy))
+    f_fac = COPY_BYTES / (cf * 1024.0)
+    w_fac = COPY_BYTES / (cw * 1024.0)
+    gf = _per_dispatch(fr, "FETCH_SIZE", is_gemm)
+    gw = _per_dispatch(wr, "WRITE_SIZE", is_gemm)
+    fetch = float(np.median(gf)) * 1024.0 * f_fac
+    write = float(np.median(gw)) * 1024.0 * w_fac
+    out = {
+        "kernel": GEMM_KERNEL, "workload": workload, "source_sha256": gemm_source_hash(),
+        "commands": commands,
+        "gemm_dispatches": [len(gf), len(gw)],
+        "gemm_fetch_kib_median": float(np.median(gf)), "gemm_write_kib_median": float(np.median(gw)),
+        "copy_bytes": COPY_BYTES, "copy_fetch_kib": cf, "copy_write_kib": cw,
+        "fetch_factor": f_fac, "write_factor": w_fac,
+        "fetch_bytes": fetch, "write_bytes": write, "traffic_bytes": fetch + write,
+    }
+    path = traffic_path(workload)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+    log(f"wrote {path}")
+
+
+def load_traffic(workload):
+    """Per-launch HBM bytes of the GEMM kernel, or None when no summary exists or
+    the kernel's sources changed since the counters were taken."""
+    try:
+        with open(traffic_path(workload)) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != gemm_source_hash():
+        return None
+    return t
+
+
+# ---------------------------------------------------------------------------
+# oracle baseline
+# ---------------------------------------------------------------------------
 
 def cpu_baseline(inp, cfg, rows):
     """Time the oracle's linear on the first `rows` rows of the workload."""
@@ -74,6 +243,10 @@ def cpu_baseline(inp, cfg, rows):
                       f"oracle preparation (SVD) excluded"}
 
 
+# ---------------------------------------------------------------------------
+# GPU benchmark
+# ---------------------------------------------------------------------------
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -84,7 +257,24 @@ def main():
     ap.add_argument("--rank", type=int, default=None, help="override the SVD rank (0 = bare W4A4)")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows for the oracle timing (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-check", action="store_true",
+                    help="also run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the GEMM traffic summary from two counter runs and exit")
+    ap.add_argument("--commands", default="", help="counter-run commands recorded in the summary")
+    ap.add_argument("--trace-summary", metavar="PROF_DIR",
+                    help="write the kernel-trace summary of a profiled run of this script and exit")
     args = ap.parse_args()
+
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary, args.workload, args.commands)
+        return
+    if args.trace_summary:
+        import workloads
+        cfg = workloads.CONFIGS[args.workload]
+        rank = (cfg.rank + cfg.lora_rank) if args.rank is None else args.rank
+        trace_summary(args.trace_summary, cfg, args, rank)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the layer shards "
@@ -97,79 +287,114 @@ def main():
     import w4a4_rank_corrected_amd as S
 
     cfg = workloads.CONFIGS[args.workload]
-    log(f"bench: workload {cfg.name} b={cfg.rows or cfg.b} m={cfg.m} n={cfg.n}")
-    inp = workloads.make_inputs(cfg)
-    b = inp["x"].shape[0]
     m, n = cfg.m, cfg.n
     rank_svd = cfg.rank if args.rank is None else args.rank
     dev = torch.device("cuda:0")
-    x = torch.from_numpy(inp["x_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
-
-    # calibration statistic on the GPU, then host preparation in the library
-    amax = S.svdq_calibrate_act_amax(x).cpu().numpy()
-    t0 = time.perf_counter()
-    host = S.svdq_prepare_weights(inp["w"], amax, rank_svd)
-    prep_s = time.perf_counter() - t0
-    if cfg.lora_rank and args.rank is None:
-        l1p, l2p = S.svdq_append_lora(host["l1"], host["l2"], m, n, rank_svd, host["lambda"],
-                                      inp["lora_a"], inp["lora_b"], inp["lora_scale"])
-        host = dict(host, l1=l1p, l2=l2p, rank=rank_svd + cfg.lora_rank)
-    r = int(host["rank"])
-    log(f"bench: host preparation {prep_s:.1f} s (rank {r})")
-    layer = S.DeviceLayer(host, device=dev)
-
     out_dtype = torch.bfloat16 if args.out == "bf16" else torch.float32
+
+    def build_set(seed):
+        inp = workloads.make_inputs(cfg, seed=seed)
+        x = torch.from_numpy(inp["x_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+        amax = S.svdq_calibrate_act_amax(x).cpu().numpy()   # calibration statistic on the GPU
+        t0 = time.perf_counter()
+        host = S.svdq_prepare_weights(inp["w"], amax, rank_svd)  # host preparation in the library
+        prep = time.perf_counter() - t0
+        if cfg.lora_rank and args.rank is None:
+            l1p, l2p = S.svdq_append_lora(host["l1"], host["l2"], m, n, rank_svd, host["lambda"],
+                                          inp["lora_a"], inp["lora_b"], inp["lora_scale"])
+            host = dict(host, l1=l1p, l2=l2p, rank=rank_svd + cfg.lora_rank)
+        layer = S.DeviceLayer(host, device=dev)
+        y = torch.empty((x.shape[0], n), dtype=out_dtype, device=dev)
+        return {"inp": inp, "x": x, "layer": layer, "y": y, "prep_s": prep}
+
+    log(f"bench: workload {cfg.name} b={cfg.rows or cfg.b} m={m} n={n}")
+    sets = [build_set(0)]
+    b = sets[0]["x"].shape[0]
+    r = int(sets[0]["layer"].rank)
+    k1_bytes, k2_bytes = algorithmic_bytes(b, m, n, r)
+    per_set, n_sets = set_plan(cfg, r, args.out)
+    for s in range(1, n_sets):
+        sets.append(build_set(s))
+        del sets[-1]["inp"]
+    log(f"bench: {n_sets} input+weight sets of {per_set / 2**20:.0f} MiB, rank {r}, "
+        f"host preparation {sets[0]['prep_s']:.1f} s per set")
+
     G = m // 64
     qx = torch.empty((G, b, 32), dtype=torch.uint8, device=dev)
     asc = torch.empty((G, b), dtype=torch.float16, device=dev)
     z = torch.empty((b, max(r, 1)), dtype=torch.float32, device=dev) if r else None
-    wsz = S.svdq_act_workspace_size(b, m, r)
-    ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=dev)
-    y = torch.empty((b, n), dtype=out_dtype, device=dev)
+    ws = torch.empty(max(S.svdq_act_workspace_size(b, m, r), 1), dtype=torch.uint8, device=dev)
     gws = torch.empty(max(S.svdq_gemm_workspace_size(b, n, m), 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(ev=None):
+    def step(st, layer=None, ev=None):
+        layer = layer or st["layer"]
+        rr = layer.rank
         if ev is not None:
             ev[0].record(stream)
-        S.svdq_quantize_act_lowrank_down(x, layer.smooth_inv, layer.l1, r, qx=qx, ascale=asc, z=z,
-                                         workspace=ws, stream=stream)
+        S.svdq_quantize_act_lowrank_down(st["x"], layer.smooth_inv, layer.l1, rr, qx=qx, ascale=asc,
+                                         z=z if rr else None, workspace=ws, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        S.svdq_gemm_w4a4_lowrank_up(qx, asc, z, layer, b, out_dtype, y=y, workspace=gws, stream=stream)
+        S.svdq_gemm_w4a4_lowrank_up(qx, asc, z if rr else None, layer, b, out_dtype, y=st["y"],
+                                    workspace=gws, stream=stream)
         if ev is not None:
             ev[2].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    # timed region: barrier (single process) + synchronize on both sides
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(events[k])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    k1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    k2_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
-    ms_per_step = elapsed * 1e3 / args.steps
+    def timed(pick, steps, layer_of=None):
+        """Steps bracketed by synchronize on both sides; per-kernel HIP events."""
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            st = pick(k)
+            step(st, layer_of(st) if layer_of else None, evs[k])
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        k1 = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        k2 = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        return wall, k1, k2
 
-    # the same work through the one-call entry point, for reference
+    # warm-up over every set, then the timed (cold, rotating) region
+    for k in range(max(args.warmup, n_sets)):
+        step(sets[k % n_sets])
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} steps rotating over {n_sets} sets")
+    ms_per_step, k1_ms, k2_ms = timed(lambda k: sets[k % n_sets], args.steps)
+
+    # warm: one set, repeated
+    log("bench: warm and rank-0 comparisons")
+    warm_ms, warm_k1, warm_k2 = timed(lambda k: sets[0], args.steps)
+    # the same codes and scales without the low-rank branch
+    l0 = sets[0]["layer"]
+    layer0 = S.DeviceLayer.from_tensors(m, n, 0, l0.qw, l0.wscale, None, None, l0.smooth_inv, l0.bias)
+    for _ in range(3):
+        step(sets[0], layer0)
+    r0_ms, r0_k1, r0_k2 = timed(lambda k: sets[0], args.steps, lambda st: layer0)
+
+    # the one-call entry point (K1 + K2 inside the library), warm
     ws_lin = torch.empty(max(S.svdq_linear_workspace_size(b, m, n, r), 1), dtype=torch.uint8, device=dev)
     for _ in range(3):
-        S.svdq_linear(x, layer, out_dtype, y=y, workspace=ws_lin, stream=stream)
+        S.svdq_linear(sets[0]["x"], l0, out_dtype, y=sets[0]["y"], workspace=ws_lin, stream=stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for _ in range(args.steps):
-        S.svdq_linear(x, layer, out_dtype, y=y, workspace=ws_lin, stream=stream)
+        S.svdq_linear(sets[0]["x"], l0, out_dtype, y=sets[0]["y"], workspace=ws_lin, stream=stream)
     torch.cuda.synchronize()
     linear_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+
+    if args.copy_check:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: copy check of {COPY_BYTES} bytes done")
 
     ops = 2.0 * b * m * n
     value = ops / (ms_per_step * 1e-3) / 1e12
     k2_tops = ops / (k2_ms * 1e-3) / 1e12
-    k1_bytes, k2_bytes = algorithmic_bytes(b, m, n, r)
+    traffic = load_traffic(cfg.name) if args.out == "bf16" and args.rank is None else None
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -184,19 +409,30 @@ def main():
         "dtype": "i8",
         "data": "synthetic",
         "config": {"workload": cfg.name, "b": b, "m": m, "n": n, "rank": r, "group": 64,
-                   "out": args.out, "parallelism": "none (1 GPU)"},
+                   "out": args.out, "parallelism": "none (1 GPU)",
+                   "timing": f"cold: steps rotate over {n_sets} seeded input+weight sets "
+                             f"({n_sets * per_set / 2**20:.0f} MiB)"},
         "roofline": {"bound": "mfma", "achieved": round(k2_tops, 2), "peak": I8_PEAK_TOPS,
-                     "unit": "TOP/s", "frac": round(k2_tops / I8_PEAK_TOPS, 4), "traffic": None},
+                     "unit": "TOP/s", "frac": round(k2_tops / I8_PEAK_TOPS, 4),
+                     "traffic": None if traffic is None else round(traffic["traffic_bytes"])},
         "kernels": {"act_quant_down_ms": round(k1_ms, 5), "gemm_w4a4_up_ms": round(k2_ms, 5),
                     "act_quant_down_GBs": round(k1_bytes / (k1_ms * 1e-3) / 1e9, 1),
                     "act_quant_down_hbm_frac": round(k1_bytes / (k1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                     "gemm_w4a4_up_TOPs": round(k2_tops, 2),
                     "gemm_algorithmic_bytes": k2_bytes, "act_algorithmic_bytes": k1_bytes,
-                    "svdq_linear_ms": round(linear_ms, 5)},
-        "prep_s": round(prep_s, 2),
+                    "gemm_hbm_fetch_bytes": None if traffic is None else round(traffic["fetch_bytes"]),
+                    "gemm_hbm_write_bytes": None if traffic is None else round(traffic["write_bytes"])},
+        "warm": {"ms_per_step": round(warm_ms, 5), "value": round(ops / (warm_ms * 1e-3) / 1e12, 2),
+                 "act_quant_down_ms": round(warm_k1, 5), "gemm_w4a4_up_ms": round(warm_k2, 5),
+                 "svdq_linear_ms": round(linear_ms, 5)},
+        "lowrank_overhead": {"rank": r, "ms_rank_r": round(warm_ms, 5), "ms_rank_0": round(r0_ms, 5),
+                             "overhead": round(warm_ms / r0_ms - 1.0, 4),
+                             "k1_ms_rank_0": round(r0_k1, 5), "k2_ms_rank_0": round(r0_k2, 5)},
+        "prep_s": round(sets[0]["prep_s"], 2),
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inp, cfg, min(args.cpu_rows, b) if args.cpu_rows else b)
+        res["cpu_baseline"] = cpu_baseline(sets[0]["inp"], cfg,
+                                           min(args.cpu_rows, b) if args.cpu_rows else b)
     print(json.dumps(res), flush=True)
 
 
