@@ -33,9 +33,14 @@
 //   records (contiguous in the group-major layout) with buffer loads, unpacks
 //   them once into LDS (double-buffered), and every wave reads its MFMA
 //   operands from there.  Global loads run DEPTH groups ahead in registers.
+//   Measured alternatives that were not faster on gfx950: 256 x 256 and
+//   128 x 256 tiles (register spills or fewer resident waves), 128 x 64 tiles
+//   at three or four waves per SIMD (more staging and LDS traffic per output),
+//   and explicit MFMA/FMA interleaving hints (the two resident workgroups
+//   already interleave).
 //
-// Schedules (tile = TM x TN outputs over all G groups; slots = two resident
-// workgroups per CU):
+// Schedules (tile = TM x TN outputs over all G groups; slots = the resident
+// workgroups of all CUs, two per CU for the configuration below):
 //   * one tile per workgroup, when the tiles fill whole rounds of slots;
 //   * otherwise a hybrid: the tiles of the last one or two rounds are shared
 //     out by stream-K among `slots` persistent workgroups (equal (tile, group)
@@ -52,6 +57,7 @@
 #include <algorithm>
 #include <atomic>
 #include <chrono>
+#include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -154,10 +160,12 @@ struct GemmCfg {
   static constexpr int A_BYTES = TM * 32 / NT;  // packed activation bytes staged per thread per group
   static constexpr int B_BYTES = TN * 32 / NT;  // packed weight bytes staged per thread per group
   static constexpr int ROWB = 64 + 16;          // LDS bytes per unpacked 64-channel row (+16 pad)
+  static constexpr int WG_PER_CU = WPE * 4 / (NT / 64);  // resident workgroups per CU (4 SIMDs)
   static_assert(DEPTH % 2 == 0, "the register ring alternates with the two LDS buffers");
+  static_assert(WG_PER_CU >= 1 && (WPE * 4) % (NT / 64) == 0, "whole workgroups per CU");
   static_assert(A_BYTES == 4 || A_BYTES == 8 || A_BYTES == 16, "activation staging piece");
   static_assert(B_BYTES == 4 || B_BYTES == 8 || B_BYTES == 16, "weight staging piece");
-  static_assert(NT >= TM + TN && TM % 64 == 0 && (TM + TN) % 64 == 0, "scale staging");
+  static_assert(NT >= TM + TN && TM % 64 == 0, "scale staging: at most one scale per thread");
 };
 
 // 128 x 128 tile, 4 waves of 64 x 64; two workgroups share a CU, so one
@@ -189,9 +197,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
   constexpr int BI = C::BI, BJ = C::BJ, ROWB = C::ROWB;
   __shared__ __align__(16) uint8_t As[2][TM * ROWB];
   __shared__ __align__(16) uint8_t Bs[2][TN * ROWB];
-  __shared__ __align__(16) float Sxq[2][TM];  // sx / 256
-  __shared__ __align__(16) float Sng[2][TM];  // -1.5*2^23 * sx / 256
-  __shared__ __align__(16) float Sw[2][TN];
+  // [sx/256 (TM) | -1.5*2^23 sx/256 (TM) | sw (TN) | unused (NT - TM - TN)]
+  __shared__ __align__(16) float Ssc[2][TM + NT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -293,24 +300,23 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
       st.w = buffer_piece<BB>(rb, b_voff);
       st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, s_voff, 0, 0);
     };
+    // Scales go to one LDS array per buffer: [sx/256 (TM) | -1.5*2^23 sx/256
+    // (TM) | sw (TN) | unused].  Thread t < TM stages row i0+t's activation
+    // scale (two words), thread TM+u column j0+u's weight scale (the same word
+    // twice; threads past TM+TN write zeros to the unused tail), so the staging
+    // is straight-line code.
     auto store_stage = [&](int buf, const Stage& st) {
       unpack_piece<AB>(&As[buf][a_row * ROWB], a_w0, st.a);
       unpack_piece<BB>(&Bs[buf][b_col * ROWB], b_w0, st.w);
       const float sv = f16_to_f32((uint16_t)st.s);
-      if (wave_u < TM / 64) {
-        const float q = sv * 0.00390625f;  // sx / 256 (exact)
-        Sxq[buf][tid] = q;
-        Sng[buf][tid] = -kMagic * q;       // exact: 3 * 2^14 * sx
-      } else if (wave_u < (TM + TN) / 64) {
-        Sw[buf][tid - TM] = sv;
-      }
+      const bool act = wave_u < TM / 64;
+      const float q = sv * 0.00390625f;  // sx / 256 (exact)
+      Ssc[buf][act ? tid : TM + tid] = act ? q : sv;
+      Ssc[buf][TM + tid] = act ? -kMagic * q : sv;  // exact: 3 * 2^14 * sx
     };
-    // One group: for each 16-row block bi, BJ MFMAs (one per 16-column block)
-    // and 8*BJ FMAs.  The MFMAs of block bi are issued next to the FMAs of block
-    // bi-1 (software pipeline).  The empty asm statements take the updated
-    // accumulators as operands: they emit nothing but pin each block's FMAs in
-    // place, so the compiler cannot sink them past later MFMAs (which would keep
-    // every MFMA result live at once).
+    // One group.  For each 16-row block bi: BJ MFMAs (one per 16-column
+    // block), whose results are applied by 8 * BJ FMAs one block later, so an
+    // MFMA's latency is covered by the previous block's FMAs.
     auto compute = [&](int buf) {
       u32x4 Pb[BJ];
       f32x4 sw4[BJ];
@@ -318,21 +324,19 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
       for (int bj = 0; bj < BJ; ++bj) {
         const int cc = WN * wn + 16 * bj;
         Pb[bj] = *reinterpret_cast<const u32x4*>(&Bs[buf][(cc + r) * ROWB + 16 * c]);
-        sw4[bj] = *reinterpret_cast<const f32x4*>(&Sw[buf][cc + 4 * c]);
+        sw4[bj] = *reinterpret_cast<const f32x4*>(&Ssc[buf][2 * TM + cc + 4 * c]);
       }
       const int rbase = WM * wm + r;
-      u32x4 Qa = *reinterpret_cast<const u32x4*>(&As[buf][rbase * ROWB + 16 * c]);
       i32x4 d[2][BJ];
       float sxq[2], sng[2];
 #pragma unroll
       for (int bi = 0; bi <= BI; ++bi) {
         const int cur = bi & 1, prev = cur ^ 1;
-        u32x4 Qn = Qa;
         if (bi < BI) {
           const int rr = rbase + 16 * bi;
-          sxq[cur] = Sxq[buf][rr];
-          sng[cur] = Sng[buf][rr];
-          if (bi + 1 < BI) Qn = *reinterpret_cast<const u32x4*>(&As[buf][(rr + 16) * ROWB + 16 * c]);
+          const u32x4 Qa = *reinterpret_cast<const u32x4*>(&As[buf][rr * ROWB + 16 * c]);
+          sxq[cur] = Ssc[buf][rr];
+          sng[cur] = Ssc[buf][TM + rr];
 #pragma unroll
           for (int bj = 0; bj < BJ; ++bj)
             d[cur][bj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
@@ -340,43 +344,45 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
         }
         if (bi > 0) {
 #pragma unroll
-          for (int bj = 0; bj < BJ; ++bj) {
+          for (int bj = 0; bj < BJ; ++bj)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
               const float t = __builtin_fmaf(__int_as_float(d[prev][bj][v]), sxq[prev], sng[prev]);
               acc[bi - 1][bj][v] = __builtin_fmaf(t, sw4[bj][v], acc[bi - 1][bj][v]);
             }
-            asm volatile("" : "+v"(acc[bi - 1][bj]));
-          }
         }
-        Qa = Qn;
       }
     };
 
-    // Pipeline: LDS[k & 1] holds group g0+k while it is computed; a ring of D
-    // register stages holds groups k+1 .. k+D (the later ones still loading).
-    // After computing group k, group k+1 moves from its register slot into the
-    // other LDS buffer and the freed slot starts loading group k+1+D.  Loads
-    // and stores are unconditional (past the end they re-read the last group
-    // into a buffer nobody reads), so no branch sits between a load and its use
-    // and each wait covers exactly one group.  The trailing barrier also makes
-    // the LDS buffers free for the next segment.
-    constexpr int D = C::DEPTH;
-    Stage st[D];
-#pragma unroll
-    for (int k = 0; k < D; ++k) load_stage(k, st[k]);
+    // Pipeline: LDS buffer k & 1 holds group k while it is computed; register
+    // stage (k + 1) & 1 holds group k + 1, and stage k & 1 group k + 2 (still
+    // loading).  A step computes group k, moves group k + 1 from its register
+    // stage into the other LDS buffer, starts loading group k + 3 into the
+    // freed stage, and ends with one barrier.  Loads and stores are
+    // unconditional (past the end they re-read the last group into a buffer
+    // nobody reads), so no branch sits inside a step and each wait covers
+    // exactly one group.  The trailing barrier also frees the LDS buffers for
+    // the next segment.
+    static_assert(C::DEPTH == 2, "two register stages");
+    Stage st[2];
+    load_stage(0, st[0]);
+    load_stage(1, st[1]);
     store_stage(0, st[0]);
-    load_stage(D, st[0]);
+    load_stage(2, st[0]);
     __syncthreads();
-    for (int k0 = 0; k0 < S; k0 += D) {
-#pragma unroll
-      for (int k = 0; k < D; ++k) {
-        if (k0 + k < S) compute(k & 1);
-        store_stage((k + 1) & 1, st[(k + 1) % D]);
-        load_stage(k0 + k + 1 + D, st[(k + 1) % D]);
-        __syncthreads();
-      }
+    auto step = [&](int k, auto BUF) {
+      constexpr int buf = decltype(BUF)::value;
+      compute(buf);
+      store_stage(buf ^ 1, st[buf ^ 1]);
+      load_stage(k + 3, st[buf ^ 1]);
+      __syncthreads();
+    };
+    int k = 0;
+    for (; k + 1 < S; k += 2) {
+      step(k, std::integral_constant<int, 0>{});
+      step(k + 1, std::integral_constant<int, 1>{});
     }
+    if (k < S) step(k, std::integral_constant<int, 0>{});
   };
 
   // ---- epilogue: bias, cast, one store of Y ---------------------------------
@@ -545,8 +551,8 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
 
 }  // namespace
 
-// Plan of the GEMM launch.  With T tiles of G groups and S = 2 * CUs
-// resident slots, one tile per workgroup leaves each slot idle for
+// Plan of the GEMM launch.  With T tiles of G groups and S = CUs * (resident
+// workgroups per CU) slots, one tile per workgroup leaves each slot idle for
 // (ceil(T / S) - T / S) * G group-iterations on average.  When that idle
 // time is at least 16 group-iterations (the measured cost of splitting a
 // tile is a few), the tiles beyond the first floor(T / S) - 1 full rounds
@@ -560,7 +566,7 @@ GemmPlan gemm_plan(int b, int n, int m, int cus) {
   p.tiles_m = (b + Cfg::TM - 1) / Cfg::TM;
   p.tiles_n = (n + Cfg::TN - 1) / Cfg::TN;
   const long long T = (long long)p.tiles_m * p.tiles_n;
-  const long long slots = 2LL * (cus > 0 ? cus : kMaxCUs);
+  const long long slots = (long long)Cfg::WG_PER_CU * (cus > 0 ? cus : kMaxCUs);
   const long long rounds = (T + slots - 1) / slots;
   const double idle = ((double)rounds - (double)T / (double)slots) * p.G;
   p.streamk = idle >= 16.0 && T * p.G >= 16;
@@ -575,7 +581,7 @@ GemmPlan gemm_plan(int b, int n, int m, int cus) {
   } else {
     p.grid = (int)T;
   }
-  const long long max_sk = std::max(1LL, std::min(2LL * kMaxCUs, T * p.G / 8));
+  const long long max_sk = std::max(1LL, std::min((long long)Cfg::WG_PER_CU * kMaxCUs, T * p.G / 8));
   p.partial_bytes = (size_t)max_sk * Cfg::TM * Cfg::TN * 4;
   p.ws_bytes = p.streamk || cus <= 0 ? p.partial_bytes + (size_t)max_sk * 8 : 0;
   return p;
