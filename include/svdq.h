@@ -12,7 +12,8 @@
  *              Inference on Consumer GPUs", section "Nunchaku".
  *
  * Conventions shared by every entry point
- *   - All matrices are row-major; dimensions are int32; b >= 0, m, n >= 1.
+ *   - All matrices are row-major; dimensions are int32; 0 <= b <= SVDQ_MAX_DIM,
+ *     1 <= m, n <= SVDQ_MAX_DIM.
  *   - The quantization group is 64 input channels (argument `group` must be
  *     SVDQ_GROUP) and m must be a multiple of 64 ([Review] sec. 8: INT4 uses
  *     group 64 on both operands with 16-bit scales).
@@ -65,6 +66,9 @@ enum { SVDQ_OUT_BF16 = 0, SVDQ_OUT_F32 = 1 };
 
 #define SVDQ_GROUP 64
 #define SVDQ_MAX_RANK 256
+/* Largest b, m and n accepted (device kernels address a group's records and a
+ * rank block of L1 with 32-bit buffer offsets). */
+#define SVDQ_MAX_DIM (1 << 22)
 
 /*
  * A prepared layer on the device ([Review] sec. 5 Algorithm 1, step 9: the

@@ -132,6 +132,9 @@ ACT_CASES = [
     (33, 320, 33, False, True),
     (16, 4096, 32, True, False),     # many groups per split
     (5, 64, 256, True, False),       # maximum rank
+    (3000, 12288, 48, True, False),  # several LDS chunks per split, odd chunk size
+    (1024, 6144, 200, True, False),  # rank > 128: one group per chunk
+    (2000, 6144, 72, False, False),  # 8 blocks of Z, two groups per chunk
 ]
 
 

@@ -175,6 +175,8 @@ def _layer(**kw):
     (dict(qw=FAKE + 4), B.SVDQ_ERR_ALIGNMENT),
     (dict(l2=None), B.SVDQ_ERR_INVALID_ARG),
     (dict(l1=None), B.SVDQ_ERR_INVALID_ARG),
+    (dict(n=B.SVDQ_MAX_DIM + 1), B.SVDQ_ERR_UNSUPPORTED),
+    (dict(m=B.SVDQ_MAX_DIM + 64), B.SVDQ_ERR_UNSUPPORTED),
 ])
 def test_linear_validation_errors(kw, code):
     L = _lib_or_skip()
@@ -197,6 +199,8 @@ def test_linear_workspace_and_dtype_errors():
     assert L.svdq_linear(None, ctypes.byref(lay), 16, FAKE, 0, FAKE, need, None) == B.SVDQ_ERR_INVALID_ARG
     assert L.svdq_linear(FAKE, None, 16, FAKE, 0, FAKE, need, None) == B.SVDQ_ERR_INVALID_ARG
     assert L.svdq_linear(FAKE, ctypes.byref(lay), -1, FAKE, 0, FAKE, need, None) == B.SVDQ_ERR_INVALID_ARG
+    assert L.svdq_linear(FAKE, ctypes.byref(lay), B.SVDQ_MAX_DIM + 1, FAKE, 0, FAKE, need, None) == \
+        B.SVDQ_ERR_UNSUPPORTED
     # empty batch: valid, nothing to do, no workspace needed
     assert L.svdq_linear(FAKE, ctypes.byref(lay), 0, None, 0, None, 0, None) == B.SVDQ_OK
 

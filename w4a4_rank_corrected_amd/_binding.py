@@ -25,6 +25,7 @@ SVDQ_OUT_BF16 = 0
 SVDQ_OUT_F32 = 1
 SVDQ_GROUP = 64
 SVDQ_MAX_RANK = 256
+SVDQ_MAX_DIM = 1 << 22
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsvdq.so")
 

@@ -23,22 +23,24 @@ void set_error(const char* fmt, ...) {
 }
 void clear_error() { g_err[0] = 0; }
 
-// Split plan of the act-quant kernel: enough workgroups to spread the rows'
-// channel groups over the whole chip (about 1024), never more splits than
-// groups.  Depends only on the shape, so the standalone kernel and the fused
+// Split plan of the act-quant kernel: workgroups of 64 rows, and enough splits
+// of the channel groups to put about 3072 waves on the chip, with at least 3
+// groups per split (each wave loads two groups ahead).  A workgroup stages
+// 1/lambda and L1 in LDS for `chunk` groups at a time (1..6, at most about
+// 40 KB).  Depends only on the shape, so the standalone kernel and the fused
 // layer sum Z in the same order.
 ActPlan act_plan(int b, int m, int rank) {
   ActPlan p;
-  p.strips = (b + 15) / 16;
+  p.strips = (b + 63) / 64;
   const int G = m / SVDQ_GROUP;
-  int splits = 1;
+  int gps = G;
   if (p.strips > 0) {
-    splits = (1024 + p.strips - 1) / p.strips;
-    splits = std::max(1, std::min(splits, std::min(G, 32)));
+    const int splits = std::max(1, (3072 + 4 * p.strips - 1) / (4 * p.strips));
+    gps = std::max((G + splits - 1) / splits, std::min(3, G));
   }
-  if (rank == 0) splits = std::max(1, splits);
-  p.groups_per_split = (G + splits - 1) / splits;
-  p.splits = (G + p.groups_per_split - 1) / p.groups_per_split;
+  p.groups_per_split = gps;
+  p.splits = (G + gps - 1) / gps;
+  p.chunk = std::max(1, std::min(6, 40960 / act_lds_group_bytes(act_blocks(rank))));
   return p;
 }
 
@@ -65,6 +67,7 @@ int check_group(int m, int group) {
   REQUIRE(group == SVDQ_GROUP, SVDQ_ERR_UNSUPPORTED, "group must be %d (got %d)", SVDQ_GROUP, group);
   REQUIRE(m >= SVDQ_GROUP && m % SVDQ_GROUP == 0, SVDQ_ERR_UNSUPPORTED,
           "m must be a positive multiple of %d (got %d)", SVDQ_GROUP, m);
+  REQUIRE(m <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "m must be <= %d (got %d)", SVDQ_MAX_DIM, m);
   return SVDQ_OK;
 }
 
@@ -103,6 +106,7 @@ int check_layer(const svdq_layer* L) {
   int st = check_group(L->m, L->group);
   if (st) return st;
   REQUIRE(L->n >= 1, SVDQ_ERR_INVALID_ARG, "n must be >= 1 (got %d)", L->n);
+  REQUIRE(L->n <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "n must be <= %d (got %d)", SVDQ_MAX_DIM, L->n);
   REQUIRE(L->rank >= 0 && L->rank <= SVDQ_MAX_RANK, SVDQ_ERR_UNSUPPORTED,
           "rank must be in [0, %d] (got %d)", SVDQ_MAX_RANK, L->rank);
   REQUIRE(L->qw && L->wscale, SVDQ_ERR_INVALID_ARG, "layer qw / wscale must not be NULL");
@@ -160,6 +164,7 @@ int svdq_quantize_residual(const float* R, int m, int n, int group, uint8_t* qw,
   int st = check_group(m, group);
   if (st) return st;
   REQUIRE(n >= 1, SVDQ_ERR_INVALID_ARG, "n must be >= 1 (got %d)", n);
+  REQUIRE(n <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "n must be <= %d (got %d)", SVDQ_MAX_DIM, n);
   REQUIRE(R && qw && wscale, SVDQ_ERR_INVALID_ARG, "R, qw and wscale must not be NULL");
   REQUIRE(all_finite(R, (size_t)m * n), SVDQ_ERR_NONFINITE, "R holds NaN or Inf");
   quantize_residual(R, m, n, qw, wscale);
@@ -173,6 +178,7 @@ int svdq_prepare_weights(const float* W, const float* act_amax, int m, int n, in
   int st = check_group(m, group);
   if (st) return st;
   REQUIRE(n >= 1, SVDQ_ERR_INVALID_ARG, "n must be >= 1 (got %d)", n);
+  REQUIRE(n <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "n must be <= %d (got %d)", SVDQ_MAX_DIM, n);
   REQUIRE(W && qw && wscale && lambda && smooth_inv, SVDQ_ERR_INVALID_ARG,
           "W, qw, wscale, lambda and smooth_inv must not be NULL");
   REQUIRE(rank >= 0 && rank <= SVDQ_MAX_RANK, SVDQ_ERR_UNSUPPORTED, "rank must be in [0, %d] (got %d)",
@@ -243,6 +249,7 @@ int svdq_append_lora(const uint16_t* l1, const uint16_t* l2, int m, int n, int r
                      uint16_t* l1_out, uint16_t* l2_out) {
   clear_error();
   REQUIRE(m >= 1 && n >= 1, SVDQ_ERR_INVALID_ARG, "m, n must be >= 1");
+  REQUIRE(m <= SVDQ_MAX_DIM && n <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "m, n must be <= %d", SVDQ_MAX_DIM);
   REQUIRE(k >= 1, SVDQ_ERR_INVALID_ARG, "adapter rank k must be >= 1 (got %d)", k);
   REQUIRE(rank >= 0 && rank + k <= SVDQ_MAX_RANK, SVDQ_ERR_UNSUPPORTED,
           "rank + k must be <= %d (got %d + %d)", SVDQ_MAX_RANK, rank, k);
@@ -276,6 +283,7 @@ int svdq_calibrate_act_amax(const uint16_t* x, int b, int m, float* amax, int ac
                             void* stream) {
   clear_error();
   REQUIRE(b >= 0 && m >= 1, SVDQ_ERR_INVALID_ARG, "need b >= 0 and m >= 1 (got b=%d m=%d)", b, m);
+  REQUIRE(b <= SVDQ_MAX_DIM && m <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "b and m must be <= %d", SVDQ_MAX_DIM);
   REQUIRE(m % 8 == 0, SVDQ_ERR_UNSUPPORTED, "m must be a multiple of 8 (got %d)", m);
   REQUIRE(amax != nullptr, SVDQ_ERR_INVALID_ARG, "amax must not be NULL");
   REQUIRE(((uintptr_t)amax & 3u) == 0, SVDQ_ERR_ALIGNMENT, "amax must be 4-byte aligned");
@@ -301,6 +309,7 @@ int svdq_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int rank, in
   int st = check_group(m, group);
   if (st) return st;
   REQUIRE(b >= 0, SVDQ_ERR_INVALID_ARG, "b must be >= 0 (got %d)", b);
+  REQUIRE(b <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "b must be <= %d (got %d)", SVDQ_MAX_DIM, b);
   REQUIRE(rank >= 0 && rank <= SVDQ_MAX_RANK, SVDQ_ERR_UNSUPPORTED, "rank must be in [0, %d] (got %d)",
           SVDQ_MAX_RANK, rank);
   if (b == 0) return SVDQ_OK;
@@ -341,6 +350,7 @@ int svdq_gemm_w4a4_lowrank_up(const uint8_t* qx, const uint16_t* ascale, const f
   int st = check_layer(layer);
   if (st) return st;
   REQUIRE(b >= 0, SVDQ_ERR_INVALID_ARG, "b must be >= 0 (got %d)", b);
+  REQUIRE(b <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "b must be <= %d (got %d)", SVDQ_MAX_DIM, b);
   st = check_y(y, y_dtype, b);
   if (st) return st;
   if (b == 0) return SVDQ_OK;
@@ -374,6 +384,7 @@ int svdq_linear(const uint16_t* x, const svdq_layer* layer, int b, void* y, int 
   int st = check_layer(layer);
   if (st) return st;
   REQUIRE(b >= 0, SVDQ_ERR_INVALID_ARG, "b must be >= 0 (got %d)", b);
+  REQUIRE(b <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "b must be <= %d (got %d)", SVDQ_MAX_DIM, b);
   st = check_y(y, y_dtype, b);
   if (st) return st;
   if (b == 0) return SVDQ_OK;

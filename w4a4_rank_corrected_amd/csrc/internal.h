@@ -32,13 +32,25 @@ void quantize_residual(const float* R, int m, int n, uint8_t* qw, uint16_t* wsca
 int host_threads();
 
 // ---- device launch plan --------------------------------------------------------
-// The act-quant kernel covers the rows in strips of 16 and may split the channel
-// groups of a strip over `splits` workgroups; each split writes its own partial
-// Z, summed in split order afterwards (deterministic).
+// The act-quant kernel covers the rows in blocks of 64 (one 16-row strip per
+// wave) and may split the channel groups of a block over `splits` workgroups;
+// each split writes its own partial Z, summed in split order afterwards
+// (deterministic).
+// 16-column blocks of Z compiled for a rank (0, 1, 2, 3, 4, 8 or 16), and the
+// LDS bytes one channel group takes in the act-quant kernel: 1/lambda (64 fp32)
+// and 16 * blocks rows of L1 at a pitch of 72 bf16 (144 B, so the MFMA operand
+// reads of 16 consecutive rows hit distinct banks).
+constexpr int kActL1Pitch = 72;
+constexpr int act_blocks(int rank) {
+  return (rank + 15) / 16 <= 4 ? (rank + 15) / 16 : ((rank + 15) / 16 <= 8 ? 8 : 16);
+}
+constexpr int act_lds_group_bytes(int blocks) { return 256 + blocks * 16 * kActL1Pitch * 2; }
+
 struct ActPlan {
-  int strips;            // ceil(b / 16)
+  int strips;            // ceil(b / 64) row blocks
   int splits;            // workgroups per strip along the channel groups
   int groups_per_split;  // channel groups handled by one workgroup
+  int chunk;             // groups staged in LDS at a time
 };
 ActPlan act_plan(int b, int m, int rank);
 
