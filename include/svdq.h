@@ -148,8 +148,11 @@ int svdq_append_lora(const uint16_t* l1, const uint16_t* l2, int m, int n, int r
 int svdq_calibrate_act_amax(const uint16_t* x, int b, int m, float* amax, int accumulate,
                             void* stream);
 
-/* Bytes of scratch svdq_quantize_act_lowrank_down needs for split-channel
- * partial sums of Z (0 when the split count for this shape is 1). */
+/* Bytes of device workspace svdq_quantize_act_lowrank_down needs when it
+ * splits the channel groups of a row block over several workgroups: the
+ * partial sums of Z, added in split order by a second kernel (0 when no
+ * split is needed).  The contents need no initialisation; calls that overlap
+ * in time must not share it. */
 size_t svdq_act_workspace_size(int b, int m, int rank);
 
 /* DEVICE: fused activation quantization + low-rank down-projection

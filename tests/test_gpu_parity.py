@@ -164,6 +164,36 @@ def test_act_quant_down_parity(S, b, m, rank, smooth, adv):
 # fused W4A4 GEMM + up-projection
 # ---------------------------------------------------------------------------
 
+def test_act_workspace_garbage_and_reuse(S):
+    """Split partial sums of Z live in the caller's workspace: random initial
+    contents, two shapes in turn on one workspace, and a repeated call must all
+    give the oracle's codes and the same Z."""
+    shapes = [(300, 2048, 24), (90, 4096, 40)]
+    need = max(S.svdq_act_workspace_size(b, m, r) for b, m, r in shapes)
+    assert need > 0
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda")
+    runs = {}
+    for rep in range(2):
+        for (b, m, rank) in shapes:
+            _say(f"act workspace reuse rep={rep} b={b} m={m} rank={rank}")
+            xb = workloads.random_bf16_bits(np.random.default_rng(b + m), (b, m), 2.0)
+            x = LY.bf16_bits_to_f32(xb)
+            l1 = O.bf16_from_f32((np.random.default_rng(rank).standard_normal((m, rank)) / np.sqrt(m))
+                                 .astype(np.float32))
+            xt, qx, sx = O.quantize_activation(x, None)
+            qd, asd, zd = S.svdq_quantize_act_lowrank_down(
+                dev_bf16(xb), None, dev_bf16(np.ascontiguousarray(LY.f32_to_bf16_bits(l1).T)), rank,
+                workspace=ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(LY.unpack_codes(qd.cpu().numpy()), qx)
+            zc = zd.cpu().numpy()
+            assert rel(zc, O.lowrank_down(xt, l1)) <= Z_TOL
+            if rep == 0:
+                runs[(b, m)] = zc
+            else:
+                assert np.array_equal(runs[(b, m)], zc)
+
+
 def _oracle_layer(rng, m, n, rank, x32):
     w = (rng.standard_normal((m, n)) / np.sqrt(m)).astype(np.float32)
     w[rng.choice(m, max(1, m // 64), replace=False)] *= 8

@@ -55,9 +55,9 @@ __global__ __launch_bounds__(256) void calibrate_kernel(const uint16_t* __restri
 //
 // Workgroup = 4 waves over 64 rows (one 16-row strip per wave) and a
 // contiguous range of gps channel groups (one split), walked in chunks of
-// `chunk` groups (1..6, at most about 40 KB of LDS): the workgroup stages a chunk's 1/lambda and L1 slices in LDS
+// `chunk` groups (at most about 40 KB of LDS): the workgroup stages a chunk's 1/lambda and L1 slices in LDS
 // (shared by the four waves), then each wave processes the chunk for its strip.
-// Activations stream through registers two groups ahead, across chunk
+// Activations stream through a register ring D groups ahead, across chunk
 // boundaries, and each wave owns its rows' Z (no cross-wave reduction).  In one wave, lane l owns row (l & 15) and, in each 64-channel
 // group, channels 8c..8c+7 and 32+8c..32+8c+7 with c = l >> 4: exactly the
 // bf16 MFMA A-operand layout, so the smoothed bf16 tile feeds both the
@@ -77,14 +77,17 @@ __global__ __launch_bounds__(256) void calibrate_kernel(const uint16_t* __restri
 // ---------------------------------------------------------------------------
 constexpr int kL1Pitch = kActL1Pitch;  // dynamic LDS: gps groups of act_lds_group_bytes(TB)
 
-template <int TB>  // 16-column blocks of Z (rank <= 16 * TB); 0 = no low-rank branch
+// TB: 16-column blocks of Z (rank <= 16 * TB; 0 = no low-rank branch);
+// SMOOTH: multiply by 1/lambda (inv != nullptr).
+template <int TB, bool SMOOTH>
 __global__ __launch_bounds__(256) void act_quant_down_kernel(
     const uint16_t* __restrict__ x, int b, int m, int G, const float* __restrict__ inv,
     const uint16_t* __restrict__ l1t, int rank, uint8_t* __restrict__ qx,
-    uint16_t* __restrict__ ascale, float* __restrict__ zout, int gps, int chunk) {
+    uint16_t* __restrict__ ascale, float* __restrict__ zout, int gps) {
   constexpr int NB = TB > 0 ? TB : 1;
   constexpr int GB = act_lds_group_bytes(TB);
-  extern __shared__ __align__(16) uint8_t lds[];
+  constexpr int chunk = act_chunk(TB);
+  __shared__ __align__(16) uint8_t lds[chunk * GB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -94,41 +97,58 @@ __global__ __launch_bounds__(256) void act_quant_down_kernel(
   const int g_end = min(G, g_begin + gps);
   const int ng = g_end - g_begin;
 
-  // stage 1/lambda and the L1 slices of groups [cb, ce) in LDS
+  // stage 1/lambda and the L1 slices of groups [cb, ce) in LDS: every thread
+  // issues all of its loads before writing any of them
   auto stage = [&](int cb, int ce) {
     const int n = ce - cb;
-    const __amdgpu_buffer_rsrc_t ri =
-        make_rsrc(inv ? inv + (size_t)cb * 64 : nullptr, inv ? (uint32_t)n * 256u : 0u);
-    for (int k = tid; k < n * 16; k += 256) {  // 16 chunks of 16 B per group
-      const int j = k >> 4, q = k & 15;
-      *reinterpret_cast<u32x4*>(lds + j * GB + 16 * q) =
-          __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ri, (uint32_t)(j * 256 + 16 * q), 0, 0));
+    if constexpr (SMOOTH) {
+      static_assert(chunk * 16 <= 256, "one 1/lambda piece per thread");
+      const __amdgpu_buffer_rsrc_t ri = make_rsrc(inv + (size_t)cb * 64, (uint32_t)n * 256u);
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ri, (uint32_t)tid * 16u, 0, 0));
+      if (tid < chunk * 16) *reinterpret_cast<u32x4*>(lds + (tid >> 4) * GB + 16 * (tid & 15)) = v;
     }
     if constexpr (TB > 0) {
-      // L1 rows t < 16 TB (zero beyond rank), 8 chunks of 16 B per (group, t)
+      // L1 rows t < 16 TB (zero beyond rank), 8 pieces of 16 B per (group, t)
+      constexpr int P = (chunk * TB * 16 * 8 + 255) / 256;
       const __amdgpu_buffer_rsrc_t rl =
           make_rsrc(l1t + (size_t)cb * 64, (uint32_t)((rank - 1) * m + n * 64) * 2u);
-      for (int k = tid; k < n * TB * 16 * 8; k += 256) {
+      u32x4 v[P];
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const int k = tid + 256 * i;
         const int q = k & 7, t = (k >> 3) % (TB * 16), j = (k >> 3) / (TB * 16);
-        const uint32_t off = t < rank ? (uint32_t)(t * m + j * 64 + 8 * q) * 2u : 0xFFFFFFF0u;
-        *reinterpret_cast<u32x4*>(lds + j * GB + 256 + (t * kL1Pitch + 8 * q) * 2) =
-            __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, off, 0, 0));
+        const uint32_t off = (t < rank && j < n) ? (uint32_t)(t * m + j * 64 + 8 * q) * 2u : 0xFFFFFFF0u;
+        v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, off, 0, 0));
+      }
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const int k = tid + 256 * i;
+        const int q = k & 7, t = (k >> 3) % (TB * 16), j = (k >> 3) / (TB * 16);
+        if (k < chunk * TB * 16 * 8)
+          *reinterpret_cast<u32x4*>(lds + j * GB + 256 + (t * kL1Pitch + 8 * q) * 2) = v[i];
       }
     }
   };
 
-  // this wave's strip (a wave past the end still takes part in the barriers)
+  // this wave's strip; a wave past the end only helps stage and takes part in
+  // the barriers
   const int row0 = blockIdx.x * 64 + wave * 16;
-  const bool strip_live = row0 < b;
+  if (row0 >= b) {
+    for (int cb = g_begin; cb < g_end; cb += chunk) {
+      __syncthreads();
+      stage(cb, min(cb + chunk, g_end));
+      __syncthreads();
+    }
+    return;
+  }
   const int row = row0 + r;
-  const bool valid = row < b;
-  const int rows_here = strip_live ? min(16, b - row0) : 1;
+  const int rows_here = min(16, b - row0);
   const uint32_t x_bytes = (uint32_t)((rows_here - 1) * m + 64) * 2u;  // per group, from its base
   const uint32_t x_off = (uint32_t)(r * m + 8 * c) * 2u;              // + 64 for channels 32+8c..
   auto load_x = [&](int g, u32x4& xa, u32x4& xb) {
-    const bool live = g < g_end && strip_live;
+    const bool live = g < g_end;
     const __amdgpu_buffer_rsrc_t rx =
-        make_rsrc(x + (size_t)(live ? row0 : 0) * m + (size_t)(live ? g : 0) * 64, live ? x_bytes : 0u);
+        make_rsrc(x + (size_t)row0 * m + (size_t)(live ? g : g_begin) * 64, live ? x_bytes : 0u);
     xa = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, x_off, 0, 0));
     xb = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, x_off + 64u, 0, 0));
   };
@@ -137,8 +157,12 @@ __global__ __launch_bounds__(256) void act_quant_down_kernel(
 #pragma unroll
   for (int t = 0; t < NB; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // code records and scales of group g are written through descriptors that
+  // end at row b, so stores of rows >= b (and of lanes c != 0 for the scale)
+  // are dropped by the hardware range check: straight-line code per group
+  const uint32_t q_off = (uint32_t)row * 32u + 4u * c;
+  const uint32_t s_off = c == 0 ? (uint32_t)row * 2u : 0xFFFFFFF0u;
   auto process = [&](int g, int j, const u32x4& xa, const u32x4& xb) {
-    if (!strip_live) return;
     const uint8_t* gl = lds + j * GB;
     float v[16];
 #pragma unroll
@@ -148,7 +172,7 @@ __global__ __launch_bounds__(256) void act_quant_down_kernel(
       v[8 + 2 * e] = bf16_lo(xb[e]);
       v[8 + 2 * e + 1] = bf16_hi(xb[e]);
     }
-    if (inv) {
+    if constexpr (SMOOTH) {
       const float* iv = reinterpret_cast<const float*>(gl);
       const f32x4 i0 = *reinterpret_cast<const f32x4*>(iv + 8 * c);
       const f32x4 i1 = *reinterpret_cast<const f32x4*>(iv + 8 * c + 4);
@@ -192,12 +216,11 @@ __global__ __launch_bounds__(256) void act_quant_down_kernel(
       else
         w1 |= nib << (4 * (e - 8));
     }
-    if (valid) {
-      uint8_t* rec = qx + ((size_t)g * b + row) * 32;
-      *reinterpret_cast<uint32_t*>(rec + 4 * c) = w0;
-      *reinterpret_cast<uint32_t*>(rec + 16 + 4 * c) = w1;
-      if (c == 0) ascale[(size_t)g * b + row] = __builtin_bit_cast(uint16_t, s16);
-    }
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qx + (size_t)g * b * 32, (uint32_t)b * 32u);
+    __builtin_amdgcn_raw_buffer_store_b32(w0, rq, q_off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(w1, rq, q_off + 16u, 0, 0);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(ascale + (size_t)g * b, (uint32_t)b * 2u);
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, s16), rs, s_off, 0, 0);
     if constexpr (TB > 0) {
       const bf16x8 a0 = __builtin_bit_cast(bf16x8, u32x4{xt[0], xt[1], xt[2], xt[3]});
       const bf16x8 a1 = __builtin_bit_cast(bf16x8, u32x4{xt[4], xt[5], xt[6], xt[7]});
@@ -212,34 +235,30 @@ __global__ __launch_bounds__(256) void act_quant_down_kernel(
     }
   };
 
-  // x two groups ahead: register stage 0 holds the even groups of the split
-  // (counted from g_begin), stage 1 the odd ones
-  u32x4 xa[2], xb[2];
-  load_x(g_begin, xa[0], xb[0]);
-  load_x(g_begin + 1, xa[1], xb[1]);
+  // x D groups ahead in a register ring: slot u holds the groups g with
+  // (g - g_begin) % D == u.  chunk is a multiple of D, so every chunk starts
+  // at slot 0 and only the split's last chunk ends early.
+  constexpr int D = act_depth(TB);
+  u32x4 xa[D], xb[D];
+#pragma unroll
+  for (int u = 0; u < D; ++u) load_x(g_begin + u, xa[u], xb[u]);
   for (int cb = g_begin; cb < g_end; cb += chunk) {
     const int ce = min(cb + chunk, g_end);
     __syncthreads();  // every wave is done with the previous chunk
     stage(cb, ce);
     __syncthreads();
     int g = cb;
-    if ((g - g_begin) & 1) {  // an odd-sized chunk left the next group odd
-      process(g, 0, xa[1], xb[1]);
-      load_x(g + 2, xa[1], xb[1]);
-      ++g;
+    for (; g + D <= ce; g += D) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        process(g + u, g + u - cb, xa[u], xb[u]);
+        load_x(g + u + D, xa[u], xb[u]);
+      }
     }
-    for (; g + 1 < ce; g += 2) {
-      process(g, g - cb, xa[0], xb[0]);
-      load_x(g + 2, xa[0], xb[0]);
-      process(g + 1, g + 1 - cb, xa[1], xb[1]);
-      load_x(g + 3, xa[1], xb[1]);
-    }
-    if (g < ce) {
-      process(g, g - cb, xa[0], xb[0]);
-      load_x(g + 2, xa[0], xb[0]);
-    }
+#pragma unroll
+    for (int u = 0; u + 1 < D; ++u)
+      if (g + u < ce) process(g + u, g + u - cb, xa[u], xb[u]);
   }
-  if (!strip_live) return;
 
   if constexpr (TB > 0) {
     // this split's Z for the strip (MFMA D layout: row 4c+v, column l & 15)
@@ -303,10 +322,15 @@ int launch_act_quant_down(const uint16_t* x, int b, int m, int rank, const float
   const int G = m / 64;
   dim3 grid(plan.strips, plan.splits);
   const int tb = act_blocks(rank);
-#define SVDQ_ACT(TBV)                                                                            \
-  hipLaunchKernelGGL(act_quant_down_kernel<TBV>, grid, dim3(256),                                \
-                     (size_t)plan.chunk * act_lds_group_bytes(TBV), st, x, b, m, G, smooth_inv,   \
-                     l1, rank, qx, ascale, zpart, plan.groups_per_split, plan.chunk)
+#define SVDQ_ACT(TBV)                                                                              \
+  do {                                                                                             \
+    if (smooth_inv)                                                                                \
+      hipLaunchKernelGGL((act_quant_down_kernel<TBV, true>), grid, dim3(256), 0, st, x, b, m, G,   \
+                         smooth_inv, l1, rank, qx, ascale, zpart, plan.groups_per_split);          \
+    else                                                                                           \
+      hipLaunchKernelGGL((act_quant_down_kernel<TBV, false>), grid, dim3(256), 0, st, x, b, m, G,  \
+                         smooth_inv, l1, rank, qx, ascale, zpart, plan.groups_per_split);          \
+  } while (0)
   if (tb == 0)
     SVDQ_ACT(0);
   else if (tb == 1)

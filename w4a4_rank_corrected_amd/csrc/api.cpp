@@ -4,6 +4,8 @@
 // preparation code (prep.cpp) or the HIP kernel launchers.
 #include <algorithm>
 #include <cmath>
+#include <atomic>
+#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -23,11 +25,29 @@ void set_error(const char* fmt, ...) {
 }
 void clear_error() { g_err[0] = 0; }
 
+namespace {
+std::atomic<unsigned long long> g_launch_counter{0};
+}  // namespace
+
+unsigned long long next_launch_epoch() {
+  // per-process base from time and address entropy (splitmix64 finaliser)
+  static const unsigned long long base = [] {
+    const unsigned long long t =
+        (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+    const unsigned long long a = (unsigned long long)(uintptr_t)&g_launch_counter;
+    unsigned long long x = t ^ (a << 17) ^ 0x9E3779B97F4A7C15ull;
+    x ^= x >> 31;
+    x *= 0xBF58476D1CE4E5B9ull;
+    x ^= x >> 29;
+    return x | 1ull;
+  }();
+  return base + g_launch_counter.fetch_add(1);
+}
+
 // Split plan of the act-quant kernel: workgroups of 64 rows, and enough splits
 // of the channel groups to put about 3072 waves on the chip, with at least 3
-// groups per split (each wave loads two groups ahead).  A workgroup stages
-// 1/lambda and L1 in LDS for `chunk` groups at a time (1..6, at most about
-// 40 KB).  Depends only on the shape, so the standalone kernel and the fused
+// groups per split (the kernel stages 1/lambda and L1 in LDS act_chunk groups
+// at a time).  Depends only on the shape, so the standalone kernel and the fused
 // layer sum Z in the same order.
 ActPlan act_plan(int b, int m, int rank) {
   ActPlan p;
@@ -40,7 +60,7 @@ ActPlan act_plan(int b, int m, int rank) {
   }
   p.groups_per_split = gps;
   p.splits = (G + gps - 1) / gps;
-  p.chunk = std::max(1, std::min(6, 40960 / act_lds_group_bytes(act_blocks(rank))));
+  (void)rank;
   return p;
 }
 

@@ -55,8 +55,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
-#include <chrono>
 #include <type_traits>
 
 #include "device_common.h"
@@ -512,25 +510,6 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
 }
 
 int g_num_cus = 0;
-std::atomic<unsigned long long> g_epoch_counter{0};  // one sequence for every launch
-
-// Base of the stream-K publication epochs: distinct per process (time and
-// address entropy), so flags left in reused memory by another process never
-// match an epoch of this one.
-unsigned long long epoch_base() {
-  static const unsigned long long base = [] {
-    const unsigned long long t =
-        (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
-    const unsigned long long a = (unsigned long long)(uintptr_t)&g_num_cus;
-    unsigned long long x = t ^ (a << 17) ^ 0x9E3779B97F4A7C15ull;
-    x ^= x >> 31;
-    x *= 0xBF58476D1CE4E5B9ull;
-    x ^= x >> 29;
-    return (x | 1ull) << 20;  // low bits left for the per-launch counter
-  }();
-  return base;
-}
-
 template <bool OUT_BF16>
 int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, const svdq_layer& L, int b,
                  void* y, const GemmPlan& plan, void* ws, hipStream_t st) {
@@ -541,7 +520,7 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
     sk.U = (long long)plan.sk_tiles * plan.G;
     sk.partials = reinterpret_cast<float*>(ws);
     sk.flags = reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(ws) + plan.partial_bytes);
-    sk.epoch = epoch_base() + g_epoch_counter.fetch_add(1);
+    sk.epoch = next_launch_epoch();
   }
   hipLaunchKernelGGL((gemm_w4a4_up_kernel<Cfg, OUT_BF16>), dim3((unsigned)plan.grid), dim3(Cfg::NT), 0, st,
                      qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,

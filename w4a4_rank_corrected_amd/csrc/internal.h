@@ -45,12 +45,24 @@ constexpr int act_blocks(int rank) {
   return (rank + 15) / 16 <= 4 ? (rank + 15) / 16 : ((rank + 15) / 16 <= 8 ? 8 : 16);
 }
 constexpr int act_lds_group_bytes(int blocks) { return 256 + blocks * 16 * kActL1Pitch * 2; }
+// Groups of activations each wave keeps in flight (a register ring), by the
+// number of Z blocks: deeper for the light kernels.
+constexpr int act_depth(int blocks) { return blocks <= 4 ? 4 : (blocks == 8 ? 2 : 1); }
+// Groups staged in LDS at a time: the most (a multiple of the depth, at most
+// 8) that fit in about 40 KB.
+constexpr int act_chunk_fit(int blocks) {
+  return 40960 / act_lds_group_bytes(blocks) < 8 ? 40960 / act_lds_group_bytes(blocks) : 8;
+}
+constexpr int act_chunk(int blocks) {
+  return act_chunk_fit(blocks) - act_chunk_fit(blocks) % act_depth(blocks) > 0
+             ? act_chunk_fit(blocks) - act_chunk_fit(blocks) % act_depth(blocks)
+             : act_depth(blocks);
+}
 
 struct ActPlan {
   int strips;            // ceil(b / 64) row blocks
   int splits;            // workgroups per strip along the channel groups
   int groups_per_split;  // channel groups handled by one workgroup
-  int chunk;             // groups staged in LDS at a time
 };
 ActPlan act_plan(int b, int m, int rank);
 
@@ -60,6 +72,11 @@ int launch_act_quant_down(const uint16_t* x, int b, int m, int rank, const float
                           const uint16_t* l1, uint8_t* qx, uint16_t* ascale, float* zpart,
                           const ActPlan& plan, void* stream);
 int launch_z_reduce(const float* zpart, int splits, int b, int rank, float* z, void* stream);
+// A fresh value per kernel launch in this process (64-bit, starting at a
+// random per-process base): tags the publication flags that kernels keep in
+// caller workspaces, so values left there by earlier launches or other
+// processes never match.
+unsigned long long next_launch_epoch();
 // GEMM launch plan (gemm_kernels.hip): one tile per workgroup, or stream-K
 // over a persistent grid with fp32 partials and publication flags in the
 // workspace.
