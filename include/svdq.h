@@ -215,6 +215,21 @@ const char* svdq_last_error(void);
 /* ABI version of this header (major * 100 + minor). */
 int svdq_abi_version(void);
 
+/* DEVICE: the same layer WITHOUT the Nunchaku fusion, for measuring what the
+ * fusion saves ([Review] sec. 6.1: a separate down-projection reads X again
+ * and a separate up-projection writes a second b x n output that must be
+ * added; [Nunchaku]: the two fused kernel pairs).  Five launches on `stream`:
+ * activation quantization alone, the W4A4 product (+ bias) into y, the
+ * down-projection alone (x read again), the up-projection alone into a b x n
+ * tensor of y's type in the workspace, and y += that tensor.  The result is
+ * the same layer as svdq_linear up to rounding: the two partial outputs are
+ * each rounded to y_dtype before the addition.  Arguments as svdq_linear; y
+ * must be 16-byte aligned; workspace >= svdq_linear_unfused_workspace_size(...)
+ * bytes, 256-byte aligned, not shared by calls that overlap in time. */
+size_t svdq_linear_unfused_workspace_size(int b, int m, int n, int rank, int group);
+int svdq_linear_unfused(const uint16_t* x, const svdq_layer* layer, int b, void* y, int y_dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

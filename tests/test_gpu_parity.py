@@ -356,12 +356,70 @@ def test_streamk_splits_deterministic_and_match_oracle(S, b, m, n):
     assert err <= 1e-4
 
 
+# the unfused path rounds the W4A4 product, the up-projection and their sum
+# to bf16 (three roundings of at most 2^-9 relative each, ~1.7e-3 Frobenius
+# apiece on these layers), so its bf16 bar is 4e-3; fp32 output keeps 1e-4
+UNFUSED_BF16_TOL = 4e-3
+
+
+@pytest.mark.parametrize("name", [c[0] for c in LINEAR_CASES])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_linear_unfused_parity(S, name, out):
+    """Without the fusion (separate down- and up-projection kernels, a second
+    b x n output and an addition) the layer is the same up to rounding."""
+    _say(f"linear unfused {name} out={out}")
+    xb, x, lay = _linear_case(name)
+    rng = np.random.default_rng(5)
+    n = lay["qw"].shape[1]
+    bias_v = O.bf16_from_f32(rng.standard_normal(n).astype(np.float32) * 0.1)
+    ref = O.linear(x, lay, bias=bias_v)
+    dl = device_layer(S, lay, LY.f32_to_bf16_bits(bias_v))
+    y = S.svdq_linear_unfused(dev_bf16(xb), dl, torch.float32 if out == "f32" else torch.bfloat16)
+    torch.cuda.synchronize()
+    err = rel(y_to_np(y), ref["y"])
+    _say(f"  rel err {err:.3e}")
+    assert err <= (1e-4 if out == "f32" else UNFUSED_BF16_TOL)
+
+
+@pytest.mark.parametrize("b,m,n,rank", [(300, 2368, 200, 16), (130, 4096, 96, 48)])
+def test_linear_unfused_split_shapes(S, b, m, n, rank):
+    """Shapes whose channel groups are split for the down-projection."""
+    _say(f"linear unfused b={b} m={m} n={n} rank={rank}")
+    rng = np.random.default_rng(b + rank)
+    xb = workloads.random_bf16_bits(rng, (b, m), 1.5)
+    x = LY.bf16_bits_to_f32(xb)
+    lay = _oracle_layer(rng, m, n, rank, x)
+    ref = O.linear(x, lay)["y"]
+    dl = device_layer(S, lay)
+    xd = dev_bf16(xb)
+    yu = S.svdq_linear_unfused(xd, dl, torch.float32)
+    yf = S.svdq_linear(xd, dl, torch.float32)
+    torch.cuda.synchronize()
+    assert rel(yu.cpu().numpy(), ref) <= 1e-4
+    assert rel(yu.cpu().numpy(), yf.cpu().numpy()) <= 1e-5
+
+
+def test_linear_unfused_rank0_is_the_fused_path(S):
+    """At rank 0 both routes launch the same two kernels: identical bits."""
+    rng = np.random.default_rng(3)
+    xb = workloads.random_bf16_bits(rng, (77, 512), 1.5)
+    x = LY.bf16_bits_to_f32(xb)
+    lay = _oracle_layer(rng, 512, 136, 0, x)
+    dl = device_layer(S, lay)
+    xd = dev_bf16(xb)
+    yu = S.svdq_linear_unfused(xd, dl, torch.bfloat16)
+    yf = S.svdq_linear(xd, dl, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(yu, yf)
+
+
 def test_linear_empty_batch(S):
     xb, x, lay = _linear_case("tiny")
     dl = device_layer(S, lay)
-    y = S.svdq_linear(torch.empty((0, 256), dtype=torch.bfloat16, device="cuda"), dl)
-    torch.cuda.synchronize()
-    assert y.shape == (0, 256)
+    for f in (S.svdq_linear, S.svdq_linear_unfused):
+        y = f(torch.empty((0, 256), dtype=torch.bfloat16, device="cuda"), dl)
+        torch.cuda.synchronize()
+        assert y.shape == (0, 256)
 
 
 # ---------------------------------------------------------------------------

@@ -205,6 +205,20 @@ def test_linear_workspace_and_dtype_errors():
     assert L.svdq_linear(FAKE, ctypes.byref(lay), 0, None, 0, None, 0, None) == B.SVDQ_OK
 
 
+def test_linear_unfused_validation_errors():
+    L = _lib_or_skip()
+    lay = _layer()
+    need = L.svdq_linear_unfused_workspace_size(16, 128, 64, 8, 64)
+    assert need > L.svdq_linear_workspace_size(16, 128, 64, 8, 64)   # the second b x n output
+    assert L.svdq_linear_unfused_workspace_size(16, 128, 64, 0, 64) == L.svdq_linear_workspace_size(16, 128, 64, 0, 64)
+    f = L.svdq_linear_unfused
+    assert f(FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE, need - 1, None) == B.SVDQ_ERR_WORKSPACE
+    assert f(FAKE, ctypes.byref(lay), 16, FAKE + 8, 0, FAKE, need, None) == B.SVDQ_ERR_ALIGNMENT
+    assert f(FAKE, ctypes.byref(_layer(group=32)), 16, FAKE, 0, FAKE, need, None) == B.SVDQ_ERR_UNSUPPORTED
+    assert f(None, ctypes.byref(lay), 16, FAKE, 0, FAKE, need, None) == B.SVDQ_ERR_INVALID_ARG
+    assert f(FAKE, ctypes.byref(lay), 0, None, 0, None, 0, None) == B.SVDQ_OK
+
+
 def test_act_and_gemm_validation_errors():
     L = _lib_or_skip()
     f = L.svdq_quantize_act_lowrank_down

@@ -58,6 +58,9 @@ SIGNATURES = [
     ("svdq_linear_workspace_size", _size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     ("svdq_linear", _c_int,
      [_vp, ctypes.POINTER(svdq_layer), _c_int, _vp, _c_int, _vp, _size, _vp]),
+    ("svdq_linear_unfused_workspace_size", _size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    ("svdq_linear_unfused", _c_int,
+     [_vp, ctypes.POINTER(svdq_layer), _c_int, _vp, _c_int, _vp, _size, _vp]),
     ("svdq_status_string", ctypes.c_char_p, [_c_int]),
     ("svdq_last_error", ctypes.c_char_p, []),
     ("svdq_abi_version", _c_int, []),
@@ -284,4 +287,25 @@ def svdq_linear(x, layer: DeviceLayer, out_dtype=None, y=None, workspace=None, s
     wsb = workspace.numel() * workspace.element_size()
     _check(lib().svdq_linear(_ptr(x), ctypes.byref(layer.struct), b, _ptr(y), code, _ptr(workspace),
                              wsb, _stream(stream)))
+    return y
+
+
+def svdq_linear_unfused_workspace_size(b: int, m: int, n: int, rank: int, group: int = SVDQ_GROUP) -> int:
+    return int(lib().svdq_linear_unfused_workspace_size(b, m, n, rank, group))
+
+
+def svdq_linear_unfused(x, layer: DeviceLayer, out_dtype=None, y=None, workspace=None, stream=None):
+    """The layer without the kernel fusion (five launches), for A/B timing."""
+    import torch
+    b, m = x.shape
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    code = SVDQ_OUT_BF16 if out_dtype == torch.bfloat16 else SVDQ_OUT_F32
+    if y is None:
+        y = torch.empty((b, layer.n), dtype=out_dtype, device=x.device)
+    if workspace is None:
+        need = svdq_linear_unfused_workspace_size(b, m, layer.n, layer.rank)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    wsb = workspace.numel() * workspace.element_size()
+    _check(lib().svdq_linear_unfused(_ptr(x), ctypes.byref(layer.struct), b, _ptr(y), code,
+                                     _ptr(workspace), wsb, _stream(stream)))
     return y

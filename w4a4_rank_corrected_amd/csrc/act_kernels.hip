@@ -78,8 +78,9 @@ __global__ __launch_bounds__(256) void calibrate_kernel(const uint16_t* __restri
 constexpr int kL1Pitch = kActL1Pitch;  // dynamic LDS: gps groups of act_lds_group_bytes(TB)
 
 // TB: 16-column blocks of Z (rank <= 16 * TB; 0 = no low-rank branch);
-// SMOOTH: multiply by 1/lambda (inv != nullptr).
-template <int TB, bool SMOOTH>
+// SMOOTH: multiply by 1/lambda (inv != nullptr); QUANT: emit codes and scales
+// (false: the down-projection alone, the unfused path's separate kernel).
+template <int TB, bool SMOOTH, bool QUANT>
 __global__ __launch_bounds__(256) void act_quant_down_kernel(
     const uint16_t* __restrict__ x, int b, int m, int G, const float* __restrict__ inv,
     const uint16_t* __restrict__ l1t, int rank, uint8_t* __restrict__ qx,
@@ -194,33 +195,35 @@ __global__ __launch_bounds__(256) void act_quant_down_kernel(
       v[2 * q] = bf16_lo(xt[q]);
       v[2 * q + 1] = bf16_hi(xt[q]);
     }
-    float am = 0.0f;
+    if constexpr (QUANT) {
+      float am = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) am = fmaxf(am, fabsf(v[e]));
-    am = max4_rows(am);
-    float s32 = am / 7.0f;                 // IEEE division (correctly rounded)
-    s32 = fminf(s32, 65504.0f);            // saturate instead of rounding to inf
-    const _Float16 s16 = (_Float16)s32;    // round to nearest even
-    const float sf = (float)s16;
-    const float rc = sf > 0.0f ? 1.0f / sf : 0.0f;
-    uint32_t w0 = 0u, w1 = 0u;
+      for (int e = 0; e < 16; ++e) am = fmaxf(am, fabsf(v[e]));
+      am = max4_rows(am);
+      float s32 = am / 7.0f;                 // IEEE division (correctly rounded)
+      s32 = fminf(s32, 65504.0f);            // saturate instead of rounding to inf
+      const _Float16 s16 = (_Float16)s32;    // round to nearest even
+      const float sf = (float)s16;
+      const float rc = sf > 0.0f ? 1.0f / sf : 0.0f;
+      uint32_t w0 = 0u, w1 = 0u;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float pq = v[e] * rc;
-      const float rem = __builtin_fmaf(-pq, sf, v[e]);
-      const float q1 = __builtin_fmaf(rem, rc, pq);
-      const float q = __builtin_amdgcn_fmed3f(q1, -7.0f, 7.0f);
-      const uint32_t nib = __float_as_uint(q + kMagic) & 0xFu;
-      if (e < 8)
-        w0 |= nib << (4 * e);
-      else
-        w1 |= nib << (4 * (e - 8));
+      for (int e = 0; e < 16; ++e) {
+        const float pq = v[e] * rc;
+        const float rem = __builtin_fmaf(-pq, sf, v[e]);
+        const float q1 = __builtin_fmaf(rem, rc, pq);
+        const float q = __builtin_amdgcn_fmed3f(q1, -7.0f, 7.0f);
+        const uint32_t nib = __float_as_uint(q + kMagic) & 0xFu;
+        if (e < 8)
+          w0 |= nib << (4 * e);
+        else
+          w1 |= nib << (4 * (e - 8));
+      }
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(qx + (size_t)g * b * 32, (uint32_t)b * 32u);
+      __builtin_amdgcn_raw_buffer_store_b32(w0, rq, q_off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(w1, rq, q_off + 16u, 0, 0);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(ascale + (size_t)g * b, (uint32_t)b * 2u);
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, s16), rs, s_off, 0, 0);
     }
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qx + (size_t)g * b * 32, (uint32_t)b * 32u);
-    __builtin_amdgcn_raw_buffer_store_b32(w0, rq, q_off, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32(w1, rq, q_off + 16u, 0, 0);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(ascale + (size_t)g * b, (uint32_t)b * 2u);
-    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, s16), rs, s_off, 0, 0);
     if constexpr (TB > 0) {
       const bf16x8 a0 = __builtin_bit_cast(bf16x8, u32x4{xt[0], xt[1], xt[2], xt[3]});
       const bf16x8 a1 = __builtin_bit_cast(bf16x8, u32x4{xt[4], xt[5], xt[6], xt[7]});
@@ -317,19 +320,27 @@ int launch_calibrate(const uint16_t* x, int b, int m, float* amax, int accumulat
 
 int launch_act_quant_down(const uint16_t* x, int b, int m, int rank, const float* smooth_inv,
                           const uint16_t* l1, uint8_t* qx, uint16_t* ascale, float* zpart,
-                          const ActPlan& plan, void* stream) {
+                          const ActPlan& plan, bool quantize, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int G = m / 64;
   dim3 grid(plan.strips, plan.splits);
   const int tb = act_blocks(rank);
 #define SVDQ_ACT(TBV)                                                                              \
   do {                                                                                             \
-    if (smooth_inv)                                                                                \
-      hipLaunchKernelGGL((act_quant_down_kernel<TBV, true>), grid, dim3(256), 0, st, x, b, m, G,   \
-                         smooth_inv, l1, rank, qx, ascale, zpart, plan.groups_per_split);          \
+    if (!quantize) {                                                                               \
+      if (smooth_inv)                                                                              \
+        hipLaunchKernelGGL((act_quant_down_kernel<TBV, true, false>), grid, dim3(256), 0, st, x, b, \
+                           m, G, smooth_inv, l1, rank, qx, ascale, zpart, plan.groups_per_split); \
+      else                                                                                         \
+        hipLaunchKernelGGL((act_quant_down_kernel<TBV, false, false>), grid, dim3(256), 0, st, x,  \
+                           b, m, G, smooth_inv, l1, rank, qx, ascale, zpart,                       \
+                           plan.groups_per_split);                                                 \
+    } else if (smooth_inv)                                                                         \
+      hipLaunchKernelGGL((act_quant_down_kernel<TBV, true, true>), grid, dim3(256), 0, st, x, b,   \
+                         m, G, smooth_inv, l1, rank, qx, ascale, zpart, plan.groups_per_split);   \
     else                                                                                           \
-      hipLaunchKernelGGL((act_quant_down_kernel<TBV, false>), grid, dim3(256), 0, st, x, b, m, G,  \
-                         smooth_inv, l1, rank, qx, ascale, zpart, plan.groups_per_split);          \
+      hipLaunchKernelGGL((act_quant_down_kernel<TBV, false, true>), grid, dim3(256), 0, st, x, b,  \
+                         m, G, smooth_inv, l1, rank, qx, ascale, zpart, plan.groups_per_split);   \
   } while (0)
   if (tb == 0)
     SVDQ_ACT(0);
@@ -346,6 +357,54 @@ int launch_act_quant_down(const uint16_t* x, int b, int m, int rank, const float
   else
     SVDQ_ACT(16);
 #undef SVDQ_ACT
+  return (int)hipGetLastError();
+}
+
+// y[i] = y[i] + t[i] in fp32, stored back in the tensors' type (bf16: round to
+// nearest even).  Eight elements per thread.
+namespace {
+template <bool BF16>
+__global__ void add_kernel(void* __restrict__ y, const void* __restrict__ t, size_t count) {
+  const size_t i0 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (i0 >= count) return;
+  if (BF16) {
+    uint16_t* yy = reinterpret_cast<uint16_t*>(y);
+    const uint16_t* tt = reinterpret_cast<const uint16_t*>(t);
+    if (i0 + 8 <= count) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(yy + i0);
+      const u32x4 c = *reinterpret_cast<const u32x4*>(tt + i0);
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[e] = pack_bf16x2(bf16_lo(a[e]) + bf16_lo(c[e]), bf16_hi(a[e]) + bf16_hi(c[e]));
+      *reinterpret_cast<u32x4*>(yy + i0) = o;
+    } else {
+      for (size_t i = i0; i < count; ++i)
+        yy[i] = bf16_bits(__uint_as_float((uint32_t)yy[i] << 16) + __uint_as_float((uint32_t)tt[i] << 16));
+    }
+  } else {
+    float* yy = reinterpret_cast<float*>(y);
+    const float* tt = reinterpret_cast<const float*>(t);
+    if (i0 + 8 <= count) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(yy + i0 + 4 * h);
+        const f32x4 c = *reinterpret_cast<const f32x4*>(tt + i0 + 4 * h);
+        *reinterpret_cast<f32x4*>(yy + i0 + 4 * h) = a + c;
+      }
+    } else {
+      for (size_t i = i0; i < count; ++i) yy[i] += tt[i];
+    }
+  }
+}
+}  // namespace
+
+int launch_add(void* y, const void* t, size_t count, int y_dtype, void* stream) {
+  const unsigned blocks = (unsigned)((count + 8 * 256 - 1) / (8 * 256));
+  if (y_dtype == SVDQ_OUT_BF16)
+    hipLaunchKernelGGL(add_kernel<true>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, y, t, count);
+  else
+    hipLaunchKernelGGL(add_kernel<false>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, y, t, count);
   return (int)hipGetLastError();
 }
 

@@ -350,7 +350,7 @@ int svdq_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int rank, in
     REQUIRE(((uintptr_t)workspace & 15u) == 0, SVDQ_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
   }
   float* zpart = (rank > 0 && p.splits > 1) ? (float*)workspace : z;
-  st = hip_status(launch_act_quant_down(x, b, m, rank, smooth_inv, l1, qx, ascale, zpart, p, stream),
+  st = hip_status(launch_act_quant_down(x, b, m, rank, smooth_inv, l1, qx, ascale, zpart, p, true, stream),
                   "act_quant_lowrank_down");
   if (st) return st;
   if (rank > 0 && p.splits > 1)
@@ -431,7 +431,7 @@ int svdq_linear(const uint16_t* x, const svdq_layer* layer, int b, void* y, int 
   ActPlan p = act_plan(b, m, rank);
   float* zpart = (rank > 0 && p.splits > 1) ? (float*)(ws + w.zpart_off) : z;
   st = hip_status(launch_act_quant_down(x, b, m, rank, layer->smooth_inv, layer->l1, qx, as, zpart, p,
-                                        stream),
+                                        true, stream),
                   "act_quant_lowrank_down");
   if (st) return st;
   if (rank > 0 && p.splits > 1) {
@@ -440,6 +440,73 @@ int svdq_linear(const uint16_t* x, const svdq_layer* layer, int b, void* y, int 
   }
   return hip_status(launch_gemm_up(qx, as, z, *layer, b, y, y_dtype, ws + w.gemm_off, stream),
                     "gemm_w4a4_lowrank_up");
+}
+
+size_t svdq_linear_unfused_workspace_size(int b, int m, int n, int rank, int group) {
+  const size_t fused = svdq_linear_workspace_size(b, m, n, rank, group);
+  if (fused == 0) return 0;
+  return round_up(fused, kAlign) + (rank > 0 ? (size_t)b * (size_t)n * 4 : 0);
+}
+
+int svdq_linear_unfused(const uint16_t* x, const svdq_layer* layer, int b, void* y, int y_dtype,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  int st = check_layer(layer);
+  if (st) return st;
+  REQUIRE(b >= 0, SVDQ_ERR_INVALID_ARG, "b must be >= 0 (got %d)", b);
+  REQUIRE(b <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "b must be <= %d (got %d)", SVDQ_MAX_DIM, b);
+  st = check_y(y, y_dtype, b);
+  if (st) return st;
+  if (b == 0) return SVDQ_OK;
+  const int m = layer->m, n = layer->n, rank = layer->rank;
+  REQUIRE(aligned16(y), SVDQ_ERR_ALIGNMENT, "y must be 16-byte aligned");
+  REQUIRE(x != nullptr, SVDQ_ERR_INVALID_ARG, "x must not be NULL");
+  REQUIRE(aligned16(x), SVDQ_ERR_ALIGNMENT, "x must be 16-byte aligned");
+  if (layer->smooth_inv)
+    REQUIRE(aligned16(layer->smooth_inv), SVDQ_ERR_ALIGNMENT, "smooth_inv must be 16-byte aligned");
+  if (rank > 0) {
+    REQUIRE(layer->l1 != nullptr, SVDQ_ERR_INVALID_ARG, "layer l1 must not be NULL when rank > 0");
+    REQUIRE(aligned16(layer->l1), SVDQ_ERR_ALIGNMENT, "layer l1 must be 16-byte aligned");
+  }
+  const LinearWorkspace w = linear_ws_layout(b, m, n, rank);
+  const size_t y2_off = round_up(w.total, kAlign);
+  const size_t need = svdq_linear_unfused_workspace_size(b, m, n, rank, SVDQ_GROUP);
+  REQUIRE(workspace != nullptr && workspace_bytes >= need, SVDQ_ERR_WORKSPACE,
+          "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
+  REQUIRE(((uintptr_t)workspace & (kAlign - 1)) == 0, SVDQ_ERR_ALIGNMENT,
+          "workspace must be %zu-byte aligned", kAlign);
+  char* ws = (char*)workspace;
+  uint8_t* qx = (uint8_t*)(ws + w.qx_off);
+  uint16_t* as = (uint16_t*)(ws + w.as_off);
+  // 1. activation quantization alone
+  const ActPlan p0 = act_plan(b, m, 0);
+  st = hip_status(launch_act_quant_down(x, b, m, 0, layer->smooth_inv, nullptr, qx, as, nullptr, p0, true,
+                                        stream),
+                  "act_quant");
+  if (st) return st;
+  // 2. the W4A4 product (+ bias) into y
+  svdq_layer M = *layer;
+  M.rank = 0;
+  M.l1 = nullptr;
+  M.l2 = nullptr;
+  st = hip_status(launch_gemm_up(qx, as, nullptr, M, b, y, y_dtype, ws + w.gemm_off, stream), "gemm_w4a4");
+  if (st || rank == 0) return st;
+  // 3. the down-projection alone, reading x again
+  float* z = (float*)(ws + w.z_off);
+  const ActPlan p = act_plan(b, m, rank);
+  float* zpart = p.splits > 1 ? (float*)(ws + w.zpart_off) : z;
+  st = hip_status(launch_act_quant_down(x, b, m, rank, layer->smooth_inv, layer->l1, nullptr, nullptr, zpart,
+                                        p, false, stream),
+                  "lowrank_down");
+  if (st) return st;
+  if (p.splits > 1) {
+    st = hip_status(launch_z_reduce(zpart, p.splits, b, rank, z, stream), "z_reduce");
+    if (st) return st;
+  }
+  // 4. the up-projection alone, into a second b x n tensor; 5. the addition
+  st = hip_status(launch_lowrank_up(z, *layer, b, ws + y2_off, y_dtype, stream), "lowrank_up");
+  if (st) return st;
+  return hip_status(launch_add(y, ws + y2_off, (size_t)b * (size_t)n, y_dtype, stream), "add");
 }
 
 }  // extern "C"

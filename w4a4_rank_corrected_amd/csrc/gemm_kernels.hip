@@ -285,6 +285,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
     const uint32_t s_voff = tid < TM ? (uint32_t)(i0 + tid) * 2u
                                      : (tid < TM + TN ? (uint32_t)(j0 + tid - TM) * 2u : 0x7FFFFFF0u);
     const int S = g1 - g0;  // groups in this segment
+    if (S <= 0) return;     // the up-projection alone (no channel groups)
     auto load_stage = [&](int k, Stage& st) {
       const int g = g0 + min(k, S - 1);
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(qx + (size_t)g * a_bytes, a_bytes);
@@ -584,6 +585,20 @@ int launch_gemm_up(const uint8_t* qx, const uint16_t* ascale, const float* z, co
   hipStream_t st = (hipStream_t)stream;
   if (y_dtype == SVDQ_OUT_BF16) return launch_typed<true>(qx, ascale, z, L, b, y, plan, ws, st);
   return launch_typed<false>(qx, ascale, z, L, b, y, plan, ws, st);
+}
+
+// The low-rank up-projection alone, y = bf16(z) L2 (the unfused path's
+// separate kernel): the GEMM kernel with no channel groups and no bias.
+int launch_lowrank_up(const float* z, const svdq_layer& L, int b, void* y, int y_dtype, void* stream) {
+  svdq_layer U = L;
+  U.m = 0;
+  U.qw = nullptr;
+  U.wscale = nullptr;
+  U.bias = nullptr;
+  const GemmPlan plan = gemm_plan(b, L.n, 0, device_cus());  // G = 0: one tile per workgroup
+  hipStream_t st = (hipStream_t)stream;
+  if (y_dtype == SVDQ_OUT_BF16) return launch_typed<true>(nullptr, nullptr, z, U, b, y, plan, nullptr, st);
+  return launch_typed<false>(nullptr, nullptr, z, U, b, y, plan, nullptr, st);
 }
 
 }  // namespace svdq

@@ -70,8 +70,10 @@ ActPlan act_plan(int b, int m, int rank);
 int launch_calibrate(const uint16_t* x, int b, int m, float* amax, int accumulate, void* stream);
 int launch_act_quant_down(const uint16_t* x, int b, int m, int rank, const float* smooth_inv,
                           const uint16_t* l1, uint8_t* qx, uint16_t* ascale, float* zpart,
-                          const ActPlan& plan, void* stream);
+                          const ActPlan& plan, bool quantize, void* stream);
 int launch_z_reduce(const float* zpart, int splits, int b, int rank, float* z, void* stream);
+int launch_add(void* y, const void* t, size_t count, int y_dtype, void* stream);
+int launch_lowrank_up(const float* z, const svdq_layer& L, int b, void* y, int y_dtype, void* stream);
 // A fresh value per kernel launch in this process (64-bit, starting at a
 // random per-process base): tags the publication flags that kernels keep in
 // caller workspaces, so values left there by earlier launches or other
