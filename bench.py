@@ -27,7 +27,11 @@ Extra modes (used with rocprofv3 runs):
                              command) into the per-launch HBM traffic summary
                              read by the JSON line's roofline.traffic;
   --trace-summary DIR        summarize a --kernel-trace --stats run of this
-                             script (same --workload/--steps/--warmup).
+                             script (same --workload/--steps/--warmup);
+  --fusion-ab [RANKS]        time the fused layer against the unfused one
+                             (separate down- and up-projection kernels, a
+                             second b x n output and an addition) at each rank,
+                             and print that table as one JSON line instead.
 """
 from __future__ import annotations
 
@@ -247,6 +251,69 @@ def cpu_baseline(inp, cfg, rows):
 # GPU benchmark
 # ---------------------------------------------------------------------------
 
+def fusion_ab(cfg, ranks, args):
+    """Fused (svdq_linear: 2 kernels) against unfused (svdq_linear_unfused: the
+    act quantization, the W4A4 product, a separate down-projection reading X
+    again, a separate up-projection writing a second b x n output, an addition)
+    at each rank, on layers the library prepares from the workload's X and W
+    (LoRA not attached: the rank is the SVD rank).  Warm timing: HIP events
+    around each call on the launch stream, median over the steps."""
+    import torch
+    import workloads
+    import w4a4_rank_corrected_amd as S
+
+    inp = workloads.make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(inp["x_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    b, m, n = x.shape[0], cfg.m, cfg.n
+    amax = S.svdq_calibrate_act_amax(x).cpu().numpy()
+    out_dtype = torch.bfloat16 if args.out == "bf16" else torch.float32
+    y = torch.empty((b, n), dtype=out_dtype, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ops = 2.0 * b * m * n
+
+    def time_pair(ws_f, ws_u):
+        """Fused and unfused calls alternate step by step (same clocks and
+        cache state for both), after a warm-up long enough to raise clocks."""
+        for _ in range(max(50, args.warmup)):
+            S.svdq_linear(x, layer, out_dtype, y=y, workspace=ws_f, stream=stream)
+            S.svdq_linear_unfused(x, layer, out_dtype, y=y, workspace=ws_u, stream=stream)
+        ev = []
+        for _ in range(args.steps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            S.svdq_linear(x, layer, out_dtype, y=y, workspace=ws_f, stream=stream)
+            e[1].record(stream)
+            S.svdq_linear_unfused(x, layer, out_dtype, y=y, workspace=ws_u, stream=stream)
+            e[2].record(stream)
+            ev.append(e)
+        torch.cuda.synchronize()
+        return (float(np.median([e[0].elapsed_time(e[1]) for e in ev])),
+                float(np.median([e[1].elapsed_time(e[2]) for e in ev])))
+
+    rows = []
+    for r in ranks:
+        host = S.svdq_prepare_weights(inp["w"], amax, r)
+        layer = S.DeviceLayer(host, device=dev)
+        wsf = torch.empty(max(S.svdq_linear_workspace_size(b, m, n, r), 1), dtype=torch.uint8, device=dev)
+        wsu = torch.empty(max(S.svdq_linear_unfused_workspace_size(b, m, n, r), 1), dtype=torch.uint8,
+                          device=dev)
+        tf, tu = time_pair(wsf, wsu)
+        rows.append({"rank": r, "fused_ms": round(tf, 5), "unfused_ms": round(tu, 5),
+                     "fused_TOPs": round(ops / (tf * 1e-3) / 1e12, 1)})
+        log(f"fusion A/B {cfg.name} rank {r}: fused {tf * 1e3:.1f} us, unfused {tu * 1e3:.1f} us")
+        del layer, wsf, wsu
+    base = next((row["fused_ms"] for row in rows if row["rank"] == 0), None)
+    for row in rows:
+        if base:
+            row["fused_overhead"] = round(row["fused_ms"] / base - 1.0, 4)
+            row["unfused_overhead"] = round(row["unfused_ms"] / base - 1.0, 4)
+    print(json.dumps({"fusion_ab": rows, "workload": cfg.name, "b": b, "m": m, "n": n, "out": args.out,
+                      "steps": args.steps,
+                      "timing": "warm; fused and unfused calls alternate; median of HIP-event times"}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,6 +331,8 @@ def main():
     ap.add_argument("--commands", default="", help="counter-run commands recorded in the summary")
     ap.add_argument("--trace-summary", metavar="PROF_DIR",
                     help="write the kernel-trace summary of a profiled run of this script and exit")
+    ap.add_argument("--fusion-ab", nargs="?", const="0,16,32,48,64,128", default=None, metavar="RANKS",
+                    help="fused vs unfused timing at these ranks (comma-separated) instead of the metric")
     args = ap.parse_args()
 
     if args.traffic_summary:
@@ -287,6 +356,9 @@ def main():
     import w4a4_rank_corrected_amd as S
 
     cfg = workloads.CONFIGS[args.workload]
+    if args.fusion_ab is not None:
+        fusion_ab(cfg, [int(v) for v in args.fusion_ab.split(",")], args)
+        return
     m, n = cfg.m, cfg.n
     rank_svd = cfg.rank if args.rank is None else args.rank
     dev = torch.device("cuda:0")
