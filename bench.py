@@ -113,11 +113,12 @@ def trace_summary(prof_dir, cfg, args, rank):
     skip = max(args.warmup, n_sets)
     short = lambda nm: re.sub(r"\(.*", "", nm.replace("svdq::(anonymous namespace)::", "")
                               .replace("void ", "").replace("svdq::", ""))
-    rows = list(c.execute("select name, start, end, grid_x, workgroup_x, vgpr_count, accum_vgpr_count, "
-                          "lds_size, scratch_size from kernels order by start"))
+    rows = list(c.execute("select name, start, end, grid_x, grid_y, workgroup_x, workgroup_y, vgpr_count, "
+                          "accum_vgpr_count, lds_size, scratch_size from kernels order by start"))
     by = {}
-    for nm, st, en, gx, wx, vg, ag, lds, scr in rows:
-        by.setdefault(nm, []).append(((en - st) / 1e3, gx // max(wx, 1), wx, vg, ag, lds, scr))
+    for nm, st, en, gx, gy, wx, wy, vg, ag, lds, scr in rows:
+        wgs = (gx // max(wx, 1)) * (gy // max(wy, 1))
+        by.setdefault(nm, []).append(((en - st) / 1e3, wgs, wx * wy, vg, ag, lds, scr))
     cmd = (f"rocprofv3 --kernel-trace --stats -d {prof_dir} -o run -- python3 bench.py --workload {cfg.name} "
            f"--steps {args.steps} --warmup {args.warmup} --no-cpu-baseline")
     out = [f"# Kernel trace: {cfg.name} (b={cfg.rows or cfg.b}, m={cfg.m}, n={cfg.n}, rank {rank})", "",
