@@ -28,6 +28,10 @@ Extra modes (used with rocprofv3 runs):
                              read by the JSON line's roofline.traffic;
   --trace-summary DIR        summarize a --kernel-trace --stats run of this
                              script (same --workload/--steps/--warmup);
+  --prep-refine [WORKLOADS]  preparation with a search over migration
+                             strengths and factor refinement against the
+                             plain preparation: layer-output error on held-out
+                             rows (one JSON line);
   --fusion-ab [RANKS]        time the fused layer against the unfused one
                              (separate down- and up-projection kernels, a
                              second b x n output and an addition) at each rank,
@@ -252,6 +256,59 @@ def cpu_baseline(inp, cfg, rows):
 # GPU benchmark
 # ---------------------------------------------------------------------------
 
+def prep_refine(names, args):
+    """Plain preparation (alpha = 0.5) against the search over migration
+    strengths (0.3 .. 0.7) with two factor-refinement steps (Algorithm 1 steps
+    6-8), both by the library on the host.  Calibration: the first 256 rows of
+    the workload's X (statistics and candidate scores); evaluation: 512 other
+    rows, through the fused GPU layer with fp32 output, against X W in fp64."""
+    import torch
+    import workloads
+    import w4a4_rank_corrected_amd as S
+
+    dev = torch.device("cuda:0")
+    alphas = (0.3, 0.4, 0.5, 0.6, 0.7)
+    rows = []
+    for name in names:
+        cfg = workloads.CONFIGS[name]
+        inp = workloads.make_inputs(cfg)
+        xb, w = inp["x_bits"], inp["w"]
+        b = xb.shape[0]
+        cal = np.ascontiguousarray(xb[:min(256, b // 2)])
+        ev = np.ascontiguousarray(xb[b // 2: b // 2 + min(512, b - b // 2)])
+        cal_d = torch.from_numpy(cal.view(np.int16)).to(dev).view(torch.bfloat16)
+        amax = S.svdq_calibrate_act_amax(cal_d).cpu().numpy()
+        ev_d = torch.from_numpy(ev.view(np.int16)).to(dev).view(torch.bfloat16)
+        xe = (ev.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        yref = xe @ w.astype(np.float64)
+
+        def held_out(host):
+            y = S.svdq_linear(ev_d, S.DeviceLayer(host, device=dev), torch.float32)
+            torch.cuda.synchronize()
+            return float(np.linalg.norm(y.cpu().numpy() - yref) / np.linalg.norm(yref))
+
+        t0 = time.perf_counter()
+        base = S.svdq_prepare_weights_refined(w, amax, cal, cfg.rank, alphas=(0.5,), iters=0)
+        t_base = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        search = S.svdq_prepare_weights_refined(w, amax, cal, cfg.rank, alphas=alphas, iters=0)
+        t_search = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        refined = S.svdq_prepare_weights_refined(w, amax, cal, cfg.rank, alphas=alphas, iters=2)
+        t_ref = time.perf_counter() - t0
+        row = {"workload": name, "rank": cfg.rank, "cal_rows": int(cal.shape[0]), "eval_rows": int(ev.shape[0])}
+        for key, host, t in (("plain", base, t_base), ("alpha_search", search, t_search),
+                             ("alpha_search_refit2", refined, t_ref)):
+            row[key] = {"alpha": host["alpha"], "iteration": host["iteration"],
+                        "cal_err": round(host["rel_err"], 6), "heldout_err": round(held_out(host), 6),
+                        "prep_s": round(t, 2)}
+        log(f"prep-refine {name}: " + ", ".join(f"{k} {row[k]['heldout_err']:.5f} (alpha {row[k]['alpha']}, "
+                                                f"it {row[k]['iteration']})"
+                                                for k in ("plain", "alpha_search", "alpha_search_refit2")))
+        rows.append(row)
+    print(json.dumps({"prep_refine": rows, "alphas": list(alphas)}), flush=True)
+
+
 def fusion_ab(cfg, ranks, args):
     """Fused (svdq_linear: 2 kernels) against unfused (svdq_linear_unfused: the
     act quantization, the W4A4 product, a separate down-projection reading X
@@ -332,6 +389,8 @@ def main():
     ap.add_argument("--commands", default="", help="counter-run commands recorded in the summary")
     ap.add_argument("--trace-summary", metavar="PROF_DIR",
                     help="write the kernel-trace summary of a profiled run of this script and exit")
+    ap.add_argument("--prep-refine", nargs="?", const="tiny,pixart_fc1,flux_qkv", default=None,
+                    metavar="WORKLOADS", help="refined vs plain preparation, output error on held-out rows")
     ap.add_argument("--fusion-ab", nargs="?", const="0,16,32,48,64,128", default=None, metavar="RANKS",
                     help="fused vs unfused timing at these ranks (comma-separated) instead of the metric")
     args = ap.parse_args()
@@ -356,6 +415,9 @@ def main():
     import workloads
     import w4a4_rank_corrected_amd as S
 
+    if args.prep_refine is not None:
+        prep_refine(args.prep_refine.split(","), args)
+        return
     cfg = workloads.CONFIGS[args.workload]
     if args.fusion_ab is not None:
         fusion_ab(cfg, [int(v) for v in args.fusion_ab.split(",")], args)

@@ -123,6 +123,28 @@ int svdq_prepare_weights(const float* W, const float* act_amax, int m, int n, in
                          int group, float alpha, uint8_t* qw, uint16_t* wscale, uint16_t* l1,
                          uint16_t* l2, float* lambda, float* smooth_inv, float* residual);
 
+/* HOST: offline preparation with candidate search and refinement ([Review]
+ * sec. 5 Algorithm 1 steps 2-8).  For each migration strength alphas[a] the
+ * layer is built as in svdq_prepare_weights (steps 2-5); then `iters` times
+ * the factors are re-fitted to the part of W~ the quantized residual leaves
+ * out, L1 L2 <- rank-r SVD of (W~ - Q(R)), and R and Q(R) are formed again
+ * (steps 6-7).  Every candidate (alpha, refinement step) is scored by its
+ * layer-output error on calibration activations, ||Y(X_cal) - X_cal W||_F /
+ * ||X_cal W||_F with Y the quantized layer exactly as the device computes it
+ * (in fp64 on the host), and the first candidate with the lowest error is
+ * returned (step 8).
+ *   x_cal     bf16 [b_cal][m] calibration rows (host), b_cal >= 1.
+ *   alphas    n_alpha (1..64) values in [0, 1]; iters in [0, 16].
+ *   Outputs as svdq_prepare_weights, plus (each nullable) alpha_out: the
+ *   chosen alpha; iter_out: its refinement step (0 = none); rel_err_out: its
+ *   relative output error.  With alphas = {alpha}, iters = 0 the layer is
+ *   identical to svdq_prepare_weights(..., alpha, ...). */
+int svdq_prepare_weights_refined(const float* W, const float* act_amax, const uint16_t* x_cal, int b_cal,
+                                 int m, int n, int rank, int group, const float* alphas, int n_alpha,
+                                 int iters, uint8_t* qw, uint16_t* wscale, uint16_t* l1, uint16_t* l2,
+                                 float* lambda, float* smooth_inv, float* residual, float* alpha_out,
+                                 int* iter_out, double* rel_err_out);
+
 /* HOST: the INT4 group quantization step alone ([Review] Algorithm 1 step 5 with
  * Eq.(1)): R fp32 [m][n] -> qw [m/64][n][32], wscale fp16 [m/64][n]. */
 int svdq_quantize_residual(const float* R, int m, int n, int group, uint8_t* qw,

@@ -42,6 +42,13 @@ Readings taken where the pages are silent (each also listed in the design doc):
   R10 the LoRA scale is absorbed into B (sec. 7 allows either factor).
   R11 quantization groups run along the input channels for both operands
       (sec. 8: group quantization on both operands, group 64).
+  R16 the candidate-selection score of Algorithm 1 step 8 is the relative
+      Frobenius error of the quantized layer's output against X W (float64) on
+      the calibration rows.
+  R17 the optional factor update of step 6 refits rank-r SVD factors to
+      W~ - Q(R) (Q(R) dequantized exactly); the residual of step 7 is then
+      formed and quantized again; of equal scores the first candidate
+      (migration strengths in the order given, then refinement steps) wins.
 """
 from __future__ import annotations
 
@@ -269,6 +276,59 @@ def prepare_weights(w32: np.ndarray, a: Optional[np.ndarray], rank: int,
     return {"lam32": lam32, "inv32": inv32, "wt": wt, "l1": l1b, "l2": l2b,
             "r64": r64, "r32": r32, "qw": qw, "sw": sw, "sigma": sigma,
             "rank": rank, "group": group, "alpha": alpha}
+
+
+def dequantize_weight_residual(qw: np.ndarray, sw: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """Q(R) = s q in float64 (exact), from codes [m][n] and scales [m/64][n]."""
+    return np.asarray(qw, np.float64) * np.repeat(np.asarray(sw, np.float64), group, axis=0)
+
+
+def refit_factors(layer: dict, group: int = GROUP, svd: str = "lapack") -> dict:
+    """Algorithm 1 steps 6-7: the factors are fitted again to what the quantized
+    residual leaves out, L1 L2 <- SVD_r(W~ - Q(R)), and the residual is formed
+    and quantized again from the new (bf16) factors."""
+    rank = layer["rank"]
+    if rank == 0:
+        return dict(layer)
+    target = layer["wt"] - dequantize_weight_residual(layer["qw"], layer["sw"], group)
+    l1, l2, sigma = truncated_svd(target, rank, svd)
+    l1b, l2b = bf16_from_f64(l1), bf16_from_f64(l2)
+    r64 = residual(layer["wt"], l1b, l2b)
+    r32 = r64.astype(np.float32)
+    qw, sw = quantize_weight_residual(r32, group)
+    return dict(layer, l1=l1b, l2=l2b, r64=r64, r32=r32, qw=qw, sw=sw, sigma=sigma)
+
+
+def layer_output_error(x32: np.ndarray, w32: np.ndarray, layer: dict, group: int = GROUP) -> float:
+    """Algorithm 1 step 8's criterion: ||Y(X) - X W||_F / ||X W||_F with Y the
+    quantized layer (``linear``) on calibration rows X and X W in float64."""
+    yref = np.asarray(x32, np.float64) @ np.asarray(w32, np.float64)
+    y = linear(x32, layer, group=group)["y"]
+    return float(np.linalg.norm(y - yref) / np.linalg.norm(yref))
+
+
+def refine_weights(w32: np.ndarray, a: Optional[np.ndarray], x_cal32: np.ndarray, rank: int,
+                   alphas=(0.5,), iters: int = 0, group: int = GROUP, svd: str = "lapack") -> dict:
+    """Algorithm 1 steps 2-8: for each migration strength the layer is built
+    (steps 2-5) and its factors refitted `iters` times (steps 6-7); every
+    candidate is scored by ``layer_output_error`` on the calibration rows and
+    the first one with the lowest error is kept (step 8).
+
+    Returns the chosen layer dict with added keys alpha, iteration, rel_err and
+    candidates (a list of (alpha, iteration, rel_err) in evaluation order)."""
+    best, cands = None, []
+    for alpha in alphas:
+        lay = prepare_weights(w32, a, rank, group, float(np.float32(alpha)), svd)
+        for it in range(iters + 1):
+            err = layer_output_error(x_cal32, w32, lay, group)
+            cands.append((float(np.float32(alpha)), it, err))
+            if best is None or err < best[2]:
+                best = (lay, it, err)
+            if it == iters or rank == 0:
+                break
+            lay = refit_factors(lay, group, svd)
+    out = dict(best[0], iteration=best[1], rel_err=best[2], candidates=cands)
+    return out
 
 
 def append_lora(l1b: np.ndarray, l2b: np.ndarray, lam32: Optional[np.ndarray],

@@ -67,3 +67,17 @@ def oracle_layer_to_host_abi(lay: dict) -> dict:
         "smooth_inv": np.ones(m, np.float32) if inv is None else np.asarray(inv, np.float32),
         "lambda": lay.get("lam32", np.ones(m, np.float32)),
     }
+
+
+def host_abi_to_oracle_layer(host: dict) -> dict:
+    """Host arrays in the ABI layouts (as the library's preparation returns
+    them) -> the oracle's logical layer dict (codes [m][n], scales [m/64][n],
+    L1 [m][r], L2 [r][n] as float32 holding bf16 values, inv32)."""
+    return {
+        "qw": np.ascontiguousarray(unpack_codes(host["qw"]).T),
+        "sw": fp16_bits_to_f32(host["wscale"]),
+        "l1": np.ascontiguousarray(bf16_bits_to_f32(host["l1"]).T),
+        "l2": np.ascontiguousarray(bf16_bits_to_f32(host["l2"]).T),
+        "inv32": np.asarray(host["smooth_inv"], np.float32),
+        "lam32": np.asarray(host["lambda"], np.float32),
+    }

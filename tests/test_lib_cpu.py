@@ -286,3 +286,66 @@ def test_workspace_sizes_cover_layout():
         assert w % 256 == 0 and gw % 256 == 0
     assert L.svdq_linear_workspace_size(16, 100, 8, 8, 64) == 0
     assert L.svdq_gemm_workspace_size(16, 8, 100) == 0
+
+
+# ---------------------------------------------------------------------------
+# preparation with candidate search and refinement (Algorithm 1 steps 6-8)
+# ---------------------------------------------------------------------------
+
+def _refine_inputs(m=256, n=192, b=64, seed=31):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((b, m))
+    x[:, rng.choice(m, 4, replace=False)] *= 40
+    xbits = workloads.bf16_bits_of(x.astype(np.float32))
+    w = (rng.standard_normal((m, n)) / np.sqrt(m)).astype(np.float32)
+    w[rng.choice(m, 4, replace=False)] *= 8
+    return xbits, LY.bf16_bits_to_f32(xbits), w
+
+
+def test_refined_single_candidate_equals_prepare_weights():
+    _lib_or_skip()
+    xbits, x, w = _refine_inputs()
+    a = O.act_amax(x)
+    got = S.svdq_prepare_weights_refined(w, a, xbits, 16, alphas=(0.5,), iters=0)
+    ref = S.svdq_prepare_weights(w, a, 16)
+    for k in ("qw", "wscale", "l1", "l2", "lambda", "smooth_inv"):
+        assert np.array_equal(got[k], ref[k]), k
+    assert got["alpha"] == 0.5 and got["iteration"] == 0
+
+
+def test_refined_reported_error_matches_oracle_evaluation():
+    """The library scores candidates with its own fp64 host evaluation of the
+    quantized layer; the oracle's evaluation of the returned layer agrees."""
+    _lib_or_skip()
+    xbits, x, w = _refine_inputs()
+    got = S.svdq_prepare_weights_refined(w, O.act_amax(x), xbits, 16, alphas=(0.4, 0.6), iters=1)
+    lay = LY.host_abi_to_oracle_layer(got)
+    err = O.layer_output_error(x, w, lay)
+    assert abs(got["rel_err"] - err) <= 1e-9 * err
+
+
+def test_refined_search_beats_baseline_and_tracks_oracle():
+    _lib_or_skip()
+    xbits, x, w = _refine_inputs()
+    a = O.act_amax(x)
+    alphas = (0.3, 0.4, 0.5, 0.6, 0.7)
+    got = S.svdq_prepare_weights_refined(w, a, xbits, 16, alphas=alphas, iters=2)
+    base = S.svdq_prepare_weights_refined(w, a, xbits, 16, alphas=(0.5,), iters=0)
+    assert got["rel_err"] <= base["rel_err"]
+    ora = O.refine_weights(w, a, x, 16, alphas=alphas, iters=2)
+    # different SVD algorithms (randomized vs LAPACK): the best scores agree closely
+    assert abs(got["rel_err"] - ora["rel_err"]) <= 0.05 * ora["rel_err"]
+
+
+def test_refined_validation_errors():
+    _lib_or_skip()
+    xbits, x, w = _refine_inputs(m=128, n=64, b=8)
+    with pytest.raises(B.SvdqError) as e:
+        S.svdq_prepare_weights_refined(w, None, xbits, 8, alphas=(1.5,))
+    assert e.value.status == B.SVDQ_ERR_INVALID_ARG
+    with pytest.raises(B.SvdqError) as e:
+        S.svdq_prepare_weights_refined(w, None, xbits, 8, iters=17)
+    assert e.value.status == B.SVDQ_ERR_INVALID_ARG
+    with pytest.raises(B.SvdqError) as e:
+        S.svdq_prepare_weights_refined(w, None, np.zeros((0, 128), np.uint16), 8)
+    assert e.value.status == B.SVDQ_ERR_INVALID_ARG

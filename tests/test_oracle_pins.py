@@ -446,3 +446,84 @@ def test_accounting_matches_printed_example():
     assert O.mac_ratio(m, n, r) == gold["mac_ratio"]
     assert O.storage_ratio(m, n, r) == gold["storage_ratio"]
     assert round(1 / O.storage_ratio(m, n, r), 2) == gold["compression_approx"]
+
+
+# ---------------------------------------------------------------------------
+# candidate search and refinement of Algorithm 1 steps 6-8 (readings R16, R17)
+# ---------------------------------------------------------------------------
+
+def _refine_case(m=128, n=96, b=48, seed=21):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((b, m))
+    x[:, rng.choice(m, 3, replace=False)] *= 30
+    x32 = workloads.bf16_bits_to_f32(workloads.bf16_bits_of(x.astype(np.float32)))
+    w = (rng.standard_normal((m, n)) / np.sqrt(m)).astype(np.float32)
+    return x32, w
+
+
+def test_layer_output_error_zero_when_quantization_is_exact():
+    """Integer activations and weights whose groups each reach 7 quantize
+    exactly (scale 1); without smoothing and with rank 0 the layer output is
+    X W, so the error is 0; scaling W by 2 in one column makes it computable by
+    hand."""
+    rng = np.random.default_rng(2)
+    m, n, b = 128, 16, 8
+    x = rng.integers(-7, 8, (b, m)).astype(np.float32)
+    x[:, ::64] = 7
+    w = rng.integers(-7, 8, (m, n)).astype(np.float32)
+    w[::64, :] = 7
+    lay = O.prepare_weights(w, None, 0)
+    assert O.layer_output_error(x, w, lay) == 0.0
+    # a layer built for W, scored against 2 W: Y = X W, reference 2 X W -> error 1/2
+    assert abs(O.layer_output_error(x, 2 * w, lay) - 0.5) < 1e-15
+
+
+def test_refine_reduces_to_prepare_weights():
+    x32, w = _refine_case()
+    a = O.act_amax(x32)
+    got = O.refine_weights(w, a, x32, 16, alphas=(0.5,), iters=0)
+    ref = O.prepare_weights(w, a, 16)
+    for k in ("qw", "sw", "l1", "l2", "lam32", "inv32"):
+        assert np.array_equal(got[k], ref[k]), k
+    assert got["iteration"] == 0 and got["candidates"] == [(0.5, 0, got["rel_err"])]
+
+
+def test_refine_keeps_the_lowest_scoring_candidate():
+    """The kept candidate has the lowest score of all candidates (first of equals),
+    each score re-evaluated here from a layer built independently."""
+    x32, w = _refine_case()
+    a = O.act_amax(x32)
+    alphas = (0.3, 0.5, 0.7)
+    got = O.refine_weights(w, a, x32, 16, alphas=alphas, iters=2)
+    scores = []
+    for al in alphas:
+        # the C ABI takes the strengths as float: the oracle rounds them the same way
+        lay = O.prepare_weights(w, a, 16, alpha=float(np.float32(al)))
+        for it in range(3):
+            scores.append(O.layer_output_error(x32, w, lay))
+            lay = O.refit_factors(lay)
+    assert [c[2] for c in got["candidates"]] == scores
+    k = int(np.argmin(scores))
+    assert got["rel_err"] == scores[k]
+    assert (got["alpha"], got["iteration"]) == (float(np.float32(alphas[k // 3])), k % 3)
+    assert got["rel_err"] <= scores[1 * 3 + 0]      # never worse than alpha = 0.5, no refinement
+
+
+def test_refit_factors_is_the_best_rank1_fit_by_power_iteration():
+    """Step 6 at rank 1: the refitted factor product is the top singular pair
+    of W~ - Q(R), here found independently by power iteration (then rounded to
+    bf16 like the stored factors)."""
+    x32, w = _refine_case(m=64, n=40)
+    lay = O.prepare_weights(w, O.act_amax(x32), 1)
+    target = lay["wt"] - O.dequantize_weight_residual(lay["qw"], lay["sw"])
+    v = np.ones(target.shape[1])
+    for _ in range(500):
+        v = target.T @ (target @ v)
+        v /= np.linalg.norm(v)
+    u = target @ v                       # = sigma_1 u_1
+    best = np.outer(u, v)
+    new = O.refit_factors(lay)
+    prod = new["l1"].astype(np.float64) @ new["l2"].astype(np.float64)
+    assert np.linalg.norm(prod - best) <= 1e-2 * np.linalg.norm(best)   # bf16 factors: ~2^-9 each
+    # and the residual is formed from the new stored factors
+    assert np.array_equal(new["r64"], lay["wt"] - prod)

@@ -45,6 +45,9 @@ class svdq_layer(ctypes.Structure):
 SIGNATURES = [
     ("svdq_prepare_weights", _c_int,
      [_vp, _vp, _c_int, _c_int, _c_int, _c_int, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    ("svdq_prepare_weights_refined", _c_int,
+     [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
+      _vp, _vp, _vp, _vp, _vp]),
     ("svdq_quantize_residual", _c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp]),
     ("svdq_append_lora", _c_int,
      [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_int, ctypes.c_float, _vp, _vp]),
@@ -151,6 +154,44 @@ def svdq_prepare_weights(W: np.ndarray, act_amax: Optional[np.ndarray], rank: in
         _ptr(out["lambda"]), _ptr(out["smooth_inv"]), _ptr(res)))
     if want_residual:
         out["residual"] = res
+    return out
+
+
+def svdq_prepare_weights_refined(W: np.ndarray, act_amax: Optional[np.ndarray], x_cal_bits: np.ndarray,
+                                 rank: int, alphas=(0.3, 0.4, 0.5, 0.6, 0.7), iters: int = 2,
+                                 group: int = SVDQ_GROUP, want_residual: bool = False) -> dict:
+    """Preparation with a search over migration strengths and factor refinement,
+    scored by layer-output error on calibration rows (bf16 bits [b_cal][m]).
+
+    Returns the keys of ``svdq_prepare_weights`` plus alpha, iteration, rel_err.
+    """
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    m, n = W.shape
+    a = None if act_amax is None else np.ascontiguousarray(act_amax, dtype=np.float32)
+    xc = np.ascontiguousarray(x_cal_bits, dtype=np.uint16)
+    al = np.ascontiguousarray(np.asarray(alphas, dtype=np.float32).ravel())
+    G = max(m // SVDQ_GROUP, 0)
+    out = {
+        "qw": np.zeros((G, n, 32), np.uint8),
+        "wscale": np.zeros((G, n), np.uint16),
+        "l1": np.zeros((rank, m), np.uint16),
+        "l2": np.zeros((n, rank), np.uint16),
+        "lambda": np.zeros(m, np.float32),
+        "smooth_inv": np.zeros(m, np.float32),
+        "m": m, "n": n, "rank": rank,
+    }
+    res = np.zeros((m, n), np.float32) if want_residual else None
+    alpha_out = np.zeros(1, np.float32)
+    iter_out = np.zeros(1, np.int32)
+    err_out = np.zeros(1, np.float64)
+    _check(lib().svdq_prepare_weights_refined(
+        _ptr(W), _ptr(a), _ptr(xc), xc.shape[0] if xc.ndim == 2 else 0, m, n, rank, group, _ptr(al), al.size,
+        iters, _ptr(out["qw"]), _ptr(out["wscale"]), _ptr(out["l1"]) if rank else None,
+        _ptr(out["l2"]) if rank else None, _ptr(out["lambda"]), _ptr(out["smooth_inv"]), _ptr(res),
+        _ptr(alpha_out), _ptr(iter_out), _ptr(err_out)))
+    if want_residual:
+        out["residual"] = res
+    out.update(alpha=float(alpha_out[0]), iteration=int(iter_out[0]), rel_err=float(err_out[0]))
     return out
 
 

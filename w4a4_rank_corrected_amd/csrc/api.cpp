@@ -83,12 +83,57 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
     }                             \
   } while (0)
 
+bool all_finite(const float* p, size_t count) {
+  for (size_t i = 0; i < count; ++i)
+    if (!std::isfinite(p[i])) return false;
+  return true;
+}
+
 int check_group(int m, int group) {
   REQUIRE(group == SVDQ_GROUP, SVDQ_ERR_UNSUPPORTED, "group must be %d (got %d)", SVDQ_GROUP, group);
   REQUIRE(m >= SVDQ_GROUP && m % SVDQ_GROUP == 0, SVDQ_ERR_UNSUPPORTED,
           "m must be a positive multiple of %d (got %d)", SVDQ_GROUP, m);
   REQUIRE(m <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "m must be <= %d (got %d)", SVDQ_MAX_DIM, m);
   return SVDQ_OK;
+}
+
+// Arguments shared by the preparation entry points.
+int check_prepare(const float* W, const float* act_amax, int m, int n, int rank, int group, const uint8_t* qw,
+                  const uint16_t* wscale, const uint16_t* l1, const uint16_t* l2, const float* lambda,
+                  const float* smooth_inv) {
+  int st = check_group(m, group);
+  if (st) return st;
+  REQUIRE(n >= 1, SVDQ_ERR_INVALID_ARG, "n must be >= 1 (got %d)", n);
+  REQUIRE(n <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "n must be <= %d (got %d)", SVDQ_MAX_DIM, n);
+  REQUIRE(W && qw && wscale && lambda && smooth_inv, SVDQ_ERR_INVALID_ARG,
+          "W, qw, wscale, lambda and smooth_inv must not be NULL");
+  REQUIRE(rank >= 0 && rank <= SVDQ_MAX_RANK, SVDQ_ERR_UNSUPPORTED, "rank must be in [0, %d] (got %d)",
+          SVDQ_MAX_RANK, rank);
+  REQUIRE(rank <= std::min(m, n), SVDQ_ERR_INVALID_ARG, "rank %d exceeds min(m, n) = %d", rank, std::min(m, n));
+  REQUIRE(rank == 0 || (l1 && l2), SVDQ_ERR_INVALID_ARG, "l1 / l2 must not be NULL when rank > 0");
+  REQUIRE(all_finite(W, (size_t)m * n), SVDQ_ERR_NONFINITE, "W holds NaN or Inf");
+  if (act_amax) {
+    REQUIRE(all_finite(act_amax, (size_t)m), SVDQ_ERR_NONFINITE, "act_amax holds NaN or Inf");
+    for (int k = 0; k < m; ++k) REQUIRE(act_amax[k] >= 0.0f, SVDQ_ERR_INVALID_ARG, "act_amax[%d] is negative", k);
+  }
+  return SVDQ_OK;
+}
+
+// Copy a host candidate to the caller's buffers (l1 transposed [rank][m], l2
+// transposed [n][rank]).
+void export_layer(const HostLayer& L, int m, int n, int rank, uint8_t* qw, uint16_t* wscale, uint16_t* l1,
+                  uint16_t* l2, float* lambda, float* smooth_inv, float* residual) {
+  std::memcpy(qw, L.qw.data(), L.qw.size());
+  std::memcpy(wscale, L.wscale.data(), sizeof(uint16_t) * L.wscale.size());
+  std::memcpy(lambda, L.lam32.data(), sizeof(float) * m);
+  std::memcpy(smooth_inv, L.inv32.data(), sizeof(float) * m);
+  if (rank > 0) {
+    for (int i = 0; i < m; ++i)
+      for (int t = 0; t < rank; ++t) l1[(size_t)t * m + i] = L.l1b[(size_t)i * rank + t];
+    for (int t = 0; t < rank; ++t)
+      for (int j = 0; j < n; ++j) l2[(size_t)j * rank + t] = L.l2b[(size_t)t * n + j];
+  }
+  if (residual) std::memcpy(residual, L.r32.data(), sizeof(float) * L.r32.size());
 }
 
 int hip_status(int err, const char* what) {
@@ -151,11 +196,6 @@ int check_y(void* y, int y_dtype, int b) {
   return SVDQ_OK;
 }
 
-bool all_finite(const float* p, size_t count) {
-  for (size_t i = 0; i < count; ++i)
-    if (!std::isfinite(p[i])) return false;
-  return true;
-}
 
 }  // namespace
 
@@ -195,72 +235,70 @@ int svdq_prepare_weights(const float* W, const float* act_amax, int m, int n, in
                          float alpha, uint8_t* qw, uint16_t* wscale, uint16_t* l1, uint16_t* l2,
                          float* lambda, float* smooth_inv, float* residual) {
   clear_error();
-  int st = check_group(m, group);
+  int st = check_prepare(W, act_amax, m, n, rank, group, qw, wscale, l1, l2, lambda, smooth_inv);
   if (st) return st;
-  REQUIRE(n >= 1, SVDQ_ERR_INVALID_ARG, "n must be >= 1 (got %d)", n);
-  REQUIRE(n <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "n must be <= %d (got %d)", SVDQ_MAX_DIM, n);
-  REQUIRE(W && qw && wscale && lambda && smooth_inv, SVDQ_ERR_INVALID_ARG,
-          "W, qw, wscale, lambda and smooth_inv must not be NULL");
-  REQUIRE(rank >= 0 && rank <= SVDQ_MAX_RANK, SVDQ_ERR_UNSUPPORTED, "rank must be in [0, %d] (got %d)",
-          SVDQ_MAX_RANK, rank);
-  REQUIRE(rank <= std::min(m, n), SVDQ_ERR_INVALID_ARG, "rank %d exceeds min(m, n) = %d", rank,
-          std::min(m, n));
-  REQUIRE(rank == 0 || (l1 && l2), SVDQ_ERR_INVALID_ARG, "l1 / l2 must not be NULL when rank > 0");
   REQUIRE(alpha >= 0.0f && alpha <= 1.0f, SVDQ_ERR_INVALID_ARG, "alpha must be in [0, 1] (got %g)",
           (double)alpha);
-  REQUIRE(all_finite(W, (size_t)m * n), SVDQ_ERR_NONFINITE, "W holds NaN or Inf");
-  if (act_amax) {
-    REQUIRE(all_finite(act_amax, (size_t)m), SVDQ_ERR_NONFINITE, "act_amax holds NaN or Inf");
-    for (int k = 0; k < m; ++k)
-      REQUIRE(act_amax[k] >= 0.0f, SVDQ_ERR_INVALID_ARG, "act_amax[%d] is negative", k);
-  }
-
-  std::vector<float> lam32(m), inv32(m);
-  smoothing_lambda(W, act_amax, m, n, (double)alpha, lam32.data(), inv32.data());
-
-  // W~ = diag(lambda) W in fp64 (Eq.(3); products of two fp32 are exact)
-  std::vector<double> wt((size_t)m * n);
-  for (int k = 0; k < m; ++k) {
-    const double lk = lam32[k];
-    for (int j = 0; j < n; ++j) wt[(size_t)k * n + j] = lk * (double)W[(size_t)k * n + j];
-  }
-
-  std::vector<double> L1((size_t)m * rank), L2((size_t)rank * n);
-  if (!truncated_svd(wt.data(), m, n, rank, L1.data(), L2.data())) {
+  HostLayer L;
+  st = build_layer(W, act_amax, m, n, rank, (double)alpha, L);
+  if (st) {
     set_error("truncated SVD did not converge (m=%d n=%d rank=%d)", m, n, rank);
-    return SVDQ_ERR_NO_CONVERGENCE;
+    return st;
   }
-  // stored bf16 factors; the residual is formed with these rounded values
-  std::vector<uint16_t> l1b((size_t)m * rank), l2b((size_t)rank * n);
-  for (size_t i = 0; i < L1.size(); ++i) l1b[i] = f64_to_bf16(L1[i]);
-  for (size_t i = 0; i < L2.size(); ++i) l2b[i] = f64_to_bf16(L2[i]);
-  std::vector<float> r32((size_t)m * n);
-  {
-    std::vector<double> l2d((size_t)rank * n);
-    for (size_t i = 0; i < l2d.size(); ++i) l2d[i] = bf16_to_f32(l2b[i]);
-    std::vector<double> acc(n);
-    for (int i = 0; i < m; ++i) {
-      std::fill(acc.begin(), acc.end(), 0.0);
-      for (int t = 0; t < rank; ++t) {
-        const double a = bf16_to_f32(l1b[(size_t)i * rank + t]);
-        const double* l2row = &l2d[(size_t)t * n];
-        for (int j = 0; j < n; ++j) acc[j] += a * l2row[j];
+  export_layer(L, m, n, rank, qw, wscale, l1, l2, lambda, smooth_inv, residual);
+  return SVDQ_OK;
+}
+
+int svdq_prepare_weights_refined(const float* W, const float* act_amax, const uint16_t* x_cal, int b_cal,
+                                 int m, int n, int rank, int group, const float* alphas, int n_alpha,
+                                 int iters, uint8_t* qw, uint16_t* wscale, uint16_t* l1, uint16_t* l2,
+                                 float* lambda, float* smooth_inv, float* residual, float* alpha_out,
+                                 int* iter_out, double* rel_err_out) {
+  clear_error();
+  int st = check_prepare(W, act_amax, m, n, rank, group, qw, wscale, l1, l2, lambda, smooth_inv);
+  if (st) return st;
+  REQUIRE(x_cal != nullptr && b_cal >= 1, SVDQ_ERR_INVALID_ARG, "x_cal must hold at least one row");
+  REQUIRE(b_cal <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "b_cal must be <= %d (got %d)", SVDQ_MAX_DIM, b_cal);
+  REQUIRE(alphas != nullptr && n_alpha >= 1 && n_alpha <= 64, SVDQ_ERR_INVALID_ARG,
+          "need 1 to 64 migration strengths (got %d)", n_alpha);
+  for (int i = 0; i < n_alpha; ++i)
+    REQUIRE(alphas[i] >= 0.0f && alphas[i] <= 1.0f, SVDQ_ERR_INVALID_ARG, "alphas[%d] = %g is outside [0, 1]", i,
+            (double)alphas[i]);
+  REQUIRE(iters >= 0 && iters <= 16, SVDQ_ERR_INVALID_ARG, "iters must be in [0, 16] (got %d)", iters);
+  std::vector<float> x32((size_t)b_cal * m);
+  for (size_t i = 0; i < x32.size(); ++i) x32[i] = bf16_to_f32(x_cal[i]);
+  REQUIRE(all_finite(x32.data(), x32.size()), SVDQ_ERR_NONFINITE, "x_cal holds NaN or Inf");
+  std::vector<double> yref((size_t)b_cal * n);
+  reference_output(x32.data(), b_cal, W, m, n, yref.data());
+  double ref_sq = 0.0;
+  for (double v : yref) ref_sq += v * v;
+
+  // every (alpha, refinement step) candidate is scored; the first best is kept
+  HostLayer best;
+  double best_sq = -1.0;
+  int best_iter = 0;
+  for (int a = 0; a < n_alpha; ++a) {
+    HostLayer L;
+    st = build_layer(W, act_amax, m, n, rank, (double)alphas[a], L);
+    for (int it = 0; st == SVDQ_OK; ++it) {
+      const double sq = layer_output_sq_error(x32.data(), b_cal, yref.data(), m, n, rank, L);
+      if (best_sq < 0.0 || sq < best_sq) {
+        best_sq = sq;
+        best = L;
+        best_iter = it;
       }
-      for (int j = 0; j < n; ++j) r32[(size_t)i * n + j] = (float)(wt[(size_t)i * n + j] - acc[j]);
+      if (it == iters || rank == 0) break;
+      st = refit_layer(m, n, rank, L);
+    }
+    if (st) {
+      set_error("truncated SVD did not converge (m=%d n=%d rank=%d)", m, n, rank);
+      return st;
     }
   }
-  quantize_residual(r32.data(), m, n, qw, wscale);
-
-  std::memcpy(lambda, lam32.data(), sizeof(float) * m);
-  std::memcpy(smooth_inv, inv32.data(), sizeof(float) * m);
-  if (rank > 0) {
-    // l1 is stored transposed [rank][m]; l2 transposed [n][rank]
-    for (int i = 0; i < m; ++i)
-      for (int t = 0; t < rank; ++t) l1[(size_t)t * m + i] = l1b[(size_t)i * rank + t];
-    for (int t = 0; t < rank; ++t)
-      for (int j = 0; j < n; ++j) l2[(size_t)j * rank + t] = l2b[(size_t)t * n + j];
-  }
-  if (residual) std::memcpy(residual, r32.data(), sizeof(float) * r32.size());
+  export_layer(best, m, n, rank, qw, wscale, l1, l2, lambda, smooth_inv, residual);
+  if (alpha_out) *alpha_out = (float)best.alpha;
+  if (iter_out) *iter_out = best_iter;
+  if (rel_err_out) *rel_err_out = ref_sq > 0.0 ? std::sqrt(best_sq / ref_sq) : std::sqrt(best_sq);
   return SVDQ_OK;
 }
 

@@ -4,6 +4,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <vector>
 
 #include "svdq.h"
 
@@ -28,6 +29,28 @@ void smoothing_lambda(const float* W, const float* act_amax, int m, int n, doubl
 bool truncated_svd(const double* Wt, int m, int n, int r, double* L1, double* L2);
 // INT4 group quantization of R (fp32 [m][n]) into group-major records.
 void quantize_residual(const float* R, int m, int n, uint8_t* qw, uint16_t* wscale);
+
+// One candidate protected layer on the host ([Review] Algorithm 1 steps 2-5).
+struct HostLayer {
+  double alpha = 0.5;
+  std::vector<float> lam32, inv32;    // [m]
+  std::vector<double> wt;             // W~ = diag(lambda) W, [m][n]
+  std::vector<uint16_t> l1b, l2b;     // bf16 factors, L1 [m][r], L2 [r][n] (row-major)
+  std::vector<float> r32;             // residual R = W~ - L1 L2, [m][n]
+  std::vector<uint8_t> qw;            // INT4 codes of R, group-major [m/64][n][32]
+  std::vector<uint16_t> wscale;       // fp16 scales [m/64][n]
+};
+// Steps 2-5 at migration strength alpha (act_amax NULL: lambda = 1).  Returns
+// SVDQ_OK or SVDQ_ERR_NO_CONVERGENCE.
+int build_layer(const float* W, const float* act_amax, int m, int n, int rank, double alpha, HostLayer& L);
+// Steps 6-7: L1 L2 <- rank-r SVD of W~ - Q(R), then R and Q(R) again.
+int refit_layer(int m, int n, int rank, HostLayer& L);
+// Step 8's criterion: ||Y(X) - X W||_F^2 of the quantized layer on calibration
+// rows x32 [b][m] (bf16 values), with X W given (fp64 [b][n]).
+double layer_output_sq_error(const float* x32, int b, const double* yref, int m, int n, int rank,
+                             const HostLayer& L);
+// Y = X W in fp64 (x32 [b][m], W [m][n]).
+void reference_output(const float* x32, int b, const float* W, int m, int n, double* y);
 // Number of worker threads used by the preparation loops.
 int host_threads();
 

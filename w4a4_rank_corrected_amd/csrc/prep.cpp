@@ -379,4 +379,158 @@ void quantize_residual(const float* R, int m, int n, uint8_t* qw, uint16_t* wsca
   }, 256);
 }
 
+// ---------------------------------------------------------------------------
+// protected-layer candidates and their selection ([Review] sec. 5, Algorithm 1)
+// ---------------------------------------------------------------------------
+
+// R = W~ - L1 L2 with the stored bf16 factors (fp64 sums), then its INT4 codes.
+static void form_residual(int m, int n, int rank, HostLayer& L) {
+  std::vector<double> l2d((size_t)rank * n);
+  for (size_t i = 0; i < l2d.size(); ++i) l2d[i] = bf16_to_f32(L.l2b[i]);
+  L.r32.assign((size_t)m * n, 0.0f);
+  parallel_for(m, [&](int64_t lo, int64_t hi) {
+    std::vector<double> acc(n);
+    for (int64_t i = lo; i < hi; ++i) {
+      std::fill(acc.begin(), acc.end(), 0.0);
+      for (int t = 0; t < rank; ++t) {
+        const double a = bf16_to_f32(L.l1b[(size_t)i * rank + t]);
+        const double* row = &l2d[(size_t)t * n];
+        for (int j = 0; j < n; ++j) acc[j] += a * row[j];
+      }
+      for (int j = 0; j < n; ++j) L.r32[(size_t)i * n + j] = (float)(L.wt[(size_t)i * n + j] - acc[j]);
+    }
+  }, 16);
+  L.qw.assign((size_t)m * n / 2, 0);
+  L.wscale.assign((size_t)(m / SVDQ_GROUP) * n, 0);
+  quantize_residual(L.r32.data(), m, n, L.qw.data(), L.wscale.data());
+}
+
+// bf16 factors of the rank-r SVD of A (fp64 [m][n]).
+static bool factor(const double* A, int m, int n, int rank, HostLayer& L) {
+  std::vector<double> L1((size_t)m * rank), L2((size_t)rank * n);
+  if (rank > 0 && !truncated_svd(A, m, n, rank, L1.data(), L2.data())) return false;
+  L.l1b.resize(L1.size());
+  L.l2b.resize(L2.size());
+  for (size_t i = 0; i < L1.size(); ++i) L.l1b[i] = f64_to_bf16(L1[i]);
+  for (size_t i = 0; i < L2.size(); ++i) L.l2b[i] = f64_to_bf16(L2[i]);
+  return true;
+}
+
+int build_layer(const float* W, const float* act_amax, int m, int n, int rank, double alpha, HostLayer& L) {
+  L.alpha = alpha;
+  L.lam32.resize(m);
+  L.inv32.resize(m);
+  smoothing_lambda(W, act_amax, m, n, alpha, L.lam32.data(), L.inv32.data());
+  // W~ = diag(lambda) W in fp64 (Eq.(3); products of two fp32 are exact)
+  L.wt.resize((size_t)m * n);
+  for (int k = 0; k < m; ++k) {
+    const double lk = L.lam32[k];
+    for (int j = 0; j < n; ++j) L.wt[(size_t)k * n + j] = lk * (double)W[(size_t)k * n + j];
+  }
+  if (!factor(L.wt.data(), m, n, rank, L)) return SVDQ_ERR_NO_CONVERGENCE;
+  form_residual(m, n, rank, L);
+  return SVDQ_OK;
+}
+
+// INT4 code k of column j from the group-major records (two's complement nibble).
+static inline int code_at(const HostLayer& L, int n, int k, int j) {
+  const uint8_t byte = L.qw[((size_t)(k / SVDQ_GROUP) * n + j) * 32 + (k % SVDQ_GROUP) / 2];
+  const int nib = (k & 1) ? (byte >> 4) : (byte & 0xF);
+  return nib >= 8 ? nib - 16 : nib;
+}
+
+int refit_layer(int m, int n, int rank, HostLayer& L) {
+  if (rank == 0) return SVDQ_OK;
+  // A = W~ - Q(R) with Q(R) = s * q (exact in fp64)
+  std::vector<double> A((size_t)m * n);
+  parallel_for(m, [&](int64_t lo, int64_t hi) {
+    for (int64_t k = lo; k < hi; ++k)
+      for (int j = 0; j < n; ++j) {
+        const double s = f16_to_f32(L.wscale[(size_t)(k / SVDQ_GROUP) * n + j]);
+        A[(size_t)k * n + j] = L.wt[(size_t)k * n + j] - s * code_at(L, n, (int)k, j);
+      }
+  }, 16);
+  if (!factor(A.data(), m, n, rank, L)) return SVDQ_ERR_NO_CONVERGENCE;
+  form_residual(m, n, rank, L);
+  return SVDQ_OK;
+}
+
+void reference_output(const float* x32, int b, const float* W, int m, int n, double* y) {
+  parallel_for(b, [&](int64_t lo, int64_t hi) {
+    for (int64_t i = lo; i < hi; ++i) {
+      double* yr = y + (size_t)i * n;
+      std::fill(yr, yr + n, 0.0);
+      for (int k = 0; k < m; ++k) {
+        const double xv = x32[(size_t)i * m + k];
+        if (xv == 0.0) continue;
+        const float* wr = W + (size_t)k * n;
+        for (int j = 0; j < n; ++j) yr[j] += xv * (double)wr[j];
+      }
+    }
+  });
+}
+
+double layer_output_sq_error(const float* x32, int b, const double* yref, int m, int n, int rank,
+                             const HostLayer& L) {
+  const int G = m / SVDQ_GROUP;
+  // dequantized weight Q(R) = s q (exact in fp64), [m][n]
+  std::vector<double> wq((size_t)m * n);
+  parallel_for(m, [&](int64_t lo, int64_t hi) {
+    for (int64_t k = lo; k < hi; ++k)
+      for (int j = 0; j < n; ++j)
+        wq[(size_t)k * n + j] = (double)f16_to_f32(L.wscale[(size_t)(k / SVDQ_GROUP) * n + j]) *
+                                code_at(L, n, (int)k, j);
+  }, 16);
+  std::vector<double> l1d((size_t)m * rank), l2d((size_t)rank * n);
+  for (size_t i = 0; i < l1d.size(); ++i) l1d[i] = bf16_to_f32(L.l1b[i]);
+  for (size_t i = 0; i < l2d.size(); ++i) l2d[i] = bf16_to_f32(L.l2b[i]);
+  std::vector<double> rowsq(b, 0.0);  // summed in row order below: deterministic
+  parallel_for(b, [&](int64_t lo, int64_t hi) {
+    std::vector<float> xt(m);
+    std::vector<double> aq(m), y(n), z(rank);
+    for (int64_t i = lo; i < hi; ++i) {
+      double sq = 0.0;
+      // x~ = bf16(fl32(x * inv32)); Q(x~) per 64-channel group (fp32 math, fp16 scale)
+      for (int k = 0; k < m; ++k) {
+        const float v = x32[(size_t)i * m + k] * L.inv32[k];
+        xt[k] = bf16_to_f32(f64_to_bf16((double)v));
+      }
+      for (int g = 0; g < G; ++g) {
+        float amax = 0.0f;
+        for (int kk = 0; kk < SVDQ_GROUP; ++kk) amax = std::max(amax, std::fabs(xt[g * SVDQ_GROUP + kk]));
+        const float s = f16_to_f32(f32_to_f16_sat(amax / 7.0f));
+        for (int kk = 0; kk < SVDQ_GROUP; ++kk) {
+          float q = 0.0f;
+          if (s > 0.0f) q = std::min(7.0f, std::max(-7.0f, std::nearbyint(xt[g * SVDQ_GROUP + kk] / s)));
+          aq[g * SVDQ_GROUP + kk] = (double)s * (double)q;
+        }
+      }
+      // Y = Q(x~) Q(R) + bf16(x~ L1) L2
+      std::fill(y.begin(), y.end(), 0.0);
+      for (int k = 0; k < m; ++k) {
+        if (aq[k] == 0.0) continue;
+        const double* wr = &wq[(size_t)k * n];
+        for (int j = 0; j < n; ++j) y[j] += aq[k] * wr[j];
+      }
+      for (int t = 0; t < rank; ++t) {
+        double acc = 0.0;
+        for (int k = 0; k < m; ++k) acc += (double)xt[k] * l1d[(size_t)k * rank + t];
+        z[t] = bf16_to_f32(f64_to_bf16(acc));
+      }
+      for (int t = 0; t < rank; ++t) {
+        const double* row = &l2d[(size_t)t * n];
+        for (int j = 0; j < n; ++j) y[j] += z[t] * row[j];
+      }
+      for (int j = 0; j < n; ++j) {
+        const double d = y[j] - yref[(size_t)i * n + j];
+        sq += d * d;
+      }
+      rowsq[i] = sq;
+    }
+  });
+  double total = 0.0;
+  for (double v : rowsq) total += v;
+  return total;
+}
+
 }  // namespace svdq
