@@ -258,7 +258,7 @@ def cpu_baseline(inp, cfg, rows):
 
 def prep_refine(names, args):
     """Plain preparation (alpha = 0.5) against the search over migration
-    strengths (0.3 .. 0.7) with two factor-refinement steps (Algorithm 1 steps
+    strengths (0.2 .. 1.0) with two factor-refinement steps (Algorithm 1 steps
     6-8), both by the library on the host.  Calibration: the first 256 rows of
     the workload's X (statistics and candidate scores); evaluation: 512 other
     rows, through the fused GPU layer with fp32 output, against X W in fp64."""
@@ -267,7 +267,7 @@ def prep_refine(names, args):
     import w4a4_rank_corrected_amd as S
 
     dev = torch.device("cuda:0")
-    alphas = (0.3, 0.4, 0.5, 0.6, 0.7)
+    alphas = (0.2, 0.3, 0.4, 0.5, 0.6, 0.7, 0.8, 0.9, 1.0)
     rows = []
     for name in names:
         cfg = workloads.CONFIGS[name]

@@ -158,7 +158,7 @@ def svdq_prepare_weights(W: np.ndarray, act_amax: Optional[np.ndarray], rank: in
 
 
 def svdq_prepare_weights_refined(W: np.ndarray, act_amax: Optional[np.ndarray], x_cal_bits: np.ndarray,
-                                 rank: int, alphas=(0.3, 0.4, 0.5, 0.6, 0.7), iters: int = 2,
+                                 rank: int, alphas=(0.2, 0.3, 0.4, 0.5, 0.6, 0.7, 0.8, 0.9, 1.0), iters: int = 2,
                                  group: int = SVDQ_GROUP, want_residual: bool = False) -> dict:
     """Preparation with a search over migration strengths and factor refinement,
     scored by layer-output error on calibration rows (bf16 bits [b_cal][m]).
