@@ -45,6 +45,11 @@ Readings taken where the pages are silent (each also listed in the design doc):
   R16 the candidate-selection score of Algorithm 1 step 8 is the relative
       Frobenius error of the quantized layer's output against X W (float64) on
       the calibration rows.
+  R19 the 8-bit setting (sec. 8: rank 16, dynamic per-token activation and
+      per-channel weight quantization) uses the same symmetric round-to-nearest
+      quantizer as INT4 with 127 in place of 7: codes in [-127, 127], 16-bit
+      (fp16) scales fp16(fl32(amax / 127)) over a whole row of X~ (per token)
+      or a whole column of R (per output channel).
   R17 the optional factor update of step 6 refits rank-r SVD factors to
       W~ - Q(R) (Q(R) dequantized exactly); the residual of step 7 is then
       formed and quantized again; of equal scores the first candidate
@@ -487,3 +492,60 @@ def naive_w4a4(x32, w32, group: int = GROUP) -> np.ndarray:
     qw, sw = quantize_weight_residual(np.asarray(w32, np.float32), group)
     _, qx, sx = quantize_activation(x32, None, group)
     return gemm_main(qx, sx, qw, sw, group)
+
+
+# --------------------------------------------------------------------------
+# The 8-bit setting ([Review] sec. 8; reading R19): W8A8 with the same
+# smoothing and low-rank branch, per-token / per-channel INT8 quantization.
+# --------------------------------------------------------------------------
+
+QMAX8 = 127
+
+
+def quantize_rows8(v32: np.ndarray):
+    """Symmetric INT8 quantization of each row (last axis) of a float32 array:
+    s = fp16(fl32(amax / 127)), q = clamp(round_half_even(fl32(v / s)), -127, 127),
+    q = 0 where s == 0 (readings R1, R3, R4 with 127 for 7).
+    Returns (codes int16 [..., K], scales float32 [...] holding fp16 values)."""
+    v32 = np.asarray(v32, dtype=np.float32)
+    amax = np.max(np.abs(v32), axis=-1)
+    s = fp16_from_f32_sat(np.float32(amax) / np.float32(QMAX8))
+    sb = s[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        quot = np.where(sb > 0, v32 / np.where(sb > 0, sb, np.float32(1)), np.float32(0)).astype(np.float32)
+    q = np.clip(np.rint(quot), -QMAX8, QMAX8)
+    q = np.where(sb > 0, q, 0).astype(np.int16)
+    return q, s.astype(np.float32)
+
+
+def prepare_weights_w8a8(w32: np.ndarray, a: Optional[np.ndarray], rank: int = 16, alpha: float = 0.5,
+                         svd: str = "lapack") -> dict:
+    """The 8-bit protected layer: smoothing and the rank-r branch as in
+    ``prepare_weights``, the residual quantized per output channel to INT8.
+    Returns lam32, inv32, wt, l1, l2, r64, r32, qw (int16 codes [m][n]),
+    sw (float32 fp16 values [n]), rank."""
+    base = prepare_weights(w32, a, rank, GROUP, alpha, svd)
+    codes_t, sw = quantize_rows8(np.ascontiguousarray(base["r32"].T))
+    return dict(base, qw=np.ascontiguousarray(codes_t.T), sw=sw, bits=8)
+
+
+def quantize_activation_w8a8(x32: np.ndarray, inv32: Optional[np.ndarray]):
+    """Per-token INT8 quantization of the smoothed bf16 activations."""
+    xt = smooth_activation(x32, inv32)
+    qx, sx = quantize_rows8(xt)
+    return xt, qx, sx
+
+
+def linear_w8a8(x32: np.ndarray, layer: dict, bias: Optional[np.ndarray] = None) -> dict:
+    """Y = sx sw (Q8(X~) Q8(R)) + bf16(X~ L1) L2 (+ bias), the integer product
+    exact (int64) and everything else in float64."""
+    xt, qx, sx = quantize_activation_w8a8(x32, layer.get("inv32"))
+    isum = qx.astype(np.int64) @ layer["qw"].astype(np.int64)
+    y = sx.astype(np.float64)[:, None] * isum.astype(np.float64) * layer["sw"].astype(np.float64)[None, :]
+    r = layer["l1"].shape[1]
+    z = lowrank_down(xt, layer["l1"]) if r else np.zeros((x32.shape[0], 0))
+    if r:
+        y = y + lowrank_up(z, layer["l2"])
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)[None, :]
+    return {"y": y, "xt": xt, "qx": qx, "sx": sx, "z": z, "isum": isum}

@@ -1,12 +1,13 @@
 /* Exhaustive host check of the division-free INT4 activation quantizer.
  *
  * Definition (SVDQuant technical review, sec. 2.2 Eq.(1), with the readings
- * ties-to-even, codes in [-7, 7], scale s = fp16(fl32(amax / 7)) saturated,
- * code 0 when s = 0):
- *     code = clamp(round_half_even(fl32(v / s)), -7, 7)
- * Division-free form evaluated by the activation kernel:
+ * ties-to-even, codes in [-Q, Q], scale s = fp16(fl32(amax / Q)) saturated,
+ * code 0 when s = 0; Q = 7 for INT4, 127 for the 8-bit setting):
+ *     code = clamp(round_half_even(fl32(v / s)), -Q, Q)
+ * Division-free form evaluated by the activation kernels:
  *     rc = fl32(1 / s); p = fl32(v * rc); e = fma(-p, s, v); q1 = fma(e, rc, p)
- *     q  = med3(q1, -7, 7);  nibble = bits(fl32(q + 1.5 * 2^23)) & 0xF
+ *     q  = med3(q1, -Q, Q);  code bits = bits(fl32(q + 1.5 * 2^23)) & mask
+ *     (mask 0xF: the nibble; 0xFF: the byte)
  *
  * Every pair the kernel can meet is enumerated: every positive finite bf16
  * group maximum A (with its scale s(A), supplied by the caller as fp16 bits
@@ -14,13 +15,15 @@
  * |v| <= A, both signs.  Prints "pairs mismatches ties nan" and exits 1 on any
  * mismatch or NaN.
  *
- * Usage: quant_exhaustive <table.bin> [nocorr]
- *   table.bin: 32768 uint16, s(A) as fp16 bits for every bf16 bit pattern A;
+ * Usage: quant_exhaustive <table.bin> <Q> [nocorr]
+ *   table.bin: 32768 uint16, s(A) = fp16(fl32(A / Q)) bits for every bf16 A;
+ *   Q:         7 or 127;
  *   nocorr:    drop the correction step (a planted mistake the check must see).
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 static float bf16_to_float(uint32_t b) {
@@ -45,8 +48,12 @@ static uint32_t float_bits(float f) {
 }
 
 int main(int argc, char** argv) {
-  if (argc != 2 && argc != 3) return 2;
-  const int corr = !(argc == 3 && strcmp(argv[2], "nocorr") == 0);
+  if (argc != 3 && argc != 4) return 2;
+  const int Q = atoi(argv[2]);
+  if (Q != 7 && Q != 127) return 2;
+  const float QF = (float)Q;
+  const uint32_t mask = Q == 7 ? 0xFu : 0xFFu;
+  const int corr = !(argc == 4 && strcmp(argv[3], "nocorr") == 0);
   static uint16_t tab[32768];
   FILE* fp = fopen(argv[1], "rb");
   if (!fp || fread(tab, 2, 32768, fp) != 32768) return 2;
@@ -65,8 +72,8 @@ int main(int argc, char** argv) {
           const float d = v / s;
           float rq = nearbyintf(d);              /* default mode: ties to even */
           if (fabsf(d - truncf(d)) == 0.5f) ++ties;
-          if (rq > 7.0f) rq = 7.0f;
-          if (rq < -7.0f) rq = -7.0f;
+          if (rq > QF) rq = QF;
+          if (rq < -QF) rq = -QF;
           code = (int)rq;
         }
         /* division-free form */
@@ -74,9 +81,9 @@ int main(int argc, char** argv) {
         const float e = fmaf(-p, s, v);
         const float q1 = corr ? fmaf(e, rc, p) : p;
         if (isnan(q1)) ++nans;
-        const float q = fminf(fmaxf(q1, -7.0f), 7.0f);
-        const uint32_t nib = float_bits(q + 12582912.0f) & 0xFu;
-        if (nib != ((uint32_t)code & 0xFu)) ++bad;
+        const float q = fminf(fmaxf(q1, -QF), QF);
+        const uint32_t bits = float_bits(q + 12582912.0f) & mask;
+        if (bits != ((uint32_t)code & mask)) ++bad;
         ++pairs;
       }
     }

@@ -527,3 +527,58 @@ def test_refit_factors_is_the_best_rank1_fit_by_power_iteration():
     assert np.linalg.norm(prod - best) <= 1e-2 * np.linalg.norm(best)   # bf16 factors: ~2^-9 each
     # and the residual is formed from the new stored factors
     assert np.array_equal(new["r64"], lay["wt"] - prod)
+
+
+# ---------------------------------------------------------------------------
+# the 8-bit setting (reading R19)
+# ---------------------------------------------------------------------------
+
+def test_quantize_rows8_brute_force():
+    """Each code is the argmin over -127..127 of |v - s q| (ties to even), with
+    s the exact-rational nearest fp16 of fl32(amax / 127)."""
+    rng = np.random.default_rng(8)
+    v = O.bf16_from_f32((rng.standard_normal((6, 96)) * rng.uniform(0.01, 50, (6, 1))).astype(np.float32))
+    v[0, :4] = [12.5, -12.5, 0.0, 127.0]
+    q, s = O.quantize_rows8(v)
+    for i in range(v.shape[0]):
+        amax = Fraction(float(np.max(np.abs(v[i]))))
+        s_f32 = _round_to_grid(amax / 127, 24, -126, Fraction(2) ** 128)
+        s_exact = _round_to_grid(s_f32, 11, -14, Fraction(65504))
+        assert Fraction(float(s[i])) == s_exact
+        for k in range(v.shape[1]):
+            quot = _round_to_grid(Fraction(float(v[i, k])) / s_exact, 24, -126, Fraction(2) ** 128)
+            best = min(range(-127, 128), key=lambda c: (abs(quot - c), c % 2))
+            assert q[i, k] == best
+
+
+def test_w8a8_linear_integer_inputs_are_exact_and_rank0_is_plain_int8_gemm():
+    rng = np.random.default_rng(9)
+    # integers with each row / column reaching 127: scales are 1 and Q is exact
+    x = rng.integers(-127, 128, (6, 128)).astype(np.float32)
+    x[:, 0] = 127
+    w = rng.integers(-127, 128, (128, 10)).astype(np.float32)
+    w[0, :] = -127
+    lay = O.prepare_weights_w8a8(w, None, 0)
+    out = O.linear_w8a8(x, lay)
+    assert np.all(out["sx"] == 1) and np.all(lay["sw"] == 1)
+    assert np.array_equal(out["y"], x.astype(np.float64) @ w.astype(np.float64))
+    # rank 0 on general inputs: dequantized per-token x per-channel product
+    inp = workloads.make_inputs("tiny")
+    lay = O.prepare_weights_w8a8(inp["w"], None, 0)
+    out = O.linear_w8a8(inp["x"], lay)
+    qx, sx = O.quantize_rows8(inp["x"])
+    qw_t, sw = O.quantize_rows8(np.ascontiguousarray(inp["w"].T))
+    ref = (qx * sx[:, None].astype(np.float64)) @ (qw_t * sw[:, None].astype(np.float64)).T
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-13, atol=1e-12)
+
+
+def test_w8a8_error_below_w4a4_on_an_outlier_layer():
+    """Direction only (the pages give no margin): eight bits per value leave a
+    smaller output error than four on the same synthetic outlier layer."""
+    inp = workloads.make_inputs("tiny")
+    x, w = inp["x"], inp["w"]
+    a = O.act_amax(x)
+    ref = x.astype(np.float64) @ w.astype(np.float64)
+    e8 = np.linalg.norm(O.linear_w8a8(x, O.prepare_weights_w8a8(w, a, 16))["y"] - ref)
+    e4 = np.linalg.norm(O.linear(x, O.prepare_weights(w, a, 16))["y"] - ref)
+    assert e8 < e4

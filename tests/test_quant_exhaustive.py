@@ -1,4 +1,5 @@
-"""Exhaustive host proof of the activation kernel's division-free quantizer.
+"""Exhaustive host proof of the activation kernels' division-free quantizer
+(INT4 codes, maximum 7, and the 8-bit setting's codes, maximum 127).
 
 The activation kernel never divides by the group scale s: it forms
 rc = fl32(1/s), p = fl32(v rc), the exact remainder e = fma(-p, s, v) and one
@@ -27,24 +28,26 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "native", "quant_exhaustive.c")
 
 
-def _scale_table():
+def _scale_table(q):
     a = (np.arange(32768, dtype=np.uint32) << np.uint32(16)).view(np.float32)
     fin = np.isfinite(a)
     with np.errstate(all="ignore"):
-        s = np.minimum(a / np.float32(7.0), np.float32(65504.0)).astype(np.float32).astype(np.float16)
+        s = np.minimum(a / np.float32(q), np.float32(65504.0)).astype(np.float32).astype(np.float16)
     s[~fin] = 0
     return a, fin, s
 
 
-def test_scale_table_matches_oracle():
-    a, fin, s = _scale_table()
+@pytest.mark.parametrize("q", [7, 127])
+def test_scale_table_matches_oracle(q):
+    a, fin, s = _scale_table(q)
     pos = fin & (a >= 0)
     amax = a[pos]
-    # one group per A: the maximum itself followed by zeros
+    # one group (row) per A: the maximum itself followed by zeros
     groups = np.zeros((amax.size, 64), np.float32)
     groups[:, 0] = amax
-    _, sc = O.quantize_groups(groups)
-    assert np.array_equal(sc[:, 0], s[pos].astype(np.float32))
+    _, sc = O.quantize_groups(groups) if q == 7 else O.quantize_rows8(groups)
+    sc = sc[:, 0] if sc.ndim == 2 else sc
+    assert np.array_equal(sc, s[pos].astype(np.float32))
 
 
 @pytest.fixture(scope="module")
@@ -55,14 +58,17 @@ def checker(tmp_path_factory):
     exe = str(d / "quant_exhaustive")
     subprocess.check_call(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
                            "-o", exe, SRC, "-lm"])
-    tab = str(d / "tab.bin")
-    _scale_table()[2].view(np.uint16).tofile(tab)
-    return exe, tab
+    tabs = {}
+    for q in (7, 127):
+        tabs[q] = str(d / f"tab{q}.bin")
+        _scale_table(q)[2].view(np.uint16).tofile(tabs[q])
+    return exe, tabs
 
 
-def test_division_free_quantizer_exhaustive(checker):
-    exe, tab = checker
-    r = subprocess.run([exe, tab], capture_output=True, text=True, timeout=600)
+@pytest.mark.parametrize("q", [7, 127])
+def test_division_free_quantizer_exhaustive(checker, q):
+    exe, tabs = checker
+    r = subprocess.run([exe, tabs[q], str(q)], capture_output=True, text=True, timeout=600)
     pairs, bad, ties, nans = map(int, r.stdout.split())
     assert pairs == 1065402238          # sum over A of 2 (A + 1), A = 1 .. 0x7F7F
     assert ties > 0                     # exact .5 quotients are exercised
@@ -70,7 +76,7 @@ def test_division_free_quantizer_exhaustive(checker):
 
 
 def test_checker_catches_missing_correction(checker):
-    exe, tab = checker
-    r = subprocess.run([exe, tab, "nocorr"], capture_output=True, text=True, timeout=600)
+    exe, tabs = checker
+    r = subprocess.run([exe, tabs[7], "7", "nocorr"], capture_output=True, text=True, timeout=600)
     pairs, bad, ties, nans = map(int, r.stdout.split())
     assert bad > 0 and r.returncode == 1
