@@ -372,6 +372,89 @@ def fusion_ab(cfg, ranks, args):
           flush=True)
 
 
+def w8a8_compare(cfg, rank, args):
+    """The 8-bit setting (per-token / per-channel INT8 + the rank-r branch)
+    against W4A4 at the same rank, on layers the library prepares from the
+    workload's X and W.  Warm timing: the four calls (W4A4 activation kernel,
+    W4A4 GEMM, 8-bit activation kernels, 8-bit GEMM) alternate step by step,
+    HIP events around each on the launch stream, median over the steps.  The
+    output error of each against the unquantized product X W (fp64, numpy) is
+    measured on sampled rows."""
+    import torch
+    import workloads
+    import w4a4_rank_corrected_amd as S
+
+    inp = workloads.make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(inp["x_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    b, m, n = x.shape[0], cfg.m, cfg.n
+    amax = S.svdq_calibrate_act_amax(x).cpu().numpy()
+    out_dtype = torch.bfloat16 if args.out == "bf16" else torch.float32
+    stream = torch.cuda.current_stream(dev)
+    l4 = S.DeviceLayer(S.svdq_prepare_weights(inp["w"], amax, rank), device=dev)
+    l8 = S.DeviceLayer8(S.svdq_w8a8_prepare_weights(inp["w"], amax, rank), device=dev)
+    G = m // 64
+    y4 = torch.empty((b, n), dtype=out_dtype, device=dev)
+    y8 = torch.empty((b, n), dtype=out_dtype, device=dev)
+    qx4 = torch.empty((G, b, 32), dtype=torch.uint8, device=dev)
+    as4 = torch.empty((G, b), dtype=torch.float16, device=dev)
+    qx8 = torch.empty((G, b, 64), dtype=torch.int8, device=dev)
+    as8 = torch.empty(b, dtype=torch.float16, device=dev)
+    z = torch.empty((b, max(rank, 1)), dtype=torch.float32, device=dev) if rank else None
+    aws = torch.empty(max(S.svdq_act_workspace_size(b, m, rank), 1), dtype=torch.uint8, device=dev)
+    gws = torch.empty(max(S.svdq_gemm_workspace_size(b, n, m), 1), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        calls = [
+            lambda: S.svdq_quantize_act_lowrank_down(x, l4.smooth_inv, l4.l1, rank, qx=qx4, ascale=as4, z=z,
+                                                     workspace=aws, stream=stream),
+            lambda: S.svdq_gemm_w4a4_lowrank_up(qx4, as4, z, l4, b, out_dtype, y=y4, workspace=gws, stream=stream),
+            lambda: S.svdq_w8a8_quantize_act_lowrank_down(x, l8.smooth_inv, l8.l1, rank, qx=qx8, ascale=as8, z=z,
+                                                          workspace=aws, stream=stream),
+            lambda: S.svdq_w8a8_gemm_lowrank_up(qx8, as8, z, l8, b, out_dtype, y=y8, workspace=gws,
+                                                stream=stream),
+        ]
+        for k, c in enumerate(calls):
+            if ev is not None:
+                ev[k].record(stream)
+            c()
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(max(50, args.warmup)):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    t = [float(np.median([e[k].elapsed_time(e[k + 1]) for e in evs])) for k in range(4)]
+    # accuracy on sampled rows against the unquantized product
+    rows = np.arange(0, b, max(1, b // 64))
+    xr = (inp["x_bits"][rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    yref = xr @ inp["w"].astype(np.float64)
+
+    def err(y):
+        yv = y[torch.from_numpy(rows).to(dev)].float().cpu().numpy().astype(np.float64)
+        return float(np.linalg.norm(yv - yref) / np.linalg.norm(yref))
+
+    ops = 2.0 * b * m * n
+    res = {"w8a8_vs_w4a4": {
+        "workload": cfg.name, "b": b, "m": m, "n": n, "rank": rank, "out": args.out, "steps": args.steps,
+        "timing": "warm; the four calls alternate; median of HIP-event times",
+        "w4a4": {"act_ms": round(t[0], 5), "gemm_ms": round(t[1], 5), "total_ms": round(t[0] + t[1], 5),
+                 "gemm_TOPs": round(ops / (t[1] * 1e-3) / 1e12, 1),
+                 "gemm_frac_i8_peak": round(ops / (t[1] * 1e-3) / 1e12 / I8_PEAK_TOPS, 4),
+                 "rel_err_vs_xw": round(err(y4), 6)},
+        "w8a8": {"act_ms": round(t[2], 5), "gemm_ms": round(t[3], 5), "total_ms": round(t[2] + t[3], 5),
+                 "gemm_TOPs": round(ops / (t[3] * 1e-3) / 1e12, 1),
+                 "gemm_frac_i8_peak": round(ops / (t[3] * 1e-3) / 1e12 / I8_PEAK_TOPS, 4),
+                 "rel_err_vs_xw": round(err(y8), 6)},
+    }}
+    log(f"w8a8 {cfg.name} rank {rank}: W4A4 {t[0] * 1e3:.1f} + {t[1] * 1e3:.1f} us, "
+        f"W8A8 {t[2] * 1e3:.1f} + {t[3] * 1e3:.1f} us")
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -393,6 +476,8 @@ def main():
                     metavar="WORKLOADS", help="refined vs plain preparation, output error on held-out rows")
     ap.add_argument("--fusion-ab", nargs="?", const="0,16,32,48,64,128", default=None, metavar="RANKS",
                     help="fused vs unfused timing at these ranks (comma-separated) instead of the metric")
+    ap.add_argument("--w8a8", nargs="?", const=16, default=None, type=int, metavar="RANK",
+                    help="8-bit setting against W4A4 at this rank (default 16) instead of the metric")
     args = ap.parse_args()
 
     if args.traffic_summary:
@@ -421,6 +506,9 @@ def main():
     cfg = workloads.CONFIGS[args.workload]
     if args.fusion_ab is not None:
         fusion_ab(cfg, [int(v) for v in args.fusion_ab.split(",")], args)
+        return
+    if args.w8a8 is not None:
+        w8a8_compare(cfg, args.w8a8, args)
         return
     m, n = cfg.m, cfg.n
     rank_svd = cfg.rank if args.rank is None else args.rank

@@ -252,6 +252,90 @@ size_t svdq_linear_unfused_workspace_size(int b, int m, int n, int rank, int gro
 int svdq_linear_unfused(const uint16_t* x, const svdq_layer* layer, int b, void* y, int y_dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* ===========================================================================
+ * The 8-bit setting ([Review] sec. 8: W8A8 keeps the smoothing and the
+ * low-rank branch, rank 16 there, with one scale per token of X~ and one per
+ * output channel of R).
+ *   - INT8 codes are symmetric in [-127, 127], one per byte (int8_t): for a
+ *     row v of X~ (or a column of R), s = fp16(fl32(max|v| / 127)) saturated,
+ *     code = clamp(round_half_even(fl32(v / s)), -127, 127), 0 where s = 0
+ *     (the INT4 quantizer of [Review] sec. 2.2 Eq.(1) with 127 for 7).
+ *   - Code tensors are GROUP-MAJOR in 64-byte records: for channels
+ *     64g..64g+63 and row (or column) r, one record holds their 64 codes in
+ *     channel order; a tensor of R rows is laid out [m/64][R][64].
+ *   - m <= SVDQ_W8A8_MAX_M, so the exact integer products over all m channels
+ *     (at most 127^2 m in magnitude) fit in int32.
+ * Other conventions as above.
+ * ========================================================================= */
+#define SVDQ_W8A8_MAX_M 131072
+
+/* A prepared 8-bit layer on the device (caller-owned DEVICE pointers).
+ *   m, n, rank  as in svdq_layer (m % 64 == 0, m <= SVDQ_W8A8_MAX_M).
+ *   smooth_inv  fp32 [m] or NULL; l1 bf16 [rank][m]; l2 bf16 [n][rank]
+ *               (any alignment); bias bf16 [n] or NULL: as in svdq_layer.
+ *   qw          INT8 codes of R, group-major [m/64][n][64].
+ *   wscale      fp16 [n]: one scale per output column (any 2-byte alignment). */
+typedef struct svdq_w8a8_layer {
+  int32_t m, n, rank;
+  const float* smooth_inv;
+  const int8_t* qw;
+  const uint16_t* wscale;
+  const uint16_t* l1;
+  const uint16_t* l2;
+  const uint16_t* bias;
+} svdq_w8a8_layer;
+
+/* HOST: offline preparation of an 8-bit layer: steps 2-4 of [Review]
+ * Algorithm 1 exactly as svdq_prepare_weights (lambda, W~, bf16 rank-r
+ * factors, R = W~ - L1 L2), then R quantized per output column to INT8.
+ * Outputs (HOST, caller-allocated): qw [m/64][n][64], wscale fp16 [n],
+ * l1 [rank][m], l2 [n][rank], lambda, smooth_inv fp32 [m], residual fp32
+ * [m][n] (nullable).  Errors as svdq_prepare_weights; m <= SVDQ_W8A8_MAX_M. */
+int svdq_w8a8_prepare_weights(const float* W, const float* act_amax, int m, int n, int rank,
+                              float alpha, int8_t* qw, uint16_t* wscale, uint16_t* l1,
+                              uint16_t* l2, float* lambda, float* smooth_inv, float* residual);
+
+/* Bytes of device workspace svdq_w8a8_quantize_act_lowrank_down needs (the
+ * split partial sums of Z, as svdq_act_workspace_size; 0 when none). */
+size_t svdq_w8a8_act_workspace_size(int b, int m, int rank);
+
+/* DEVICE: per-token activation quantization + low-rank down-projection.
+ *     x~ = bf16(fl32(x * smooth_inv))
+ *     ascale[i] = fp16(fl32(max_k |x~[i,k]| / 127)),  qx = the INT8 codes of x~
+ *     z = x~ L1 (fp32 accumulation; the same kernel and summation order as
+ *       svdq_quantize_act_lowrank_down, so z is bit-identical to its z)
+ * A row's scale needs the whole row, so the codes come from a kernel of their
+ * own (one wave per row) and x is read a second time for z.
+ *   x bf16 [b][m]; outputs qx [m/64][b][64], ascale fp16 [b] (any 2-byte
+ *   alignment), z fp32 [b][rank] (NULL iff rank == 0).  Other arguments as
+ *   svdq_quantize_act_lowrank_down. */
+int svdq_w8a8_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int rank,
+                                        const float* smooth_inv, const uint16_t* l1, int8_t* qx,
+                                        uint16_t* ascale, float* z, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace svdq_w8a8_gemm_lowrank_up may need (int32 partial
+ * tiles and flags of its stream-K schedule; an upper bound on every gfx950). */
+size_t svdq_w8a8_gemm_workspace_size(int b, int n, int m);
+
+/* DEVICE: 8-bit GEMM + low-rank up-projection:
+ *     isum[i,j] = sum_k qx[i,k] qw[k,j]                    (exact, int32)
+ *     Y[i,j] = fl32(fl32(isum) * (ascale[i] wscale[j])) + (bf16(z) L2)[i,j] + bias[j]
+ *   qx, ascale, z as produced by svdq_w8a8_quantize_act_lowrank_down; y, the
+ *   workspace and determinism as svdq_gemm_w4a4_lowrank_up. */
+int svdq_w8a8_gemm_lowrank_up(const int8_t* qx, const uint16_t* ascale, const float* z,
+                              const svdq_w8a8_layer* layer, int b, void* y, int y_dtype,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace svdq_w8a8_linear needs. */
+size_t svdq_w8a8_linear_workspace_size(int b, int m, int n, int rank);
+
+/* DEVICE: the whole 8-bit layer: exactly the kernels of the two entry points
+ * above, back to back on `stream` (bit-identical output).  Arguments as
+ * svdq_linear. */
+int svdq_w8a8_linear(const uint16_t* x, const svdq_w8a8_layer* layer, int b, void* y, int y_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

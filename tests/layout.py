@@ -81,3 +81,33 @@ def host_abi_to_oracle_layer(host: dict) -> dict:
         "inv32": np.asarray(host["smooth_inv"], np.float32),
         "lam32": np.asarray(host["lambda"], np.float32),
     }
+
+
+# ---- the 8-bit setting: one code per byte, 64-byte group-major records ----------
+
+def pack_codes8(codes: np.ndarray) -> np.ndarray:
+    """integer codes [R][K] in [-127, 127] -> int8 records [K/64][R][64]."""
+    R, K = codes.shape
+    c = np.asarray(codes).astype(np.int8).reshape(R, K // GROUP, GROUP)
+    return np.ascontiguousarray(c.transpose(1, 0, 2))
+
+
+def unpack_codes8(recs: np.ndarray) -> np.ndarray:
+    """int8 records [G][R][64] -> codes int16 [R][G*64]."""
+    recs = np.asarray(recs, dtype=np.int8)
+    G, R, _ = recs.shape
+    return np.ascontiguousarray(recs.transpose(1, 0, 2).reshape(R, G * GROUP)).astype(np.int16)
+
+
+def oracle_w8a8_to_host_abi(lay: dict) -> dict:
+    """Oracle-prepared 8-bit layer -> host arrays in the ABI layouts."""
+    m, n = lay["qw"].shape
+    inv = lay.get("inv32")
+    return {
+        "m": m, "n": n, "rank": lay["l1"].shape[1],
+        "qw": pack_codes8(np.ascontiguousarray(lay["qw"].T)),
+        "wscale": f32_to_fp16_bits(lay["sw"]),
+        "l1": np.ascontiguousarray(f32_to_bf16_bits(lay["l1"]).T),
+        "l2": np.ascontiguousarray(f32_to_bf16_bits(lay["l2"]).T),
+        "smooth_inv": np.ones(m, np.float32) if inv is None else np.asarray(inv, np.float32),
+    }

@@ -32,7 +32,7 @@ def test_exports_every_symbol_declared_in_header():
     for nm in names:
         assert hasattr(L, nm), nm
     assert {s[0] for s in B.SIGNATURES} == names
-    assert L.svdq_abi_version() == 100
+    assert L.svdq_abi_version() == 101
 
 
 def test_status_strings():
@@ -348,4 +348,111 @@ def test_refined_validation_errors():
     assert e.value.status == B.SVDQ_ERR_INVALID_ARG
     with pytest.raises(B.SvdqError) as e:
         S.svdq_prepare_weights_refined(w, None, np.zeros((0, 128), np.uint16), 8)
+    assert e.value.status == B.SVDQ_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# the 8-bit setting: host preparation and validation
+# ---------------------------------------------------------------------------
+
+def _codes8_by_column(qw):
+    """[m/64][n][64] int8 records -> codes [n][m]."""
+    G, n, _ = qw.shape
+    return np.ascontiguousarray(qw.transpose(1, 0, 2).reshape(n, G * 64)).astype(np.int16)
+
+
+def test_w8a8_prepare_shares_steps_2_to_4_and_quantizes_per_column(tiny):
+    _lib_or_skip()
+    inp, a, _ = tiny
+    p4 = S.svdq_prepare_weights(inp["w"], a, 16, want_residual=True)
+    p8 = S.svdq_w8a8_prepare_weights(inp["w"], a, 16, want_residual=True)
+    for k in ("lambda", "smooth_inv", "l1", "l2", "residual"):
+        assert np.array_equal(p4[k], p8[k]), k
+    codes, sw = O.quantize_rows8(np.ascontiguousarray(p8["residual"].T))
+    assert np.array_equal(_codes8_by_column(p8["qw"]), codes)
+    assert np.array_equal(p8["wscale"], LY.f32_to_fp16_bits(sw))
+
+
+def test_w8a8_quantizer_adversarial_columns():
+    _lib_or_skip()
+    rng = np.random.default_rng(8)
+    R = (rng.standard_normal((256, 40)) * np.exp(rng.uniform(-6, 6, (1, 40)))).astype(np.float32)
+    R[:, 0] = 0.0                                     # all-zero column
+    R[:, 1] = 1e-9                                    # underflowing scale
+    R[:, 2] = np.tile([127.0, 2.5, 3.5, -2.5, 0.5, 1.5, -127.0, 0.0], 32)  # exact ties
+    R[:, 3] = 1e8                                     # saturating scale
+    R[0, 4] = -3e5
+    p = S.svdq_w8a8_prepare_weights(R, None, 0, want_residual=True)   # rank 0, lambda = 1: R = W
+    assert np.array_equal(p["residual"], R)
+    codes, sw = O.quantize_rows8(np.ascontiguousarray(R.T))
+    assert np.array_equal(_codes8_by_column(p["qw"]), codes)
+    assert np.array_equal(p["wscale"], LY.f32_to_fp16_bits(sw))
+    assert codes[2].tolist()[:8] == [127, 2, 4, -2, 0, 2, -127, 0]
+
+
+def _layer8(**kw):
+    d = dict(m=128, n=64, rank=8, smooth_inv=None, qw=FAKE, wscale=FAKE, l1=FAKE, l2=FAKE, bias=None)
+    d.update(kw)
+    return B.svdq_w8a8_layer(d["m"], d["n"], d["rank"], d["smooth_inv"], d["qw"], d["wscale"], d["l1"],
+                             d["l2"], d["bias"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(m=100), B.SVDQ_ERR_UNSUPPORTED),
+    (dict(m=B.SVDQ_W8A8_MAX_M + 64), B.SVDQ_ERR_UNSUPPORTED),
+    (dict(n=0), B.SVDQ_ERR_INVALID_ARG),
+    (dict(rank=300), B.SVDQ_ERR_UNSUPPORTED),
+    (dict(qw=None), B.SVDQ_ERR_INVALID_ARG),
+    (dict(qw=FAKE + 8), B.SVDQ_ERR_ALIGNMENT),
+    (dict(wscale=FAKE + 1), B.SVDQ_ERR_ALIGNMENT),
+    (dict(l2=None), B.SVDQ_ERR_INVALID_ARG),
+    (dict(l1=None), B.SVDQ_ERR_INVALID_ARG),
+])
+def test_w8a8_linear_validation_errors(kw, code):
+    L = _lib_or_skip()
+    lay = _layer8(**kw)
+    st = L.svdq_w8a8_linear(FAKE, ctypes.byref(lay), 16, FAKE, B.SVDQ_OUT_BF16, FAKE, 1 << 30, None)
+    assert st == code, L.svdq_last_error()
+    assert L.svdq_last_error()
+
+
+def test_w8a8_act_gemm_workspace_validation():
+    L = _lib_or_skip()
+    lay = _layer8()
+    need = L.svdq_w8a8_linear_workspace_size(16, 128, 64, 8)
+    assert need > 0 and need % 256 == 0
+    f = L.svdq_w8a8_linear
+    assert f(FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE, need - 1, None) == B.SVDQ_ERR_WORKSPACE
+    assert f(FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE + 16, need, None) == B.SVDQ_ERR_ALIGNMENT
+    assert f(FAKE, ctypes.byref(lay), 16, FAKE, 5, FAKE, need, None) == B.SVDQ_ERR_INVALID_ARG
+    assert f(FAKE, ctypes.byref(lay), 0, None, 0, None, 0, None) == B.SVDQ_OK
+    a = L.svdq_w8a8_quantize_act_lowrank_down
+    assert a(FAKE, 16, 96, 8, None, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.SVDQ_ERR_UNSUPPORTED
+    assert a(FAKE, 16, B.SVDQ_W8A8_MAX_M + 64, 0, None, None, FAKE, FAKE, None, None, 0, None) == \
+        B.SVDQ_ERR_UNSUPPORTED
+    assert a(FAKE, 16, 128, 8, None, None, FAKE, FAKE, FAKE, None, 0, None) == B.SVDQ_ERR_INVALID_ARG
+    assert a(FAKE, 16, 128, 0, None, None, FAKE + 8, FAKE, None, None, 0, None) == B.SVDQ_ERR_ALIGNMENT
+    assert a(FAKE, 16, 128, 0, None, None, FAKE, FAKE + 1, None, None, 0, None) == B.SVDQ_ERR_ALIGNMENT
+    assert a(FAKE, 0, 128, 8, None, None, None, None, None, None, 0, None) == B.SVDQ_OK
+    assert L.svdq_w8a8_act_workspace_size(64, 4096, 32) == L.svdq_act_workspace_size(64, 4096, 32) > 0
+    assert a(FAKE, 64, 4096, 32, None, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.SVDQ_ERR_WORKSPACE
+    g = L.svdq_w8a8_gemm_lowrank_up
+    gneed = L.svdq_w8a8_gemm_workspace_size(16, 64, 128)
+    assert gneed == L.svdq_gemm_workspace_size(16, 64, 128) > 0
+    assert g(FAKE, FAKE, None, ctypes.byref(lay), 16, FAKE, 0, FAKE, gneed, None) == B.SVDQ_ERR_INVALID_ARG
+    assert g(FAKE + 4, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE, gneed, None) == B.SVDQ_ERR_ALIGNMENT
+    assert g(FAKE, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE, gneed - 1, None) == B.SVDQ_ERR_WORKSPACE
+    for (b, m, n, r) in [(1, 64, 8, 0), (37, 256, 200, 16), (4096, 3072, 9216, 16)]:
+        w = L.svdq_w8a8_linear_workspace_size(b, m, n, r)
+        assert w >= m * b + 2 * b + b * r * 4 + L.svdq_w8a8_gemm_workspace_size(b, n, m)
+    assert L.svdq_w8a8_linear_workspace_size(16, B.SVDQ_W8A8_MAX_M + 64, 8, 8) == 0
+
+
+def test_w8a8_prepare_validation_errors():
+    _lib_or_skip()
+    with pytest.raises(B.SvdqError) as e:
+        S.svdq_w8a8_prepare_weights(np.ones((128, 32), np.float32), None, 64)
+    assert e.value.status == B.SVDQ_ERR_INVALID_ARG
+    with pytest.raises(B.SvdqError) as e:
+        S.svdq_w8a8_prepare_weights(np.ones((128, 32), np.float32), None, 4, alpha=-0.1)
     assert e.value.status == B.SVDQ_ERR_INVALID_ARG

@@ -9,7 +9,9 @@ from ._binding import (  # noqa: F401
     svdq_act_workspace_size, svdq_append_lora, svdq_gemm_workspace_size, svdq_calibrate_act_amax, svdq_gemm_w4a4_lowrank_up,
     svdq_linear, svdq_linear_workspace_size, svdq_linear_unfused, svdq_linear_unfused_workspace_size,
     svdq_prepare_weights, svdq_prepare_weights_refined, svdq_quantize_act_lowrank_down,
-    svdq_quantize_residual)
+    svdq_quantize_residual, SVDQ_W8A8_MAX_M, DeviceLayer8, svdq_w8a8_act_workspace_size,
+    svdq_w8a8_gemm_lowrank_up, svdq_w8a8_gemm_workspace_size, svdq_w8a8_linear,
+    svdq_w8a8_linear_workspace_size, svdq_w8a8_prepare_weights, svdq_w8a8_quantize_act_lowrank_down)
 
 __all__ = [
     "SVDQ_GROUP", "SVDQ_MAX_RANK", "SVDQ_OUT_BF16", "SVDQ_OUT_F32", "SvdqError", "DeviceLayer",
@@ -18,5 +20,7 @@ __all__ = [
     "svdq_gemm_w4a4_lowrank_up", "svdq_linear", "svdq_linear_workspace_size",
     "svdq_linear_unfused", "svdq_linear_unfused_workspace_size",
     "svdq_prepare_weights", "svdq_prepare_weights_refined", "svdq_quantize_act_lowrank_down",
-    "svdq_quantize_residual",
+    "svdq_quantize_residual", "SVDQ_W8A8_MAX_M", "DeviceLayer8", "svdq_w8a8_act_workspace_size",
+    "svdq_w8a8_gemm_lowrank_up", "svdq_w8a8_gemm_workspace_size", "svdq_w8a8_linear",
+    "svdq_w8a8_linear_workspace_size", "svdq_w8a8_prepare_weights", "svdq_w8a8_quantize_act_lowrank_down",
 ]

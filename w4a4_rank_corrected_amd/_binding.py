@@ -26,6 +26,7 @@ SVDQ_OUT_F32 = 1
 SVDQ_GROUP = 64
 SVDQ_MAX_RANK = 256
 SVDQ_MAX_DIM = 1 << 22
+SVDQ_W8A8_MAX_M = 131072
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsvdq.so")
 
@@ -39,6 +40,12 @@ class svdq_layer(ctypes.Structure):
     _fields_ = [("m", ctypes.c_int32), ("n", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("smooth_inv", _vp), ("qw", _vp), ("wscale", _vp),
                 ("l1", _vp), ("l2", _vp), ("bias", _vp)]
+
+
+class svdq_w8a8_layer(ctypes.Structure):
+    """Mirror of ``struct svdq_w8a8_layer`` (all pointers are device addresses)."""
+    _fields_ = [("m", ctypes.c_int32), ("n", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("smooth_inv", _vp), ("qw", _vp), ("wscale", _vp), ("l1", _vp), ("l2", _vp), ("bias", _vp)]
 
 
 # (name, restype, argtypes) for every exported symbol of include/svdq.h
@@ -67,6 +74,17 @@ SIGNATURES = [
     ("svdq_status_string", ctypes.c_char_p, [_c_int]),
     ("svdq_last_error", ctypes.c_char_p, []),
     ("svdq_abi_version", _c_int, []),
+    ("svdq_w8a8_prepare_weights", _c_int,
+     [_vp, _vp, _c_int, _c_int, _c_int, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    ("svdq_w8a8_act_workspace_size", _size, [_c_int, _c_int, _c_int]),
+    ("svdq_w8a8_quantize_act_lowrank_down", _c_int,
+     [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _size, _vp]),
+    ("svdq_w8a8_gemm_workspace_size", _size, [_c_int, _c_int, _c_int]),
+    ("svdq_w8a8_gemm_lowrank_up", _c_int,
+     [_vp, _vp, _vp, ctypes.POINTER(svdq_w8a8_layer), _c_int, _vp, _c_int, _vp, _size, _vp]),
+    ("svdq_w8a8_linear_workspace_size", _size, [_c_int, _c_int, _c_int, _c_int]),
+    ("svdq_w8a8_linear", _c_int,
+     [_vp, ctypes.POINTER(svdq_w8a8_layer), _c_int, _vp, _c_int, _vp, _size, _vp]),
 ]
 
 _lib = None
@@ -349,4 +367,120 @@ def svdq_linear_unfused(x, layer: DeviceLayer, out_dtype=None, y=None, workspace
     wsb = workspace.numel() * workspace.element_size()
     _check(lib().svdq_linear_unfused(_ptr(x), ctypes.byref(layer.struct), b, _ptr(y), code,
                                      _ptr(workspace), wsb, _stream(stream)))
+    return y
+
+
+# ---------------------------------------------------------------------------
+# the 8-bit setting (per-token / per-channel INT8 with the low-rank branch)
+# ---------------------------------------------------------------------------
+
+def svdq_w8a8_prepare_weights(W: np.ndarray, act_amax: Optional[np.ndarray], rank: int, alpha: float = 0.5,
+                              want_residual: bool = False) -> dict:
+    """Host preparation of an 8-bit layer.  Keys: qw int8 [m/64][n][64],
+    wscale uint16 (fp16 bits) [n], l1, l2, lambda, smooth_inv, residual (if
+    requested), m, n, rank."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    m, n = W.shape
+    a = None if act_amax is None else np.ascontiguousarray(act_amax, dtype=np.float32)
+    out = {
+        "qw": np.zeros((max(m // SVDQ_GROUP, 0), n, 64), np.int8),
+        "wscale": np.zeros(n, np.uint16),
+        "l1": np.zeros((rank, m), np.uint16),
+        "l2": np.zeros((n, rank), np.uint16),
+        "lambda": np.zeros(m, np.float32),
+        "smooth_inv": np.zeros(m, np.float32),
+        "m": m, "n": n, "rank": rank,
+    }
+    res = np.zeros((m, n), np.float32) if want_residual else None
+    _check(lib().svdq_w8a8_prepare_weights(
+        _ptr(W), _ptr(a), m, n, rank, alpha, _ptr(out["qw"]), _ptr(out["wscale"]),
+        _ptr(out["l1"]) if rank else None, _ptr(out["l2"]) if rank else None,
+        _ptr(out["lambda"]), _ptr(out["smooth_inv"]), _ptr(res)))
+    if want_residual:
+        out["residual"] = res
+    return out
+
+
+class DeviceLayer8:
+    """A prepared 8-bit layer resident in device memory plus its ``svdq_w8a8_layer`` struct."""
+
+    def __init__(self, host: dict, device="cuda", bias: Optional[np.ndarray] = None, smoothing: bool = True):
+        import torch
+        self.m, self.n, self.rank = int(host["m"]), int(host["n"]), int(host["rank"])
+        t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(device=device).view(dt)
+        self.qw = t(host["qw"], torch.int8)
+        self.wscale = t(host["wscale"].view(np.int16), torch.float16)
+        self.smooth_inv = t(host["smooth_inv"], torch.float32) if smoothing else None
+        self.l1 = t(host["l1"].view(np.int16), torch.bfloat16) if self.rank else None
+        self.l2 = t(host["l2"].view(np.int16), torch.bfloat16) if self.rank else None
+        self.bias = None if bias is None else t(np.asarray(bias, np.uint16).view(np.int16), torch.bfloat16)
+        self.struct = svdq_w8a8_layer(self.m, self.n, self.rank, _ptr(self.smooth_inv), _ptr(self.qw),
+                                      _ptr(self.wscale), _ptr(self.l1), _ptr(self.l2), _ptr(self.bias))
+
+
+def svdq_w8a8_act_workspace_size(b: int, m: int, rank: int) -> int:
+    return int(lib().svdq_w8a8_act_workspace_size(b, m, rank))
+
+
+def svdq_w8a8_quantize_act_lowrank_down(x, smooth_inv, l1, rank: int, qx=None, ascale=None, z=None,
+                                        workspace=None, stream=None):
+    """Returns (qx int8 [m/64][b][64], ascale fp16 [b], z fp32 [b][rank] or None)."""
+    import torch
+    b, m = x.shape
+    dev = x.device
+    if qx is None:
+        qx = torch.empty((m // SVDQ_GROUP, b, 64), dtype=torch.int8, device=dev)
+    if ascale is None:
+        ascale = torch.empty(b, dtype=torch.float16, device=dev)
+    if z is None and rank > 0:
+        z = torch.empty((b, rank), dtype=torch.float32, device=dev)
+    need = svdq_w8a8_act_workspace_size(b, m, rank)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().svdq_w8a8_quantize_act_lowrank_down(
+        _ptr(x), b, m, rank, _ptr(smooth_inv), _ptr(l1), _ptr(qx), _ptr(ascale), _ptr(z),
+        _ptr(workspace), wsb, _stream(stream)))
+    return qx, ascale, z
+
+
+def svdq_w8a8_gemm_workspace_size(b: int, n: int, m: int) -> int:
+    return int(lib().svdq_w8a8_gemm_workspace_size(b, n, m))
+
+
+def svdq_w8a8_gemm_lowrank_up(qx, ascale, z, layer: DeviceLayer8, b: Optional[int] = None, out_dtype=None,
+                              y=None, workspace=None, stream=None):
+    import torch
+    if b is None:
+        b = qx.shape[1]
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    code = SVDQ_OUT_BF16 if out_dtype == torch.bfloat16 else SVDQ_OUT_F32
+    if y is None:
+        y = torch.empty((b, layer.n), dtype=out_dtype, device=qx.device)
+    if workspace is None:
+        need = svdq_w8a8_gemm_workspace_size(b, layer.n, layer.m)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=qx.device)
+    wsb = workspace.numel() * workspace.element_size()
+    _check(lib().svdq_w8a8_gemm_lowrank_up(_ptr(qx), _ptr(ascale), _ptr(z), ctypes.byref(layer.struct), b,
+                                           _ptr(y), code, _ptr(workspace), wsb, _stream(stream)))
+    return y
+
+
+def svdq_w8a8_linear_workspace_size(b: int, m: int, n: int, rank: int) -> int:
+    return int(lib().svdq_w8a8_linear_workspace_size(b, m, n, rank))
+
+
+def svdq_w8a8_linear(x, layer: DeviceLayer8, out_dtype=None, y=None, workspace=None, stream=None):
+    import torch
+    b, m = x.shape
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    code = SVDQ_OUT_BF16 if out_dtype == torch.bfloat16 else SVDQ_OUT_F32
+    if y is None:
+        y = torch.empty((b, layer.n), dtype=out_dtype, device=x.device)
+    if workspace is None:
+        need = svdq_w8a8_linear_workspace_size(b, m, layer.n, layer.rank)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    wsb = workspace.numel() * workspace.element_size()
+    _check(lib().svdq_w8a8_linear(_ptr(x), ctypes.byref(layer.struct), b, _ptr(y), code, _ptr(workspace),
+                                  wsb, _stream(stream)))
     return y

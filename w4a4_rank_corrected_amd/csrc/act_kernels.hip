@@ -1,6 +1,7 @@
 // Activation-side kernels: calibration statistic, the fused activation
-// quantization + low-rank down-projection (first fused pair of Nunchaku), and
-// the ordered reduction of split partial sums.
+// quantization + low-rank down-projection (first fused pair of Nunchaku), the
+// per-token INT8 quantizer of the 8-bit setting, and the ordered reduction of
+// split partial sums.
 //
 // [Review] = "SVDQuant: How a Small High-Precision Branch Makes 4-Bit Diffusion
 // Practical" (technical review of arXiv:2411.05007v4).
@@ -280,6 +281,88 @@ __global__ __launch_bounds__(256) void act_quant_down_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Per-token INT8 codes of X~ (the 8-bit setting: [Review] sec. 8, with the
+// quantizer of Eq.(1) and 127 in place of 7).  A row's scale needs the maximum
+// over all of its m channels, so one wave owns one row: lane l handles the
+// 8-channel pieces p = l, l + 64, ... (each wave step reads 1 KB of the row,
+// coalesced).  Pass 1 smooths the pieces to bf16, keeping them in registers
+// when the row fits in RP pieces per lane, and reduces max |x~| over the wave;
+// then s = fp16(fl32(amax / 127)) (saturated) and r = fl32(1 / s).  Pass 2
+// quantizes with the same division-free quotient as the INT4 kernel (checked
+// exhaustively on the host for codes up to 127 as well):
+//   p = fl(x~ r); e = fma(-p, s, x~); q = med3(fma(e, r, p), -127, 127)
+// and stores 8 codes per lane: piece p lies in channel group p / 8, at byte
+// 8 (p % 8) of the row's 64-byte record [m/64][b][64].
+// ---------------------------------------------------------------------------
+template <int RP>  // pieces per lane kept in registers (0: smooth the row again in pass 2)
+__global__ __launch_bounds__(256) void act8_quant_kernel(const uint16_t* __restrict__ x, int b, int m,
+                                                         const float* __restrict__ inv, int8_t* __restrict__ qx,
+                                                         uint16_t* __restrict__ ascale) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= b) return;  // no barriers below
+  const int P = m >> 3;
+  const uint16_t* xr = x + (size_t)row * m;
+  auto smooth = [&](int p) -> u32x4 {
+    const u32x4 w = ldg16(xr + 8 * p);
+    if (!inv) return w;  // x~ = x
+    const f32x4 i0 = *reinterpret_cast<const f32x4*>(inv + 8 * p);
+    const f32x4 i1 = *reinterpret_cast<const f32x4*>(inv + 8 * p + 4);
+    return u32x4{pack_bf16x2(bf16_lo(w[0]) * i0[0], bf16_hi(w[0]) * i0[1]),
+                 pack_bf16x2(bf16_lo(w[1]) * i0[2], bf16_hi(w[1]) * i0[3]),
+                 pack_bf16x2(bf16_lo(w[2]) * i1[0], bf16_hi(w[2]) * i1[1]),
+                 pack_bf16x2(bf16_lo(w[3]) * i1[2], bf16_hi(w[3]) * i1[3])};
+  };
+  auto piece_max = [](const u32x4& v, float am) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) am = fmaxf(am, fmaxf(fabsf(bf16_lo(v[e])), fabsf(bf16_hi(v[e]))));
+    return am;
+  };
+  float sf = 0.0f, rc = 0.0f;
+  auto set_scale = [&](float am) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+    float s32 = am / 127.0f;               // IEEE division (correctly rounded)
+    s32 = fminf(s32, 65504.0f);            // saturate instead of rounding to inf
+    const _Float16 s16 = (_Float16)s32;    // round to nearest even
+    sf = (float)s16;
+    rc = sf > 0.0f ? 1.0f / sf : 0.0f;
+    if (lane == 0) ascale[row] = __builtin_bit_cast(uint16_t, s16);
+  };
+  auto quant = [&](int p, const u32x4& v) {
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float val = (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
+      const float pq = val * rc;
+      const float rem = __builtin_fmaf(-pq, sf, val);
+      const float q = __builtin_amdgcn_fmed3f(__builtin_fmaf(rem, rc, pq), -127.0f, 127.0f);
+      w[e >> 2] |= (__float_as_uint(q + kMagic) & 0xFFu) << (8 * (e & 3));
+    }
+    *reinterpret_cast<uint2*>(qx + ((size_t)(p >> 3) * b + row) * 64 + 8 * (p & 7)) = uint2{w[0], w[1]};
+  };
+  if constexpr (RP > 0) {
+    u32x4 v[RP];
+    float am = 0.0f;
+#pragma unroll
+    for (int k = 0; k < RP; ++k) {  // loads unconditional (clamped), so all are in flight together
+      const int p = 64 * k + lane;
+      v[k] = smooth(p < P ? p : P - 1);
+      if (p < P) am = piece_max(v[k], am);
+    }
+    set_scale(am);
+#pragma unroll
+    for (int k = 0; k < RP; ++k)
+      if (64 * k + lane < P) quant(64 * k + lane, v[k]);
+  } else {
+    float am = 0.0f;
+    for (int p = lane; p < P; p += 64) am = piece_max(smooth(p), am);
+    set_scale(am);
+    for (int p = lane; p < P; p += 64) quant(p, smooth(p));
+  }
+}
+
 // z[i][t] = sum over splits s (in order) of zpart[s][i][t].  Loads are issued
 // eight splits at a time; the additions keep the split order.
 __global__ void z_reduce_kernel(const float* __restrict__ zpart, int splits, size_t count,
@@ -405,6 +488,23 @@ int launch_add(void* y, const void* t, size_t count, int y_dtype, void* stream) 
     hipLaunchKernelGGL(add_kernel<true>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, y, t, count);
   else
     hipLaunchKernelGGL(add_kernel<false>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, y, t, count);
+  return (int)hipGetLastError();
+}
+
+int launch_act8_quant(const uint16_t* x, int b, int m, const float* smooth_inv, int8_t* qx, uint16_t* ascale,
+                      void* stream) {
+  if (b == 0) return 0;
+  hipStream_t st = (hipStream_t)stream;
+  const dim3 grid((unsigned)((b + 3) / 4));
+  const int per_lane = (m / 8 + 63) / 64;  // pieces of the row per lane
+  if (per_lane <= 4)
+    hipLaunchKernelGGL(act8_quant_kernel<4>, grid, dim3(256), 0, st, x, b, m, smooth_inv, qx, ascale);
+  else if (per_lane <= 8)
+    hipLaunchKernelGGL(act8_quant_kernel<8>, grid, dim3(256), 0, st, x, b, m, smooth_inv, qx, ascale);
+  else if (per_lane <= 24)
+    hipLaunchKernelGGL(act8_quant_kernel<24>, grid, dim3(256), 0, st, x, b, m, smooth_inv, qx, ascale);
+  else
+    hipLaunchKernelGGL(act8_quant_kernel<0>, grid, dim3(256), 0, st, x, b, m, smooth_inv, qx, ascale);
   return (int)hipGetLastError();
 }
 

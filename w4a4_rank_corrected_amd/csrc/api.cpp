@@ -185,6 +185,58 @@ int check_layer(const svdq_layer* L) {
   return SVDQ_OK;
 }
 
+// The 8-bit layer: the checks of check_layer, with the INT8 bound on m.
+int check_layer8(const svdq_w8a8_layer* L) {
+  REQUIRE(L != nullptr, SVDQ_ERR_INVALID_ARG, "layer is NULL");
+  int st = check_group(L->m, SVDQ_GROUP);
+  if (st) return st;
+  REQUIRE(L->m <= SVDQ_W8A8_MAX_M, SVDQ_ERR_UNSUPPORTED, "m must be <= %d for 8-bit codes (got %d)",
+          SVDQ_W8A8_MAX_M, L->m);
+  REQUIRE(L->n >= 1, SVDQ_ERR_INVALID_ARG, "n must be >= 1 (got %d)", L->n);
+  REQUIRE(L->n <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "n must be <= %d (got %d)", SVDQ_MAX_DIM, L->n);
+  REQUIRE(L->rank >= 0 && L->rank <= SVDQ_MAX_RANK, SVDQ_ERR_UNSUPPORTED,
+          "rank must be in [0, %d] (got %d)", SVDQ_MAX_RANK, L->rank);
+  REQUIRE(L->qw && L->wscale, SVDQ_ERR_INVALID_ARG, "layer qw / wscale must not be NULL");
+  REQUIRE(aligned16(L->qw), SVDQ_ERR_ALIGNMENT, "layer qw must be 16-byte aligned");
+  REQUIRE(((uintptr_t)L->wscale & 1u) == 0, SVDQ_ERR_ALIGNMENT, "layer wscale must be 2-byte aligned");
+  if (L->rank > 0) {
+    REQUIRE(L->l2 != nullptr, SVDQ_ERR_INVALID_ARG, "layer l2 must not be NULL when rank > 0");
+    REQUIRE(((uintptr_t)L->l2 & 1u) == 0, SVDQ_ERR_ALIGNMENT, "layer l2 must be 2-byte aligned");
+  }
+  if (L->bias) REQUIRE(((uintptr_t)L->bias & 1u) == 0, SVDQ_ERR_ALIGNMENT, "bias must be 2-byte aligned");
+  return SVDQ_OK;
+}
+
+// Workspace of the 8-bit layer: INT8 codes, per-token scales, Z, its split
+// partials, the GEMM's workspace.
+LinearWorkspace linear8_ws_layout(int b, int m, int n, int rank) {
+  LinearWorkspace w;
+  ActPlan p = act_plan(b, m, rank);
+  w.qx_off = 0;
+  w.as_off = round_up((size_t)m * (size_t)b, kAlign);
+  w.z_off = round_up(w.as_off + (size_t)b * 2, kAlign);
+  w.zpart_off = round_up(w.z_off + (size_t)b * (size_t)rank * 4, kAlign);
+  const size_t zpart = (rank > 0 && p.splits > 1) ? (size_t)p.splits * (size_t)b * (size_t)rank * 4 : 0;
+  w.gemm_off = round_up(w.zpart_off + zpart, kAlign);
+  w.total = round_up(w.gemm_off + gemm_ws_bytes(b, n, m), kAlign);
+  if (b == 0) w.total = 0;
+  return w;
+}
+
+// Per-token codes, then Z = x~ L1 with the act kernel's down-projection alone
+// (and the ordered split reduction).
+int run_act8(const uint16_t* x, int b, int m, int rank, const float* smooth_inv, const uint16_t* l1, int8_t* qx,
+             uint16_t* ascale, float* z, float* zpart, void* stream) {
+  int st = hip_status(launch_act8_quant(x, b, m, smooth_inv, qx, ascale, stream), "act8_quant");
+  if (st || rank == 0) return st;
+  const ActPlan p = act_plan(b, m, rank);
+  float* zp = p.splits > 1 ? zpart : z;
+  st = hip_status(launch_act_quant_down(x, b, m, rank, smooth_inv, l1, nullptr, nullptr, zp, p, false, stream),
+                  "lowrank_down");
+  if (st || p.splits <= 1) return st;
+  return hip_status(launch_z_reduce(zp, p.splits, b, rank, z, stream), "z_reduce");
+}
+
 int check_y(void* y, int y_dtype, int b) {
   REQUIRE(y_dtype == SVDQ_OUT_BF16 || y_dtype == SVDQ_OUT_F32, SVDQ_ERR_INVALID_ARG,
           "y_dtype must be SVDQ_OUT_BF16 or SVDQ_OUT_F32 (got %d)", y_dtype);
@@ -201,7 +253,7 @@ int check_y(void* y, int y_dtype, int b) {
 
 extern "C" {
 
-int svdq_abi_version(void) { return 100; }
+int svdq_abi_version(void) { return 101; }
 
 const char* svdq_last_error(void) { return g_err; }
 
@@ -545,6 +597,146 @@ int svdq_linear_unfused(const uint16_t* x, const svdq_layer* layer, int b, void*
   st = hip_status(launch_lowrank_up(z, *layer, b, ws + y2_off, y_dtype, stream), "lowrank_up");
   if (st) return st;
   return hip_status(launch_add(y, ws + y2_off, (size_t)b * (size_t)n, y_dtype, stream), "add");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The 8-bit setting ([Review] sec. 8)
+// ---------------------------------------------------------------------------
+extern "C" {
+
+int svdq_w8a8_prepare_weights(const float* W, const float* act_amax, int m, int n, int rank, float alpha,
+                              int8_t* qw, uint16_t* wscale, uint16_t* l1, uint16_t* l2, float* lambda,
+                              float* smooth_inv, float* residual) {
+  clear_error();
+  // the INT4 buffers are not used: pass the 8-bit ones for the NULL checks
+  int st = check_prepare(W, act_amax, m, n, rank, SVDQ_GROUP, reinterpret_cast<const uint8_t*>(qw), wscale, l1,
+                         l2, lambda, smooth_inv);
+  if (st) return st;
+  REQUIRE(m <= SVDQ_W8A8_MAX_M, SVDQ_ERR_UNSUPPORTED, "m must be <= %d for 8-bit codes (got %d)",
+          SVDQ_W8A8_MAX_M, m);
+  REQUIRE(alpha >= 0.0f && alpha <= 1.0f, SVDQ_ERR_INVALID_ARG, "alpha must be in [0, 1] (got %g)",
+          (double)alpha);
+  HostLayer L;
+  st = build_layer(W, act_amax, m, n, rank, (double)alpha, L);
+  if (st) {
+    set_error("truncated SVD did not converge (m=%d n=%d rank=%d)", m, n, rank);
+    return st;
+  }
+  quantize_residual8(L.r32.data(), m, n, qw, wscale);
+  std::memcpy(lambda, L.lam32.data(), sizeof(float) * m);
+  std::memcpy(smooth_inv, L.inv32.data(), sizeof(float) * m);
+  for (int i = 0; i < m && rank > 0; ++i)
+    for (int t = 0; t < rank; ++t) l1[(size_t)t * m + i] = L.l1b[(size_t)i * rank + t];
+  for (int t = 0; t < rank; ++t)
+    for (int j = 0; j < n; ++j) l2[(size_t)j * rank + t] = L.l2b[(size_t)t * n + j];
+  if (residual) std::memcpy(residual, L.r32.data(), sizeof(float) * L.r32.size());
+  return SVDQ_OK;
+}
+
+size_t svdq_w8a8_act_workspace_size(int b, int m, int rank) { return svdq_act_workspace_size(b, m, rank); }
+
+int svdq_w8a8_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int rank, const float* smooth_inv,
+                                        const uint16_t* l1, int8_t* qx, uint16_t* ascale, float* z,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  int st = check_group(m, SVDQ_GROUP);
+  if (st) return st;
+  REQUIRE(m <= SVDQ_W8A8_MAX_M, SVDQ_ERR_UNSUPPORTED, "m must be <= %d for 8-bit codes (got %d)",
+          SVDQ_W8A8_MAX_M, m);
+  REQUIRE(b >= 0, SVDQ_ERR_INVALID_ARG, "b must be >= 0 (got %d)", b);
+  REQUIRE(b <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "b must be <= %d (got %d)", SVDQ_MAX_DIM, b);
+  REQUIRE(rank >= 0 && rank <= SVDQ_MAX_RANK, SVDQ_ERR_UNSUPPORTED, "rank must be in [0, %d] (got %d)",
+          SVDQ_MAX_RANK, rank);
+  if (b == 0) return SVDQ_OK;
+  REQUIRE(x && qx && ascale, SVDQ_ERR_INVALID_ARG, "x, qx and ascale must not be NULL");
+  REQUIRE(aligned16(x) && aligned16(qx), SVDQ_ERR_ALIGNMENT, "x and qx must be 16-byte aligned");
+  REQUIRE(((uintptr_t)ascale & 1u) == 0, SVDQ_ERR_ALIGNMENT, "ascale must be 2-byte aligned");
+  if (smooth_inv) REQUIRE(aligned16(smooth_inv), SVDQ_ERR_ALIGNMENT, "smooth_inv must be 16-byte aligned");
+  if (rank > 0) {
+    REQUIRE(l1 && z, SVDQ_ERR_INVALID_ARG, "l1 and z must not be NULL when rank > 0");
+    REQUIRE(aligned16(l1), SVDQ_ERR_ALIGNMENT, "l1 must be 16-byte aligned");
+    REQUIRE(((uintptr_t)z & 3u) == 0, SVDQ_ERR_ALIGNMENT, "z must be 4-byte aligned");
+  }
+  const size_t need = svdq_act_workspace_size(b, m, rank);
+  if (need > 0) {
+    REQUIRE(workspace != nullptr && workspace_bytes >= need, SVDQ_ERR_WORKSPACE,
+            "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
+    REQUIRE(((uintptr_t)workspace & 15u) == 0, SVDQ_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  }
+  return run_act8(x, b, m, rank, smooth_inv, l1, qx, ascale, z, (float*)workspace, stream);
+}
+
+size_t svdq_w8a8_gemm_workspace_size(int b, int n, int m) { return svdq_gemm_workspace_size(b, n, m); }
+
+int svdq_w8a8_gemm_lowrank_up(const int8_t* qx, const uint16_t* ascale, const float* z,
+                              const svdq_w8a8_layer* layer, int b, void* y, int y_dtype, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  clear_error();
+  int st = check_layer8(layer);
+  if (st) return st;
+  REQUIRE(b >= 0, SVDQ_ERR_INVALID_ARG, "b must be >= 0 (got %d)", b);
+  REQUIRE(b <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "b must be <= %d (got %d)", SVDQ_MAX_DIM, b);
+  st = check_y(y, y_dtype, b);
+  if (st) return st;
+  if (b == 0) return SVDQ_OK;
+  REQUIRE(qx && ascale, SVDQ_ERR_INVALID_ARG, "qx and ascale must not be NULL");
+  REQUIRE(aligned16(qx), SVDQ_ERR_ALIGNMENT, "qx must be 16-byte aligned");
+  REQUIRE(((uintptr_t)ascale & 1u) == 0, SVDQ_ERR_ALIGNMENT, "ascale must be 2-byte aligned");
+  if (layer->rank > 0) {
+    REQUIRE(z != nullptr, SVDQ_ERR_INVALID_ARG, "z must not be NULL when rank > 0");
+    REQUIRE(((uintptr_t)z & 3u) == 0, SVDQ_ERR_ALIGNMENT, "z must be 4-byte aligned");
+  }
+  const size_t need = gemm_ws_bytes(b, layer->n, layer->m);
+  if (need > 0) {
+    REQUIRE(workspace != nullptr && workspace_bytes >= need, SVDQ_ERR_WORKSPACE,
+            "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
+    REQUIRE(((uintptr_t)workspace & 15u) == 0, SVDQ_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  }
+  return hip_status(launch_gemm8_up(qx, ascale, z, *layer, b, y, y_dtype, workspace, stream),
+                    "gemm_w8a8_lowrank_up");
+}
+
+size_t svdq_w8a8_linear_workspace_size(int b, int m, int n, int rank) {
+  if (m < SVDQ_GROUP || m % SVDQ_GROUP || m > SVDQ_W8A8_MAX_M || b <= 0 || n <= 0 || rank < 0 ||
+      rank > SVDQ_MAX_RANK)
+    return 0;
+  return linear8_ws_layout(b, m, n, rank).total;
+}
+
+int svdq_w8a8_linear(const uint16_t* x, const svdq_w8a8_layer* layer, int b, void* y, int y_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  int st = check_layer8(layer);
+  if (st) return st;
+  REQUIRE(b >= 0, SVDQ_ERR_INVALID_ARG, "b must be >= 0 (got %d)", b);
+  REQUIRE(b <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "b must be <= %d (got %d)", SVDQ_MAX_DIM, b);
+  st = check_y(y, y_dtype, b);
+  if (st) return st;
+  if (b == 0) return SVDQ_OK;
+  const int m = layer->m, rank = layer->rank;
+  REQUIRE(x != nullptr, SVDQ_ERR_INVALID_ARG, "x must not be NULL");
+  REQUIRE(aligned16(x), SVDQ_ERR_ALIGNMENT, "x must be 16-byte aligned");
+  if (layer->smooth_inv)
+    REQUIRE(aligned16(layer->smooth_inv), SVDQ_ERR_ALIGNMENT, "smooth_inv must be 16-byte aligned");
+  if (rank > 0) {
+    REQUIRE(layer->l1 != nullptr, SVDQ_ERR_INVALID_ARG, "layer l1 must not be NULL when rank > 0");
+    REQUIRE(aligned16(layer->l1), SVDQ_ERR_ALIGNMENT, "layer l1 must be 16-byte aligned");
+  }
+  const LinearWorkspace w = linear8_ws_layout(b, m, layer->n, rank);
+  REQUIRE(workspace != nullptr && workspace_bytes >= w.total, SVDQ_ERR_WORKSPACE,
+          "workspace of %zu bytes needed (got %zu)", w.total, workspace ? workspace_bytes : (size_t)0);
+  REQUIRE(((uintptr_t)workspace & (kAlign - 1)) == 0, SVDQ_ERR_ALIGNMENT,
+          "workspace must be %zu-byte aligned", kAlign);
+  char* ws = (char*)workspace;
+  int8_t* qx = (int8_t*)(ws + w.qx_off);
+  uint16_t* as = (uint16_t*)(ws + w.as_off);
+  float* z = rank > 0 ? (float*)(ws + w.z_off) : nullptr;
+  st = run_act8(x, b, m, rank, layer->smooth_inv, layer->l1, qx, as, z, (float*)(ws + w.zpart_off), stream);
+  if (st) return st;
+  return hip_status(launch_gemm8_up(qx, as, z, *layer, b, y, y_dtype, ws + w.gemm_off, stream),
+                    "gemm_w8a8_lowrank_up");
 }
 
 }  // extern "C"

@@ -81,11 +81,20 @@ template <>
 struct Piece<16> {
   uint32_t w[4];
 };
+template <>
+struct Piece<32> {
+  uint32_t w[8];
+};
 
 template <int BYTES>
 __device__ __forceinline__ Piece<BYTES> buffer_piece(__amdgpu_buffer_rsrc_t rs, uint32_t voff) {
   Piece<BYTES> p;
-  if constexpr (BYTES == 16) {
+  if constexpr (BYTES == 32) {
+    const u32x4 v0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+    const u32x4 v1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16u, 0, 0));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p.w[e] = v0[e], p.w[4 + e] = v1[e];
+  } else if constexpr (BYTES == 16) {
     const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
     p.w[0] = v[0], p.w[1] = v[1], p.w[2] = v[2], p.w[3] = v[3];
   } else if constexpr (BYTES == 8) {
@@ -122,6 +131,13 @@ __device__ __forceinline__ void unpack_piece(uint8_t* row, int w0, const Piece<B
     *reinterpret_cast<uint32_t*>(lo_dst) = lo[0];
     *reinterpret_cast<uint32_t*>(lo_dst + 16) = hi[0];
   }
+}
+
+// Copy a piece of an 8-bit record (64 codes, one byte each) starting at word w0
+// into the LDS row `row` unchanged.
+__device__ __forceinline__ void copy_piece(uint8_t* row, int w0, const Piece<32>& p) {
+  *reinterpret_cast<u32x4*>(row + 4 * w0) = u32x4{p.w[0], p.w[1], p.w[2], p.w[3]};
+  *reinterpret_cast<u32x4*>(row + 4 * w0 + 16) = u32x4{p.w[4], p.w[5], p.w[6], p.w[7]};
 }
 
 // Linear tile index -> (tile row, tile column), in bands of 4 tile-rows
@@ -163,6 +179,7 @@ struct GemmCfg {
   static_assert(WG_PER_CU >= 1 && (WPE * 4) % (NT / 64) == 0, "whole workgroups per CU");
   static_assert(A_BYTES == 4 || A_BYTES == 8 || A_BYTES == 16, "activation staging piece");
   static_assert(B_BYTES == 4 || B_BYTES == 8 || B_BYTES == 16, "weight staging piece");
+  static_assert(2 * A_BYTES == 32 && 2 * B_BYTES == 32, "8-bit records: 32-byte staging pieces");
   static_assert(NT >= TM + TN && TM % 64 == 0, "scale staging: at most one scale per thread");
 };
 
@@ -184,8 +201,15 @@ struct StreamK {
   unsigned long long epoch;       // this launch's epoch
 };
 
-template <class C, bool OUT_BF16>
-__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void gemm_w4a4_up_kernel(
+// The kernel body, for INT4 group-scaled operands (W8 = false) or for the
+// 8-bit setting (W8 = true: per-token activation and per-output-channel weight
+// INT8 codes, one byte each, in 64-byte group-major records [m/64][rows][64],
+// with one fp16 scale per row and per column).  With 8-bit codes the MFMAs
+// chain over all groups into i32 accumulators (|sum| <= 127^2 m < 2^31 for the
+// m the library accepts) and the scales are applied once, in the epilogue, so
+// no per-group VALU work remains; stream-K partials are then i32 sums.
+template <class C, bool OUT_BF16, bool W8>
+__device__ __forceinline__ void gemm_up_body(
     const uint8_t* __restrict__ qx, const uint16_t* __restrict__ ascale,
     const float* __restrict__ z, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ l2t,
@@ -196,20 +220,23 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
   __shared__ __align__(16) uint8_t As[2][TM * ROWB];
   __shared__ __align__(16) uint8_t Bs[2][TN * ROWB];
   // [sx/256 (TM) | -1.5*2^23 sx/256 (TM) | sw (TN) | unused (NT - TM - TN)]
-  __shared__ __align__(16) float Ssc[2][TM + NT];
+  // (no per-group scales with 8-bit codes)
+  __shared__ __align__(16) float Ssc[2][W8 ? 4 : TM + NT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int r = lane & 15, c = lane >> 4;
-  constexpr int AB = C::A_BYTES, BB = C::B_BYTES;
-  const int a_row = tid * AB / 32, a_w0 = (tid * AB % 32) / 4;
-  const int b_col = tid * BB / 32, b_w0 = (tid * BB % 32) / 4;
-  const uint32_t a_bytes = (uint32_t)b * 32u, b_bytes = (uint32_t)n * 32u;
+  constexpr int REC = W8 ? 64 : 32;  // record bytes of one row in one group
+  constexpr int AB = W8 ? 2 * C::A_BYTES : C::A_BYTES, BB = W8 ? 2 * C::B_BYTES : C::B_BYTES;
+  const int a_row = tid * AB / REC, a_w0 = (tid * AB % REC) / 4;
+  const int b_col = tid * BB / REC, b_w0 = (tid * BB % REC) / 4;
+  const uint32_t a_bytes = (uint32_t)b * REC, b_bytes = (uint32_t)n * REC;
   const i32x4 magic = {kMagicBits, kMagicBits, kMagicBits, kMagicBits};
 
   f32x4 acc[BI][BJ];
+  i32x4 iacc[BI][BJ];  // 8-bit setting: integer sums over all groups
 
   // ---- low-rank branch: acc = bf16(Z) L2 over K = rank in chunks of 32 -------
   // 16-byte loads when every row of l2 / z starts 16-byte aligned
@@ -278,8 +305,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
     uint32_t s;
   };
   auto main_branch = [&](int i0, int j0, int g0, int g1) {
-    const uint32_t a_voff = (uint32_t)(i0 + a_row) * 32u + 4u * a_w0;
-    const uint32_t b_voff = (uint32_t)(j0 + b_col) * 32u + 4u * b_w0;
+    const uint32_t a_voff = (uint32_t)(i0 + a_row) * REC + 4u * a_w0;
+    const uint32_t b_voff = (uint32_t)(j0 + b_col) * REC + 4u * b_w0;
     // activation scale of row i0+tid, weight scale of column j0+tid-TM, or an
     // out-of-range offset (reads 0) for the threads that stage no scale
     const uint32_t s_voff = tid < TM ? (uint32_t)(i0 + tid) * 2u
@@ -290,14 +317,16 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
       const int g = g0 + min(k, S - 1);
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(qx + (size_t)g * a_bytes, a_bytes);
       const __amdgpu_buffer_rsrc_t rb = make_rsrc(qw + (size_t)g * b_bytes, b_bytes);
-      // wave-uniform choice (waves 0 .. TM/64-1 stage activation scales), so the
-      // descriptor stays in scalar registers
-      const __amdgpu_buffer_rsrc_t rs =
-          wave_u < TM / 64 ? make_rsrc(ascale + (size_t)g * b, (uint32_t)b * 2u)
-                           : make_rsrc(wscale + (size_t)g * n, (uint32_t)n * 2u);
       st.a = buffer_piece<AB>(ra, a_voff);
       st.w = buffer_piece<BB>(rb, b_voff);
-      st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, s_voff, 0, 0);
+      if constexpr (!W8) {
+        // wave-uniform choice (waves 0 .. TM/64-1 stage activation scales), so
+        // the descriptor stays in scalar registers
+        const __amdgpu_buffer_rsrc_t rs =
+            wave_u < TM / 64 ? make_rsrc(ascale + (size_t)g * b, (uint32_t)b * 2u)
+                             : make_rsrc(wscale + (size_t)g * n, (uint32_t)n * 2u);
+        st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, s_voff, 0, 0);
+      }
     };
     // Scales go to one LDS array per buffer: [sx/256 (TM) | -1.5*2^23 sx/256
     // (TM) | sw (TN) | unused].  Thread t < TM stages row i0+t's activation
@@ -305,18 +334,38 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
     // twice; threads past TM+TN write zeros to the unused tail), so the staging
     // is straight-line code.
     auto store_stage = [&](int buf, const Stage& st) {
-      unpack_piece<AB>(&As[buf][a_row * ROWB], a_w0, st.a);
-      unpack_piece<BB>(&Bs[buf][b_col * ROWB], b_w0, st.w);
-      const float sv = f16_to_f32((uint16_t)st.s);
-      const bool act = wave_u < TM / 64;
-      const float q = sv * 0.00390625f;  // sx / 256 (exact)
-      Ssc[buf][act ? tid : TM + tid] = act ? q : sv;
-      Ssc[buf][TM + tid] = act ? -kMagic * q : sv;  // exact: 3 * 2^14 * sx
+      if constexpr (W8) {
+        copy_piece(&As[buf][a_row * ROWB], a_w0, st.a);
+        copy_piece(&Bs[buf][b_col * ROWB], b_w0, st.w);
+      } else {
+        unpack_piece<AB>(&As[buf][a_row * ROWB], a_w0, st.a);
+        unpack_piece<BB>(&Bs[buf][b_col * ROWB], b_w0, st.w);
+        const float sv = f16_to_f32((uint16_t)st.s);
+        const bool act = wave_u < TM / 64;
+        const float q = sv * 0.00390625f;  // sx / 256 (exact)
+        Ssc[buf][act ? tid : TM + tid] = act ? q : sv;
+        Ssc[buf][TM + tid] = act ? -kMagic * q : sv;  // exact: 3 * 2^14 * sx
+      }
     };
-    // One group.  For each 16-row block bi: BJ MFMAs (one per 16-column
+    // One group.  INT4: for each 16-row block bi, BJ MFMAs (one per 16-column
     // block), whose results are applied by 8 * BJ FMAs one block later, so an
-    // MFMA's latency is covered by the previous block's FMAs.
+    // MFMA's latency is covered by the previous block's FMAs.  8-bit: the
+    // MFMAs accumulate into the integer sums directly.
     auto compute = [&](int buf) {
+      if constexpr (W8) {
+        u32x4 Pb[BJ];
+#pragma unroll
+        for (int bj = 0; bj < BJ; ++bj)
+          Pb[bj] = *reinterpret_cast<const u32x4*>(&Bs[buf][(WN * wn + 16 * bj + r) * ROWB + 16 * c]);
+#pragma unroll
+        for (int bi = 0; bi < BI; ++bi) {
+          const u32x4 Qa = *reinterpret_cast<const u32x4*>(&As[buf][(WM * wm + 16 * bi + r) * ROWB + 16 * c]);
+#pragma unroll
+          for (int bj = 0; bj < BJ; ++bj)
+            iacc[bi][bj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                __builtin_bit_cast(i32x4, Pb[bj]), __builtin_bit_cast(i32x4, Qa), iacc[bi][bj], 0, 0, 0);
+        }
+      } else {
       u32x4 Pb[BJ];
       f32x4 sw4[BJ];
 #pragma unroll
@@ -350,6 +399,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
               acc[bi - 1][bj][v] = __builtin_fmaf(t, sw4[bj][v], acc[bi - 1][bj][v]);
             }
         }
+      }
       }
     };
 
@@ -431,7 +481,32 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
 #pragma unroll
     for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
-      for (int bj = 0; bj < BJ; ++bj) acc[bi][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int bj = 0; bj < BJ; ++bj) {
+        if constexpr (W8)
+          iacc[bi][bj] = i32x4{0, 0, 0, 0};
+        else
+          acc[bi][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+  };
+
+  // 8-bit setting, after all groups: acc = isum * (sx sw); the product of the
+  // two fp16 scales is exact in fp32, so each element takes the rounding of the
+  // conversion and of one multiplication
+  auto scale_sums = [&](int i0, int j0) {
+#pragma unroll
+    for (int bj = 0; bj < BJ; ++bj) {
+      const int j = j0 + WN * wn + 16 * bj + 4 * c;
+      float sw[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sw[v] = j + v < n ? f16_to_f32(wscale[j + v]) : 0.0f;
+#pragma unroll
+      for (int bi = 0; bi < BI; ++bi) {
+        const int i = i0 + WM * wm + 16 * bi + r;
+        const float sx = i < b ? f16_to_f32(ascale[i]) : 0.0f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[bi][bj][v] = (float)iacc[bi][bj][v] * (sx * sw[v]);
+      }
+    }
   };
 
   if ((int)blockIdx.x >= sk.P) {  // one tile per workgroup
@@ -439,8 +514,12 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
     int ti, tj;
     band_tile(dp_tile((int)blockIdx.x - sk.P, T - sk.T, sk.T), tiles_m, tiles_n, ti, tj);
     zero_acc();
-    lowrank(ti * TM, tj * TN);
+    if constexpr (!W8) lowrank(ti * TM, tj * TN);
     main_branch(ti * TM, tj * TN, 0, G);
+    if constexpr (W8) {
+      scale_sums(ti * TM, tj * TN);
+      lowrank(ti * TM, tj * TN);
+    }
     store_tile(ti * TM, tj * TN);
     return;
   }
@@ -457,7 +536,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
     band_tile((int)t, tiles_m, tiles_n, ti, tj);
     const int i0 = ti * TM, j0 = tj * TN;
     zero_acc();
-    if (g1 == G) lowrank(i0, j0);  // the tile's last groups carry the low-rank branch
+    if (!W8 && g1 == G) lowrank(i0, j0);  // the tile's last groups carry the low-rank branch
     main_branch(i0, j0, g0, g1);
     if (g1 < G) {
       // Publish this partial (this workgroup's first work item) for the
@@ -471,8 +550,9 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
       for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
         for (int bj = 0; bj < BJ; ++bj)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[bi][bj]), rp,
-                                                 (uint32_t)(((bi * BJ + bj) * NT + tid) * 16), 0, kCoherent);
+          __builtin_amdgcn_raw_buffer_store_b128(W8 ? __builtin_bit_cast(u32x4, iacc[bi][bj])
+                                                    : __builtin_bit_cast(u32x4, acc[bi][bj]),
+                                                 rp, (uint32_t)(((bi * BJ + bj) * NT + tid) * 16), 0, kCoherent);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
       if (tid == 0) __hip_atomic_store(&sk.flags[p], sk.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -498,11 +578,19 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
 #pragma unroll
           for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
-            for (int bj = 0; bj < BJ; ++bj)
-              acc[bi][bj] += __builtin_bit_cast(
-                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)(((bi * BJ + bj) * NT + tid) * 16), 0,
-                                                               kCoherent));
+            for (int bj = 0; bj < BJ; ++bj) {
+              const auto v = __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)(((bi * BJ + bj) * NT + tid) * 16), 0,
+                                                                   kCoherent);
+              if constexpr (W8)
+                iacc[bi][bj] += __builtin_bit_cast(i32x4, v);
+              else
+                acc[bi][bj] += __builtin_bit_cast(f32x4, v);
+            }
         }
+      }
+      if constexpr (W8) {
+        scale_sums(i0, j0);
+        lowrank(i0, j0);
       }
       store_tile(i0, j0);
     }
@@ -510,9 +598,38 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
   }
 }
 
+template <class C, bool OUT_BF16>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void gemm_w4a4_up_kernel(
+    const uint8_t* __restrict__ qx, const uint16_t* __restrict__ ascale,
+    const float* __restrict__ z, const uint8_t* __restrict__ qw,
+    const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ l2t,
+    const uint16_t* __restrict__ bias, int b, int n, int G, int rank, int tiles_m, int tiles_n,
+    void* __restrict__ yout, StreamK sk) {
+  gemm_up_body<C, OUT_BF16, false>(qx, ascale, z, qw, wscale, l2t, bias, b, n, G, rank, tiles_m, tiles_n, yout, sk);
+}
+
+template <class C, bool OUT_BF16>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void gemm_w8a8_up_kernel(
+    const uint8_t* __restrict__ qx, const uint16_t* __restrict__ ascale,
+    const float* __restrict__ z, const uint8_t* __restrict__ qw,
+    const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ l2t,
+    const uint16_t* __restrict__ bias, int b, int n, int G, int rank, int tiles_m, int tiles_n,
+    void* __restrict__ yout, StreamK sk) {
+  gemm_up_body<C, OUT_BF16, true>(qx, ascale, z, qw, wscale, l2t, bias, b, n, G, rank, tiles_m, tiles_n, yout, sk);
+}
+
 int g_num_cus = 0;
-template <bool OUT_BF16>
-int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, const svdq_layer& L, int b,
+// Weight-side operands of one launch (INT4 or 8-bit layer).
+struct Operands {
+  const uint8_t* qw;
+  const uint16_t* wscale;
+  const uint16_t* l2;
+  const uint16_t* bias;
+  int n, rank;
+};
+
+template <bool OUT_BF16, bool W8>
+int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, const Operands& L, int b,
                  void* y, const GemmPlan& plan, void* ws, hipStream_t st) {
   StreamK sk{0, 0, 0, nullptr, nullptr, 0};
   if (plan.streamk) {
@@ -523,9 +640,14 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
     sk.flags = reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(ws) + plan.partial_bytes);
     sk.epoch = next_launch_epoch();
   }
-  hipLaunchKernelGGL((gemm_w4a4_up_kernel<Cfg, OUT_BF16>), dim3((unsigned)plan.grid), dim3(Cfg::NT), 0, st,
-                     qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
-                     plan.tiles_n, y, sk);
+  if constexpr (W8)
+    hipLaunchKernelGGL((gemm_w8a8_up_kernel<Cfg, OUT_BF16>), dim3((unsigned)plan.grid), dim3(Cfg::NT), 0, st,
+                       qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
+                       plan.tiles_n, y, sk);
+  else
+    hipLaunchKernelGGL((gemm_w4a4_up_kernel<Cfg, OUT_BF16>), dim3((unsigned)plan.grid), dim3(Cfg::NT), 0, st,
+                       qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
+                       plan.tiles_n, y, sk);
   return (int)hipGetLastError();
 }
 
@@ -582,23 +704,30 @@ int device_cus() {
 int launch_gemm_up(const uint8_t* qx, const uint16_t* ascale, const float* z, const svdq_layer& L,
                    int b, void* y, int y_dtype, void* ws, void* stream) {
   const GemmPlan plan = gemm_plan(b, L.n, L.m, device_cus());
+  const Operands o{L.qw, L.wscale, L.l2, L.bias, L.n, L.rank};
   hipStream_t st = (hipStream_t)stream;
-  if (y_dtype == SVDQ_OUT_BF16) return launch_typed<true>(qx, ascale, z, L, b, y, plan, ws, st);
-  return launch_typed<false>(qx, ascale, z, L, b, y, plan, ws, st);
+  if (y_dtype == SVDQ_OUT_BF16) return launch_typed<true, false>(qx, ascale, z, o, b, y, plan, ws, st);
+  return launch_typed<false, false>(qx, ascale, z, o, b, y, plan, ws, st);
+}
+
+int launch_gemm8_up(const int8_t* qx, const uint16_t* ascale, const float* z, const svdq_w8a8_layer& L,
+                    int b, void* y, int y_dtype, void* ws, void* stream) {
+  const GemmPlan plan = gemm_plan(b, L.n, L.m, device_cus());
+  const Operands o{reinterpret_cast<const uint8_t*>(L.qw), L.wscale, L.l2, L.bias, L.n, L.rank};
+  const uint8_t* a = reinterpret_cast<const uint8_t*>(qx);
+  hipStream_t st = (hipStream_t)stream;
+  if (y_dtype == SVDQ_OUT_BF16) return launch_typed<true, true>(a, ascale, z, o, b, y, plan, ws, st);
+  return launch_typed<false, true>(a, ascale, z, o, b, y, plan, ws, st);
 }
 
 // The low-rank up-projection alone, y = bf16(z) L2 (the unfused path's
 // separate kernel): the GEMM kernel with no channel groups and no bias.
 int launch_lowrank_up(const float* z, const svdq_layer& L, int b, void* y, int y_dtype, void* stream) {
-  svdq_layer U = L;
-  U.m = 0;
-  U.qw = nullptr;
-  U.wscale = nullptr;
-  U.bias = nullptr;
   const GemmPlan plan = gemm_plan(b, L.n, 0, device_cus());  // G = 0: one tile per workgroup
+  const Operands o{nullptr, nullptr, L.l2, nullptr, L.n, L.rank};
   hipStream_t st = (hipStream_t)stream;
-  if (y_dtype == SVDQ_OUT_BF16) return launch_typed<true>(nullptr, nullptr, z, U, b, y, plan, nullptr, st);
-  return launch_typed<false>(nullptr, nullptr, z, U, b, y, plan, nullptr, st);
+  if (y_dtype == SVDQ_OUT_BF16) return launch_typed<true, false>(nullptr, nullptr, z, o, b, y, plan, nullptr, st);
+  return launch_typed<false, false>(nullptr, nullptr, z, o, b, y, plan, nullptr, st);
 }
 
 }  // namespace svdq

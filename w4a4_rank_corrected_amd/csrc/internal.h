@@ -29,6 +29,9 @@ void smoothing_lambda(const float* W, const float* act_amax, int m, int n, doubl
 bool truncated_svd(const double* Wt, int m, int n, int r, double* L1, double* L2);
 // INT4 group quantization of R (fp32 [m][n]) into group-major records.
 void quantize_residual(const float* R, int m, int n, uint8_t* qw, uint16_t* wscale);
+// INT8 quantization of each column of R (fp32 [m][n]) into 64-byte group-major
+// records [m/64][n][64] and one fp16 scale per column.
+void quantize_residual8(const float* R, int m, int n, int8_t* qw, uint16_t* wscale);
 
 // One candidate protected layer on the host ([Review] Algorithm 1 steps 2-5).
 struct HostLayer {
@@ -95,6 +98,9 @@ int launch_act_quant_down(const uint16_t* x, int b, int m, int rank, const float
                           const uint16_t* l1, uint8_t* qx, uint16_t* ascale, float* zpart,
                           const ActPlan& plan, bool quantize, void* stream);
 int launch_z_reduce(const float* zpart, int splits, int b, int rank, float* z, void* stream);
+// Per-token INT8 codes and scales of the smoothed activations (one wave per row).
+int launch_act8_quant(const uint16_t* x, int b, int m, const float* smooth_inv, int8_t* qx, uint16_t* ascale,
+                      void* stream);
 int launch_add(void* y, const void* t, size_t count, int y_dtype, void* stream);
 int launch_lowrank_up(const float* z, const svdq_layer& L, int b, void* y, int y_dtype, void* stream);
 // A fresh value per kernel launch in this process (64-bit, starting at a
@@ -120,6 +126,8 @@ GemmPlan gemm_plan(int b, int n, int m, int cus);
 int device_cus();
 int launch_gemm_up(const uint8_t* qx, const uint16_t* ascale, const float* z, const svdq_layer& L,
                    int b, void* y, int y_dtype, void* ws, void* stream);
+int launch_gemm8_up(const int8_t* qx, const uint16_t* ascale, const float* z, const svdq_w8a8_layer& L,
+                    int b, void* y, int y_dtype, void* ws, void* stream);
 const char* hip_error_name(int err);
 
 }  // namespace svdq

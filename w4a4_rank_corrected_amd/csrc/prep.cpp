@@ -379,6 +379,35 @@ void quantize_residual(const float* R, int m, int n, uint8_t* qw, uint16_t* wsca
   }, 256);
 }
 
+// The 8-bit setting ([Review] sec. 8): one scale per output column over all m
+// rows, s = fp16(fl32(amax / 127)), codes clamp(round_even(fl32(v / s)),
+// -127, 127), 0 where s = 0; 64-byte group-major records [m/64][n][64].
+void quantize_residual8(const float* R, int m, int n, int8_t* qw, uint16_t* wscale) {
+  constexpr int CB = 16;  // columns per task: each row is read 64 contiguous bytes at a time
+  parallel_for((n + CB - 1) / CB, [&](int64_t lo, int64_t hi) {
+    for (int64_t blk = lo; blk < hi; ++blk) {
+      const int j0 = (int)blk * CB, j1 = std::min(n, j0 + CB);
+      float amax[CB] = {};
+      for (int k = 0; k < m; ++k)
+        for (int j = j0; j < j1; ++j) amax[j - j0] = std::max(amax[j - j0], std::fabs(R[(int64_t)k * n + j]));
+      float s[CB];
+      for (int j = j0; j < j1; ++j) {
+        wscale[j] = f32_to_f16_sat(amax[j - j0] / 127.0f);
+        s[j - j0] = f16_to_f32(wscale[j]);
+      }
+      for (int k = 0; k < m; ++k)
+        for (int j = j0; j < j1; ++j) {
+          float q = 0.0f;
+          if (s[j - j0] > 0.0f) {
+            q = std::nearbyint(R[(int64_t)k * n + j] / s[j - j0]);
+            q = std::min(127.0f, std::max(-127.0f, q));
+          }
+          qw[((int64_t)(k / SVDQ_GROUP) * n + j) * SVDQ_GROUP + k % SVDQ_GROUP] = (int8_t)q;
+        }
+    }
+  });
+}
+
 // ---------------------------------------------------------------------------
 // protected-layer candidates and their selection ([Review] sec. 5, Algorithm 1)
 // ---------------------------------------------------------------------------
