@@ -56,6 +56,7 @@
 
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "device_common.h"
 #include "internal.h"
@@ -106,15 +107,24 @@ __device__ __forceinline__ Piece<BYTES> buffer_piece(__amdgpu_buffer_rsrc_t rs, 
   return p;
 }
 
-// Unpack a piece starting at word w0 of a record into the LDS row `row`: the
-// low nibbles of record word w go to byte 32*(w/4) + 4*(w%4), the high nibbles
-// 16 bytes further, each nibble becoming the signed byte 16*q.  Activations and
-// weights use the same placement, so the channel permutation cancels in the
-// dot product.
+// LDS rows hold the 64 bytes of one row of one channel group as four 16-byte
+// chunks; chunk j of row `row` sits at chunk position j ^ chunk_swz(row).  With
+// this permutation both access patterns are free of bank conflicts whether
+// the LDS serves 8 or 16 lanes of a 16-byte access per cycle: the staging
+// stores (lanes 2t, 2t+1 write the two halves of row t) and the MFMA operand
+// reads (16 consecutive rows at one chunk index).
+__device__ __forceinline__ int chunk_swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+
+// Unpack a piece starting at word w0 of a record into the LDS row `row` (whose
+// swizzle is rs): the low nibbles of record word w go to byte 4*(w%4) of chunk
+// 2*(w/4), the high nibbles to the same byte of chunk 2*(w/4)+1, each nibble
+// becoming the signed byte 16*q.  Activations and weights use the same
+// placement, so the channel permutation cancels in the dot product.
 template <int BYTES>
-__device__ __forceinline__ void unpack_piece(uint8_t* row, int w0, const Piece<BYTES>& p) {
+__device__ __forceinline__ void unpack_piece(uint8_t* row, int rs, int w0, const Piece<BYTES>& p) {
   constexpr int NW = BYTES / 4;
-  uint8_t* lo_dst = row + 32 * (w0 >> 2) + 4 * (w0 & 3);
+  uint8_t* lo_dst = row + 16 * ((2 * (w0 >> 2)) ^ rs) + 4 * (w0 & 3);
+  uint8_t* hi_dst = row + 16 * ((2 * (w0 >> 2) + 1) ^ rs) + 4 * (w0 & 3);
   uint32_t lo[NW], hi[NW];
 #pragma unroll
   for (int e = 0; e < NW; ++e) {
@@ -123,21 +133,29 @@ __device__ __forceinline__ void unpack_piece(uint8_t* row, int w0, const Piece<B
   }
   if constexpr (NW == 4) {
     *reinterpret_cast<u32x4*>(lo_dst) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-    *reinterpret_cast<u32x4*>(lo_dst + 16) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    *reinterpret_cast<u32x4*>(hi_dst) = u32x4{hi[0], hi[1], hi[2], hi[3]};
   } else if constexpr (NW == 2) {
     *reinterpret_cast<uint2*>(lo_dst) = uint2{lo[0], lo[1]};
-    *reinterpret_cast<uint2*>(lo_dst + 16) = uint2{hi[0], hi[1]};
+    *reinterpret_cast<uint2*>(hi_dst) = uint2{hi[0], hi[1]};
   } else {
     *reinterpret_cast<uint32_t*>(lo_dst) = lo[0];
-    *reinterpret_cast<uint32_t*>(lo_dst + 16) = hi[0];
+    *reinterpret_cast<uint32_t*>(hi_dst) = hi[0];
   }
 }
 
 // Copy a piece of an 8-bit record (64 codes, one byte each) starting at word w0
-// into the LDS row `row` unchanged.
-__device__ __forceinline__ void copy_piece(uint8_t* row, int w0, const Piece<32>& p) {
-  *reinterpret_cast<u32x4*>(row + 4 * w0) = u32x4{p.w[0], p.w[1], p.w[2], p.w[3]};
-  *reinterpret_cast<u32x4*>(row + 4 * w0 + 16) = u32x4{p.w[4], p.w[5], p.w[6], p.w[7]};
+// into the LDS row `row` (swizzle rs), chunk by chunk.
+__device__ __forceinline__ void copy_piece(uint8_t* row, int rs, int w0, const Piece<32>& p) {
+  const int j = w0 >> 2;
+  *reinterpret_cast<u32x4*>(row + 16 * (j ^ rs)) = u32x4{p.w[0], p.w[1], p.w[2], p.w[3]};
+  *reinterpret_cast<u32x4*>(row + 16 * ((j + 1) ^ rs)) = u32x4{p.w[4], p.w[5], p.w[6], p.w[7]};
+}
+
+// f(integral_constant<int, U>) for each U of the sequence, in order (compile-time
+// indices for register arrays).
+template <int... U, class F>
+__device__ __forceinline__ void unrolled(std::integer_sequence<int, U...>, F&& f) {
+  (f(std::integral_constant<int, U>{}), ...);
 }
 
 // Linear tile index -> (tile row, tile column), in bands of 4 tile-rows
@@ -162,20 +180,21 @@ __device__ __forceinline__ int dp_tile(int d, int count, int base) {
   return base + (xcd < extra ? xcd * (per + 1) + k : extra * (per + 1) + (xcd - extra) * per + k);
 }
 
-template <int TM_, int TN_, int WM_, int WN_, int WPE_, int DEPTH_>
+template <int TM_, int TN_, int WM_, int WN_, int WPE_, int DEPTH_, int KG_ = 1>
 struct GemmCfg {
   static constexpr int TM = TM_, TN = TN_;  // workgroup tile: rows (tokens) x output columns
   static constexpr int WM = WM_, WN = WN_;  // wave tile
   static constexpr int WPE = WPE_;          // waves per SIMD the register budget must allow
-  static constexpr int DEPTH = DEPTH_;      // groups of global loads in flight (even)
+  static constexpr int DEPTH = DEPTH_;      // pipeline steps of global loads in flight
+  static constexpr int KG = KG_;            // channel groups per pipeline step (per barrier)
   static constexpr int WAVES_N = TN / WN;
   static constexpr int NT = 64 * (TM / WM) * WAVES_N;
   static constexpr int BI = WM / 16, BJ = WN / 16;
   static constexpr int A_BYTES = TM * 32 / NT;  // packed activation bytes staged per thread per group
   static constexpr int B_BYTES = TN * 32 / NT;  // packed weight bytes staged per thread per group
-  static constexpr int ROWB = 64 + 16;          // LDS bytes per unpacked 64-channel row (+16 pad)
+  static constexpr int ROWB = 64;               // LDS bytes per unpacked 64-channel row
   static constexpr int WG_PER_CU = WPE * 4 / (NT / 64);  // resident workgroups per CU (4 SIMDs)
-  static_assert(DEPTH % 2 == 0, "the register ring alternates with the two LDS buffers");
+  static_assert(DEPTH >= 1 && KG >= 1, "pipeline shape");
   static_assert(WG_PER_CU >= 1 && (WPE * 4) % (NT / 64) == 0, "whole workgroups per CU");
   static_assert(A_BYTES == 4 || A_BYTES == 8 || A_BYTES == 16, "activation staging piece");
   static_assert(B_BYTES == 4 || B_BYTES == 8 || B_BYTES == 16, "weight staging piece");
@@ -186,6 +205,9 @@ struct GemmCfg {
 // 128 x 128 tile, 4 waves of 64 x 64; two workgroups share a CU, so one
 // workgroup's barrier and LDS-latency phases overlap the other's compute.
 using Cfg = GemmCfg<128, 128, 64, 64, 2, 2>;
+// 8-bit codes: no per-group VALU work, so a group's compute is short and the
+// loads run four groups ahead to cover the memory latency.
+using Cfg8 = GemmCfg<128, 128, 64, 64, 2, 4>;
 
 // Cache policy of the stream-K partials: sc1 = device-coherent.
 constexpr int kCoherent = 16;
@@ -217,17 +239,23 @@ __device__ __forceinline__ void gemm_up_body(
     void* __restrict__ yout, StreamK sk) {
   constexpr int TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN, NT = C::NT;
   constexpr int BI = C::BI, BJ = C::BJ, ROWB = C::ROWB;
-  __shared__ __align__(16) uint8_t As[2][TM * ROWB];
-  __shared__ __align__(16) uint8_t Bs[2][TN * ROWB];
-  // [sx/256 (TM) | -1.5*2^23 sx/256 (TM) | sw (TN) | unused (NT - TM - TN)]
-  // (no per-group scales with 8-bit codes)
-  __shared__ __align__(16) float Ssc[2][W8 ? 4 : TM + NT];
+  constexpr int KG = C::KG;
+  // per buffer: KG groups of TM (TN) rows
+  __shared__ __align__(16) uint8_t As[2][KG * TM * ROWB];
+  __shared__ __align__(16) uint8_t Bs[2][KG * TN * ROWB];
+  // per buffer and group: [sx/256 (TM) | -1.5*2^23 sx/256 (TM) | sw (TN) |
+  // unused (NT - TM - TN)] (no per-group scales with 8-bit codes)
+  constexpr int SSC = TM + NT;
+  __shared__ __align__(16) float Ssc[2][W8 ? 4 : KG * SSC];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int r = lane & 15, c = lane >> 4;
+  // this lane's 16-byte chunk of an MFMA operand row in LDS (rows of a block
+  // start at multiples of 16, so the row's swizzle is that of r)
+  const int cs = 16 * (c ^ chunk_swz(r));
   constexpr int REC = W8 ? 64 : 32;  // record bytes of one row in one group
   constexpr int AB = W8 ? 2 * C::A_BYTES : C::A_BYTES, BB = W8 ? 2 * C::B_BYTES : C::B_BYTES;
   const int a_row = tid * AB / REC, a_w0 = (tid * AB % REC) / 4;
@@ -298,11 +326,12 @@ __device__ __forceinline__ void gemm_up_body(
   // Staging: per group every thread issues the same three buffer loads: one
   // piece of an activation record, one piece of a weight record, one fp16
   // scale.  The per-group base lives in the (scalar) buffer descriptor, whose
-  // size bound makes rows >= b and columns >= n read as zero.
+  // size bound makes rows >= b and columns >= n read as zero.  A pipeline step
+  // stages KG consecutive groups.
   struct Stage {
-    Piece<AB> a;
-    Piece<BB> w;
-    uint32_t s;
+    Piece<AB> a[KG];
+    Piece<BB> w[KG];
+    uint32_t s[KG];
   };
   auto main_branch = [&](int i0, int j0, int g0, int g1) {
     const uint32_t a_voff = (uint32_t)(i0 + a_row) * REC + 4u * a_w0;
@@ -311,127 +340,149 @@ __device__ __forceinline__ void gemm_up_body(
     // out-of-range offset (reads 0) for the threads that stage no scale
     const uint32_t s_voff = tid < TM ? (uint32_t)(i0 + tid) * 2u
                                      : (tid < TM + TN ? (uint32_t)(j0 + tid - TM) * 2u : 0x7FFFFFF0u);
-    const int S = g1 - g0;  // groups in this segment
-    if (S <= 0) return;     // the up-projection alone (no channel groups)
+    const int NG = g1 - g0;            // groups in this segment
+    if (NG <= 0) return;               // the up-projection alone (no channel groups)
+    const int S = (NG + KG - 1) / KG;  // pipeline steps
+    // Step k's groups g0 + KG k + q.  A group past the segment's end reads as
+    // zero (size-0 descriptors: zero codes and scales add nothing); a step past
+    // the last one is never computed.
     auto load_stage = [&](int k, Stage& st) {
-      const int g = g0 + min(k, S - 1);
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(qx + (size_t)g * a_bytes, a_bytes);
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(qw + (size_t)g * b_bytes, b_bytes);
-      st.a = buffer_piece<AB>(ra, a_voff);
-      st.w = buffer_piece<BB>(rb, b_voff);
-      if constexpr (!W8) {
-        // wave-uniform choice (waves 0 .. TM/64-1 stage activation scales), so
-        // the descriptor stays in scalar registers
-        const __amdgpu_buffer_rsrc_t rs =
-            wave_u < TM / 64 ? make_rsrc(ascale + (size_t)g * b, (uint32_t)b * 2u)
-                             : make_rsrc(wscale + (size_t)g * n, (uint32_t)n * 2u);
-        st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, s_voff, 0, 0);
+#pragma unroll
+      for (int q = 0; q < KG; ++q) {
+        const int gi = KG * k + q;
+        const bool live = gi < NG;
+        const int g = g0 + (live ? gi : NG - 1);
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(qx + (size_t)g * a_bytes, live ? a_bytes : 0u);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(qw + (size_t)g * b_bytes, live ? b_bytes : 0u);
+        st.a[q] = buffer_piece<AB>(ra, a_voff);
+        st.w[q] = buffer_piece<BB>(rb, b_voff);
+        if constexpr (!W8) {
+          // wave-uniform choice (waves 0 .. TM/64-1 stage activation scales), so
+          // the descriptor stays in scalar registers
+          const __amdgpu_buffer_rsrc_t rs =
+              wave_u < TM / 64 ? make_rsrc(ascale + (size_t)g * b, live ? (uint32_t)b * 2u : 0u)
+                               : make_rsrc(wscale + (size_t)g * n, live ? (uint32_t)n * 2u : 0u);
+          st.s[q] = __builtin_amdgcn_raw_buffer_load_b16(rs, s_voff, 0, 0);
+        }
       }
     };
-    // Scales go to one LDS array per buffer: [sx/256 (TM) | -1.5*2^23 sx/256
-    // (TM) | sw (TN) | unused].  Thread t < TM stages row i0+t's activation
-    // scale (two words), thread TM+u column j0+u's weight scale (the same word
-    // twice; threads past TM+TN write zeros to the unused tail), so the staging
-    // is straight-line code.
+    // Scales go to one LDS array per buffer and group: [sx/256 (TM) |
+    // -1.5*2^23 sx/256 (TM) | sw (TN) | unused].  Thread t < TM stages row
+    // i0+t's activation scale (two words), thread TM+u column j0+u's weight
+    // scale (the same word twice; threads past TM+TN write zeros to the unused
+    // tail), so the staging is straight-line code.
     auto store_stage = [&](int buf, const Stage& st) {
-      if constexpr (W8) {
-        copy_piece(&As[buf][a_row * ROWB], a_w0, st.a);
-        copy_piece(&Bs[buf][b_col * ROWB], b_w0, st.w);
-      } else {
-        unpack_piece<AB>(&As[buf][a_row * ROWB], a_w0, st.a);
-        unpack_piece<BB>(&Bs[buf][b_col * ROWB], b_w0, st.w);
-        const float sv = f16_to_f32((uint16_t)st.s);
-        const bool act = wave_u < TM / 64;
-        const float q = sv * 0.00390625f;  // sx / 256 (exact)
-        Ssc[buf][act ? tid : TM + tid] = act ? q : sv;
-        Ssc[buf][TM + tid] = act ? -kMagic * q : sv;  // exact: 3 * 2^14 * sx
+#pragma unroll
+      for (int q = 0; q < KG; ++q) {
+        uint8_t* as = &As[buf][(q * TM + a_row) * ROWB];
+        uint8_t* bs = &Bs[buf][(q * TN + b_col) * ROWB];
+        if constexpr (W8) {
+          copy_piece(as, chunk_swz(a_row), a_w0, st.a[q]);
+          copy_piece(bs, chunk_swz(b_col), b_w0, st.w[q]);
+        } else {
+          unpack_piece<AB>(as, chunk_swz(a_row), a_w0, st.a[q]);
+          unpack_piece<BB>(bs, chunk_swz(b_col), b_w0, st.w[q]);
+          const float sv = f16_to_f32((uint16_t)st.s[q]);
+          const bool act = wave_u < TM / 64;
+          const float h = sv * 0.00390625f;  // sx / 256 (exact)
+          float* sc = &Ssc[buf][q * SSC];
+          sc[act ? tid : TM + tid] = act ? h : sv;
+          sc[TM + tid] = act ? -kMagic * h : sv;  // exact: 3 * 2^14 * sx
+        }
       }
     };
-    // One group.  INT4: for each 16-row block bi, BJ MFMAs (one per 16-column
-    // block), whose results are applied by 8 * BJ FMAs one block later, so an
-    // MFMA's latency is covered by the previous block's FMAs.  8-bit: the
-    // MFMAs accumulate into the integer sums directly.
-    auto compute = [&](int buf) {
+    // One group q of a buffer.  INT4: for each 16-row block bi, BJ MFMAs (one
+    // per 16-column block), whose results are applied by 8 * BJ FMAs one block
+    // later, so an MFMA's latency is covered by the previous block's FMAs.
+    // 8-bit: the MFMAs accumulate into the integer sums directly.
+    auto compute_group = [&](int buf, int q) {
+      const uint8_t* as = &As[buf][q * TM * ROWB];
+      const uint8_t* bs = &Bs[buf][q * TN * ROWB];
       if constexpr (W8) {
         u32x4 Pb[BJ];
 #pragma unroll
         for (int bj = 0; bj < BJ; ++bj)
-          Pb[bj] = *reinterpret_cast<const u32x4*>(&Bs[buf][(WN * wn + 16 * bj + r) * ROWB + 16 * c]);
+          Pb[bj] = *reinterpret_cast<const u32x4*>(bs + (WN * wn + 16 * bj + r) * ROWB + cs);
 #pragma unroll
         for (int bi = 0; bi < BI; ++bi) {
-          const u32x4 Qa = *reinterpret_cast<const u32x4*>(&As[buf][(WM * wm + 16 * bi + r) * ROWB + 16 * c]);
+          const u32x4 Qa = *reinterpret_cast<const u32x4*>(as + (WM * wm + 16 * bi + r) * ROWB + cs);
 #pragma unroll
           for (int bj = 0; bj < BJ; ++bj)
             iacc[bi][bj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
                 __builtin_bit_cast(i32x4, Pb[bj]), __builtin_bit_cast(i32x4, Qa), iacc[bi][bj], 0, 0, 0);
         }
       } else {
-      u32x4 Pb[BJ];
-      f32x4 sw4[BJ];
+        const float* sc = &Ssc[buf][q * SSC];
+        u32x4 Pb[BJ];
+        f32x4 sw4[BJ];
 #pragma unroll
-      for (int bj = 0; bj < BJ; ++bj) {
-        const int cc = WN * wn + 16 * bj;
-        Pb[bj] = *reinterpret_cast<const u32x4*>(&Bs[buf][(cc + r) * ROWB + 16 * c]);
-        sw4[bj] = *reinterpret_cast<const f32x4*>(&Ssc[buf][2 * TM + cc + 4 * c]);
-      }
-      const int rbase = WM * wm + r;
-      i32x4 d[2][BJ];
-      float sxq[2], sng[2];
-#pragma unroll
-      for (int bi = 0; bi <= BI; ++bi) {
-        const int cur = bi & 1, prev = cur ^ 1;
-        if (bi < BI) {
-          const int rr = rbase + 16 * bi;
-          const u32x4 Qa = *reinterpret_cast<const u32x4*>(&As[buf][rr * ROWB + 16 * c]);
-          sxq[cur] = Ssc[buf][rr];
-          sng[cur] = Ssc[buf][TM + rr];
-#pragma unroll
-          for (int bj = 0; bj < BJ; ++bj)
-            d[cur][bj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                __builtin_bit_cast(i32x4, Pb[bj]), __builtin_bit_cast(i32x4, Qa), magic, 0, 0, 0);
+        for (int bj = 0; bj < BJ; ++bj) {
+          const int cc = WN * wn + 16 * bj;
+          Pb[bj] = *reinterpret_cast<const u32x4*>(bs + (cc + r) * ROWB + cs);
+          sw4[bj] = *reinterpret_cast<const f32x4*>(sc + 2 * TM + cc + 4 * c);
         }
-        if (bi > 0) {
+        const int rbase = WM * wm + r;
+        i32x4 d[2][BJ];
+        float sxq[2], sng[2];
 #pragma unroll
-          for (int bj = 0; bj < BJ; ++bj)
+        for (int bi = 0; bi <= BI; ++bi) {
+          const int cur = bi & 1, prev = cur ^ 1;
+          if (bi < BI) {
+            const int rr = rbase + 16 * bi;
+            const u32x4 Qa = *reinterpret_cast<const u32x4*>(as + rr * ROWB + cs);
+            sxq[cur] = sc[rr];
+            sng[cur] = sc[TM + rr];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const float t = __builtin_fmaf(__int_as_float(d[prev][bj][v]), sxq[prev], sng[prev]);
-              acc[bi - 1][bj][v] = __builtin_fmaf(t, sw4[bj][v], acc[bi - 1][bj][v]);
-            }
+            for (int bj = 0; bj < BJ; ++bj)
+              d[cur][bj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                  __builtin_bit_cast(i32x4, Pb[bj]), __builtin_bit_cast(i32x4, Qa), magic, 0, 0, 0);
+          }
+          if (bi > 0) {
+#pragma unroll
+            for (int bj = 0; bj < BJ; ++bj)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const float t = __builtin_fmaf(__int_as_float(d[prev][bj][v]), sxq[prev], sng[prev]);
+                acc[bi - 1][bj][v] = __builtin_fmaf(t, sw4[bj][v], acc[bi - 1][bj][v]);
+              }
+          }
         }
-      }
       }
     };
 
-    // Pipeline: LDS buffer k & 1 holds group k while it is computed; register
-    // stage (k + 1) & 1 holds group k + 1, and stage k & 1 group k + 2 (still
-    // loading).  A step computes group k, moves group k + 1 from its register
-    // stage into the other LDS buffer, starts loading group k + 3 into the
-    // freed stage, and ends with one barrier.  Loads and stores are
-    // unconditional (past the end they re-read the last group into a buffer
-    // nobody reads), so no branch sits inside a step and each wait covers
-    // exactly one group.  The trailing barrier also frees the LDS buffers for
-    // the next segment.
-    static_assert(C::DEPTH == 2, "two register stages");
-    Stage st[2];
-    load_stage(0, st[0]);
-    load_stage(1, st[1]);
+    // Pipeline over D = C::DEPTH register stages: LDS buffer k & 1 holds step
+    // k's groups while they are computed, register stage j % D holds step j's
+    // for k < j <= k + D (the later ones still loading).  A step computes its
+    // groups, moves step k + 1's from their register stage into the other LDS
+    // buffer, starts loading step k + 1 + D's into the freed stage, and ends
+    // with one barrier, so loads have D steps to arrive.  Loads and stores are
+    // unconditional (past the last step they re-read the last group into a
+    // buffer nobody reads), so no branch sits inside a step and each wait
+    // covers exactly one step.  The trailing barrier also frees the LDS
+    // buffers for the next segment.  The loop is unrolled over lcm(D, 2) steps
+    // so that stage and buffer indices are compile-time constants.
+    constexpr int D = C::DEPTH;
+    constexpr int UNR = D % 2 == 0 ? D : 2 * D;
+    Stage st[D];
+#pragma unroll
+    for (int u = 0; u < D; ++u) load_stage(u, st[u]);
     store_stage(0, st[0]);
-    load_stage(2, st[0]);
+    load_stage(D, st[0]);
     __syncthreads();
-    auto step = [&](int k, auto BUF) {
-      constexpr int buf = decltype(BUF)::value;
-      compute(buf);
-      store_stage(buf ^ 1, st[buf ^ 1]);
-      load_stage(k + 3, st[buf ^ 1]);
+    auto step = [&](int k, auto U) {
+      constexpr int u = decltype(U)::value;  // k % UNR
+#pragma unroll
+      for (int q = 0; q < KG; ++q) compute_group(u & 1, q);
+      store_stage((u & 1) ^ 1, st[(u + 1) % D]);
+      load_stage(k + 1 + D, st[(u + 1) % D]);
       __syncthreads();
     };
     int k = 0;
-    for (; k + 1 < S; k += 2) {
-      step(k, std::integral_constant<int, 0>{});
-      step(k + 1, std::integral_constant<int, 1>{});
-    }
-    if (k < S) step(k, std::integral_constant<int, 0>{});
+    for (; k + UNR - 1 < S; k += UNR)
+      unrolled(std::make_integer_sequence<int, UNR>{}, [&](auto U) { step(k + decltype(U)::value, U); });
+    unrolled(std::make_integer_sequence<int, UNR - 1>{}, [&](auto U) {
+      if (k + decltype(U)::value < S) step(k + decltype(U)::value, U);
+    });
   };
 
   // ---- epilogue: bias, cast, one store of Y ---------------------------------
@@ -641,7 +692,7 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
     sk.epoch = next_launch_epoch();
   }
   if constexpr (W8)
-    hipLaunchKernelGGL((gemm_w8a8_up_kernel<Cfg, OUT_BF16>), dim3((unsigned)plan.grid), dim3(Cfg::NT), 0, st,
+    hipLaunchKernelGGL((gemm_w8a8_up_kernel<Cfg8, OUT_BF16>), dim3((unsigned)plan.grid), dim3(Cfg8::NT), 0, st,
                        qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
                        plan.tiles_n, y, sk);
   else
@@ -662,13 +713,15 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
 // iterations / 8) stream-K workgroups, dispatched first, and the full rounds
 // follow one tile per workgroup.  The workspace bound assumes the largest
 // gfx950 part (256 CUs), so it does not depend on the device.
-GemmPlan gemm_plan(int b, int n, int m, int cus) {
+GemmPlan gemm_plan(int b, int n, int m, int cus, bool w8) {
+  static_assert(Cfg::TM == Cfg8::TM && Cfg::TN == Cfg8::TN, "one tiling for both settings");
+  constexpr int kMaxWgPerCu = Cfg::WG_PER_CU > Cfg8::WG_PER_CU ? Cfg::WG_PER_CU : Cfg8::WG_PER_CU;
   GemmPlan p;
   p.G = m / 64;
   p.tiles_m = (b + Cfg::TM - 1) / Cfg::TM;
   p.tiles_n = (n + Cfg::TN - 1) / Cfg::TN;
   const long long T = (long long)p.tiles_m * p.tiles_n;
-  const long long slots = (long long)Cfg::WG_PER_CU * (cus > 0 ? cus : kMaxCUs);
+  const long long slots = (long long)(w8 ? Cfg8::WG_PER_CU : Cfg::WG_PER_CU) * (cus > 0 ? cus : kMaxCUs);
   const long long rounds = (T + slots - 1) / slots;
   const double idle = ((double)rounds - (double)T / (double)slots) * p.G;
   p.streamk = idle >= 16.0 && T * p.G >= 16;
@@ -683,7 +736,7 @@ GemmPlan gemm_plan(int b, int n, int m, int cus) {
   } else {
     p.grid = (int)T;
   }
-  const long long max_sk = std::max(1LL, std::min((long long)Cfg::WG_PER_CU * kMaxCUs, T * p.G / 8));
+  const long long max_sk = std::max(1LL, std::min((long long)kMaxWgPerCu * kMaxCUs, T * p.G / 8));
   p.partial_bytes = (size_t)max_sk * Cfg::TM * Cfg::TN * 4;
   p.ws_bytes = p.streamk || cus <= 0 ? p.partial_bytes + (size_t)max_sk * 8 : 0;
   return p;
@@ -712,7 +765,7 @@ int launch_gemm_up(const uint8_t* qx, const uint16_t* ascale, const float* z, co
 
 int launch_gemm8_up(const int8_t* qx, const uint16_t* ascale, const float* z, const svdq_w8a8_layer& L,
                     int b, void* y, int y_dtype, void* ws, void* stream) {
-  const GemmPlan plan = gemm_plan(b, L.n, L.m, device_cus());
+  const GemmPlan plan = gemm_plan(b, L.n, L.m, device_cus(), true);
   const Operands o{reinterpret_cast<const uint8_t*>(L.qw), L.wscale, L.l2, L.bias, L.n, L.rank};
   const uint8_t* a = reinterpret_cast<const uint8_t*>(qx);
   hipStream_t st = (hipStream_t)stream;

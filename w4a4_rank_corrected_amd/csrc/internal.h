@@ -121,8 +121,9 @@ struct GemmPlan {
   size_t partial_bytes; // partial-sum area at the start of the workspace
   size_t ws_bytes;      // workspace this launch needs (0 for one tile per workgroup)
 };
-// cus <= 0 gives the device-independent upper bound used to size workspaces.
-GemmPlan gemm_plan(int b, int n, int m, int cus);
+// cus <= 0 gives the device-independent upper bound used to size workspaces
+// (valid for both settings); w8 selects the 8-bit kernel's residency.
+GemmPlan gemm_plan(int b, int n, int m, int cus, bool w8 = false);
 int device_cus();
 int launch_gemm_up(const uint8_t* qx, const uint16_t* ascale, const float* z, const svdq_layer& L,
                    int b, void* y, int y_dtype, void* ws, void* stream);
