@@ -113,8 +113,9 @@ def trace_summary(prof_dir, cfg, args, rank):
     if not dbs:
         raise SystemExit(f"no rocpd database under {prof_dir}")
     c = sqlite3.connect(dbs[0])
+    w8 = args.w8a8 is not None
     _, n_sets = set_plan(cfg, rank, args.out)
-    skip = max(args.warmup, n_sets)
+    skip = max(50, args.warmup) if w8 else max(args.warmup, n_sets)
     short = lambda nm: re.sub(r"\(.*", "", nm.replace("svdq::(anonymous namespace)::", "")
                               .replace("void ", "").replace("svdq::", ""))
     rows = list(c.execute("select name, start, end, grid_x, grid_y, workgroup_x, workgroup_y, vgpr_count, "
@@ -123,15 +124,23 @@ def trace_summary(prof_dir, cfg, args, rank):
     for nm, st, en, gx, gy, wx, wy, vg, ag, lds, scr in rows:
         wgs = (gx // max(wx, 1)) * (gy // max(wy, 1))
         by.setdefault(nm, []).append(((en - st) / 1e3, wgs, wx * wy, vg, ag, lds, scr))
+    mode = f" --w8a8 {args.w8a8}" if w8 else " --no-cpu-baseline"
     cmd = (f"rocprofv3 --kernel-trace --stats -d {prof_dir} -o run -- python3 bench.py --workload {cfg.name} "
-           f"--steps {args.steps} --warmup {args.warmup} --no-cpu-baseline")
-    out = [f"# Kernel trace: {cfg.name} (b={cfg.rows or cfg.b}, m={cfg.m}, n={cfg.n}, rank {rank})", "",
+           f"--steps {args.steps} --warmup {args.warmup}{mode}")
+    if w8:
+        region = (f"Timed region: {args.steps} steps after {skip} untimed ones; each step runs the INT4 "
+                  f"activation kernel, the INT4 GEMM, the 8-bit activation kernels and the 8-bit GEMM, "
+                  f"all at rank {rank} on one input and weight set (warm).")
+        title = f"# Kernel trace, 8-bit setting against INT4: {cfg.name}"
+    else:
+        region = (f"Timed region: {args.steps} steps after {skip} untimed ones, rotating over {n_sets} "
+                  f"input+weight sets; the script then times warm steps, rank-0 steps and the one-call entry "
+                  f"point, which the all-dispatch columns include.")
+        title = f"# Kernel trace: {cfg.name}"
+    out = [f"{title} (b={cfg.rows or cfg.b}, m={cfg.m}, n={cfg.n}, rank {rank})", "",
            "Command (repository root, one MI355X), then the summary:", "", "```", cmd,
            f"python bench.py --trace-summary {prof_dir} --workload {cfg.name} --steps {args.steps} "
-           f"--warmup {args.warmup}", "```", "",
-           f"Timed region: {args.steps} steps after {skip} untimed ones, rotating over {n_sets} "
-           f"input+weight sets; the script then times warm steps, rank-0 steps and the one-call entry "
-           f"point, which the all-dispatch columns include.", "",
+           f"--warmup {args.warmup}" + (f" --w8a8 {args.w8a8}" if w8 else ""), "```", "", region, "",
            "| kernel | dispatches | mean, timed region (us) | mean, all (us) | total (ms) | workgroups | "
            "threads | LDS (B) | scratch (B) |",
            "|---|---|---|---|---|---|---|---|---|"]
@@ -145,7 +154,7 @@ def trace_summary(prof_dir, cfg, args, rank):
         out.append(f"| `{short(nm)}` | {len(v)} | {t} | {np.mean(durs):.2f} | {sum(durs) / 1e3:.3f} | "
                    f"{d0[1]} | {d0[2]} | {d0[5]} | {d0[6]} |")
     out += ["", f"All kernels: {total / 1e3:.3f} ms of GPU time.", ""]
-    path = os.path.join(ROOT, "profiles", f"kernel_trace_{cfg.name}.md")
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{'w8a8_' if w8 else ''}{cfg.name}.md")
     with open(path, "w") as f:
         f.write("\n".join(out))
     print("\n".join(out))
@@ -487,7 +496,7 @@ def main():
         import workloads
         cfg = workloads.CONFIGS[args.workload]
         rank = (cfg.rank + cfg.lora_rank) if args.rank is None else args.rank
-        trace_summary(args.trace_summary, cfg, args, rank)
+        trace_summary(args.trace_summary, cfg, args, args.w8a8 if args.w8a8 is not None else rank)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
