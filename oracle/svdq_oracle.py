@@ -50,6 +50,20 @@ Readings taken where the pages are silent (each also listed in the design doc):
       quantizer as INT4 with 127 in place of 7: codes in [-127, 127], 16-bit
       (fp16) scales fp16(fl32(amax / 127)) over a whole row of X~ (per token)
       or a whole column of R (per output channel).
+  R20 the NVFP4 setting (sec. 8: group size 16 with FP8 scales; sec. 2.2 notes
+      FP4's nonuniform grid): element codes are FP4 E2M1 (values 0, 0.5, 1,
+      1.5, 2, 3, 4, 6; sign bit 3), block scales FP8 E4M3 (bias 7, largest
+      finite 448, subnormal quantum 2^-9), one per 16 consecutive input
+      channels of a row of X~ or of a column of R, and one power-of-two fp32
+      scale t per tensor that places the block scales in E4M3's range:
+      t = 2^ceil(log2(A / (6 * 448))) with A the tensor's largest magnitude
+      (for X~, its calibration maximum; t = 1 without calibration).  Per block
+      sb = E4M3_RNE_sat(fl32(amax / 6) / t) and S = sb * t; codes are
+      E2M1_RNE_sat(fl32(v / S)) with ties to the even code and the sign of the
+      quotient (so -0 is code 8); sb = 0 gives codes 0.  The product is
+      Y = t_x t_w (X^ W^) + bf16(Z) L2 (+ bias), X^ and W^ the dequantized
+      codes (exact), the rank-r branch as for INT4 (the 4-bit setting's rank
+      32).
   R17 the optional factor update of step 6 refits rank-r SVD factors to
       W~ - Q(R) (Q(R) dequantized exactly); the residual of step 7 is then
       formed and quantized again; of equal scores the first candidate
@@ -549,3 +563,141 @@ def linear_w8a8(x32: np.ndarray, layer: dict, bias: Optional[np.ndarray] = None)
     if bias is not None:
         y = y + np.asarray(bias, dtype=np.float64)[None, :]
     return {"y": y, "xt": xt, "qx": qx, "sx": sx, "z": z, "isum": isum}
+
+
+# --------------------------------------------------------------------------
+# The NVFP4 setting ([Review] sec. 8 and sec. 2.2; reading R20): FP4 E2M1
+# codes in blocks of 16 with FP8 E4M3 block scales and a power-of-two tensor
+# scale.
+# --------------------------------------------------------------------------
+
+FP4_BLOCK = 16
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+E4M3_MAX = 448.0
+FP4_RANGE = 6.0 * E4M3_MAX   # the largest magnitude a block can represent at t = 1
+
+
+def e4m3_round(x) -> np.ndarray:
+    """Nearest FP8 E4M3 value of x >= 0 (float64 result): quantum 2^(e-3) in
+    the binade [2^e, 2^(e+1)) for e >= -6 and 2^-9 below (subnormals), ties to
+    even, saturated at 448."""
+    x = np.asarray(x, dtype=np.float64)
+    _, ex = np.frexp(np.where(x > 0, x, 1.0))          # x = m 2^ex, m in [0.5, 1)
+    e = np.maximum(ex - 1, -6)
+    quantum = np.ldexp(1.0, e - 3)
+    return np.minimum(np.rint(x / quantum) * quantum, E4M3_MAX)
+
+
+def e4m3_bits(v) -> np.ndarray:
+    """FP8 E4M3 bit patterns (uint8) of non-negative E4M3 values."""
+    v = np.asarray(v, dtype=np.float64)
+    _, ex = np.frexp(np.where(v > 0, v, 1.0))
+    e = ex - 1
+    normal = (v >= 2.0 ** -6)
+    mant_n = np.rint((v / np.ldexp(1.0, e) - 1.0) * 8.0)
+    mant_s = np.rint(v / 2.0 ** -9)
+    bits = np.where(normal, ((e + 7) << 3) + mant_n, mant_s)
+    return bits.astype(np.uint8)
+
+
+def e4m3_from_bits(bits) -> np.ndarray:
+    """Value of FP8 E4M3 bit patterns (sign ignored; 0x7F/0xFF are NaN and not produced)."""
+    b = np.asarray(bits, dtype=np.int64) & 0x7F
+    e, m = b >> 3, b & 7
+    return np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
+
+
+def e2m1_codes(y32) -> np.ndarray:
+    """FP4 E2M1 codes (uint8, sign in bit 3) of float32 quotients: the nearest
+    grid value, ties to the even code, magnitudes beyond 6 saturated; the sign
+    bit is the quotient's (so -0 and small negatives give code 8)."""
+    y = np.asarray(y32, dtype=np.float32)
+    a = np.abs(y).astype(np.float64)
+    d = np.abs(a[..., None] - E2M1_VALUES)
+    i = np.argmin(d, axis=-1)                            # lowest index among equal distances
+    nxt = np.minimum(i + 1, 7)
+    tie_up = (i % 2 == 1) & (np.take_along_axis(d, nxt[..., None], -1)[..., 0] ==
+                             np.take_along_axis(d, i[..., None], -1)[..., 0])
+    i = np.where(tie_up, nxt, i)
+    return (i + np.where(np.signbit(y), 8, 0)).astype(np.uint8)
+
+
+def e2m1_values(codes) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.int64)
+    return np.where(c & 8, -1.0, 1.0) * E2M1_VALUES[c & 7]
+
+
+def pow2_ceil(x: float) -> float:
+    """2^ceil(log2 x) for x > 0 (exact), 1.0 for x <= 0."""
+    if not x > 0:
+        return 1.0
+    m, e = math.frexp(x)
+    return x if m == 0.5 else math.ldexp(1.0, e)
+
+
+def fp4_tensor_scale(amax: float) -> float:
+    """Power-of-two tensor scale t = 2^ceil(log2(amax / (6 * 448))) (reading R20)."""
+    return pow2_ceil(float(amax) / FP4_RANGE)
+
+
+def quantize_fp4_blocks(v32: np.ndarray, t: float):
+    """Blocks of 16 along the last axis of a float32 array.  Returns (codes
+    uint8 [..., K], block scales sb float64 [..., K/16] holding E4M3 values)."""
+    v32 = np.asarray(v32, dtype=np.float32)
+    K = v32.shape[-1]
+    blocks = v32.reshape(v32.shape[:-1] + (K // FP4_BLOCK, FP4_BLOCK))
+    amax = np.max(np.abs(blocks), axis=-1)
+    u = (amax / np.float32(6.0)).astype(np.float32)     # fl32(amax / 6)
+    sb = e4m3_round(u.astype(np.float64) / t)             # t is a power of two: exact
+    S = (sb * t).astype(np.float32)                       # exact
+    Sb = S[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = np.where(Sb > 0, blocks / np.where(Sb > 0, Sb, np.float32(1)), np.float32(0)).astype(np.float32)
+    codes = np.where(Sb > 0, e2m1_codes(y), 0).astype(np.uint8)
+    return codes.reshape(v32.shape), sb
+
+
+def dequantize_fp4_blocks(codes: np.ndarray, sb: np.ndarray) -> np.ndarray:
+    """code value x block scale (float64, exact; the tensor scale is separate)."""
+    return e2m1_values(codes) * np.repeat(np.asarray(sb, np.float64), FP4_BLOCK, axis=-1)
+
+
+def prepare_weights_fp4(w32: np.ndarray, a: Optional[np.ndarray], rank: int = 32, alpha: float = 0.5,
+                        svd: str = "lapack") -> dict:
+    """The NVFP4 protected layer: smoothing and the rank-r branch as in
+    ``prepare_weights``, R quantized per output column in blocks of 16 input
+    channels.  Returns the keys of ``prepare_weights`` plus qw (codes [m][n]),
+    sbw (E4M3 block scales [m/16][n]), t_w, t_x."""
+    base = prepare_weights(w32, a, rank, GROUP, alpha, svd)
+    r32 = base["r32"]
+    t_w = fp4_tensor_scale(np.max(np.abs(r32)))
+    codes_t, sb_t = quantize_fp4_blocks(np.ascontiguousarray(r32.T), t_w)
+    if a is None:
+        t_x = 1.0
+    else:
+        # calibration maximum of |X~| per channel: bf16(fl32(a_k * inv_k)) (reading R7)
+        xt_max = bf16_from_f32(np.asarray(a, np.float32) * base["inv32"]).astype(np.float64)
+        t_x = fp4_tensor_scale(np.max(xt_max))
+    return dict(base, qw=np.ascontiguousarray(codes_t.T), sbw=np.ascontiguousarray(sb_t.T), t_w=t_w, t_x=t_x,
+                fmt="nvfp4")
+
+
+def quantize_activation_fp4(x32: np.ndarray, inv32: Optional[np.ndarray], t_x: float):
+    xt = smooth_activation(x32, inv32)
+    qx, sbx = quantize_fp4_blocks(xt, t_x)
+    return xt, qx, sbx
+
+
+def linear_fp4(x32: np.ndarray, layer: dict, bias: Optional[np.ndarray] = None) -> dict:
+    """Y = t_x t_w (X^ W^) + bf16(X~ L1) L2 (+ bias) in float64 (reading R20)."""
+    xt, qx, sbx = quantize_activation_fp4(x32, layer.get("inv32"), layer["t_x"])
+    xhat = dequantize_fp4_blocks(qx, sbx)
+    what = dequantize_fp4_blocks(layer["qw"].T, layer["sbw"].T).T
+    y = (layer["t_x"] * layer["t_w"]) * (xhat @ what)
+    r = layer["l1"].shape[1]
+    z = lowrank_down(xt, layer["l1"]) if r else np.zeros((x32.shape[0], 0))
+    if r:
+        y = y + lowrank_up(z, layer["l2"])
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)[None, :]
+    return {"y": y, "xt": xt, "qx": qx, "sbx": sbx, "z": z}

@@ -582,3 +582,131 @@ def test_w8a8_error_below_w4a4_on_an_outlier_layer():
     e8 = np.linalg.norm(O.linear_w8a8(x, O.prepare_weights_w8a8(w, a, 16))["y"] - ref)
     e4 = np.linalg.norm(O.linear(x, O.prepare_weights(w, a, 16))["y"] - ref)
     assert e8 < e4
+
+
+# ---------------------------------------------------------------------------
+# the NVFP4 setting (reading R20)
+# ---------------------------------------------------------------------------
+
+def _e4m3_by_rationals(x: Fraction) -> Fraction:
+    """4 significant bits, smallest normal binade 2^-6, saturation at 448."""
+    v = _round_to_grid(x, 4, -6, Fraction(448))
+    return Fraction(448) if v == math.inf else v
+
+
+def test_e4m3_round_matches_rational_rounding_and_bit_patterns():
+    # every finite non-negative E4M3 value decodes, encodes and rounds to itself
+    vals = O.e4m3_from_bits(np.arange(0x7F))
+    assert vals[0x01] == 2.0 ** -9 and vals[0x08] == 2.0 ** -6 and vals[0x7E] == 448.0
+    assert np.array_equal(O.e4m3_bits(vals), np.arange(0x7F, dtype=np.uint8))
+    assert np.array_equal(O.e4m3_round(vals), vals)
+    # midpoints (ties), their neighbours, random magnitudes and values past the range
+    mids = (vals[1:] + vals[:-1]) / 2
+    rng = np.random.default_rng(20)
+    xs = np.concatenate([mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+                         np.exp(rng.uniform(np.log(2.0 ** -12), np.log(600.0), 3000)), [0.0, 449.0, 1e6]])
+    xs = xs.astype(np.float32).astype(np.float64)
+    got = O.e4m3_round(xs)
+    for x, g in zip(xs, got):
+        assert Fraction(float(g)) == _e4m3_by_rationals(Fraction(float(x))), x
+
+
+def _e2m1_by_thresholds(y: float) -> int:
+    """Independent form of the E2M1 rounding: count the midpoints below |y|;
+    a quotient exactly on a midpoint goes to the even code (up at 0.75, 1.75,
+    3.5; down at 0.25, 1.25, 2.5, 5)."""
+    a = abs(y)
+    up_on_tie = {0.75, 1.75, 3.5}
+    idx = sum(1 for t in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0) if a > t or (a == t and t in up_on_tie))
+    return idx + (8 if math.copysign(1.0, y) < 0 else 0)
+
+
+def test_e2m1_codes_match_threshold_form_on_every_bf16_and_the_ties():
+    bits = np.arange(0x10000, dtype=np.uint32)
+    ys = (bits << 16).view(np.float32)
+    ys = ys[np.isfinite(ys) & (np.abs(ys) <= 16)]
+    extra = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], np.float32)
+    ys = np.concatenate([ys, extra, -extra, np.nextafter(extra, np.float32(0)), np.nextafter(extra, np.float32(9))])
+    got = O.e2m1_codes(ys)
+    want = np.array([_e2m1_by_thresholds(float(y)) for y in ys])
+    assert np.array_equal(got, want)
+    assert np.array_equal(O.e2m1_values(np.arange(16)),
+                          [0, .5, 1, 1.5, 2, 3, 4, 6, -0.0, -.5, -1, -1.5, -2, -3, -4, -6])
+
+
+def test_fp4_block_quantizer_hand_example():
+    """Two blocks worked by hand at t = 1.
+    Block 0: amax 6 -> fl32(6/6) = 1 -> sb = 1, S = 1; the codes are the grid
+    roundings of the values themselves.
+    Block 1: amax 0.9 -> fl32(0.9/6) = 0.15 (fl32) lies in [2^-3, 2^-2), E4M3
+    quantum 2^-6: 0.15 / 2^-6 = 9.6 -> 10 -> sb = 0.15625; 0.9 / S = 5.76 -> 6."""
+    b0 = [6, -3, 1.3, 0.2, 0.26, -0.75, 2.5, 5, 0, -0.0, 1.75, 3.5, -5.5, 0.25, 1.25, -6]
+    b1 = [0.9, -0.1, 0.2, 0.0] + [0.05] * 12
+    v = np.array([b0 + b1], np.float32)
+    codes, sb = O.quantize_fp4_blocks(v, 1.0)
+    assert sb.tolist() == [[1.0, 0.15625]]
+    want0 = [7, 13, 3, 0, 1, 10, 4, 6, 0, 8, 4, 6, 15, 0, 2, 15]
+    # block 1: 0.9/S = 5.76 -> 6 (7); -0.1/S = -0.64 -> -0.5 (9); 0.2/S = 1.28 -> 1.5 (3);
+    # 0 -> 0; 0.05/S = 0.32 -> 0.5 (1)
+    want1 = [7, 9, 3, 0] + [1] * 12
+    assert codes[0].tolist() == want0 + want1
+    # a zero block and a block whose scale underflows E4M3 give code 0 everywhere
+    z = np.zeros((1, 32), np.float32)
+    z[0, 16:] = 1e-6
+    cz, sz = O.quantize_fp4_blocks(z, 1.0)
+    assert sz.tolist() == [[0.0, 0.0]] and not cz.any()
+
+
+def test_fp4_codes_within_half_a_grid_step():
+    """|v/S - value(code)| is at most half the grid spacing at |v/S| (0.25 below
+    2, 0.5 below 4, 1 above), or the overshoot past 6 when sb rounded down."""
+    rng = np.random.default_rng(21)
+    v = (rng.standard_normal((40, 64)) * np.exp(rng.uniform(-8, 4, (40, 1)))).astype(np.float32)
+    t = O.fp4_tensor_scale(np.max(np.abs(v)))
+    codes, sb = O.quantize_fp4_blocks(v, t)
+    S = np.repeat(sb * t, 16, axis=-1)
+    ok = S > 0
+    y = np.abs(v.astype(np.float64)[ok] / S[ok])
+    err = np.abs(y - np.abs(O.e2m1_values(codes[ok])))
+    half = np.where(y < 2, 0.25, np.where(y < 4, 0.5, 1.0))
+    assert np.all(err <= np.maximum(half, y - 6.0) + 1e-12)
+    # E4M3 rounding moves the block scale by at most half a quantum: 2^-4
+    # relative for normal scales, 2^-10 t absolute for subnormal ones
+    amax_b = np.max(np.abs(v.reshape(40, 4, 16)), -1).astype(np.float64)
+    assert np.all(np.abs(sb * t - amax_b / 6) <= np.maximum(amax_b / 6 * 2 ** -4, 2 ** -10 * t) * (1 + 1e-6))
+
+
+def test_fp4_linear_exact_when_blocks_sit_on_the_grid():
+    """Rank 0, no smoothing; every 16-block of X and of each column of W holds
+    grid values times one power of two and reaches 6 * 2^k, so every block
+    scale is 2^k / t exactly and Q loses nothing: Y = X W exactly."""
+    rng = np.random.default_rng(22)
+    def grid_blocks(rows, K):
+        v = O.E2M1_VALUES[rng.integers(0, 8, (rows, K))] * rng.choice([-1.0, 1.0], (rows, K))
+        v[:, ::16] = 6.0
+        return v * np.repeat(2.0 ** rng.integers(-3, 4, (rows, K // 16)), 16, axis=1)
+    x = grid_blocks(5, 64).astype(np.float32)
+    w = grid_blocks(24, 64).T.astype(np.float32)          # blocks along the input channels
+    lay = O.prepare_weights_fp4(w, None, 0)
+    assert lay["t_x"] == 1.0
+    out = O.linear_fp4(x, lay)
+    assert np.array_equal(out["y"], x.astype(np.float64) @ w.astype(np.float64))
+
+
+def test_fp4_tensor_scale_places_block_scales_in_range():
+    for amax in [1e-6, 0.01, 1.0, 2688.0, 2689.0, 1e6]:
+        t = O.fp4_tensor_scale(amax)
+        assert math.frexp(t)[0] == 0.5                     # a power of two
+        assert amax / (6 * t) <= 448.0 < 2 * amax / (6 * t)
+
+
+def test_fp4_error_below_int4_on_an_outlier_layer():
+    """Direction only (the pages report better similarity for NVFP4 than INT4,
+    sec. 8 / Table 1, without a margin that transfers to synthetic layers)."""
+    inp = workloads.make_inputs("tiny")
+    x, w = inp["x"], inp["w"]
+    a = O.act_amax(x)
+    ref = x.astype(np.float64) @ w.astype(np.float64)
+    ef = np.linalg.norm(O.linear_fp4(x, O.prepare_weights_fp4(w, a, 16))["y"] - ref)
+    e4 = np.linalg.norm(O.linear(x, O.prepare_weights(w, a, 16))["y"] - ref)
+    assert ef < e4
