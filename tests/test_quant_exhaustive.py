@@ -80,3 +80,41 @@ def test_checker_catches_missing_correction(checker):
     r = subprocess.run([exe, tabs[7], "7", "nocorr"], capture_output=True, text=True, timeout=600)
     pairs, bad, ties, nans = map(int, r.stdout.split())
     assert bad > 0 and r.returncode == 1
+
+
+# ---------------------------------------------------------------------------
+# the NVFP4 setting: division-free quotient against v / S for every E4M3
+# block scale, tensor-scale exponent and bf16 value
+# ---------------------------------------------------------------------------
+
+FP4_SRC = os.path.join(HERE, "native", "fp4_quotient_exhaustive.c")
+
+
+@pytest.fixture(scope="module")
+def fp4_checker(tmp_path_factory):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    exe = str(tmp_path_factory.mktemp("fp4q") / "fp4_quotient_exhaustive")
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+                           "-o", exe, FP4_SRC, "-lm"])
+    return exe
+
+
+def test_fp4_division_free_quotient_exhaustive(fp4_checker):
+    r = subprocess.run([fp4_checker], capture_output=True, text=True, timeout=600)
+    pairs, bad, _ = map(int, r.stdout.split())
+    assert pairs == 126 * 41 * (65536 - 256)   # finite bf16 patterns, 126 scales, 41 exponents
+    assert bad == 0 and r.returncode == 0
+
+
+def test_fp4_checker_catches_missing_correction(fp4_checker):
+    r = subprocess.run([fp4_checker, "nocorr"], capture_output=True, text=True, timeout=600)
+    _, bad, _ = map(int, r.stdout.split())
+    assert bad > 0 and r.returncode == 1
+
+
+def test_fp4_checker_code_rule_matches_oracle():
+    """The checker's threshold-form E2M1 rounding and E4M3 decoding are those of
+    the oracle (the checker is C; this ties the two together on all inputs)."""
+    vals = O.e4m3_from_bits(np.arange(1, 0x7F))
+    assert vals.min() == 2.0 ** -9 and vals.max() == 448.0 and len(set(vals.tolist())) == 126
