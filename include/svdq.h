@@ -336,6 +336,90 @@ size_t svdq_w8a8_linear_workspace_size(int b, int m, int n, int rank);
 int svdq_w8a8_linear(const uint16_t* x, const svdq_w8a8_layer* layer, int b, void* y, int y_dtype,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* ===========================================================================
+ * The NVFP4 setting ([Review] sec. 8: the 4-bit setting with group size 16
+ * and FP8 scales; sec. 2.2: FP4's nonuniform grid).
+ *   - FP4 E2M1 codes (values 0, 0.5, 1, 1.5, 2, 3, 4, 6; bit 3 = sign), two
+ *     per byte in the INT4 record layout: for channels 64g..64g+63 and row
+ *     (or column) r one 32-byte record, byte t = code[2t] | code[2t+1] << 4;
+ *     a tensor of R rows is [m/64][R][32].
+ *   - One FP8 E4M3 block scale (bias 7, largest finite 448) per 16 consecutive
+ *     channels, stored as bytes [m/64][R][4] (byte j = channels 64g+16j ..).
+ *   - One power-of-two fp32 tensor scale t per operand placing the block
+ *     scales in E4M3's range: for a block of magnitudes amax,
+ *     sb = E4M3_RNE_sat(fl32(amax / 6) / t), S = sb t, and each code is
+ *     E2M1_RNE_sat(fl32(v / S)) with ties to the even code and the quotient's
+ *     sign (sb = 0: codes 0).
+ *   - Y = t_x t_w (X^ W^) + bf16(Z) L2 + bias, X^ and W^ the dequantized codes
+ *     (code value times block scale, exact in f16), fp32 accumulation.
+ * ========================================================================= */
+
+/* A prepared NVFP4 layer on the device (caller-owned DEVICE pointers).
+ *   m, n, rank   as in svdq_layer (m % 64 == 0).
+ *   t_x, t_w     the activation and weight tensor scales (positive powers of two).
+ *   smooth_inv, l1, l2, bias   as in svdq_layer.
+ *   qw           FP4 codes of R, [m/64][n][32].
+ *   wscale       E4M3 block scales, bytes [m/64][n][4]. */
+typedef struct svdq_fp4_layer {
+  int32_t m, n, rank;
+  float t_x, t_w;
+  const float* smooth_inv;
+  const uint8_t* qw;
+  const uint8_t* wscale;
+  const uint16_t* l1;
+  const uint16_t* l2;
+  const uint16_t* bias;
+} svdq_fp4_layer;
+
+/* HOST: offline preparation of an NVFP4 layer: steps 2-4 of [Review]
+ * Algorithm 1 exactly as svdq_prepare_weights, then R quantized per output
+ * column in blocks of 16 input channels with t_w = 2^ceil(log2(max|R| / 2688)).
+ * The activation tensor scale comes from the calibration statistic:
+ * t_x = 2^ceil(log2(A / 2688)) with A = max_k bf16(fl32(a_k / lambda_k)), the
+ * largest smoothed calibration magnitude (t_x = 1 when act_amax is NULL).
+ * Outputs (HOST, caller-allocated): qw [m/64][n][32], wscale [m/64][n][4],
+ * l1, l2, lambda, smooth_inv, residual (nullable) as svdq_prepare_weights,
+ * t_x and t_w (one float each).  Errors as svdq_prepare_weights. */
+int svdq_fp4_prepare_weights(const float* W, const float* act_amax, int m, int n, int rank, float alpha,
+                             uint8_t* qw, uint8_t* wscale, uint16_t* l1, uint16_t* l2, float* lambda,
+                             float* smooth_inv, float* residual, float* t_x, float* t_w);
+
+/* Bytes of device workspace svdq_fp4_quantize_act_lowrank_down needs (as
+ * svdq_act_workspace_size). */
+size_t svdq_fp4_act_workspace_size(int b, int m, int rank);
+
+/* DEVICE: fused NVFP4 activation quantization + low-rank down-projection (the
+ * act-quant kernel of svdq_quantize_act_lowrank_down with the NVFP4 quantizer):
+ *     x~ = bf16(fl32(x * smooth_inv)); per row and 16 channels sb, codes as
+ *     above with tensor scale t_x; z = x~ L1 (fp32).
+ *   Outputs: qx [m/64][b][32], ascale bytes [m/64][b][4] (any alignment), z
+ *   fp32 [b][rank] (NULL iff rank == 0).  t_x a positive power of two.  Other
+ *   arguments as svdq_quantize_act_lowrank_down. */
+int svdq_fp4_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int rank, const float* smooth_inv,
+                                       const uint16_t* l1, float t_x, uint8_t* qx, uint8_t* ascale, float* z,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace svdq_fp4_gemm_lowrank_up may need (fp32 partial
+ * tiles and flags of its stream-K schedule). */
+size_t svdq_fp4_gemm_workspace_size(int b, int n, int m);
+
+/* DEVICE: NVFP4 GEMM + low-rank up-projection:
+ *     Y = t_x t_w sum_k x^[i,k] w^[k,j] + (bf16(z) L2)[i,j] + bias[j]
+ *   x^ = E2M1(qx) * E4M3(ascale block), w^ likewise (exact f16 values), fp32
+ *   accumulation in a fixed order (deterministic).  y, the workspace and the
+ *   remaining arguments as svdq_gemm_w4a4_lowrank_up. */
+int svdq_fp4_gemm_lowrank_up(const uint8_t* qx, const uint8_t* ascale, const float* z,
+                             const svdq_fp4_layer* layer, int b, void* y, int y_dtype, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace svdq_fp4_linear needs. */
+size_t svdq_fp4_linear_workspace_size(int b, int m, int n, int rank);
+
+/* DEVICE: the whole NVFP4 layer: exactly the kernels of the two entry points
+ * above (bit-identical output).  Arguments as svdq_linear. */
+int svdq_fp4_linear(const uint16_t* x, const svdq_fp4_layer* layer, int b, void* y, int y_dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -111,3 +111,48 @@ def oracle_w8a8_to_host_abi(lay: dict) -> dict:
         "l2": np.ascontiguousarray(f32_to_bf16_bits(lay["l2"]).T),
         "smooth_inv": np.ones(m, np.float32) if inv is None else np.asarray(inv, np.float32),
     }
+
+
+# ---- the NVFP4 setting: E2M1 codes two per byte, E4M3 block-scale bytes -------
+
+def pack_fp4_codes(codes: np.ndarray) -> np.ndarray:
+    """4-bit code patterns [R][K] (uint8, sign in bit 3) -> records uint8 [K/64][R][32]."""
+    R, K = codes.shape
+    c = (np.asarray(codes).astype(np.uint8) & 0xF).reshape(R, K // GROUP, 32, 2)
+    return np.ascontiguousarray((c[..., 0] | (c[..., 1] << 4)).transpose(1, 0, 2))
+
+
+def unpack_fp4_codes(recs: np.ndarray) -> np.ndarray:
+    """records uint8 [G][R][32] -> 4-bit code patterns uint8 [R][G*64]."""
+    recs = np.asarray(recs, dtype=np.uint8)
+    G, R, _ = recs.shape
+    codes = np.stack([recs & 0xF, recs >> 4], axis=-1).reshape(G, R, GROUP)
+    return np.ascontiguousarray(codes.transpose(1, 0, 2).reshape(R, G * GROUP))
+
+
+def pack_fp4_scales(scale_bits: np.ndarray) -> np.ndarray:
+    """E4M3 bytes [R][K/16] -> [K/64][R][4]."""
+    R, B = scale_bits.shape
+    return np.ascontiguousarray(np.asarray(scale_bits, np.uint8).reshape(R, B // 4, 4).transpose(1, 0, 2))
+
+
+def unpack_fp4_scales(recs: np.ndarray) -> np.ndarray:
+    """[G][R][4] bytes -> [R][G*4]."""
+    recs = np.asarray(recs, dtype=np.uint8)
+    G, R, _ = recs.shape
+    return np.ascontiguousarray(recs.transpose(1, 0, 2).reshape(R, G * 4))
+
+
+def oracle_fp4_to_host_abi(lay: dict, e4m3_bits) -> dict:
+    """Oracle-prepared NVFP4 layer -> host arrays in the ABI layouts (e4m3_bits:
+    the E4M3 value -> byte map, passed in so this module stays arithmetic-free)."""
+    m, n = lay["qw"].shape
+    inv = lay.get("inv32")
+    return {
+        "m": m, "n": n, "rank": lay["l1"].shape[1], "t_x": lay["t_x"], "t_w": lay["t_w"],
+        "qw": pack_fp4_codes(np.ascontiguousarray(lay["qw"].T)),
+        "wscale": pack_fp4_scales(e4m3_bits(np.ascontiguousarray(lay["sbw"].T))),
+        "l1": np.ascontiguousarray(f32_to_bf16_bits(lay["l1"]).T),
+        "l2": np.ascontiguousarray(f32_to_bf16_bits(lay["l2"]).T),
+        "smooth_inv": np.ones(m, np.float32) if inv is None else np.asarray(inv, np.float32),
+    }

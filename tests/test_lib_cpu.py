@@ -32,7 +32,7 @@ def test_exports_every_symbol_declared_in_header():
     for nm in names:
         assert hasattr(L, nm), nm
     assert {s[0] for s in B.SIGNATURES} == names
-    assert L.svdq_abi_version() == 101
+    assert L.svdq_abi_version() == 102
 
 
 def test_status_strings():
@@ -456,3 +456,107 @@ def test_w8a8_prepare_validation_errors():
     with pytest.raises(B.SvdqError) as e:
         S.svdq_w8a8_prepare_weights(np.ones((128, 32), np.float32), None, 4, alpha=-0.1)
     assert e.value.status == B.SVDQ_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# the NVFP4 setting: host preparation and validation
+# ---------------------------------------------------------------------------
+
+def test_fp4_prepare_shares_steps_2_to_4_and_matches_oracle_quantizer(tiny):
+    _lib_or_skip()
+    inp, a, _ = tiny
+    p4 = S.svdq_prepare_weights(inp["w"], a, 16, want_residual=True)
+    pf = S.svdq_fp4_prepare_weights(inp["w"], a, 16, want_residual=True)
+    for k in ("lambda", "smooth_inv", "l1", "l2", "residual"):
+        assert np.array_equal(p4[k], pf[k]), k
+    ref = O.prepare_weights_fp4(inp["w"], a, 16)
+    assert pf["t_x"] == ref["t_x"]
+    assert pf["t_w"] == O.fp4_tensor_scale(np.max(np.abs(pf["residual"])))
+    codes, sb = O.quantize_fp4_blocks(np.ascontiguousarray(pf["residual"].T), pf["t_w"])
+    assert np.array_equal(LY.unpack_fp4_codes(pf["qw"]), codes)
+    assert np.array_equal(LY.unpack_fp4_scales(pf["wscale"]), O.e4m3_bits(sb))
+
+
+def test_fp4_quantizer_adversarial_columns():
+    _lib_or_skip()
+    rng = np.random.default_rng(23)
+    R = (rng.standard_normal((256, 40)) * np.exp(rng.uniform(-6, 6, (1, 40)))).astype(np.float32)
+    R[:, 0] = 0.0                                                   # all-zero column
+    R[:16, 1] = 1e-12                                               # a block whose scale underflows
+    R[:, 2] = np.tile([6.0, 0.25, 0.75, -1.25, 1.75, 2.5, 3.5, 5.0, -0.0, 4.0, 3.0, 1.5, -0.5, 2.0, 1.0, 0.1], 16)
+    R[:, 3] *= 1e6                                                  # a huge column
+    p = S.svdq_fp4_prepare_weights(R, None, 0, want_residual=True)  # rank 0, lambda = 1: R = W
+    assert np.array_equal(p["residual"], R) and p["t_x"] == 1.0
+    t_w = O.fp4_tensor_scale(np.max(np.abs(R)))
+    assert p["t_w"] == t_w
+    codes, sb = O.quantize_fp4_blocks(np.ascontiguousarray(R.T), t_w)
+    assert np.array_equal(LY.unpack_fp4_codes(p["qw"]), codes)
+    assert np.array_equal(LY.unpack_fp4_scales(p["wscale"]), O.e4m3_bits(sb))
+
+
+def _layer_fp4(**kw):
+    d = dict(m=128, n=64, rank=8, t_x=1.0, t_w=0.5, smooth_inv=None, qw=FAKE, wscale=FAKE, l1=FAKE, l2=FAKE,
+             bias=None)
+    d.update(kw)
+    return B.svdq_fp4_layer(d["m"], d["n"], d["rank"], d["t_x"], d["t_w"], d["smooth_inv"], d["qw"], d["wscale"],
+                            d["l1"], d["l2"], d["bias"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(m=100), B.SVDQ_ERR_UNSUPPORTED),
+    (dict(n=0), B.SVDQ_ERR_INVALID_ARG),
+    (dict(rank=300), B.SVDQ_ERR_UNSUPPORTED),
+    (dict(t_x=0.75), B.SVDQ_ERR_INVALID_ARG),       # not a power of two
+    (dict(t_w=0.0), B.SVDQ_ERR_INVALID_ARG),
+    (dict(t_w=2.0 ** 70), B.SVDQ_ERR_INVALID_ARG),
+    (dict(t_x=float("nan")), B.SVDQ_ERR_INVALID_ARG),
+    (dict(qw=None), B.SVDQ_ERR_INVALID_ARG),
+    (dict(qw=FAKE + 8), B.SVDQ_ERR_ALIGNMENT),
+    (dict(wscale=FAKE + 1), B.SVDQ_ERR_ALIGNMENT),
+    (dict(l2=None), B.SVDQ_ERR_INVALID_ARG),
+    (dict(l1=None), B.SVDQ_ERR_INVALID_ARG),
+])
+def test_fp4_linear_validation_errors(kw, code):
+    L = _lib_or_skip()
+    lay = _layer_fp4(**kw)
+    st = L.svdq_fp4_linear(FAKE, ctypes.byref(lay), 16, FAKE, B.SVDQ_OUT_BF16, FAKE, 1 << 30, None)
+    assert st == code, L.svdq_last_error()
+    assert L.svdq_last_error()
+
+
+def test_fp4_act_gemm_workspace_validation():
+    L = _lib_or_skip()
+    lay = _layer_fp4()
+    need = L.svdq_fp4_linear_workspace_size(16, 128, 64, 8)
+    assert need > 0 and need % 256 == 0
+    f = L.svdq_fp4_linear
+    assert f(FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE, need - 1, None) == B.SVDQ_ERR_WORKSPACE
+    assert f(FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE + 16, need, None) == B.SVDQ_ERR_ALIGNMENT
+    assert f(FAKE, ctypes.byref(lay), 0, None, 0, None, 0, None) == B.SVDQ_OK
+    a = L.svdq_fp4_quantize_act_lowrank_down
+    assert a(FAKE, 16, 96, 8, None, FAKE, 1.0, FAKE, FAKE, FAKE, None, 0, None) == B.SVDQ_ERR_UNSUPPORTED
+    assert a(FAKE, 16, 128, 8, None, FAKE, 3.0, FAKE, FAKE, FAKE, None, 0, None) == B.SVDQ_ERR_INVALID_ARG
+    assert a(FAKE, 16, 128, 8, None, None, 1.0, FAKE, FAKE, FAKE, None, 0, None) == B.SVDQ_ERR_INVALID_ARG
+    assert a(FAKE, 16, 128, 0, None, None, 1.0, FAKE + 8, FAKE, None, None, 0, None) == B.SVDQ_ERR_ALIGNMENT
+    assert a(FAKE, 0, 128, 8, None, None, 1.0, None, None, None, None, 0, None) == B.SVDQ_OK
+    assert L.svdq_fp4_act_workspace_size(64, 4096, 32) == L.svdq_act_workspace_size(64, 4096, 32) > 0
+    assert a(FAKE, 64, 4096, 32, None, FAKE, 1.0, FAKE, FAKE, FAKE, None, 0, None) == B.SVDQ_ERR_WORKSPACE
+    g = L.svdq_fp4_gemm_lowrank_up
+    gneed = L.svdq_fp4_gemm_workspace_size(16, 64, 128)
+    assert gneed == L.svdq_gemm_workspace_size(16, 64, 128) > 0
+    assert g(FAKE, FAKE, None, ctypes.byref(lay), 16, FAKE, 0, FAKE, gneed, None) == B.SVDQ_ERR_INVALID_ARG
+    assert g(FAKE + 4, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE, gneed, None) == B.SVDQ_ERR_ALIGNMENT
+    assert g(FAKE, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE, gneed - 1, None) == B.SVDQ_ERR_WORKSPACE
+    for (b, m, n, r) in [(1, 64, 8, 0), (37, 256, 200, 16), (4608, 3072, 9216, 32)]:
+        w = L.svdq_fp4_linear_workspace_size(b, m, n, r)
+        assert w >= m * b // 2 + m * b // 16 + b * r * 4 + L.svdq_fp4_gemm_workspace_size(b, n, m)
+
+
+def test_fp4_prepare_validation_errors():
+    _lib_or_skip()
+    with pytest.raises(B.SvdqError) as e:
+        S.svdq_fp4_prepare_weights(np.ones((128, 32), np.float32), None, 64)
+    assert e.value.status == B.SVDQ_ERR_INVALID_ARG
+    with pytest.raises(B.SvdqError) as e:
+        S.svdq_fp4_prepare_weights(np.ones((96, 32), np.float32), None, 4)
+    assert e.value.status == B.SVDQ_ERR_UNSUPPORTED

@@ -11,7 +11,10 @@ from ._binding import (  # noqa: F401
     svdq_prepare_weights, svdq_prepare_weights_refined, svdq_quantize_act_lowrank_down,
     svdq_quantize_residual, SVDQ_W8A8_MAX_M, DeviceLayer8, svdq_w8a8_act_workspace_size,
     svdq_w8a8_gemm_lowrank_up, svdq_w8a8_gemm_workspace_size, svdq_w8a8_linear,
-    svdq_w8a8_linear_workspace_size, svdq_w8a8_prepare_weights, svdq_w8a8_quantize_act_lowrank_down)
+    svdq_w8a8_linear_workspace_size, svdq_w8a8_prepare_weights, svdq_w8a8_quantize_act_lowrank_down,
+    DeviceLayerFp4, svdq_fp4_act_workspace_size, svdq_fp4_gemm_lowrank_up, svdq_fp4_gemm_workspace_size,
+    svdq_fp4_linear, svdq_fp4_linear_workspace_size, svdq_fp4_prepare_weights,
+    svdq_fp4_quantize_act_lowrank_down)
 
 __all__ = [
     "SVDQ_GROUP", "SVDQ_MAX_RANK", "SVDQ_OUT_BF16", "SVDQ_OUT_F32", "SvdqError", "DeviceLayer",
@@ -23,4 +26,7 @@ __all__ = [
     "svdq_quantize_residual", "SVDQ_W8A8_MAX_M", "DeviceLayer8", "svdq_w8a8_act_workspace_size",
     "svdq_w8a8_gemm_lowrank_up", "svdq_w8a8_gemm_workspace_size", "svdq_w8a8_linear",
     "svdq_w8a8_linear_workspace_size", "svdq_w8a8_prepare_weights", "svdq_w8a8_quantize_act_lowrank_down",
+    "DeviceLayerFp4", "svdq_fp4_act_workspace_size", "svdq_fp4_gemm_lowrank_up", "svdq_fp4_gemm_workspace_size",
+    "svdq_fp4_linear", "svdq_fp4_linear_workspace_size", "svdq_fp4_prepare_weights",
+    "svdq_fp4_quantize_act_lowrank_down",
 ]

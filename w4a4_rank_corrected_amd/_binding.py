@@ -48,6 +48,13 @@ class svdq_w8a8_layer(ctypes.Structure):
                 ("smooth_inv", _vp), ("qw", _vp), ("wscale", _vp), ("l1", _vp), ("l2", _vp), ("bias", _vp)]
 
 
+class svdq_fp4_layer(ctypes.Structure):
+    """Mirror of ``struct svdq_fp4_layer`` (all pointers are device addresses)."""
+    _fields_ = [("m", ctypes.c_int32), ("n", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("t_x", ctypes.c_float), ("t_w", ctypes.c_float), ("smooth_inv", _vp), ("qw", _vp),
+                ("wscale", _vp), ("l1", _vp), ("l2", _vp), ("bias", _vp)]
+
+
 # (name, restype, argtypes) for every exported symbol of include/svdq.h
 SIGNATURES = [
     ("svdq_prepare_weights", _c_int,
@@ -85,6 +92,17 @@ SIGNATURES = [
     ("svdq_w8a8_linear_workspace_size", _size, [_c_int, _c_int, _c_int, _c_int]),
     ("svdq_w8a8_linear", _c_int,
      [_vp, ctypes.POINTER(svdq_w8a8_layer), _c_int, _vp, _c_int, _vp, _size, _vp]),
+    ("svdq_fp4_prepare_weights", _c_int,
+     [_vp, _vp, _c_int, _c_int, _c_int, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    ("svdq_fp4_act_workspace_size", _size, [_c_int, _c_int, _c_int]),
+    ("svdq_fp4_quantize_act_lowrank_down", _c_int,
+     [_vp, _c_int, _c_int, _c_int, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _size, _vp]),
+    ("svdq_fp4_gemm_workspace_size", _size, [_c_int, _c_int, _c_int]),
+    ("svdq_fp4_gemm_lowrank_up", _c_int,
+     [_vp, _vp, _vp, ctypes.POINTER(svdq_fp4_layer), _c_int, _vp, _c_int, _vp, _size, _vp]),
+    ("svdq_fp4_linear_workspace_size", _size, [_c_int, _c_int, _c_int, _c_int]),
+    ("svdq_fp4_linear", _c_int,
+     [_vp, ctypes.POINTER(svdq_fp4_layer), _c_int, _vp, _c_int, _vp, _size, _vp]),
 ]
 
 _lib = None
@@ -483,4 +501,127 @@ def svdq_w8a8_linear(x, layer: DeviceLayer8, out_dtype=None, y=None, workspace=N
     wsb = workspace.numel() * workspace.element_size()
     _check(lib().svdq_w8a8_linear(_ptr(x), ctypes.byref(layer.struct), b, _ptr(y), code, _ptr(workspace),
                                   wsb, _stream(stream)))
+    return y
+
+
+# ---------------------------------------------------------------------------
+# the NVFP4 setting (FP4 E2M1 codes, E4M3 scales per 16 channels, tensor scales)
+# ---------------------------------------------------------------------------
+
+def svdq_fp4_prepare_weights(W: np.ndarray, act_amax: Optional[np.ndarray], rank: int, alpha: float = 0.5,
+                             want_residual: bool = False) -> dict:
+    """Host preparation of an NVFP4 layer.  Keys: qw uint8 [m/64][n][32] (E2M1
+    codes), wscale uint8 [m/64][n][4] (E4M3 block scales), l1, l2, lambda,
+    smooth_inv, residual (if requested), t_x, t_w, m, n, rank."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    m, n = W.shape
+    a = None if act_amax is None else np.ascontiguousarray(act_amax, dtype=np.float32)
+    G = max(m // SVDQ_GROUP, 0)
+    out = {
+        "qw": np.zeros((G, n, 32), np.uint8),
+        "wscale": np.zeros((G, n, 4), np.uint8),
+        "l1": np.zeros((rank, m), np.uint16),
+        "l2": np.zeros((n, rank), np.uint16),
+        "lambda": np.zeros(m, np.float32),
+        "smooth_inv": np.zeros(m, np.float32),
+        "m": m, "n": n, "rank": rank,
+    }
+    res = np.zeros((m, n), np.float32) if want_residual else None
+    tx = np.zeros(1, np.float32)
+    tw = np.zeros(1, np.float32)
+    _check(lib().svdq_fp4_prepare_weights(
+        _ptr(W), _ptr(a), m, n, rank, alpha, _ptr(out["qw"]), _ptr(out["wscale"]),
+        _ptr(out["l1"]) if rank else None, _ptr(out["l2"]) if rank else None,
+        _ptr(out["lambda"]), _ptr(out["smooth_inv"]), _ptr(res), _ptr(tx), _ptr(tw)))
+    if want_residual:
+        out["residual"] = res
+    out.update(t_x=float(tx[0]), t_w=float(tw[0]))
+    return out
+
+
+class DeviceLayerFp4:
+    """A prepared NVFP4 layer resident in device memory plus its ``svdq_fp4_layer`` struct."""
+
+    def __init__(self, host: dict, device="cuda", bias: Optional[np.ndarray] = None, smoothing: bool = True):
+        import torch
+        self.m, self.n, self.rank = int(host["m"]), int(host["n"]), int(host["rank"])
+        self.t_x, self.t_w = float(host["t_x"]), float(host["t_w"])
+        t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(device=device).view(dt)
+        self.qw = t(host["qw"], torch.uint8)
+        self.wscale = t(host["wscale"], torch.uint8)
+        self.smooth_inv = t(host["smooth_inv"], torch.float32) if smoothing else None
+        self.l1 = t(host["l1"].view(np.int16), torch.bfloat16) if self.rank else None
+        self.l2 = t(host["l2"].view(np.int16), torch.bfloat16) if self.rank else None
+        self.bias = None if bias is None else t(np.asarray(bias, np.uint16).view(np.int16), torch.bfloat16)
+        self.struct = svdq_fp4_layer(self.m, self.n, self.rank, self.t_x, self.t_w, _ptr(self.smooth_inv),
+                                     _ptr(self.qw), _ptr(self.wscale), _ptr(self.l1), _ptr(self.l2),
+                                     _ptr(self.bias))
+
+
+def svdq_fp4_act_workspace_size(b: int, m: int, rank: int) -> int:
+    return int(lib().svdq_fp4_act_workspace_size(b, m, rank))
+
+
+def svdq_fp4_quantize_act_lowrank_down(x, smooth_inv, l1, rank: int, t_x: float, qx=None, ascale=None, z=None,
+                                       workspace=None, stream=None):
+    """Returns (qx uint8 [m/64][b][32], ascale uint8 [m/64][b][4], z fp32 [b][rank] or None)."""
+    import torch
+    b, m = x.shape
+    dev = x.device
+    G = m // SVDQ_GROUP
+    if qx is None:
+        qx = torch.empty((G, b, 32), dtype=torch.uint8, device=dev)
+    if ascale is None:
+        ascale = torch.empty((G, b, 4), dtype=torch.uint8, device=dev)
+    if z is None and rank > 0:
+        z = torch.empty((b, rank), dtype=torch.float32, device=dev)
+    need = svdq_fp4_act_workspace_size(b, m, rank)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().svdq_fp4_quantize_act_lowrank_down(
+        _ptr(x), b, m, rank, _ptr(smooth_inv), _ptr(l1), float(t_x), _ptr(qx), _ptr(ascale), _ptr(z),
+        _ptr(workspace), wsb, _stream(stream)))
+    return qx, ascale, z
+
+
+def svdq_fp4_gemm_workspace_size(b: int, n: int, m: int) -> int:
+    return int(lib().svdq_fp4_gemm_workspace_size(b, n, m))
+
+
+def svdq_fp4_gemm_lowrank_up(qx, ascale, z, layer: DeviceLayerFp4, b: Optional[int] = None, out_dtype=None,
+                             y=None, workspace=None, stream=None):
+    import torch
+    if b is None:
+        b = qx.shape[1]
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    code = SVDQ_OUT_BF16 if out_dtype == torch.bfloat16 else SVDQ_OUT_F32
+    if y is None:
+        y = torch.empty((b, layer.n), dtype=out_dtype, device=qx.device)
+    if workspace is None:
+        need = svdq_fp4_gemm_workspace_size(b, layer.n, layer.m)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=qx.device)
+    wsb = workspace.numel() * workspace.element_size()
+    _check(lib().svdq_fp4_gemm_lowrank_up(_ptr(qx), _ptr(ascale), _ptr(z), ctypes.byref(layer.struct), b,
+                                          _ptr(y), code, _ptr(workspace), wsb, _stream(stream)))
+    return y
+
+
+def svdq_fp4_linear_workspace_size(b: int, m: int, n: int, rank: int) -> int:
+    return int(lib().svdq_fp4_linear_workspace_size(b, m, n, rank))
+
+
+def svdq_fp4_linear(x, layer: DeviceLayerFp4, out_dtype=None, y=None, workspace=None, stream=None):
+    import torch
+    b, m = x.shape
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    code = SVDQ_OUT_BF16 if out_dtype == torch.bfloat16 else SVDQ_OUT_F32
+    if y is None:
+        y = torch.empty((b, layer.n), dtype=out_dtype, device=x.device)
+    if workspace is None:
+        need = svdq_fp4_linear_workspace_size(b, m, layer.n, layer.rank)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    wsb = workspace.numel() * workspace.element_size()
+    _check(lib().svdq_fp4_linear(_ptr(x), ctypes.byref(layer.struct), b, _ptr(y), code, _ptr(workspace),
+                                 wsb, _stream(stream)))
     return y

@@ -79,13 +79,34 @@ __global__ __launch_bounds__(256) void calibrate_kernel(const uint16_t* __restri
 constexpr int kL1Pitch = kActL1Pitch;  // dynamic LDS: gps groups of act_lds_group_bytes(TB)
 
 // TB: 16-column blocks of Z (rank <= 16 * TB; 0 = no low-rank branch);
-// SMOOTH: multiply by 1/lambda (inv != nullptr); QUANT: emit codes and scales
-// (false: the down-projection alone, the unfused path's separate kernel).
-template <int TB, bool SMOOTH, bool QUANT>
+// SMOOTH: multiply by 1/lambda (inv != nullptr); Q: the codes and scales
+// emitted (kActQuantNone: the down-projection alone, the unfused path's and the
+// 8-bit setting's separate kernel; kActQuantInt4; kActQuantFp4).
+
+// FP8 E4M3 rounding of x >= 0 (nearest, ties to even, saturated at 448): the
+// quantum is 2^(e-3) in the binade [2^e, 2^(e+1)) for e >= -6, 2^-9 below.
+__device__ __forceinline__ float e4m3_round(float x) {
+  if (!(x < 448.0f)) return 448.0f;
+  const int e = max((int)((__float_as_uint(x) >> 23) & 0xFF) - 127, -6);
+  const float down = __uint_as_float((uint32_t)(127 - (e - 3)) << 23);  // 2^-(e-3), exact
+  const float up = __uint_as_float((uint32_t)(127 + (e - 3)) << 23);    // 2^(e-3)
+  return fminf(__builtin_rintf(x * down) * up, 448.0f);
+}
+
+// Bit pattern of a non-negative E4M3 value.
+__device__ __forceinline__ uint32_t e4m3_bits(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const int e = (int)((u >> 23) & 0xFF) - 127;
+  if (v == 0.0f) return 0u;
+  if (e >= -6) return ((uint32_t)(e + 7) << 3) | ((u >> 20) & 7u);
+  return (uint32_t)(v * 512.0f);  // subnormal: v = m 2^-9, m = 1..7 (exact)
+}
+
+template <int TB, bool SMOOTH, int Q>
 __global__ __launch_bounds__(256) void act_quant_down_kernel(
     const uint16_t* __restrict__ x, int b, int m, int G, const float* __restrict__ inv,
     const uint16_t* __restrict__ l1t, int rank, uint8_t* __restrict__ qx,
-    uint16_t* __restrict__ ascale, float* __restrict__ zout, int gps) {
+    uint16_t* __restrict__ ascale, float* __restrict__ zout, int gps, float tx) {
   constexpr int NB = TB > 0 ? TB : 1;
   constexpr int GB = act_lds_group_bytes(TB);
   constexpr int chunk = act_chunk(TB);
@@ -196,7 +217,56 @@ __global__ __launch_bounds__(256) void act_quant_down_kernel(
       v[2 * q] = bf16_lo(xt[q]);
       v[2 * q + 1] = bf16_hi(xt[q]);
     }
-    if constexpr (QUANT) {
+    if constexpr (Q == kActQuantFp4) {
+      // NVFP4: blocks of 16 channels; this lane holds half of block c >> 1
+      // (v[0..7]) and half of block 2 + (c >> 1) (v[8..15]), lane l ^ 16 the
+      // other halves.  sb = E4M3(fl32(amax / 6) / t), S = sb t (t a power of
+      // two), codes E2M1_RNE_sat(fl32(v / S)) with the quotient's sign.
+      float am[2] = {0.0f, 0.0f};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) am[e >> 3] = fmaxf(am[e >> 3], fabsf(v[e]));
+      uint32_t w[2];
+      uint32_t sbits[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float a = fmaxf(am[h], __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(am[h]), 0x401F)));
+        const float u = a / 6.0f;                    // IEEE division (correctly rounded)
+        const float sb = e4m3_round(u * (1.0f / tx));  // 1/t and the product are exact
+        sbits[h] = e4m3_bits(sb);
+        const float S = sb * tx;                      // exact
+        const float rc = S > 0.0f ? 1.0f / S : 0.0f;
+        const float S8 = 8.0f * S;
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float vv = v[8 * h + e];
+          const float pq = vv * rc;
+          const float rem = __builtin_fmaf(-pq, S, vv);
+          const float q1 = __builtin_fmaf(rem, rc, pq);
+          y[e] = S > 0.0f ? __builtin_copysignf(fabsf(vv) <= S8 ? q1 : 8.0f, vv) : 0.0f;
+        }
+        // two codes per byte, the even channel in the low nibble (RNE on the
+        // E2M1 grid, saturating: the hardware conversion at unit scale)
+        uint32_t word = 0u;
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[0], y[1], 1.0f, 0);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[2], y[3], 1.0f, 1);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[4], y[5], 1.0f, 2);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[6], y[7], 1.0f, 3);
+        w[h] = word;
+      }
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(qx + (size_t)g * b * 32, (uint32_t)b * 32u);
+      __builtin_amdgcn_raw_buffer_store_b32(w[0], rq, q_off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(w[1], rq, q_off + 16u, 0, 0);
+      // block scales: record [m/64][b][4] bytes, byte j = block j; the lanes
+      // with even c store blocks c/2 and 2 + c/2 (odd c: an offset past the
+      // end, dropped)
+      uint8_t* sc8 = reinterpret_cast<uint8_t*>(ascale);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(sc8 + (size_t)g * b * 4, (uint32_t)b * 4u);
+      const uint32_t s8_off = (c & 1) == 0 ? (uint32_t)row * 4u + (uint32_t)(c >> 1) : 0x7FFFFFF0u;
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbits[0], rs, s8_off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbits[1], rs, s8_off + 2u, 0, 0);
+    }
+    if constexpr (Q == kActQuantInt4) {
       float am = 0.0f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) am = fmaxf(am, fabsf(v[e]));
@@ -403,27 +473,29 @@ int launch_calibrate(const uint16_t* x, int b, int m, float* amax, int accumulat
 
 int launch_act_quant_down(const uint16_t* x, int b, int m, int rank, const float* smooth_inv,
                           const uint16_t* l1, uint8_t* qx, uint16_t* ascale, float* zpart,
-                          const ActPlan& plan, bool quantize, void* stream) {
+                          const ActPlan& plan, int qmode, float tx, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int G = m / 64;
   dim3 grid(plan.strips, plan.splits);
   const int tb = act_blocks(rank);
-#define SVDQ_ACT(TBV)                                                                              \
-  do {                                                                                             \
-    if (!quantize) {                                                                               \
-      if (smooth_inv)                                                                              \
-        hipLaunchKernelGGL((act_quant_down_kernel<TBV, true, false>), grid, dim3(256), 0, st, x, b, \
-                           m, G, smooth_inv, l1, rank, qx, ascale, zpart, plan.groups_per_split); \
-      else                                                                                         \
-        hipLaunchKernelGGL((act_quant_down_kernel<TBV, false, false>), grid, dim3(256), 0, st, x,  \
-                           b, m, G, smooth_inv, l1, rank, qx, ascale, zpart,                       \
-                           plan.groups_per_split);                                                 \
-    } else if (smooth_inv)                                                                         \
-      hipLaunchKernelGGL((act_quant_down_kernel<TBV, true, true>), grid, dim3(256), 0, st, x, b,   \
-                         m, G, smooth_inv, l1, rank, qx, ascale, zpart, plan.groups_per_split);   \
-    else                                                                                           \
-      hipLaunchKernelGGL((act_quant_down_kernel<TBV, false, true>), grid, dim3(256), 0, st, x, b,  \
-                         m, G, smooth_inv, l1, rank, qx, ascale, zpart, plan.groups_per_split);   \
+#define SVDQ_ACT_Q(TBV, SM, QV)                                                                    \
+  hipLaunchKernelGGL((act_quant_down_kernel<TBV, SM, QV>), grid, dim3(256), 0, st, x, b, m, G,     \
+                     smooth_inv, l1, rank, qx, ascale, zpart, plan.groups_per_split, tx)
+#define SVDQ_ACT_S(TBV, QV)           \
+  do {                                \
+    if (smooth_inv)                   \
+      SVDQ_ACT_Q(TBV, true, QV);      \
+    else                              \
+      SVDQ_ACT_Q(TBV, false, QV);     \
+  } while (0)
+#define SVDQ_ACT(TBV)                                  \
+  do {                                                 \
+    if (qmode == kActQuantInt4)                           \
+      SVDQ_ACT_S(TBV, kActQuantInt4);                     \
+    else if (qmode == kActQuantFp4)                       \
+      SVDQ_ACT_S(TBV, kActQuantFp4);                      \
+    else                                               \
+      SVDQ_ACT_S(TBV, kActQuantNone);                     \
   } while (0)
   if (tb == 0)
     SVDQ_ACT(0);
@@ -440,6 +512,8 @@ int launch_act_quant_down(const uint16_t* x, int b, int m, int rank, const float
   else
     SVDQ_ACT(16);
 #undef SVDQ_ACT
+#undef SVDQ_ACT_S
+#undef SVDQ_ACT_Q
   return (int)hipGetLastError();
 }
 

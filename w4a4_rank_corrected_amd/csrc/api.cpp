@@ -231,9 +231,67 @@ int run_act8(const uint16_t* x, int b, int m, int rank, const float* smooth_inv,
   if (st || rank == 0) return st;
   const ActPlan p = act_plan(b, m, rank);
   float* zp = p.splits > 1 ? zpart : z;
-  st = hip_status(launch_act_quant_down(x, b, m, rank, smooth_inv, l1, nullptr, nullptr, zp, p, false, stream),
+  st = hip_status(launch_act_quant_down(x, b, m, rank, smooth_inv, l1, nullptr, nullptr, zp, p, kActQuantNone, 1.0f, stream),
                   "lowrank_down");
   if (st || p.splits <= 1) return st;
+  return hip_status(launch_z_reduce(zp, p.splits, b, rank, z, stream), "z_reduce");
+}
+
+// A tensor scale of the NVFP4 setting: a power of two in [2^-60, 2^60] (so
+// t_x t_w stays a normal fp32 number and every scaling by it is exact).
+bool fp4_scale_ok(float t) {
+  if (!(t >= 0x1p-60f && t <= 0x1p60f)) return false;
+  int e = 0;
+  return std::frexp(t, &e) == 0.5f;
+}
+
+int check_layer_fp4(const svdq_fp4_layer* L) {
+  REQUIRE(L != nullptr, SVDQ_ERR_INVALID_ARG, "layer is NULL");
+  int st = check_group(L->m, SVDQ_GROUP);
+  if (st) return st;
+  REQUIRE(L->n >= 1, SVDQ_ERR_INVALID_ARG, "n must be >= 1 (got %d)", L->n);
+  REQUIRE(L->n <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "n must be <= %d (got %d)", SVDQ_MAX_DIM, L->n);
+  REQUIRE(L->rank >= 0 && L->rank <= SVDQ_MAX_RANK, SVDQ_ERR_UNSUPPORTED,
+          "rank must be in [0, %d] (got %d)", SVDQ_MAX_RANK, L->rank);
+  REQUIRE(fp4_scale_ok(L->t_x) && fp4_scale_ok(L->t_w), SVDQ_ERR_INVALID_ARG,
+          "t_x and t_w must be powers of two in [2^-60, 2^60] (got %g, %g)", (double)L->t_x, (double)L->t_w);
+  REQUIRE(L->qw && L->wscale, SVDQ_ERR_INVALID_ARG, "layer qw / wscale must not be NULL");
+  REQUIRE(aligned16(L->qw), SVDQ_ERR_ALIGNMENT, "layer qw must be 16-byte aligned");
+  REQUIRE(((uintptr_t)L->wscale & 1u) == 0, SVDQ_ERR_ALIGNMENT, "layer wscale must be 2-byte aligned");
+  if (L->rank > 0) {
+    REQUIRE(L->l2 != nullptr, SVDQ_ERR_INVALID_ARG, "layer l2 must not be NULL when rank > 0");
+    REQUIRE(((uintptr_t)L->l2 & 1u) == 0, SVDQ_ERR_ALIGNMENT, "layer l2 must be 2-byte aligned");
+  }
+  if (L->bias) REQUIRE(((uintptr_t)L->bias & 1u) == 0, SVDQ_ERR_ALIGNMENT, "bias must be 2-byte aligned");
+  return SVDQ_OK;
+}
+
+// Workspace of the NVFP4 layer: codes, block scales, Z, its split partials,
+// the GEMM's workspace.
+LinearWorkspace linear_fp4_ws_layout(int b, int m, int n, int rank) {
+  LinearWorkspace w;
+  const size_t G = (size_t)(m / SVDQ_GROUP);
+  ActPlan p = act_plan(b, m, rank);
+  w.qx_off = 0;
+  w.as_off = round_up(G * (size_t)b * 32, kAlign);
+  w.z_off = round_up(w.as_off + G * (size_t)b * 4, kAlign);
+  w.zpart_off = round_up(w.z_off + (size_t)b * (size_t)rank * 4, kAlign);
+  const size_t zpart = (rank > 0 && p.splits > 1) ? (size_t)p.splits * (size_t)b * (size_t)rank * 4 : 0;
+  w.gemm_off = round_up(w.zpart_off + zpart, kAlign);
+  w.total = round_up(w.gemm_off + gemm_ws_bytes(b, n, m), kAlign);
+  if (b == 0) w.total = 0;
+  return w;
+}
+
+// The NVFP4 act kernel, then the ordered reduction of split partial sums of Z.
+int run_act_fp4(const uint16_t* x, int b, int m, int rank, const float* smooth_inv, const uint16_t* l1, float t_x,
+                uint8_t* qx, uint8_t* ascale, float* z, float* zpart, void* stream) {
+  const ActPlan p = act_plan(b, m, rank);
+  float* zp = (rank > 0 && p.splits > 1) ? zpart : z;
+  int st = hip_status(launch_act_quant_down(x, b, m, rank, smooth_inv, l1, qx, reinterpret_cast<uint16_t*>(ascale),
+                                            zp, p, kActQuantFp4, t_x, stream),
+                      "act_quant_lowrank_down_fp4");
+  if (st || rank == 0 || p.splits <= 1) return st;
   return hip_status(launch_z_reduce(zp, p.splits, b, rank, z, stream), "z_reduce");
 }
 
@@ -253,7 +311,7 @@ int check_y(void* y, int y_dtype, int b) {
 
 extern "C" {
 
-int svdq_abi_version(void) { return 101; }
+int svdq_abi_version(void) { return 102; }
 
 const char* svdq_last_error(void) { return g_err; }
 
@@ -440,7 +498,7 @@ int svdq_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int rank, in
     REQUIRE(((uintptr_t)workspace & 15u) == 0, SVDQ_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
   }
   float* zpart = (rank > 0 && p.splits > 1) ? (float*)workspace : z;
-  st = hip_status(launch_act_quant_down(x, b, m, rank, smooth_inv, l1, qx, ascale, zpart, p, true, stream),
+  st = hip_status(launch_act_quant_down(x, b, m, rank, smooth_inv, l1, qx, ascale, zpart, p, kActQuantInt4, 1.0f, stream),
                   "act_quant_lowrank_down");
   if (st) return st;
   if (rank > 0 && p.splits > 1)
@@ -521,7 +579,7 @@ int svdq_linear(const uint16_t* x, const svdq_layer* layer, int b, void* y, int 
   ActPlan p = act_plan(b, m, rank);
   float* zpart = (rank > 0 && p.splits > 1) ? (float*)(ws + w.zpart_off) : z;
   st = hip_status(launch_act_quant_down(x, b, m, rank, layer->smooth_inv, layer->l1, qx, as, zpart, p,
-                                        true, stream),
+                                        kActQuantInt4, 1.0f, stream),
                   "act_quant_lowrank_down");
   if (st) return st;
   if (rank > 0 && p.splits > 1) {
@@ -570,8 +628,8 @@ int svdq_linear_unfused(const uint16_t* x, const svdq_layer* layer, int b, void*
   uint16_t* as = (uint16_t*)(ws + w.as_off);
   // 1. activation quantization alone
   const ActPlan p0 = act_plan(b, m, 0);
-  st = hip_status(launch_act_quant_down(x, b, m, 0, layer->smooth_inv, nullptr, qx, as, nullptr, p0, true,
-                                        stream),
+  st = hip_status(launch_act_quant_down(x, b, m, 0, layer->smooth_inv, nullptr, qx, as, nullptr, p0,
+                                        kActQuantInt4, 1.0f, stream),
                   "act_quant");
   if (st) return st;
   // 2. the W4A4 product (+ bias) into y
@@ -586,7 +644,7 @@ int svdq_linear_unfused(const uint16_t* x, const svdq_layer* layer, int b, void*
   const ActPlan p = act_plan(b, m, rank);
   float* zpart = p.splits > 1 ? (float*)(ws + w.zpart_off) : z;
   st = hip_status(launch_act_quant_down(x, b, m, rank, layer->smooth_inv, layer->l1, nullptr, nullptr, zpart,
-                                        p, false, stream),
+                                        p, kActQuantNone, 1.0f, stream),
                   "lowrank_down");
   if (st) return st;
   if (p.splits > 1) {
@@ -737,6 +795,157 @@ int svdq_w8a8_linear(const uint16_t* x, const svdq_w8a8_layer* layer, int b, voi
   if (st) return st;
   return hip_status(launch_gemm8_up(qx, as, z, *layer, b, y, y_dtype, ws + w.gemm_off, stream),
                     "gemm_w8a8_lowrank_up");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The NVFP4 setting ([Review] sec. 8: group size 16 with FP8 scales)
+// ---------------------------------------------------------------------------
+extern "C" {
+
+int svdq_fp4_prepare_weights(const float* W, const float* act_amax, int m, int n, int rank, float alpha,
+                             uint8_t* qw, uint8_t* wscale, uint16_t* l1, uint16_t* l2, float* lambda,
+                             float* smooth_inv, float* residual, float* t_x, float* t_w) {
+  clear_error();
+  int st = check_prepare(W, act_amax, m, n, rank, SVDQ_GROUP, qw, reinterpret_cast<const uint16_t*>(wscale), l1, l2,
+                         lambda, smooth_inv);
+  if (st) return st;
+  REQUIRE(t_x && t_w, SVDQ_ERR_INVALID_ARG, "t_x and t_w must not be NULL");
+  REQUIRE(alpha >= 0.0f && alpha <= 1.0f, SVDQ_ERR_INVALID_ARG, "alpha must be in [0, 1] (got %g)",
+          (double)alpha);
+  HostLayer L;
+  st = build_layer(W, act_amax, m, n, rank, (double)alpha, L);
+  if (st) {
+    set_error("truncated SVD did not converge (m=%d n=%d rank=%d)", m, n, rank);
+    return st;
+  }
+  double rmax = 0.0;
+  for (float v : L.r32) rmax = std::max(rmax, (double)std::fabs(v));
+  const double tw = fp4_tensor_scale(rmax);
+  double tx = 1.0;
+  if (act_amax) {
+    // the largest smoothed calibration magnitude, bf16(fl32(a_k * (1/lambda_k)))
+    double amax = 0.0;
+    for (int k = 0; k < m; ++k)
+      amax = std::max(amax, (double)bf16_to_f32(f64_to_bf16((double)(act_amax[k] * L.inv32[k]))));
+    tx = fp4_tensor_scale(amax);
+  }
+  REQUIRE(fp4_scale_ok((float)tx) && fp4_scale_ok((float)tw), SVDQ_ERR_UNSUPPORTED,
+          "tensor scales out of range (t_x %g, t_w %g)", tx, tw);
+  quantize_residual_fp4(L.r32.data(), m, n, tw, qw, wscale);
+  std::memcpy(lambda, L.lam32.data(), sizeof(float) * m);
+  std::memcpy(smooth_inv, L.inv32.data(), sizeof(float) * m);
+  for (int i = 0; i < m && rank > 0; ++i)
+    for (int t = 0; t < rank; ++t) l1[(size_t)t * m + i] = L.l1b[(size_t)i * rank + t];
+  for (int t = 0; t < rank; ++t)
+    for (int j = 0; j < n; ++j) l2[(size_t)j * rank + t] = L.l2b[(size_t)t * n + j];
+  if (residual) std::memcpy(residual, L.r32.data(), sizeof(float) * L.r32.size());
+  *t_x = (float)tx;
+  *t_w = (float)tw;
+  return SVDQ_OK;
+}
+
+size_t svdq_fp4_act_workspace_size(int b, int m, int rank) { return svdq_act_workspace_size(b, m, rank); }
+
+int svdq_fp4_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int rank, const float* smooth_inv,
+                                       const uint16_t* l1, float t_x, uint8_t* qx, uint8_t* ascale, float* z,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  int st = check_group(m, SVDQ_GROUP);
+  if (st) return st;
+  REQUIRE(b >= 0, SVDQ_ERR_INVALID_ARG, "b must be >= 0 (got %d)", b);
+  REQUIRE(b <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "b must be <= %d (got %d)", SVDQ_MAX_DIM, b);
+  REQUIRE(rank >= 0 && rank <= SVDQ_MAX_RANK, SVDQ_ERR_UNSUPPORTED, "rank must be in [0, %d] (got %d)",
+          SVDQ_MAX_RANK, rank);
+  REQUIRE(fp4_scale_ok(t_x), SVDQ_ERR_INVALID_ARG, "t_x must be a power of two in [2^-60, 2^60] (got %g)",
+          (double)t_x);
+  if (b == 0) return SVDQ_OK;
+  REQUIRE(x && qx && ascale, SVDQ_ERR_INVALID_ARG, "x, qx and ascale must not be NULL");
+  REQUIRE(aligned16(x) && aligned16(qx), SVDQ_ERR_ALIGNMENT, "x and qx must be 16-byte aligned");
+  if (smooth_inv) REQUIRE(aligned16(smooth_inv), SVDQ_ERR_ALIGNMENT, "smooth_inv must be 16-byte aligned");
+  if (rank > 0) {
+    REQUIRE(l1 && z, SVDQ_ERR_INVALID_ARG, "l1 and z must not be NULL when rank > 0");
+    REQUIRE(aligned16(l1), SVDQ_ERR_ALIGNMENT, "l1 must be 16-byte aligned");
+    REQUIRE(((uintptr_t)z & 3u) == 0, SVDQ_ERR_ALIGNMENT, "z must be 4-byte aligned");
+  }
+  const size_t need = svdq_act_workspace_size(b, m, rank);
+  if (need > 0) {
+    REQUIRE(workspace != nullptr && workspace_bytes >= need, SVDQ_ERR_WORKSPACE,
+            "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
+    REQUIRE(((uintptr_t)workspace & 15u) == 0, SVDQ_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  }
+  return run_act_fp4(x, b, m, rank, smooth_inv, l1, t_x, qx, ascale, z, (float*)workspace, stream);
+}
+
+size_t svdq_fp4_gemm_workspace_size(int b, int n, int m) { return svdq_gemm_workspace_size(b, n, m); }
+
+int svdq_fp4_gemm_lowrank_up(const uint8_t* qx, const uint8_t* ascale, const float* z,
+                             const svdq_fp4_layer* layer, int b, void* y, int y_dtype, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  clear_error();
+  int st = check_layer_fp4(layer);
+  if (st) return st;
+  REQUIRE(b >= 0, SVDQ_ERR_INVALID_ARG, "b must be >= 0 (got %d)", b);
+  REQUIRE(b <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "b must be <= %d (got %d)", SVDQ_MAX_DIM, b);
+  st = check_y(y, y_dtype, b);
+  if (st) return st;
+  if (b == 0) return SVDQ_OK;
+  REQUIRE(qx && ascale, SVDQ_ERR_INVALID_ARG, "qx and ascale must not be NULL");
+  REQUIRE(aligned16(qx), SVDQ_ERR_ALIGNMENT, "qx must be 16-byte aligned");
+  REQUIRE(((uintptr_t)ascale & 1u) == 0, SVDQ_ERR_ALIGNMENT, "ascale must be 2-byte aligned");
+  if (layer->rank > 0) {
+    REQUIRE(z != nullptr, SVDQ_ERR_INVALID_ARG, "z must not be NULL when rank > 0");
+    REQUIRE(((uintptr_t)z & 3u) == 0, SVDQ_ERR_ALIGNMENT, "z must be 4-byte aligned");
+  }
+  const size_t need = gemm_ws_bytes(b, layer->n, layer->m);
+  if (need > 0) {
+    REQUIRE(workspace != nullptr && workspace_bytes >= need, SVDQ_ERR_WORKSPACE,
+            "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
+    REQUIRE(((uintptr_t)workspace & 15u) == 0, SVDQ_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  }
+  return hip_status(launch_gemm_fp4_up(qx, ascale, z, *layer, b, y, y_dtype, workspace, stream),
+                    "gemm_fp4_lowrank_up");
+}
+
+size_t svdq_fp4_linear_workspace_size(int b, int m, int n, int rank) {
+  if (m < SVDQ_GROUP || m % SVDQ_GROUP || b <= 0 || n <= 0 || rank < 0 || rank > SVDQ_MAX_RANK) return 0;
+  return linear_fp4_ws_layout(b, m, n, rank).total;
+}
+
+int svdq_fp4_linear(const uint16_t* x, const svdq_fp4_layer* layer, int b, void* y, int y_dtype,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  int st = check_layer_fp4(layer);
+  if (st) return st;
+  REQUIRE(b >= 0, SVDQ_ERR_INVALID_ARG, "b must be >= 0 (got %d)", b);
+  REQUIRE(b <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "b must be <= %d (got %d)", SVDQ_MAX_DIM, b);
+  st = check_y(y, y_dtype, b);
+  if (st) return st;
+  if (b == 0) return SVDQ_OK;
+  const int m = layer->m, rank = layer->rank;
+  REQUIRE(x != nullptr, SVDQ_ERR_INVALID_ARG, "x must not be NULL");
+  REQUIRE(aligned16(x), SVDQ_ERR_ALIGNMENT, "x must be 16-byte aligned");
+  if (layer->smooth_inv)
+    REQUIRE(aligned16(layer->smooth_inv), SVDQ_ERR_ALIGNMENT, "smooth_inv must be 16-byte aligned");
+  if (rank > 0) {
+    REQUIRE(layer->l1 != nullptr, SVDQ_ERR_INVALID_ARG, "layer l1 must not be NULL when rank > 0");
+    REQUIRE(aligned16(layer->l1), SVDQ_ERR_ALIGNMENT, "layer l1 must be 16-byte aligned");
+  }
+  const LinearWorkspace w = linear_fp4_ws_layout(b, m, layer->n, rank);
+  REQUIRE(workspace != nullptr && workspace_bytes >= w.total, SVDQ_ERR_WORKSPACE,
+          "workspace of %zu bytes needed (got %zu)", w.total, workspace ? workspace_bytes : (size_t)0);
+  REQUIRE(((uintptr_t)workspace & (kAlign - 1)) == 0, SVDQ_ERR_ALIGNMENT,
+          "workspace must be %zu-byte aligned", kAlign);
+  char* ws = (char*)workspace;
+  uint8_t* qx = (uint8_t*)(ws + w.qx_off);
+  uint8_t* as = (uint8_t*)(ws + w.as_off);
+  float* z = rank > 0 ? (float*)(ws + w.z_off) : nullptr;
+  st = run_act_fp4(x, b, m, rank, layer->smooth_inv, layer->l1, layer->t_x, qx, as, z, (float*)(ws + w.zpart_off),
+                   stream);
+  if (st) return st;
+  return hip_status(launch_gemm_fp4_up(qx, as, z, *layer, b, y, y_dtype, ws + w.gemm_off, stream),
+                    "gemm_fp4_lowrank_up");
 }
 
 }  // extern "C"

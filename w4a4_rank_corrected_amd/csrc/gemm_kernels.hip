@@ -223,22 +223,48 @@ struct StreamK {
   unsigned long long epoch;       // this launch's epoch
 };
 
-// The kernel body, for INT4 group-scaled operands (W8 = false) or for the
-// 8-bit setting (W8 = true: per-token activation and per-output-channel weight
-// INT8 codes, one byte each, in 64-byte group-major records [m/64][rows][64],
-// with one fp16 scale per row and per column).  With 8-bit codes the MFMAs
-// chain over all groups into i32 accumulators (|sum| <= 127^2 m < 2^31 for the
-// m the library accepts) and the scales are applied once, in the epilogue, so
-// no per-group VALU work remains; stream-K partials are then i32 sums.
-template <class C, bool OUT_BF16, bool W8>
+// Operand formats of the kernel body.
+enum { kFmtInt4 = 0, kFmtInt8 = 1, kFmtFp4 = 2 };
+
+// E4M3 block-scale byte -> (2^e, M) with value = M 2^e, M in [1, 2) (M = 0 for
+// a zero scale): the FP4 -> f16 conversion applies only the exponent of its
+// scale operand, the mantissa M is multiplied in afterwards.
+__device__ __forceinline__ void e4m3_split(uint32_t bits, float& p2, _Float16& M) {
+  const uint32_t ex = (bits >> 3) & 15u, mant = bits & 7u;
+  const float v = ex ? __uint_as_float(((ex + 120u) << 23) | (mant << 20)) : (float)mant * 0.001953125f;
+  p2 = __uint_as_float(__float_as_uint(v) & 0x7F800000u);
+  M = v > 0.0f ? (_Float16)__uint_as_float((__float_as_uint(v) & 0x007FFFFFu) | 0x3F800000u) : (_Float16)0.0f;
+}
+
+// The kernel body for three operand formats (FMT):
+//  * kFmtInt4: INT4 codes in 32-byte group records with per-group fp16 scales
+//    (the exact per-group sums and fp32 scale epilogue described above);
+//  * kFmtInt8: the 8-bit setting, per-token activation and per-output-channel
+//    weight INT8 codes, one byte each, in 64-byte group-major records
+//    [m/64][rows][64], with one fp16 scale per row and per column.  The MFMAs
+//    chain over all groups into i32 accumulators (|sum| <= 127^2 m < 2^31 for
+//    the m the library accepts) and the scales are applied once, in the
+//    epilogue, so no per-group VALU work remains; stream-K partials are then
+//    i32 sums;
+//  * kFmtFp4: the NVFP4 setting, FP4 E2M1 codes in the INT4 record layout and
+//    one FP8 E4M3 scale per 16 channels (records [m/64][rows][4] bytes).  A
+//    code times its block scale is exact in f16 (at most 6 significant bits,
+//    magnitudes 2^-10 .. 2688), so staging dequantizes the codes once per
+//    workgroup into f16 LDS rows and the f16 MFMAs accumulate sum_k x^ w^ in
+//    fp32; the two power-of-two tensor scales (txw = t_x t_w) are applied
+//    once in the epilogue, exactly.
+template <class C, bool OUT_BF16, int FMT>
 __device__ __forceinline__ void gemm_up_body(
     const uint8_t* __restrict__ qx, const uint16_t* __restrict__ ascale,
     const float* __restrict__ z, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, int b, int n, int G, int rank, int tiles_m, int tiles_n,
-    void* __restrict__ yout, StreamK sk) {
+    void* __restrict__ yout, StreamK sk, float txw) {
+  constexpr bool W8 = FMT == kFmtInt8, F4 = FMT == kFmtFp4;
+  constexpr bool POST = W8 || F4;  // scales and the low-rank branch after the main loop
   constexpr int TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN, NT = C::NT;
-  constexpr int BI = C::BI, BJ = C::BJ, ROWB = C::ROWB;
+  constexpr int BI = C::BI, BJ = C::BJ;
+  constexpr int ROWB = F4 ? 128 : C::ROWB;  // LDS bytes per row and group (f16 rows for FP4)
   constexpr int KG = C::KG;
   // per buffer: KG groups of TM (TN) rows
   __shared__ __align__(16) uint8_t As[2][KG * TM * ROWB];
@@ -246,7 +272,7 @@ __device__ __forceinline__ void gemm_up_body(
   // per buffer and group: [sx/256 (TM) | -1.5*2^23 sx/256 (TM) | sw (TN) |
   // unused (NT - TM - TN)] (no per-group scales with 8-bit codes)
   constexpr int SSC = TM + NT;
-  __shared__ __align__(16) float Ssc[2][W8 ? 4 : KG * SSC];
+  __shared__ __align__(16) float Ssc[2][POST ? 4 : KG * SSC];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -256,6 +282,11 @@ __device__ __forceinline__ void gemm_up_body(
   // this lane's 16-byte chunk of an MFMA operand row in LDS (rows of a block
   // start at multiples of 16, so the row's swizzle is that of r)
   const int cs = 16 * (c ^ chunk_swz(r));
+  // FP4: 128-byte f16 rows of eight 16-byte chunks, chunk j at position
+  // j ^ f4_swz(row) (free of bank conflicts for the operand reads with 8 or 16
+  // lanes per cycle); this lane reads chunks c and 4 + c of its row
+  const int f4r = (r & 7) ^ ((r >> 3) & 1);
+  const int cs0 = 16 * (c ^ f4r), cs1 = 16 * ((4 + c) ^ f4r);
   constexpr int REC = W8 ? 64 : 32;  // record bytes of one row in one group
   constexpr int AB = W8 ? 2 * C::A_BYTES : C::A_BYTES, BB = W8 ? 2 * C::B_BYTES : C::B_BYTES;
   const int a_row = tid * AB / REC, a_w0 = (tid * AB % REC) / 4;
@@ -331,7 +362,8 @@ __device__ __forceinline__ void gemm_up_body(
   struct Stage {
     Piece<AB> a[KG];
     Piece<BB> w[KG];
-    uint32_t s[KG];
+    uint32_t s[KG];   // INT4: this thread's group scale; FP4: the activation row's two block scales
+    uint32_t s2[KG];  // FP4: the weight column's two block scales
   };
   auto main_branch = [&](int i0, int j0, int g0, int g1) {
     const uint32_t a_voff = (uint32_t)(i0 + a_row) * REC + 4u * a_w0;
@@ -356,7 +388,16 @@ __device__ __forceinline__ void gemm_up_body(
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(qw + (size_t)g * b_bytes, live ? b_bytes : 0u);
         st.a[q] = buffer_piece<AB>(ra, a_voff);
         st.w[q] = buffer_piece<BB>(rb, b_voff);
-        if constexpr (!W8) {
+        if constexpr (F4) {
+          // the two block scales of this thread's 32 codes: bytes 2h, 2h+1 of
+          // the row's 4-byte scale record (h = the record half it stages)
+          const uint8_t* as8 = reinterpret_cast<const uint8_t*>(ascale);
+          const uint8_t* ws8 = reinterpret_cast<const uint8_t*>(wscale);
+          const __amdgpu_buffer_rsrc_t rsa = make_rsrc(as8 + (size_t)g * b * 4, live ? (uint32_t)b * 4u : 0u);
+          const __amdgpu_buffer_rsrc_t rsw = make_rsrc(ws8 + (size_t)g * n * 4, live ? (uint32_t)n * 4u : 0u);
+          st.s[q] = __builtin_amdgcn_raw_buffer_load_b16(rsa, (uint32_t)(i0 + a_row) * 4u + 2u * (a_w0 >> 2), 0, 0);
+          st.s2[q] = __builtin_amdgcn_raw_buffer_load_b16(rsw, (uint32_t)(j0 + b_col) * 4u + 2u * (b_w0 >> 2), 0, 0);
+        } else if constexpr (!W8) {
           // wave-uniform choice (waves 0 .. TM/64-1 stage activation scales), so
           // the descriptor stays in scalar registers
           const __amdgpu_buffer_rsrc_t rs =
@@ -371,12 +412,38 @@ __device__ __forceinline__ void gemm_up_body(
     // i0+t's activation scale (two words), thread TM+u column j0+u's weight
     // scale (the same word twice; threads past TM+TN write zeros to the unused
     // tail), so the staging is straight-line code.
+    // FP4: 16 code bytes (channels 32h .. 32h+31 of the record, h = w0 / 4)
+    // -> four 16-byte f16 chunks 4h .. 4h+3 of the LDS row; words 0-1 use
+    // block 2h's scale (byte 0 of sc), words 2-3 block 2h+1's (byte 1)
+    auto dequant_fp4 = [&](uint8_t* row, int ridx, int w0, const Piece<16>& pc, uint32_t sc) {
+      typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+      const int swz = (ridx & 7) ^ ((ridx >> 3) & 1);
+      float p2[2];
+      _Float16 M[2];
+      e4m3_split(sc & 0xFFu, p2[0], M[0]);
+      e4m3_split((sc >> 8) & 0xFFu, p2[1], M[1]);
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        const int k = wd >> 1;
+        const f16x2 mm = {M[k], M[k]};
+        const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(pc.w[wd], p2[k], 0) * mm;
+        const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(pc.w[wd], p2[k], 1) * mm;
+        const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(pc.w[wd], p2[k], 2) * mm;
+        const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(pc.w[wd], p2[k], 3) * mm;
+        *reinterpret_cast<u32x4*>(row + 16 * (((w0 & 4) + wd) ^ swz)) =
+            u32x4{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
+                  __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
+      }
+    };
     auto store_stage = [&](int buf, const Stage& st) {
 #pragma unroll
       for (int q = 0; q < KG; ++q) {
         uint8_t* as = &As[buf][(q * TM + a_row) * ROWB];
         uint8_t* bs = &Bs[buf][(q * TN + b_col) * ROWB];
-        if constexpr (W8) {
+        if constexpr (F4) {
+          dequant_fp4(as, a_row, a_w0, st.a[q], st.s[q]);
+          dequant_fp4(bs, b_col, b_w0, st.w[q], st.s2[q]);
+        } else if constexpr (W8) {
           copy_piece(as, chunk_swz(a_row), a_w0, st.a[q]);
           copy_piece(bs, chunk_swz(b_col), b_w0, st.w[q]);
         } else {
@@ -398,7 +465,25 @@ __device__ __forceinline__ void gemm_up_body(
     auto compute_group = [&](int buf, int q) {
       const uint8_t* as = &As[buf][q * TM * ROWB];
       const uint8_t* bs = &Bs[buf][q * TN * ROWB];
-      if constexpr (W8) {
+      if constexpr (F4) {
+        typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {  // channels 0-31, then 32-63 of the group
+          const int co = kh ? cs1 : cs0;
+          u32x4 Pb[BJ];
+#pragma unroll
+          for (int bj = 0; bj < BJ; ++bj)
+            Pb[bj] = *reinterpret_cast<const u32x4*>(bs + (WN * wn + 16 * bj + r) * ROWB + co);
+#pragma unroll
+          for (int bi = 0; bi < BI; ++bi) {
+            const u32x4 Qa = *reinterpret_cast<const u32x4*>(as + (WM * wm + 16 * bi + r) * ROWB + co);
+#pragma unroll
+            for (int bj = 0; bj < BJ; ++bj)
+              acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                  __builtin_bit_cast(f16x8, Pb[bj]), __builtin_bit_cast(f16x8, Qa), acc[bi][bj], 0, 0, 0);
+          }
+        }
+      } else if constexpr (W8) {
         u32x4 Pb[BJ];
 #pragma unroll
         for (int bj = 0; bj < BJ; ++bj)
@@ -544,6 +629,13 @@ __device__ __forceinline__ void gemm_up_body(
   // two fp16 scales is exact in fp32, so each element takes the rounding of the
   // conversion and of one multiplication
   auto scale_sums = [&](int i0, int j0) {
+    if constexpr (F4) {  // a power of two: exact
+#pragma unroll
+      for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < BJ; ++bj) acc[bi][bj] *= txw;
+      return;
+    }
 #pragma unroll
     for (int bj = 0; bj < BJ; ++bj) {
       const int j = j0 + WN * wn + 16 * bj + 4 * c;
@@ -565,9 +657,9 @@ __device__ __forceinline__ void gemm_up_body(
     int ti, tj;
     band_tile(dp_tile((int)blockIdx.x - sk.P, T - sk.T, sk.T), tiles_m, tiles_n, ti, tj);
     zero_acc();
-    if constexpr (!W8) lowrank(ti * TM, tj * TN);
+    if constexpr (!POST) lowrank(ti * TM, tj * TN);
     main_branch(ti * TM, tj * TN, 0, G);
-    if constexpr (W8) {
+    if constexpr (POST) {
       scale_sums(ti * TM, tj * TN);
       lowrank(ti * TM, tj * TN);
     }
@@ -587,7 +679,7 @@ __device__ __forceinline__ void gemm_up_body(
     band_tile((int)t, tiles_m, tiles_n, ti, tj);
     const int i0 = ti * TM, j0 = tj * TN;
     zero_acc();
-    if (!W8 && g1 == G) lowrank(i0, j0);  // the tile's last groups carry the low-rank branch
+    if (!POST && g1 == G) lowrank(i0, j0);  // the tile's last groups carry the low-rank branch
     main_branch(i0, j0, g0, g1);
     if (g1 < G) {
       // Publish this partial (this workgroup's first work item) for the
@@ -639,7 +731,7 @@ __device__ __forceinline__ void gemm_up_body(
             }
         }
       }
-      if constexpr (W8) {
+      if constexpr (POST) {
         scale_sums(i0, j0);
         lowrank(i0, j0);
       }
@@ -655,8 +747,9 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
     const float* __restrict__ z, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, int b, int n, int G, int rank, int tiles_m, int tiles_n,
-    void* __restrict__ yout, StreamK sk) {
-  gemm_up_body<C, OUT_BF16, false>(qx, ascale, z, qw, wscale, l2t, bias, b, n, G, rank, tiles_m, tiles_n, yout, sk);
+    void* __restrict__ yout, StreamK sk, float txw) {
+  gemm_up_body<C, OUT_BF16, kFmtInt4>(qx, ascale, z, qw, wscale, l2t, bias, b, n, G, rank, tiles_m, tiles_n, yout,
+                                      sk, txw);
 }
 
 template <class C, bool OUT_BF16>
@@ -665,8 +758,20 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
     const float* __restrict__ z, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, int b, int n, int G, int rank, int tiles_m, int tiles_n,
-    void* __restrict__ yout, StreamK sk) {
-  gemm_up_body<C, OUT_BF16, true>(qx, ascale, z, qw, wscale, l2t, bias, b, n, G, rank, tiles_m, tiles_n, yout, sk);
+    void* __restrict__ yout, StreamK sk, float txw) {
+  gemm_up_body<C, OUT_BF16, kFmtInt8>(qx, ascale, z, qw, wscale, l2t, bias, b, n, G, rank, tiles_m, tiles_n, yout,
+                                      sk, txw);
+}
+
+template <class C, bool OUT_BF16>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void gemm_fp4_up_kernel(
+    const uint8_t* __restrict__ qx, const uint16_t* __restrict__ ascale,
+    const float* __restrict__ z, const uint8_t* __restrict__ qw,
+    const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ l2t,
+    const uint16_t* __restrict__ bias, int b, int n, int G, int rank, int tiles_m, int tiles_n,
+    void* __restrict__ yout, StreamK sk, float txw) {
+  gemm_up_body<C, OUT_BF16, kFmtFp4>(qx, ascale, z, qw, wscale, l2t, bias, b, n, G, rank, tiles_m, tiles_n, yout,
+                                     sk, txw);
 }
 
 int g_num_cus = 0;
@@ -679,9 +784,9 @@ struct Operands {
   int n, rank;
 };
 
-template <bool OUT_BF16, bool W8>
+template <bool OUT_BF16, int FMT>
 int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, const Operands& L, int b,
-                 void* y, const GemmPlan& plan, void* ws, hipStream_t st) {
+                 void* y, const GemmPlan& plan, void* ws, hipStream_t st, float txw = 1.0f) {
   StreamK sk{0, 0, 0, nullptr, nullptr, 0};
   if (plan.streamk) {
     sk.P = plan.sk_grid;
@@ -691,14 +796,18 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
     sk.flags = reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(ws) + plan.partial_bytes);
     sk.epoch = next_launch_epoch();
   }
-  if constexpr (W8)
+  if constexpr (FMT == kFmtInt8)
     hipLaunchKernelGGL((gemm_w8a8_up_kernel<Cfg8, OUT_BF16>), dim3((unsigned)plan.grid), dim3(Cfg8::NT), 0, st,
                        qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
-                       plan.tiles_n, y, sk);
+                       plan.tiles_n, y, sk, txw);
+  else if constexpr (FMT == kFmtFp4)
+    hipLaunchKernelGGL((gemm_fp4_up_kernel<Cfg, OUT_BF16>), dim3((unsigned)plan.grid), dim3(Cfg::NT), 0, st,
+                       qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
+                       plan.tiles_n, y, sk, txw);
   else
     hipLaunchKernelGGL((gemm_w4a4_up_kernel<Cfg, OUT_BF16>), dim3((unsigned)plan.grid), dim3(Cfg::NT), 0, st,
                        qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
-                       plan.tiles_n, y, sk);
+                       plan.tiles_n, y, sk, txw);
   return (int)hipGetLastError();
 }
 
@@ -759,8 +868,8 @@ int launch_gemm_up(const uint8_t* qx, const uint16_t* ascale, const float* z, co
   const GemmPlan plan = gemm_plan(b, L.n, L.m, device_cus());
   const Operands o{L.qw, L.wscale, L.l2, L.bias, L.n, L.rank};
   hipStream_t st = (hipStream_t)stream;
-  if (y_dtype == SVDQ_OUT_BF16) return launch_typed<true, false>(qx, ascale, z, o, b, y, plan, ws, st);
-  return launch_typed<false, false>(qx, ascale, z, o, b, y, plan, ws, st);
+  if (y_dtype == SVDQ_OUT_BF16) return launch_typed<true, kFmtInt4>(qx, ascale, z, o, b, y, plan, ws, st);
+  return launch_typed<false, kFmtInt4>(qx, ascale, z, o, b, y, plan, ws, st);
 }
 
 int launch_gemm8_up(const int8_t* qx, const uint16_t* ascale, const float* z, const svdq_w8a8_layer& L,
@@ -769,8 +878,19 @@ int launch_gemm8_up(const int8_t* qx, const uint16_t* ascale, const float* z, co
   const Operands o{reinterpret_cast<const uint8_t*>(L.qw), L.wscale, L.l2, L.bias, L.n, L.rank};
   const uint8_t* a = reinterpret_cast<const uint8_t*>(qx);
   hipStream_t st = (hipStream_t)stream;
-  if (y_dtype == SVDQ_OUT_BF16) return launch_typed<true, true>(a, ascale, z, o, b, y, plan, ws, st);
-  return launch_typed<false, true>(a, ascale, z, o, b, y, plan, ws, st);
+  if (y_dtype == SVDQ_OUT_BF16) return launch_typed<true, kFmtInt8>(a, ascale, z, o, b, y, plan, ws, st);
+  return launch_typed<false, kFmtInt8>(a, ascale, z, o, b, y, plan, ws, st);
+}
+
+int launch_gemm_fp4_up(const uint8_t* qx, const uint8_t* ascale, const float* z, const svdq_fp4_layer& L, int b,
+                       void* y, int y_dtype, void* ws, void* stream) {
+  const GemmPlan plan = gemm_plan(b, L.n, L.m, device_cus());
+  const Operands o{L.qw, reinterpret_cast<const uint16_t*>(L.wscale), L.l2, L.bias, L.n, L.rank};
+  const uint16_t* as = reinterpret_cast<const uint16_t*>(ascale);
+  const float txw = L.t_x * L.t_w;  // powers of two: exact
+  hipStream_t st = (hipStream_t)stream;
+  if (y_dtype == SVDQ_OUT_BF16) return launch_typed<true, kFmtFp4>(qx, as, z, o, b, y, plan, ws, st, txw);
+  return launch_typed<false, kFmtFp4>(qx, as, z, o, b, y, plan, ws, st, txw);
 }
 
 // The low-rank up-projection alone, y = bf16(z) L2 (the unfused path's
@@ -779,8 +899,8 @@ int launch_lowrank_up(const float* z, const svdq_layer& L, int b, void* y, int y
   const GemmPlan plan = gemm_plan(b, L.n, 0, device_cus());  // G = 0: one tile per workgroup
   const Operands o{nullptr, nullptr, L.l2, nullptr, L.n, L.rank};
   hipStream_t st = (hipStream_t)stream;
-  if (y_dtype == SVDQ_OUT_BF16) return launch_typed<true, false>(nullptr, nullptr, z, o, b, y, plan, nullptr, st);
-  return launch_typed<false, false>(nullptr, nullptr, z, o, b, y, plan, nullptr, st);
+  if (y_dtype == SVDQ_OUT_BF16) return launch_typed<true, kFmtInt4>(nullptr, nullptr, z, o, b, y, plan, nullptr, st);
+  return launch_typed<false, kFmtInt4>(nullptr, nullptr, z, o, b, y, plan, nullptr, st);
 }
 
 }  // namespace svdq

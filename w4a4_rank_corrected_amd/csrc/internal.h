@@ -32,6 +32,12 @@ void quantize_residual(const float* R, int m, int n, uint8_t* qw, uint16_t* wsca
 // INT8 quantization of each column of R (fp32 [m][n]) into 64-byte group-major
 // records [m/64][n][64] and one fp16 scale per column.
 void quantize_residual8(const float* R, int m, int n, int8_t* qw, uint16_t* wscale);
+// NVFP4 quantization of each column of R (fp32 [m][n]) in blocks of 16 input
+// channels with power-of-two tensor scale t: codes [m/64][n][32], E4M3 block
+// scales [m/64][n][4].
+void quantize_residual_fp4(const float* R, int m, int n, double t, uint8_t* qw, uint8_t* wscale);
+// 2^ceil(log2(amax / (6 * 448))) (1 when amax is 0): the NVFP4 tensor scale.
+double fp4_tensor_scale(double amax);
 
 // One candidate protected layer on the host ([Review] Algorithm 1 steps 2-5).
 struct HostLayer {
@@ -94,9 +100,14 @@ ActPlan act_plan(int b, int m, int rank);
 
 // ---- kernel launchers (HIP; return a hipError_t value, 0 = success) ------------
 int launch_calibrate(const uint16_t* x, int b, int m, float* amax, int accumulate, void* stream);
+// qmode: kActQuantNone (Z only), kActQuantInt4, kActQuantFp4 (tx: the power-of-
+// two tensor scale of the FP4 block scales; unused otherwise).  For FP4, qx
+// holds E2M1 codes in the INT4 record layout and ascale is read as bytes
+// [m/64][b][4] (E4M3 block scales).
+enum { kActQuantNone = 0, kActQuantInt4 = 1, kActQuantFp4 = 2 };
 int launch_act_quant_down(const uint16_t* x, int b, int m, int rank, const float* smooth_inv,
                           const uint16_t* l1, uint8_t* qx, uint16_t* ascale, float* zpart,
-                          const ActPlan& plan, bool quantize, void* stream);
+                          const ActPlan& plan, int qmode, float tx, void* stream);
 int launch_z_reduce(const float* zpart, int splits, int b, int rank, float* z, void* stream);
 // Per-token INT8 codes and scales of the smoothed activations (one wave per row).
 int launch_act8_quant(const uint16_t* x, int b, int m, const float* smooth_inv, int8_t* qx, uint16_t* ascale,
@@ -129,6 +140,8 @@ int launch_gemm_up(const uint8_t* qx, const uint16_t* ascale, const float* z, co
                    int b, void* y, int y_dtype, void* ws, void* stream);
 int launch_gemm8_up(const int8_t* qx, const uint16_t* ascale, const float* z, const svdq_w8a8_layer& L,
                     int b, void* y, int y_dtype, void* ws, void* stream);
+int launch_gemm_fp4_up(const uint8_t* qx, const uint8_t* ascale, const float* z, const svdq_fp4_layer& L, int b,
+                       void* y, int y_dtype, void* ws, void* stream);
 const char* hip_error_name(int err);
 
 }  // namespace svdq

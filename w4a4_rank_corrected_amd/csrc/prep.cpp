@@ -408,6 +408,65 @@ void quantize_residual8(const float* R, int m, int n, int8_t* qw, uint16_t* wsca
   });
 }
 
+// The NVFP4 setting ([Review] sec. 8, group 16 with FP8 scales): E4M3 block
+// scales sb = E4M3_RNE_sat(fl32(amax / 6) / t), codes E2M1_RNE_sat(fl32(v / S))
+// with S = sb t, ties to the even code, the quotient's sign in bit 3.
+double fp4_tensor_scale(double amax) {
+  if (!(amax > 0.0)) return 1.0;
+  int e = 0;
+  const double mnt = std::frexp(amax / (6.0 * 448.0), &e);  // q = mnt 2^e, mnt in [0.5, 1)
+  return mnt == 0.5 ? std::ldexp(1.0, e - 1) : std::ldexp(1.0, e);
+}
+
+static double e4m3_round_host(double x) {  // x >= 0
+  if (!(x < 448.0)) return 448.0;
+  if (x == 0.0) return 0.0;
+  int e = 0;
+  std::frexp(x, &e);
+  const int q = std::max(e - 1, -6) - 3;  // quantum exponent
+  return std::min(std::nearbyint(std::ldexp(x, -q)) * std::ldexp(1.0, q), 448.0);
+}
+
+static uint8_t e4m3_bits_host(double v) {  // v a non-negative E4M3 value
+  if (v == 0.0) return 0;
+  int e = 0;
+  const double mnt = std::frexp(v, &e);  // v = mnt 2^e
+  const int ex = e - 1;
+  if (ex >= -6) return (uint8_t)(((ex + 7) << 3) | (int)std::lround((mnt * 2.0 - 1.0) * 8.0));
+  return (uint8_t)std::lround(std::ldexp(v, 9));
+}
+
+static uint8_t e2m1_code_host(float y) {  // RNE on the grid, saturating; ties to the even code
+  const float a = std::fabs(y);
+  const int idx = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  return (uint8_t)(idx | (std::signbit(y) ? 8 : 0));
+}
+
+void quantize_residual_fp4(const float* R, int m, int n, double t, uint8_t* qw, uint8_t* wscale) {
+  const int G = m / SVDQ_GROUP;
+  parallel_for((int64_t)G * n, [&](int64_t lo, int64_t hi) {
+    for (int64_t idx = lo; idx < hi; ++idx) {
+      const int g = (int)(idx / n), j = (int)(idx % n);
+      uint8_t* rec = qw + ((int64_t)g * n + j) * 32;
+      std::memset(rec, 0, 32);
+      for (int blk = 0; blk < 4; ++blk) {
+        const int k0 = g * SVDQ_GROUP + 16 * blk;
+        float amax = 0.0f;
+        for (int kk = 0; kk < 16; ++kk) amax = std::max(amax, std::fabs(R[(int64_t)(k0 + kk) * n + j]));
+        const float u = amax / 6.0f;                        // fl32(amax / 6)
+        const double sb = e4m3_round_host((double)u / t);   // t a power of two: exact
+        wscale[((int64_t)g * n + j) * 4 + blk] = e4m3_bits_host(sb);
+        const float S = (float)(sb * t);                    // exact
+        for (int kk = 0; kk < 16; ++kk) {
+          const uint8_t code = S > 0.0f ? e2m1_code_host(R[(int64_t)(k0 + kk) * n + j] / S) : 0;
+          const int ch = 16 * blk + kk;
+          rec[ch >> 1] |= (uint8_t)(code << (4 * (ch & 1)));
+        }
+      }
+    }
+  }, 64);
+}
+
 // ---------------------------------------------------------------------------
 // protected-layer candidates and their selection ([Review] sec. 5, Algorithm 1)
 // ---------------------------------------------------------------------------
