@@ -56,6 +56,7 @@ sys.path.insert(0, ROOT)
 
 I8_PEAK_TOPS = 5000.0      # MI355X dense i8 MFMA, TOP/s
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 / bf16 MFMA, TFLOP/s
 METRIC = "fused W4A4+low-rank linear TOPS (2·b·m·n/s), FLUX shapes; % of i8 MFMA peak"
 GEMM_KERNEL = "gemm_w4a4_up_kernel"
 # sources whose text defines the GEMM kernel and its launch plan
@@ -114,8 +115,10 @@ def trace_summary(prof_dir, cfg, args, rank):
         raise SystemExit(f"no rocpd database under {prof_dir}")
     c = sqlite3.connect(dbs[0])
     w8 = args.w8a8 is not None
+    f4 = args.fp4 is not None
+    cmp_mode = w8 or f4
     _, n_sets = set_plan(cfg, rank, args.out)
-    skip = max(50, args.warmup) if w8 else max(args.warmup, n_sets)
+    skip = max(50, args.warmup) if cmp_mode else max(args.warmup, n_sets)
     short = lambda nm: re.sub(r"\(.*", "", nm.replace("svdq::(anonymous namespace)::", "")
                               .replace("void ", "").replace("svdq::", ""))
     rows = list(c.execute("select name, start, end, grid_x, grid_y, workgroup_x, workgroup_y, vgpr_count, "
@@ -124,14 +127,15 @@ def trace_summary(prof_dir, cfg, args, rank):
     for nm, st, en, gx, gy, wx, wy, vg, ag, lds, scr in rows:
         wgs = (gx // max(wx, 1)) * (gy // max(wy, 1))
         by.setdefault(nm, []).append(((en - st) / 1e3, wgs, wx * wy, vg, ag, lds, scr))
-    mode = f" --w8a8 {args.w8a8}" if w8 else " --no-cpu-baseline"
+    mode = f" --w8a8 {args.w8a8}" if w8 else (f" --fp4 {args.fp4}" if f4 else " --no-cpu-baseline")
     cmd = (f"rocprofv3 --kernel-trace --stats -d {prof_dir} -o run -- python3 bench.py --workload {cfg.name} "
            f"--steps {args.steps} --warmup {args.warmup}{mode}")
-    if w8:
+    if cmp_mode:
+        other = "8-bit" if w8 else "NVFP4"
         region = (f"Timed region: {args.steps} steps after {skip} untimed ones; each step runs the INT4 "
-                  f"activation kernel, the INT4 GEMM, the 8-bit activation kernels and the 8-bit GEMM, "
+                  f"activation kernel, the INT4 GEMM, the {other} activation kernel(s) and the {other} GEMM, "
                   f"all at rank {rank} on one input and weight set (warm).")
-        title = f"# Kernel trace, 8-bit setting against INT4: {cfg.name}"
+        title = f"# Kernel trace, {other} setting against INT4: {cfg.name}"
     else:
         region = (f"Timed region: {args.steps} steps after {skip} untimed ones, rotating over {n_sets} "
                   f"input+weight sets; the script then times warm steps, rank-0 steps and the one-call entry "
@@ -140,7 +144,7 @@ def trace_summary(prof_dir, cfg, args, rank):
     out = [f"{title} (b={cfg.rows or cfg.b}, m={cfg.m}, n={cfg.n}, rank {rank})", "",
            "Command (repository root, one MI355X), then the summary:", "", "```", cmd,
            f"python bench.py --trace-summary {prof_dir} --workload {cfg.name} --steps {args.steps} "
-           f"--warmup {args.warmup}" + (f" --w8a8 {args.w8a8}" if w8 else ""), "```", "", region, "",
+           f"--warmup {args.warmup}" + mode.replace(" --no-cpu-baseline", ""), "```", "", region, "",
            "| kernel | dispatches | mean, timed region (us) | mean, all (us) | total (ms) | workgroups | "
            "threads | LDS (B) | scratch (B) |",
            "|---|---|---|---|---|---|---|---|---|"]
@@ -154,7 +158,8 @@ def trace_summary(prof_dir, cfg, args, rank):
         out.append(f"| `{short(nm)}` | {len(v)} | {t} | {np.mean(durs):.2f} | {sum(durs) / 1e3:.3f} | "
                    f"{d0[1]} | {d0[2]} | {d0[5]} | {d0[6]} |")
     out += ["", f"All kernels: {total / 1e3:.3f} ms of GPU time.", ""]
-    path = os.path.join(ROOT, "profiles", f"kernel_trace_{'w8a8_' if w8 else ''}{cfg.name}.md")
+    prefix = "w8a8_" if w8 else ("nvfp4_" if f4 else "")
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{prefix}{cfg.name}.md")
     with open(path, "w") as f:
         f.write("\n".join(out))
     print("\n".join(out))
@@ -464,6 +469,84 @@ def w8a8_compare(cfg, rank, args):
     print(json.dumps(res), flush=True)
 
 
+def fp4_compare(cfg, rank, args):
+    """The NVFP4 setting (E2M1 codes, E4M3 scales per 16 channels, f16 MFMA on
+    exactly dequantized operands) against INT4 at the same rank, on layers the
+    library prepares from the workload's X and W.  Warm timing as in
+    ``w8a8_compare``; output error against the unquantized X W on sampled rows."""
+    import torch
+    import workloads
+    import w4a4_rank_corrected_amd as S
+
+    inp = workloads.make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(inp["x_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    b, m, n = x.shape[0], cfg.m, cfg.n
+    amax = S.svdq_calibrate_act_amax(x).cpu().numpy()
+    out_dtype = torch.bfloat16 if args.out == "bf16" else torch.float32
+    stream = torch.cuda.current_stream(dev)
+    l4 = S.DeviceLayer(S.svdq_prepare_weights(inp["w"], amax, rank), device=dev)
+    lf = S.DeviceLayerFp4(S.svdq_fp4_prepare_weights(inp["w"], amax, rank), device=dev)
+    G = m // 64
+    y4 = torch.empty((b, n), dtype=out_dtype, device=dev)
+    yf = torch.empty((b, n), dtype=out_dtype, device=dev)
+    qx4 = torch.empty((G, b, 32), dtype=torch.uint8, device=dev)
+    as4 = torch.empty((G, b), dtype=torch.float16, device=dev)
+    qxf = torch.empty((G, b, 32), dtype=torch.uint8, device=dev)
+    asf = torch.empty((G, b, 4), dtype=torch.uint8, device=dev)
+    z = torch.empty((b, max(rank, 1)), dtype=torch.float32, device=dev) if rank else None
+    aws = torch.empty(max(S.svdq_act_workspace_size(b, m, rank), 1), dtype=torch.uint8, device=dev)
+    gws = torch.empty(max(S.svdq_gemm_workspace_size(b, n, m), 1), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        calls = [
+            lambda: S.svdq_quantize_act_lowrank_down(x, l4.smooth_inv, l4.l1, rank, qx=qx4, ascale=as4, z=z,
+                                                     workspace=aws, stream=stream),
+            lambda: S.svdq_gemm_w4a4_lowrank_up(qx4, as4, z, l4, b, out_dtype, y=y4, workspace=gws, stream=stream),
+            lambda: S.svdq_fp4_quantize_act_lowrank_down(x, lf.smooth_inv, lf.l1, rank, lf.t_x, qx=qxf, ascale=asf,
+                                                         z=z, workspace=aws, stream=stream),
+            lambda: S.svdq_fp4_gemm_lowrank_up(qxf, asf, z, lf, b, out_dtype, y=yf, workspace=gws, stream=stream),
+        ]
+        for k, c in enumerate(calls):
+            if ev is not None:
+                ev[k].record(stream)
+            c()
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(max(50, args.warmup)):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    t = [float(np.median([e[k].elapsed_time(e[k + 1]) for e in evs])) for k in range(4)]
+    rows = np.arange(0, b, max(1, b // 64))
+    xr = (inp["x_bits"][rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    yref = xr @ inp["w"].astype(np.float64)
+
+    def err(y):
+        yv = y[torch.from_numpy(rows).to(dev)].float().cpu().numpy().astype(np.float64)
+        return float(np.linalg.norm(yv - yref) / np.linalg.norm(yref))
+
+    ops = 2.0 * b * m * n
+    res = {"fp4_vs_w4a4": {
+        "workload": cfg.name, "b": b, "m": m, "n": n, "rank": rank, "out": args.out, "steps": args.steps,
+        "timing": "warm; the four calls alternate; median of HIP-event times",
+        "w4a4": {"act_ms": round(t[0], 5), "gemm_ms": round(t[1], 5), "total_ms": round(t[0] + t[1], 5),
+                 "gemm_TOPs": round(ops / (t[1] * 1e-3) / 1e12, 1),
+                 "gemm_frac_i8_peak": round(ops / (t[1] * 1e-3) / 1e12 / I8_PEAK_TOPS, 4),
+                 "rel_err_vs_xw": round(err(y4), 6)},
+        "nvfp4": {"act_ms": round(t[2], 5), "gemm_ms": round(t[3], 5), "total_ms": round(t[2] + t[3], 5),
+                  "gemm_TFLOPs": round(ops / (t[3] * 1e-3) / 1e12, 1),
+                  "gemm_frac_f16_peak": round(ops / (t[3] * 1e-3) / 1e12 / F16_PEAK_TFLOPS, 4),
+                  "rel_err_vs_xw": round(err(yf), 6), "t_x": lf.t_x, "t_w": lf.t_w},
+    }}
+    log(f"fp4 {cfg.name} rank {rank}: W4A4 {t[0] * 1e3:.1f} + {t[1] * 1e3:.1f} us, "
+        f"NVFP4 {t[2] * 1e3:.1f} + {t[3] * 1e3:.1f} us")
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -487,6 +570,8 @@ def main():
                     help="fused vs unfused timing at these ranks (comma-separated) instead of the metric")
     ap.add_argument("--w8a8", nargs="?", const=16, default=None, type=int, metavar="RANK",
                     help="8-bit setting against W4A4 at this rank (default 16) instead of the metric")
+    ap.add_argument("--fp4", nargs="?", const=32, default=None, type=int, metavar="RANK",
+                    help="NVFP4 setting against W4A4 at this rank (default 32) instead of the metric")
     args = ap.parse_args()
 
     if args.traffic_summary:
@@ -496,7 +581,11 @@ def main():
         import workloads
         cfg = workloads.CONFIGS[args.workload]
         rank = (cfg.rank + cfg.lora_rank) if args.rank is None else args.rank
-        trace_summary(args.trace_summary, cfg, args, args.w8a8 if args.w8a8 is not None else rank)
+        if args.w8a8 is not None:
+            rank = args.w8a8
+        elif args.fp4 is not None:
+            rank = args.fp4
+        trace_summary(args.trace_summary, cfg, args, rank)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -518,6 +607,9 @@ def main():
         return
     if args.w8a8 is not None:
         w8a8_compare(cfg, args.w8a8, args)
+        return
+    if args.fp4 is not None:
+        fp4_compare(cfg, args.fp4, args)
         return
     m, n = cfg.m, cfg.n
     rank_svd = cfg.rank if args.rank is None else args.rank
