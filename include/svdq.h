@@ -208,8 +208,10 @@ size_t svdq_gemm_workspace_size(int b, int n, int m);
  *   element alignment.  layer->smooth_inv and layer->l1 are not used.
  *   workspace: device, 16-byte aligned, >= svdq_gemm_workspace_size(b, n, m)
  *   bytes.  Its contents need no initialisation, and calls that overlap in time
- *   must not share it.  Per-group sums are accumulated in a fixed order that
- *   depends only on the shape and the device's CU count, so results are
+ *   must not share it.  A launch leaves its publication flags cleared, so a
+ *   launch captured in a HIP graph may be replayed (stream-ordered) on the same
+ *   workspace.  Per-group sums are accumulated in a fixed order that depends
+ *   only on the shape and the device's CU count, so results are
  *   deterministic. */
 int svdq_gemm_w4a4_lowrank_up(const uint8_t* qx, const uint16_t* ascale, const float* z,
                               const svdq_layer* layer, int b, void* y, int y_dtype, void* workspace,

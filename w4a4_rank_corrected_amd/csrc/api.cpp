@@ -41,7 +41,8 @@ unsigned long long next_launch_epoch() {
     x ^= x >> 29;
     return x | 1ull;
   }();
-  return base + g_launch_counter.fetch_add(1);
+  const unsigned long long e = base + g_launch_counter.fetch_add(1);
+  return e ? e : base;  // never 0: a consumed flag is cleared to 0
 }
 
 // Split plan of the act-quant kernel: workgroups of 64 rows, and enough splits

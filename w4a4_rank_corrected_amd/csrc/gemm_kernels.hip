@@ -50,8 +50,9 @@
 //     (as the first work item of a lower-numbered, earlier-dispatched
 //     workgroup), stored as an fp32 partial and published with a flag.  The
 //     workgroup holding the tile's last groups adds the low-rank branch, waits
-//     for all of the tile's flags (bounded spin), adds the partials in a fixed
-//     order and stores Y.  Results are deterministic for a shape and CU count.
+//     for all of the tile's flags (bounded spin), clears them, adds the
+//     partials in a fixed order and stores Y.  Results are deterministic for a
+//     shape and CU count.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -707,11 +708,15 @@ __device__ __forceinline__ void gemm_up_body(
       while (qlo > 0 && (long long)qlo * sk.U / sk.P > ts) --qlo;
       if (qlo < p) {
         if (tid == 0) {
-          for (int q = p - 1; q >= qlo; --q)
+          for (int q = p - 1; q >= qlo; --q) {
             for (int spin = 0; spin < (1 << 24); ++spin) {  // bound: guards misuse of the workspace
               if (__hip_atomic_load(&sk.flags[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == sk.epoch) break;
               __builtin_amdgcn_s_sleep(2);
             }
+            // each flag has exactly one consumer: clear it, so that a replay of
+            // this launch (same epoch, e.g. from a captured graph) waits again
+            __hip_atomic_store(&sk.flags[q], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
         // the flag loads have completed before the barrier; the partials are
         // then read with device-coherent loads, in the fixed order p-1 .. qlo
