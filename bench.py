@@ -185,6 +185,67 @@ def _per_dispatch(rows, counter, name_pred):
     return list(vals.values())
 
 
+SQ_COUNTERS = ("SQ_INSTS_VALU SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT "
+               "SQ_WAVES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY GRBM_GUI_ACTIVE")
+N_XCD, N_SIMD = 8, 1024    # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+PEAK_CLOCK_GHZ = 2.4       # MI355X peak engine clock
+
+
+def _per_dispatch_duration(rows, name_pred):
+    d = {}
+    for r in rows:
+        if name_pred(r["Kernel_Name"]):
+            d[r["Dispatch_Id"]] = (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-9
+    return list(d.values())
+
+
+def counter_summary(sq_dir, fetch_dir, write_dir, workload, commands):
+    """Markdown summary of the two kernels' counters: MFMA and VALU utilisation
+    (SQ counters over the dispatch's duration at the peak engine clock) and HBM
+    bytes / GB/s (FETCH_SIZE and WRITE_SIZE scaled by the plain copy, as in the
+    traffic summary).  Medians over dispatches."""
+    sq, fr, wr = _counter_rows(sq_dir), _counter_rows(fetch_dir), _counter_rows(write_dir)
+    is_copy = lambda k: "elementwise" in k or "copy" in k.lower()
+    f_fac = COPY_BYTES / (max(_per_dispatch(fr, "FETCH_SIZE", is_copy)) * 1024.0)
+    w_fac = COPY_BYTES / (max(_per_dispatch(wr, "WRITE_SIZE", is_copy)) * 1024.0)
+    kernels = [("GEMM + up-projection", lambda k: GEMM_KERNEL in k),
+               ("act-quant + down-projection", lambda k: "act_quant_down_kernel" in k and ", 1>" in k)]
+    med = lambda v: float(np.median(v)) if v else float("nan")
+    out = [f"# Counters: {workload} (one MI355X)", "", "Commands (repository root), then the summary:", "", "```",
+           commands, "```", "",
+           "Per kernel, medians over its dispatches. Cycles = dispatch duration x 2.4 GHz (the peak engine "
+           "clock; GRBM_GUI_ACTIVE / 8 XCDs gives the clock the dispatch ran at, which the short activation "
+           "kernel's counter window overstates). MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles). "
+           "VALU issue = 4 x SQ_INSTS_VALU / (1024 x cycles) "
+           "(a wave64 VALU instruction occupies a SIMD for 4 cycles). HBM bytes = FETCH_SIZE and WRITE_SIZE, "
+           f"each scaled by what it reads for a plain {COPY_BYTES >> 20} MiB device copy in the same run "
+           f"(factors {f_fac:.3f} and {w_fac:.3f}). Durations are the counter runs' dispatch timestamps "
+           "(profiling adds overhead).", "",
+           "| kernel | dispatches | duration (us) | clock (GHz) | MFMA busy | VALU issue | LDS conflict cycles / LDS instr "
+           "| HBM fetch (MB) | HBM write (MB) | HBM GB/s | % of 8 TB/s |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for label, pred in kernels:
+        dur = med(_per_dispatch_duration(sq, pred))
+        gui = med(_per_dispatch(sq, "GRBM_GUI_ACTIVE", pred))
+        cyc = dur * PEAK_CLOCK_GHZ * 1e9
+        mf = med(_per_dispatch(sq, "SQ_VALU_MFMA_BUSY_CYCLES", pred)) / (N_SIMD * cyc)
+        va = 4.0 * med(_per_dispatch(sq, "SQ_INSTS_VALU", pred)) / (N_SIMD * cyc)
+        lds = med(_per_dispatch(sq, "SQ_LDS_BANK_CONFLICT", pred)) / max(med(_per_dispatch(sq, "SQ_INSTS_LDS", pred)), 1)
+        fb = med(_per_dispatch(fr, "FETCH_SIZE", pred)) * 1024.0 * f_fac
+        wb = med(_per_dispatch(wr, "WRITE_SIZE", pred)) * 1024.0 * w_fac
+        fdur = med(_per_dispatch_duration(fr, pred))
+        gbs = (fb + wb) / fdur / 1e9
+        out.append(f"| {label} | {len(_per_dispatch(sq, 'GRBM_GUI_ACTIVE', pred))} | {dur * 1e6:.1f} | "
+                   f"{gui / N_XCD / dur / 1e9:.2f} | {100 * mf:.1f} % | {100 * va:.1f} % | {lds:.2f} | {fb / 1e6:.1f} | "
+                   f"{wb / 1e6:.1f} | {gbs:.0f} | {100 * gbs / HBM_PEAK_GBS:.1f} % |")
+    out.append("")
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out))
+    print("\n".join(out))
+    log(f"wrote {path}")
+
+
 def traffic_summary(fetch_dir, write_dir, workload, commands):
     """Per-launch HBM bytes of the GEMM kernel from a FETCH_SIZE run and a
     WRITE_SIZE run (KiB per dispatch), each scaled by what the same counter
@@ -562,6 +623,8 @@ def main():
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the GEMM traffic summary from two counter runs and exit")
     ap.add_argument("--commands", default="", help="counter-run commands recorded in the summary")
+    ap.add_argument("--counter-summary", nargs=3, metavar=("SQ_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the per-kernel counter summary (MFMA / VALU utilisation, HBM GB/s) and exit")
     ap.add_argument("--trace-summary", metavar="PROF_DIR",
                     help="write the kernel-trace summary of a profiled run of this script and exit")
     ap.add_argument("--prep-refine", nargs="?", const="tiny,pixart_fc1,flux_qkv", default=None,
@@ -576,6 +639,9 @@ def main():
 
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary, args.workload, args.commands)
+        return
+    if args.counter_summary:
+        counter_summary(*args.counter_summary, args.workload, args.commands)
         return
     if args.trace_summary:
         import workloads
