@@ -199,7 +199,6 @@ struct GemmCfg {
   static_assert(WG_PER_CU >= 1 && (WPE * 4) % (NT / 64) == 0, "whole workgroups per CU");
   static_assert(A_BYTES == 4 || A_BYTES == 8 || A_BYTES == 16, "activation staging piece");
   static_assert(B_BYTES == 4 || B_BYTES == 8 || B_BYTES == 16, "weight staging piece");
-  static_assert(2 * A_BYTES == 32 && 2 * B_BYTES == 32, "8-bit records: 32-byte staging pieces");
   static_assert(NT >= TM + TN && TM % 64 == 0, "scale staging: at most one scale per thread");
 };
 
@@ -209,6 +208,8 @@ using Cfg = GemmCfg<128, 128, 64, 64, 2, 2>;
 // 8-bit codes: no per-group VALU work, so a group's compute is short and the
 // loads run four groups ahead to cover the memory latency.
 using Cfg8 = GemmCfg<128, 128, 64, 64, 2, 4>;
+// NVFP4: 16-byte code pieces dequantized to f16 rows (64 KB of LDS per workgroup).
+using CfgF4 = GemmCfg<128, 128, 64, 64, 2, 2>;
 
 // Cache policy of the stream-K partials: sc1 = device-coherent.
 constexpr int kCoherent = 16;
@@ -263,6 +264,8 @@ __device__ __forceinline__ void gemm_up_body(
     void* __restrict__ yout, StreamK sk, float txw) {
   constexpr bool W8 = FMT == kFmtInt8, F4 = FMT == kFmtFp4;
   constexpr bool POST = W8 || F4;  // scales and the low-rank branch after the main loop
+  static_assert(!W8 || (2 * C::A_BYTES == 32 && 2 * C::B_BYTES == 32), "8-bit records: 32-byte staging pieces");
+  static_assert(!F4 || (C::A_BYTES == 16 && C::B_BYTES == 16), "FP4 records: 16-byte staging pieces");
   constexpr int TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN, NT = C::NT;
   constexpr int BI = C::BI, BJ = C::BJ;
   constexpr int ROWB = F4 ? 128 : C::ROWB;  // LDS bytes per row and group (f16 rows for FP4)
@@ -806,7 +809,7 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
                        qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
                        plan.tiles_n, y, sk, txw);
   else if constexpr (FMT == kFmtFp4)
-    hipLaunchKernelGGL((gemm_fp4_up_kernel<Cfg, OUT_BF16>), dim3((unsigned)plan.grid), dim3(Cfg::NT), 0, st,
+    hipLaunchKernelGGL((gemm_fp4_up_kernel<CfgF4, OUT_BF16>), dim3((unsigned)plan.grid), dim3(CfgF4::NT), 0, st,
                        qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
                        plan.tiles_n, y, sk, txw);
   else
@@ -828,7 +831,9 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
 // follow one tile per workgroup.  The workspace bound assumes the largest
 // gfx950 part (256 CUs), so it does not depend on the device.
 GemmPlan gemm_plan(int b, int n, int m, int cus, bool w8) {
-  static_assert(Cfg::TM == Cfg8::TM && Cfg::TN == Cfg8::TN, "one tiling for both settings");
+  static_assert(Cfg::TM == Cfg8::TM && Cfg::TN == Cfg8::TN && Cfg::TM == CfgF4::TM && Cfg::TN == CfgF4::TN,
+                "one tiling for every setting");
+  static_assert(CfgF4::WG_PER_CU == Cfg::WG_PER_CU, "the NVFP4 kernel's residency is planned as INT4's");
   constexpr int kMaxWgPerCu = Cfg::WG_PER_CU > Cfg8::WG_PER_CU ? Cfg::WG_PER_CU : Cfg8::WG_PER_CU;
   GemmPlan p;
   p.G = m / 64;
