@@ -216,12 +216,12 @@ def counter_summary(sq_dir, fetch_dir, write_dir, workload, commands):
            "Per kernel, medians over its dispatches. Cycles = dispatch duration x 2.4 GHz (the peak engine "
            "clock; GRBM_GUI_ACTIVE / 8 XCDs gives the clock the dispatch ran at, which the short activation "
            "kernel's counter window overstates). MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles). "
-           "VALU issue = 4 x SQ_INSTS_VALU / (1024 x cycles) "
-           "(a wave64 VALU instruction occupies a SIMD for 4 cycles). HBM bytes = FETCH_SIZE and WRITE_SIZE, "
+           "VALU rate = SQ_INSTS_VALU / (1024 x cycles), wave64 VALU instructions per SIMD per cycle. "
+           "HBM bytes = FETCH_SIZE and WRITE_SIZE, "
            f"each scaled by what it reads for a plain {COPY_BYTES >> 20} MiB device copy in the same run "
            f"(factors {f_fac:.3f} and {w_fac:.3f}). Durations are the counter runs' dispatch timestamps "
            "(profiling adds overhead).", "",
-           "| kernel | dispatches | duration (us) | clock (GHz) | MFMA busy | VALU issue | LDS conflict cycles / LDS instr "
+           "| kernel | dispatches | duration (us) | clock (GHz) | MFMA busy | VALU instr / SIMD / cycle | LDS conflict cycles / LDS instr "
            "| HBM fetch (MB) | HBM write (MB) | HBM GB/s | % of 8 TB/s |",
            "|---|---|---|---|---|---|---|---|---|---|---|"]
     for label, pred in kernels:
@@ -229,14 +229,14 @@ def counter_summary(sq_dir, fetch_dir, write_dir, workload, commands):
         gui = med(_per_dispatch(sq, "GRBM_GUI_ACTIVE", pred))
         cyc = dur * PEAK_CLOCK_GHZ * 1e9
         mf = med(_per_dispatch(sq, "SQ_VALU_MFMA_BUSY_CYCLES", pred)) / (N_SIMD * cyc)
-        va = 4.0 * med(_per_dispatch(sq, "SQ_INSTS_VALU", pred)) / (N_SIMD * cyc)
+        va = med(_per_dispatch(sq, "SQ_INSTS_VALU", pred)) / (N_SIMD * cyc)
         lds = med(_per_dispatch(sq, "SQ_LDS_BANK_CONFLICT", pred)) / max(med(_per_dispatch(sq, "SQ_INSTS_LDS", pred)), 1)
         fb = med(_per_dispatch(fr, "FETCH_SIZE", pred)) * 1024.0 * f_fac
         wb = med(_per_dispatch(wr, "WRITE_SIZE", pred)) * 1024.0 * w_fac
         fdur = med(_per_dispatch_duration(fr, pred))
         gbs = (fb + wb) / fdur / 1e9
         out.append(f"| {label} | {len(_per_dispatch(sq, 'GRBM_GUI_ACTIVE', pred))} | {dur * 1e6:.1f} | "
-                   f"{gui / N_XCD / dur / 1e9:.2f} | {100 * mf:.1f} % | {100 * va:.1f} % | {lds:.2f} | {fb / 1e6:.1f} | "
+                   f"{gui / N_XCD / dur / 1e9:.2f} | {100 * mf:.1f} % | {va:.3f} | {lds:.2f} | {fb / 1e6:.1f} | "
                    f"{wb / 1e6:.1f} | {gbs:.0f} | {100 * gbs / HBM_PEAK_GBS:.1f} % |")
     out.append("")
     path = os.path.join(ROOT, "profiles", f"counters_{workload}.md")
