@@ -811,7 +811,8 @@ def main():
                     "gemm_w4a4_up_TOPs": round(k2_tops, 2),
                     "gemm_algorithmic_bytes": k2_bytes, "act_algorithmic_bytes": k1_bytes,
                     "gemm_hbm_fetch_bytes": None if traffic is None else round(traffic["fetch_bytes"]),
-                    "gemm_hbm_write_bytes": None if traffic is None else round(traffic["write_bytes"])},
+                    "gemm_hbm_write_bytes": None if traffic is None else round(traffic["write_bytes"]),
+                    "gemm_schedule": S.svdq_gemm_schedule(b, n, m)},
         "warm": {"ms_per_step": round(warm_ms, 5), "value": round(ops / (warm_ms * 1e-3) / 1e12, 2),
                  "act_quant_down_ms": round(warm_k1, 5), "gemm_w4a4_up_ms": round(warm_k2, 5),
                  "svdq_linear_ms": round(linear_ms, 5)},

@@ -198,6 +198,22 @@ int svdq_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int rank, in
  * its stream-K schedule (an upper bound valid on every gfx950 device). */
 size_t svdq_gemm_workspace_size(int b, int n, int m);
 
+/* Operand settings of the GEMM kernels, for svdq_gemm_schedule. */
+enum { SVDQ_GEMM_INT4 = 0, SVDQ_GEMM_W8A8 = 1, SVDQ_GEMM_FP4 = 2 };
+
+/* HOST (queries the current device's CU count; no launch): the schedule the
+ * GEMM kernel of `setting` (SVDQ_GEMM_*) would use for an output of b x n with
+ * m input channels ([Nunchaku]: one kernel per fused pair; the split of output
+ * tiles over workgroups is this library's own).  Writes info[0] = 128 x 128
+ * output tiles, info[1] = workgroups launched, info[2] = stream-K workgroups
+ * (0 when every workgroup computes one whole tile), info[3] = tiles shared out
+ * by stream-K, info[4] = resident workgroups per CU of the kernel chosen.
+ * info: host, 5 ints, owned by the caller.  On an error info is
+ * untouched: SVDQ_ERR_INVALID_ARG for a null info, an unknown setting, b < 0
+ * or n < 1; SVDQ_ERR_UNSUPPORTED for b, n or m above SVDQ_MAX_DIM, m not a
+ * positive multiple of 64, or m > SVDQ_W8A8_MAX_M with SVDQ_GEMM_W8A8. */
+int svdq_gemm_schedule(int b, int n, int m, int setting, int* info);
+
 /* DEVICE: fused W4A4 GEMM + low-rank up-projection ([Review] sec. 6.1
  * Algorithm 2 steps 4-8; Eq.(7)):
  *     isum[i,j,g] = sum_{k in g} qx[i,k] qw[k,j]          (exact integer)

@@ -356,6 +356,33 @@ def test_streamk_splits_deterministic_and_match_oracle(S, b, m, n):
     assert err <= 1e-4
 
 
+def test_hybrid_schedule_matches_oracle(S):
+    """A shape whose schedule runs a stream-K part and then full rounds of one
+    tile per workgroup (found with the library's own schedule query, so it
+    holds for the device's CU count): bit-identical repeats, and rows from
+    both parts match the oracle."""
+    m, n = 1536, 5120
+    b = next((128 * tm - 37 for tm in range(1, 256)
+              if 0 < S.svdq_gemm_schedule(128 * tm, n, m)["stream_k_workgroups"]
+              < S.svdq_gemm_schedule(128 * tm, n, m)["grid"]), None)
+    assert b is not None, "no hybrid schedule for this device"
+    sch = S.svdq_gemm_schedule(b, n, m)
+    _say(f"hybrid schedule b={b} m={m} n={n}: {sch}")
+    rng = np.random.default_rng(11)
+    xb = workloads.random_bf16_bits(rng, (b, m), 1.5)
+    x = LY.bf16_bits_to_f32(xb)
+    lay = _oracle_layer(rng, m, n, 32, x)
+    dl = device_layer(S, lay)
+    xd = dev_bf16(xb)
+    ys = [S.svdq_linear(xd, dl, torch.float32) for _ in range(2)]
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1])
+    rows = np.unique(np.concatenate([np.arange(0, b, max(1, b // 48)), [b - 1]]))
+    err = rel(ys[0].cpu().numpy()[rows], O.linear_rows(x[rows], lay))
+    _say(f"  sampled rows {len(rows)}: rel err {err:.3e}")
+    assert err <= 1e-4
+
+
 # the unfused path rounds the W4A4 product, the up-projection and their sum
 # to bf16 (three roundings of at most 2^-9 relative each, ~1.7e-3 Frobenius
 # apiece on these layers), so its bf16 bar is 4e-3; fp32 output keeps 1e-4

@@ -32,7 +32,49 @@ def test_exports_every_symbol_declared_in_header():
     for nm in names:
         assert hasattr(L, nm), nm
     assert {s[0] for s in B.SIGNATURES} == names
-    assert L.svdq_abi_version() == 102
+    assert L.svdq_abi_version() == 103
+
+
+# Host logic of the GEMM schedule (the planner runs on the host; without a GPU
+# the library plans for 256 CUs, the MI355X count).  Residency: three INT4
+# workgroups per CU, two for the 8-bit and NVFP4 kernels.
+SCHEDULES = [
+    # (b, n, m, setting, tiles, grid, stream-K workgroups, stream-K tiles, workgroups per CU)
+    (4608, 9216, 3072, "int4", 2592, 2592, 0, 0, 3),      # 3/CU: last round 3/8 full, one tile per workgroup
+    (4096, 4608, 1152, "int4", 1152, 1152, 0, 0, 3),      # 3/CU: last round half full
+    (4608, 3072, 12288, "int4", 864, 864, 0, 0, 2),       # 3/CU would split (1/8 full); 2/CU: 11/16 full
+    (4608, 9216, 3072, "w8a8", 2592, 2560, 512, 544, 2),  # 2/CU: 1/16 full, stream-K part then 4 full rounds
+    (4608, 9216, 3072, "fp4", 2592, 2560, 512, 544, 2),
+    (256, 21504, 3072, "int4", 336, 512, 512, 336, 2),    # under one round: stream-K at 2/CU
+    (4992, 5120, 1536, "int4", 1560, 1536, 512, 536, 2),  # hybrid: 536 tiles by stream-K, then 2 rounds
+    (4608, 3072, 1024, "int4", 864, 864, 0, 0, 3),        # G = 16: too few groups to split
+    (256, 256, 64, "int4", 4, 4, 0, 0, 3),                # one group
+    (0, 256, 256, "int4", 0, 0, 0, 0, 3),
+]
+
+
+@pytest.mark.parametrize("b,n,m,setting,tiles,grid,skw,skt,wpc", SCHEDULES)
+def test_gemm_schedule(b, n, m, setting, tiles, grid, skw, skt, wpc):
+    _lib_or_skip()
+    if S.svdq_gemm_schedule(128, 128, 64)["grid"] != 1:
+        pytest.skip("unexpected device")
+    got = S.svdq_gemm_schedule(b, n, m, setting)
+    assert got == {"tiles": tiles, "grid": grid, "stream_k_workgroups": skw, "stream_k_tiles": skt,
+                   "workgroups_per_cu": wpc}
+
+
+def test_gemm_schedule_rejects_bad_arguments():
+    L = _lib_or_skip()
+    info = (ctypes.c_int * 5)(-5, -5, -5, -5, -5)
+    assert L.svdq_gemm_schedule(64, 64, 64, 0, None) == 1
+    assert L.svdq_gemm_schedule(64, 64, 64, 3, info) == 1
+    assert L.svdq_gemm_schedule(-1, 64, 64, 0, info) == 1
+    assert L.svdq_gemm_schedule(64, 0, 64, 0, info) == 1
+    for m in (0, 100, 1 << 23):
+        assert L.svdq_gemm_schedule(64, 64, m, 0, info) != 0
+    assert L.svdq_gemm_schedule(64, 64, 2 * 131072, 1, info) != 0   # above the 8-bit limit
+    assert list(info) == [-5] * 5                            # untouched on error
+    assert L.svdq_gemm_schedule(64, 64, 2 * 131072, 0, info) == 0
 
 
 def test_status_strings():

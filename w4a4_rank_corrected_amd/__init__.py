@@ -6,7 +6,8 @@ marshals arguments to it (``_binding``); it raises if the library is missing.
 """
 from ._binding import (  # noqa: F401
     SVDQ_GROUP, SVDQ_MAX_RANK, SVDQ_OUT_BF16, SVDQ_OUT_F32, SvdqError, DeviceLayer, lib,
-    svdq_act_workspace_size, svdq_append_lora, svdq_gemm_workspace_size, svdq_calibrate_act_amax, svdq_gemm_w4a4_lowrank_up,
+    svdq_act_workspace_size, svdq_append_lora, svdq_gemm_workspace_size, svdq_gemm_schedule,
+    svdq_calibrate_act_amax, svdq_gemm_w4a4_lowrank_up,
     svdq_linear, svdq_linear_workspace_size, svdq_linear_unfused, svdq_linear_unfused_workspace_size,
     svdq_prepare_weights, svdq_prepare_weights_refined, svdq_quantize_act_lowrank_down,
     svdq_quantize_residual, SVDQ_W8A8_MAX_M, DeviceLayer8, svdq_w8a8_act_workspace_size,
@@ -19,7 +20,7 @@ from ._binding import (  # noqa: F401
 __all__ = [
     "SVDQ_GROUP", "SVDQ_MAX_RANK", "SVDQ_OUT_BF16", "SVDQ_OUT_F32", "SvdqError", "DeviceLayer",
     "lib", "svdq_act_workspace_size", "svdq_append_lora", "svdq_calibrate_act_amax",
-    "svdq_gemm_workspace_size",
+    "svdq_gemm_workspace_size", "svdq_gemm_schedule",
     "svdq_gemm_w4a4_lowrank_up", "svdq_linear", "svdq_linear_workspace_size",
     "svdq_linear_unfused", "svdq_linear_unfused_workspace_size",
     "svdq_prepare_weights", "svdq_prepare_weights_refined", "svdq_quantize_act_lowrank_down",

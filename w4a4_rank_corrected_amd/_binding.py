@@ -70,6 +70,7 @@ SIGNATURES = [
     ("svdq_quantize_act_lowrank_down", _c_int,
      [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _size, _vp]),
     ("svdq_gemm_workspace_size", _size, [_c_int, _c_int, _c_int]),
+    ("svdq_gemm_schedule", _c_int, [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_c_int)]),
     ("svdq_gemm_w4a4_lowrank_up", _c_int,
      [_vp, _vp, _vp, ctypes.POINTER(svdq_layer), _c_int, _vp, _c_int, _vp, _size, _vp]),
     ("svdq_linear_workspace_size", _size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
@@ -327,6 +328,20 @@ class DeviceLayer:
 
 def svdq_gemm_workspace_size(b: int, n: int, m: int) -> int:
     return int(lib().svdq_gemm_workspace_size(b, n, m))
+
+
+GEMM_SETTINGS = {"int4": 0, "w8a8": 1, "fp4": 2}  # SVDQ_GEMM_INT4, _W8A8, _FP4
+
+
+def svdq_gemm_schedule(b: int, n: int, m: int, setting: str = "int4") -> dict:
+    """The GEMM kernel's schedule for a b x n output with m input channels on
+    the current device: tiles, workgroups launched, stream-K workgroups and the
+    tiles they share (both 0 when each workgroup computes one tile), and the
+    resident workgroups per CU of the kernel chosen."""
+    info = (_c_int * 5)()
+    _check(lib().svdq_gemm_schedule(b, n, m, GEMM_SETTINGS[setting], info))
+    return {"tiles": info[0], "grid": info[1], "stream_k_workgroups": info[2], "stream_k_tiles": info[3],
+            "workgroups_per_cu": info[4]}
 
 
 def svdq_gemm_w4a4_lowrank_up(qx, ascale, z, layer: DeviceLayer, b: Optional[int] = None,

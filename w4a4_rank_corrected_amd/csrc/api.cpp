@@ -312,7 +312,7 @@ int check_y(void* y, int y_dtype, int b) {
 
 extern "C" {
 
-int svdq_abi_version(void) { return 102; }
+int svdq_abi_version(void) { return 103; }
 
 const char* svdq_last_error(void) { return g_err; }
 
@@ -510,6 +510,28 @@ int svdq_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int rank, in
 size_t svdq_gemm_workspace_size(int b, int n, int m) {
   if (b <= 0 || n <= 0 || m < SVDQ_GROUP || m % SVDQ_GROUP) return 0;
   return gemm_ws_bytes(b, n, m);
+}
+
+int svdq_gemm_schedule(int b, int n, int m, int setting, int* info) {
+  clear_error();
+  REQUIRE(info, SVDQ_ERR_INVALID_ARG, "info must not be NULL");
+  REQUIRE(setting == SVDQ_GEMM_INT4 || setting == SVDQ_GEMM_W8A8 || setting == SVDQ_GEMM_FP4,
+          SVDQ_ERR_INVALID_ARG, "unknown GEMM setting %d", setting);
+  REQUIRE(b >= 0 && n >= 1, SVDQ_ERR_INVALID_ARG, "need b >= 0 and n >= 1 (got b=%d, n=%d)", b, n);
+  REQUIRE(b <= SVDQ_MAX_DIM && n <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "b and n must be <= %d (got b=%d, n=%d)",
+          SVDQ_MAX_DIM, b, n);
+  int st = check_group(m, SVDQ_GROUP);
+  if (st) return st;
+  REQUIRE(setting != SVDQ_GEMM_W8A8 || m <= SVDQ_W8A8_MAX_M, SVDQ_ERR_UNSUPPORTED,
+          "the 8-bit setting needs m <= %d (got %d)", SVDQ_W8A8_MAX_M, m);
+  const int fmt = setting == SVDQ_GEMM_W8A8 ? kFmtInt8 : setting == SVDQ_GEMM_FP4 ? kFmtFp4 : kFmtInt4;
+  const GemmPlan p = gemm_plan(b, n, m, device_cus(), fmt);
+  info[0] = p.tiles_m * p.tiles_n;
+  info[1] = p.grid;
+  info[2] = p.streamk ? p.sk_grid : 0;
+  info[3] = p.streamk ? p.sk_tiles : 0;
+  info[4] = p.wg_per_cu;
+  return SVDQ_OK;
 }
 
 int svdq_gemm_w4a4_lowrank_up(const uint8_t* qx, const uint16_t* ascale, const float* z,

@@ -22,8 +22,9 @@
 // The two FMAs per (output element, group) make the kernel VALU-bound on
 // gfx950 (a 16x16x64 i8 MFMA covers 256 element-groups in 16 cycles; their 8
 // wave64 FMAs need 32).  The work decomposition therefore aims at keeping the
-// VALU busy: many waves per SIMD so MFMAs co-issue with other waves' FMAs,
-// unpacking each code once per workgroup, and few barriers.
+// VALU busy: three waves per SIMD so MFMAs co-issue with other waves' FMAs,
+// unpacking each code once per workgroup, few LDS reads of scales, and few
+// barriers.
 //
 // Work decomposition (gfx950: 256 CUs in 8 XCDs, 4 SIMDs per CU, wave64),
 // parameterised by GemmCfg:
@@ -36,12 +37,15 @@
 //   Measured alternatives that were not faster on gfx950: 256 x 256 and
 //   128 x 256 tiles (register spills or fewer resident waves), 128 x 64 tiles
 //   at three or four waves per SIMD (more staging and LDS traffic per output),
-//   and explicit MFMA/FMA interleaving hints (the two resident workgroups
+//   and explicit MFMA/FMA interleaving hints (the resident workgroups
 //   already interleave).
 //
 // Schedules (tile = TM x TN outputs over all G groups; slots = the resident
-// workgroups of all CUs, two per CU for the configuration below):
-//   * one tile per workgroup, when the tiles fill whole rounds of slots;
+// workgroups of all CUs: three per CU for INT4 codes with one tile per
+// workgroup, two for INT4 launches with a stream-K part and for the 8-bit and
+// NVFP4 settings):
+//   * one tile per workgroup, unless the tiles leave the last round of slots
+//     at most a quarter full;
 //   * otherwise a hybrid: the tiles of the last one or two rounds are shared
 //     out by stream-K among `slots` persistent workgroups (equal (tile, group)
 //     iteration ranges), which are dispatched first; the remaining full rounds
@@ -199,16 +203,26 @@ struct GemmCfg {
   static_assert(WG_PER_CU >= 1 && (WPE * 4) % (NT / 64) == 0, "whole workgroups per CU");
   static_assert(A_BYTES == 4 || A_BYTES == 8 || A_BYTES == 16, "activation staging piece");
   static_assert(B_BYTES == 4 || B_BYTES == 8 || B_BYTES == 16, "weight staging piece");
-  static_assert(NT >= TM + TN && TM % 64 == 0, "scale staging: at most one scale per thread");
+  static_assert(NT == TM + TN && TM % 64 == 0, "scale staging: one scale per thread");
+  static_assert(BI == 4 && BJ % 2 == 0, "scale reads: one 16-byte row-scale vector, whole fp16 column vectors");
 };
 
-// 128 x 128 tile, 4 waves of 64 x 64; two workgroups share a CU, so one
-// workgroup's barrier and LDS-latency phases overlap the other's compute.
-using Cfg = GemmCfg<128, 128, 64, 64, 2, 2>;
+// 128 x 128 tile, 4 waves of 64 x 64; three workgroups share a CU (168
+// registers per lane), so one workgroup's barrier and LDS-latency phases
+// overlap the others' compute, and loads run one group ahead.  This kernel
+// runs schedules of one tile per workgroup only: built with the stream-K code
+// at this register budget, the compiler spills the stream-K loop's registers
+// to scratch, and that build returned wrong stream-K tiles on gfx950 (cause
+// not established), so stream-K launches use CfgSk.
+using Cfg = GemmCfg<128, 128, 64, 64, 3, 1>;
+// INT4 launches with a stream-K part: two workgroups per CU, loads two groups
+// ahead (no spills at 256 registers).
+using CfgSk = GemmCfg<128, 128, 64, 64, 2, 2>;
 // 8-bit codes: no per-group VALU work, so a group's compute is short and the
 // loads run four groups ahead to cover the memory latency.
 using Cfg8 = GemmCfg<128, 128, 64, 64, 2, 4>;
-// NVFP4: 16-byte code pieces dequantized to f16 rows (64 KB of LDS per workgroup).
+// NVFP4: 16-byte code pieces dequantized to f16 rows (64 KB of LDS per
+// workgroup, so two workgroups per CU).
 using CfgF4 = GemmCfg<128, 128, 64, 64, 2, 2>;
 
 // Cache policy of the stream-K partials: sc1 = device-coherent.
@@ -224,9 +238,6 @@ struct StreamK {
   unsigned long long* flags;      // [P] publication epochs
   unsigned long long epoch;       // this launch's epoch
 };
-
-// Operand formats of the kernel body.
-enum { kFmtInt4 = 0, kFmtInt8 = 1, kFmtFp4 = 2 };
 
 // E4M3 block-scale byte -> (2^e, M) with value = M 2^e, M in [1, 2) (M = 0 for
 // a zero scale): the FP4 -> f16 conversion applies only the exponent of its
@@ -255,7 +266,7 @@ __device__ __forceinline__ void e4m3_split(uint32_t bits, float& p2, _Float16& M
 //    workgroup into f16 LDS rows and the f16 MFMAs accumulate sum_k x^ w^ in
 //    fp32; the two power-of-two tensor scales (txw = t_x t_w) are applied
 //    once in the epilogue, exactly.
-template <class C, bool OUT_BF16, int FMT>
+template <class C, bool OUT_BF16, int FMT, bool SK = true>
 __device__ __forceinline__ void gemm_up_body(
     const uint8_t* __restrict__ qx, const uint16_t* __restrict__ ascale,
     const float* __restrict__ z, const uint8_t* __restrict__ qw,
@@ -273,9 +284,10 @@ __device__ __forceinline__ void gemm_up_body(
   // per buffer: KG groups of TM (TN) rows
   __shared__ __align__(16) uint8_t As[2][KG * TM * ROWB];
   __shared__ __align__(16) uint8_t Bs[2][KG * TN * ROWB];
-  // per buffer and group: [sx/256 (TM) | -1.5*2^23 sx/256 (TM) | sw (TN) |
-  // unused (NT - TM - TN)] (no per-group scales with 8-bit codes)
-  constexpr int SSC = TM + NT;
+  // per buffer and group: [sx/256 (TM floats) | sw (TN fp16)], each in the
+  // order in which a lane reads its rows and columns (see store_stage); no
+  // per-group scales with 8-bit or FP4 codes
+  constexpr int SSC = TM + TN / 2;
   __shared__ __align__(16) float Ssc[2][POST ? 4 : KG * SSC];
 
   const int tid = threadIdx.x;
@@ -411,11 +423,13 @@ __device__ __forceinline__ void gemm_up_body(
         }
       }
     };
-    // Scales go to one LDS array per buffer and group: [sx/256 (TM) |
-    // -1.5*2^23 sx/256 (TM) | sw (TN) | unused].  Thread t < TM stages row
-    // i0+t's activation scale (two words), thread TM+u column j0+u's weight
-    // scale (the same word twice; threads past TM+TN write zeros to the unused
-    // tail), so the staging is straight-line code.
+    // Scales go to one LDS array per buffer and group: [sx/256 (TM floats) |
+    // sw (TN fp16)].  Thread t < TM stages row i0+t's activation scale, thread
+    // TM+u column j0+u's weight scale (the choice is wave-uniform).  Both are
+    // permuted so that a lane's values are contiguous: row l = 16 bi + r of a
+    // wave's row block sits at BI r + bi (one 16-byte read gives a lane its BI
+    // rows), column l = 16 bj + 4 c + v of a wave's column block at
+    // 4 BJ c + 4 bj + v (BJ/2 16-byte reads give a lane its 4 BJ columns).
     // FP4: 16 code bytes (channels 32h .. 32h+31 of the record, h = w0 / 4)
     // -> four 16-byte f16 chunks 4h .. 4h+3 of the LDS row; words 0-1 use
     // block 2h's scale (byte 0 of sc), words 2-3 block 2h+1's (byte 1)
@@ -453,19 +467,24 @@ __device__ __forceinline__ void gemm_up_body(
         } else {
           unpack_piece<AB>(as, chunk_swz(a_row), a_w0, st.a[q]);
           unpack_piece<BB>(bs, chunk_swz(b_col), b_w0, st.w[q]);
-          const float sv = f16_to_f32((uint16_t)st.s[q]);
+          // one 32-bit store per thread: sx/256 (exact), or the fp16 pair of
+          // columns (l, l ^ 1), which lanes u and u ^ 1 both write
+          const uint32_t sv = st.s[q];
+          const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)sv, 0xB1, 0xF, 0xF, false);  // lane ^ 1
           const bool act = wave_u < TM / 64;
-          const float h = sv * 0.00390625f;  // sx / 256 (exact)
-          float* sc = &Ssc[buf][q * SSC];
-          sc[act ? tid : TM + tid] = act ? h : sv;
-          sc[TM + tid] = act ? -kMagic * h : sv;  // exact: 3 * 2^14 * sx
+          const int la = tid % WM, lw = (tid - TM) % WN;
+          const int pa = tid - la + BI * (la & 15) + (la >> 4);
+          const int pw = TM + ((tid - TM - lw + 4 * BJ * ((lw & 15) >> 2) + 4 * (lw >> 4) + (lw & 3)) >> 1);
+          const uint32_t va = __float_as_uint(f16_to_f32((uint16_t)sv) * 0.00390625f);
+          const uint32_t vw = (lw & 1) ? (nb | (sv << 16)) : (sv | (nb << 16));
+          reinterpret_cast<uint32_t*>(&Ssc[buf][q * SSC])[act ? pa : pw] = act ? va : vw;
         }
       }
     };
     // One group q of a buffer.  INT4: for each 16-row block bi, BJ MFMAs (one
-    // per 16-column block), whose results are applied by 8 * BJ FMAs one block
-    // later, so an MFMA's latency is covered by the previous block's FMAs.
-    // 8-bit: the MFMAs accumulate into the integer sums directly.
+    // per 16-column block), whose results are applied by 8 * BJ FMAs (the
+    // other resident waves cover the MFMA latency).  8-bit: the MFMAs
+    // accumulate into the integer sums directly.
     auto compute_group = [&](int buf, int q) {
       const uint8_t* as = &As[buf][q * TM * ROWB];
       const uint8_t* bs = &Bs[buf][q * TN * ROWB];
@@ -501,40 +520,37 @@ __device__ __forceinline__ void gemm_up_body(
                 __builtin_bit_cast(i32x4, Pb[bj]), __builtin_bit_cast(i32x4, Qa), iacc[bi][bj], 0, 0, 0);
         }
       } else {
+        typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
         const float* sc = &Ssc[buf][q * SSC];
         u32x4 Pb[BJ];
-        f32x4 sw4[BJ];
 #pragma unroll
-        for (int bj = 0; bj < BJ; ++bj) {
-          const int cc = WN * wn + 16 * bj;
-          Pb[bj] = *reinterpret_cast<const u32x4*>(bs + (cc + r) * ROWB + cs);
-          sw4[bj] = *reinterpret_cast<const f32x4*>(sc + 2 * TM + cc + 4 * c);
-        }
+        for (int bj = 0; bj < BJ; ++bj)
+          Pb[bj] = *reinterpret_cast<const u32x4*>(bs + (WN * wn + 16 * bj + r) * ROWB + cs);
+        // this lane's BI row scales sx/256 and 4 BJ column scales sw (fp16,
+        // applied by mixed-precision FMAs: the conversion is exact)
+        const f32x4 sx4 = *reinterpret_cast<const f32x4*>(sc + WM * wm + BI * r);
+        f16x8 sw8[BJ / 2];
+#pragma unroll
+        for (int h = 0; h < BJ / 2; ++h)
+          sw8[h] = *reinterpret_cast<const f16x8*>(reinterpret_cast<const _Float16*>(sc + TM) + WN * wn +
+                                                   4 * BJ * c + 8 * h);
         const int rbase = WM * wm + r;
-        i32x4 d[2][BJ];
-        float sxq[2], sng[2];
 #pragma unroll
-        for (int bi = 0; bi <= BI; ++bi) {
-          const int cur = bi & 1, prev = cur ^ 1;
-          if (bi < BI) {
-            const int rr = rbase + 16 * bi;
-            const u32x4 Qa = *reinterpret_cast<const u32x4*>(as + rr * ROWB + cs);
-            sxq[cur] = sc[rr];
-            sng[cur] = sc[TM + rr];
+        for (int bi = 0; bi < BI; ++bi) {
+          const u32x4 Qa = *reinterpret_cast<const u32x4*>(as + (rbase + 16 * bi) * ROWB + cs);
+          const float sxq = sx4[bi], sng = -kMagic * sx4[bi];  // exact: 3 * 2^14 * sx
+          i32x4 d[BJ];
 #pragma unroll
-            for (int bj = 0; bj < BJ; ++bj)
-              d[cur][bj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                  __builtin_bit_cast(i32x4, Pb[bj]), __builtin_bit_cast(i32x4, Qa), magic, 0, 0, 0);
-          }
-          if (bi > 0) {
+          for (int bj = 0; bj < BJ; ++bj)
+            d[bj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                __builtin_bit_cast(i32x4, Pb[bj]), __builtin_bit_cast(i32x4, Qa), magic, 0, 0, 0);
 #pragma unroll
-            for (int bj = 0; bj < BJ; ++bj)
+          for (int bj = 0; bj < BJ; ++bj)
 #pragma unroll
-              for (int v = 0; v < 4; ++v) {
-                const float t = __builtin_fmaf(__int_as_float(d[prev][bj][v]), sxq[prev], sng[prev]);
-                acc[bi - 1][bj][v] = __builtin_fmaf(t, sw4[bj][v], acc[bi - 1][bj][v]);
-              }
-          }
+            for (int v = 0; v < 4; ++v) {
+              const float t = __builtin_fmaf(__int_as_float(d[bj][v]), sxq, sng);
+              acc[bi][bj][v] = __builtin_fmaf(t, (float)sw8[bj >> 1][4 * (bj & 1) + v], acc[bi][bj][v]);
+            }
         }
       }
     };
@@ -656,7 +672,7 @@ __device__ __forceinline__ void gemm_up_body(
     }
   };
 
-  if ((int)blockIdx.x >= sk.P) {  // one tile per workgroup
+  if (!SK || (int)blockIdx.x >= sk.P) {  // one tile per workgroup
     const int T = tiles_m * tiles_n;
     int ti, tj;
     band_tile(dp_tile((int)blockIdx.x - sk.P, T - sk.T, sk.T), tiles_m, tiles_n, ti, tj);
@@ -670,6 +686,7 @@ __device__ __forceinline__ void gemm_up_body(
     store_tile(ti * TM, tj * TN);
     return;
   }
+  if constexpr (!SK) return;
 
   // ---- stream-K: iterations [u0, u1) of this workgroup, descending ----------
   const int p = blockIdx.x;
@@ -749,15 +766,15 @@ __device__ __forceinline__ void gemm_up_body(
   }
 }
 
-template <class C, bool OUT_BF16>
+template <class C, bool OUT_BF16, bool SK>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void gemm_w4a4_up_kernel(
     const uint8_t* __restrict__ qx, const uint16_t* __restrict__ ascale,
     const float* __restrict__ z, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, int b, int n, int G, int rank, int tiles_m, int tiles_n,
     void* __restrict__ yout, StreamK sk, float txw) {
-  gemm_up_body<C, OUT_BF16, kFmtInt4>(qx, ascale, z, qw, wscale, l2t, bias, b, n, G, rank, tiles_m, tiles_n, yout,
-                                      sk, txw);
+  gemm_up_body<C, OUT_BF16, kFmtInt4, SK>(qx, ascale, z, qw, wscale, l2t, bias, b, n, G, rank, tiles_m, tiles_n,
+                                          yout, sk, txw);
 }
 
 template <class C, bool OUT_BF16>
@@ -812,9 +829,13 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
     hipLaunchKernelGGL((gemm_fp4_up_kernel<CfgF4, OUT_BF16>), dim3((unsigned)plan.grid), dim3(CfgF4::NT), 0, st,
                        qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
                        plan.tiles_n, y, sk, txw);
-  else
-    hipLaunchKernelGGL((gemm_w4a4_up_kernel<Cfg, OUT_BF16>), dim3((unsigned)plan.grid), dim3(Cfg::NT), 0, st,
+  else if (plan.wg_per_cu == Cfg::WG_PER_CU && !plan.streamk)
+    hipLaunchKernelGGL((gemm_w4a4_up_kernel<Cfg, OUT_BF16, false>), dim3((unsigned)plan.grid), dim3(Cfg::NT), 0, st,
                        qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
+                       plan.tiles_n, y, sk, txw);
+  else
+    hipLaunchKernelGGL((gemm_w4a4_up_kernel<CfgSk, OUT_BF16, true>), dim3((unsigned)plan.grid), dim3(CfgSk::NT), 0,
+                       st, qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
                        plan.tiles_n, y, sk, txw);
   return (int)hipGetLastError();
 }
@@ -822,32 +843,29 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
 }  // namespace
 
 // Plan of the GEMM launch.  With T tiles of G groups and S = CUs * (resident
-// workgroups per CU) slots, one tile per workgroup leaves each slot idle for
-// (ceil(T / S) - T / S) * G group-iterations on average.  When that idle
-// time is at least 16 group-iterations (the measured cost of splitting a
-// tile is a few), the tiles beyond the first floor(T / S) - 1 full rounds
+// workgroups per CU of the kernel) slots, one tile per workgroup runs
+// ceil(T / S) rounds, the last one a fraction f of slots full.  Stream-K is
+// chosen when the idle time of that round, (1 - f) * G group-iterations per
+// slot, is at least 16 (splitting a tile costs a few) and either T < S or
+// f <= 1/4: then the tiles beyond the first floor(T / S) - 1 full rounds
 // (between S and 2S of them, or all T when T < 2S) go to min(S, their
 // iterations / 8) stream-K workgroups, dispatched first, and the full rounds
-// follow one tile per workgroup.  The workspace bound assumes the largest
-// gfx950 part (256 CUs), so it does not depend on the device.
-GemmPlan gemm_plan(int b, int n, int m, int cus, bool w8) {
-  static_assert(Cfg::TM == Cfg8::TM && Cfg::TN == Cfg8::TN && Cfg::TM == CfgF4::TM && Cfg::TN == CfgF4::TN,
-                "one tiling for every setting");
-  static_assert(CfgF4::WG_PER_CU == Cfg::WG_PER_CU, "the NVFP4 kernel's residency is planned as INT4's");
-  constexpr int kMaxWgPerCu = Cfg::WG_PER_CU > Cfg8::WG_PER_CU ? Cfg::WG_PER_CU : Cfg8::WG_PER_CU;
-  GemmPlan p;
-  p.G = m / 64;
-  p.tiles_m = (b + Cfg::TM - 1) / Cfg::TM;
-  p.tiles_n = (n + Cfg::TN - 1) / Cfg::TN;
+// follow one tile per workgroup.  A last round fuller than a quarter runs one
+// tile per workgroup: its workgroups finish faster on the emptier CUs, which
+// measured better than splitting tiles.  INT4 codes first try the
+// three-per-CU kernel (one tile per workgroup only); if that residency calls
+// for stream-K, the two-per-CU kernel is planned by the same rule.  The
+// workspace bound assumes the largest gfx950 part (256 CUs) and the largest
+// stream-K residency, so it does not depend on the device or the format.
+namespace {
+void plan_rounds(GemmPlan& p, long long slots) {
   const long long T = (long long)p.tiles_m * p.tiles_n;
-  const long long slots = (long long)(w8 ? Cfg8::WG_PER_CU : Cfg::WG_PER_CU) * (cus > 0 ? cus : kMaxCUs);
-  const long long rounds = (T + slots - 1) / slots;
-  const double idle = ((double)rounds - (double)T / (double)slots) * p.G;
-  p.streamk = idle >= 16.0 && T * p.G >= 16;
+  const long long full = T / slots, rest = T - full * slots;  // rest / slots = f
+  const bool idle = (slots - rest) * p.G >= 16 * slots;      // (1 - f) G >= 16
+  p.streamk = T * p.G >= 16 && idle && (full == 0 || (rest > 0 && 4 * rest <= slots));
   p.sk_tiles = 0;
   p.sk_grid = 0;
   if (p.streamk) {
-    const long long full = T / slots;
     const long long dp = full >= 2 ? (full - 1) * slots : 0;
     p.sk_tiles = (int)(T - dp);
     p.sk_grid = (int)std::max(1LL, std::min(slots, (long long)p.sk_tiles * p.G / 8));
@@ -855,7 +873,27 @@ GemmPlan gemm_plan(int b, int n, int m, int cus, bool w8) {
   } else {
     p.grid = (int)T;
   }
-  const long long max_sk = std::max(1LL, std::min((long long)kMaxWgPerCu * kMaxCUs, T * p.G / 8));
+}
+}  // namespace
+
+GemmPlan gemm_plan(int b, int n, int m, int cus, int fmt) {
+  static_assert(Cfg::TM == Cfg8::TM && Cfg::TN == Cfg8::TN && Cfg::TM == CfgF4::TM && Cfg::TN == CfgF4::TN &&
+                    Cfg::TM == CfgSk::TM && Cfg::TN == CfgSk::TN,
+                "one tiling for every setting");
+  constexpr int kMaxSkWgPerCu = std::max({CfgSk::WG_PER_CU, Cfg8::WG_PER_CU, CfgF4::WG_PER_CU});
+  const int ncu = cus > 0 ? cus : kMaxCUs;
+  GemmPlan p;
+  p.G = m / 64;
+  p.tiles_m = (b + Cfg::TM - 1) / Cfg::TM;
+  p.tiles_n = (n + Cfg::TN - 1) / Cfg::TN;
+  p.wg_per_cu = fmt == kFmtInt8 ? Cfg8::WG_PER_CU : fmt == kFmtFp4 ? CfgF4::WG_PER_CU : Cfg::WG_PER_CU;
+  plan_rounds(p, (long long)p.wg_per_cu * ncu);
+  if (fmt == kFmtInt4 && p.streamk) {
+    p.wg_per_cu = CfgSk::WG_PER_CU;
+    plan_rounds(p, (long long)p.wg_per_cu * ncu);
+  }
+  const long long T = (long long)p.tiles_m * p.tiles_n;
+  const long long max_sk = std::max(1LL, std::min((long long)kMaxSkWgPerCu * kMaxCUs, T * p.G / 8));
   p.partial_bytes = (size_t)max_sk * Cfg::TM * Cfg::TN * 4;
   p.ws_bytes = p.streamk || cus <= 0 ? p.partial_bytes + (size_t)max_sk * 8 : 0;
   return p;
@@ -884,7 +922,7 @@ int launch_gemm_up(const uint8_t* qx, const uint16_t* ascale, const float* z, co
 
 int launch_gemm8_up(const int8_t* qx, const uint16_t* ascale, const float* z, const svdq_w8a8_layer& L,
                     int b, void* y, int y_dtype, void* ws, void* stream) {
-  const GemmPlan plan = gemm_plan(b, L.n, L.m, device_cus(), true);
+  const GemmPlan plan = gemm_plan(b, L.n, L.m, device_cus(), kFmtInt8);
   const Operands o{reinterpret_cast<const uint8_t*>(L.qw), L.wscale, L.l2, L.bias, L.n, L.rank};
   const uint8_t* a = reinterpret_cast<const uint8_t*>(qx);
   hipStream_t st = (hipStream_t)stream;
@@ -894,7 +932,7 @@ int launch_gemm8_up(const int8_t* qx, const uint16_t* ascale, const float* z, co
 
 int launch_gemm_fp4_up(const uint8_t* qx, const uint8_t* ascale, const float* z, const svdq_fp4_layer& L, int b,
                        void* y, int y_dtype, void* ws, void* stream) {
-  const GemmPlan plan = gemm_plan(b, L.n, L.m, device_cus());
+  const GemmPlan plan = gemm_plan(b, L.n, L.m, device_cus(), kFmtFp4);
   const Operands o{L.qw, reinterpret_cast<const uint16_t*>(L.wscale), L.l2, L.bias, L.n, L.rank};
   const uint16_t* as = reinterpret_cast<const uint16_t*>(ascale);
   const float txw = L.t_x * L.t_w;  // powers of two: exact

@@ -129,12 +129,16 @@ struct GemmPlan {
   int streamk;          // 1 = hybrid schedule with a stream-K part
   int sk_tiles;         // tiles shared out by stream-K (linear tiles [0, sk_tiles))
   int sk_grid;          // stream-K workgroups (dispatched first)
+  int wg_per_cu;        // resident workgroups per CU of the kernel planned for
   size_t partial_bytes; // partial-sum area at the start of the workspace
   size_t ws_bytes;      // workspace this launch needs (0 for one tile per workgroup)
 };
+// Operand formats of the GEMM kernel body (INT4 codes, the 8-bit setting, the
+// NVFP4 setting); each has its own resident workgroups per CU.
+enum GemmFormat { kFmtInt4 = 0, kFmtInt8 = 1, kFmtFp4 = 2 };
 // cus <= 0 gives the device-independent upper bound used to size workspaces
-// (valid for both settings); w8 selects the 8-bit kernel's residency.
-GemmPlan gemm_plan(int b, int n, int m, int cus, bool w8 = false);
+// (valid for every format); fmt selects the kernel whose residency is planned.
+GemmPlan gemm_plan(int b, int n, int m, int cus, int fmt = kFmtInt4);
 int device_cus();
 int launch_gemm_up(const uint8_t* qx, const uint16_t* ascale, const float* z, const svdq_layer& L,
                    int b, void* y, int y_dtype, void* ws, void* stream);
