@@ -42,7 +42,9 @@ SCHEDULES = [
     # (b, n, m, setting, tiles, grid, stream-K workgroups, stream-K tiles, workgroups per CU)
     (4608, 9216, 3072, "int4", 2592, 2592, 0, 0, 3),      # 3/CU: last round 3/8 full, one tile per workgroup
     (4096, 4608, 1152, "int4", 1152, 1152, 0, 0, 3),      # 3/CU: last round half full
-    (4608, 3072, 12288, "int4", 864, 864, 0, 0, 2),       # 3/CU would split (1/8 full); 2/CU: 11/16 full
+    (4608, 3072, 12288, "int4", 864, 512, 512, 864, 2),   # G = 192: 3/CU splits (1/8 full); at 2/CU the
+                                                          # last round is 11/16 full but idle for 60 groups
+    (4608, 3072, 12288, "w8a8", 864, 512, 512, 864, 2),
     (4608, 9216, 3072, "w8a8", 2592, 2560, 512, 544, 2),  # 2/CU: 1/16 full, stream-K part then 4 full rounds
     (4608, 9216, 3072, "fp4", 2592, 2560, 512, 544, 2),
     (256, 21504, 3072, "int4", 336, 512, 512, 336, 2),    # under one round: stream-K at 2/CU

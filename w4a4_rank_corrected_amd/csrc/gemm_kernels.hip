@@ -482,9 +482,8 @@ __device__ __forceinline__ void gemm_up_body(
       }
     };
     // One group q of a buffer.  INT4: for each 16-row block bi, BJ MFMAs (one
-    // per 16-column block), whose results are applied by 8 * BJ FMAs (the
-    // other resident waves cover the MFMA latency).  8-bit: the MFMAs
-    // accumulate into the integer sums directly.
+    // per 16-column block), whose results are applied by 8 * BJ FMAs.  8-bit:
+    // the MFMAs accumulate into the integer sums directly.
     auto compute_group = [&](int buf, int q) {
       const uint8_t* as = &As[buf][q * TM * ROWB];
       const uint8_t* bs = &Bs[buf][q * TN * ROWB];
@@ -535,22 +534,36 @@ __device__ __forceinline__ void gemm_up_body(
           sw8[h] = *reinterpret_cast<const f16x8*>(reinterpret_cast<const _Float16*>(sc + TM) + WN * wn +
                                                    4 * BJ * c + 8 * h);
         const int rbase = WM * wm + r;
+        // an FMA needs its block's MFMA results: at two waves per SIMD the
+        // FMAs of block bi run after the MFMAs of block bi + 1 (results
+        // double-buffered) to cover the MFMA latency; at three the register
+        // budget holds one block's results and the other waves cover it
+        constexpr bool DB = C::WPE <= 2;
+        i32x4 d[DB ? 2 : 1][BJ];
+        float sxq[2], sng[2];
 #pragma unroll
-        for (int bi = 0; bi < BI; ++bi) {
-          const u32x4 Qa = *reinterpret_cast<const u32x4*>(as + (rbase + 16 * bi) * ROWB + cs);
-          const float sxq = sx4[bi], sng = -kMagic * sx4[bi];  // exact: 3 * 2^14 * sx
-          i32x4 d[BJ];
+        for (int bi = 0; bi <= BI; ++bi) {
+          const int cur = DB ? bi & 1 : 0, prev = DB ? cur ^ 1 : 0;
+          const int ab = DB ? bi - 1 : bi;  // the block whose results are applied
+          if (bi < BI) {
+            const u32x4 Qa = *reinterpret_cast<const u32x4*>(as + (rbase + 16 * bi) * ROWB + cs);
+            sxq[bi & 1] = sx4[bi];
+            sng[bi & 1] = -kMagic * sx4[bi];  // exact: 3 * 2^14 * sx
 #pragma unroll
-          for (int bj = 0; bj < BJ; ++bj)
-            d[bj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                __builtin_bit_cast(i32x4, Pb[bj]), __builtin_bit_cast(i32x4, Qa), magic, 0, 0, 0);
+            for (int bj = 0; bj < BJ; ++bj)
+              d[cur][bj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                  __builtin_bit_cast(i32x4, Pb[bj]), __builtin_bit_cast(i32x4, Qa), magic, 0, 0, 0);
+          }
+          if (ab >= 0 && ab < BI) {
+            const int rd = DB ? prev : cur;
 #pragma unroll
-          for (int bj = 0; bj < BJ; ++bj)
+            for (int bj = 0; bj < BJ; ++bj)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const float t = __builtin_fmaf(__int_as_float(d[bj][v]), sxq, sng);
-              acc[bi][bj][v] = __builtin_fmaf(t, (float)sw8[bj >> 1][4 * (bj & 1) + v], acc[bi][bj][v]);
-            }
+              for (int v = 0; v < 4; ++v) {
+                const float t = __builtin_fmaf(__int_as_float(d[rd][bj][v]), sxq[ab & 1], sng[ab & 1]);
+                acc[ab][bj][v] = __builtin_fmaf(t, (float)sw8[bj >> 1][4 * (bj & 1) + v], acc[ab][bj][v]);
+              }
+          }
         }
       }
     };
@@ -844,15 +857,17 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
 
 // Plan of the GEMM launch.  With T tiles of G groups and S = CUs * (resident
 // workgroups per CU of the kernel) slots, one tile per workgroup runs
-// ceil(T / S) rounds, the last one a fraction f of slots full.  Stream-K is
-// chosen when the idle time of that round, (1 - f) * G group-iterations per
-// slot, is at least 16 (splitting a tile costs a few) and either T < S or
-// f <= 1/4: then the tiles beyond the first floor(T / S) - 1 full rounds
+// ceil(T / S) rounds, the last one a fraction f of slots full, idle for
+// I = (1 - f) * G group-iterations per slot.  Stream-K is chosen when
+// I >= 16 (splitting a tile costs a few group-iterations) and T < S, f <= 1/4
+// or I >= 40: then the tiles beyond the first floor(T / S) - 1 full rounds
 // (between S and 2S of them, or all T when T < 2S) go to min(S, their
 // iterations / 8) stream-K workgroups, dispatched first, and the full rounds
-// follow one tile per workgroup.  A last round fuller than a quarter runs one
-// tile per workgroup: its workgroups finish faster on the emptier CUs, which
-// measured better than splitting tiles.  INT4 codes first try the
+// follow one tile per workgroup.  Otherwise one tile per workgroup: a last
+// round more than a quarter full finishes faster on its emptier CUs, which
+// measured better than splitting short tiles (FLUX QKV, G = 48, at three
+// workgroups per CU: I = 30) but not long ones (FLUX fc2, G = 192, at two per
+// CU: I = 60).  INT4 codes first try the
 // three-per-CU kernel (one tile per workgroup only); if that residency calls
 // for stream-K, the two-per-CU kernel is planned by the same rule.  The
 // workspace bound assumes the largest gfx950 part (256 CUs) and the largest
@@ -861,8 +876,9 @@ namespace {
 void plan_rounds(GemmPlan& p, long long slots) {
   const long long T = (long long)p.tiles_m * p.tiles_n;
   const long long full = T / slots, rest = T - full * slots;  // rest / slots = f
-  const bool idle = (slots - rest) * p.G >= 16 * slots;      // (1 - f) G >= 16
-  p.streamk = T * p.G >= 16 && idle && (full == 0 || (rest > 0 && 4 * rest <= slots));
+  const long long idle = (slots - rest) * p.G;               // (1 - f) G, in units of 1/slots
+  p.streamk = T * p.G >= 16 && idle >= 16 * slots &&
+              (full == 0 || (rest > 0 && (4 * rest <= slots || idle >= 40 * slots)));
   p.sk_tiles = 0;
   p.sk_grid = 0;
   if (p.streamk) {
