@@ -356,18 +356,38 @@ def test_streamk_splits_deterministic_and_match_oracle(S, b, m, n):
     assert err <= 1e-4
 
 
-def test_hybrid_schedule_matches_oracle(S):
-    """A shape whose schedule runs a stream-K part and then full rounds of one
-    tile per workgroup (found with the library's own schedule query, so it
-    holds for the device's CU count): bit-identical repeats, and rows from
-    both parts match the oracle."""
-    m, n = 1536, 5120
-    b = next((128 * tm - 37 for tm in range(1, 256)
-              if 0 < S.svdq_gemm_schedule(128 * tm, n, m)["stream_k_workgroups"]
-              < S.svdq_gemm_schedule(128 * tm, n, m)["grid"]), None)
-    assert b is not None, "no hybrid schedule for this device"
+# The INT4 GEMM has four schedules (three-per-CU kernel with one tile per
+# workgroup; two-per-CU kernel with one tile per workgroup, all tiles by
+# stream-K, or a stream-K part followed by full rounds).  Each case finds the
+# smallest b x n (m = 1536) that the library schedules that way on this device.
+SCHEDULE_KINDS = {
+    "one_tile_3cu": lambda s: s["workgroups_per_cu"] == 3,
+    "one_tile_2cu": lambda s: s["workgroups_per_cu"] == 2 and s["stream_k_workgroups"] == 0,
+    "stream_k": lambda s: 0 < s["stream_k_workgroups"] == s["grid"],
+    "hybrid": lambda s: 0 < s["stream_k_workgroups"] < s["grid"],
+}
+
+
+def _shape_for(S, kind, m=1536):
+    best = None
+    for tm in range(1, 48):
+        for tn in range(1, 64):
+            if best is not None and tm * tn >= best[0]:
+                break
+            if SCHEDULE_KINDS[kind](S.svdq_gemm_schedule(128 * tm, 128 * tn, m)):
+                best = (tm * tn, tm, tn)
+    assert best is not None, f"no {kind} schedule for this device"
+    return 128 * best[1] - 37, 128 * best[2] - 5, m   # ragged rows and columns, same tiles
+
+
+@pytest.mark.parametrize("kind", list(SCHEDULE_KINDS))
+def test_schedule_kinds_match_oracle(S, kind):
+    """Every schedule the planner can choose: bit-identical repeats, and rows
+    spread over the whole output (every tile row) against the oracle."""
+    b, n, m = _shape_for(S, kind)
     sch = S.svdq_gemm_schedule(b, n, m)
-    _say(f"hybrid schedule b={b} m={m} n={n}: {sch}")
+    assert SCHEDULE_KINDS[kind](sch)
+    _say(f"schedule {kind}: b={b} m={m} n={n}: {sch}")
     rng = np.random.default_rng(11)
     xb = workloads.random_bf16_bits(rng, (b, m), 1.5)
     x = LY.bf16_bits_to_f32(xb)
