@@ -218,8 +218,10 @@ using Cfg = GemmCfg<128, 128, 64, 64, 3, 1>;
 // INT4 launches with a stream-K part: two workgroups per CU, loads two groups
 // ahead (no spills at 256 registers).
 using CfgSk = GemmCfg<128, 128, 64, 64, 2, 2>;
-// 8-bit codes: no per-group VALU work, so a group's compute is short and the
-// loads run four groups ahead to cover the memory latency.
+// 8-bit codes: no per-group VALU work, so a group's compute is short.  One
+// tile per workgroup: three workgroups per CU (140 registers), loads two
+// groups ahead; stream-K launches: two per CU, loads four groups ahead.
+using Cfg8Dp = GemmCfg<128, 128, 64, 64, 3, 2>;
 using Cfg8 = GemmCfg<128, 128, 64, 64, 2, 4>;
 // NVFP4: 16-byte code pieces dequantized to f16 rows (64 KB of LDS per
 // workgroup, so two workgroups per CU).
@@ -790,15 +792,15 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
                                           yout, sk, txw);
 }
 
-template <class C, bool OUT_BF16>
+template <class C, bool OUT_BF16, bool SK>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void gemm_w8a8_up_kernel(
     const uint8_t* __restrict__ qx, const uint16_t* __restrict__ ascale,
     const float* __restrict__ z, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, int b, int n, int G, int rank, int tiles_m, int tiles_n,
     void* __restrict__ yout, StreamK sk, float txw) {
-  gemm_up_body<C, OUT_BF16, kFmtInt8>(qx, ascale, z, qw, wscale, l2t, bias, b, n, G, rank, tiles_m, tiles_n, yout,
-                                      sk, txw);
+  gemm_up_body<C, OUT_BF16, kFmtInt8, SK>(qx, ascale, z, qw, wscale, l2t, bias, b, n, G, rank, tiles_m, tiles_n,
+                                          yout, sk, txw);
 }
 
 template <class C, bool OUT_BF16>
@@ -834,10 +836,16 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
     sk.flags = reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(ws) + plan.partial_bytes);
     sk.epoch = next_launch_epoch();
   }
-  if constexpr (FMT == kFmtInt8)
-    hipLaunchKernelGGL((gemm_w8a8_up_kernel<Cfg8, OUT_BF16>), dim3((unsigned)plan.grid), dim3(Cfg8::NT), 0, st,
-                       qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
-                       plan.tiles_n, y, sk, txw);
+  if constexpr (FMT == kFmtInt8) {
+    if (plan.wg_per_cu == Cfg8Dp::WG_PER_CU && !plan.streamk)
+      hipLaunchKernelGGL((gemm_w8a8_up_kernel<Cfg8Dp, OUT_BF16, false>), dim3((unsigned)plan.grid), dim3(Cfg8Dp::NT),
+                         0, st, qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
+                         plan.tiles_n, y, sk, txw);
+    else
+      hipLaunchKernelGGL((gemm_w8a8_up_kernel<Cfg8, OUT_BF16, true>), dim3((unsigned)plan.grid), dim3(Cfg8::NT), 0,
+                         st, qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
+                         plan.tiles_n, y, sk, txw);
+  }
   else if constexpr (FMT == kFmtFp4)
     hipLaunchKernelGGL((gemm_fp4_up_kernel<CfgF4, OUT_BF16>), dim3((unsigned)plan.grid), dim3(CfgF4::NT), 0, st,
                        qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
@@ -867,9 +875,9 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
 // round more than a quarter full finishes faster on its emptier CUs, which
 // measured better than splitting short tiles (FLUX QKV, G = 48, at three
 // workgroups per CU: I = 30) but not long ones (FLUX fc2, G = 192, at two per
-// CU: I = 60).  INT4 codes first try the
-// three-per-CU kernel (one tile per workgroup only); if that residency calls
-// for stream-K, the two-per-CU kernel is planned by the same rule.  The
+// CU: I = 60).  INT4 and 8-bit codes first try their three-per-CU kernels
+// (one tile per workgroup only); if that residency calls for stream-K, the
+// two-per-CU kernel is planned by the same rule.  The
 // workspace bound assumes the largest gfx950 part (256 CUs) and the largest
 // stream-K residency, so it does not depend on the device or the format.
 namespace {
@@ -894,7 +902,7 @@ void plan_rounds(GemmPlan& p, long long slots) {
 
 GemmPlan gemm_plan(int b, int n, int m, int cus, int fmt) {
   static_assert(Cfg::TM == Cfg8::TM && Cfg::TN == Cfg8::TN && Cfg::TM == CfgF4::TM && Cfg::TN == CfgF4::TN &&
-                    Cfg::TM == CfgSk::TM && Cfg::TN == CfgSk::TN,
+                    Cfg::TM == CfgSk::TM && Cfg::TN == CfgSk::TN && Cfg::TM == Cfg8Dp::TM && Cfg::TN == Cfg8Dp::TN,
                 "one tiling for every setting");
   constexpr int kMaxSkWgPerCu = std::max({CfgSk::WG_PER_CU, Cfg8::WG_PER_CU, CfgF4::WG_PER_CU});
   const int ncu = cus > 0 ? cus : kMaxCUs;
@@ -902,10 +910,10 @@ GemmPlan gemm_plan(int b, int n, int m, int cus, int fmt) {
   p.G = m / 64;
   p.tiles_m = (b + Cfg::TM - 1) / Cfg::TM;
   p.tiles_n = (n + Cfg::TN - 1) / Cfg::TN;
-  p.wg_per_cu = fmt == kFmtInt8 ? Cfg8::WG_PER_CU : fmt == kFmtFp4 ? CfgF4::WG_PER_CU : Cfg::WG_PER_CU;
+  p.wg_per_cu = fmt == kFmtInt8 ? Cfg8Dp::WG_PER_CU : fmt == kFmtFp4 ? CfgF4::WG_PER_CU : Cfg::WG_PER_CU;
   plan_rounds(p, (long long)p.wg_per_cu * ncu);
-  if (fmt == kFmtInt4 && p.streamk) {
-    p.wg_per_cu = CfgSk::WG_PER_CU;
+  if (fmt != kFmtFp4 && p.streamk) {
+    p.wg_per_cu = fmt == kFmtInt8 ? Cfg8::WG_PER_CU : CfgSk::WG_PER_CU;
     plan_rounds(p, (long long)p.wg_per_cu * ncu);
   }
   const long long T = (long long)p.tiles_m * p.tiles_n;
