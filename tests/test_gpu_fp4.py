@@ -229,6 +229,38 @@ def test_fp4_gemm_exact_products(S, b, m, n):
     assert torch.equal(ys[0], ys[1])
 
 
+@pytest.mark.parametrize("m", [256, 4096])
+def test_fp4_gemm_every_block_scale(S, m):
+    """Every nonzero E4M3 block scale (codes 1..126, subnormals included) on
+    both operands: row i of X and column j of W use one scale each, so every
+    partial sum is s_i s_j (at most 8 significant bits) times a multiple of 1/4
+    below 2^14, exact in fp32, and the result equals the oracle's bit for bit.
+    m = 256 (all codes) runs one tile per workgroup; m = 4096 (codes of
+    magnitude <= 1, to keep the sums below 2^14) splits the tiles by
+    stream-K."""
+    b, n = 126, 130
+    _say(f"fp4 gemm every block scale m={m}")
+    rng = np.random.default_rng(m)
+    pool = np.arange(16, dtype=np.uint8) if m <= 256 else np.array([0, 1, 2, 8, 9, 10], np.uint8)
+    qx = rng.choice(pool, (b, m))
+    qw = rng.choice(pool, (n, m))
+    cx, cw = O.e2m1_values(qx), O.e2m1_values(qw)
+    assert (np.abs(cx) @ np.abs(cw).T).max() < 2 ** 14
+    codes_x = (np.arange(b) % 126 + 1).astype(np.uint8)
+    codes_w = (np.arange(n) % 126 + 1).astype(np.uint8)
+    sbx = np.repeat(O.e4m3_from_bits(codes_x)[:, None], m // 16, axis=1)
+    sbw = np.repeat(O.e4m3_from_bits(codes_w)[:, None], m // 16, axis=1)
+    y_ref = O.dequantize_fp4_blocks(qx, sbx) @ O.dequantize_fp4_blocks(qw, sbw).T
+    host = {"m": m, "n": n, "rank": 0, "t_x": 1.0, "t_w": 1.0, "qw": LY.pack_fp4_codes(qw),
+            "wscale": LY.pack_fp4_scales(O.e4m3_bits(sbw)), "l1": np.zeros((0, m), np.uint16),
+            "l2": np.zeros((n, 0), np.uint16), "smooth_inv": np.ones(m, np.float32)}
+    dl = S.DeviceLayerFp4(host, smoothing=False)
+    y = S.svdq_fp4_gemm_lowrank_up(dev_u8(LY.pack_fp4_codes(qx)), dev_u8(LY.pack_fp4_scales(O.e4m3_bits(sbx))),
+                                   None, dl, b, torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), y_ref.astype(np.float32))
+
+
 # ---------------------------------------------------------------------------
 # whole NVFP4 layer
 # ---------------------------------------------------------------------------

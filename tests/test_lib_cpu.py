@@ -47,7 +47,9 @@ SCHEDULES = [
     (4608, 3072, 12288, "w8a8", 864, 512, 512, 864, 2),
     (4608, 9216, 3072, "w8a8", 2592, 2592, 0, 0, 3),      # the 8-bit setting plans like INT4
     (4608, 5760, 3072, "w8a8", 1620, 1536, 512, 596, 2),  # 3/CU: 0.11 full; 2/CU: 0.16 full -> hybrid
-    (4608, 9216, 3072, "fp4", 2592, 2560, 512, 544, 2),
+    (4608, 9216, 3072, "fp4", 2592, 2592, 0, 0, 3),
+    (4608, 3072, 12288, "fp4", 864, 864, 0, 0, 3),        # NVFP4 splits only tiles under one round
+    (256, 21504, 3072, "fp4", 336, 512, 512, 336, 2),
     (256, 21504, 3072, "int4", 336, 512, 512, 336, 2),    # under one round: stream-K at 2/CU
     (4992, 5120, 1536, "int4", 1560, 1536, 512, 536, 2),  # hybrid: 536 tiles by stream-K, then 2 rounds
     (4608, 3072, 1024, "int4", 864, 864, 0, 0, 3),        # G = 16: too few groups to split

@@ -41,9 +41,8 @@
 //   already interleave).
 //
 // Schedules (tile = TM x TN outputs over all G groups; slots = the resident
-// workgroups of all CUs: three per CU for INT4 codes with one tile per
-// workgroup, two for INT4 launches with a stream-K part and for the 8-bit and
-// NVFP4 settings):
+// workgroups of all CUs: three per CU for launches with one tile per
+// workgroup, two for launches with a stream-K part):
 //   * one tile per workgroup, unless the tiles leave the last round of slots
 //     at most a quarter full;
 //   * otherwise a hybrid: the tiles of the last one or two rounds are shared
@@ -223,8 +222,10 @@ using CfgSk = GemmCfg<128, 128, 64, 64, 2, 2>;
 // groups ahead; stream-K launches: two per CU, loads four groups ahead.
 using Cfg8Dp = GemmCfg<128, 128, 64, 64, 3, 2>;
 using Cfg8 = GemmCfg<128, 128, 64, 64, 2, 4>;
-// NVFP4: 16-byte code pieces dequantized to f16 rows (64 KB of LDS per
-// workgroup, so two workgroups per CU).
+// NVFP4 (packed records in LDS, 20 KB per workgroup): like INT4, a
+// stream-K-free build at three workgroups per CU for one tile per workgroup,
+// and two per CU for stream-K launches.
+using CfgF4Dp = GemmCfg<128, 128, 64, 64, 3, 1>;
 using CfgF4 = GemmCfg<128, 128, 64, 64, 2, 2>;
 
 // Cache policy of the stream-K partials: sc1 = device-coherent.
@@ -241,14 +242,32 @@ struct StreamK {
   unsigned long long epoch;       // this launch's epoch
 };
 
-// E4M3 block-scale byte -> (2^e, M) with value = M 2^e, M in [1, 2) (M = 0 for
-// a zero scale): the FP4 -> f16 conversion applies only the exponent of its
-// scale operand, the mantissa M is multiplied in afterwards.
-__device__ __forceinline__ void e4m3_split(uint32_t bits, float& p2, _Float16& M) {
+// Non-negative E4M3 block-scale byte -> its value as fp16 bits (exact: E4M3
+// values are 2^-9 .. 448 with at most 4 significant bits).
+// Branch-free: a normal E4M3 value keeps its fields (exponent rebiased from 7
+// to 15, mantissa moved up 7 bits); a subnormal one, mant * 2^-9, is
+// converted through fp32.
+__device__ __forceinline__ uint32_t e4m3_to_f16_bits(uint32_t bits) {
   const uint32_t ex = (bits >> 3) & 15u, mant = bits & 7u;
-  const float v = ex ? __uint_as_float(((ex + 120u) << 23) | (mant << 20)) : (float)mant * 0.001953125f;
-  p2 = __uint_as_float(__float_as_uint(v) & 0x7F800000u);
-  M = v > 0.0f ? (_Float16)__uint_as_float((__float_as_uint(v) & 0x007FFFFFu) | 0x3F800000u) : (_Float16)0.0f;
+  const uint32_t normal = ((bits & 0x7Fu) << 7) + 0x2000u;
+  const uint32_t sub = __builtin_bit_cast(uint16_t, (_Float16)((float)mant * 0.001953125f));
+  return ex ? normal : sub;
+}
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Eight FP4 codes (one 32-bit word, the even channel in each byte's low
+// nibble) -> the f16 operand code * s, in channel order.  The conversion at
+// unit scale is exact, and so is the product: an E2M1 value times an E4M3
+// scale has at most 6 significant bits and lies in 2^-10 .. 2688.
+__device__ __forceinline__ f16x8 fp4_operand(uint32_t w, _Float16 s) {
+  const f16x2 ss = {s, s};
+  const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+  const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+  const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+  const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
+  return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
 // The kernel body for three operand formats (FMT):
@@ -264,8 +283,9 @@ __device__ __forceinline__ void e4m3_split(uint32_t bits, float& p2, _Float16& M
 //  * kFmtFp4: the NVFP4 setting, FP4 E2M1 codes in the INT4 record layout and
 //    one FP8 E4M3 scale per 16 channels (records [m/64][rows][4] bytes).  A
 //    code times its block scale is exact in f16 (at most 6 significant bits,
-//    magnitudes 2^-10 .. 2688), so staging dequantizes the codes once per
-//    workgroup into f16 LDS rows and the f16 MFMAs accumulate sum_k x^ w^ in
+//    magnitudes 2^-10 .. 2688).  LDS holds the packed code records and the
+//    block scales as fp16; each wave dequantizes its MFMA operands in
+//    registers (fp4_operand), and the f16 MFMAs accumulate sum_k x^ w^ in
 //    fp32; the two power-of-two tensor scales (txw = t_x t_w) are applied
 //    once in the epilogue, exactly.
 template <class C, bool OUT_BF16, int FMT, bool SK = true>
@@ -281,11 +301,14 @@ __device__ __forceinline__ void gemm_up_body(
   static_assert(!F4 || (C::A_BYTES == 16 && C::B_BYTES == 16), "FP4 records: 16-byte staging pieces");
   constexpr int TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN, NT = C::NT;
   constexpr int BI = C::BI, BJ = C::BJ;
-  constexpr int ROWB = F4 ? 128 : C::ROWB;  // LDS bytes per row and group (f16 rows for FP4)
+  constexpr int ROWB = F4 ? 32 : C::ROWB;  // LDS bytes per row and group (packed records for FP4)
   constexpr int KG = C::KG;
   // per buffer: KG groups of TM (TN) rows
   __shared__ __align__(16) uint8_t As[2][KG * TM * ROWB];
   __shared__ __align__(16) uint8_t Bs[2][KG * TN * ROWB];
+  // FP4: per buffer and group, the four block scales (fp16) of each of the TM
+  // activation rows, then of the TN weight columns
+  __shared__ __align__(16) uint16_t F4s[2][F4 ? KG * (TM + TN) * 4 : 4];
   // per buffer and group: [sx/256 (TM floats) | sw (TN fp16)], each in the
   // order in which a lane reads its rows and columns (see store_stage); no
   // per-group scales with 8-bit or FP4 codes
@@ -300,11 +323,10 @@ __device__ __forceinline__ void gemm_up_body(
   // this lane's 16-byte chunk of an MFMA operand row in LDS (rows of a block
   // start at multiples of 16, so the row's swizzle is that of r)
   const int cs = 16 * (c ^ chunk_swz(r));
-  // FP4: 128-byte f16 rows of eight 16-byte chunks, chunk j at position
-  // j ^ f4_swz(row) (free of bank conflicts for the operand reads with 8 or 16
-  // lanes per cycle); this lane reads chunks c and 4 + c of its row
-  const int f4r = (r & 7) ^ ((r >> 3) & 1);
-  const int cs0 = 16 * (c ^ f4r), cs1 = 16 * ((4 + c) ^ f4r);
+  // FP4: 32-byte packed rows, word j at position j ^ 4 in rows with bit 3 set
+  // (the operand reads of 16 rows then hit 64 distinct banks); this lane reads
+  // word 4 kh + c of its rows (channels 32 kh + 8c .. +7, block 2 kh + c/2)
+  const int f4w0 = c ^ (4 * ((r >> 3) & 1)), f4w1 = (4 + c) ^ (4 * ((r >> 3) & 1));
   constexpr int REC = W8 ? 64 : 32;  // record bytes of one row in one group
   constexpr int AB = W8 ? 2 * C::A_BYTES : C::A_BYTES, BB = W8 ? 2 * C::B_BYTES : C::B_BYTES;
   const int a_row = tid * AB / REC, a_w0 = (tid * AB % REC) / 4;
@@ -432,28 +454,14 @@ __device__ __forceinline__ void gemm_up_body(
     // wave's row block sits at BI r + bi (one 16-byte read gives a lane its BI
     // rows), column l = 16 bj + 4 c + v of a wave's column block at
     // 4 BJ c + 4 bj + v (BJ/2 16-byte reads give a lane its 4 BJ columns).
-    // FP4: 16 code bytes (channels 32h .. 32h+31 of the record, h = w0 / 4)
-    // -> four 16-byte f16 chunks 4h .. 4h+3 of the LDS row; words 0-1 use
-    // block 2h's scale (byte 0 of sc), words 2-3 block 2h+1's (byte 1)
-    auto dequant_fp4 = [&](uint8_t* row, int ridx, int w0, const Piece<16>& pc, uint32_t sc) {
-      typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-      const int swz = (ridx & 7) ^ ((ridx >> 3) & 1);
-      float p2[2];
-      _Float16 M[2];
-      e4m3_split(sc & 0xFFu, p2[0], M[0]);
-      e4m3_split((sc >> 8) & 0xFFu, p2[1], M[1]);
-#pragma unroll
-      for (int wd = 0; wd < 4; ++wd) {
-        const int k = wd >> 1;
-        const f16x2 mm = {M[k], M[k]};
-        const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(pc.w[wd], p2[k], 0) * mm;
-        const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(pc.w[wd], p2[k], 1) * mm;
-        const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(pc.w[wd], p2[k], 2) * mm;
-        const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(pc.w[wd], p2[k], 3) * mm;
-        *reinterpret_cast<u32x4*>(row + 16 * (((w0 & 4) + wd) ^ swz)) =
-            u32x4{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
-                  __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
-      }
+    // FP4: a 16-byte code piece (words w0 .. w0+3 of the record) is copied to
+    // its row (swizzled as above), and its two E4M3 block scales (blocks
+    // w0/2 and w0/2 + 1: bytes 0 and 1 of sc) go to the row's scale slots as
+    // fp16, with one 32-bit store
+    auto stage_fp4 = [&](uint8_t* row, int ridx, int w0, const Piece<16>& pc, uint32_t sc, uint16_t* srow) {
+      *reinterpret_cast<u32x4*>(row + 4 * (w0 ^ (4 * ((ridx >> 3) & 1)))) = u32x4{pc.w[0], pc.w[1], pc.w[2], pc.w[3]};
+      reinterpret_cast<uint32_t*>(srow)[w0 >> 2] =
+          e4m3_to_f16_bits(sc & 0xFFu) | (e4m3_to_f16_bits((sc >> 8) & 0xFFu) << 16);
     };
     auto store_stage = [&](int buf, const Stage& st) {
 #pragma unroll
@@ -461,8 +469,9 @@ __device__ __forceinline__ void gemm_up_body(
         uint8_t* as = &As[buf][(q * TM + a_row) * ROWB];
         uint8_t* bs = &Bs[buf][(q * TN + b_col) * ROWB];
         if constexpr (F4) {
-          dequant_fp4(as, a_row, a_w0, st.a[q], st.s[q]);
-          dequant_fp4(bs, b_col, b_w0, st.w[q], st.s2[q]);
+          uint16_t* fs = &F4s[buf][q * (TM + TN) * 4];
+          stage_fp4(as, a_row, a_w0, st.a[q], st.s[q], fs + a_row * 4);
+          stage_fp4(bs, b_col, b_w0, st.w[q], st.s2[q], fs + (TM + b_col) * 4);
         } else if constexpr (W8) {
           copy_piece(as, chunk_swz(a_row), a_w0, st.a[q]);
           copy_piece(bs, chunk_swz(b_col), b_w0, st.w[q]);
@@ -490,21 +499,25 @@ __device__ __forceinline__ void gemm_up_body(
       const uint8_t* as = &As[buf][q * TM * ROWB];
       const uint8_t* bs = &Bs[buf][q * TN * ROWB];
       if constexpr (F4) {
-        typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+        const uint32_t* aw = reinterpret_cast<const uint32_t*>(as);
+        const uint32_t* bw = reinterpret_cast<const uint32_t*>(bs);
+        const _Float16* fs = reinterpret_cast<const _Float16*>(&F4s[buf][q * (TM + TN) * 4]);
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {  // channels 0-31, then 32-63 of the group
-          const int co = kh ? cs1 : cs0;
-          u32x4 Pb[BJ];
+          const int wo = kh ? f4w1 : f4w0, blk = 2 * kh + (c >> 1);
+          f16x8 Pb[BJ];
 #pragma unroll
-          for (int bj = 0; bj < BJ; ++bj)
-            Pb[bj] = *reinterpret_cast<const u32x4*>(bs + (WN * wn + 16 * bj + r) * ROWB + co);
+          for (int bj = 0; bj < BJ; ++bj) {
+            const int row = WN * wn + 16 * bj + r;
+            Pb[bj] = fp4_operand(bw[row * 8 + wo], fs[(TM + row) * 4 + blk]);
+          }
 #pragma unroll
           for (int bi = 0; bi < BI; ++bi) {
-            const u32x4 Qa = *reinterpret_cast<const u32x4*>(as + (WM * wm + 16 * bi + r) * ROWB + co);
+            const int row = WM * wm + 16 * bi + r;
+            const f16x8 Qa = fp4_operand(aw[row * 8 + wo], fs[row * 4 + blk]);
 #pragma unroll
             for (int bj = 0; bj < BJ; ++bj)
-              acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                  __builtin_bit_cast(f16x8, Pb[bj]), __builtin_bit_cast(f16x8, Qa), acc[bi][bj], 0, 0, 0);
+              acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Pb[bj], Qa, acc[bi][bj], 0, 0, 0);
           }
         }
       } else if constexpr (W8) {
@@ -803,15 +816,15 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
                                           yout, sk, txw);
 }
 
-template <class C, bool OUT_BF16>
+template <class C, bool OUT_BF16, bool SK>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void gemm_fp4_up_kernel(
     const uint8_t* __restrict__ qx, const uint16_t* __restrict__ ascale,
     const float* __restrict__ z, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, int b, int n, int G, int rank, int tiles_m, int tiles_n,
     void* __restrict__ yout, StreamK sk, float txw) {
-  gemm_up_body<C, OUT_BF16, kFmtFp4>(qx, ascale, z, qw, wscale, l2t, bias, b, n, G, rank, tiles_m, tiles_n, yout,
-                                     sk, txw);
+  gemm_up_body<C, OUT_BF16, kFmtFp4, SK>(qx, ascale, z, qw, wscale, l2t, bias, b, n, G, rank, tiles_m, tiles_n,
+                                         yout, sk, txw);
 }
 
 int g_num_cus = 0;
@@ -846,10 +859,16 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
                          st, qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
                          plan.tiles_n, y, sk, txw);
   }
-  else if constexpr (FMT == kFmtFp4)
-    hipLaunchKernelGGL((gemm_fp4_up_kernel<CfgF4, OUT_BF16>), dim3((unsigned)plan.grid), dim3(CfgF4::NT), 0, st,
-                       qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
-                       plan.tiles_n, y, sk, txw);
+  else if constexpr (FMT == kFmtFp4) {
+    if (plan.wg_per_cu == CfgF4Dp::WG_PER_CU && !plan.streamk)
+      hipLaunchKernelGGL((gemm_fp4_up_kernel<CfgF4Dp, OUT_BF16, false>), dim3((unsigned)plan.grid),
+                         dim3(CfgF4Dp::NT), 0, st, qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G,
+                         L.rank, plan.tiles_m, plan.tiles_n, y, sk, txw);
+    else
+      hipLaunchKernelGGL((gemm_fp4_up_kernel<CfgF4, OUT_BF16, true>), dim3((unsigned)plan.grid), dim3(CfgF4::NT), 0,
+                         st, qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
+                         plan.tiles_n, y, sk, txw);
+  }
   else if (plan.wg_per_cu == Cfg::WG_PER_CU && !plan.streamk)
     hipLaunchKernelGGL((gemm_w4a4_up_kernel<Cfg, OUT_BF16, false>), dim3((unsigned)plan.grid), dim3(Cfg::NT), 0, st,
                        qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
@@ -875,18 +894,18 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
 // round more than a quarter full finishes faster on its emptier CUs, which
 // measured better than splitting short tiles (FLUX QKV, G = 48, at three
 // workgroups per CU: I = 30) but not long ones (FLUX fc2, G = 192, at two per
-// CU: I = 60).  INT4 and 8-bit codes first try their three-per-CU kernels
-// (one tile per workgroup only); if that residency calls for stream-K, the
-// two-per-CU kernel is planned by the same rule.  The
+// CU: I = 60).  Every setting first tries its three-per-CU kernel (one tile
+// per workgroup only); if that residency calls for stream-K, the two-per-CU
+// kernel is planned by the same rule.  NVFP4 uses stream-K only for T < S.  The
 // workspace bound assumes the largest gfx950 part (256 CUs) and the largest
 // stream-K residency, so it does not depend on the device or the format.
 namespace {
-void plan_rounds(GemmPlan& p, long long slots) {
+void plan_rounds(GemmPlan& p, long long slots, bool split_last_round) {
   const long long T = (long long)p.tiles_m * p.tiles_n;
   const long long full = T / slots, rest = T - full * slots;  // rest / slots = f
   const long long idle = (slots - rest) * p.G;               // (1 - f) G, in units of 1/slots
   p.streamk = T * p.G >= 16 && idle >= 16 * slots &&
-              (full == 0 || (rest > 0 && (4 * rest <= slots || idle >= 40 * slots)));
+              (full == 0 || (split_last_round && rest > 0 && (4 * rest <= slots || idle >= 40 * slots)));
   p.sk_tiles = 0;
   p.sk_grid = 0;
   if (p.streamk) {
@@ -902,7 +921,8 @@ void plan_rounds(GemmPlan& p, long long slots) {
 
 GemmPlan gemm_plan(int b, int n, int m, int cus, int fmt) {
   static_assert(Cfg::TM == Cfg8::TM && Cfg::TN == Cfg8::TN && Cfg::TM == CfgF4::TM && Cfg::TN == CfgF4::TN &&
-                    Cfg::TM == CfgSk::TM && Cfg::TN == CfgSk::TN && Cfg::TM == Cfg8Dp::TM && Cfg::TN == Cfg8Dp::TN,
+                    Cfg::TM == CfgSk::TM && Cfg::TN == CfgSk::TN && Cfg::TM == Cfg8Dp::TM && Cfg::TN == Cfg8Dp::TN &&
+                    Cfg::TM == CfgF4Dp::TM && Cfg::TN == CfgF4Dp::TN,
                 "one tiling for every setting");
   constexpr int kMaxSkWgPerCu = std::max({CfgSk::WG_PER_CU, Cfg8::WG_PER_CU, CfgF4::WG_PER_CU});
   const int ncu = cus > 0 ? cus : kMaxCUs;
@@ -910,11 +930,16 @@ GemmPlan gemm_plan(int b, int n, int m, int cus, int fmt) {
   p.G = m / 64;
   p.tiles_m = (b + Cfg::TM - 1) / Cfg::TM;
   p.tiles_n = (n + Cfg::TN - 1) / Cfg::TN;
-  p.wg_per_cu = fmt == kFmtInt8 ? Cfg8Dp::WG_PER_CU : fmt == kFmtFp4 ? CfgF4::WG_PER_CU : Cfg::WG_PER_CU;
-  plan_rounds(p, (long long)p.wg_per_cu * ncu);
-  if (fmt != kFmtFp4 && p.streamk) {
-    p.wg_per_cu = fmt == kFmtInt8 ? Cfg8::WG_PER_CU : CfgSk::WG_PER_CU;
-    plan_rounds(p, (long long)p.wg_per_cu * ncu);
+  p.wg_per_cu = fmt == kFmtInt8 ? Cfg8Dp::WG_PER_CU : fmt == kFmtFp4 ? CfgF4Dp::WG_PER_CU : Cfg::WG_PER_CU;
+  // NVFP4 splits only tiles that do not fill one round: its two-per-CU build,
+  // whose operand dequantization then runs at two waves per SIMD, measured
+  // slower than one tile per workgroup at three per CU (FLUX fc2 and single
+  // out: 7-8 %)
+  const bool split_last_round = fmt != kFmtFp4;
+  plan_rounds(p, (long long)p.wg_per_cu * ncu, split_last_round);
+  if (p.streamk) {
+    p.wg_per_cu = fmt == kFmtInt8 ? Cfg8::WG_PER_CU : fmt == kFmtFp4 ? CfgF4::WG_PER_CU : CfgSk::WG_PER_CU;
+    plan_rounds(p, (long long)p.wg_per_cu * ncu, split_last_round);
   }
   const long long T = (long long)p.tiles_m * p.tiles_n;
   const long long max_sk = std::max(1LL, std::min((long long)kMaxSkWgPerCu * kMaxCUs, T * p.G / 8));
