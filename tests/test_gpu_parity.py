@@ -320,6 +320,38 @@ def test_linear_parity(S, name, out):
         assert err <= 1e-4
 
 
+def _random_shape(k):
+    rng = np.random.default_rng(1000 + k)
+    b = int(rng.integers(1, 600))
+    m = 64 * int(rng.integers(1, 41))
+    n = int(rng.integers(1, 600))
+    rank = int(rng.integers(0, min(64, m, n) + 1))
+    return rng, b, m, n, rank, bool(rng.integers(0, 2))
+
+
+@pytest.mark.parametrize("k", range(16))
+def test_linear_random_shapes(S, k):
+    """Seeded random layers (ragged b and n, any group count and rank up to
+    64, with and without bias) on whatever schedule the planner picks: fp32
+    output within 1e-4 of the oracle, and repeat calls bit-identical."""
+    rng, b, m, n, rank, with_bias = _random_shape(k)
+    _say(f"random layer {k}: b={b} m={m} n={n} rank={rank} bias={with_bias} "
+         f"schedule={S.svdq_gemm_schedule(b, n, m)}")
+    xb = workloads.random_bf16_bits(rng, (b, m), 1.5)
+    x = LY.bf16_bits_to_f32(xb)
+    lay = _oracle_layer(rng, m, n, rank, x)
+    bias_v = O.bf16_from_f32(rng.standard_normal(n).astype(np.float32) * 0.1) if with_bias else None
+    ref = O.linear(x, lay, bias=bias_v)["y"]
+    dl = device_layer(S, lay, None if bias_v is None else LY.f32_to_bf16_bits(bias_v))
+    xd = dev_bf16(xb)
+    ys = [S.svdq_linear(xd, dl, torch.float32) for _ in range(2)]
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1])
+    err = rel(ys[0].cpu().numpy(), ref)
+    _say(f"  rel err {err:.3e}")
+    assert err <= 1e-4
+
+
 def test_linear_equals_standalone_kernels_bitwise(S):
     """svdq_linear = act kernel then GEMM kernel; Z partials are summed in the
     same order in both routes, so the outputs agree bit for bit."""
