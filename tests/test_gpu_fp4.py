@@ -342,3 +342,35 @@ def test_fp4_linear_full_size_sampled(S):
     assert np.array_equal(LY.unpack_fp4_codes(qd[:, ridx, :].cpu().numpy()), ref["qx"])
     assert np.array_equal(LY.unpack_fp4_scales(asd[:, ridx, :].cpu().numpy()), O.e4m3_bits(ref["sbx"]))
     assert rel(zd.cpu().numpy()[rows], ref["z"]) <= Z_TOL
+
+
+# ---------------------------------------------------------------------------
+# seeded random layers on whatever schedule the planner picks
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("k", range(8))
+def test_fp4_linear_random_shapes(S, k):
+    """Seeded random NVFP4 layers (ragged b and n, any group count and rank up to
+    64, with and without bias): fp32 output within 1e-4 of the oracle, and
+    repeat calls bit-identical."""
+    rng = np.random.default_rng(3000 + k)
+    b, m, n = int(rng.integers(1, 600)), 64 * int(rng.integers(1, 41)), int(rng.integers(1, 600))
+    rank = int(rng.integers(0, min(64, m, n) + 1))
+    with_bias = bool(rng.integers(0, 2))
+    _say(f"random NVFP4 layer {k}: b={b} m={m} n={n} rank={rank} bias={with_bias} "
+         f"schedule={S.svdq_gemm_schedule(b, n, m, 'fp4')}")
+    xb = workloads.random_bf16_bits(rng, (b, m), 1.5)
+    x = LY.bf16_bits_to_f32(xb)
+    w = (rng.standard_normal((m, n)) / np.sqrt(m)).astype(np.float32)
+    w[rng.choice(m, max(1, m // 64), replace=False)] *= 8
+    lay = O.prepare_weights_fp4(w, O.act_amax(x), rank)
+    bias_v = O.bf16_from_f32(rng.standard_normal(n).astype(np.float32) * 0.1) if with_bias else None
+    ref = O.linear_fp4(x, lay, bias=bias_v)["y"]
+    dl = device_layer_fp4(S, lay, None if bias_v is None else LY.f32_to_bf16_bits(bias_v))
+    xd = dev_bf16(xb)
+    ys = [S.svdq_fp4_linear(xd, dl, torch.float32) for _ in range(2)]
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1])
+    err = rel(ys[0].cpu().numpy(), ref)
+    _say(f"  rel err {err:.3e}")
+    assert err <= 1e-4
