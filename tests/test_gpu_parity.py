@@ -501,6 +501,40 @@ def test_linear_empty_batch(S):
         assert y.shape == (0, 256)
 
 
+def test_binding_rejects_mismatched_tensors(S):
+    """Tensors whose device, dtype or shape do not match the layer raise before
+    any launch (a kernel would otherwise read or write out of bounds)."""
+    xb, x, lay = _linear_case("tiny")
+    dl = device_layer(S, lay)
+    xd = dev_bf16(xb)
+    b, m = xd.shape
+    y_ok = S.svdq_linear(xd, dl, torch.float32)
+    torch.cuda.synchronize()
+    with pytest.raises(ValueError, match="out_dtype"):
+        S.svdq_linear(xd, dl, torch.float16)
+    with pytest.raises(ValueError, match="dtype"):
+        S.svdq_linear(xd, dl, torch.float32, y=torch.empty((b, dl.n), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError, match="shape"):
+        S.svdq_linear(xd, dl, torch.float32, y=torch.empty((b, dl.n - 1), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError, match="dtype"):
+        S.svdq_linear(xd.float(), dl)
+    with pytest.raises(ValueError, match="channels"):
+        S.svdq_linear(xd[:, :m - 64].contiguous(), dl)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        S.svdq_linear(xd.cpu(), dl)
+    qx, asc, z = S.svdq_quantize_act_lowrank_down(xd, dl.smooth_inv, dl.l1, dl.rank)
+    with pytest.raises(ValueError, match="qx has shape"):
+        S.svdq_gemm_w4a4_lowrank_up(qx, asc, z, dl, b - 1)
+    with pytest.raises(ValueError, match="z has shape"):
+        S.svdq_gemm_w4a4_lowrank_up(qx, asc, z[:, :1].contiguous(), dl)
+    with pytest.raises(ValueError, match="qx has shape"):
+        S.svdq_quantize_act_lowrank_down(xd, dl.smooth_inv, dl.l1, dl.rank, qx=qx[:, 1:].contiguous())
+    # the valid calls still agree after the rejected ones
+    y2 = S.svdq_gemm_w4a4_lowrank_up(qx, asc, z, dl, None, torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y_ok)
+
+
 # ---------------------------------------------------------------------------
 # full-size layers, sampled rows (the configurations the benchmark times)
 # ---------------------------------------------------------------------------

@@ -607,3 +607,112 @@ def test_fp4_prepare_validation_errors():
     with pytest.raises(B.SvdqError) as e:
         S.svdq_fp4_prepare_weights(np.ones((96, 32), np.float32), None, 4)
     assert e.value.status == B.SVDQ_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# the Python binding checks every device tensor before a call reaches the
+# library (a host tensor, a wrong dtype or shape would be read or written out
+# of bounds by a kernel)
+# ---------------------------------------------------------------------------
+
+class _FakeGpuTensor:
+    """Stands in for a GPU tensor (device, dtype, shape) on a machine without one."""
+
+    def __init__(self, shape, dtype, device="cuda:0", contiguous=True):
+        import torch
+        self.shape, self.dtype, self.device = tuple(shape), dtype, torch.device(device)
+        self.is_cuda, self._c = True, contiguous
+
+    def is_contiguous(self):
+        return self._c
+
+    def dim(self):
+        return len(self.shape)
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    import types
+    x = torch.zeros((16, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        S.svdq_linear(x, None)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        S.svdq_linear_unfused(x, None)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        S.svdq_w8a8_linear(x, None)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        S.svdq_fp4_linear(x, None)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        S.svdq_calibrate_act_amax(x)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        S.svdq_quantize_act_lowrank_down(x, None, None, 0)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        S.svdq_w8a8_quantize_act_lowrank_down(x, None, None, 0)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        S.svdq_fp4_quantize_act_lowrank_down(x, None, None, 0, 1.0)
+    lay = types.SimpleNamespace(m=128, n=64, rank=0)
+    qx = torch.zeros((2, 16, 32), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        S.svdq_gemm_w4a4_lowrank_up(qx, None, None, lay)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        S.svdq_fp4_gemm_lowrank_up(qx, None, None, lay)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        S.svdq_w8a8_gemm_lowrank_up(qx.view(torch.int8), None, None, lay)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        S.DeviceLayer.from_tensors(128, 64, 0, qx, None)
+
+
+def test_binding_checks_dtype_shape_and_output_type():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError, match="out_dtype"):
+        B._out_code(torch.float16)
+    assert B._out_code(None) == B.SVDQ_OUT_BF16
+    assert B._out_code(torch.bfloat16) == B.SVDQ_OUT_BF16
+    assert B._out_code(torch.float32) == B.SVDQ_OUT_F32
+    dev = torch.device("cuda:0")
+    # a preallocated output must match the requested dtype and [b][n]
+    with pytest.raises(ValueError, match="dtype"):
+        B._output(_FakeGpuTensor((16, 64), torch.bfloat16), 16, 64, torch.float32, dev)
+    with pytest.raises(ValueError, match="shape"):
+        B._output(_FakeGpuTensor((16, 32), torch.float32), 16, 64, torch.float32, dev)
+    y = _FakeGpuTensor((16, 64), torch.float32)
+    assert B._output(y, 16, 64, torch.float32, dev) == (y, B.SVDQ_OUT_F32)
+    with pytest.raises(ValueError, match="contiguous"):
+        B._output(_FakeGpuTensor((16, 64), torch.float32, contiguous=False), 16, 64, torch.float32, dev)
+    with pytest.raises(ValueError, match="expected cuda:0"):
+        B._output(_FakeGpuTensor((16, 64), torch.float32, device="cuda:1"), 16, 64, torch.float32, dev)
+    # activations are bf16 matrices
+    with pytest.raises(ValueError, match="dtype"):
+        B._input(_FakeGpuTensor((16, 128), torch.float32))
+    with pytest.raises(ValueError, match="2-D"):
+        B._input(_FakeGpuTensor((2, 16, 128), torch.bfloat16))
+    assert tuple(B._input(_FakeGpuTensor((16, 128), torch.bfloat16))) == (16, 128)
+    # GEMM inputs follow the layer: [m/64][b][record] codes, per-group scales, z [b][rank]
+    import types
+    lay = types.SimpleNamespace(m=128, n=64, rank=8, qw=_FakeGpuTensor((2, 64, 32), torch.uint8))
+    qx = _FakeGpuTensor((2, 16, 32), torch.uint8)
+    asc = _FakeGpuTensor((2, 16), torch.float16)
+    z = _FakeGpuTensor((16, 8), torch.float32)
+    assert B._gemm_operands(qx, asc, z, lay, None, True, 32, torch.uint8, torch.float16) == 16
+    with pytest.raises(ValueError, match="qx has shape"):
+        B._gemm_operands(qx, asc, z, lay, 8, True, 32, torch.uint8, torch.float16)
+    with pytest.raises(ValueError, match="qx has shape"):
+        B._gemm_operands(_FakeGpuTensor((3, 16, 32), torch.uint8), asc, z, lay, None, True, 32, torch.uint8,
+                         torch.float16)
+    with pytest.raises(ValueError, match="ascale has shape"):
+        B._gemm_operands(qx, _FakeGpuTensor((2, 15), torch.float16), z, lay, None, True, 32, torch.uint8,
+                         torch.float16)
+    with pytest.raises(ValueError, match="z has shape"):
+        B._gemm_operands(qx, asc, _FakeGpuTensor((16, 4), torch.float32), lay, None, True, 32, torch.uint8,
+                         torch.float16)
+    with pytest.raises(ValueError, match="ascale has dtype"):
+        B._gemm_operands(qx, _FakeGpuTensor((2, 16), torch.float32), z, lay, None, True, 32, torch.uint8,
+                         torch.float16)
+    # the 8-bit setting: one scale per token; NVFP4: four E4M3 bytes per row and group
+    assert B._gemm_operands(_FakeGpuTensor((2, 16, 64), torch.int8), _FakeGpuTensor((16,), torch.float16), z, lay,
+                            None, False, 64, torch.int8, torch.float16) == 16
+    assert B._gemm_operands(qx, _FakeGpuTensor((2, 16, 4), torch.uint8), z, lay, None, True, 32, torch.uint8,
+                            torch.uint8, (4,)) == 16
+    # host arrays and tensors must be contiguous (a ValueError, not an assert)
+    with pytest.raises(ValueError, match="contiguous"):
+        B._ptr(np.zeros((4, 4), np.float32)[:, ::2])

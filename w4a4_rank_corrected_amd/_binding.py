@@ -143,10 +143,69 @@ def _ptr(a) -> Optional[int]:
     if a is None:
         return None
     if isinstance(a, np.ndarray):
-        assert a.flags["C_CONTIGUOUS"], "host arrays must be C-contiguous"
+        if not a.flags["C_CONTIGUOUS"]:
+            raise ValueError("host arrays must be C-contiguous")
         return a.ctypes.data
-    assert a.is_contiguous(), "tensors must be contiguous"
+    if not a.is_contiguous():
+        raise ValueError("tensors must be contiguous")
     return a.data_ptr()
+
+
+# The device entry points take raw addresses, so a tensor of the wrong device,
+# dtype or shape would make a kernel read or write out of bounds.  Every tensor
+# a device call receives is checked here first (None passes where the C ABI
+# allows NULL).
+def _dev(t, name: str, dtype=None, shape=None, device=None) -> None:
+    if t is None:
+        return
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _input(x, name: str = "x"):
+    """A bf16 GPU activation matrix [b][m]; returns (b, m)."""
+    import torch
+    _dev(x, name, torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError(f"{name} must be 2-D [b][m], got shape {tuple(x.shape)}")
+    return x.shape
+
+
+def _out_code(out_dtype) -> int:
+    import torch
+    if out_dtype is None or out_dtype == torch.bfloat16:
+        return SVDQ_OUT_BF16
+    if out_dtype == torch.float32:
+        return SVDQ_OUT_F32
+    raise ValueError(f"out_dtype must be torch.bfloat16 or torch.float32, not {out_dtype}")
+
+
+def _output(y, b: int, n: int, out_dtype, device):
+    """The output tensor [b][n] (allocated if None) and its C-ABI dtype code."""
+    import torch
+    code = _out_code(out_dtype)
+    dt = torch.bfloat16 if code == SVDQ_OUT_BF16 else torch.float32
+    if y is None:
+        return torch.empty((b, n), dtype=dt, device=device), code
+    _dev(y, "y", dt, (b, n), device)
+    return y, code
+
+
+def _workspace(ws, need: int, device):
+    """The workspace (allocated if None; at least one byte) and its size in bytes."""
+    import torch
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _dev(ws, "workspace", device=device)
+    return ws, ws.numel() * ws.element_size()
 
 
 def _stream(stream) -> Optional[int]:
@@ -263,9 +322,10 @@ def svdq_append_lora(l1: Optional[np.ndarray], l2: Optional[np.ndarray], m: int,
 def svdq_calibrate_act_amax(x, amax=None, accumulate: bool = False, stream=None):
     """x: bf16 CUDA tensor [b][m]; returns fp32 amax [m] (allocated if None)."""
     import torch
-    b, m = x.shape
+    b, m = _input(x)
     if amax is None:
         amax = torch.empty(m, dtype=torch.float32, device=x.device)
+    _dev(amax, "amax", torch.float32, (m,), x.device)
     _check(lib().svdq_calibrate_act_amax(_ptr(x), b, m, _ptr(amax), int(accumulate), _stream(stream)))
     return amax
 
@@ -278,7 +338,7 @@ def svdq_quantize_act_lowrank_down(x, smooth_inv, l1, rank: int, group: int = SV
                                    qx=None, ascale=None, z=None, workspace=None, stream=None):
     """Returns (qx uint8 [m/64][b][32], ascale fp16 [m/64][b], z fp32 [b][rank] or None)."""
     import torch
-    b, m = x.shape
+    b, m = _input(x)
     dev = x.device
     G = m // SVDQ_GROUP
     if qx is None:
@@ -287,14 +347,42 @@ def svdq_quantize_act_lowrank_down(x, smooth_inv, l1, rank: int, group: int = SV
         ascale = torch.empty((G, b), dtype=torch.float16, device=dev)
     if z is None and rank > 0:
         z = torch.empty((b, rank), dtype=torch.float32, device=dev)
+    _act_operands(dev, m, rank, smooth_inv, l1, qx, (G, b, 32), torch.uint8, ascale, (G, b), torch.float16, z, b)
     need = svdq_act_workspace_size(b, m, rank)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", device=dev)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().svdq_quantize_act_lowrank_down(
         _ptr(x), b, m, rank, group, _ptr(smooth_inv), _ptr(l1), _ptr(qx), _ptr(ascale), _ptr(z),
         _ptr(workspace), wsb, _stream(stream)))
     return qx, ascale, z
+
+
+def _act_operands(dev, m, rank, smooth_inv, l1, qx, qx_shape, qx_dtype, ascale, as_shape, as_dtype, z, b):
+    import torch
+    _dev(smooth_inv, "smooth_inv", torch.float32, (m,), dev)
+    _dev(l1, "l1", torch.bfloat16, (rank, m), dev)
+    _dev(qx, "qx", qx_dtype, qx_shape, dev)
+    _dev(ascale, "ascale", as_dtype, as_shape, dev)
+    _dev(z, "z", torch.float32, (b, rank), dev)
+
+
+def _gemm_operands(qx, ascale, z, layer, b, per_group_scales: bool, record: int, qx_dtype, as_dtype,
+                   as_tail=()):
+    """Checks the GEMM's activation-side inputs against the layer; returns b."""
+    import torch
+    G = layer.m // SVDQ_GROUP
+    _dev(qx, "qx", qx_dtype)
+    if b is None:
+        if qx.dim() != 3:
+            raise ValueError(f"qx must be 3-D [m/64][b][{record}], got shape {tuple(qx.shape)}")
+        b = qx.shape[1]
+    dev = layer.qw.device
+    _dev(qx, "qx", qx_dtype, (G, b, record), dev)
+    _dev(ascale, "ascale", as_dtype, ((G, b) if per_group_scales else (b,)) + tuple(as_tail), dev)
+    _dev(z, "z", torch.float32, (b, layer.rank), dev)
+    return b
 
 
 class DeviceLayer:
@@ -317,6 +405,15 @@ class DeviceLayer:
 
     @classmethod
     def from_tensors(cls, m, n, rank, qw, wscale, l1=None, l2=None, smooth_inv=None, bias=None):
+        import torch
+        dev = qw.device
+        G = m // SVDQ_GROUP
+        _dev(qw, "qw", torch.uint8, (G, n, 32), dev)
+        _dev(wscale, "wscale", torch.float16, (G, n), dev)
+        _dev(l1, "l1", torch.bfloat16, (rank, m), dev)
+        _dev(l2, "l2", torch.bfloat16, (n, rank), dev)
+        _dev(smooth_inv, "smooth_inv", torch.float32, (m,), dev)
+        _dev(bias, "bias", torch.bfloat16, (n,), dev)
         self = cls.__new__(cls)
         self.m, self.n, self.rank = m, n, rank
         self.qw, self.wscale, self.l1, self.l2 = qw, wscale, l1, l2
@@ -347,16 +444,9 @@ def svdq_gemm_schedule(b: int, n: int, m: int, setting: str = "int4") -> dict:
 def svdq_gemm_w4a4_lowrank_up(qx, ascale, z, layer: DeviceLayer, b: Optional[int] = None,
                               out_dtype=None, y=None, workspace=None, stream=None):
     import torch
-    if b is None:
-        b = qx.shape[1]
-    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
-    code = SVDQ_OUT_BF16 if out_dtype == torch.bfloat16 else SVDQ_OUT_F32
-    if y is None:
-        y = torch.empty((b, layer.n), dtype=out_dtype, device=qx.device)
-    if workspace is None:
-        need = svdq_gemm_workspace_size(b, layer.n, layer.m)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=qx.device)
-    wsb = workspace.numel() * workspace.element_size()
+    b = _gemm_operands(qx, ascale, z, layer, b, True, 32, torch.uint8, torch.float16)
+    y, code = _output(y, b, layer.n, out_dtype, qx.device)
+    workspace, wsb = _workspace(workspace, svdq_gemm_workspace_size(b, layer.n, layer.m), qx.device)
     _check(lib().svdq_gemm_w4a4_lowrank_up(_ptr(qx), _ptr(ascale), _ptr(z), ctypes.byref(layer.struct),
                                            b, _ptr(y), code, _ptr(workspace), wsb, _stream(stream)))
     return y
@@ -367,16 +457,12 @@ def svdq_linear_workspace_size(b: int, m: int, n: int, rank: int, group: int = S
 
 
 def svdq_linear(x, layer: DeviceLayer, out_dtype=None, y=None, workspace=None, stream=None):
-    import torch
-    b, m = x.shape
-    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
-    code = SVDQ_OUT_BF16 if out_dtype == torch.bfloat16 else SVDQ_OUT_F32
-    if y is None:
-        y = torch.empty((b, layer.n), dtype=out_dtype, device=x.device)
-    if workspace is None:
-        need = svdq_linear_workspace_size(b, m, layer.n, layer.rank)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    wsb = workspace.numel() * workspace.element_size()
+    b, m = _input(x)
+    _dev(x, "x", device=layer.qw.device)
+    if m != layer.m:
+        raise ValueError(f"x has {m} channels, the layer {layer.m}")
+    y, code = _output(y, b, layer.n, out_dtype, x.device)
+    workspace, wsb = _workspace(workspace, svdq_linear_workspace_size(b, m, layer.n, layer.rank), x.device)
     _check(lib().svdq_linear(_ptr(x), ctypes.byref(layer.struct), b, _ptr(y), code, _ptr(workspace),
                              wsb, _stream(stream)))
     return y
@@ -388,16 +474,12 @@ def svdq_linear_unfused_workspace_size(b: int, m: int, n: int, rank: int, group:
 
 def svdq_linear_unfused(x, layer: DeviceLayer, out_dtype=None, y=None, workspace=None, stream=None):
     """The layer without the kernel fusion (five launches), for A/B timing."""
-    import torch
-    b, m = x.shape
-    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
-    code = SVDQ_OUT_BF16 if out_dtype == torch.bfloat16 else SVDQ_OUT_F32
-    if y is None:
-        y = torch.empty((b, layer.n), dtype=out_dtype, device=x.device)
-    if workspace is None:
-        need = svdq_linear_unfused_workspace_size(b, m, layer.n, layer.rank)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    wsb = workspace.numel() * workspace.element_size()
+    b, m = _input(x)
+    _dev(x, "x", device=layer.qw.device)
+    if m != layer.m:
+        raise ValueError(f"x has {m} channels, the layer {layer.m}")
+    y, code = _output(y, b, layer.n, out_dtype, x.device)
+    workspace, wsb = _workspace(workspace, svdq_linear_unfused_workspace_size(b, m, layer.n, layer.rank), x.device)
     _check(lib().svdq_linear_unfused(_ptr(x), ctypes.byref(layer.struct), b, _ptr(y), code,
                                      _ptr(workspace), wsb, _stream(stream)))
     return y
@@ -459,17 +541,20 @@ def svdq_w8a8_quantize_act_lowrank_down(x, smooth_inv, l1, rank: int, qx=None, a
                                         workspace=None, stream=None):
     """Returns (qx int8 [m/64][b][64], ascale fp16 [b], z fp32 [b][rank] or None)."""
     import torch
-    b, m = x.shape
+    b, m = _input(x)
     dev = x.device
+    G = m // SVDQ_GROUP
     if qx is None:
-        qx = torch.empty((m // SVDQ_GROUP, b, 64), dtype=torch.int8, device=dev)
+        qx = torch.empty((G, b, 64), dtype=torch.int8, device=dev)
     if ascale is None:
         ascale = torch.empty(b, dtype=torch.float16, device=dev)
     if z is None and rank > 0:
         z = torch.empty((b, rank), dtype=torch.float32, device=dev)
+    _act_operands(dev, m, rank, smooth_inv, l1, qx, (G, b, 64), torch.int8, ascale, (b,), torch.float16, z, b)
     need = svdq_w8a8_act_workspace_size(b, m, rank)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", device=dev)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().svdq_w8a8_quantize_act_lowrank_down(
         _ptr(x), b, m, rank, _ptr(smooth_inv), _ptr(l1), _ptr(qx), _ptr(ascale), _ptr(z),
@@ -484,16 +569,9 @@ def svdq_w8a8_gemm_workspace_size(b: int, n: int, m: int) -> int:
 def svdq_w8a8_gemm_lowrank_up(qx, ascale, z, layer: DeviceLayer8, b: Optional[int] = None, out_dtype=None,
                               y=None, workspace=None, stream=None):
     import torch
-    if b is None:
-        b = qx.shape[1]
-    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
-    code = SVDQ_OUT_BF16 if out_dtype == torch.bfloat16 else SVDQ_OUT_F32
-    if y is None:
-        y = torch.empty((b, layer.n), dtype=out_dtype, device=qx.device)
-    if workspace is None:
-        need = svdq_w8a8_gemm_workspace_size(b, layer.n, layer.m)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=qx.device)
-    wsb = workspace.numel() * workspace.element_size()
+    b = _gemm_operands(qx, ascale, z, layer, b, False, 64, torch.int8, torch.float16)
+    y, code = _output(y, b, layer.n, out_dtype, qx.device)
+    workspace, wsb = _workspace(workspace, svdq_w8a8_gemm_workspace_size(b, layer.n, layer.m), qx.device)
     _check(lib().svdq_w8a8_gemm_lowrank_up(_ptr(qx), _ptr(ascale), _ptr(z), ctypes.byref(layer.struct), b,
                                            _ptr(y), code, _ptr(workspace), wsb, _stream(stream)))
     return y
@@ -504,16 +582,12 @@ def svdq_w8a8_linear_workspace_size(b: int, m: int, n: int, rank: int) -> int:
 
 
 def svdq_w8a8_linear(x, layer: DeviceLayer8, out_dtype=None, y=None, workspace=None, stream=None):
-    import torch
-    b, m = x.shape
-    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
-    code = SVDQ_OUT_BF16 if out_dtype == torch.bfloat16 else SVDQ_OUT_F32
-    if y is None:
-        y = torch.empty((b, layer.n), dtype=out_dtype, device=x.device)
-    if workspace is None:
-        need = svdq_w8a8_linear_workspace_size(b, m, layer.n, layer.rank)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    wsb = workspace.numel() * workspace.element_size()
+    b, m = _input(x)
+    _dev(x, "x", device=layer.qw.device)
+    if m != layer.m:
+        raise ValueError(f"x has {m} channels, the layer {layer.m}")
+    y, code = _output(y, b, layer.n, out_dtype, x.device)
+    workspace, wsb = _workspace(workspace, svdq_w8a8_linear_workspace_size(b, m, layer.n, layer.rank), x.device)
     _check(lib().svdq_w8a8_linear(_ptr(x), ctypes.byref(layer.struct), b, _ptr(y), code, _ptr(workspace),
                                   wsb, _stream(stream)))
     return y
@@ -581,7 +655,7 @@ def svdq_fp4_quantize_act_lowrank_down(x, smooth_inv, l1, rank: int, t_x: float,
                                        workspace=None, stream=None):
     """Returns (qx uint8 [m/64][b][32], ascale uint8 [m/64][b][4], z fp32 [b][rank] or None)."""
     import torch
-    b, m = x.shape
+    b, m = _input(x)
     dev = x.device
     G = m // SVDQ_GROUP
     if qx is None:
@@ -590,9 +664,11 @@ def svdq_fp4_quantize_act_lowrank_down(x, smooth_inv, l1, rank: int, t_x: float,
         ascale = torch.empty((G, b, 4), dtype=torch.uint8, device=dev)
     if z is None and rank > 0:
         z = torch.empty((b, rank), dtype=torch.float32, device=dev)
+    _act_operands(dev, m, rank, smooth_inv, l1, qx, (G, b, 32), torch.uint8, ascale, (G, b, 4), torch.uint8, z, b)
     need = svdq_fp4_act_workspace_size(b, m, rank)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", device=dev)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().svdq_fp4_quantize_act_lowrank_down(
         _ptr(x), b, m, rank, _ptr(smooth_inv), _ptr(l1), float(t_x), _ptr(qx), _ptr(ascale), _ptr(z),
@@ -607,16 +683,9 @@ def svdq_fp4_gemm_workspace_size(b: int, n: int, m: int) -> int:
 def svdq_fp4_gemm_lowrank_up(qx, ascale, z, layer: DeviceLayerFp4, b: Optional[int] = None, out_dtype=None,
                              y=None, workspace=None, stream=None):
     import torch
-    if b is None:
-        b = qx.shape[1]
-    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
-    code = SVDQ_OUT_BF16 if out_dtype == torch.bfloat16 else SVDQ_OUT_F32
-    if y is None:
-        y = torch.empty((b, layer.n), dtype=out_dtype, device=qx.device)
-    if workspace is None:
-        need = svdq_fp4_gemm_workspace_size(b, layer.n, layer.m)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=qx.device)
-    wsb = workspace.numel() * workspace.element_size()
+    b = _gemm_operands(qx, ascale, z, layer, b, True, 32, torch.uint8, torch.uint8, (4,))
+    y, code = _output(y, b, layer.n, out_dtype, qx.device)
+    workspace, wsb = _workspace(workspace, svdq_fp4_gemm_workspace_size(b, layer.n, layer.m), qx.device)
     _check(lib().svdq_fp4_gemm_lowrank_up(_ptr(qx), _ptr(ascale), _ptr(z), ctypes.byref(layer.struct), b,
                                           _ptr(y), code, _ptr(workspace), wsb, _stream(stream)))
     return y
@@ -627,16 +696,12 @@ def svdq_fp4_linear_workspace_size(b: int, m: int, n: int, rank: int) -> int:
 
 
 def svdq_fp4_linear(x, layer: DeviceLayerFp4, out_dtype=None, y=None, workspace=None, stream=None):
-    import torch
-    b, m = x.shape
-    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
-    code = SVDQ_OUT_BF16 if out_dtype == torch.bfloat16 else SVDQ_OUT_F32
-    if y is None:
-        y = torch.empty((b, layer.n), dtype=out_dtype, device=x.device)
-    if workspace is None:
-        need = svdq_fp4_linear_workspace_size(b, m, layer.n, layer.rank)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    wsb = workspace.numel() * workspace.element_size()
+    b, m = _input(x)
+    _dev(x, "x", device=layer.qw.device)
+    if m != layer.m:
+        raise ValueError(f"x has {m} channels, the layer {layer.m}")
+    y, code = _output(y, b, layer.n, out_dtype, x.device)
+    workspace, wsb = _workspace(workspace, svdq_fp4_linear_workspace_size(b, m, layer.n, layer.rank), x.device)
     _check(lib().svdq_fp4_linear(_ptr(x), ctypes.byref(layer.struct), b, _ptr(y), code, _ptr(workspace),
                                  wsb, _stream(stream)))
     return y
