@@ -162,17 +162,28 @@ __device__ __forceinline__ void unrolled(std::integer_sequence<int, U...>, F&& f
   (f(std::integral_constant<int, U>{}), ...);
 }
 
-// Linear tile index -> (tile row, tile column), in bands of 4 tile-rows
-// (column-major inside a band), so that tiles with nearby indices share
-// activation and weight records.
+// Linear tile index -> (tile row, tile column), so that tiles with nearby
+// indices share activation and weight records.  Each XCD runs a contiguous
+// range of linear tiles (dp_tile), and its L2 keeps the records that range
+// re-reads most.
+//  * Row bands (COLS = false): bands of 4 tile-rows, column-major inside.  An
+//    XCD keeps its few activation rows and streams the weight columns.
+//  * Column bands (COLS = true): bands of ceil(tiles_n / 8) tile-columns,
+//    row-major inside.  An XCD keeps its eighth of the weight columns and
+//    streams the activation rows.  Against row bands, measured on gfx950:
+//    2-3 % faster with the stream-K build (FLUX fc2 and single-block out),
+//    but 1-4 % slower with the one-tile build (FLUX QKV, despite 26 % less
+//    HBM fetch), which therefore keeps row bands.
+template <bool COLS>
 __device__ __forceinline__ void band_tile(int t, int tiles_m, int tiles_n, int& ti, int& tj) {
-  constexpr int GM = 4;
-  const int band = t / (GM * tiles_n);
-  const int first = band * GM;
-  const int gm = min(tiles_m - first, GM);
-  const int in_band = t - band * GM * tiles_n;
-  ti = first + in_band % gm;
-  tj = in_band / gm;
+  const int along = COLS ? tiles_n : tiles_m, across = COLS ? tiles_m : tiles_n;
+  const int GB = COLS ? max(1, (tiles_n + 7) >> 3) : 4;
+  const int band = t / (GB * across);
+  const int first = band * GB;
+  const int gb = min(along - first, GB);
+  const int in_band = t - band * GB * across;
+  (COLS ? tj : ti) = first + in_band % gb;
+  (COLS ? ti : tj) = in_band / gb;
 }
 
 // Workgroup d of `count` one-tile workgroups -> linear tile base + t.
@@ -297,6 +308,7 @@ __device__ __forceinline__ void gemm_up_body(
     void* __restrict__ yout, StreamK sk, float txw) {
   constexpr bool W8 = FMT == kFmtInt8, F4 = FMT == kFmtFp4;
   constexpr bool POST = W8 || F4;  // scales and the low-rank branch after the main loop
+  constexpr bool kColBands = SK && FMT == kFmtInt4;  // tile order (band_tile)
   static_assert(!W8 || (2 * C::A_BYTES == 32 && 2 * C::B_BYTES == 32), "8-bit records: 32-byte staging pieces");
   static_assert(!F4 || (C::A_BYTES == 16 && C::B_BYTES == 16), "FP4 records: 16-byte staging pieces");
   constexpr int TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN, NT = C::NT;
@@ -703,7 +715,7 @@ __device__ __forceinline__ void gemm_up_body(
   if (!SK || (int)blockIdx.x >= sk.P) {  // one tile per workgroup
     const int T = tiles_m * tiles_n;
     int ti, tj;
-    band_tile(dp_tile((int)blockIdx.x - sk.P, T - sk.T, sk.T), tiles_m, tiles_n, ti, tj);
+    band_tile<kColBands>(dp_tile((int)blockIdx.x - sk.P, T - sk.T, sk.T), tiles_m, tiles_n, ti, tj);
     zero_acc();
     if constexpr (!POST) lowrank(ti * TM, tj * TN);
     main_branch(ti * TM, tj * TN, 0, G);
@@ -725,7 +737,7 @@ __device__ __forceinline__ void gemm_up_body(
     const long long lo = u0 > ts ? u0 : ts;
     const int g0 = (int)(lo - ts), g1 = (int)(u - ts);
     int ti, tj;
-    band_tile((int)t, tiles_m, tiles_n, ti, tj);
+    band_tile<kColBands>((int)t, tiles_m, tiles_n, ti, tj);
     const int i0 = ti * TM, j0 = tj * TN;
     zero_acc();
     if (!POST && g1 == G) lowrank(i0, j0);  // the tile's last groups carry the low-rank branch
