@@ -28,6 +28,8 @@ Extra modes (used with rocprofv3 runs):
                              read by the JSON line's roofline.traffic;
   --trace-summary DIR        summarize a --kernel-trace --stats run of this
                              script (same --workload/--steps/--warmup);
+  --cpu-threads N            time the oracle baseline on at most N BLAS threads
+                             (default: all the process may use);
   --prep-refine [WORKLOADS]  preparation with a search over migration
                              strengths and factor refinement against the
                              plain preparation: layer-output error on held-out
@@ -296,14 +298,12 @@ def load_traffic(workload):
 # oracle baseline
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(inp, cfg, rows):
-    """Time the oracle's linear on the first `rows` rows of the workload."""
+def cpu_baseline(inp, cfg, rows, max_threads=0):
+    """Time the oracle's linear on the first `rows` rows of the workload (its
+    BLAS on at most `max_threads` threads when that is > 0; the oracle's
+    preparation, which is not timed, always uses every thread)."""
+    import contextlib
     from oracle import svdq_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
     x = inp["x"]
     log(f"cpu_baseline: oracle preparation (ARPACK SVD) for {cfg.name}")
     lay = O.prepare_weights(inp["w"], O.act_amax(x), cfg.rank, svd="arpack")
@@ -312,18 +312,28 @@ def cpu_baseline(inp, cfg, rows):
                                  inp["lora_scale"])
         lay = dict(lay, l1=l1p, l2=l2p)
     xs = x[:rows]
-    O.linear(xs[: min(rows, 64)], lay)  # warm-up
-    times = []
-    for _ in range(3):
-        t0 = time.perf_counter()
-        O.linear(xs, lay)
-        times.append(time.perf_counter() - t0)
+    limit = contextlib.nullcontext()
+    if max_threads > 0:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=max_threads)
+    with limit:
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        except Exception:  # pragma: no cover
+            threads = len(os.sched_getaffinity(0))
+        O.linear(xs[: min(rows, 64)], lay)  # warm-up
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            O.linear(xs, lay)
+            times.append(time.perf_counter() - t0)
     dt = float(np.median(times))
     ops = 2.0 * rows * cfg.m * cfg.n
-    log(f"cpu_baseline: {rows} rows, median {dt:.2f} s of 3 runs, {threads} threads")
+    log(f"cpu_baseline: {rows} rows, median {dt:.3g} s of 3 runs, {threads} threads")
     return {"value": ops / dt / 1e12, "unit": "TOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"oracle linear (numpy fp64: quantize, Z, dequantized dgemm, up-projection) on "
-                      f"{rows} of {x.shape[0]} rows of {cfg.name}; median of 3 runs = {dt:.2f} s; "
+                      f"{rows} of {x.shape[0]} rows of {cfg.name}; median of 3 runs = {dt:.3g} s; "
                       f"oracle preparation (SVD) excluded"}
 
 
@@ -617,6 +627,8 @@ def main():
     ap.add_argument("--out", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--rank", type=int, default=None, help="override the SVD rank (0 = bare W4A4)")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows for the oracle timing (0 = all)")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="BLAS threads for the oracle timing (0 = all the process may use)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-check", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
@@ -823,7 +835,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(sets[0]["inp"], cfg,
-                                           min(args.cpu_rows, b) if args.cpu_rows else b)
+                                           min(args.cpu_rows, b) if args.cpu_rows else b, args.cpu_threads)
     print(json.dumps(res), flush=True)
 
 
