@@ -433,23 +433,27 @@ __global__ __launch_bounds__(256) void act8_quant_kernel(const uint16_t* __restr
   }
 }
 
-// z[i][t] = sum over splits s (in order) of zpart[s][i][t].  Loads are issued
-// eight splits at a time; the additions keep the split order.
+// z[i][t] = sum over splits s (in order) of zpart[s][i][t]: one sum per
+// element, split 0 first, then 1, 2, ...  Each thread handles V consecutive
+// elements (V = 4: 16-byte loads and stores) and issues the loads of up to 16
+// splits before adding them, so a batch of partials costs one memory latency.
+template <int V>
 __global__ void z_reduce_kernel(const float* __restrict__ zpart, int splits, size_t count,
                                 float* __restrict__ z) {
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  typedef float fv __attribute__((ext_vector_type(V)));
+  const size_t idx = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * V;
   if (idx >= count) return;
-  float s = zpart[idx];
-  int k = 1;
-  for (; k + 8 <= splits; k += 8) {
-    float v[8];
+  fv s;
+  for (int k = 0; k < splits; k += 16) {
+    fv v[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = zpart[(size_t)(k + u) * count + idx];
+    for (int u = 0; u < 16; ++u)
+      if (k + u < splits) v[u] = *reinterpret_cast<const fv*>(zpart + (size_t)(k + u) * count + idx);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s += v[u];
+    for (int u = 0; u < 16; ++u)
+      if (k + u < splits) s = (k + u == 0) ? v[u] : s + v[u];
   }
-  for (; k < splits; ++k) s += zpart[(size_t)k * count + idx];
-  z[idx] = s;
+  *reinterpret_cast<fv*>(z + idx) = s;
 }
 
 }  // namespace
@@ -584,8 +588,15 @@ int launch_act8_quant(const uint16_t* x, int b, int m, const float* smooth_inv, 
 
 int launch_z_reduce(const float* zpart, int splits, int b, int rank, float* z, void* stream) {
   const size_t count = (size_t)b * rank;
-  hipLaunchKernelGGL(z_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
-                     (hipStream_t)stream, zpart, splits, count, z);
+  // 16-byte accesses when every split's slice and z start 16-byte aligned
+  // (the workspace is 256-byte aligned; each slice is count floats)
+  const bool vec = count % 4 == 0 && ((uintptr_t)zpart & 15u) == 0 && ((uintptr_t)z & 15u) == 0;
+  if (vec)
+    hipLaunchKernelGGL(z_reduce_kernel<4>, dim3((unsigned)((count / 4 + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)stream, zpart, splits, count, z);
+  else
+    hipLaunchKernelGGL(z_reduce_kernel<1>, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)stream, zpart, splits, count, z);
   return (int)hipGetLastError();
 }
 
