@@ -21,8 +21,10 @@
 //
 // The two FMAs per (output element, group) make the kernel VALU-bound on
 // gfx950 (a 16x16x64 i8 MFMA covers 256 element-groups in 16 cycles; their 8
-// wave64 FMAs need 32).  The work decomposition therefore aims at keeping the
-// VALU busy: three waves per SIMD so MFMAs co-issue with other waves' FMAs,
+// wave64 FMAs need 32), and only about 40 % of an MFMA's time overlaps VALU
+// work, whether the two come from one wave or from different waves (measured
+// with a microbenchmark).  The work decomposition therefore aims at keeping
+// the VALU busy: three waves per SIMD to cover each other's latencies,
 // unpacking each code once per workgroup, few LDS reads of scales, and few
 // barriers.
 //
