@@ -667,8 +667,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the layer shards "
-              "over token rows with no communication; see DESIGN.md). Run with --gpus 1.",
+        print("bench.py measures one GPU: only the one-GPU path exists (the layer would shard over "
+              "token rows with no communication). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -21,7 +21,7 @@ Sources, cited by section and equation:
             Model Inference on Consumer GPUs", section "Nunchaku": two 4-bit
             values per byte.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   R1  ties in round() go to even (IEEE default).
   R2  codes are emitted in [-7, 7]: the review's symmetric grid (sec. 2.2).
   R3  16-bit scale = fp16(fl32(amax / 7)), saturated at 65504.
