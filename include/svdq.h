@@ -255,6 +255,14 @@ const char* svdq_last_error(void);
 /* ABI version of this header (major * 100 + minor). */
 int svdq_abi_version(void);
 
+/* TEST HOOK, not for production use: caps the iterations the preparation's
+ * eigen-solver (the Rayleigh-Ritz step of the truncated SVD) may spend on one
+ * eigenvalue; limit < 0 restores the default (60).  With a limit of 0 every
+ * preparation of a layer with rank > 0 fails with SVDQ_ERR_NO_CONVERGENCE, so
+ * tests can reach that error path.  Process-wide (not per thread); returns the
+ * previous limit. */
+int svdq_test_set_svd_iteration_limit(int limit);
+
 /* DEVICE: the same layer WITHOUT the Nunchaku fusion, for measuring what the
  * fusion saves ([Review] sec. 6.1: a separate down-projection reads X again
  * and a separate up-projection writes a second b x n output that must be

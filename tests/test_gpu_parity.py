@@ -435,10 +435,15 @@ def test_schedule_kinds_match_oracle(S, kind):
     assert err <= 1e-4
 
 
-# the unfused path rounds the W4A4 product, the up-projection and their sum
-# to bf16 (three roundings of at most 2^-9 relative each, ~1.7e-3 Frobenius
-# apiece on these layers), so its bf16 bar is 4e-3; fp32 output keeps 1e-4
-UNFUSED_BF16_TOL = 4e-3
+# The unfused path rounds the W4A4 product to bf16 in y, the up-projection to
+# bf16 in its own b x n output, and their sum to bf16 again: two roundings of
+# full-size values where the fused path has one.  One round-to-nearest-even to
+# bf16 costs about 1.66e-3 relative Frobenius error on these Gaussian-like
+# outputs, and independent roundings add in quadrature, so the unfused path
+# sits near sqrt(2) * 1.66e-3 = 2.35e-3 (2.36e-3 measured on the tiny layer) and
+# cannot meet the fused layer's 2e-3.  Its bf16 bar is that figure with 25 %
+# margin; fp32 output (one rounding of each part, no bf16) keeps 1e-4.
+UNFUSED_BF16_TOL = 3e-3
 
 
 @pytest.mark.parametrize("name", [c[0] for c in LINEAR_CASES])

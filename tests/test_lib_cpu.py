@@ -32,7 +32,7 @@ def test_exports_every_symbol_declared_in_header():
     for nm in names:
         assert hasattr(L, nm), nm
     assert {s[0] for s in B.SIGNATURES} == names
-    assert L.svdq_abi_version() == 103
+    assert L.svdq_abi_version() == 104
 
 
 # Host logic of the GEMM schedule (the planner runs on the host; without a GPU
@@ -123,6 +123,93 @@ def test_prepare_svd_near_optimal_and_decomposition_exact(tiny):
     # the quantized residual is the library's own quantization of that residual
     qw2, ws2 = S.svdq_quantize_residual(p["residual"])
     assert np.array_equal(qw2, p["qw"]) and np.array_equal(ws2, p["wscale"])
+
+
+@pytest.mark.parametrize("name", ["pixart_fc1", "flux_qkv"])
+def test_prepare_svd_near_optimal_full_size(name):
+    """The library's SVD on the PixArt- and FLUX-shaped synthetic layers, whose
+    smoothed weights have a flat Marchenko-Pastur-like bulk (sigma_r and
+    sigma_{r+1} nearly equal, so the rank-r subspace is ill-determined and the
+    factors are judged by optimality, Eq.(10)): the residual's energy within
+    1e-3 of the oracle's (ARPACK factors, rounded to bf16 the same way), the
+    energy the branch removes at least (1 - 1e-3) of the top-r singular values'
+    energy, the decomposition exact, and the codes and scales the oracle's
+    quantization of the library's residual."""
+    _lib_or_skip()
+    inp = workloads.make_inputs(name)
+    c = inp["cfg"]
+    a = O.act_amax(inp["x"])
+    p = S.svdq_prepare_weights(inp["w"], a, c.rank, want_residual=True)
+    ref = O.prepare_weights(inp["w"], a, c.rank, svd="arpack")
+    assert np.array_equal(p["lambda"], ref["lam32"]) and np.array_equal(p["smooth_inv"], ref["inv32"])
+    l1 = LY.bf16_bits_to_f32(p["l1"]).T.astype(np.float64)
+    l2 = LY.bf16_bits_to_f32(p["l2"]).T.astype(np.float64)
+    wt = ref["wt"]
+    low = l1 @ l2
+    assert np.linalg.norm(wt - (low + p["residual"])) <= 1e-6 * np.linalg.norm(wt)
+    tail = np.linalg.norm(wt - low) ** 2
+    assert tail <= (1 + 1e-3) * np.linalg.norm(ref["r64"]) ** 2
+    assert np.linalg.norm(wt) ** 2 - tail >= (1 - 1e-3) * np.sum(ref["sigma"][:c.rank] ** 2)
+    codes, sw = O.quantize_weight_residual(p["residual"])
+    assert np.array_equal(LY.unpack_codes(p["qw"]), np.ascontiguousarray(codes.T))
+    assert np.array_equal(p["wscale"], LY.f32_to_fp16_bits(sw))
+
+
+def test_prepare_svd_exact_when_the_space_is_whole():
+    """Small layers (the Krylov space covers the short side) get the exact
+    truncated SVD.  With a spectrum with clear gaps the singular vectors are
+    unique up to sign, and both sides fix the sign the same way (largest entry
+    of each L1 column positive), so the library's bf16 factors equal the bf16
+    rounding of LAPACK's factors (the oracle's), wide and tall, up to full rank."""
+    _lib_or_skip()
+    rng = np.random.default_rng(8)
+    for (m, n, r) in [(192, 256, 12), (256, 128, 20), (64, 64, 64), (128, 320, 1)]:
+        U, _ = np.linalg.qr(rng.standard_normal((m, min(m, n))))
+        V, _ = np.linalg.qr(rng.standard_normal((n, min(m, n))))
+        sig = np.exp(-np.arange(min(m, n)) / 6.0)
+        w = ((U * sig) @ V.T).astype(np.float32)
+        p = S.svdq_prepare_weights(w, None, r, want_residual=True)
+        ref = O.prepare_weights(w, None, r)
+        assert np.array_equal(p["l1"], LY.f32_to_bf16_bits(ref["l1"]).T), (m, n, r)
+        assert np.array_equal(p["l2"], LY.f32_to_bf16_bits(ref["l2"]).T), (m, n, r)
+
+
+def test_svd_no_convergence_is_reported():
+    """With the eigen-solver's iteration limit forced to 0 (the test hook),
+    every preparation entry point returns SVDQ_ERR_NO_CONVERGENCE with its
+    message and leaves the outputs untouched; rank 0 needs no SVD and still
+    succeeds; restoring the limit restores the result bit for bit."""
+    L = _lib_or_skip()
+    rng = np.random.default_rng(9)
+    w = (rng.standard_normal((128, 96)) / 11).astype(np.float32)
+    a = np.abs(rng.standard_normal(128)).astype(np.float32) + 0.5
+    good = S.svdq_prepare_weights(w, a, 8)
+    prev = L.svdq_test_set_svd_iteration_limit(0)
+    try:
+        assert prev == 60
+        calls = [lambda: S.svdq_prepare_weights(w, a, 8),
+                 lambda: S.svdq_w8a8_prepare_weights(w, a, 8),
+                 lambda: S.svdq_fp4_prepare_weights(w, a, 8),
+                 lambda: S.svdq_prepare_weights_refined(
+                     w, a, workloads.random_bf16_bits(rng, (16, 128)), 8, alphas=(0.5,), iters=1)]
+        for call in calls:
+            with pytest.raises(B.SvdqError) as ei:
+                call()
+            assert ei.value.status == B.SVDQ_ERR_NO_CONVERGENCE
+            assert "did not converge" in str(ei.value)
+        S.svdq_prepare_weights(w, a, 0)  # no SVD at rank 0
+        # outputs untouched on the error path
+        qw = np.full((2, 96, 32), 0xAB, np.uint8)
+        st = L.svdq_prepare_weights(B._ptr(w), B._ptr(a), 128, 96, 8, 64, 0.5, B._ptr(qw),
+                                    B._ptr(np.zeros((2, 96), np.uint16)), B._ptr(np.zeros((8, 128), np.uint16)),
+                                    B._ptr(np.zeros((96, 8), np.uint16)), B._ptr(np.zeros(128, np.float32)),
+                                    B._ptr(np.zeros(128, np.float32)), None)
+        assert st == B.SVDQ_ERR_NO_CONVERGENCE and np.all(qw == 0xAB)
+    finally:
+        assert L.svdq_test_set_svd_iteration_limit(-1) == 0
+    again = S.svdq_prepare_weights(w, a, 8)
+    for key in ("qw", "wscale", "l1", "l2", "lambda", "smooth_inv"):
+        assert np.array_equal(again[key], good[key]), key
 
 
 def test_quantize_residual_bit_exact_given_same_R(tiny):

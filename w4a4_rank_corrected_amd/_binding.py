@@ -82,6 +82,7 @@ SIGNATURES = [
     ("svdq_status_string", ctypes.c_char_p, [_c_int]),
     ("svdq_last_error", ctypes.c_char_p, []),
     ("svdq_abi_version", _c_int, []),
+    ("svdq_test_set_svd_iteration_limit", _c_int, [_c_int]),
     ("svdq_w8a8_prepare_weights", _c_int,
      [_vp, _vp, _c_int, _c_int, _c_int, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     ("svdq_w8a8_act_workspace_size", _size, [_c_int, _c_int, _c_int]),

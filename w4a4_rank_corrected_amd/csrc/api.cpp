@@ -312,7 +312,9 @@ int check_y(void* y, int y_dtype, int b) {
 
 extern "C" {
 
-int svdq_abi_version(void) { return 103; }
+int svdq_abi_version(void) { return 104; }
+
+int svdq_test_set_svd_iteration_limit(int limit) { return set_eig_iteration_limit(limit); }
 
 const char* svdq_last_error(void) { return g_err; }
 

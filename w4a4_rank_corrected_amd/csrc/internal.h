@@ -27,6 +27,11 @@ void smoothing_lambda(const float* W, const float* act_amax, int m, int n, doubl
 // Rank-r truncated SVD of Wt (m x n, row-major fp64): L1 = U_r Sigma_r (m x r,
 // row-major), L2 = V_r^T (r x n, row-major).  Returns false if it failed.
 bool truncated_svd(const double* Wt, int m, int n, int r, double* L1, double* L2);
+// QL iterations the SVD's eigen-solver may spend on one eigenvalue, and the
+// test hook that changes it (limit < 0 restores the default); returns the
+// previous limit.
+constexpr int kEigIterationLimit = 60;
+int set_eig_iteration_limit(int limit);
 // INT4 group quantization of R (fp32 [m][n]) into group-major records.
 void quantize_residual(const float* R, int m, int n, uint8_t* qw, uint16_t* wscale);
 // INT8 quantization of each column of R (fp32 [m][n]) into 64-byte group-major
@@ -147,5 +152,6 @@ int launch_gemm8_up(const int8_t* qx, const uint16_t* ascale, const float* z, co
 int launch_gemm_fp4_up(const uint8_t* qx, const uint8_t* ascale, const float* z, const svdq_fp4_layer& L, int b,
                        void* y, int y_dtype, void* ws, void* stream);
 const char* hip_error_name(int err);
+
 
 }  // namespace svdq

@@ -7,14 +7,16 @@
 //   residual INT4 quantization sec. 2.2 Eq.(1), Algorithm 1 step 5, sec. 8
 //   LoRA concatenation         sec. 7, Eq.(13)
 //
-// The SVD is our own: randomized subspace iteration (Halko, Martinsson & Tropp,
-// SIAM Review 2011, Alg. 4.4) with twice-repeated modified Gram-Schmidt, then a
-// one-sided (Hestenes) Jacobi SVD of the small projected factor.  No LAPACK.
+// The SVD is our own: a randomized block Krylov method (Musco & Musco, NeurIPS
+// 2015) with block Gram-Schmidt orthonormalisation, and a Rayleigh-Ritz step
+// solved by Householder tridiagonalisation and implicit QL iterations (Golub &
+// Van Loan, sec. 8.3).  No LAPACK.
 #include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstring>
 #include <functional>
+#include <limits>
 #include <thread>
 #include <vector>
 
@@ -140,132 +142,337 @@ void smoothing_lambda(const float* W, const float* act_amax, int m, int n, doubl
 // ---------------------------------------------------------------------------
 // dense helpers for the SVD (row-major fp64)
 // ---------------------------------------------------------------------------
-// Y (m x k) = A (m x n) * X (n x k)
-static void mat_mul_ax(const double* A, int m, int n, const double* X, int k, double* Y) {
-  const int JB = 256;
-  parallel_for(m, [&](int64_t lo, int64_t hi) {
-    const int IB = 32;
-    for (int64_t i0 = lo; i0 < hi; i0 += IB) {
-      int64_t i1 = std::min<int64_t>(hi, i0 + IB);
-      for (int64_t i = i0; i < i1; ++i) std::fill(Y + i * k, Y + (i + 1) * k, 0.0);
-      for (int j0 = 0; j0 < n; j0 += JB) {
-        int j1 = std::min(n, j0 + JB);
-        for (int64_t i = i0; i < i1; ++i) {
-          double* y = Y + i * k;
-          const double* a = A + i * (int64_t)n;
-          for (int j = j0; j < j1; ++j) {
-            double w = a[j];
-            const double* x = X + (int64_t)j * k;
-            for (int c = 0; c < k; ++c) y[c] += w * x[c];
-          }
+// The inner loops are compiled twice (AVX2 and baseline x86-64) and picked at
+// load time.  Every element is a plain sum of products in a fixed order
+// (fp-contract off), so both clones give identical bits.
+__attribute__((target_clones("avx2", "default")))
+static void ax_rows(const double* A, int64_t lo, int64_t hi, int n, const double* X, int k, double* Y) {
+  const int JB = 256, IB = 32;
+  for (int64_t i0 = lo; i0 < hi; i0 += IB) {
+    const int64_t i1 = std::min<int64_t>(hi, i0 + IB);
+    for (int64_t i = i0; i < i1; ++i) std::fill(Y + i * k, Y + (i + 1) * k, 0.0);
+    for (int j0 = 0; j0 < n; j0 += JB) {
+      const int j1 = std::min(n, j0 + JB);
+      for (int64_t i = i0; i < i1; ++i) {
+        double* __restrict__ y = Y + i * k;
+        const double* a = A + i * (int64_t)n;
+        for (int j = j0; j < j1; ++j) {
+          const double w = a[j];
+          const double* __restrict__ x = X + (int64_t)j * k;
+          for (int c = 0; c < k; ++c) y[c] += w * x[c];
         }
       }
     }
-  }, 16);
+  }
+}
+
+__attribute__((target_clones("avx2", "default")))
+static void atx_rows(const double* A, int m, int n, int64_t lo, int64_t hi, const double* Q, int k, double* Z) {
+  const int64_t JB = 128;
+  for (int64_t j0 = lo; j0 < hi; j0 += JB) {
+    const int64_t j1 = std::min<int64_t>(hi, j0 + JB);
+    for (int64_t j = j0; j < j1; ++j) std::fill(Z + j * k, Z + (j + 1) * k, 0.0);
+    for (int i = 0; i < m; ++i) {
+      const double* a = A + (int64_t)i * n;
+      const double* __restrict__ q = Q + (int64_t)i * k;
+      for (int64_t j = j0; j < j1; ++j) {
+        const double w = a[j];
+        double* __restrict__ z = Z + j * k;
+        for (int c = 0; c < k; ++c) z[c] += w * q[c];
+      }
+    }
+  }
+}
+
+// Y (m x k) = A (m x n) * X (n x k)
+static void mat_mul_ax(const double* A, int m, int n, const double* X, int k, double* Y) {
+  parallel_for(m, [&](int64_t lo, int64_t hi) { ax_rows(A, lo, hi, n, X, k, Y); }, 16);
 }
 
 // Z (n x k) = A^T (n x m) * Q (m x k), A is m x n
 static void mat_mul_atx(const double* A, int m, int n, const double* Q, int k, double* Z) {
-  parallel_for(n, [&](int64_t lo, int64_t hi) {
-    const int64_t JB = 128;
-    for (int64_t j0 = lo; j0 < hi; j0 += JB) {
-      int64_t j1 = std::min<int64_t>(hi, j0 + JB);
-      for (int64_t j = j0; j < j1; ++j) std::fill(Z + j * k, Z + (j + 1) * k, 0.0);
-      for (int i = 0; i < m; ++i) {
-        const double* a = A + (int64_t)i * n;
-        const double* q = Q + (int64_t)i * k;
-        for (int64_t j = j0; j < j1; ++j) {
-          double w = a[j];
-          double* z = Z + j * k;
-          for (int c = 0; c < k; ++c) z[c] += w * q[c];
-        }
-      }
-    }
-  }, 64);
+  parallel_for(n, [&](int64_t lo, int64_t hi) { atx_rows(A, m, n, lo, hi, Q, k, Z); }, 64);
 }
 
-// Orthonormalise the k columns of Y (rows x k, row-major) in place with
-// modified Gram-Schmidt applied twice.  If R is given, Y_in = Q R with R upper
-// triangular (k x k, row-major).
-static void orthonormalize(double* Y, int64_t rows, int k, double* R) {
-  std::vector<double> col(rows), qi(rows);
-  if (R) std::fill(R, R + (int64_t)k * k, 0.0);
-  for (int j = 0; j < k; ++j) {
-    for (int64_t r = 0; r < rows; ++r) col[r] = Y[r * k + j];
-    double norm0 = 0.0;
-    for (int64_t r = 0; r < rows; ++r) norm0 += col[r] * col[r];
-    norm0 = std::sqrt(norm0);
-    for (int pass = 0; pass < 2; ++pass) {
-      for (int i = 0; i < j; ++i) {
+// The operator whose singular subspace is sought, seen from its SHORT side:
+// S (ls x ll) is W~ itself when m <= n, or W~^T when m > n, so every basis the
+// Krylov method builds has the short length ls.
+struct ShortSide {
+  const double* W;  // W~, m x n row-major
+  int m, n;
+  bool wide() const { return m <= n; }
+  int ls() const { return wide() ? m : n; }
+  int ll() const { return wide() ? n : m; }
+  // Y (ls x k) = S X, X is ll x k
+  void apply(const double* X, int k, double* Y) const {
+    if (wide()) mat_mul_ax(W, m, n, X, k, Y);
+    else mat_mul_atx(W, m, n, X, k, Y);
+  }
+  // Z (ll x k) = S^T Y, Y is ls x k
+  void apply_t(const double* Y, int k, double* Z) const {
+    if (wide()) mat_mul_atx(W, m, n, Y, k, Z);
+    else mat_mul_ax(W, m, n, Y, k, Z);
+  }
+};
+
+// Modified Gram-Schmidt, applied twice, on the columns [c0, c1) of the
+// column-major block B (each column `rows` long), among themselves; columns
+// [0, c0) are already orthonormal and orthogonal to them.  A column that is
+// numerically dependent (norm below 1e-12 of its norm before the projections)
+// is replaced by a unit vector made orthogonal to every previous column, so
+// the result is always an orthonormal set.
+static void mgs_columns(double* B, int64_t rows, int c0, int c1) {
+  auto proj_out = [&](double* col, int from, int upto) {
+    for (int pass = 0; pass < 2; ++pass)
+      for (int i = from; i < upto; ++i) {
+        const double* q = B + (int64_t)i * rows;
         double c = 0.0;
-        for (int64_t r = 0; r < rows; ++r) c += Y[r * k + i] * col[r];
-        for (int64_t r = 0; r < rows; ++r) col[r] -= c * Y[r * k + i];
-        if (R) R[(int64_t)i * k + j] += c;
+        for (int64_t r = 0; r < rows; ++r) c += q[r] * col[r];
+        for (int64_t r = 0; r < rows; ++r) col[r] -= c * q[r];
       }
-    }
-    double norm = 0.0;
-    for (int64_t r = 0; r < rows; ++r) norm += col[r] * col[r];
-    norm = std::sqrt(norm);
-    if (!(norm > 1e-13 * norm0) || norm == 0.0) {
-      // numerically dependent column: replace by a unit vector orthogonal to the
-      // previous ones (keeps the basis orthonormal; R gets a zero diagonal)
+  };
+  auto norm = [&](const double* col) {
+    double s = 0.0;
+    for (int64_t r = 0; r < rows; ++r) s += col[r] * col[r];
+    return std::sqrt(s);
+  };
+  for (int j = c0; j < c1; ++j) {
+    double* col = B + (int64_t)j * rows;
+    const double n0 = norm(col);
+    proj_out(col, c0, j);
+    double nr = norm(col);
+    if (!(nr > 1e-12 * n0) || nr == 0.0) {
       for (int64_t start = 0; start < rows; ++start) {
-        std::fill(col.begin(), col.end(), 0.0);
+        std::fill(col, col + rows, 0.0);
         col[(start + j) % rows] = 1.0;
-        for (int pass = 0; pass < 2; ++pass)
-          for (int i = 0; i < j; ++i) {
-            double c = 0.0;
-            for (int64_t r = 0; r < rows; ++r) c += Y[r * k + i] * col[r];
-            for (int64_t r = 0; r < rows; ++r) col[r] -= c * Y[r * k + i];
-          }
-        norm = 0.0;
-        for (int64_t r = 0; r < rows; ++r) norm += col[r] * col[r];
-        norm = std::sqrt(norm);
-        if (norm > 0.5) break;
+        proj_out(col, 0, j);
+        nr = norm(col);
+        if (nr > 0.5) break;
       }
-      if (R) R[(int64_t)j * k + j] = 0.0;
-    } else if (R) {
-      R[(int64_t)j * k + j] = norm;
     }
-    for (int64_t r = 0; r < rows; ++r) Y[r * k + j] = col[r] / norm;
+    for (int64_t r = 0; r < rows; ++r) col[r] /= nr;
   }
 }
 
-// One-sided Jacobi SVD of a square k x k matrix A (row-major, overwritten):
-// A V = U Sigma.  On return A holds U Sigma column-wise, V the rotations.
-static bool jacobi_svd(double* A, int k, double* V) {
-  for (int i = 0; i < k; ++i)
-    for (int j = 0; j < k; ++j) V[(int64_t)i * k + j] = (i == j) ? 1.0 : 0.0;
-  const double eps = 1e-15;
-  for (int sweep = 0; sweep < 80; ++sweep) {
-    bool rotated = false;
-    for (int p = 0; p < k - 1; ++p) {
-      for (int q = p + 1; q < k; ++q) {
-        double alpha = 0, beta = 0, gamma = 0;
-        for (int r = 0; r < k; ++r) {
-          double ap = A[(int64_t)r * k + p], aq = A[(int64_t)r * k + q];
-          alpha += ap * ap;
-          beta += aq * aq;
-          gamma += ap * aq;
-        }
-        if (gamma == 0.0 || std::fabs(gamma) <= eps * std::sqrt(alpha * beta)) continue;
-        rotated = true;
-        double zeta = (beta - alpha) / (2.0 * gamma);
-        double t = (zeta >= 0 ? 1.0 : -1.0) / (std::fabs(zeta) + std::sqrt(1.0 + zeta * zeta));
-        double c = 1.0 / std::sqrt(1.0 + t * t), s = c * t;
-        for (int r = 0; r < k; ++r) {
-          double ap = A[(int64_t)r * k + p], aq = A[(int64_t)r * k + q];
-          A[(int64_t)r * k + p] = c * ap - s * aq;
-          A[(int64_t)r * k + q] = s * ap + c * aq;
-          double vp = V[(int64_t)r * k + p], vq = V[(int64_t)r * k + q];
-          V[(int64_t)r * k + p] = c * vp - s * vq;
-          V[(int64_t)r * k + q] = s * vp + c * vq;
-        }
+// Orthonormalise the columns [c0, k) of Y (rows x k, row-major) against its
+// (already orthonormal) columns [0, c0) and among themselves.  Blocks of
+// columns are first projected against everything before them twice (block
+// classical Gram-Schmidt: two passes of a product with the previous columns,
+// parallel over rows, deterministic), then finished by mgs_columns on a
+// column-major copy.
+static void orthonormalize(double* Y, int64_t rows, int k, int c0 = 0) {
+  const int BS = 32;
+  for (int b0 = c0; b0 < k; b0 += BS) {
+    const int b1 = std::min(k, b0 + BS), bw = b1 - b0;
+    if (b0 > 0) {
+      for (int pass = 0; pass < 2; ++pass) {
+        // C (b0 x bw) = Y[:, :b0]^T Y[:, b0:b1], summed over row chunks in a fixed order
+        const int64_t chunks = std::max<int64_t>(1, std::min<int64_t>(host_threads(), rows / 256));
+        std::vector<double> part((size_t)chunks * b0 * bw, 0.0);
+        parallel_for(chunks, [&](int64_t lo, int64_t hi) {
+          for (int64_t ch = lo; ch < hi; ++ch) {
+            double* C = &part[(size_t)ch * b0 * bw];
+            const int64_t r0 = rows * ch / chunks, r1 = rows * (ch + 1) / chunks;
+            for (int64_t r = r0; r < r1; ++r) {
+              const double* y = Y + r * k;
+              for (int i = 0; i < b0; ++i) {
+                const double yi = y[i];
+                double* Ci = C + (size_t)i * bw;
+                for (int j = 0; j < bw; ++j) Ci[j] += yi * y[b0 + j];
+              }
+            }
+          }
+        });
+        std::vector<double> C((size_t)b0 * bw, 0.0);
+        for (int64_t ch = 0; ch < chunks; ++ch)
+          for (size_t t = 0; t < C.size(); ++t) C[t] += part[(size_t)ch * b0 * bw + t];
+        // Y[:, b0:b1] -= Y[:, :b0] C
+        parallel_for(rows, [&](int64_t lo, int64_t hi) {
+          double acc[BS];
+          for (int64_t r = lo; r < hi; ++r) {
+            double* y = Y + r * k;
+            std::fill(acc, acc + bw, 0.0);
+            for (int i = 0; i < b0; ++i) {
+              const double yi = y[i];
+              const double* Ci = &C[(size_t)i * bw];
+              for (int j = 0; j < bw; ++j) acc[j] += yi * Ci[j];
+            }
+            for (int j = 0; j < bw; ++j) y[b0 + j] -= acc[j];
+          }
+        }, 64);
       }
     }
-    if (!rotated) return true;
+    // finish the block with MGS on a column-major copy (columns [0, b1) so that
+    // dependent columns can be completed against everything before them)
+    std::vector<double> cm((size_t)b1 * rows);
+    for (int64_t r = 0; r < rows; ++r)
+      for (int j = 0; j < b1; ++j) cm[(size_t)j * rows + r] = Y[r * k + j];
+    mgs_columns(cm.data(), rows, b0, b1);
+    for (int64_t r = 0; r < rows; ++r)
+      for (int j = b0; j < b1; ++j) Y[r * k + j] = cm[(size_t)j * rows + r];
   }
-  return false;
+}
+
+// Eigen-decomposition of a symmetric K x K matrix A (row-major, full storage):
+// Householder reduction to tridiagonal form with the reflections accumulated,
+// then implicit QL iterations with Wilkinson-type shifts (Golub & Van Loan,
+// Matrix Computations, sec. 8.3).  On return w holds the eigenvalues in
+// descending order and V (K x K, row-major) the matching eigenvectors as
+// columns.  Returns false if an eigenvalue needed more than the iteration
+// limit (kEigIterationLimit unless a test lowered it).
+// Iterations the QL phase may spend on one eigenvalue (a test hook lowers it).
+static std::atomic<int> g_eig_iteration_limit{kEigIterationLimit};
+
+int set_eig_iteration_limit(int limit) {
+  return g_eig_iteration_limit.exchange(limit < 0 ? kEigIterationLimit : limit);
+}
+
+static bool sym_eig(std::vector<double>& A, int K, std::vector<double>& w, std::vector<double>& V) {
+  const int iteration_limit = g_eig_iteration_limit.load();
+  std::vector<double> d(K), e(K, 0.0);
+  // ---- tridiagonalisation: A <- H A H for reflections H = I - beta v v^T that
+  // zero column k below the subdiagonal; v is kept in A[k+1.., k]
+  std::vector<double> beta(K, 0.0), p(K), q(K), v(K);
+  for (int k = 0; k + 2 < K; ++k) {
+    const int s = k + 1, len = K - s;
+    double xn = 0.0;
+    for (int i = s; i < K; ++i) xn += A[(size_t)i * K + k] * A[(size_t)i * K + k];
+    xn = std::sqrt(xn);
+    if (xn == 0.0) { beta[k] = 0.0; continue; }
+    const double x0 = A[(size_t)s * K + k];
+    const double alpha = x0 >= 0 ? -xn : xn;  // H x = alpha e_1, no cancellation in v_0
+    const double v0 = x0 - alpha;
+    // v = x - alpha e_1 scaled so that v_0 = 1; beta = 2 / (v^T v)
+    double vv = 1.0;
+    A[(size_t)s * K + k] = 1.0;
+    for (int i = s + 1; i < K; ++i) {
+      A[(size_t)i * K + k] /= v0;
+      vv += A[(size_t)i * K + k] * A[(size_t)i * K + k];
+    }
+    const double bt = 2.0 / vv;
+    beta[k] = bt;
+    for (int i = s; i < K; ++i) v[i] = A[(size_t)i * K + k];
+    // p = beta * A22 v (A22 = trailing block, symmetric, full storage)
+    auto pv = [&](int64_t lo, int64_t hi) {
+      for (int64_t i = s + lo; i < s + hi; ++i) {
+        const double* row = &A[(size_t)i * K];
+        double acc = 0.0;
+        for (int j = s; j < K; ++j) acc += row[j] * v[j];
+        p[i] = bt * acc;
+      }
+    };
+    if (len >= 256) parallel_for(len, pv, 32); else pv(0, len);
+    double pv_dot = 0.0;
+    for (int i = s; i < K; ++i) pv_dot += p[i] * v[i];
+    const double h = 0.5 * bt * pv_dot;
+    for (int i = s; i < K; ++i) q[i] = p[i] - h * v[i];
+    // A22 <- A22 - v q^T - q v^T
+    auto upd = [&](int64_t lo, int64_t hi) {
+      for (int64_t i = s + lo; i < s + hi; ++i) {
+        double* row = &A[(size_t)i * K];
+        const double vi = v[i], qi = q[i];
+        for (int j = s; j < K; ++j) row[j] -= vi * q[j] + qi * v[j];
+      }
+    };
+    if (len >= 256) parallel_for(len, upd, 32); else upd(0, len);
+    e[k] = alpha;  // T[k+1][k]
+  }
+  for (int i = 0; i < K; ++i) d[i] = A[(size_t)i * K + i];
+  if (K >= 2) e[K - 2] = A[(size_t)(K - 1) * K + (K - 2)];
+  // Q = H_0 H_1 ... H_{K-3}, built backwards into V (row-major)
+  V.assign((size_t)K * K, 0.0);
+  for (int i = 0; i < K; ++i) V[(size_t)i * K + i] = 1.0;
+  for (int k = K - 3; k >= 0; --k) {
+    if (beta[k] == 0.0) continue;
+    const int s = k + 1;
+    // V[s:, s:] <- (I - beta v v^T) V[s:, s:]
+    std::vector<double> t(K, 0.0);
+    for (int i = s; i < K; ++i) {
+      const double vi = A[(size_t)i * K + k];
+      const double* row = &V[(size_t)i * K];
+      for (int j = s; j < K; ++j) t[j] += vi * row[j];
+    }
+    for (int i = s; i < K; ++i) {
+      const double f = beta[k] * A[(size_t)i * K + k];
+      double* row = &V[(size_t)i * K];
+      for (int j = s; j < K; ++j) row[j] -= f * t[j];
+    }
+  }
+  // ---- implicit QL on the tridiagonal (d, e), e[i] coupling i and i+1.  The
+  // rotations act on columns of V; they are applied to its transpose Vt (rows
+  // contiguous), in parallel over the components.
+  std::vector<double> Vt((size_t)K * K);
+  for (int i = 0; i < K; ++i)
+    for (int j = 0; j < K; ++j) Vt[(size_t)j * K + i] = V[(size_t)i * K + j];
+  std::vector<double> cs(K), sn(K);
+  for (int l = 0; l < K; ++l) {
+    int iter = 0;
+    for (;;) {
+      int mm = l;
+      for (; mm + 1 < K; ++mm) {
+        const double dd = std::fabs(d[mm]) + std::fabs(d[mm + 1]);
+        if (std::fabs(e[mm]) <= std::numeric_limits<double>::epsilon() * dd) break;
+      }
+      if (mm == l) break;
+      if (++iter > iteration_limit) return false;
+      // shift from the leading 2 x 2 block: its eigenvalue nearer d[l]
+      double g = (d[l + 1] - d[l]) / (2.0 * e[l]);
+      double r = std::hypot(g, 1.0);
+      g = d[mm] - d[l] + e[l] / (g + (g >= 0 ? r : -r));
+      double s = 1.0, c = 1.0, pp = 0.0;
+      int i = mm - 1, stop = l - 1;
+      for (; i >= l; --i) {
+        const double f = s * e[i], bb = c * e[i];
+        r = std::hypot(f, g);
+        e[i + 1] = r;
+        if (r == 0.0) {  // split: the rest of the chase is not needed
+          d[i + 1] -= pp;
+          e[mm] = 0.0;
+          stop = i;
+          break;
+        }
+        s = f / r;
+        c = g / r;
+        g = d[i + 1] - pp;
+        r = (d[i] - g) * s + 2.0 * c * bb;
+        pp = s * r;
+        d[i + 1] = g + pp;
+        g = c * r - bb;
+        cs[i] = c;
+        sn[i] = s;
+      }
+      // apply the rotations i = mm-1 .. stop+1 (in that order) to rows i, i+1 of Vt
+      const int first = mm - 1, last = stop + 1;
+      auto rot = [&](int64_t lo, int64_t hi) {
+        for (int ii = first; ii >= last; --ii) {
+          double* a = &Vt[(size_t)ii * K];
+          double* b = &Vt[(size_t)(ii + 1) * K];
+          const double c2 = cs[ii], s2 = sn[ii];
+          for (int64_t j = lo; j < hi; ++j) {
+            const double f = b[j];
+            b[j] = s2 * a[j] + c2 * f;
+            a[j] = c2 * a[j] - s2 * f;
+          }
+        }
+      };
+      if ((int64_t)(first - last + 1) * K >= (1 << 16)) parallel_for(K, rot, 64); else rot(0, K);
+      if (stop >= l) continue;  // split: iterate again on the same l
+      d[l] -= pp;
+      e[l] = g;
+      e[mm] = 0.0;
+    }
+  }
+  // sort descending; eigenvector j of the result = row order[j] of Vt
+  std::vector<int> order(K);
+  for (int i = 0; i < K; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return d[a] > d[b]; });
+  w.resize(K);
+  for (int j = 0; j < K; ++j) {
+    w[j] = d[order[j]];
+    const double* src = &Vt[(size_t)order[j] * K];
+    for (int i = 0; i < K; ++i) V[(size_t)i * K + j] = src[i];
+  }
+  return true;
 }
 
 static uint64_t splitmix64(uint64_t& s) {
@@ -275,71 +482,103 @@ static uint64_t splitmix64(uint64_t& s) {
   return z ^ (z >> 31);
 }
 
+// Rank-r truncated SVD by a randomized block Krylov method (Musco & Musco,
+// "Randomized Block Krylov Methods for Stronger and Faster Approximate
+// Singular Value Decomposition", NeurIPS 2015): a Gaussian block of width bw
+// is pushed through q rounds of S S^T, the blocks of all rounds together span
+// a Krylov space of dimension K = (q + 1) bw on the short side, and the
+// rank-r approximation is taken from the Rayleigh-Ritz problem on that space
+// (the eigen-decomposition of the K x K matrix Q^T S S^T Q).  Flat
+// (Marchenko-Pastur-like) spectra, where sigma_r and sigma_{r+1} nearly
+// coincide, are where plain subspace iteration converges slowly; the Krylov
+// space reaches near-optimal tail energy on them at a comparable cost.  When
+// K would reach the short dimension, the space is all of it and the result is
+// the exact truncated SVD.
 bool truncated_svd(const double* Wt, int m, int n, int r, double* L1, double* L2) {
   if (r == 0) return true;
-  const int mn = std::min(m, n);
-  // Oversampled width and power iterations sized for flat (Marchenko-Pastur)
-  // spectra, where sigma_r and sigma_{r+1} nearly coincide: the rank-r tail
-  // energy comes within ~1e-5 of the optimum on such matrices.
-  const int k = std::min(mn, r + std::max(32, r));
-  const int power_iters = 8;
-
-  // Gaussian test matrix Omega (n x k), Box-Muller on a fixed-seed splitmix64 stream
-  std::vector<double> omega((int64_t)n * k);
-  uint64_t state = 0x5EED5EEDull;
-  for (int64_t i = 0; i < (int64_t)n * k; i += 2) {
-    double u1 = ((splitmix64(state) >> 11) + 1) * (1.0 / 9007199254740993.0);
-    double u2 = (splitmix64(state) >> 11) * (1.0 / 9007199254740992.0);
-    double rad = std::sqrt(-2.0 * std::log(u1));
-    omega[i] = rad * std::cos(2.0 * M_PI * u2);
-    if (i + 1 < (int64_t)n * k) omega[i + 1] = rad * std::sin(2.0 * M_PI * u2);
+  const ShortSide S{Wt, m, n};
+  const int ls = S.ls(), ll = S.ll();
+  const int bw = r + std::max(16, r / 2);
+  const int kmax = std::max(480, 3 * bw);
+  const int q = std::max(2, std::min(8, kmax / bw - 1));
+  int K = (q + 1) * bw;
+  const bool full = K >= ls;
+  std::vector<double> Q;  // ls x K, orthonormal columns
+  if (full) {
+    K = ls;
+    Q.assign((size_t)ls * K, 0.0);
+    for (int i = 0; i < ls; ++i) Q[(size_t)i * K + i] = 1.0;
+  } else {
+    // Gaussian block Omega (ll x bw): Box-Muller on a fixed-seed splitmix64 stream
+    std::vector<double> omega((size_t)ll * bw);
+    uint64_t state = 0x5EED5EEDull;
+    for (size_t i = 0; i < omega.size(); i += 2) {
+      const double u1 = ((splitmix64(state) >> 11) + 1) * (1.0 / 9007199254740993.0);
+      const double u2 = (splitmix64(state) >> 11) * (1.0 / 9007199254740992.0);
+      const double rad = std::sqrt(-2.0 * std::log(u1));
+      omega[i] = rad * std::cos(2.0 * M_PI * u2);
+      if (i + 1 < omega.size()) omega[i + 1] = rad * std::sin(2.0 * M_PI * u2);
+    }
+    std::vector<double> Y((size_t)ls * bw), Z((size_t)ll * bw);
+    Q.assign((size_t)ls * K, 0.0);
+    S.apply(omega.data(), bw, Y.data());
+    for (int it = 0;; ++it) {
+      orthonormalize(Y.data(), ls, bw);
+      for (int i = 0; i < ls; ++i)
+        std::copy(&Y[(size_t)i * bw], &Y[(size_t)i * bw] + bw, &Q[(size_t)i * K + (size_t)it * bw]);
+      if (it == q) break;
+      S.apply_t(Y.data(), bw, Z.data());
+      orthonormalize(Z.data(), ll, bw);
+      S.apply(Z.data(), bw, Y.data());
+    }
+    // one orthonormal basis of the whole Krylov space (each block already is one)
+    orthonormalize(Q.data(), ls, K, bw);
   }
-  std::vector<double> Y((int64_t)m * k), Zn((int64_t)n * k);
-  mat_mul_ax(Wt, m, n, omega.data(), k, Y.data());
-  orthonormalize(Y.data(), m, k, nullptr);
-  for (int it = 0; it < power_iters; ++it) {
-    mat_mul_atx(Wt, m, n, Y.data(), k, Zn.data());
-    orthonormalize(Zn.data(), n, k, nullptr);
-    mat_mul_ax(Wt, m, n, Zn.data(), k, Y.data());
-    orthonormalize(Y.data(), m, k, nullptr);
-  }
-  // B^T = W^T Q (n x k) = Q2 R2;  R2 = U_R Sigma V_R^T  =>  W ~ (Q V_R) Sigma (Q2 U_R)^T
-  mat_mul_atx(Wt, m, n, Y.data(), k, Zn.data());
-  std::vector<double> R2((int64_t)k * k), VR((int64_t)k * k);
-  orthonormalize(Zn.data(), n, k, R2.data());
-  if (!jacobi_svd(R2.data(), k, VR.data())) return false;
-  std::vector<double> sig(k);
-  for (int c = 0; c < k; ++c) {
-    double s = 0;
-    for (int rr = 0; rr < k; ++rr) s += R2[(int64_t)rr * k + c] * R2[(int64_t)rr * k + c];
-    sig[c] = std::sqrt(s);
-  }
-  std::vector<int> order(k);
-  for (int c = 0; c < k; ++c) order[c] = c;
-  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return sig[a] > sig[b]; });
-
+  // P = S^T Q (ll x K); Rayleigh-Ritz on G = P^T P = Q^T S S^T Q
+  std::vector<double> P((size_t)ll * K), G((size_t)K * K);
+  S.apply_t(Q.data(), K, P.data());
+  mat_mul_atx(P.data(), ll, K, P.data(), K, G.data());
+  for (int i = 0; i < K; ++i)  // exact symmetry (both triangles are the same sums)
+    for (int j = i + 1; j < K; ++j) G[(size_t)j * K + i] = G[(size_t)i * K + j];
+  std::vector<double> lam, V;
+  if (!sym_eig(G, K, lam, V)) return false;
+  // short-side singular vectors Us = Q V_r (ls x r); long side S^T Us = P V_r
+  std::vector<double> Us((size_t)ls * r, 0.0), Ul((size_t)ll * r, 0.0), sig(r);
+  for (int t = 0; t < r; ++t) sig[t] = std::sqrt(std::max(lam[t], 0.0));
+  parallel_for(ls, [&](int64_t lo, int64_t hi) {
+    for (int64_t i = lo; i < hi; ++i)
+      for (int j = 0; j < K; ++j) {
+        const double qv = Q[(size_t)i * K + j];
+        for (int t = 0; t < r; ++t) Us[(size_t)i * r + t] += qv * V[(size_t)j * K + t];
+      }
+  }, 64);
+  parallel_for(ll, [&](int64_t lo, int64_t hi) {
+    for (int64_t i = lo; i < hi; ++i)
+      for (int j = 0; j < K; ++j) {
+        const double pv = P[(size_t)i * K + j];
+        for (int t = 0; t < r; ++t) Ul[(size_t)i * r + t] += pv * V[(size_t)j * K + t];
+      }
+  }, 64);
+  // L1 = U Sigma (m x r), L2 = V^T (r x n).  Wide (S = W~): U = Us, Sigma V^T =
+  // Ul^T.  Tall (S = W~^T): V = Us, U Sigma = Ul.  Singular values that vanish
+  // give zero columns / rows.  Sign: the largest-magnitude entry of each L1
+  // column is positive.
+  const double tiny = sig[0] * 1e-300;
   for (int t = 0; t < r; ++t) {
-    int c = order[t];
-    double s = sig[c];
-    // left vector u = Q * VR[:, c]; right vector v = Q2 * (R2[:, c] / s)
+    const double s = sig[t];
     std::vector<double> u(m), v(n);
-    for (int i = 0; i < m; ++i) {
-      double acc = 0;
-      for (int j = 0; j < k; ++j) acc += Y[(int64_t)i * k + j] * VR[(int64_t)j * k + c];
-      u[i] = acc;
+    if (S.wide()) {
+      for (int i = 0; i < m; ++i) u[i] = Us[(size_t)i * r + t] * s;
+      for (int j = 0; j < n; ++j) v[j] = s > tiny ? Ul[(size_t)j * r + t] / s : 0.0;
+    } else {
+      for (int i = 0; i < m; ++i) u[i] = Ul[(size_t)i * r + t];
+      for (int j = 0; j < n; ++j) v[j] = Us[(size_t)j * r + t];
     }
-    for (int j = 0; j < n; ++j) {
-      double acc = 0;
-      if (s > 0)
-        for (int q = 0; q < k; ++q) acc += Zn[(int64_t)j * k + q] * (R2[(int64_t)q * k + c] / s);
-      v[j] = acc;
-    }
-    // sign convention: the largest-magnitude entry of u is positive
     int imax = 0;
     for (int i = 1; i < m; ++i)
       if (std::fabs(u[i]) > std::fabs(u[imax])) imax = i;
-    double sgn = u[imax] < 0 ? -1.0 : 1.0;
-    for (int i = 0; i < m; ++i) L1[(int64_t)i * r + t] = sgn * u[i] * s;
+    const double sgn = u[imax] < 0 ? -1.0 : 1.0;
+    for (int i = 0; i < m; ++i) L1[(int64_t)i * r + t] = sgn * u[i];
     for (int j = 0; j < n; ++j) L2[(int64_t)t * n + j] = sgn * v[j];
   }
   return true;
