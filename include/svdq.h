@@ -246,6 +246,23 @@ size_t svdq_linear_workspace_size(int b, int m, int n, int rank, int group);
 int svdq_linear(const uint16_t* x, const svdq_layer* layer, int b, void* y, int y_dtype,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* DEVICE: svdq_linear without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It runs exactly svdq_linear's kernels
+ * (bit-identical output) on a workspace taken from device scratch memory that
+ * the library holds in a static device array of
+ * svdq_linear_noalloc_max_workspace() bytes (128 MiB) on each GPU it runs
+ * on, until the process ends.  It calls no allocator.
+ *   Arguments as svdq_linear.  Returns SVDQ_ERR_WORKSPACE, before any launch,
+ *   when svdq_linear_workspace_size(b, m, n, rank, 64) exceeds the scratch.
+ *   Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *   time on one GPU (on different streams, or from several threads without
+ *   ordering) race and give undefined results; stream-ordered calls are safe.
+ *   The scratch keeps whatever the last call left; no part of it needs
+ *   clearing (publication flags carry a per-launch epoch). */
+int svdq_linear_noalloc(const uint16_t* x, const svdq_layer* layer, int b, void* y, int y_dtype, void* stream);
+size_t svdq_linear_noalloc_max_workspace(void);
+
 /* Static description of a status code. */
 const char* svdq_status_string(int status);
 

@@ -76,6 +76,8 @@ SIGNATURES = [
     ("svdq_linear_workspace_size", _size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     ("svdq_linear", _c_int,
      [_vp, ctypes.POINTER(svdq_layer), _c_int, _vp, _c_int, _vp, _size, _vp]),
+    ("svdq_linear_noalloc", _c_int, [_vp, ctypes.POINTER(svdq_layer), _c_int, _vp, _c_int, _vp]),
+    ("svdq_linear_noalloc_max_workspace", _size, []),
     ("svdq_linear_unfused_workspace_size", _size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     ("svdq_linear_unfused", _c_int,
      [_vp, ctypes.POINTER(svdq_layer), _c_int, _vp, _c_int, _vp, _size, _vp]),
@@ -467,6 +469,22 @@ def svdq_linear(x, layer: DeviceLayer, out_dtype=None, y=None, workspace=None, s
     _check(lib().svdq_linear(_ptr(x), ctypes.byref(layer.struct), b, _ptr(y), code, _ptr(workspace),
                              wsb, _stream(stream)))
     return y
+
+
+def svdq_linear_noalloc(x, layer: DeviceLayer, out_dtype=None, y=None, stream=None):
+    """svdq_linear on the library's device scratch (no workspace argument; y is
+    allocated here when None, so callers that must not allocate pass y)."""
+    b, m = _input(x)
+    _dev(x, "x", device=layer.qw.device)
+    if m != layer.m:
+        raise ValueError(f"x has {m} channels, the layer {layer.m}")
+    y, code = _output(y, b, layer.n, out_dtype, x.device)
+    _check(lib().svdq_linear_noalloc(_ptr(x), ctypes.byref(layer.struct), b, _ptr(y), code, _stream(stream)))
+    return y
+
+
+def svdq_linear_noalloc_max_workspace() -> int:
+    return int(lib().svdq_linear_noalloc_max_workspace())
 
 
 def svdq_linear_unfused_workspace_size(b: int, m: int, n: int, rank: int, group: int = SVDQ_GROUP) -> int:

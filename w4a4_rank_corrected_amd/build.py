@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsvdq.so")
 
 HOST_SOURCES = ["api.cpp", "prep.cpp"]
-HIP_SOURCES = ["act_kernels.hip", "gemm_kernels.hip"]
+HIP_SOURCES = ["act_kernels.hip", "gemm_kernels.hip", "scratch.hip"]
 HEADERS = ["internal.h", "device_common.h"]
 
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")

@@ -571,41 +571,20 @@ size_t svdq_linear_workspace_size(int b, int m, int n, int rank, int group) {
   return linear_ws_layout(b, m, n, rank).total;
 }
 
-int svdq_linear(const uint16_t* x, const svdq_layer* layer, int b, void* y, int y_dtype,
-                void* workspace, size_t workspace_bytes, void* stream) {
-  clear_error();
-  int st = check_layer(layer);
-  if (st) return st;
-  REQUIRE(b >= 0, SVDQ_ERR_INVALID_ARG, "b must be >= 0 (got %d)", b);
-  REQUIRE(b <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "b must be <= %d (got %d)", SVDQ_MAX_DIM, b);
-  st = check_y(y, y_dtype, b);
-  if (st) return st;
-  if (b == 0) return SVDQ_OK;
+// The two kernels of the layer on the workspace `ws` (laid out by
+// linear_ws_layout): the act kernel (+ the ordered Z reduction when the
+// channel groups are split), then the GEMM kernel.
+static int run_linear(const uint16_t* x, const svdq_layer* layer, int b, void* y, int y_dtype, char* ws,
+                      const LinearWorkspace& w, void* stream) {
   const int m = layer->m, rank = layer->rank;
-  REQUIRE(x != nullptr, SVDQ_ERR_INVALID_ARG, "x must not be NULL");
-  REQUIRE(aligned16(x), SVDQ_ERR_ALIGNMENT, "x must be 16-byte aligned");
-  if (layer->smooth_inv)
-    REQUIRE(aligned16(layer->smooth_inv), SVDQ_ERR_ALIGNMENT, "smooth_inv must be 16-byte aligned");
-  if (rank > 0) {
-    REQUIRE(layer->l1 != nullptr, SVDQ_ERR_INVALID_ARG, "layer l1 must not be NULL when rank > 0");
-    REQUIRE(aligned16(layer->l1), SVDQ_ERR_ALIGNMENT, "layer l1 must be 16-byte aligned");
-  }
-  LinearWorkspace w = linear_ws_layout(b, m, layer->n, rank);
-  REQUIRE(workspace != nullptr && workspace_bytes >= w.total, SVDQ_ERR_WORKSPACE,
-          "workspace of %zu bytes needed (got %zu)", w.total, workspace ? workspace_bytes : (size_t)0);
-  REQUIRE(((uintptr_t)workspace & (kAlign - 1)) == 0, SVDQ_ERR_ALIGNMENT,
-          "workspace must be %zu-byte aligned", kAlign);
-  // exactly the standalone route: act kernel (+ ordered Z reduction when the
-  // channel groups are split), then the GEMM kernel
-  char* ws = (char*)workspace;
   uint8_t* qx = (uint8_t*)(ws + w.qx_off);
   uint16_t* as = (uint16_t*)(ws + w.as_off);
   float* z = rank > 0 ? (float*)(ws + w.z_off) : nullptr;
   ActPlan p = act_plan(b, m, rank);
   float* zpart = (rank > 0 && p.splits > 1) ? (float*)(ws + w.zpart_off) : z;
-  st = hip_status(launch_act_quant_down(x, b, m, rank, layer->smooth_inv, layer->l1, qx, as, zpart, p,
-                                        kActQuantInt4, 1.0f, stream),
-                  "act_quant_lowrank_down");
+  int st = hip_status(launch_act_quant_down(x, b, m, rank, layer->smooth_inv, layer->l1, qx, as, zpart, p,
+                                            kActQuantInt4, 1.0f, stream),
+                      "act_quant_lowrank_down");
   if (st) return st;
   if (rank > 0 && p.splits > 1) {
     st = hip_status(launch_z_reduce(zpart, p.splits, b, rank, z, stream), "z_reduce");
@@ -613,6 +592,63 @@ int svdq_linear(const uint16_t* x, const svdq_layer* layer, int b, void* y, int 
   }
   return hip_status(launch_gemm_up(qx, as, z, *layer, b, y, y_dtype, ws + w.gemm_off, stream),
                     "gemm_w4a4_lowrank_up");
+}
+
+// Checks shared by svdq_linear and svdq_linear_noalloc (everything but the
+// workspace).  Sets *done when there is nothing to launch (b == 0).
+static int check_linear(const uint16_t* x, const svdq_layer* layer, int b, void* y, int y_dtype, bool* done) {
+  *done = false;
+  int st = check_layer(layer);
+  if (st) return st;
+  REQUIRE(b >= 0, SVDQ_ERR_INVALID_ARG, "b must be >= 0 (got %d)", b);
+  REQUIRE(b <= SVDQ_MAX_DIM, SVDQ_ERR_UNSUPPORTED, "b must be <= %d (got %d)", SVDQ_MAX_DIM, b);
+  st = check_y(y, y_dtype, b);
+  if (st) return st;
+  if (b == 0) {
+    *done = true;
+    return SVDQ_OK;
+  }
+  REQUIRE(x != nullptr, SVDQ_ERR_INVALID_ARG, "x must not be NULL");
+  REQUIRE(aligned16(x), SVDQ_ERR_ALIGNMENT, "x must be 16-byte aligned");
+  if (layer->smooth_inv)
+    REQUIRE(aligned16(layer->smooth_inv), SVDQ_ERR_ALIGNMENT, "smooth_inv must be 16-byte aligned");
+  if (layer->rank > 0) {
+    REQUIRE(layer->l1 != nullptr, SVDQ_ERR_INVALID_ARG, "layer l1 must not be NULL when rank > 0");
+    REQUIRE(aligned16(layer->l1), SVDQ_ERR_ALIGNMENT, "layer l1 must be 16-byte aligned");
+  }
+  return SVDQ_OK;
+}
+
+int svdq_linear(const uint16_t* x, const svdq_layer* layer, int b, void* y, int y_dtype,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  bool done = false;
+  int st = check_linear(x, layer, b, y, y_dtype, &done);
+  if (st || done) return st;
+  LinearWorkspace w = linear_ws_layout(b, layer->m, layer->n, layer->rank);
+  REQUIRE(workspace != nullptr && workspace_bytes >= w.total, SVDQ_ERR_WORKSPACE,
+          "workspace of %zu bytes needed (got %zu)", w.total, workspace ? workspace_bytes : (size_t)0);
+  REQUIRE(((uintptr_t)workspace & (kAlign - 1)) == 0, SVDQ_ERR_ALIGNMENT,
+          "workspace must be %zu-byte aligned", kAlign);
+  return run_linear(x, layer, b, y, y_dtype, (char*)workspace, w, stream);
+}
+
+size_t svdq_linear_noalloc_max_workspace(void) { return kScratchBytes; }
+
+int svdq_linear_noalloc(const uint16_t* x, const svdq_layer* layer, int b, void* y, int y_dtype, void* stream) {
+  clear_error();
+  bool done = false;
+  int st = check_linear(x, layer, b, y, y_dtype, &done);
+  if (st || done) return st;
+  LinearWorkspace w = linear_ws_layout(b, layer->m, layer->n, layer->rank);
+  REQUIRE(w.total <= kScratchBytes, SVDQ_ERR_WORKSPACE,
+          "layer needs %zu bytes of workspace, above the %zu bytes of device scratch of svdq_linear_noalloc "
+          "(use svdq_linear with a caller workspace)",
+          w.total, kScratchBytes);
+  void* scratch = nullptr;
+  st = hip_status(scratch_buffer(&scratch), "device scratch lookup");
+  if (st) return st;
+  return run_linear(x, layer, b, y, y_dtype, (char*)scratch, w, stream);
 }
 
 size_t svdq_linear_unfused_workspace_size(int b, int m, int n, int rank, int group) {

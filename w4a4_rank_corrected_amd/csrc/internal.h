@@ -153,5 +153,10 @@ int launch_gemm_fp4_up(const uint8_t* qx, const uint8_t* ascale, const float* z,
                        void* y, int y_dtype, void* ws, void* stream);
 const char* hip_error_name(int err);
 
+// Device scratch of the allocation-free entry point (scratch.hip): the
+// current device's copy of a file-scope device array of kScratchBytes, its
+// address looked up once per device.  Returns a hipError_t value (0 = success).
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+int scratch_buffer(void** out);
 
 }  // namespace svdq
