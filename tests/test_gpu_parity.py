@@ -388,6 +388,38 @@ def test_streamk_splits_deterministic_and_match_oracle(S, b, m, n):
     assert err <= 1e-4
 
 
+def test_streamk_workspace_garbage_and_alternating_shapes(S):
+    """Stream-K partial slots and per-tile arrival counters live in the
+    caller's workspace: random initial bytes (any counter value a previous
+    launch or process could leave), two split shapes alternating on one
+    workspace, and repeats must all give the same bits and the oracle's Y."""
+    shapes = [(256, 4096, 256), (300, 2368, 520)]
+    need = max(S.svdq_linear_workspace_size(b, m, n, 16) for b, m, n in shapes)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda")
+    cases = []
+    for (b, m, n) in shapes:
+        sch = S.svdq_gemm_schedule(b, n, m)
+        assert sch["stream_k_workgroups"] > 0, sch
+        rng = np.random.default_rng(b * 7 + n)
+        xb = workloads.random_bf16_bits(rng, (b, m), 1.5)
+        x = LY.bf16_bits_to_f32(xb)
+        lay = _oracle_layer(rng, m, n, 16, x)
+        cases.append((dev_bf16(xb), device_layer(S, lay), O.linear(x, lay)["y"]))
+    first = {}
+    for rep in range(3):
+        for k, (xd, dl, ref) in enumerate(cases):
+            _say(f"stream-K workspace reuse rep={rep} shape={shapes[k]}")
+            y = S.svdq_linear(xd, dl, torch.float32, workspace=ws)
+            torch.cuda.synchronize()
+            if rep == 0:
+                first[k] = y
+                assert rel(y.cpu().numpy(), ref) <= 1e-4
+            else:
+                assert torch.equal(y, first[k])
+        if rep == 0:  # scribble over the workspace between rounds
+            ws.random_(0, 256)
+
+
 # The INT4 GEMM has four schedules (three-per-CU kernel with one tile per
 # workgroup; two-per-CU kernel with one tile per workgroup, all tiles by
 # stream-K, or a stream-K part followed by full rounds).  Each case finds the

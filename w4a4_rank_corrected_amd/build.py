@@ -7,6 +7,7 @@ the HIP kernels with hipcc for ``--offload-arch=gfx950``.  Objects go to
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -49,6 +50,50 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
+def kernel_resources(remarks: str) -> list:
+    """Per-kernel register and scratch use from the compiler's
+    ``-Rpass-analysis=kernel-resource-usage`` remarks: a list of dicts with
+    name, vgprs, agprs, sgprs, scratch (bytes per lane) and occupancy."""
+    rows, cur = [], None
+    keys = {"VGPRs": "vgprs", "AGPRs": "agprs", "SGPRs": "sgprs",
+            "ScratchSize [bytes/lane]": "scratch", "Occupancy [waves/SIMD]": "occupancy"}
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = {"name": m.group(1)}
+            rows.append(cur)
+            continue
+        if cur is None:
+            continue
+        for label, key in keys.items():
+            m = re.search(re.escape(label) + r": (\d+)", line)
+            if m:
+                cur[key] = int(m.group(1))
+    return rows
+
+
+def _compile_kernels(src: str, obj: str, verbose: bool) -> None:
+    """hipcc for gfx950 with the resource-usage remarks; fails the build if any
+    kernel spills to scratch (a spilled kernel is slow, and a spill around a
+    divergent region has produced wrong results in a GEMM build)."""
+    cmd = [HIPCC, *HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if res.returncode != 0:
+        out = "\n".join(l for l in res.stdout.splitlines() if "remark:" not in l)
+        raise RuntimeError(f"build step failed ({res.returncode}): {' '.join(cmd)}\n{out}")
+    rows = kernel_resources(res.stdout)
+    spilled = [r for r in rows if r.get("scratch", 0) > 0]
+    if spilled:
+        raise RuntimeError(f"{src}: kernels spill to scratch: " +
+                           ", ".join(f"{r['name']} ({r['scratch']} B/lane)" for r in spilled))
+    if verbose:
+        for r in rows:
+            print(f"  {r['name'][:100]}: {r.get('vgprs')} VGPRs, {r.get('sgprs')} SGPRs, "
+                  f"occupancy {r.get('occupancy')}, scratch {r.get('scratch')}", flush=True)
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link ``libsvdq.so``; returns its path."""
     if not os.path.exists(HIPCC):
@@ -61,7 +106,7 @@ def build(verbose: bool = False) -> str:
         objs.append(obj)
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        _compile_kernels(src, obj, verbose)
         objs.append(obj)
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs, "-lpthread"], verbose)

@@ -434,26 +434,35 @@ __global__ __launch_bounds__(256) void act8_quant_kernel(const uint16_t* __restr
 }
 
 // z[i][t] = sum over splits s (in order) of zpart[s][i][t]: one sum per
-// element, split 0 first, then 1, 2, ...  Each thread handles V consecutive
-// elements (V = 4: 16-byte loads and stores) and issues the loads of up to 16
-// splits before adding them, so a batch of partials costs one memory latency.
-template <int V>
+// element, split 0 first, then 1, 2, ...  Each thread handles 4 consecutive
+// elements (16-byte loads and stores) and issues the loads of up to 16 splits
+// before adding them, so a batch of partials costs one memory latency.
 __global__ void z_reduce_kernel(const float* __restrict__ zpart, int splits, size_t count,
                                 float* __restrict__ z) {
-  typedef float fv __attribute__((ext_vector_type(V)));
-  const size_t idx = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * V;
+  const size_t idx = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (idx >= count) return;
-  fv s;
+  f32x4 s;
   for (int k = 0; k < splits; k += 16) {
-    fv v[16];
+    f32x4 v[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u)
-      if (k + u < splits) v[u] = *reinterpret_cast<const fv*>(zpart + (size_t)(k + u) * count + idx);
+      if (k + u < splits) v[u] = *reinterpret_cast<const f32x4*>(zpart + (size_t)(k + u) * count + idx);
 #pragma unroll
     for (int u = 0; u < 16; ++u)
       if (k + u < splits) s = (k + u == 0) ? v[u] : s + v[u];
   }
-  *reinterpret_cast<fv*>(z + idx) = s;
+  *reinterpret_cast<f32x4*>(z + idx) = s;
+}
+
+// The same sums one element per thread (counts or pointers that do not allow
+// 16-byte accesses).
+__global__ void z_reduce1_kernel(const float* __restrict__ zpart, int splits, size_t count,
+                                 float* __restrict__ z) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= count) return;
+  float s = zpart[idx];
+  for (int k = 1; k < splits; ++k) s += zpart[(size_t)k * count + idx];
+  z[idx] = s;
 }
 
 }  // namespace
@@ -592,10 +601,10 @@ int launch_z_reduce(const float* zpart, int splits, int b, int rank, float* z, v
   // (the workspace is 256-byte aligned; each slice is count floats)
   const bool vec = count % 4 == 0 && ((uintptr_t)zpart & 15u) == 0 && ((uintptr_t)z & 15u) == 0;
   if (vec)
-    hipLaunchKernelGGL(z_reduce_kernel<4>, dim3((unsigned)((count / 4 + 255) / 256)), dim3(256), 0,
+    hipLaunchKernelGGL(z_reduce_kernel, dim3((unsigned)((count / 4 + 255) / 256)), dim3(256), 0,
                        (hipStream_t)stream, zpart, splits, count, z);
   else
-    hipLaunchKernelGGL(z_reduce_kernel<1>, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
+    hipLaunchKernelGGL(z_reduce1_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
                        (hipStream_t)stream, zpart, splits, count, z);
   return (int)hipGetLastError();
 }

@@ -139,6 +139,10 @@ void export_layer(const HostLayer& L, int m, int n, int rank, uint8_t* qw, uint1
 
 int hip_status(int err, const char* what) {
   if (err == 0) return SVDQ_OK;
+  if (err == kErrKernelScratch) {
+    set_error("%s: the kernel was built with register spills to scratch memory; refused", what);
+    return SVDQ_ERR_UNSUPPORTED;
+  }
   set_error("%s: HIP error %d (%s)", what, err, hip_error_name(err));
   return SVDQ_ERR_HIP;
 }

@@ -51,17 +51,21 @@
 //     out by stream-K among `slots` persistent workgroups (equal (tile, group)
 //     iteration ranges), which are dispatched first; the remaining full rounds
 //     run one tile per workgroup after them.  A stream-K workgroup walks its
-//     range in descending order, so a tile's earlier groups are finished first
-//     (as the first work item of a lower-numbered, earlier-dispatched
-//     workgroup), stored as an fp32 partial and published with a flag.  The
-//     workgroup holding the tile's last groups adds the low-rank branch, waits
-//     for all of the tile's flags (bounded spin), clears them, adds the
-//     partials in a fixed order and stores Y.  Results are deterministic for a
-//     shape and CU count.
+//     range piece by piece (a piece = the part of one tile inside the range).
+//     A whole tile is stored directly; any other piece writes its fp32 sums to
+//     a partial slot and registers its arrival on the tile's counter (a
+//     device-scope atomic).  The last piece of a tile to arrive adds all of
+//     the tile's partial slots in ascending group order and stores the tile.
+//     No workgroup waits for another, so correctness does not depend on the
+//     order or residency in which workgroups are dispatched, and results are
+//     deterministic for a shape and CU count (the summation order is fixed,
+//     whoever arrives last).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
+#include <unordered_map>
 #include <utility>
 
 #include "device_common.h"
@@ -221,11 +225,11 @@ struct GemmCfg {
 
 // 128 x 128 tile, 4 waves of 64 x 64; three workgroups share a CU (168
 // registers per lane), so one workgroup's barrier and LDS-latency phases
-// overlap the others' compute, and loads run one group ahead.  This kernel
-// runs schedules of one tile per workgroup only: built with the stream-K code
-// at this register budget, the compiler spills the stream-K loop's registers
-// to scratch, and that build returned wrong stream-K tiles on gfx950 (cause
-// not established), so stream-K launches use CfgSk.
+// overlap the others' compute, and loads run one group ahead.  This build
+// runs schedules of one tile per workgroup only: with the stream-K code it
+// needs more than 168 registers and would spill, which the build refuses
+// (every kernel of the library is checked for zero scratch at build time and
+// before its first launch), so stream-K launches use CfgSk.
 using Cfg = GemmCfg<128, 128, 64, 64, 3, 1>;
 // INT4 launches with a stream-K part: two workgroups per CU, loads two groups
 // ahead (no spills at 256 registers).
@@ -249,10 +253,10 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 struct StreamK {
   int P;                          // stream-K workgroups: blockIdx < P (0 = none)
   int T;                          // stream-K tiles: linear tiles [0, T)
-  long long U;                    // their (tile, group) iterations: T * G
-  float* partials;                // [P][TM*TN] fp32, in accumulator order
-  unsigned long long* flags;      // [P] publication epochs
-  unsigned long long epoch;       // this launch's epoch
+  unsigned U;                     // their (tile, group) iterations: T * G (U * P < 2^32)
+  float* partials;                // [2 P][TM*TN] fp32 (or i32), in accumulator order
+  unsigned long long* counters;   // [T] per-tile arrival counters: (tag << 32) | arrivals
+  unsigned tag;                   // this launch's tag (low 32 bits of its epoch)
 };
 
 // Non-negative E4M3 block-scale byte -> its value as fp16 bits (exact: E4M3
@@ -743,12 +747,36 @@ __device__ __forceinline__ void gemm_up_body(
   if constexpr (!SK) return;
 
   // ---- stream-K: iterations [u0, u1) of this workgroup, descending ----------
-  const int p = blockIdx.x;
-  const long long u0 = (long long)p * sk.U / sk.P, u1 = (long long)(p + 1) * sk.U / sk.P;
-  long long u = u1;
+  // A piece = the part of one tile inside this workgroup's range.  A whole
+  // tile is stored directly.  Otherwise the piece's sums go to a partial slot
+  // (slot 2p for the piece holding the range's last iteration, 2p + 1 for the
+  // one holding its first), and the workgroup registers its arrival on the
+  // tile's counter; the LAST of the tile's pieces to arrive adds all of the
+  // tile's partial slots in ascending group order (a fixed order, whoever
+  // arrives last) and stores the tile.  No workgroup ever waits for another,
+  // so nothing depends on the order in which workgroups are dispatched.
+  // Counters carry the launch's tag in their upper half: a counter left by
+  // another launch (or never initialised) reads as no arrivals; the finisher
+  // resets its tile's counter to (tag, 0), so a replay of the same launch
+  // (a captured graph) starts from zero arrivals too.
+  // Ranges in 32-bit arithmetic: the planner keeps U * P below 2^32.
+  const unsigned p = blockIdx.x, P = (unsigned)sk.P, U = sk.U, Gu = (unsigned)G;
+  // Partial slot layout, in 16-byte units: [wave][block k = bi BJ + bj][lane],
+  // so each store or load of a wave moves 1 KB contiguous.  The byte offset
+  // wave*16 KB + k KB + 16 lane is split into a per-lane base, a scalar
+  // 4 KB multiple and an instruction immediate below 4 KB (few scalar
+  // registers, no per-block vector offsets).
+  static_assert(BI * BJ == 16 && NT == 256, "partial layout: 16 blocks of 1 KB per wave");
+  const uint32_t part_voff = (uint32_t)(wave * 16384 + lane * 16);
+  auto partial_offset = [](int k) { return (uint32_t)((k & 3) * 1024); };
+  auto partial_soffset = [](int k) { return (k >> 2) * 4096; };
+  auto range_start = [&](unsigned q) { return q * U / P; };
+  const unsigned u0 = range_start(p), u1 = range_start(p + 1);
+  __shared__ int s_last;
+  unsigned u = u1;
   while (u > u0) {
-    const long long t = (u - 1) / G, ts = t * G;
-    const long long lo = u0 > ts ? u0 : ts;
+    const unsigned t = (u - 1) / Gu, ts = t * Gu;
+    const unsigned lo = u0 > ts ? u0 : ts;
     const int g0 = (int)(lo - ts), g1 = (int)(u - ts);
     int ti, tj;
     band_tile<kColBands>((int)t, tiles_m, tiles_n, ti, tj);
@@ -756,66 +784,71 @@ __device__ __forceinline__ void gemm_up_body(
     zero_acc();
     if (!POST && g1 == G) lowrank(i0, j0);  // the tile's last groups carry the low-rank branch
     main_branch(i0, j0, g0, g1);
-    if (g1 < G) {
-      // Publish this partial (this workgroup's first work item) for the
-      // finisher.  Partials are written and read only with device-coherent
-      // (sc1) buffer accesses, the cache policy of device-scope atomics, so
-      // no L2 writeback or invalidate is needed: each wave waits for its
-      // stores to complete (vmcnt 0) before the barrier after which the flag
-      // (a device-scope atomic) is raised.
-      const __amdgpu_buffer_rsrc_t rp = make_rsrc(sk.partials + (size_t)p * (TM * TN), TM * TN * 4);
+    if (g0 > 0 || g1 < G) {
+      // workgroups qlo .. qhi hold the tile's pieces (every stream-K workgroup
+      // has at least 8 iterations, so none is empty); q's piece is in its
+      // slot 0 when q's range ends inside this tile
+      unsigned qlo = p, qhi = p;
+      while (qlo > 0 && range_start(qlo) > ts) --qlo;
+      while (qhi + 1 < P && range_start(qhi + 1) < ts + Gu) ++qhi;
+      auto slot_of = [&](unsigned q) {
+        const unsigned last = range_start(q + 1) - 1;
+        return 2 * q + (last >= ts && last < ts + Gu ? 0u : 1u);
+      };
+      // Partials are written and read only with device-coherent (sc1) buffer
+      // accesses, so no L2 writeback or invalidate is needed: each wave waits
+      // for its stores to complete (vmcnt 0) before the barrier after which
+      // the arrival (a device-scope atomic) is registered.
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc(sk.partials + (size_t)slot_of(p) * (TM * TN), TM * TN * 4);
 #pragma unroll
       for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
         for (int bj = 0; bj < BJ; ++bj)
           __builtin_amdgcn_raw_buffer_store_b128(W8 ? __builtin_bit_cast(u32x4, iacc[bi][bj])
                                                     : __builtin_bit_cast(u32x4, acc[bi][bj]),
-                                                 rp, (uint32_t)(((bi * BJ + bj) * NT + tid) * 16), 0, kCoherent);
+                                                 rp, part_voff + partial_offset(bi * BJ + bj), partial_soffset(bi * BJ + bj),
+                                                 kCoherent);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
-      if (tid == 0) __hip_atomic_store(&sk.flags[p], sk.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      // finisher: the tile's earlier groups were published by workgroups
-      // qlo .. p-1 (lower-numbered, dispatched earlier, and each running that
-      // piece as its first work item, which waits on nothing)
-      int qlo = p;
-      while (qlo > 0 && (long long)qlo * sk.U / sk.P > ts) --qlo;
-      if (qlo < p) {
-        if (tid == 0) {
-          for (int q = p - 1; q >= qlo; --q) {
-            for (int spin = 0; spin < (1 << 24); ++spin) {  // bound: guards misuse of the workspace
-              if (__hip_atomic_load(&sk.flags[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == sk.epoch) break;
-              __builtin_amdgcn_s_sleep(2);
-            }
-            // each flag has exactly one consumer: clear it, so that a replay of
-            // this launch (same epoch, e.g. from a captured graph) waits again
-            __hip_atomic_store(&sk.flags[q], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) {
+        unsigned long long* cnt = sk.counters + t;
+        unsigned long long seen = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), next;
+        do {  // lock-free: a failed exchange means another piece arrived
+          next = (unsigned)(seen >> 32) == sk.tag ? seen + 1 : ((unsigned long long)sk.tag << 32) | 1ull;
+        } while (!__hip_atomic_compare_exchange_weak(cnt, &seen, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT));
+        const bool last = (unsigned)next == qhi - qlo + 1;
+        if (last) __hip_atomic_store(cnt, (unsigned long long)sk.tag << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = last ? 1 : 0;
+      }
+      __syncthreads();
+      const int last = __builtin_amdgcn_readfirstlane(s_last);
+      __syncthreads();  // s_last is rewritten by the next piece
+      if (!last) {
+        u = lo;
+        continue;
+      }
+      // the tile's partial slots in ascending group order (device-coherent loads)
+      for (unsigned q = qlo; q <= qhi; ++q) {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(sk.partials + (size_t)slot_of(q) * (TM * TN), TM * TN * 4);
+#pragma unroll
+        for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < BJ; ++bj) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rq, part_voff + partial_offset(bi * BJ + bj),
+                                                                 partial_soffset(bi * BJ + bj), kCoherent);
+            if constexpr (W8)
+              iacc[bi][bj] = q == qlo ? __builtin_bit_cast(i32x4, v) : iacc[bi][bj] + __builtin_bit_cast(i32x4, v);
+            else
+              acc[bi][bj] = q == qlo ? __builtin_bit_cast(f32x4, v) : acc[bi][bj] + __builtin_bit_cast(f32x4, v);
           }
-        }
-        // the flag loads have completed before the barrier; the partials are
-        // then read with device-coherent loads, in the fixed order p-1 .. qlo
-        __syncthreads();
-        for (int q = p - 1; q >= qlo; --q) {
-          const __amdgpu_buffer_rsrc_t rq = make_rsrc(sk.partials + (size_t)q * (TM * TN), TM * TN * 4);
-#pragma unroll
-          for (int bi = 0; bi < BI; ++bi)
-#pragma unroll
-            for (int bj = 0; bj < BJ; ++bj) {
-              const auto v = __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)(((bi * BJ + bj) * NT + tid) * 16), 0,
-                                                                   kCoherent);
-              if constexpr (W8)
-                iacc[bi][bj] += __builtin_bit_cast(i32x4, v);
-              else
-                acc[bi][bj] += __builtin_bit_cast(f32x4, v);
-            }
-        }
       }
-      if constexpr (POST) {
-        scale_sums(i0, j0);
-        lowrank(i0, j0);
-      }
-      store_tile(i0, j0);
     }
+    if constexpr (POST) {
+      scale_sums(i0, j0);
+      lowrank(i0, j0);
+    }
+    store_tile(i0, j0);
     u = lo;
   }
 }
@@ -863,47 +896,60 @@ struct Operands {
   int n, rank;
 };
 
+// A GEMM kernel that uses scratch memory (register spills) is refused before
+// its first launch: spills cost bandwidth, and a spill around a divergent
+// region once produced wrong results in a GEMM build.  The build checks the
+// same; this guards a library rebuilt with another compiler.  Queried once per
+// kernel and process.
+int scratch_free(const void* kernel) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, int> seen;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = seen.find(kernel);
+  if (it != seen.end()) return it->second;
+  hipFuncAttributes attr{};
+  const hipError_t e = hipFuncGetAttributes(&attr, kernel);
+  const int status = e != hipSuccess ? (int)e : (attr.localSizeBytes != 0 ? kErrKernelScratch : 0);
+  seen[kernel] = status;
+  return status;
+}
+
+template <class K, class... Args>
+int launch_checked(K kernel, const GemmPlan& plan, int threads, hipStream_t st, Args... args) {
+  const int ok = scratch_free(reinterpret_cast<const void*>(kernel));
+  if (ok != 0) return ok;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)plan.grid), dim3(threads), 0, st, args...);
+  return (int)hipGetLastError();
+}
+
 template <bool OUT_BF16, int FMT>
 int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, const Operands& L, int b,
                  void* y, const GemmPlan& plan, void* ws, hipStream_t st, float txw = 1.0f) {
-  StreamK sk{0, 0, 0, nullptr, nullptr, 0};
+  StreamK sk{0, 0, 0, nullptr, nullptr, 0u};
   if (plan.streamk) {
     sk.P = plan.sk_grid;
     sk.T = plan.sk_tiles;
-    sk.U = (long long)plan.sk_tiles * plan.G;
+    sk.U = (unsigned)plan.sk_tiles * (unsigned)plan.G;
     sk.partials = reinterpret_cast<float*>(ws);
-    sk.flags = reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(ws) + plan.partial_bytes);
-    sk.epoch = next_launch_epoch();
+    sk.counters = reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(ws) + plan.partial_bytes);
+    sk.tag = (unsigned)next_launch_epoch();
   }
+#define SVDQ_GEMM_ARGS qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m, \
+                       plan.tiles_n, y, sk, txw
   if constexpr (FMT == kFmtInt8) {
     if (plan.wg_per_cu == Cfg8Dp::WG_PER_CU && !plan.streamk)
-      hipLaunchKernelGGL((gemm_w8a8_up_kernel<Cfg8Dp, OUT_BF16, false>), dim3((unsigned)plan.grid), dim3(Cfg8Dp::NT),
-                         0, st, qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
-                         plan.tiles_n, y, sk, txw);
-    else
-      hipLaunchKernelGGL((gemm_w8a8_up_kernel<Cfg8, OUT_BF16, true>), dim3((unsigned)plan.grid), dim3(Cfg8::NT), 0,
-                         st, qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
-                         plan.tiles_n, y, sk, txw);
-  }
-  else if constexpr (FMT == kFmtFp4) {
+      return launch_checked(gemm_w8a8_up_kernel<Cfg8Dp, OUT_BF16, false>, plan, Cfg8Dp::NT, st, SVDQ_GEMM_ARGS);
+    return launch_checked(gemm_w8a8_up_kernel<Cfg8, OUT_BF16, true>, plan, Cfg8::NT, st, SVDQ_GEMM_ARGS);
+  } else if constexpr (FMT == kFmtFp4) {
     if (plan.wg_per_cu == CfgF4Dp::WG_PER_CU && !plan.streamk)
-      hipLaunchKernelGGL((gemm_fp4_up_kernel<CfgF4Dp, OUT_BF16, false>), dim3((unsigned)plan.grid),
-                         dim3(CfgF4Dp::NT), 0, st, qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G,
-                         L.rank, plan.tiles_m, plan.tiles_n, y, sk, txw);
-    else
-      hipLaunchKernelGGL((gemm_fp4_up_kernel<CfgF4, OUT_BF16, true>), dim3((unsigned)plan.grid), dim3(CfgF4::NT), 0,
-                         st, qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
-                         plan.tiles_n, y, sk, txw);
+      return launch_checked(gemm_fp4_up_kernel<CfgF4Dp, OUT_BF16, false>, plan, CfgF4Dp::NT, st, SVDQ_GEMM_ARGS);
+    return launch_checked(gemm_fp4_up_kernel<CfgF4, OUT_BF16, true>, plan, CfgF4::NT, st, SVDQ_GEMM_ARGS);
+  } else {
+    if (plan.wg_per_cu == Cfg::WG_PER_CU && !plan.streamk)
+      return launch_checked(gemm_w4a4_up_kernel<Cfg, OUT_BF16, false>, plan, Cfg::NT, st, SVDQ_GEMM_ARGS);
+    return launch_checked(gemm_w4a4_up_kernel<CfgSk, OUT_BF16, true>, plan, CfgSk::NT, st, SVDQ_GEMM_ARGS);
   }
-  else if (plan.wg_per_cu == Cfg::WG_PER_CU && !plan.streamk)
-    hipLaunchKernelGGL((gemm_w4a4_up_kernel<Cfg, OUT_BF16, false>), dim3((unsigned)plan.grid), dim3(Cfg::NT), 0, st,
-                       qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
-                       plan.tiles_n, y, sk, txw);
-  else
-    hipLaunchKernelGGL((gemm_w4a4_up_kernel<CfgSk, OUT_BF16, true>), dim3((unsigned)plan.grid), dim3(CfgSk::NT), 0,
-                       st, qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m,
-                       plan.tiles_n, y, sk, txw);
-  return (int)hipGetLastError();
+#undef SVDQ_GEMM_ARGS
 }
 
 }  // namespace
@@ -939,9 +985,13 @@ void plan_rounds(GemmPlan& p, long long slots, bool split_last_round) {
     p.sk_tiles = (int)(T - dp);
     p.sk_grid = (int)std::max(1LL, std::min(slots, (long long)p.sk_tiles * p.G / 8));
     p.grid = (int)(p.sk_grid + dp);
-  } else {
-    p.grid = (int)T;
+    // the kernel splits the iterations in 32-bit arithmetic: U * P < 2^32
+    if ((unsigned long long)p.sk_tiles * (unsigned long long)p.G * (unsigned long long)p.sk_grid >= (1ull << 32)) {
+      p.streamk = 0;
+      p.sk_tiles = p.sk_grid = 0;
+    }
   }
+  if (!p.streamk) p.grid = (int)T;
 }
 }  // namespace
 
@@ -969,8 +1019,8 @@ GemmPlan gemm_plan(int b, int n, int m, int cus, int fmt) {
   }
   const long long T = (long long)p.tiles_m * p.tiles_n;
   const long long max_sk = std::max(1LL, std::min((long long)kMaxSkWgPerCu * kMaxCUs, T * p.G / 8));
-  p.partial_bytes = (size_t)max_sk * Cfg::TM * Cfg::TN * 4;
-  p.ws_bytes = p.streamk || cus <= 0 ? p.partial_bytes + (size_t)max_sk * 8 : 0;
+  p.partial_bytes = (size_t)(2 * max_sk) * Cfg::TM * Cfg::TN * 4;  // two partial slots per workgroup
+  p.ws_bytes = p.streamk || cus <= 0 ? p.partial_bytes + (size_t)std::max(1LL, T) * 8 : 0;
   return p;
 }
 

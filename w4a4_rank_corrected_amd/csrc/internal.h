@@ -152,6 +152,8 @@ int launch_gemm8_up(const int8_t* qx, const uint16_t* ascale, const float* z, co
 int launch_gemm_fp4_up(const uint8_t* qx, const uint8_t* ascale, const float* z, const svdq_fp4_layer& L, int b,
                        void* y, int y_dtype, void* ws, void* stream);
 const char* hip_error_name(int err);
+// Launcher status (not a hipError_t) of a kernel that would use scratch memory.
+constexpr int kErrKernelScratch = -1000;
 
 // Device scratch of the allocation-free entry point (scratch.hip): the
 // current device's copy of a file-scope device array of kScratchBytes, its
