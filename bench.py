@@ -13,11 +13,16 @@ Timed region ("cold"): the steps rotate over several independently seeded
 input + weight sets whose footprint exceeds the 256 MB last-level cache, so a
 step does not find its layer's weights or activations cached by the previous
 step.  Also reported: the same steps on one set ("warm"), the low-rank
-overhead t(rank r) / t(rank 0, same codes and scales) - 1, and the one-call
-``svdq_linear`` entry point.
+overhead t(rank r) / t(rank 0, same codes and scales) - 1 from rank-r and
+rank-0 steps interleaved on one set (median HIP-event step times), the
+one-call ``svdq_linear`` entry point, and the GEMM's fractions of the i8 MFMA
+peak, of HBM bandwidth and of the fp32 FMA peak its scale epilogue needs.
 
 Prints ONE JSON line.  Default workload: the FLUX-shaped fused QKV projection
-(b=4608 tokens, m=3072, n=9216, rank 32, group 64).
+(b=4608 tokens, m=3072, n=9216, rank 32, group 64).  The other FLUX- and
+PixArt-shaped layers are timed by the same method in the same run and reported
+under ``extra_configs`` (their cold sets are copies of one prepared set at
+fresh addresses, which keeps the run short).
 
 Extra modes (used with rocprofv3 runs):
   --copy-check               also run a plain device copy of known size, which
@@ -59,6 +64,8 @@ sys.path.insert(0, ROOT)
 I8_PEAK_TOPS = 5000.0      # MI355X dense i8 MFMA, TOP/s
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 / bf16 MFMA, TFLOP/s
+FP32_FMA_PEAK_TFLOPS = 78.6  # MI355X fp32 FMA without packed math: 256 CUs x 64 lanes x 2 flops x 2.4 GHz
+EXTRA_CONFIGS = "flux_fc2,flux_single_fc,flux_single_out,flux_single_fc_b256,flux_single_out_b256,pixart_fc1"
 METRIC = "fused W4A4+low-rank linear TOPS (2·b·m·n/s), FLUX shapes; % of i8 MFMA peak"
 GEMM_KERNEL = "gemm_w4a4_up_kernel"
 # sources whose text defines the GEMM kernel and its launch plan
@@ -630,6 +637,10 @@ def main():
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="BLAS threads for the oracle timing (0 = all the process may use)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra-configs", default=EXTRA_CONFIGS,
+                    help="further workloads timed by the same method in the same run (comma-separated; "
+                         "'' for none)")
+    ap.add_argument("--extra-steps", type=int, default=30, help="timed steps of each extra configuration")
     ap.add_argument("--copy-check", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -689,6 +700,41 @@ def main():
     if args.fp4 is not None:
         fp4_compare(cfg, args.fp4, args)
         return
+    res = measure_layer(cfg, args, distinct_sets=True, steps=args.steps, warmup=args.warmup,
+                        copy_check=args.copy_check)
+    extra = {}
+    if args.extra_configs:
+        for name in [w for w in args.extra_configs.split(",") if w and w != cfg.name]:
+            log(f"bench: extra configuration {name}")
+            extra[name] = summarize_extra(measure_layer(workloads.CONFIGS[name], args, distinct_sets=False,
+                                                        steps=args.extra_steps, warmup=args.warmup))
+    line = headline(res, cfg, args)
+    if extra:
+        line["extra_configs"] = extra
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(res["inp"], cfg,
+                                            min(args.cpu_rows, res["b"]) if args.cpu_rows else res["b"],
+                                            args.cpu_threads)
+    print(json.dumps(line), flush=True)
+
+
+def measure_layer(cfg, args, distinct_sets, steps, warmup, copy_check=False):
+    """Time one layer configuration through the C ABI (one step = the act
+    kernel + its Z reduction, then the GEMM kernel).
+
+    Cold: the steps rotate over enough input + weight sets to exceed the
+    last-level cache.  With distinct_sets every set is drawn and prepared from
+    its own seed; otherwise one prepared set is copied to fresh device buffers
+    (the same values at other addresses: just as cold, a fraction of the
+    preparation time).  Reported: wall time per step between synchronisations
+    (mean), and per kernel the mean and median of HIP events recorded on the
+    launch stream; the same on one set (warm); the low-rank overhead from
+    rank-r and rank-0 steps interleaved on one set (median of HIP-event step
+    times each, same codes and scales); and the one-call svdq_linear (warm)."""
+    import torch
+    import workloads
+    import w4a4_rank_corrected_amd as S
+
     m, n = cfg.m, cfg.n
     rank_svd = cfg.rank if args.rank is None else args.rank
     dev = torch.device("cuda:0")
@@ -709,16 +755,23 @@ def main():
         y = torch.empty((x.shape[0], n), dtype=out_dtype, device=dev)
         return {"inp": inp, "x": x, "layer": layer, "y": y, "prep_s": prep}
 
+    def copy_set(st):
+        lay = st["layer"]
+        c = lambda t: None if t is None else t.clone()
+        layer = S.DeviceLayer.from_tensors(m, n, lay.rank, c(lay.qw), c(lay.wscale), c(lay.l1), c(lay.l2),
+                                           c(lay.smooth_inv), c(lay.bias))
+        return {"x": st["x"].clone(), "layer": layer, "y": torch.empty_like(st["y"]), "prep_s": st["prep_s"]}
+
     log(f"bench: workload {cfg.name} b={cfg.rows or cfg.b} m={m} n={n}")
     sets = [build_set(0)]
     b = sets[0]["x"].shape[0]
     r = int(sets[0]["layer"].rank)
-    k1_bytes, k2_bytes = algorithmic_bytes(b, m, n, r)
     per_set, n_sets = set_plan(cfg, r, args.out)
     for s in range(1, n_sets):
-        sets.append(build_set(s))
-        del sets[-1]["inp"]
-    log(f"bench: {n_sets} input+weight sets of {per_set / 2**20:.0f} MiB, rank {r}, "
+        sets.append(build_set(s) if distinct_sets else copy_set(sets[0]))
+        sets[-1].pop("inp", None)
+    log(f"bench: {n_sets} input+weight sets of {per_set / 2**20:.0f} MiB "
+        f"({'each drawn and prepared' if distinct_sets else 'copies of one prepared set'}), rank {r}, "
         f"host preparation {sets[0]['prep_s']:.1f} s per set")
 
     G = m // 64
@@ -743,36 +796,51 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
-    def timed(pick, steps, layer_of=None):
+    def timed(pick, nsteps, layer_of=None):
         """Steps bracketed by synchronize on both sides; per-kernel HIP events."""
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nsteps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for k in range(steps):
+        for k in range(nsteps):
             st = pick(k)
             step(st, layer_of(st) if layer_of else None, evs[k])
         torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) * 1e3 / steps
-        k1 = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-        k2 = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-        return wall, k1, k2
+        wall = (time.perf_counter() - t0) * 1e3 / nsteps
+        k1 = [e[0].elapsed_time(e[1]) for e in evs]
+        k2 = [e[1].elapsed_time(e[2]) for e in evs]
+        return {"wall": wall, "k1_mean": float(np.mean(k1)), "k2_mean": float(np.mean(k2)),
+                "k1_median": float(np.median(k1)), "k2_median": float(np.median(k2)),
+                "step_median": float(np.median([e[0].elapsed_time(e[2]) for e in evs]))}
 
     # warm-up over every set, then the timed (cold, rotating) region
-    for k in range(max(args.warmup, n_sets)):
+    for k in range(max(warmup, n_sets)):
         step(sets[k % n_sets])
     torch.cuda.synchronize()
-    log(f"bench: timing {args.steps} steps rotating over {n_sets} sets")
-    ms_per_step, k1_ms, k2_ms = timed(lambda k: sets[k % n_sets], args.steps)
+    log(f"bench: timing {steps} steps rotating over {n_sets} sets")
+    cold = timed(lambda k: sets[k % n_sets], steps)
 
-    # warm: one set, repeated
-    log("bench: warm and rank-0 comparisons")
-    warm_ms, warm_k1, warm_k2 = timed(lambda k: sets[0], args.steps)
-    # the same codes and scales without the low-rank branch
+    log("bench: warm steps, rank-0 steps interleaved with rank-r steps, svdq_linear")
+    warm = timed(lambda k: sets[0], steps)
+    # the same codes and scales without the low-rank branch, interleaved step
+    # by step with the rank-r layer (same clocks and cache state for both)
     l0 = sets[0]["layer"]
     layer0 = S.DeviceLayer.from_tensors(m, n, 0, l0.qw, l0.wscale, None, None, l0.smooth_inv, l0.bias)
     for _ in range(3):
         step(sets[0], layer0)
-    r0_ms, r0_k1, r0_k2 = timed(lambda k: sets[0], args.steps, lambda st: layer0)
+        step(sets[0])
+    pair = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        step(sets[0], None, pair[k][0])
+        step(sets[0], layer0, pair[k][1])
+    torch.cuda.synchronize()
+    med = lambda f: float(np.median([f(e) for e in pair]))
+    ov = {"ms_rank_r": med(lambda e: e[0][0].elapsed_time(e[0][2])),
+          "ms_rank_0": med(lambda e: e[1][0].elapsed_time(e[1][2])),
+          "k1_ms_rank_r": med(lambda e: e[0][0].elapsed_time(e[0][1])),
+          "k2_ms_rank_r": med(lambda e: e[0][1].elapsed_time(e[0][2])),
+          "k1_ms_rank_0": med(lambda e: e[1][0].elapsed_time(e[1][1])),
+          "k2_ms_rank_0": med(lambda e: e[1][1].elapsed_time(e[1][2]))}
 
     # the one-call entry point (K1 + K2 inside the library), warm
     ws_lin = torch.empty(max(S.svdq_linear_workspace_size(b, m, n, r), 1), dtype=torch.uint8, device=dev)
@@ -780,31 +848,75 @@ def main():
         S.svdq_linear(sets[0]["x"], l0, out_dtype, y=sets[0]["y"], workspace=ws_lin, stream=stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         S.svdq_linear(sets[0]["x"], l0, out_dtype, y=sets[0]["y"], workspace=ws_lin, stream=stream)
     torch.cuda.synchronize()
-    linear_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+    linear_ms = (time.perf_counter() - t1) * 1e3 / steps
 
-    if args.copy_check:
+    if copy_check:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         for _ in range(2):
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"bench: copy check of {COPY_BYTES} bytes done")
+    return {"cfg": cfg, "b": b, "m": m, "n": n, "r": r, "n_sets": n_sets, "per_set": per_set,
+            "cold": cold, "warm": warm, "overhead": ov, "linear_ms": linear_ms, "prep_s": sets[0]["prep_s"],
+            "schedule": S.svdq_gemm_schedule(b, n, m), "inp": sets[0].get("inp"),
+            "distinct_sets": distinct_sets, "steps": steps}
 
+
+def kernel_fractions(b, m, n, r, k1_ms, k2_ms):
+    """Roofline fractions of the two kernels at the given mean durations: the
+    GEMM against the i8 MFMA peak (2 b m n ops), against HBM (its algorithmic
+    bytes) and against the fp32 FMA peak for its scale epilogue (2 FMAs per
+    output element and channel group, 4 b n (m/64) flops; packed FP32 is not
+    used, so the peak is 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz =
+    78.6 TFLOP/s); the act kernel against HBM."""
     ops = 2.0 * b * m * n
-    value = ops / (ms_per_step * 1e-3) / 1e12
-    k2_tops = ops / (k2_ms * 1e-3) / 1e12
+    k1_bytes, k2_bytes = algorithmic_bytes(b, m, n, r)
+    epi = 4.0 * b * n * (m // 64)
+    return {"gemm_TOPs": ops / (k2_ms * 1e-3) / 1e12,
+            "gemm_frac_i8_peak": ops / (k2_ms * 1e-3) / 1e12 / I8_PEAK_TOPS,
+            "gemm_hbm_frac": k2_bytes / (k2_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "gemm_epilogue_fma_frac": epi / (k2_ms * 1e-3) / 1e12 / FP32_FMA_PEAK_TFLOPS,
+            "act_hbm_frac": k1_bytes / (k1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "gemm_algorithmic_bytes": k2_bytes, "act_algorithmic_bytes": k1_bytes}
+
+
+def summarize_extra(res):
+    """Compact record of one extra configuration (same method as the headline)."""
+    b, m, n, r = res["b"], res["m"], res["n"], res["r"]
+    c, ov = res["cold"], res["overhead"]
+    f = kernel_fractions(b, m, n, r, c["k1_mean"], c["k2_mean"])
+    return {"b": b, "m": m, "n": n, "rank": r,
+            "value_TOPs": round(2.0 * b * m * n / (c["wall"] * 1e-3) / 1e12, 2),
+            "ms_per_step": round(c["wall"], 5),
+            "act_quant_down_ms": round(c["k1_mean"], 5), "gemm_w4a4_up_ms": round(c["k2_mean"], 5),
+            "gemm_frac_i8_peak": round(f["gemm_frac_i8_peak"], 4), "gemm_hbm_frac": round(f["gemm_hbm_frac"], 4),
+            "gemm_epilogue_fma_frac": round(f["gemm_epilogue_fma_frac"], 4),
+            "act_hbm_frac": round(f["act_hbm_frac"], 4),
+            "lowrank_overhead": round(ov["ms_rank_r"] / ov["ms_rank_0"] - 1.0, 4),
+            "schedule": res["schedule"],
+            "timing": f"cold: {res['steps']} steps rotating over {res['n_sets']} copies of one prepared set"}
+
+
+def headline(res, cfg, args):
+    """The benchmark's JSON line for the main configuration."""
+    b, m, n, r = res["b"], res["m"], res["n"], res["r"]
+    c, w, ov = res["cold"], res["warm"], res["overhead"]
+    ops = 2.0 * b * m * n
+    value = ops / (c["wall"] * 1e-3) / 1e12
+    f = kernel_fractions(b, m, n, r, c["k1_mean"], c["k2_mean"])
     traffic = load_traffic(cfg.name) if args.out == "bf16" and args.rank is None else None
-    res = {
+    return {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "TOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(c["wall"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -812,31 +924,35 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "b": b, "m": m, "n": n, "rank": r, "group": 64,
                    "out": args.out, "parallelism": "none (1 GPU)",
-                   "timing": f"cold: steps rotate over {n_sets} seeded input+weight sets "
-                             f"({n_sets * per_set / 2**20:.0f} MiB)"},
-        "roofline": {"bound": "mfma", "achieved": round(k2_tops, 2), "peak": I8_PEAK_TOPS,
-                     "unit": "TOP/s", "frac": round(k2_tops / I8_PEAK_TOPS, 4),
+                   "timing": f"cold: steps rotate over {res['n_sets']} seeded input+weight sets "
+                             f"({res['n_sets'] * res['per_set'] / 2**20:.0f} MiB)"},
+        "roofline": {"bound": "mfma", "achieved": round(f["gemm_TOPs"], 2), "peak": I8_PEAK_TOPS,
+                     "unit": "TOP/s", "frac": round(f["gemm_frac_i8_peak"], 4),
                      "traffic": None if traffic is None else round(traffic["traffic_bytes"])},
-        "kernels": {"act_quant_down_ms": round(k1_ms, 5), "gemm_w4a4_up_ms": round(k2_ms, 5),
-                    "act_quant_down_GBs": round(k1_bytes / (k1_ms * 1e-3) / 1e9, 1),
-                    "act_quant_down_hbm_frac": round(k1_bytes / (k1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                    "gemm_w4a4_up_TOPs": round(k2_tops, 2),
-                    "gemm_algorithmic_bytes": k2_bytes, "act_algorithmic_bytes": k1_bytes,
+        "kernels": {"act_quant_down_ms": round(c["k1_mean"], 5), "gemm_w4a4_up_ms": round(c["k2_mean"], 5),
+                    "act_quant_down_median_ms": round(c["k1_median"], 5),
+                    "gemm_w4a4_up_median_ms": round(c["k2_median"], 5),
+                    "act_quant_down_GBs": round(f["act_algorithmic_bytes"] / (c["k1_mean"] * 1e-3) / 1e9, 1),
+                    "act_quant_down_hbm_frac": round(f["act_hbm_frac"], 4),
+                    "gemm_w4a4_up_TOPs": round(f["gemm_TOPs"], 2),
+                    "gemm_hbm_frac": round(f["gemm_hbm_frac"], 4),
+                    "gemm_epilogue_fma_frac": round(f["gemm_epilogue_fma_frac"], 4),
+                    "gemm_algorithmic_bytes": f["gemm_algorithmic_bytes"],
+                    "act_algorithmic_bytes": f["act_algorithmic_bytes"],
                     "gemm_hbm_fetch_bytes": None if traffic is None else round(traffic["fetch_bytes"]),
                     "gemm_hbm_write_bytes": None if traffic is None else round(traffic["write_bytes"]),
-                    "gemm_schedule": S.svdq_gemm_schedule(b, n, m)},
-        "warm": {"ms_per_step": round(warm_ms, 5), "value": round(ops / (warm_ms * 1e-3) / 1e12, 2),
-                 "act_quant_down_ms": round(warm_k1, 5), "gemm_w4a4_up_ms": round(warm_k2, 5),
-                 "svdq_linear_ms": round(linear_ms, 5)},
-        "lowrank_overhead": {"rank": r, "ms_rank_r": round(warm_ms, 5), "ms_rank_0": round(r0_ms, 5),
-                             "overhead": round(warm_ms / r0_ms - 1.0, 4),
-                             "k1_ms_rank_0": round(r0_k1, 5), "k2_ms_rank_0": round(r0_k2, 5)},
-        "prep_s": round(sets[0]["prep_s"], 2),
+                    "gemm_schedule": res["schedule"]},
+        "warm": {"ms_per_step": round(w["wall"], 5), "value": round(ops / (w["wall"] * 1e-3) / 1e12, 2),
+                 "act_quant_down_ms": round(w["k1_median"], 5), "gemm_w4a4_up_ms": round(w["k2_median"], 5),
+                 "svdq_linear_ms": round(res["linear_ms"], 5)},
+        "lowrank_overhead": {"rank": r, "ms_rank_r": round(ov["ms_rank_r"], 5), "ms_rank_0": round(ov["ms_rank_0"], 5),
+                             "overhead": round(ov["ms_rank_r"] / ov["ms_rank_0"] - 1.0, 4),
+                             "k1_ms_rank_r": round(ov["k1_ms_rank_r"], 5), "k2_ms_rank_r": round(ov["k2_ms_rank_r"], 5),
+                             "k1_ms_rank_0": round(ov["k1_ms_rank_0"], 5), "k2_ms_rank_0": round(ov["k2_ms_rank_0"], 5),
+                             "method": "rank-r and rank-0 steps interleaved on one set (warm), "
+                                       "median of HIP-event step times"},
+        "prep_s": round(res["prep_s"], 2),
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(sets[0]["inp"], cfg,
-                                           min(args.cpu_rows, b) if args.cpu_rows else b, args.cpu_threads)
-    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

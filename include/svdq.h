@@ -59,7 +59,8 @@ typedef enum svdq_status {
   SVDQ_ERR_NONFINITE = 4,      /* NaN / Inf in a preparation input */
   SVDQ_ERR_NO_CONVERGENCE = 5, /* truncated SVD did not converge */
   SVDQ_ERR_WORKSPACE = 6,      /* workspace missing or too small */
-  SVDQ_ERR_HIP = 7             /* a HIP launch or runtime call failed */
+  SVDQ_ERR_HIP = 7,            /* a HIP launch or runtime call failed */
+  SVDQ_ERR_IO = 8              /* a layer file could not be written or read, or is not valid */
 } svdq_status;
 
 enum { SVDQ_OUT_BF16 = 0, SVDQ_OUT_F32 = 1 };
@@ -144,6 +145,50 @@ int svdq_prepare_weights_refined(const float* W, const float* act_amax, const ui
                                  int iters, uint8_t* qw, uint16_t* wscale, uint16_t* l1, uint16_t* l2,
                                  float* lambda, float* smooth_inv, float* residual, float* alpha_out,
                                  int* iter_out, double* rel_err_out);
+
+/* ---------------------------------------------------------------------------
+ * HOST: stored layers ([Review] sec. 5 Algorithm 1 step 9: keep the protected
+ * factors, the quantized residual, its scales and the smoothing transform, so
+ * a layer is prepared once and loaded afterwards).
+ *
+ * A prepared INT4 layer as HOST arrays in the layouts of svdq_layer
+ * (caller-owned; what svdq_prepare_weights and svdq_append_lora produce):
+ *   lambda, smooth_inv fp32 [m]; qw [m/64][n][32]; wscale fp16 [m/64][n];
+ *   l1 bf16 [rank][m], l2 bf16 [n][rank] (NULL iff rank == 0); bias bf16 [n]
+ *   or NULL; alpha: the migration strength it was prepared with (recorded).
+ * ------------------------------------------------------------------------- */
+typedef struct svdq_host_layer {
+  int32_t m, n, rank, group;
+  float alpha;
+  const float* lambda;
+  const float* smooth_inv;
+  const uint8_t* qw;
+  const uint16_t* wscale;
+  const uint16_t* l1;
+  const uint16_t* l2;
+  const uint16_t* bias;
+} svdq_host_layer;
+
+/* Write `layer` to `path` (versioned binary file: a 64-byte header with the
+ * dimensions, rank, group, alpha, a bias flag and an FNV-1a checksum of the
+ * payload, then the arrays in the order above).  The file is written under a
+ * temporary name and renamed, so readers never see a partial file.
+ * SVDQ_ERR_INVALID_ARG / SVDQ_ERR_UNSUPPORTED for bad arguments (as
+ * svdq_prepare_weights), SVDQ_ERR_IO if the file cannot be written. */
+int svdq_save_layer(const char* path, const svdq_host_layer* layer);
+
+/* Read the header of a layer file: m, n, rank, has_bias (0/1), alpha
+ * (nullable).  SVDQ_ERR_IO if the file is missing, not a layer file, of
+ * another version, or its payload size does not match its dimensions. */
+int svdq_load_layer_info(const char* path, int32_t* m, int32_t* n, int32_t* rank, int32_t* has_bias,
+                         float* alpha);
+
+/* Read a layer file into caller HOST buffers sized from svdq_load_layer_info
+ * (l1 / l2 may be NULL iff rank == 0, bias iff none is stored).  The buffers
+ * are written only if the whole payload is present and its checksum matches;
+ * otherwise SVDQ_ERR_IO and the buffers are untouched. */
+int svdq_load_layer(const char* path, float* lambda, float* smooth_inv, uint8_t* qw, uint16_t* wscale,
+                    uint16_t* l1, uint16_t* l2, uint16_t* bias);
 
 /* HOST: the INT4 group quantization step alone ([Review] Algorithm 1 step 5 with
  * Eq.(1)): R fp32 [m][n] -> qw [m/64][n][32], wscale fp16 [m/64][n]. */

@@ -21,7 +21,9 @@ step is pinned against the oracle at that size:
     applied to the library's own residual;
   * the LoRA-widened factors (sec. 7 Eq.(13)) bit-exact against the oracle;
   * then the whole layer through svdq_linear against the oracle's linear on
-    that same layer, on sampled rows: bf16 output <= 2e-3, fp32 <= 1e-4.
+    that same layer, on sampled rows: bf16 output <= 2e-3, fp32 <= 1e-4;
+  * the layer written to a layer file and read back (Algorithm 1 step 9)
+    gives the same Y bit for bit.
 
 Inputs are the seeded FLUX-shaped synthetic layers (workloads.py); every
 expected value comes from the oracle.
@@ -60,7 +62,7 @@ def rel(a, b):
 
 
 @pytest.mark.parametrize("cfg", ["flux_qkv", "flux_single_fc"])
-def test_library_prepared_full_size_layer(S, cfg):
+def test_library_prepared_full_size_layer(S, cfg, tmp_path):
     inp = workloads.make_inputs(cfg)
     c = inp["cfg"]
     x, xb, w = inp["x"], inp["x_bits"], inp["w"]
@@ -125,3 +127,11 @@ def test_library_prepared_full_size_layer(S, cfg):
     _say(f"{cfg}: sampled rows {len(rows)}: rel err bf16 {e16:.3e}, fp32 {e32:.3e}")
     assert e16 <= 2e-3
     assert e32 <= 1e-4
+
+    path = str(tmp_path / f"{cfg}.svdq")
+    S.svdq_save_layer(path, host, alpha=0.5)
+    back = S.svdq_load_layer(path)
+    y16b = S.svdq_linear(xd, S.DeviceLayer(back), torch.bfloat16)
+    torch.cuda.synchronize()
+    _say(f"{cfg}: layer file round trip, {len(open(path, 'rb').read()) >> 20} MiB")
+    assert torch.equal(y16b, y16)

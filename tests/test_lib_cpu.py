@@ -32,7 +32,7 @@ def test_exports_every_symbol_declared_in_header():
     for nm in names:
         assert hasattr(L, nm), nm
     assert {s[0] for s in B.SIGNATURES} == names
-    assert L.svdq_abi_version() == 104
+    assert L.svdq_abi_version() == 105
 
 
 # Host logic of the GEMM schedule (the planner runs on the host; without a GPU
@@ -84,7 +84,7 @@ def test_gemm_schedule_rejects_bad_arguments():
 
 def test_status_strings():
     L = _lib_or_skip()
-    for st in range(0, 8):
+    for st in range(0, 9):
         assert L.svdq_status_string(st)
     assert L.svdq_status_string(99) == b"unknown status"
 
@@ -803,3 +803,104 @@ def test_binding_checks_dtype_shape_and_output_type():
     # host arrays and tensors must be contiguous (a ValueError, not an assert)
     with pytest.raises(ValueError, match="contiguous"):
         B._ptr(np.zeros((4, 4), np.float32)[:, ::2])
+
+
+# ---------------------------------------------------------------------------
+# stored layer files (Algorithm 1 step 9: keep the prepared layer)
+# ---------------------------------------------------------------------------
+
+LAYER_KEYS = ("lambda", "smooth_inv", "qw", "wscale", "l1", "l2")
+
+
+def _prepared(rank=16, lora=0):
+    inp = workloads.make_inputs("tiny")
+    host = S.svdq_prepare_weights(inp["w"], O.act_amax(inp["x"]), rank)
+    if lora:
+        rng = np.random.default_rng(12)
+        A = (rng.standard_normal((256, lora)) * 0.14).astype(np.float32)
+        Bm = (rng.standard_normal((lora, 256)) * 0.14).astype(np.float32)
+        l1, l2 = S.svdq_append_lora(host["l1"], host["l2"], 256, 256, rank, host["lambda"], A, Bm, 1.0)
+        host = dict(host, l1=l1, l2=l2, rank=rank + lora)
+    return host
+
+
+@pytest.mark.parametrize("rank,lora,with_bias", [(16, 0, False), (16, 8, True), (0, 0, True)])
+def test_layer_file_round_trip(tmp_path, rank, lora, with_bias):
+    _lib_or_skip()
+    host = _prepared(rank, lora)
+    bias = workloads.bf16_bits_of(np.linspace(-1, 1, 256).astype(np.float32)) if with_bias else None
+    path = str(tmp_path / "layer.svdq")
+    S.svdq_save_layer(path, host, alpha=0.5, bias=bias)
+    back = S.svdq_load_layer(path)
+    assert (back["m"], back["n"], back["rank"], back["alpha"]) == (256, 256, rank + lora, 0.5)
+    for key in LAYER_KEYS:
+        assert np.array_equal(back[key], host[key] if back["rank"] or key not in ("l1", "l2")
+                              else np.zeros_like(back[key])), key
+    if with_bias:
+        assert np.array_equal(back["bias"], bias)
+    else:
+        assert back["bias"] is None
+    assert os.path.getsize(path) == 64 + 4 * 256 * 2 + 4 * 256 * 32 + 2 * 4 * 256 + \
+        2 * (rank + lora) * 512 + (512 if with_bias else 0)
+
+
+def test_layer_file_rejects_damaged_files(tmp_path):
+    """Corrupted, truncated, extended, foreign and missing files give
+    SVDQ_ERR_IO and leave the caller's buffers untouched."""
+    L = _lib_or_skip()
+    host = _prepared()
+    good = str(tmp_path / "good.svdq")
+    S.svdq_save_layer(good, host)
+    raw = open(good, "rb").read()
+
+    def variant(name, data):
+        p = str(tmp_path / name)
+        with open(p, "wb") as f:
+            f.write(data)
+        return p
+
+    flipped = bytearray(raw)
+    flipped[64 + 1000] ^= 0x10                        # one payload bit
+    header = bytearray(raw)
+    header[0:8] = b"NOTALAYR"
+    version = bytearray(raw)
+    version[8] = 2
+    dims = bytearray(raw)
+    dims[16:20] = (320).to_bytes(4, "little")         # m no longer matches the payload size
+    cases = {"corrupt": variant("c.svdq", bytes(flipped)), "truncated": variant("t.svdq", raw[:-10]),
+             "extended": variant("e.svdq", raw + b"\0"), "magic": variant("m.svdq", bytes(header)),
+             "version": variant("v.svdq", bytes(version)), "dims": variant("d.svdq", bytes(dims)),
+             "short": variant("s.svdq", raw[:40]), "missing": str(tmp_path / "none.svdq")}
+    for what, path in cases.items():
+        with pytest.raises(B.SvdqError) as ei:
+            S.svdq_load_layer(path)
+        assert ei.value.status == B.SVDQ_ERR_IO, what
+    # buffers untouched when the checksum fails
+    lam = np.full(256, 7.0, np.float32)
+    qw = np.full((4, 256, 32), 0x5A, np.uint8)
+    st = L.svdq_load_layer(os.fsencode(cases["corrupt"]), B._ptr(lam), B._ptr(np.zeros(256, np.float32)),
+                           B._ptr(qw), B._ptr(np.zeros((4, 256), np.uint16)), B._ptr(np.zeros((16, 256), np.uint16)),
+                           B._ptr(np.zeros((256, 16), np.uint16)), None)
+    assert st == B.SVDQ_ERR_IO and b"checksum" in L.svdq_last_error()
+    assert np.all(lam == 7.0) and np.all(qw == 0x5A)
+
+
+def test_layer_file_argument_errors(tmp_path):
+    L = _lib_or_skip()
+    host = _prepared()
+    path = str(tmp_path / "x.svdq")
+    assert L.svdq_save_layer(None, None) == B.SVDQ_ERR_INVALID_ARG
+    with pytest.raises(ValueError, match="shape"):
+        S.svdq_save_layer(path, dict(host, qw=host["qw"][:, :-1]))
+    with pytest.raises(B.SvdqError) as ei:
+        S.svdq_save_layer(str(tmp_path / "no_dir" / "x.svdq"), host)
+    assert ei.value.status == B.SVDQ_ERR_IO
+    S.svdq_save_layer(path, host)
+    m = ctypes.c_int32()
+    assert L.svdq_load_layer_info(os.fsencode(path), ctypes.byref(m), None, None, None, None) == \
+        B.SVDQ_ERR_INVALID_ARG
+    # l1 / l2 are required for a rank-16 file
+    st = L.svdq_load_layer(os.fsencode(path), B._ptr(np.zeros(256, np.float32)), B._ptr(np.zeros(256, np.float32)),
+                           B._ptr(np.zeros((4, 256, 32), np.uint8)), B._ptr(np.zeros((4, 256), np.uint16)),
+                           None, None, None)
+    assert st == B.SVDQ_ERR_INVALID_ARG

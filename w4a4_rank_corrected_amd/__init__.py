@@ -11,7 +11,7 @@ from ._binding import (  # noqa: F401
     svdq_linear, svdq_linear_workspace_size, svdq_linear_unfused, svdq_linear_noalloc,
     svdq_linear_noalloc_max_workspace, svdq_linear_unfused_workspace_size,
     svdq_prepare_weights, svdq_prepare_weights_refined, svdq_quantize_act_lowrank_down,
-    svdq_quantize_residual, SVDQ_W8A8_MAX_M, DeviceLayer8, svdq_w8a8_act_workspace_size,
+    svdq_quantize_residual, svdq_save_layer, svdq_load_layer, SVDQ_W8A8_MAX_M, DeviceLayer8, svdq_w8a8_act_workspace_size,
     svdq_w8a8_gemm_lowrank_up, svdq_w8a8_gemm_workspace_size, svdq_w8a8_linear,
     svdq_w8a8_linear_workspace_size, svdq_w8a8_prepare_weights, svdq_w8a8_quantize_act_lowrank_down,
     DeviceLayerFp4, svdq_fp4_act_workspace_size, svdq_fp4_gemm_lowrank_up, svdq_fp4_gemm_workspace_size,
@@ -26,7 +26,7 @@ __all__ = [
     "svdq_linear_noalloc_max_workspace",
     "svdq_linear_unfused", "svdq_linear_unfused_workspace_size",
     "svdq_prepare_weights", "svdq_prepare_weights_refined", "svdq_quantize_act_lowrank_down",
-    "svdq_quantize_residual", "SVDQ_W8A8_MAX_M", "DeviceLayer8", "svdq_w8a8_act_workspace_size",
+    "svdq_quantize_residual", "svdq_save_layer", "svdq_load_layer", "SVDQ_W8A8_MAX_M", "DeviceLayer8", "svdq_w8a8_act_workspace_size",
     "svdq_w8a8_gemm_lowrank_up", "svdq_w8a8_gemm_workspace_size", "svdq_w8a8_linear",
     "svdq_w8a8_linear_workspace_size", "svdq_w8a8_prepare_weights", "svdq_w8a8_quantize_act_lowrank_down",
     "DeviceLayerFp4", "svdq_fp4_act_workspace_size", "svdq_fp4_gemm_lowrank_up", "svdq_fp4_gemm_workspace_size",

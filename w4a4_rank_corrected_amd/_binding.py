@@ -21,6 +21,7 @@ SVDQ_ERR_NONFINITE = 4
 SVDQ_ERR_NO_CONVERGENCE = 5
 SVDQ_ERR_WORKSPACE = 6
 SVDQ_ERR_HIP = 7
+SVDQ_ERR_IO = 8
 SVDQ_OUT_BF16 = 0
 SVDQ_OUT_F32 = 1
 SVDQ_GROUP = 64
@@ -40,6 +41,13 @@ class svdq_layer(ctypes.Structure):
     _fields_ = [("m", ctypes.c_int32), ("n", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("smooth_inv", _vp), ("qw", _vp), ("wscale", _vp),
                 ("l1", _vp), ("l2", _vp), ("bias", _vp)]
+
+
+class svdq_host_layer(ctypes.Structure):
+    """Mirror of ``struct svdq_host_layer`` (all pointers are host addresses)."""
+    _fields_ = [("m", ctypes.c_int32), ("n", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("alpha", ctypes.c_float), ("lambda_", _vp), ("smooth_inv", _vp),
+                ("qw", _vp), ("wscale", _vp), ("l1", _vp), ("l2", _vp), ("bias", _vp)]
 
 
 class svdq_w8a8_layer(ctypes.Structure):
@@ -63,6 +71,9 @@ SIGNATURES = [
      [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
       _vp, _vp, _vp, _vp, _vp]),
     ("svdq_quantize_residual", _c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp]),
+    ("svdq_save_layer", _c_int, [ctypes.c_char_p, ctypes.POINTER(svdq_host_layer)]),
+    ("svdq_load_layer_info", _c_int, [ctypes.c_char_p, _vp, _vp, _vp, _vp, _vp]),
+    ("svdq_load_layer", _c_int, [ctypes.c_char_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     ("svdq_append_lora", _c_int,
      [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_int, ctypes.c_float, _vp, _vp]),
     ("svdq_calibrate_act_amax", _c_int, [_vp, _c_int, _c_int, _vp, _c_int, _vp]),
@@ -291,6 +302,47 @@ def svdq_prepare_weights_refined(W: np.ndarray, act_amax: Optional[np.ndarray], 
     if want_residual:
         out["residual"] = res
     out.update(alpha=float(alpha_out[0]), iteration=int(iter_out[0]), rel_err=float(err_out[0]))
+    return out
+
+
+def svdq_save_layer(path: str, host: dict, alpha: float = 0.5, bias: Optional[np.ndarray] = None) -> None:
+    """Write a prepared layer (the host dict of ``svdq_prepare_weights``, with
+    ``l1``/``l2`` possibly widened by ``svdq_append_lora``) to a layer file."""
+    m, n, rank = int(host["m"]), int(host["n"]), int(host["rank"])
+    arr = lambda a, dt: None if a is None else np.ascontiguousarray(a, dtype=dt)
+    lam, inv = arr(host["lambda"], np.float32), arr(host["smooth_inv"], np.float32)
+    qw, ws = arr(host["qw"], np.uint8), arr(host["wscale"], np.uint16)
+    l1 = arr(host["l1"], np.uint16) if rank else None
+    l2 = arr(host["l2"], np.uint16) if rank else None
+    bb = arr(bias, np.uint16)
+    G = m // SVDQ_GROUP
+    expect = {"lambda": (lam, (m,)), "smooth_inv": (inv, (m,)), "qw": (qw, (G, n, 32)), "wscale": (ws, (G, n)),
+              "l1": (l1, (rank, m)), "l2": (l2, (n, rank)), "bias": (bb, (n,))}
+    for name, (a, shape) in expect.items():
+        if a is not None and a.shape != shape:
+            raise ValueError(f"{name} has shape {a.shape}, expected {shape}")
+    L = svdq_host_layer(m, n, rank, SVDQ_GROUP, float(alpha), _ptr(lam), _ptr(inv), _ptr(qw), _ptr(ws),
+                        _ptr(l1), _ptr(l2), _ptr(bb))
+    _check(lib().svdq_save_layer(os.fsencode(path), ctypes.byref(L)))
+
+
+def svdq_load_layer(path: str) -> dict:
+    """Read a layer file; returns the host dict (keys of ``svdq_prepare_weights``
+    plus ``alpha`` and ``bias``, None when the file stores none)."""
+    m, n, rank, hb = (ctypes.c_int32() for _ in range(4))
+    alpha = ctypes.c_float()
+    _check(lib().svdq_load_layer_info(os.fsencode(path), ctypes.byref(m), ctypes.byref(n), ctypes.byref(rank),
+                                      ctypes.byref(hb), ctypes.byref(alpha)))
+    m, n, rank = m.value, n.value, rank.value
+    G = m // SVDQ_GROUP
+    out = {"m": m, "n": n, "rank": rank, "alpha": float(alpha.value),
+           "lambda": np.zeros(m, np.float32), "smooth_inv": np.zeros(m, np.float32),
+           "qw": np.zeros((G, n, 32), np.uint8), "wscale": np.zeros((G, n), np.uint16),
+           "l1": np.zeros((rank, m), np.uint16), "l2": np.zeros((n, rank), np.uint16),
+           "bias": np.zeros(n, np.uint16) if hb.value else None}
+    _check(lib().svdq_load_layer(os.fsencode(path), _ptr(out["lambda"]), _ptr(out["smooth_inv"]), _ptr(out["qw"]),
+                                 _ptr(out["wscale"]), _ptr(out["l1"]) if rank else None,
+                                 _ptr(out["l2"]) if rank else None, _ptr(out["bias"])))
     return out
 
 

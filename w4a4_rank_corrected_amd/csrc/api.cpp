@@ -316,7 +316,7 @@ int check_y(void* y, int y_dtype, int b) {
 
 extern "C" {
 
-int svdq_abi_version(void) { return 104; }
+int svdq_abi_version(void) { return 105; }
 
 int svdq_test_set_svd_iteration_limit(int limit) { return set_eig_iteration_limit(limit); }
 
@@ -332,6 +332,7 @@ const char* svdq_status_string(int status) {
     case SVDQ_ERR_NO_CONVERGENCE: return "SVD did not converge";
     case SVDQ_ERR_WORKSPACE: return "workspace missing or too small";
     case SVDQ_ERR_HIP: return "HIP runtime error";
+    case SVDQ_ERR_IO: return "layer file missing, unreadable or invalid";
     default: return "unknown status";
   }
 }

@@ -423,7 +423,9 @@ __device__ __forceinline__ void gemm_up_body(
     uint32_t s[KG];   // INT4: this thread's group scale; FP4: the activation row's two block scales
     uint32_t s2[KG];  // FP4: the weight column's two block scales
   };
-  auto main_branch = [&](int i0, int j0, int g0, int g1) {
+  // `pre` runs once the first groups' loads are in flight (the low-rank
+  // branch: its own loads and MFMAs then overlap those loads' latency).
+  auto main_branch = [&](int i0, int j0, int g0, int g1, auto&& pre) {
     const uint32_t a_voff = (uint32_t)(i0 + a_row) * REC + 4u * a_w0;
     const uint32_t b_voff = (uint32_t)(j0 + b_col) * REC + 4u * b_w0;
     // activation scale of row i0+tid, weight scale of column j0+tid-TM, or an
@@ -431,7 +433,10 @@ __device__ __forceinline__ void gemm_up_body(
     const uint32_t s_voff = tid < TM ? (uint32_t)(i0 + tid) * 2u
                                      : (tid < TM + TN ? (uint32_t)(j0 + tid - TM) * 2u : 0x7FFFFFF0u);
     const int NG = g1 - g0;            // groups in this segment
-    if (NG <= 0) return;               // the up-projection alone (no channel groups)
+    if (NG <= 0) {                     // the up-projection alone (no channel groups)
+      pre();
+      return;
+    }
     const int S = (NG + KG - 1) / KG;  // pipeline steps
     // Step k's groups g0 + KG k + q.  A group past the segment's end reads as
     // zero (size-0 descriptors: zero codes and scales add nothing); a step past
@@ -629,6 +634,7 @@ __device__ __forceinline__ void gemm_up_body(
     Stage st[D];
 #pragma unroll
     for (int u = 0; u < D; ++u) load_stage(u, st[u]);
+    pre();
     store_stage(0, st[0]);
     load_stage(D, st[0]);
     __syncthreads();
@@ -735,8 +741,9 @@ __device__ __forceinline__ void gemm_up_body(
     int ti, tj;
     band_tile<kColBands>(dp_tile((int)blockIdx.x - sk.P, T - sk.T, sk.T), tiles_m, tiles_n, ti, tj);
     zero_acc();
-    if constexpr (!POST) lowrank(ti * TM, tj * TN);
-    main_branch(ti * TM, tj * TN, 0, G);
+    main_branch(ti * TM, tj * TN, 0, G, [&] {
+      if constexpr (!POST) lowrank(ti * TM, tj * TN);
+    });
     if constexpr (POST) {
       scale_sums(ti * TM, tj * TN);
       lowrank(ti * TM, tj * TN);
@@ -782,8 +789,9 @@ __device__ __forceinline__ void gemm_up_body(
     band_tile<kColBands>((int)t, tiles_m, tiles_n, ti, tj);
     const int i0 = ti * TM, j0 = tj * TN;
     zero_acc();
-    if (!POST && g1 == G) lowrank(i0, j0);  // the tile's last groups carry the low-rank branch
-    main_branch(i0, j0, g0, g1);
+    main_branch(i0, j0, g0, g1, [&] {
+      if (!POST && g1 == G) lowrank(i0, j0);  // the tile's last groups carry the low-rank branch
+    });
     if (g0 > 0 || g1 < G) {
       // workgroups qlo .. qhi hold the tile's pieces (every stream-K workgroup
       // has at least 8 iterations, so none is empty); q's piece is in its
