@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsvdq.so")
 
-HOST_SOURCES = ["api.cpp", "prep.cpp", "bundle.cpp"]
+HOST_SOURCES = ["api.cpp", "prep.cpp", "bundle.cpp", "plan.cpp"]
 HIP_SOURCES = ["act_kernels.hip", "gemm_kernels.hip", "scratch.hip"]
 HEADERS = ["internal.h", "device_common.h"]
 

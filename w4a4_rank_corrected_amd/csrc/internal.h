@@ -141,6 +141,10 @@ struct GemmPlan {
 // Operand formats of the GEMM kernel body (INT4 codes, the 8-bit setting, the
 // NVFP4 setting); each has its own resident workgroups per CU.
 enum GemmFormat { kFmtInt4 = 0, kFmtInt8 = 1, kFmtFp4 = 2 };
+// Output tile of every GEMM build, and the resident workgroups per CU of each
+// format's build for one tile per workgroup [0] and for stream-K launches [1].
+constexpr int kGemmTileM = 128, kGemmTileN = 128;
+constexpr int kGemmWgPerCu[3][2] = {{3, 2}, {3, 2}, {3, 2}};
 // cus <= 0 gives the device-independent upper bound used to size workspaces
 // (valid for every format); fmt selects the kernel whose residency is planned.
 GemmPlan gemm_plan(int b, int n, int m, int cus, int fmt = kFmtInt4);
