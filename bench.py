@@ -136,7 +136,7 @@ def trace_summary(prof_dir, cfg, args, rank):
     for nm, st, en, gx, gy, wx, wy, vg, ag, lds, scr in rows:
         wgs = (gx // max(wx, 1)) * (gy // max(wy, 1))
         by.setdefault(nm, []).append(((en - st) / 1e3, wgs, wx * wy, vg, ag, lds, scr))
-    mode = f" --w8a8 {args.w8a8}" if w8 else (f" --fp4 {args.fp4}" if f4 else " --no-cpu-baseline")
+    mode = f" --w8a8 {args.w8a8}" if w8 else (f" --fp4 {args.fp4}" if f4 else " --no-cpu-baseline --extra-configs ''")
     cmd = (f"rocprofv3 --kernel-trace --stats -d {prof_dir} -o run -- python3 bench.py --workload {cfg.name} "
            f"--steps {args.steps} --warmup {args.warmup}{mode}")
     if cmp_mode:
@@ -147,13 +147,13 @@ def trace_summary(prof_dir, cfg, args, rank):
         title = f"# Kernel trace, {other} setting against INT4: {cfg.name}"
     else:
         region = (f"Timed region: {args.steps} steps after {skip} untimed ones, rotating over {n_sets} "
-                  f"input+weight sets; the script then times warm steps, rank-0 steps and the one-call entry "
-                  f"point, which the all-dispatch columns include.")
+                  f"input+weight sets; the script then times warm steps, rank-r and rank-0 steps interleaved "
+                  f"and the one-call entry point, which the all-dispatch columns include.")
         title = f"# Kernel trace: {cfg.name}"
     out = [f"{title} (b={cfg.rows or cfg.b}, m={cfg.m}, n={cfg.n}, rank {rank})", "",
            "Command (repository root, one MI355X), then the summary:", "", "```", cmd,
            f"python bench.py --trace-summary {prof_dir} --workload {cfg.name} --steps {args.steps} "
-           f"--warmup {args.warmup}" + mode.replace(" --no-cpu-baseline", ""), "```", "", region, "",
+           f"--warmup {args.warmup}" + mode.replace(" --no-cpu-baseline --extra-configs ''", ""), "```", "", region, "",
            "| kernel | dispatches | mean, timed region (us) | mean, all (us) | total (ms) | workgroups | "
            "threads | LDS (B) | scratch (B) |",
            "|---|---|---|---|---|---|---|---|---|"]
