@@ -239,8 +239,9 @@ int svdq_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int rank, in
                                    size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace svdq_gemm_w4a4_lowrank_up may need for an output
- * of b x n with m input channels: fp32 partial tiles and publication flags of
- * its stream-K schedule (an upper bound valid on every gfx950 device). */
+ * of b x n with m input channels: the partial tiles of its split-K schedule
+ * (an upper bound valid on every gfx950 device and GEMM setting; 0 when m has
+ * too few channel groups to split). */
 size_t svdq_gemm_workspace_size(int b, int n, int m);
 
 /* Operand settings of the GEMM kernels, for svdq_gemm_schedule. */
@@ -250,9 +251,11 @@ enum { SVDQ_GEMM_INT4 = 0, SVDQ_GEMM_W8A8 = 1, SVDQ_GEMM_FP4 = 2 };
  * GEMM kernel of `setting` (SVDQ_GEMM_*) would use for an output of b x n with
  * m input channels ([Nunchaku]: one kernel per fused pair; the split of output
  * tiles over workgroups is this library's own).  Writes info[0] = 128 x 128
- * output tiles, info[1] = workgroups launched, info[2] = stream-K workgroups
- * (0 when every workgroup computes one whole tile), info[3] = tiles shared out
- * by stream-K, info[4] = resident workgroups per CU of the kernel chosen.
+ * output tiles, info[1] = workgroups launched, info[2] = split workgroups
+ * (each computes one piece of a tile's channel groups, and a reduction kernel
+ * then adds the pieces; 0 when every workgroup computes one whole tile),
+ * info[3] = tiles split (info[2] / info[3] pieces each), info[4] = resident
+ * workgroups per CU of the kernel chosen.
  * info: host, 5 ints, owned by the caller.  On an error info is
  * untouched: SVDQ_ERR_INVALID_ARG for a null info, an unknown setting, b < 0
  * or n < 1; SVDQ_ERR_UNSUPPORTED for b, n or m above SVDQ_MAX_DIM, m not a
@@ -268,12 +271,13 @@ int svdq_gemm_schedule(int b, int n, int m, int setting, int* info);
  *   (SVDQ_OUT_BF16, round-to-nearest-even, or SVDQ_OUT_F32); y needs only
  *   element alignment.  layer->smooth_inv and layer->l1 are not used.
  *   workspace: device, 16-byte aligned, >= svdq_gemm_workspace_size(b, n, m)
- *   bytes.  Its contents need no initialisation, and calls that overlap in time
- *   must not share it.  A launch leaves its publication flags cleared, so a
- *   launch captured in a HIP graph may be replayed (stream-ordered) on the same
- *   workspace.  Per-group sums are accumulated in a fixed order that depends
- *   only on the shape and the device's CU count, so results are
- *   deterministic. */
+ *   bytes.  Its contents need no initialisation (every slot read is first
+ *   written by the same call), and calls that overlap in time must not share
+ *   it; a launch captured in a HIP graph may be replayed (stream-ordered) on
+ *   the same workspace.  A split schedule launches two kernels on `stream`
+ *   (the GEMM, then the reduction of the split tiles).  Per-group sums, and
+ *   the pieces of a split tile, are added in a fixed order that depends only
+ *   on the shape and the device's CU count, so results are deterministic. */
 int svdq_gemm_w4a4_lowrank_up(const uint8_t* qx, const uint16_t* ascale, const float* z,
                               const svdq_layer* layer, int b, void* y, int y_dtype, void* workspace,
                               size_t workspace_bytes, void* stream);
@@ -304,7 +308,7 @@ int svdq_linear(const uint16_t* x, const svdq_layer* layer, int b, void* y, int 
  *   time on one GPU (on different streams, or from several threads without
  *   ordering) race and give undefined results; stream-ordered calls are safe.
  *   The scratch keeps whatever the last call left; no part of it needs
- *   clearing (publication flags carry a per-launch epoch). */
+ *   clearing (every byte a call reads it first writes). */
 int svdq_linear_noalloc(const uint16_t* x, const svdq_layer* layer, int b, void* y, int y_dtype, void* stream);
 size_t svdq_linear_noalloc_max_workspace(void);
 
@@ -403,7 +407,8 @@ int svdq_w8a8_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int ran
                                         size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace svdq_w8a8_gemm_lowrank_up may need (int32 partial
- * tiles and flags of its stream-K schedule; an upper bound on every gfx950). */
+ * tiles of its split-K schedule and one fp32 low-rank tile per split tile; the
+ * bound of svdq_gemm_workspace_size). */
 size_t svdq_w8a8_gemm_workspace_size(int b, int n, int m);
 
 /* DEVICE: 8-bit GEMM + low-rank up-projection:
@@ -487,8 +492,9 @@ int svdq_fp4_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int rank
                                        const uint16_t* l1, float t_x, uint8_t* qx, uint8_t* ascale, float* z,
                                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace svdq_fp4_gemm_lowrank_up may need (fp32 partial
- * tiles and flags of its stream-K schedule). */
+/* Bytes of device workspace svdq_fp4_gemm_lowrank_up accepts (the bound of
+ * svdq_gemm_workspace_size; NVFP4 tiles are never split, so the kernels do
+ * not use it). */
 size_t svdq_fp4_gemm_workspace_size(int b, int n, int m);
 
 /* DEVICE: NVFP4 GEMM + low-rank up-projection:

@@ -155,8 +155,8 @@ GEMM_CASES = [
     (130, 128, 260, 0, True),
     (1, 64, 7, 3, False),
     (256, 512, 384, 48, True),
-    (256, 4096, 256, 16, True),   # stream-K
-    (300, 2368, 200, 24, False),  # stream-K, uneven splits, ragged edges
+    (256, 4096, 256, 16, True),   # 64 groups per tile (NVFP4 tiles are never split)
+    (300, 2368, 200, 24, False),  # 37 groups, ragged edges
 ]
 
 
@@ -206,7 +206,7 @@ def test_fp4_gemm_exact_products(S, b, m, n):
     """Rank 0, fp32 output, tensor scales 1, block scales 2^k for k in [-2, 2]:
     every product and partial sum is a multiple of 2^-6 below 2^17, so the
     fp32 result is exact and equals the oracle's bit for bit, on one-tile and
-    stream-K schedules."""
+    K-long shapes (NVFP4 tiles are never split)."""
     _say(f"fp4 gemm exact b={b} m={m} n={n}")
     rng = np.random.default_rng(b + m + n)
     qx = rng.integers(0, 16, (b, m)).astype(np.uint8)
@@ -236,8 +236,8 @@ def test_fp4_gemm_every_block_scale(S, m):
     partial sum is s_i s_j (at most 8 significant bits) times a multiple of 1/4
     below 2^14, exact in fp32, and the result equals the oracle's bit for bit.
     m = 256 (all codes) runs one tile per workgroup; m = 4096 (codes of
-    magnitude <= 1, to keep the sums below 2^14) splits the tiles by
-    stream-K."""
+    magnitude <= 1, to keep the sums below 2^14) runs 64 groups per
+    tile."""
     b, n = 126, 130
     _say(f"fp4 gemm every block scale m={m}")
     rng = np.random.default_rng(m)

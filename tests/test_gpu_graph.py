@@ -1,11 +1,10 @@
 """Replays of a captured HIP graph of the layer (all three settings).
 
-The stream-K schedule keeps publication flags in the caller's workspace,
-tagged with an epoch chosen when the launch is recorded; a captured launch
-replays that epoch.  The finishing workgroup clears every flag it consumed, so
-each replay waits for its own partial sums again.  Each replay runs on new
-inputs copied in eagerly (with synchronizations between replays) and must
-equal, bit for bit, the eager call on the same inputs.
+A split-K launch is two kernels: the GEMM stores each piece's partial sums in
+the caller's workspace and a reduction kernel adds them; a captured graph
+replays both, and each replay overwrites every slot it reads.  Each replay runs
+on new inputs copied in eagerly (with synchronizations between replays) and
+must equal, bit for bit, the eager call on the same inputs.
 """
 import sys
 

@@ -207,8 +207,8 @@ GEMM_CASES = [
     (130, 128, 260, 0, True),     # rank 0 = plain W4A4
     (1, 64, 7, 3, False),
     (256, 512, 384, 48, True),
-    (256, 4096, 256, 16, True),   # stream-K: each tile split over 8 workgroups
-    (300, 2368, 200, 24, False),  # stream-K: uneven splits, ragged edges
+    (256, 4096, 256, 16, True),   # split-K: each tile split over 8 workgroups
+    (300, 2368, 200, 24, False),  # split-K: uneven splits, ragged edges
 ]
 
 
@@ -368,11 +368,11 @@ def test_linear_equals_standalone_kernels_bitwise(S):
 
 
 @pytest.mark.parametrize("b,m,n", [(256, 4096, 256), (300, 2368, 200), (512, 3072, 1024)])
-def test_streamk_splits_deterministic_and_match_oracle(S, b, m, n):
+def test_splitk_deterministic_and_match_oracle(S, b, m, n):
     """Shapes whose tiles are split over several workgroups (partial sums
     published and added in a fixed order): repeated runs are bit-identical and
     match the oracle."""
-    _say(f"stream-K b={b} m={m} n={n}")
+    _say(f"split-K b={b} m={m} n={n}")
     rng = np.random.default_rng(b + m + n)
     xb = workloads.random_bf16_bits(rng, (b, m), 1.5)
     x = LY.bf16_bits_to_f32(xb)
@@ -388,8 +388,8 @@ def test_streamk_splits_deterministic_and_match_oracle(S, b, m, n):
     assert err <= 1e-4
 
 
-def test_streamk_workspace_garbage_and_alternating_shapes(S):
-    """Stream-K partial slots and per-tile arrival counters live in the
+def test_splitk_workspace_garbage_and_alternating_shapes(S):
+    """Split-K partial slots and per-tile arrival counters live in the
     caller's workspace: random initial bytes (any counter value a previous
     launch or process could leave), two split shapes alternating on one
     workspace, and repeats must all give the same bits and the oracle's Y."""
@@ -399,7 +399,7 @@ def test_streamk_workspace_garbage_and_alternating_shapes(S):
     cases = []
     for (b, m, n) in shapes:
         sch = S.svdq_gemm_schedule(b, n, m)
-        assert sch["stream_k_workgroups"] > 0, sch
+        assert sch["split_workgroups"] > 0, sch
         rng = np.random.default_rng(b * 7 + n)
         xb = workloads.random_bf16_bits(rng, (b, m), 1.5)
         x = LY.bf16_bits_to_f32(xb)
@@ -408,7 +408,7 @@ def test_streamk_workspace_garbage_and_alternating_shapes(S):
     first = {}
     for rep in range(3):
         for k, (xd, dl, ref) in enumerate(cases):
-            _say(f"stream-K workspace reuse rep={rep} shape={shapes[k]}")
+            _say(f"split-K workspace reuse rep={rep} shape={shapes[k]}")
             y = S.svdq_linear(xd, dl, torch.float32, workspace=ws)
             torch.cuda.synchronize()
             if rep == 0:
@@ -420,15 +420,14 @@ def test_streamk_workspace_garbage_and_alternating_shapes(S):
             ws.random_(0, 256)
 
 
-# The INT4 GEMM has four schedules (three-per-CU kernel with one tile per
-# workgroup; two-per-CU kernel with one tile per workgroup, all tiles by
-# stream-K, or a stream-K part followed by full rounds).  Each case finds the
-# smallest b x n (m = 1536) that the library schedules that way on this device.
+# The INT4 GEMM has three schedules: one tile per workgroup, every tile split
+# into pieces (under half a round of tiles), or a split last round after full
+# rounds of whole tiles.  Each case finds the smallest b x n (m = 1536) that the
+# library schedules that way on this device.
 SCHEDULE_KINDS = {
-    "one_tile_3cu": lambda s: s["workgroups_per_cu"] == 3,
-    "one_tile_2cu": lambda s: s["workgroups_per_cu"] == 2 and s["stream_k_workgroups"] == 0,
-    "stream_k": lambda s: 0 < s["stream_k_workgroups"] == s["grid"],
-    "hybrid": lambda s: 0 < s["stream_k_workgroups"] < s["grid"],
+    "one_tile": lambda s: s["split_workgroups"] == 0,
+    "split": lambda s: 0 < s["split_workgroups"] == s["grid"],
+    "hybrid": lambda s: 0 < s["split_workgroups"] < s["grid"],
 }
 
 

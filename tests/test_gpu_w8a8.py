@@ -151,8 +151,8 @@ GEMM8_CASES = [
     (130, 128, 260, 0, True),     # rank 0 = plain W8A8
     (1, 64, 7, 3, False),
     (256, 512, 384, 48, True),
-    (256, 4096, 256, 16, True),   # stream-K: int32 partials
-    (300, 2368, 200, 24, False),  # stream-K: uneven splits, ragged edges
+    (256, 4096, 256, 16, True),   # split-K: int32 partials
+    (300, 2368, 200, 24, False),  # split-K: uneven splits, ragged edges
 ]
 
 
@@ -190,7 +190,7 @@ def test_gemm8_parity(S, b, m, n, rank, bias, out):
 @pytest.mark.parametrize("b,m,n", [(50, 256, 72), (256, 4096, 256), (300, 2368, 200)])
 def test_gemm8_exact_integer_sums(S, b, m, n):
     """Unit scales, rank 0, fp32 output: Y = qx qw exactly (|sum| < 2^24), on
-    one-tile and stream-K schedules (int32 partials)."""
+    one-tile and split-K schedules (int32 partials)."""
     _say(f"gemm8 exact sums b={b} m={m} n={n}")
     rng = np.random.default_rng(b + m)
     qx = rng.integers(-127, 128, (b, m)).astype(np.int16)

@@ -32,27 +32,33 @@ def test_exports_every_symbol_declared_in_header():
     for nm in names:
         assert hasattr(L, nm), nm
     assert {s[0] for s in B.SIGNATURES} == names
-    assert L.svdq_abi_version() == 105
+    assert L.svdq_abi_version() == 106
 
 
 # Host logic of the GEMM schedule (the planner runs on the host; without a GPU
-# the library plans for 256 CUs, the MI355X count).  Residency: three INT4
-# workgroups per CU, two for the 8-bit and NVFP4 kernels.
+# the library plans for 256 CUs, the MI355X count).  Every setting runs three
+# workgroups per CU, so a round is 768 tiles.  After full rounds, a last round
+# of R tiles is split into k = min(768 // R, 8, G // 8) pieces per tile when
+# k >= 3; when all T tiles fit in one round, into k = min(768 // T, 16, G // 8)
+# pieces when k >= 2.  NVFP4 tiles are never split.
 SCHEDULES = [
-    # (b, n, m, setting, tiles, grid, stream-K workgroups, stream-K tiles, workgroups per CU)
-    (4608, 9216, 3072, "int4", 2592, 2592, 0, 0, 3),      # 3/CU: last round 3/8 full, one tile per workgroup
-    (4096, 4608, 1152, "int4", 1152, 1152, 0, 0, 3),      # 3/CU: last round half full
-    (4608, 3072, 12288, "int4", 864, 512, 512, 864, 2),   # G = 192: 3/CU splits (1/8 full); at 2/CU the
-                                                          # last round is 11/16 full but idle for 60 groups
-    (4608, 3072, 12288, "w8a8", 864, 512, 512, 864, 2),
-    (4608, 9216, 3072, "w8a8", 2592, 2592, 0, 0, 3),      # the 8-bit setting plans like INT4
-    (4608, 5760, 3072, "w8a8", 1620, 1536, 512, 596, 2),  # 3/CU: 0.11 full; 2/CU: 0.16 full -> hybrid
+    # (b, n, m, setting, tiles, grid, split workgroups, split tiles, workgroups per CU)
+    (4608, 9216, 3072, "int4", 2592, 2592, 0, 0, 3),      # last round 288 tiles: halves are not used
+    (4096, 4608, 1152, "int4", 1152, 1152, 0, 0, 3),      # last round half full: one tile per workgroup
+    (4608, 3072, 12288, "int4", 864, 1536, 768, 96, 3),   # last round 96 tiles: 8 pieces of 24 groups
+    (4608, 3072, 12288, "w8a8", 864, 1536, 768, 96, 3),   # the 8-bit setting plans like INT4
+    (4608, 9216, 3072, "w8a8", 2592, 2592, 0, 0, 3),
+    (4608, 5760, 3072, "w8a8", 1620, 2040, 504, 84, 3),   # 768 // 84 = 9 pieces, capped at G // 8 = 6
     (4608, 9216, 3072, "fp4", 2592, 2592, 0, 0, 3),
-    (4608, 3072, 12288, "fp4", 864, 864, 0, 0, 3),        # NVFP4 splits only tiles under one round
-    (256, 21504, 3072, "fp4", 336, 512, 512, 336, 2),
-    (256, 21504, 3072, "int4", 336, 512, 512, 336, 2),    # under one round: stream-K at 2/CU
-    (4992, 5120, 1536, "int4", 1560, 1536, 512, 536, 2),  # hybrid: 536 tiles by stream-K, then 2 rounds
-    (4608, 3072, 1024, "int4", 864, 864, 0, 0, 3),        # G = 16: too few groups to split
+    (4608, 3072, 12288, "fp4", 864, 864, 0, 0, 3),        # NVFP4: never split
+    (256, 21504, 3072, "fp4", 336, 336, 0, 0, 3),
+    (256, 21504, 3072, "int4", 336, 672, 672, 336, 3),    # one round: 768 // 336 = 2 pieces of 24 groups
+    (256, 3072, 15360, "int4", 48, 768, 768, 48, 3),      # one round: 16 pieces (the cap) of 15 groups
+    (256, 3072, 15360, "w8a8", 48, 768, 768, 48, 3),
+    (4992, 5120, 1536, "int4", 1560, 1608, 72, 24, 3),    # 24 tiles left: 32 pieces, capped at G // 8 = 3
+    (4608, 5376, 3072, "int4", 1512, 1512, 0, 0, 3),      # last round 744 tiles: no split
+    (4608, 3072, 1024, "int4", 864, 864, 0, 0, 3),        # G = 16: at most 2 pieces after full rounds
+    (256, 3072, 1024, "int4", 48, 96, 96, 48, 3),         # one round, G = 16: 2 pieces of 8 groups
     (256, 256, 64, "int4", 4, 4, 0, 0, 3),                # one group
     (0, 256, 256, "int4", 0, 0, 0, 0, 3),
 ]
@@ -64,7 +70,7 @@ def test_gemm_schedule(b, n, m, setting, tiles, grid, skw, skt, wpc):
     if S.svdq_gemm_schedule(128, 128, 64)["grid"] != 1:
         pytest.skip("unexpected device")
     got = S.svdq_gemm_schedule(b, n, m, setting)
-    assert got == {"tiles": tiles, "grid": grid, "stream_k_workgroups": skw, "stream_k_tiles": skt,
+    assert got == {"tiles": tiles, "grid": grid, "split_workgroups": skw, "split_tiles": skt,
                    "workgroups_per_cu": wpc}
 
 
@@ -374,7 +380,10 @@ def test_act_and_gemm_validation_errors():
     assert g(None, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE, W, None) == B.SVDQ_ERR_INVALID_ARG
     assert g(FAKE + 1, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE, W, None) == B.SVDQ_ERR_ALIGNMENT
     assert g(FAKE, FAKE, FAKE, ctypes.byref(lay), 16, FAKE + 2, 1, FAKE, W, None) == B.SVDQ_ERR_ALIGNMENT
-    gneed = L.svdq_gemm_workspace_size(16, 64, 128)
+    # two channel groups can never be split: no GEMM workspace; 32 groups can
+    assert L.svdq_gemm_workspace_size(16, 64, 128) == 0
+    lay = _layer(m=2048)
+    gneed = L.svdq_gemm_workspace_size(16, 64, 2048)
     assert gneed > 0
     assert g(FAKE, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE, gneed - 1, None) == B.SVDQ_ERR_WORKSPACE
     assert g(FAKE, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, None, gneed, None) == B.SVDQ_ERR_WORKSPACE
@@ -571,8 +580,10 @@ def test_w8a8_act_gemm_workspace_validation():
     assert L.svdq_w8a8_act_workspace_size(64, 4096, 32) == L.svdq_act_workspace_size(64, 4096, 32) > 0
     assert a(FAKE, 64, 4096, 32, None, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.SVDQ_ERR_WORKSPACE
     g = L.svdq_w8a8_gemm_lowrank_up
-    gneed = L.svdq_w8a8_gemm_workspace_size(16, 64, 128)
-    assert gneed == L.svdq_gemm_workspace_size(16, 64, 128) > 0
+    assert L.svdq_w8a8_gemm_workspace_size(16, 64, 128) == 0   # two groups: never split
+    lay = _layer8(m=2048)
+    gneed = L.svdq_w8a8_gemm_workspace_size(16, 64, 2048)
+    assert gneed == L.svdq_gemm_workspace_size(16, 64, 2048) > 0
     assert g(FAKE, FAKE, None, ctypes.byref(lay), 16, FAKE, 0, FAKE, gneed, None) == B.SVDQ_ERR_INVALID_ARG
     assert g(FAKE + 4, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE, gneed, None) == B.SVDQ_ERR_ALIGNMENT
     assert g(FAKE, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE, gneed - 1, None) == B.SVDQ_ERR_WORKSPACE
@@ -676,8 +687,10 @@ def test_fp4_act_gemm_workspace_validation():
     assert L.svdq_fp4_act_workspace_size(64, 4096, 32) == L.svdq_act_workspace_size(64, 4096, 32) > 0
     assert a(FAKE, 64, 4096, 32, None, FAKE, 1.0, FAKE, FAKE, FAKE, None, 0, None) == B.SVDQ_ERR_WORKSPACE
     g = L.svdq_fp4_gemm_lowrank_up
-    gneed = L.svdq_fp4_gemm_workspace_size(16, 64, 128)
-    assert gneed == L.svdq_gemm_workspace_size(16, 64, 128) > 0
+    assert L.svdq_fp4_gemm_workspace_size(16, 64, 128) == 0    # two groups: never split
+    lay = _layer_fp4(m=2048)
+    gneed = L.svdq_fp4_gemm_workspace_size(16, 64, 2048)
+    assert gneed == L.svdq_gemm_workspace_size(16, 64, 2048) > 0
     assert g(FAKE, FAKE, None, ctypes.byref(lay), 16, FAKE, 0, FAKE, gneed, None) == B.SVDQ_ERR_INVALID_ARG
     assert g(FAKE + 4, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE, gneed, None) == B.SVDQ_ERR_ALIGNMENT
     assert g(FAKE, FAKE, FAKE, ctypes.byref(lay), 16, FAKE, 0, FAKE, gneed - 1, None) == B.SVDQ_ERR_WORKSPACE

@@ -46,7 +46,7 @@ def _rel(a, b):
     return np.linalg.norm(np.asarray(a, np.float64) - b) / np.linalg.norm(b)
 
 
-# (b, m, n, rank): a split-K shape (stream-K partials and flags in the scratch),
+# (b, m, n, rank): a split-K shape (partial sums in the scratch, added by the reduction kernel),
 # then a smaller one-tile shape on the same scratch
 CASES = [(300, 2368, 520, 24), (45, 512, 200, 16)]
 

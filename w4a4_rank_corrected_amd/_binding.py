@@ -487,12 +487,12 @@ GEMM_SETTINGS = {"int4": 0, "w8a8": 1, "fp4": 2}  # SVDQ_GEMM_INT4, _W8A8, _FP4
 
 def svdq_gemm_schedule(b: int, n: int, m: int, setting: str = "int4") -> dict:
     """The GEMM kernel's schedule for a b x n output with m input channels on
-    the current device: tiles, workgroups launched, stream-K workgroups and the
-    tiles they share (both 0 when each workgroup computes one tile), and the
-    resident workgroups per CU of the kernel chosen."""
+    the current device: tiles, workgroups launched, the split workgroups and
+    the tiles they split (both 0 when each workgroup computes one whole tile),
+    and the resident workgroups per CU of the kernel chosen."""
     info = (_c_int * 5)()
     _check(lib().svdq_gemm_schedule(b, n, m, GEMM_SETTINGS[setting], info))
-    return {"tiles": info[0], "grid": info[1], "stream_k_workgroups": info[2], "stream_k_tiles": info[3],
+    return {"tiles": info[0], "grid": info[1], "split_workgroups": info[2], "split_tiles": info[3],
             "workgroups_per_cu": info[4]}
 
 

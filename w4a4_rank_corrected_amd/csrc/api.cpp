@@ -4,8 +4,6 @@
 // preparation code (prep.cpp) or the HIP kernel launchers.
 #include <algorithm>
 #include <cmath>
-#include <atomic>
-#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -25,25 +23,6 @@ void set_error(const char* fmt, ...) {
 }
 void clear_error() { g_err[0] = 0; }
 
-namespace {
-std::atomic<unsigned long long> g_launch_counter{0};
-}  // namespace
-
-unsigned long long next_launch_epoch() {
-  // per-process base from time and address entropy (splitmix64 finaliser)
-  static const unsigned long long base = [] {
-    const unsigned long long t =
-        (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
-    const unsigned long long a = (unsigned long long)(uintptr_t)&g_launch_counter;
-    unsigned long long x = t ^ (a << 17) ^ 0x9E3779B97F4A7C15ull;
-    x ^= x >> 31;
-    x *= 0xBF58476D1CE4E5B9ull;
-    x ^= x >> 29;
-    return x | 1ull;
-  }();
-  const unsigned long long e = base + g_launch_counter.fetch_add(1);
-  return e ? e : base;  // never 0: a consumed flag is cleared to 0
-}
 
 // Split plan of the act-quant kernel: workgroups of 64 rows, and enough splits
 // of the channel groups to put about 3072 waves on the chip, with at least 3
@@ -316,7 +295,7 @@ int check_y(void* y, int y_dtype, int b) {
 
 extern "C" {
 
-int svdq_abi_version(void) { return 105; }
+int svdq_abi_version(void) { return 106; }
 
 int svdq_test_set_svd_iteration_limit(int limit) { return set_eig_iteration_limit(limit); }
 
@@ -535,8 +514,8 @@ int svdq_gemm_schedule(int b, int n, int m, int setting, int* info) {
   const GemmPlan p = gemm_plan(b, n, m, device_cus(), fmt);
   info[0] = p.tiles_m * p.tiles_n;
   info[1] = p.grid;
-  info[2] = p.streamk ? p.sk_grid : 0;
-  info[3] = p.streamk ? p.sk_tiles : 0;
+  info[2] = p.split ? p.split_grid : 0;
+  info[3] = p.split ? p.split_tiles : 0;
   info[4] = p.wg_per_cu;
   return SVDQ_OK;
 }

@@ -43,23 +43,22 @@
 //   already interleave).
 //
 // Schedules (tile = TM x TN outputs over all G groups; slots = the resident
-// workgroups of all CUs: three per CU for launches with one tile per
-// workgroup, two for launches with a stream-K part):
-//   * one tile per workgroup, unless the tiles leave the last round of slots
-//     at most a quarter full;
-//   * otherwise a hybrid: the tiles of the last one or two rounds are shared
-//     out by stream-K among `slots` persistent workgroups (equal (tile, group)
-//     iteration ranges), which are dispatched first; the remaining full rounds
-//     run one tile per workgroup after them.  A stream-K workgroup walks its
-//     range piece by piece (a piece = the part of one tile inside the range).
-//     A whole tile is stored directly; any other piece writes its fp32 sums to
-//     a partial slot and registers its arrival on the tile's counter (a
-//     device-scope atomic).  The last piece of a tile to arrive adds all of
-//     the tile's partial slots in ascending group order and stores the tile.
-//     No workgroup waits for another, so correctness does not depend on the
-//     order or residency in which workgroups are dispatched, and results are
-//     deterministic for a shape and CU count (the summation order is fixed,
-//     whoever arrives last).
+// workgroups of all CUs, three per CU):
+//   * one whole tile per workgroup, when the tiles fill whole rounds of slots
+//     or their last round is more than a third full;
+//   * otherwise the tiles of the last round are split along the channel
+//     groups into k pieces each, one piece per workgroup (split workgroups
+//     first in the grid, then the full rounds of whole tiles).  A piece
+//     stores its sums in a partial slot of the workspace and ends; a
+//     reduction kernel launched next on the same stream adds each tile's k
+//     slots in piece order, applies the epilogue and stores the tile.  No
+//     workgroup waits for or signals another (the kernel boundary orders the
+//     slots' stores before their loads), so correctness does not depend on
+//     the order or residency in which workgroups are dispatched, and results
+//     are deterministic for a shape and CU count.  Device-scope atomics and
+//     coherent loads, the alternative inside one kernel, measured 4-5 us per
+//     round trip here: the last piece of a 256-row FLUX tile spent 35 us
+//     adding eight 64 KB slots.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -169,27 +168,20 @@ __device__ __forceinline__ void unrolled(std::integer_sequence<int, U...>, F&& f
 }
 
 // Linear tile index -> (tile row, tile column), so that tiles with nearby
-// indices share activation and weight records.  Each XCD runs a contiguous
-// range of linear tiles (dp_tile), and its L2 keeps the records that range
-// re-reads most.
-//  * Row bands (COLS = false): bands of 4 tile-rows, column-major inside.  An
-//    XCD keeps its few activation rows and streams the weight columns.
-//  * Column bands (COLS = true): bands of ceil(tiles_n / 8) tile-columns,
-//    row-major inside.  An XCD keeps its eighth of the weight columns and
-//    streams the activation rows.  Against row bands, measured on gfx950:
-//    2-3 % faster with the stream-K build (FLUX fc2 and single-block out),
-//    but 1-4 % slower with the one-tile build (FLUX QKV, despite 26 % less
-//    HBM fetch), which therefore keeps row bands.
-template <bool COLS>
+// indices share activation and weight records: bands of 4 tile-rows,
+// column-major inside.  Each XCD runs a contiguous range of linear tiles
+// (dp_tile) and keeps its few activation rows in L2 while it streams the
+// weight columns.  Measured on gfx950: column bands (an XCD keeping an eighth
+// of the weight columns) were 1-4 % slower for one tile per workgroup, despite
+// 26 % less HBM fetch on FLUX QKV.
 __device__ __forceinline__ void band_tile(int t, int tiles_m, int tiles_n, int& ti, int& tj) {
-  const int along = COLS ? tiles_n : tiles_m, across = COLS ? tiles_m : tiles_n;
-  const int GB = COLS ? max(1, (tiles_n + 7) >> 3) : 4;
-  const int band = t / (GB * across);
+  constexpr int GB = 4;
+  const int band = t / (GB * tiles_n);
   const int first = band * GB;
-  const int gb = min(along - first, GB);
-  const int in_band = t - band * GB * across;
-  (COLS ? tj : ti) = first + in_band % gb;
-  (COLS ? ti : tj) = in_band / gb;
+  const int gb = min(tiles_m - first, GB);
+  const int in_band = t - band * GB * tiles_n;
+  ti = first + in_band % gb;
+  tj = in_band / gb;
 }
 
 // Workgroup d of `count` one-tile workgroups -> linear tile base + t.
@@ -225,38 +217,27 @@ struct GemmCfg {
 
 // 128 x 128 tile, 4 waves of 64 x 64; three workgroups share a CU (168
 // registers per lane), so one workgroup's barrier and LDS-latency phases
-// overlap the others' compute, and loads run one group ahead.  This build
-// runs schedules of one tile per workgroup only: with the stream-K code it
-// needs more than 168 registers and would spill, which the build refuses
-// (every kernel of the library is checked for zero scratch at build time and
-// before its first launch), so stream-K launches use CfgSk.
+// overlap the others' compute, and loads run one group ahead.  Each format
+// has one configuration; launches with split tiles use its build with the
+// split-K code (SK = true), which fits the same register budget (every kernel
+// of the library is checked for zero scratch at build time and before its
+// first launch).
 using Cfg = GemmCfg<128, 128, 64, 64, 3, 1>;
-// INT4 launches with a stream-K part: two workgroups per CU, loads two groups
-// ahead (no spills at 256 registers).
-using CfgSk = GemmCfg<128, 128, 64, 64, 2, 2>;
-// 8-bit codes: no per-group VALU work, so a group's compute is short.  One
-// tile per workgroup: three workgroups per CU (140 registers), loads two
-// groups ahead; stream-K launches: two per CU, loads four groups ahead.
-using Cfg8Dp = GemmCfg<128, 128, 64, 64, 3, 2>;
-using Cfg8 = GemmCfg<128, 128, 64, 64, 2, 4>;
-// NVFP4 (packed records in LDS, 20 KB per workgroup): like INT4, a
-// stream-K-free build at three workgroups per CU for one tile per workgroup,
-// and two per CU for stream-K launches.
-using CfgF4Dp = GemmCfg<128, 128, 64, 64, 3, 1>;
-using CfgF4 = GemmCfg<128, 128, 64, 64, 2, 2>;
+// 8-bit codes: no per-group VALU work, so a group's compute is short: loads
+// run two groups ahead (140 registers).
+using Cfg8 = GemmCfg<128, 128, 64, 64, 3, 2>;
+// NVFP4 (packed records in LDS, 20 KB per workgroup).
+using CfgF4 = GemmCfg<128, 128, 64, 64, 3, 1>;
 
-// Cache policy of the stream-K partials: sc1 = device-coherent.
-constexpr int kCoherent = 16;
-// s_waitcnt immediate that waits for vmcnt 0 only (expcnt 7, lgkmcnt 15).
-constexpr int kWaitVmcnt0 = 0x0F70;
-
-struct StreamK {
-  int P;                          // stream-K workgroups: blockIdx < P (0 = none)
-  int T;                          // stream-K tiles: linear tiles [0, T)
-  unsigned U;                     // their (tile, group) iterations: T * G (U * P < 2^32)
-  float* partials;                // [2 P][TM*TN] fp32 (or i32), in accumulator order
-  unsigned long long* counters;   // [T] per-tile arrival counters: (tag << 32) | arrivals
-  unsigned tag;                   // this launch's tag (low 32 bits of its epoch)
+// Split tiles of a launch: workgroups [0, P) each compute one piece of one of
+// the first T linear tiles (k pieces per tile, P = T k); the remaining
+// workgroups compute whole tiles.
+struct SplitK {
+  int P;            // split workgroups: blockIdx < P (0 = none)
+  int T;            // split tiles: linear tiles [0, T)
+  int k;            // pieces per split tile
+  float* partials;  // [k + 1][T][TM*TN] fp32 (or i32): piece q of tile t in slot q*T + t,
+                    // the low-rank product of tile t (8-bit setting) in slot k*T + t
 };
 
 // Non-negative E4M3 block-scale byte -> its value as fp16 bits (exact: E4M3
@@ -295,7 +276,7 @@ __device__ __forceinline__ f16x8 fp4_operand(uint32_t w, _Float16 s) {
 //    [m/64][rows][64], with one fp16 scale per row and per column.  The MFMAs
 //    chain over all groups into i32 accumulators (|sum| <= 127^2 m < 2^31 for
 //    the m the library accepts) and the scales are applied once, in the
-//    epilogue, so no per-group VALU work remains; stream-K partials are then
+//    epilogue, so no per-group VALU work remains; split-K partials are then
 //    i32 sums;
 //  * kFmtFp4: the NVFP4 setting, FP4 E2M1 codes in the INT4 record layout and
 //    one FP8 E4M3 scale per 16 channels (records [m/64][rows][4] bytes).  A
@@ -311,10 +292,11 @@ __device__ __forceinline__ void gemm_up_body(
     const float* __restrict__ z, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, int b, int n, int G, int rank, int tiles_m, int tiles_n,
-    void* __restrict__ yout, StreamK sk, float txw) {
+    void* __restrict__ yout, SplitK sk, float txw) {
   constexpr bool W8 = FMT == kFmtInt8, F4 = FMT == kFmtFp4;
-  constexpr bool POST = W8 || F4;  // scales and the low-rank branch after the main loop
-  constexpr bool kColBands = SK && FMT == kFmtInt4;  // tile order (band_tile)
+  // INT4 starts the accumulators from the low-rank product; the 8-bit and
+  // NVFP4 settings apply their scales after the main loop and then add it.
+  constexpr bool POST = W8 || F4;
   static_assert(!W8 || (2 * C::A_BYTES == 32 && 2 * C::B_BYTES == 32), "8-bit records: 32-byte staging pieces");
   static_assert(!F4 || (C::A_BYTES == 16 && C::B_BYTES == 16), "FP4 records: 16-byte staging pieces");
   constexpr int TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN, NT = C::NT;
@@ -572,48 +554,33 @@ __device__ __forceinline__ void gemm_up_body(
           sw8[h] = *reinterpret_cast<const f16x8*>(reinterpret_cast<const _Float16*>(sc + TM) + WN * wn +
                                                    4 * BJ * c + 8 * h);
         const int rbase = WM * wm + r;
-        // an FMA needs its block's MFMA results: at two waves per SIMD the
-        // FMAs of block bi run after the MFMAs of block bi + 1 (results
-        // double-buffered) to cover the MFMA latency; at three the register
-        // budget holds one block's results and the other waves cover it
-        constexpr bool DB = C::WPE <= 2;
-        i32x4 d[DB ? 2 : 1][BJ];
-        float sxq[2], sng[2];
-        // At three waves per SIMD, the wave's BI activation fragments are all
-        // read up front (the compiler would otherwise read each just before
-        // its block's MFMAs and wait out the LDS latency BI times per group):
-        // measured 2-4 % faster on FLUX QKV and PixArt fc1.  The two-per-CU
-        // build reads them block by block (1-2 % faster there).
-        u32x4 Qall[DB ? 1 : BI];
-        if constexpr (!DB) {
+        // The wave's BI activation fragments are all read up front (the
+        // compiler would otherwise read each just before its block's MFMAs and
+        // wait out the LDS latency BI times per group): measured 2-4 % faster
+        // on FLUX QKV and PixArt fc1.  An FMA needs its block's MFMA results;
+        // the register budget holds one block's results, and the other waves
+        // of the SIMD cover the MFMA latency.
+        u32x4 Qall[BI];
 #pragma unroll
-          for (int bi = 0; bi < BI; ++bi)
-            Qall[bi] = *reinterpret_cast<const u32x4*>(as + (rbase + 16 * bi) * ROWB + cs);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int bi = 0; bi < BI; ++bi)
+          Qall[bi] = *reinterpret_cast<const u32x4*>(as + (rbase + 16 * bi) * ROWB + cs);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int bi = 0; bi <= BI; ++bi) {
-          const int cur = DB ? bi & 1 : 0, prev = DB ? cur ^ 1 : 0;
-          const int ab = DB ? bi - 1 : bi;  // the block whose results are applied
-          if (bi < BI) {
-            const u32x4 Qa = DB ? *reinterpret_cast<const u32x4*>(as + (rbase + 16 * bi) * ROWB + cs) : Qall[DB ? 0 : bi];
-            sxq[bi & 1] = sx4[bi];
-            sng[bi & 1] = -kMagic * sx4[bi];  // exact: 3 * 2^14 * sx
+        for (int bi = 0; bi < BI; ++bi) {
+          const float sxq = sx4[bi];
+          const float sng = -kMagic * sx4[bi];  // exact: 3 * 2^14 * sx
+          i32x4 d[BJ];
 #pragma unroll
-            for (int bj = 0; bj < BJ; ++bj)
-              d[cur][bj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                  __builtin_bit_cast(i32x4, Pb[bj]), __builtin_bit_cast(i32x4, Qa), magic, 0, 0, 0);
-          }
-          if (ab >= 0 && ab < BI) {
-            const int rd = DB ? prev : cur;
+          for (int bj = 0; bj < BJ; ++bj)
+            d[bj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, Pb[bj]),
+                                                          __builtin_bit_cast(i32x4, Qall[bi]), magic, 0, 0, 0);
 #pragma unroll
-            for (int bj = 0; bj < BJ; ++bj)
+          for (int bj = 0; bj < BJ; ++bj)
 #pragma unroll
-              for (int v = 0; v < 4; ++v) {
-                const float t = __builtin_fmaf(__int_as_float(d[rd][bj][v]), sxq[ab & 1], sng[ab & 1]);
-                acc[ab][bj][v] = __builtin_fmaf(t, (float)sw8[bj >> 1][4 * (bj & 1) + v], acc[ab][bj][v]);
-              }
-          }
+            for (int v = 0; v < 4; ++v) {
+              const float t = __builtin_fmaf(__int_as_float(d[bj][v]), sxq, sng);
+              acc[bi][bj][v] = __builtin_fmaf(t, (float)sw8[bj >> 1][4 * (bj & 1) + v], acc[bi][bj][v]);
+            }
         }
       }
     };
@@ -708,6 +675,12 @@ __device__ __forceinline__ void gemm_up_body(
           acc[bi][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
   };
+  auto zero_acc_f32 = [&]() {
+#pragma unroll
+    for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < BJ; ++bj) acc[bi][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
 
   // 8-bit setting, after all groups: acc = isum * (sx sw); the product of the
   // two fp16 scales is exact in fp32, so each element takes the rounding of the
@@ -736,129 +709,93 @@ __device__ __forceinline__ void gemm_up_body(
     }
   };
 
-  if (!SK || (int)blockIdx.x >= sk.P) {  // one tile per workgroup
-    const int T = tiles_m * tiles_n;
-    int ti, tj;
-    band_tile<kColBands>(dp_tile((int)blockIdx.x - sk.P, T - sk.T, sk.T), tiles_m, tiles_n, ti, tj);
-    zero_acc();
-    main_branch(ti * TM, tj * TN, 0, G, [&] {
-      if constexpr (!POST) lowrank(ti * TM, tj * TN);
-    });
-    if constexpr (POST) {
-      scale_sums(ti * TM, tj * TN);
-      lowrank(ti * TM, tj * TN);
-    }
-    store_tile(ti * TM, tj * TN);
-    return;
+  // ---- this workgroup's work: a whole tile, or one piece of a split tile ----
+  // Split pieces come first in the grid.  A piece stores its raw sums (fp32,
+  // or i32 in the 8-bit setting) in its partial slot and ends; the reduction
+  // kernel launched after this one adds each tile's k slots in piece order
+  // and applies the epilogue.  The kernel boundary orders the slots' stores
+  // before their loads, so no workgroup waits for or signals another, and the
+  // result does not depend on dispatch order (deterministic for a shape and
+  // CU count).  The piece with the tile's last groups carries the low-rank
+  // product in its sums (INT4), or, in the 8-bit setting (integer sums),
+  // stores it alone in slot k of the tile (NVFP4 tiles are never split).
+  const int T = tiles_m * tiles_n;
+  const bool split = SK && (int)blockIdx.x < sk.P;
+  int t, g0 = 0, g1 = G;
+  if (split) {
+    t = (int)blockIdx.x / sk.k;
+    const int j = (int)blockIdx.x - t * sk.k;
+    g0 = (int)((long long)j * G / sk.k);
+    g1 = (int)((long long)(j + 1) * G / sk.k);
+  } else {
+    t = dp_tile((int)blockIdx.x - sk.P, T - sk.T, sk.T);
   }
-  if constexpr (!SK) return;
-
-  // ---- stream-K: iterations [u0, u1) of this workgroup, descending ----------
-  // A piece = the part of one tile inside this workgroup's range.  A whole
-  // tile is stored directly.  Otherwise the piece's sums go to a partial slot
-  // (slot 2p for the piece holding the range's last iteration, 2p + 1 for the
-  // one holding its first), and the workgroup registers its arrival on the
-  // tile's counter; the LAST of the tile's pieces to arrive adds all of the
-  // tile's partial slots in ascending group order (a fixed order, whoever
-  // arrives last) and stores the tile.  No workgroup ever waits for another,
-  // so nothing depends on the order in which workgroups are dispatched.
-  // Counters carry the launch's tag in their upper half: a counter left by
-  // another launch (or never initialised) reads as no arrivals; the finisher
-  // resets its tile's counter to (tag, 0), so a replay of the same launch
-  // (a captured graph) starts from zero arrivals too.
-  // Ranges in 32-bit arithmetic: the planner keeps U * P below 2^32.
-  const unsigned p = blockIdx.x, P = (unsigned)sk.P, U = sk.U, Gu = (unsigned)G;
-  // Partial slot layout, in 16-byte units: [wave][block k = bi BJ + bj][lane],
-  // so each store or load of a wave moves 1 KB contiguous.  The byte offset
-  // wave*16 KB + k KB + 16 lane is split into a per-lane base, a scalar
-  // 4 KB multiple and an instruction immediate below 4 KB (few scalar
-  // registers, no per-block vector offsets).
-  static_assert(BI * BJ == 16 && NT == 256, "partial layout: 16 blocks of 1 KB per wave");
-  const uint32_t part_voff = (uint32_t)(wave * 16384 + lane * 16);
-  auto partial_offset = [](int k) { return (uint32_t)((k & 3) * 1024); };
-  auto partial_soffset = [](int k) { return (k >> 2) * 4096; };
-  auto range_start = [&](unsigned q) { return q * U / P; };
-  const unsigned u0 = range_start(p), u1 = range_start(p + 1);
-  __shared__ int s_last;
-  unsigned u = u1;
-  while (u > u0) {
-    const unsigned t = (u - 1) / Gu, ts = t * Gu;
-    const unsigned lo = u0 > ts ? u0 : ts;
-    const int g0 = (int)(lo - ts), g1 = (int)(u - ts);
-    int ti, tj;
-    band_tile<kColBands>((int)t, tiles_m, tiles_n, ti, tj);
-    const int i0 = ti * TM, j0 = tj * TN;
-    zero_acc();
-    main_branch(i0, j0, g0, g1, [&] {
-      if (!POST && g1 == G) lowrank(i0, j0);  // the tile's last groups carry the low-rank branch
-    });
-    if (g0 > 0 || g1 < G) {
-      // workgroups qlo .. qhi hold the tile's pieces (every stream-K workgroup
-      // has at least 8 iterations, so none is empty); q's piece is in its
-      // slot 0 when q's range ends inside this tile
-      unsigned qlo = p, qhi = p;
-      while (qlo > 0 && range_start(qlo) > ts) --qlo;
-      while (qhi + 1 < P && range_start(qhi + 1) < ts + Gu) ++qhi;
-      auto slot_of = [&](unsigned q) {
-        const unsigned last = range_start(q + 1) - 1;
-        return 2 * q + (last >= ts && last < ts + Gu ? 0u : 1u);
-      };
-      // Partials are written and read only with device-coherent (sc1) buffer
-      // accesses, so no L2 writeback or invalidate is needed: each wave waits
-      // for its stores to complete (vmcnt 0) before the barrier after which
-      // the arrival (a device-scope atomic) is registered.
-      const __amdgpu_buffer_rsrc_t rp = make_rsrc(sk.partials + (size_t)slot_of(p) * (TM * TN), TM * TN * 4);
-#pragma unroll
-      for (int bi = 0; bi < BI; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < BJ; ++bj)
-          __builtin_amdgcn_raw_buffer_store_b128(W8 ? __builtin_bit_cast(u32x4, iacc[bi][bj])
-                                                    : __builtin_bit_cast(u32x4, acc[bi][bj]),
-                                                 rp, part_voff + partial_offset(bi * BJ + bj), partial_soffset(bi * BJ + bj),
-                                                 kCoherent);
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __syncthreads();
-      if (tid == 0) {
-        unsigned long long* cnt = sk.counters + t;
-        unsigned long long seen = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), next;
-        do {  // lock-free: a failed exchange means another piece arrived
-          next = (unsigned)(seen >> 32) == sk.tag ? seen + 1 : ((unsigned long long)sk.tag << 32) | 1ull;
-        } while (!__hip_atomic_compare_exchange_weak(cnt, &seen, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT));
-        const bool last = (unsigned)next == qhi - qlo + 1;
-        if (last) __hip_atomic_store(cnt, (unsigned long long)sk.tag << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = last ? 1 : 0;
-      }
-      __syncthreads();
-      const int last = __builtin_amdgcn_readfirstlane(s_last);
-      __syncthreads();  // s_last is rewritten by the next piece
-      if (!last) {
-        u = lo;
-        continue;
-      }
-      // the tile's partial slots in ascending group order (device-coherent loads)
-      for (unsigned q = qlo; q <= qhi; ++q) {
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(sk.partials + (size_t)slot_of(q) * (TM * TN), TM * TN * 4);
+  int ti, tj;
+  band_tile(t, tiles_m, tiles_n, ti, tj);
+  const int i0 = ti * TM, j0 = tj * TN;
+  zero_acc();
+  main_branch(i0, j0, g0, g1, [&] {
+    // the tile's last groups carry the low-rank branch
+    if constexpr (!POST)
+      if (g1 == G) lowrank(i0, j0);
+  });
+  if constexpr (SK) {
+    if (split) {
+      // Slot layout, in 16-byte units: [wave][block k = bi BJ + bj][lane], so
+      // each store of a wave writes 1 KB contiguous (the reduction kernel
+      // maps units back to outputs the same way); the byte offset
+      // wave*16 KB + k KB + 16 lane is split into a per-lane base, a scalar
+      // 4 KB multiple and an instruction immediate below 4 KB.  Slots are
+      // piece-major: piece q of split tile t in slot q*T + t.
+      static_assert(BI * BJ == 16 && NT == 256, "partial layout: 16 blocks of 1 KB per wave");
+      const uint32_t part_voff = (uint32_t)(wave * 16384 + lane * 16);
+      auto partial_offset = [](int q) { return (uint32_t)((q & 3) * 1024); };
+      auto partial_soffset = [](int q) { return (q >> 2) * 4096; };
+      auto store_slot = [&](int slot, auto&& val) {
+        const __amdgpu_buffer_rsrc_t rp = make_rsrc(sk.partials + (size_t)slot * (TM * TN), TM * TN * 4);
 #pragma unroll
         for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
-          for (int bj = 0; bj < BJ; ++bj) {
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rq, part_voff + partial_offset(bi * BJ + bj),
-                                                                 partial_soffset(bi * BJ + bj), kCoherent);
-            if constexpr (W8)
-              iacc[bi][bj] = q == qlo ? __builtin_bit_cast(i32x4, v) : iacc[bi][bj] + __builtin_bit_cast(i32x4, v);
-            else
-              acc[bi][bj] = q == qlo ? __builtin_bit_cast(f32x4, v) : acc[bi][bj] + __builtin_bit_cast(f32x4, v);
-          }
+          for (int bj = 0; bj < BJ; ++bj)
+            __builtin_amdgcn_raw_buffer_store_b128(val(bi, bj), rp, part_voff + partial_offset(bi * BJ + bj),
+                                                   partial_soffset(bi * BJ + bj), 0);
+      };
+      const int piece = (int)blockIdx.x - t * sk.k;
+      if constexpr (W8)
+        store_slot(piece * sk.T + t, [&](int bi, int bj) { return __builtin_bit_cast(u32x4, iacc[bi][bj]); });
+      else
+        store_slot(piece * sk.T + t, [&](int bi, int bj) { return __builtin_bit_cast(u32x4, acc[bi][bj]); });
+      if constexpr (!POST) {
+        return;
+      } else {
+        // the piece with the tile's last groups: its low-rank product alone,
+        // in slot k of the tile (one lowrank call site below keeps the
+        // register allocation of the epilogue shared)
+        if (g1 != G || rank <= 0) return;
+        zero_acc_f32();
       }
     }
-    if constexpr (POST) {
-      scale_sums(i0, j0);
-      lowrank(i0, j0);
-    }
-    store_tile(i0, j0);
-    u = lo;
   }
+  if constexpr (POST) {
+    if (!split) scale_sums(i0, j0);
+    lowrank(i0, j0);
+    if constexpr (SK) {
+      if (split) {
+        const __amdgpu_buffer_rsrc_t rp =
+            make_rsrc(sk.partials + ((size_t)sk.k * sk.T + t) * (TM * TN), TM * TN * 4);
+        const uint32_t part_voff = (uint32_t)(wave * 16384 + lane * 16);
+#pragma unroll
+        for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < BJ; ++bj)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[bi][bj]), rp,
+                                                   part_voff + (uint32_t)(((bi * BJ + bj) & 3) * 1024),
+                                                   ((bi * BJ + bj) >> 2) * 4096, 0);
+        return;
+      }
+    }
+  }
+  store_tile(i0, j0);
 }
 
 template <class C, bool OUT_BF16, bool SK>
@@ -867,7 +804,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
     const float* __restrict__ z, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, int b, int n, int G, int rank, int tiles_m, int tiles_n,
-    void* __restrict__ yout, StreamK sk, float txw) {
+    void* __restrict__ yout, SplitK sk, float txw) {
   gemm_up_body<C, OUT_BF16, kFmtInt4, SK>(qx, ascale, z, qw, wscale, l2t, bias, b, n, G, rank, tiles_m, tiles_n,
                                           yout, sk, txw);
 }
@@ -878,7 +815,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
     const float* __restrict__ z, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, int b, int n, int G, int rank, int tiles_m, int tiles_n,
-    void* __restrict__ yout, StreamK sk, float txw) {
+    void* __restrict__ yout, SplitK sk, float txw) {
   gemm_up_body<C, OUT_BF16, kFmtInt8, SK>(qx, ascale, z, qw, wscale, l2t, bias, b, n, G, rank, tiles_m, tiles_n,
                                           yout, sk, txw);
 }
@@ -889,9 +826,87 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE, C
     const float* __restrict__ z, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, int b, int n, int G, int rank, int tiles_m, int tiles_n,
-    void* __restrict__ yout, StreamK sk, float txw) {
+    void* __restrict__ yout, SplitK sk, float txw) {
   gemm_up_body<C, OUT_BF16, kFmtFp4, SK>(qx, ascale, z, qw, wscale, l2t, bias, b, n, G, rank, tiles_m, tiles_n,
                                          yout, sk, txw);
+}
+
+// Reduction of the split tiles: thread u handles 16-byte unit u of every slot
+// of its tile (4 consecutive outputs of one row, in the slot layout the pieces
+// store), adds the k pieces' units in piece order (i32 in the 8-bit setting,
+// exact), applies the epilogue the whole tiles apply (8-bit: the per-row and
+// per-column scales, then the tile's low-rank slot), adds the bias and stores
+// Y.  All k loads are issued before the first add.  (NVFP4 tiles are never
+// split.)
+template <class C, int FMT, bool OUT_BF16>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(
+    const float* __restrict__ partials, int T, int k, int tiles_m, int tiles_n, int b, int n,
+    const uint16_t* __restrict__ ascale, const uint16_t* __restrict__ wscale, int lowrank_slot,
+    const uint16_t* __restrict__ bias, void* __restrict__ yout) {
+  static_assert(C::NT == 256 && C::BI * C::BJ == 16 && kMaxPiecesAll <= 16, "unit layout of the slots");
+  static_assert(FMT == kFmtInt4 || FMT == kFmtInt8, "INT4 and 8-bit tiles only");
+  constexpr int UNITS = C::TM * C::TN / 4;  // 16-byte units per slot
+  const int u = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  const int t = u / UNITS, w = u - t * UNITS;
+  if (t >= T) return;
+  const int wave = w >> 10, blk = (w >> 6) & 15, lane = w & 63;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int bi = blk / C::BJ, bj = blk % C::BJ;
+  int ti, tj;
+  band_tile(t, tiles_m, tiles_n, ti, tj);
+  const int i = ti * C::TM + C::WM * wm + 16 * bi + (lane & 15);
+  const int j = tj * C::TN + C::WN * wn + 16 * bj + 4 * (lane >> 4);
+  if (i >= b || j >= n) return;
+  const f32x4* slots = reinterpret_cast<const f32x4*>(partials);
+  const size_t stride = (size_t)T * UNITS, base = (size_t)t * UNITS + w;
+  f32x4 v[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    if (q < k) v[q] = slots[base + (size_t)q * stride];
+  f32x4 o;
+  if constexpr (FMT == kFmtInt8) {
+    i32x4 s = __builtin_bit_cast(i32x4, v[0]);
+#pragma unroll
+    for (int q = 1; q < 16; ++q)
+      if (q < k) s += __builtin_bit_cast(i32x4, v[q]);
+    const float sx = f16_to_f32(ascale[i]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (float)s[e] * (sx * (j + e < n ? f16_to_f32(wscale[j + e]) : 0.0f));
+  } else {
+    o = v[0];
+#pragma unroll
+    for (int q = 1; q < 16; ++q)
+      if (q < k) o += v[q];
+  }
+  if (lowrank_slot) o += slots[base + (size_t)k * stride];
+  float bv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (bias) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (j + e < n) bv[e] = __uint_as_float((uint32_t)bias[j + e] << 16);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] += bv[e];
+  const bool vec_ok = (n & 3) == 0 && ((uintptr_t)yout & (OUT_BF16 ? 7u : 15u)) == 0 && j + 3 < n;
+  if (OUT_BF16) {
+    uint16_t* y = reinterpret_cast<uint16_t*>(yout) + (size_t)i * n + j;
+    if (vec_ok) {
+      *reinterpret_cast<uint2*>(y) = uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j + e < n) y[e] = bf16_bits(o[e]);
+    }
+  } else {
+    float* y = reinterpret_cast<float*>(yout) + (size_t)i * n + j;
+    if (vec_ok) {
+      *reinterpret_cast<f32x4*>(y) = o;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j + e < n) y[e] = o[e];
+    }
+  }
 }
 
 int g_num_cus = 0;
@@ -923,41 +938,52 @@ int scratch_free(const void* kernel) {
 }
 
 template <class K, class... Args>
-int launch_checked(K kernel, const GemmPlan& plan, int threads, hipStream_t st, Args... args) {
+int launch_checked(K kernel, int grid, int threads, hipStream_t st, Args... args) {
   const int ok = scratch_free(reinterpret_cast<const void*>(kernel));
   if (ok != 0) return ok;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)plan.grid), dim3(threads), 0, st, args...);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(threads), 0, st, args...);
   return (int)hipGetLastError();
 }
 
 template <bool OUT_BF16, int FMT>
 int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, const Operands& L, int b,
                  void* y, const GemmPlan& plan, void* ws, hipStream_t st, float txw = 1.0f) {
-  StreamK sk{0, 0, 0, nullptr, nullptr, 0u};
-  if (plan.streamk) {
-    sk.P = plan.sk_grid;
-    sk.T = plan.sk_tiles;
-    sk.U = (unsigned)plan.sk_tiles * (unsigned)plan.G;
+  SplitK sk{0, 0, 1, nullptr};
+  if (plan.split) {
+    sk.P = plan.split_grid;
+    sk.T = plan.split_tiles;
+    sk.k = plan.pieces;
     sk.partials = reinterpret_cast<float*>(ws);
-    sk.counters = reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(ws) + plan.partial_bytes);
-    sk.tag = (unsigned)next_launch_epoch();
   }
+  using CF = std::conditional_t<FMT == kFmtInt8, Cfg8, Cfg>;
 #define SVDQ_GEMM_ARGS qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m, \
                        plan.tiles_n, y, sk, txw
+  int st_gemm;
   if constexpr (FMT == kFmtInt8) {
-    if (plan.wg_per_cu == Cfg8Dp::WG_PER_CU && !plan.streamk)
-      return launch_checked(gemm_w8a8_up_kernel<Cfg8Dp, OUT_BF16, false>, plan, Cfg8Dp::NT, st, SVDQ_GEMM_ARGS);
-    return launch_checked(gemm_w8a8_up_kernel<Cfg8, OUT_BF16, true>, plan, Cfg8::NT, st, SVDQ_GEMM_ARGS);
+    st_gemm = plan.split
+                  ? launch_checked(gemm_w8a8_up_kernel<Cfg8, OUT_BF16, true>, plan.grid, Cfg8::NT, st, SVDQ_GEMM_ARGS)
+                  : launch_checked(gemm_w8a8_up_kernel<Cfg8, OUT_BF16, false>, plan.grid, Cfg8::NT, st, SVDQ_GEMM_ARGS);
   } else if constexpr (FMT == kFmtFp4) {
-    if (plan.wg_per_cu == CfgF4Dp::WG_PER_CU && !plan.streamk)
-      return launch_checked(gemm_fp4_up_kernel<CfgF4Dp, OUT_BF16, false>, plan, CfgF4Dp::NT, st, SVDQ_GEMM_ARGS);
-    return launch_checked(gemm_fp4_up_kernel<CfgF4, OUT_BF16, true>, plan, CfgF4::NT, st, SVDQ_GEMM_ARGS);
+    // the planner never splits NVFP4 tiles (its split build exceeds the
+    // register budget of three workgroups per CU)
+    if (plan.split) return (int)hipErrorInvalidValue;
+    st_gemm = launch_checked(gemm_fp4_up_kernel<CfgF4, OUT_BF16, false>, plan.grid, CfgF4::NT, st, SVDQ_GEMM_ARGS);
   } else {
-    if (plan.wg_per_cu == Cfg::WG_PER_CU && !plan.streamk)
-      return launch_checked(gemm_w4a4_up_kernel<Cfg, OUT_BF16, false>, plan, Cfg::NT, st, SVDQ_GEMM_ARGS);
-    return launch_checked(gemm_w4a4_up_kernel<CfgSk, OUT_BF16, true>, plan, CfgSk::NT, st, SVDQ_GEMM_ARGS);
+    st_gemm = plan.split
+                  ? launch_checked(gemm_w4a4_up_kernel<Cfg, OUT_BF16, true>, plan.grid, Cfg::NT, st, SVDQ_GEMM_ARGS)
+                  : launch_checked(gemm_w4a4_up_kernel<Cfg, OUT_BF16, false>, plan.grid, Cfg::NT, st, SVDQ_GEMM_ARGS);
   }
 #undef SVDQ_GEMM_ARGS
+  if (st_gemm != 0 || !plan.split) return st_gemm;
+  if constexpr (FMT == kFmtFp4) {
+    return st_gemm;
+  } else {
+    constexpr int UNITS = CF::TM * CF::TN / 4;
+    const int lr_slot = FMT == kFmtInt8 && L.rank > 0 ? 1 : 0;
+    return launch_checked(splitk_reduce_kernel<CF, FMT, OUT_BF16>, (int)(((long long)sk.T * UNITS + 255) / 256),
+                          256, st, (const float*)sk.partials, sk.T, sk.k, plan.tiles_m, plan.tiles_n, b, L.n,
+                          ascale, L.wscale, lr_slot, L.bias, y);
+  }
 }
 
 }  // namespace
@@ -965,13 +991,10 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
 // The launch plan (gemm_plan) is host logic in plan.cpp; the kernel builds
 // here must match the tiling and residencies it plans for.
 static_assert(Cfg::TM == kGemmTileM && Cfg::TN == kGemmTileN, "tile shape");
-static_assert(Cfg::TM == Cfg8::TM && Cfg::TN == Cfg8::TN && Cfg::TM == CfgF4::TM && Cfg::TN == CfgF4::TN &&
-                  Cfg::TM == CfgSk::TM && Cfg::TN == CfgSk::TN && Cfg::TM == Cfg8Dp::TM && Cfg::TN == Cfg8Dp::TN &&
-                  Cfg::TM == CfgF4Dp::TM && Cfg::TN == CfgF4Dp::TN,
+static_assert(Cfg::TM == Cfg8::TM && Cfg::TN == Cfg8::TN && Cfg::TM == CfgF4::TM && Cfg::TN == CfgF4::TN,
               "one tiling for every setting");
-static_assert(Cfg::WG_PER_CU == kGemmWgPerCu[kFmtInt4][0] && CfgSk::WG_PER_CU == kGemmWgPerCu[kFmtInt4][1] &&
-                  Cfg8Dp::WG_PER_CU == kGemmWgPerCu[kFmtInt8][0] && Cfg8::WG_PER_CU == kGemmWgPerCu[kFmtInt8][1] &&
-                  CfgF4Dp::WG_PER_CU == kGemmWgPerCu[kFmtFp4][0] && CfgF4::WG_PER_CU == kGemmWgPerCu[kFmtFp4][1],
+static_assert(Cfg::WG_PER_CU == kGemmWgPerCu[kFmtInt4] && Cfg8::WG_PER_CU == kGemmWgPerCu[kFmtInt8] &&
+                  CfgF4::WG_PER_CU == kGemmWgPerCu[kFmtFp4],
               "resident workgroups per CU of each build");
 
 int device_cus() {

@@ -119,32 +119,32 @@ int launch_act8_quant(const uint16_t* x, int b, int m, const float* smooth_inv, 
                       void* stream);
 int launch_add(void* y, const void* t, size_t count, int y_dtype, void* stream);
 int launch_lowrank_up(const float* z, const svdq_layer& L, int b, void* y, int y_dtype, void* stream);
-// A fresh value per kernel launch in this process (64-bit, starting at a
-// random per-process base): tags the publication flags that kernels keep in
-// caller workspaces, so values left there by earlier launches or other
-// processes never match.
-unsigned long long next_launch_epoch();
-// GEMM launch plan (gemm_kernels.hip): one tile per workgroup, or stream-K
-// over a persistent grid with fp32 partials and publication flags in the
-// workspace.
+// GEMM launch plan (plan.cpp): one tile per workgroup, or the last round's
+// tiles split along the channel groups into pieces, one per workgroup, whose
+// partial sums (in the workspace) a reduction kernel adds after the GEMM.
 constexpr int kMaxCUs = 256;  // largest gfx950 part
 struct GemmPlan {
   int tiles_m, tiles_n, G;
   int grid;             // workgroups launched
-  int streamk;          // 1 = hybrid schedule with a stream-K part
-  int sk_tiles;         // tiles shared out by stream-K (linear tiles [0, sk_tiles))
-  int sk_grid;          // stream-K workgroups (dispatched first)
+  int split;            // 1 = some tiles are split into pieces (split-K)
+  int split_tiles;      // split tiles (linear tiles [0, split_tiles))
+  int pieces;           // pieces per split tile
+  int split_grid;       // split workgroups, split_tiles * pieces (dispatched first)
   int wg_per_cu;        // resident workgroups per CU of the kernel planned for
   size_t partial_bytes; // partial-sum area at the start of the workspace
-  size_t ws_bytes;      // workspace this launch needs (0 for one tile per workgroup)
+  size_t ws_bytes;      // workspace bound for the shape (0 when m has too few groups to split)
 };
 // Operand formats of the GEMM kernel body (INT4 codes, the 8-bit setting, the
 // NVFP4 setting); each has its own resident workgroups per CU.
 enum GemmFormat { kFmtInt4 = 0, kFmtInt8 = 1, kFmtFp4 = 2 };
 // Output tile of every GEMM build, and the resident workgroups per CU of each
-// format's build for one tile per workgroup [0] and for stream-K launches [1].
+// format's kernel (the same with and without split tiles).
 constexpr int kGemmTileM = 128, kGemmTileN = 128;
-constexpr int kGemmWgPerCu[3][2] = {{3, 2}, {3, 2}, {3, 2}};
+constexpr int kGemmWgPerCu[3] = {3, 3, 3};
+// Split-K: pieces per split tile when full rounds of whole tiles run too
+// (kMinPieces .. kMaxPieces) and when every tile is split (2 ..
+// kMaxPiecesAll); each piece has at least kMinPieceGroups channel groups.
+constexpr int kMinPieces = 3, kMaxPieces = 8, kMaxPiecesAll = 16, kMinPieceGroups = 8;
 // cus <= 0 gives the device-independent upper bound used to size workspaces
 // (valid for every format); fmt selects the kernel whose residency is planned.
 GemmPlan gemm_plan(int b, int n, int m, int cus, int fmt = kFmtInt4);
