@@ -108,6 +108,7 @@ ACT_CASES = [
     (5, 64, 256, True, False, 0),        # maximum rank
     (64, 512, 16, True, False, -6),      # t_x too small: block scales saturate at 448
     (64, 512, 16, True, False, 20),      # t_x too large: block scales underflow
+    (4100, 640, 40, True, False, 0),     # wide kernel (16-row strips, waves over the groups)
 ]
 
 

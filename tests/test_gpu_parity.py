@@ -135,6 +135,8 @@ ACT_CASES = [
     (3000, 12288, 48, True, False),  # several LDS chunks per split, odd chunk size
     (1024, 6144, 200, True, False),  # rank > 128: one group per chunk
     (2000, 6144, 72, False, False),  # 8 blocks of Z, two groups per chunk
+    (4100, 640, 40, True, False),    # wide kernel: 16-row strips (ragged last), 10 groups over 8 waves
+    (4096, 1536, 0, False, True),    # wide kernel, codes only, 3 groups per wave
 ]
 
 

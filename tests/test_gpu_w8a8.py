@@ -107,6 +107,7 @@ ACT8_CASES = [
     (7, 12288, 16, True, True),      # 24 pieces per lane
     (5, 16384, 16, True, False),     # row read twice (beyond the register budget)
     (3, 131072, 0, True, False),     # largest m
+    (4100, 640, 24, True, False),    # Z by the wide kernel (16-row strips, waves over the groups)
 ]
 
 

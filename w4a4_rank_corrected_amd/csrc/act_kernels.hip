@@ -102,6 +102,96 @@ __device__ __forceinline__ uint32_t e4m3_bits(float v) {
   return (uint32_t)(v * 512.0f);  // subnormal: v = m 2^-9, m = 1..7 (exact)
 }
 
+// Quantizes one row-group piece of the smoothed tile and stores its codes and
+// scale (INT4 or NVFP4; nothing for kActQuantNone).  v: this lane's 16
+// smoothed bf16 values (channels 8c..8c+7 and 32+8c..32+8c+7 of group g of
+// row `row`), in the lane layout of the act-quant kernels: lanes l, l ^ 16,
+// l ^ 32, l ^ 48 hold the same row.  q_off / s_off: this lane's byte offsets
+// of its code words and of the row's scale in the group's records.
+template <int Q>
+__device__ __forceinline__ void quant_store(const float (&v)[16], int g, int b, int row, int c, uint32_t q_off,
+                                            uint32_t s_off, uint8_t* __restrict__ qx,
+                                            uint16_t* __restrict__ ascale, float tx) {
+  if constexpr (Q == kActQuantFp4) {
+    // NVFP4: blocks of 16 channels; this lane holds half of block c >> 1
+    // (v[0..7]) and half of block 2 + (c >> 1) (v[8..15]), lane l ^ 16 the
+    // other halves.  sb = E4M3(fl32(amax / 6) / t), S = sb t (t a power of
+    // two), codes E2M1_RNE_sat(fl32(v / S)) with the quotient's sign.
+    float am[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) am[e >> 3] = fmaxf(am[e >> 3], fabsf(v[e]));
+    uint32_t w[2];
+    uint32_t sbits[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float a = fmaxf(am[h], __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(am[h]), 0x401F)));
+      const float u = a / 6.0f;                    // IEEE division (correctly rounded)
+      const float sb = e4m3_round(u * (1.0f / tx));  // 1/t and the product are exact
+      sbits[h] = e4m3_bits(sb);
+      const float S = sb * tx;                      // exact
+      const float rc = S > 0.0f ? 1.0f / S : 0.0f;
+      const float S8 = 8.0f * S;
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float vv = v[8 * h + e];
+        const float pq = vv * rc;
+        const float rem = __builtin_fmaf(-pq, S, vv);
+        const float q1 = __builtin_fmaf(rem, rc, pq);
+        y[e] = S > 0.0f ? __builtin_copysignf(fabsf(vv) <= S8 ? q1 : 8.0f, vv) : 0.0f;
+      }
+      // two codes per byte, the even channel in the low nibble (RNE on the
+      // E2M1 grid, saturating: the hardware conversion at unit scale)
+      uint32_t word = 0u;
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[0], y[1], 1.0f, 0);
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[2], y[3], 1.0f, 1);
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[4], y[5], 1.0f, 2);
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[6], y[7], 1.0f, 3);
+      w[h] = word;
+    }
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qx + (size_t)g * b * 32, (uint32_t)b * 32u);
+    __builtin_amdgcn_raw_buffer_store_b32(w[0], rq, q_off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(w[1], rq, q_off + 16u, 0, 0);
+    // block scales: record [m/64][b][4] bytes, byte j = block j; the lanes
+    // with even c store blocks c/2 and 2 + c/2 (odd c: an offset past the
+    // end, dropped)
+    uint8_t* sc8 = reinterpret_cast<uint8_t*>(ascale);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sc8 + (size_t)g * b * 4, (uint32_t)b * 4u);
+    const uint32_t s8_off = (c & 1) == 0 ? (uint32_t)row * 4u + (uint32_t)(c >> 1) : 0x7FFFFFF0u;
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbits[0], rs, s8_off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbits[1], rs, s8_off + 2u, 0, 0);
+  }
+  if constexpr (Q == kActQuantInt4) {
+    float am = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) am = fmaxf(am, fabsf(v[e]));
+    am = max4_rows(am);
+    float s32 = am / 7.0f;                 // IEEE division (correctly rounded)
+    s32 = fminf(s32, 65504.0f);            // saturate instead of rounding to inf
+    const _Float16 s16 = (_Float16)s32;    // round to nearest even
+    const float sf = (float)s16;
+    const float rc = sf > 0.0f ? 1.0f / sf : 0.0f;
+    uint32_t w0 = 0u, w1 = 0u;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pq = v[e] * rc;
+      const float rem = __builtin_fmaf(-pq, sf, v[e]);
+      const float q1 = __builtin_fmaf(rem, rc, pq);
+      const float q = __builtin_amdgcn_fmed3f(q1, -7.0f, 7.0f);
+      const uint32_t nib = __float_as_uint(q + kMagic) & 0xFu;
+      if (e < 8)
+        w0 |= nib << (4 * e);
+      else
+        w1 |= nib << (4 * (e - 8));
+    }
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qx + (size_t)g * b * 32, (uint32_t)b * 32u);
+    __builtin_amdgcn_raw_buffer_store_b32(w0, rq, q_off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(w1, rq, q_off + 16u, 0, 0);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(ascale + (size_t)g * b, (uint32_t)b * 2u);
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, s16), rs, s_off, 0, 0);
+  }
+}
+
 template <int TB, bool SMOOTH, int Q>
 __global__ __launch_bounds__(256) void act_quant_down_kernel(
     const uint16_t* __restrict__ x, int b, int m, int G, const float* __restrict__ inv,
@@ -217,84 +307,7 @@ __global__ __launch_bounds__(256) void act_quant_down_kernel(
       v[2 * q] = bf16_lo(xt[q]);
       v[2 * q + 1] = bf16_hi(xt[q]);
     }
-    if constexpr (Q == kActQuantFp4) {
-      // NVFP4: blocks of 16 channels; this lane holds half of block c >> 1
-      // (v[0..7]) and half of block 2 + (c >> 1) (v[8..15]), lane l ^ 16 the
-      // other halves.  sb = E4M3(fl32(amax / 6) / t), S = sb t (t a power of
-      // two), codes E2M1_RNE_sat(fl32(v / S)) with the quotient's sign.
-      float am[2] = {0.0f, 0.0f};
-#pragma unroll
-      for (int e = 0; e < 16; ++e) am[e >> 3] = fmaxf(am[e >> 3], fabsf(v[e]));
-      uint32_t w[2];
-      uint32_t sbits[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float a = fmaxf(am[h], __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(am[h]), 0x401F)));
-        const float u = a / 6.0f;                    // IEEE division (correctly rounded)
-        const float sb = e4m3_round(u * (1.0f / tx));  // 1/t and the product are exact
-        sbits[h] = e4m3_bits(sb);
-        const float S = sb * tx;                      // exact
-        const float rc = S > 0.0f ? 1.0f / S : 0.0f;
-        const float S8 = 8.0f * S;
-        float y[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float vv = v[8 * h + e];
-          const float pq = vv * rc;
-          const float rem = __builtin_fmaf(-pq, S, vv);
-          const float q1 = __builtin_fmaf(rem, rc, pq);
-          y[e] = S > 0.0f ? __builtin_copysignf(fabsf(vv) <= S8 ? q1 : 8.0f, vv) : 0.0f;
-        }
-        // two codes per byte, the even channel in the low nibble (RNE on the
-        // E2M1 grid, saturating: the hardware conversion at unit scale)
-        uint32_t word = 0u;
-        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[0], y[1], 1.0f, 0);
-        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[2], y[3], 1.0f, 1);
-        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[4], y[5], 1.0f, 2);
-        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[6], y[7], 1.0f, 3);
-        w[h] = word;
-      }
-      const __amdgpu_buffer_rsrc_t rq = make_rsrc(qx + (size_t)g * b * 32, (uint32_t)b * 32u);
-      __builtin_amdgcn_raw_buffer_store_b32(w[0], rq, q_off, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(w[1], rq, q_off + 16u, 0, 0);
-      // block scales: record [m/64][b][4] bytes, byte j = block j; the lanes
-      // with even c store blocks c/2 and 2 + c/2 (odd c: an offset past the
-      // end, dropped)
-      uint8_t* sc8 = reinterpret_cast<uint8_t*>(ascale);
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(sc8 + (size_t)g * b * 4, (uint32_t)b * 4u);
-      const uint32_t s8_off = (c & 1) == 0 ? (uint32_t)row * 4u + (uint32_t)(c >> 1) : 0x7FFFFFF0u;
-      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbits[0], rs, s8_off, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbits[1], rs, s8_off + 2u, 0, 0);
-    }
-    if constexpr (Q == kActQuantInt4) {
-      float am = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) am = fmaxf(am, fabsf(v[e]));
-      am = max4_rows(am);
-      float s32 = am / 7.0f;                 // IEEE division (correctly rounded)
-      s32 = fminf(s32, 65504.0f);            // saturate instead of rounding to inf
-      const _Float16 s16 = (_Float16)s32;    // round to nearest even
-      const float sf = (float)s16;
-      const float rc = sf > 0.0f ? 1.0f / sf : 0.0f;
-      uint32_t w0 = 0u, w1 = 0u;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pq = v[e] * rc;
-        const float rem = __builtin_fmaf(-pq, sf, v[e]);
-        const float q1 = __builtin_fmaf(rem, rc, pq);
-        const float q = __builtin_amdgcn_fmed3f(q1, -7.0f, 7.0f);
-        const uint32_t nib = __float_as_uint(q + kMagic) & 0xFu;
-        if (e < 8)
-          w0 |= nib << (4 * e);
-        else
-          w1 |= nib << (4 * (e - 8));
-      }
-      const __amdgpu_buffer_rsrc_t rq = make_rsrc(qx + (size_t)g * b * 32, (uint32_t)b * 32u);
-      __builtin_amdgcn_raw_buffer_store_b32(w0, rq, q_off, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(w1, rq, q_off + 16u, 0, 0);
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(ascale + (size_t)g * b, (uint32_t)b * 2u);
-      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, s16), rs, s_off, 0, 0);
-    }
+    quant_store<Q>(v, g, b, row, c, q_off, s_off, qx, ascale, tx);
     if constexpr (TB > 0) {
       const bf16x8 a0 = __builtin_bit_cast(bf16x8, u32x4{xt[0], xt[1], xt[2], xt[3]});
       const bf16x8 a1 = __builtin_bit_cast(bf16x8, u32x4{xt[4], xt[5], xt[6], xt[7]});
@@ -347,6 +360,158 @@ __global__ __launch_bounds__(256) void act_quant_down_kernel(
           if (zr < b) zs[(size_t)zr * rank + t] = acc[tb][vv];
         }
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The same computation for many rows (a few thousand): a workgroup of 8
+// waves owns 16 rows, and the waves split the channel groups (wave w takes
+// groups w, w + 8, w + 16, ...), so each row's Z is complete inside one
+// workgroup: the waves' partial Z tiles are added in LDS in wave order and
+// stored once (no split partials in memory, no reduction launch).  Each wave
+// streams its groups through a register ring D groups ahead: the activation
+// piece, its L1 operand pieces (16 B per Z block and channel half; L1 is small
+// and stays in L2) and the group's 64 values of 1/lambda (one dword per lane,
+// passed through a 256-byte LDS slot of the wave to reach the lanes that use
+// them).  The waves never wait for each other before the final reduction.
+// Per element and per row/group the arithmetic is the act-quant kernel's
+// (quant_store); Z is summed over groups in a fixed order for a shape.
+// ---------------------------------------------------------------------------
+constexpr int kWideWaves = kWideWavesPlan;
+template <int TB, bool SMOOTH, int Q>
+__global__ __launch_bounds__(64 * kWideWaves) void act_quant_wide_kernel(
+    const uint16_t* __restrict__ x, int b, int m, int G, const float* __restrict__ inv,
+    const uint16_t* __restrict__ l1t, int rank, uint8_t* __restrict__ qx,
+    uint16_t* __restrict__ ascale, float* __restrict__ zout, float tx) {
+  constexpr int NW = kWideWaves;
+  constexpr int NB = TB > 0 ? TB : 1;
+  constexpr int D = 2;
+  __shared__ __align__(16) float s_inv[NW][64];
+  __shared__ __align__(16) float s_z[TB > 0 ? NW * 16 * 16 * TB : 1];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, c = lane >> 4;
+  const int row0 = blockIdx.x * 16;
+  const int row = row0 + r;
+  const int rows_here = min(16, b - row0);
+  const uint32_t x_bytes = (uint32_t)((rows_here - 1) * m + 64) * 2u;
+  const uint32_t x_off = (uint32_t)(r * m + 8 * c) * 2u;
+  const uint32_t l1_bytes = TB > 0 ? (uint32_t)((rank - 1) * m + 64) * 2u : 0u;
+  const int nj = wave < G ? (G - wave + NW - 1) / NW : 0;  // groups of this wave
+
+  struct Stage {
+    u32x4 xa, xb;
+    u32x4 la[NB], lb[NB];  // L1 rows tb*16 + r, channels 8c.. and 32 + 8c..
+    uint32_t iv;           // 1/lambda of channel `lane` of the group
+  };
+  auto load = [&](int j, Stage& st) {
+    const bool live = j < nj;
+    const int g = live ? wave + NW * j : 0;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (size_t)row0 * m + (size_t)g * 64, live ? x_bytes : 0u);
+    st.xa = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, x_off, 0, 0));
+    st.xb = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, x_off + 64u, 0, 0));
+    if constexpr (TB > 0) {
+      const __amdgpu_buffer_rsrc_t rl = make_rsrc(l1t + (size_t)g * 64, live ? l1_bytes : 0u);
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const int t = tb * 16 + r;
+        const uint32_t off = t < rank ? (uint32_t)(t * m + 8 * c) * 2u : 0xFFFFFFF0u;
+        st.la[tb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, off, 0, 0));
+        st.lb[tb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, off + 64u, 0, 0));
+      }
+    }
+    if constexpr (SMOOTH) {
+      const __amdgpu_buffer_rsrc_t ri = make_rsrc(inv + (size_t)g * 64, live ? 256u : 0u);
+      st.iv = __builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)lane * 4u, 0, 0);
+    }
+  };
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t q_off = (uint32_t)row * 32u + 4u * c;
+  const uint32_t s_off = c == 0 ? (uint32_t)row * 2u : 0xFFFFFFF0u;
+
+  auto process = [&](int j, const Stage& st) {
+    const int g = wave + NW * j;
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = bf16_lo(st.xa[e]);
+      v[2 * e + 1] = bf16_hi(st.xa[e]);
+      v[8 + 2 * e] = bf16_lo(st.xb[e]);
+      v[8 + 2 * e + 1] = bf16_hi(st.xb[e]);
+    }
+    if constexpr (SMOOTH) {
+      // the wave's own slot: LDS accesses of one wave complete in order, so
+      // the previous group's reads finish before this write lands
+      s_inv[wave][lane] = __uint_as_float(st.iv);
+      const float* iv = s_inv[wave];
+      const f32x4 i0 = *reinterpret_cast<const f32x4*>(iv + 8 * c);
+      const f32x4 i1 = *reinterpret_cast<const f32x4*>(iv + 8 * c + 4);
+      const f32x4 i2 = *reinterpret_cast<const f32x4*>(iv + 32 + 8 * c);
+      const f32x4 i3 = *reinterpret_cast<const f32x4*>(iv + 36 + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] *= i0[e];
+        v[4 + e] *= i1[e];
+        v[8 + e] *= i2[e];
+        v[12 + e] *= i3[e];
+      }
+    }
+    uint32_t xt[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      xt[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+      v[2 * q] = bf16_lo(xt[q]);
+      v[2 * q + 1] = bf16_hi(xt[q]);
+    }
+    quant_store<Q>(v, g, b, row, c, q_off, s_off, qx, ascale, tx);
+    if constexpr (TB > 0) {
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, u32x4{xt[0], xt[1], xt[2], xt[3]});
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, u32x4{xt[4], xt[5], xt[6], xt[7]});
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8, st.la[tb]), acc[tb], 0, 0, 0);
+        acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8, st.lb[tb]), acc[tb], 0, 0, 0);
+      }
+    }
+  };
+
+  if (row0 < b) {
+    Stage st[D];
+#pragma unroll
+    for (int u = 0; u < D; ++u) load(u, st[u]);
+    int j = 0;
+    for (; j + D <= nj; j += D) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        process(j + u, st[u]);
+        load(j + u + D, st[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u + 1 < D; ++u)
+      if (j + u < nj) process(j + u, st[u]);
+  }
+
+  if constexpr (TB > 0) {
+    // partial Z of each wave (MFMA D layout: row 4c + v, column 16 tb + r),
+    // then Z[row0 + i][t] = sum over waves in order
+    constexpr int ZC = 16 * TB;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int vv = 0; vv < 4; ++vv) s_z[(wave * 16 + 4 * c + vv) * ZC + tb * 16 + r] = acc[tb][vv];
+    __syncthreads();
+    for (int e = tid; e < 16 * ZC; e += 64 * NW) {
+      const int i = e / ZC, t = e - i * ZC;
+      float zsum = s_z[i * ZC + t];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) zsum += s_z[(w * 16 + i) * ZC + t];
+      if (row0 + i < b && t < rank) zout[(size_t)(row0 + i) * rank + t] = zsum;
     }
   }
 }
@@ -491,6 +656,43 @@ int launch_act_quant_down(const uint16_t* x, int b, int m, int rank, const float
   const int G = m / 64;
   dim3 grid(plan.strips, plan.splits);
   const int tb = act_blocks(rank);
+  if (plan.wide) {  // 16 rows per workgroup, waves over the groups; Z written directly
+#define SVDQ_WIDE_Q(TBV, SM, QV)                                                                        \
+  hipLaunchKernelGGL((act_quant_wide_kernel<TBV, SM, QV>), dim3(plan.strips), dim3(64 * kWideWaves), 0, st, \
+                     x, b, m, G, smooth_inv, l1, rank, qx, ascale, zpart, tx)
+#define SVDQ_WIDE_S(TBV, QV)          \
+  do {                                \
+    if (smooth_inv)                   \
+      SVDQ_WIDE_Q(TBV, true, QV);     \
+    else                              \
+      SVDQ_WIDE_Q(TBV, false, QV);    \
+  } while (0)
+#define SVDQ_WIDE(TBV)                                 \
+  do {                                                 \
+    if (qmode == kActQuantInt4)                        \
+      SVDQ_WIDE_S(TBV, kActQuantInt4);                 \
+    else if (qmode == kActQuantFp4)                    \
+      SVDQ_WIDE_S(TBV, kActQuantFp4);                  \
+    else                                               \
+      SVDQ_WIDE_S(TBV, kActQuantNone);                 \
+  } while (0)
+    if (tb == 0)
+      SVDQ_WIDE(0);
+    else if (tb == 1)
+      SVDQ_WIDE(1);
+    else if (tb == 2)
+      SVDQ_WIDE(2);
+    else if (tb == 3)
+      SVDQ_WIDE(3);
+    else if (tb == 4)
+      SVDQ_WIDE(4);
+    else
+      return (int)hipErrorInvalidValue;  // the plan allows the wide kernel up to rank 64
+#undef SVDQ_WIDE
+#undef SVDQ_WIDE_S
+#undef SVDQ_WIDE_Q
+    return (int)hipGetLastError();
+  }
 #define SVDQ_ACT_Q(TBV, SM, QV)                                                                    \
   hipLaunchKernelGGL((act_quant_down_kernel<TBV, SM, QV>), grid, dim3(256), 0, st, x, b, m, G,     \
                      smooth_inv, l1, rank, qx, ascale, zpart, plan.groups_per_split, tx)

@@ -24,15 +24,31 @@ void set_error(const char* fmt, ...) {
 void clear_error() { g_err[0] = 0; }
 
 
-// Split plan of the act-quant kernel: workgroups of 64 rows, and enough splits
-// of the channel groups to put about 3072 waves on the chip, with at least 3
-// groups per split (the kernel stages 1/lambda and L1 in LDS act_chunk groups
-// at a time).  Depends only on the shape, so the standalone kernel and the fused
-// layer sum Z in the same order.
+// Plan of the act-quant kernels.  With at least 256 strips of 16 rows (b >=
+// 4081), rank <= 48 and at most 3 channel groups per wave (m <= 1536), the
+// wide kernel: one workgroup of 8 waves per strip, each wave over every 8th
+// channel group, Z complete per workgroup (no split partials, no reduction
+// launch).  With more groups per wave its two-deep ring no longer covers the
+// load latency (measured slower than the split kernel and its reduction on
+// the FLUX shapes, m >= 3072).  Otherwise workgroups of 64 rows and enough
+// splits of the channel groups to put about 3072 waves on the chip, with at
+// least 3 groups per split (the kernel stages 1/lambda and L1 in LDS
+// act_chunk groups at a time); the splits' partial Z are added in split order
+// by a second kernel.  Depends only on the shape, so every setting's
+// act-quant kernel, the standalone kernels and the fused layer sum Z in the
+// same order.
 ActPlan act_plan(int b, int m, int rank) {
   ActPlan p;
-  p.strips = (b + 63) / 64;
   const int G = m / SVDQ_GROUP;
+  if ((b + 15) / 16 >= 256 && act_blocks(rank) <= 3 && G <= 3 * kWideWavesPlan) {
+    p.wide = 1;
+    p.strips = (b + 15) / 16;
+    p.splits = 1;
+    p.groups_per_split = G;
+    return p;
+  }
+  p.wide = 0;
+  p.strips = (b + 63) / 64;
   int gps = G;
   if (p.strips > 0) {
     const int splits = std::max(1, (3072 + 4 * p.strips - 1) / (4 * p.strips));
@@ -40,7 +56,6 @@ ActPlan act_plan(int b, int m, int rank) {
   }
   p.groups_per_split = gps;
   p.splits = (G + gps - 1) / gps;
-  (void)rank;
   return p;
 }
 
@@ -449,12 +464,15 @@ int svdq_calibrate_act_amax(const uint16_t* x, int b, int m, float* amax, int ac
   return hip_status(launch_calibrate(x, b, m, amax, accumulate, stream), "calibrate_act_amax");
 }
 
-size_t svdq_act_workspace_size(int b, int m, int rank) {
+// split partials of Z of the act-quant kernels (every setting plans alike)
+static size_t act_ws_bytes(int b, int m, int rank) {
   if (b <= 0 || m < SVDQ_GROUP || m % SVDQ_GROUP || rank <= 0 || rank > SVDQ_MAX_RANK) return 0;
   ActPlan p = act_plan(b, m, rank);
   if (p.splits <= 1) return 0;
   return round_up((size_t)p.splits * (size_t)b * (size_t)rank * 4, kAlign);
 }
+
+size_t svdq_act_workspace_size(int b, int m, int rank) { return act_ws_bytes(b, m, rank); }
 
 int svdq_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int rank, int group,
                                    const float* smooth_inv, const uint16_t* l1, uint8_t* qx,
@@ -738,7 +756,7 @@ int svdq_w8a8_prepare_weights(const float* W, const float* act_amax, int m, int 
   return SVDQ_OK;
 }
 
-size_t svdq_w8a8_act_workspace_size(int b, int m, int rank) { return svdq_act_workspace_size(b, m, rank); }
+size_t svdq_w8a8_act_workspace_size(int b, int m, int rank) { return act_ws_bytes(b, m, rank); }
 
 int svdq_w8a8_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int rank, const float* smooth_inv,
                                         const uint16_t* l1, int8_t* qx, uint16_t* ascale, float* z,
@@ -891,7 +909,7 @@ int svdq_fp4_prepare_weights(const float* W, const float* act_amax, int m, int n
   return SVDQ_OK;
 }
 
-size_t svdq_fp4_act_workspace_size(int b, int m, int rank) { return svdq_act_workspace_size(b, m, rank); }
+size_t svdq_fp4_act_workspace_size(int b, int m, int rank) { return act_ws_bytes(b, m, rank); }
 
 int svdq_fp4_quantize_act_lowrank_down(const uint16_t* x, int b, int m, int rank, const float* smooth_inv,
                                        const uint16_t* l1, float t_x, uint8_t* qx, uint8_t* ascale, float* z,

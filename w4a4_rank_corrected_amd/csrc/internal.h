@@ -96,8 +96,10 @@ constexpr int act_chunk(int blocks) {
              : act_depth(blocks);
 }
 
+constexpr int kWideWavesPlan = 8;  // waves per workgroup of the wide act-quant kernel
 struct ActPlan {
-  int strips;            // ceil(b / 64) row blocks
+  int wide;              // 1: the wide kernel (16-row strips, waves over all groups, no splits)
+  int strips;            // row blocks: ceil(b / 64), or ceil(b / 16) for the wide kernel
   int splits;            // workgroups per strip along the channel groups
   int groups_per_split;  // channel groups handled by one workgroup
 };
