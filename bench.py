@@ -71,7 +71,8 @@ GEMM_KERNEL = "gemm_w4a4_up_kernel"
 # sources whose text defines the GEMM kernel and its launch plan
 GEMM_SOURCES = ["w4a4_rank_corrected_amd/csrc/gemm_kernels.hip",
                 "w4a4_rank_corrected_amd/csrc/device_common.h",
-                "w4a4_rank_corrected_amd/csrc/internal.h"]
+                "w4a4_rank_corrected_amd/csrc/internal.h",
+                "w4a4_rank_corrected_amd/csrc/plan.cpp"]
 COPY_BYTES = 256 << 20     # plain copy used to calibrate the byte counters
 COLD_BYTES = 512 << 20     # rotated footprint of the cold measurement
 

@@ -236,6 +236,7 @@ struct SplitK {
   int P;            // split workgroups: blockIdx < P (0 = none)
   int T;            // split tiles: linear tiles [0, T)
   int k;            // pieces per split tile
+  int lr;           // the low-rank product's cost in groups, taken off the last piece
   float* partials;  // [k + 1][T][TM*TN] fp32 (or i32): piece q of tile t in slot q*T + t,
                     // the low-rank product of tile t (8-bit setting) in slot k*T + t
 };
@@ -723,10 +724,13 @@ __device__ __forceinline__ void gemm_up_body(
   const bool split = SK && (int)blockIdx.x < sk.P;
   int t, g0 = 0, g1 = G;
   if (split) {
+    // pieces of equal time: the tile's work counts the low-rank product (done
+    // by the last piece) as lr groups, so the last piece gets lr fewer
     t = (int)blockIdx.x / sk.k;
     const int j = (int)blockIdx.x - t * sk.k;
-    g0 = (int)((long long)j * G / sk.k);
-    g1 = (int)((long long)(j + 1) * G / sk.k);
+    const int Ge = G + sk.lr;
+    g0 = (int)((long long)j * Ge / sk.k);
+    g1 = j + 1 == sk.k ? G : (int)((long long)(j + 1) * Ge / sk.k);
   } else {
     t = dp_tile((int)blockIdx.x - sk.P, T - sk.T, sk.T);
   }
@@ -948,11 +952,15 @@ int launch_checked(K kernel, int grid, int threads, hipStream_t st, Args... args
 template <bool OUT_BF16, int FMT>
 int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, const Operands& L, int b,
                  void* y, const GemmPlan& plan, void* ws, hipStream_t st, float txw = 1.0f) {
-  SplitK sk{0, 0, 1, nullptr};
+  SplitK sk{0, 0, 1, 0, nullptr};
   if (plan.split) {
     sk.P = plan.split_grid;
     sk.T = plan.split_tiles;
     sk.k = plan.pieces;
+    // about one memory round trip of its loads, measured at 4-6 us, the time
+    // of 4 groups at three workgroups per CU; (k - 1) lr < G - k holds since
+    // every piece has at least kMinPieceGroups groups
+    sk.lr = L.rank > 0 ? kLowRankPieceGroups : 0;
     sk.partials = reinterpret_cast<float*>(ws);
   }
   using CF = std::conditional_t<FMT == kFmtInt8, Cfg8, Cfg>;

@@ -147,6 +147,11 @@ constexpr int kGemmWgPerCu[3] = {3, 3, 3};
 // (kMinPieces .. kMaxPieces) and when every tile is split (2 ..
 // kMaxPiecesAll); each piece has at least kMinPieceGroups channel groups.
 constexpr int kMinPieces = 3, kMaxPieces = 8, kMaxPiecesAll = 16, kMinPieceGroups = 8;
+// The low-rank product's cost in groups: the piece that computes it (the last
+// of its tile) gets this many groups fewer, so a tile's pieces end together.
+constexpr int kLowRankPieceGroups = 4;
+static_assert((kMaxPiecesAll - 1) * kLowRankPieceGroups < kMaxPiecesAll * (kMinPieceGroups - 1),
+              "the last piece keeps at least one group");
 // cus <= 0 gives the device-independent upper bound used to size workspaces
 // (valid for every format); fmt selects the kernel whose residency is planned.
 GemmPlan gemm_plan(int b, int n, int m, int cus, int fmt = kFmtInt4);
