@@ -162,6 +162,32 @@ def test_act_quant_down_parity(S, b, m, rank, smooth, adv):
         assert rel(zd.cpu().numpy(), z_ref) <= Z_TOL
 
 
+def test_z_split_reduction_same_bits_on_both_paths(S):
+    """Few rows and many channel groups: Z is summed over 64 splits (chunks of
+    every 16th split, then the chunks in order).  The 16-byte reduction kernel
+    (z 16-byte aligned) and the one-element kernel (z only 4-byte aligned) must
+    give the same bits, within the oracle's bar."""
+    b, m, rank = 64, 12288, 24
+    need = S.svdq_act_workspace_size(b, m, rank)
+    assert need >= 17 * b * rank * 4      # more than 16 splits: the chunked order matters
+    rng = np.random.default_rng(77)
+    xb = workloads.random_bf16_bits(rng, (b, m), 2.0)
+    x = LY.bf16_bits_to_f32(xb)
+    l1 = O.bf16_from_f32((rng.standard_normal((m, rank)) / np.sqrt(m)).astype(np.float32))
+    xd = dev_bf16(xb)
+    l1d = dev_bf16(np.ascontiguousarray(LY.f32_to_bf16_bits(l1).T))
+    _say(f"z split reduction b={b} m={m} rank={rank}")
+    _, _, za = S.svdq_quantize_act_lowrank_down(xd, None, l1d, rank)
+    store = torch.empty(b * rank + 1, dtype=torch.float32, device="cuda")
+    zm = store[1:].view(b, rank)          # 4-byte aligned, not 16
+    assert zm.data_ptr() % 16 != 0
+    S.svdq_quantize_act_lowrank_down(xd, None, l1d, rank, z=zm)
+    torch.cuda.synchronize()
+    assert torch.equal(za, zm)
+    xt, _, _ = O.quantize_activation(x, None)
+    assert rel(za.cpu().numpy(), O.lowrank_down(xt, l1)) <= Z_TOL
+
+
 # ---------------------------------------------------------------------------
 # fused W4A4 GEMM + up-projection
 # ---------------------------------------------------------------------------

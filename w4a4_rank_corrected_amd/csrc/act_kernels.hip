@@ -598,25 +598,65 @@ __global__ __launch_bounds__(256) void act8_quant_kernel(const uint16_t* __restr
   }
 }
 
-// z[i][t] = sum over splits s (in order) of zpart[s][i][t]: one sum per
-// element, split 0 first, then 1, 2, ...  Each thread handles 4 consecutive
-// elements (16-byte loads and stores) and issues the loads of up to 16 splits
-// before adding them, so a batch of partials costs one memory latency.
+// z[i][t] = the splits' partial sums zpart[s][i][t] added in one fixed order:
+// chunk c (c = 0..15) sums the splits s = c, c + 16, c + 32, ... in turn, then
+// the chunks' sums are added in chunk order (with at most 16 splits this is
+// simply split 0, then 1, 2, ...).  The kernels below all add in exactly this
+// order, so which of them runs (it depends on alignment) changes no bit.
+constexpr int kZChunks = 16;
+
+// At most 16 splits (one per chunk: the order is split 0, 1, 2, ...): each
+// thread handles 4 consecutive elements (16-byte loads and stores) and issues
+// all of its loads before adding them.
 __global__ void z_reduce_kernel(const float* __restrict__ zpart, int splits, size_t count,
                                 float* __restrict__ z) {
   const size_t idx = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (idx >= count) return;
-  f32x4 s;
-  for (int k = 0; k < splits; k += 16) {
-    f32x4 v[16];
+  f32x4 v[kZChunks];
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (k + u < splits) v[u] = *reinterpret_cast<const f32x4*>(zpart + (size_t)(k + u) * count + idx);
+  for (int u = 0; u < kZChunks; ++u)
+    if (u < splits) v[u] = *reinterpret_cast<const f32x4*>(zpart + (size_t)u * count + idx);
+  f32x4 s = v[0];
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (k + u < splits) s = (k + u == 0) ? v[u] : s + v[u];
-  }
+  for (int u = 1; u < kZChunks; ++u)
+    if (u < splits) s += v[u];
   *reinterpret_cast<f32x4*>(z + idx) = s;
+}
+
+// More than 16 splits (few rows, many channel groups): a workgroup takes 16
+// units of 4 consecutive elements, and thread (unit u, chunk c) issues the
+// loads of its chunk's splits at once, so the partials cost one or two memory
+// latencies instead of one per 16 splits.
+__global__ __launch_bounds__(256) void z_reduce_chunked_kernel(const float* __restrict__ zpart, int splits,
+                                                               size_t count, float* __restrict__ z) {
+  __shared__ f32x4 part[kZChunks][16];
+  const int u = threadIdx.x & 15, c = threadIdx.x >> 4;
+  const size_t idx = ((size_t)blockIdx.x * 16 + u) * 4;
+  const bool live = idx < count && c < splits;
+  f32x4 q = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    constexpr int B = 4;  // loads in flight per batch
+    for (int s0 = c; s0 < splits; s0 += B * kZChunks) {
+      f32x4 v[B];
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        const int sp = s0 + j * kZChunks;
+        if (sp < splits) v[j] = *reinterpret_cast<const f32x4*>(zpart + (size_t)sp * count + idx);
+      }
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        const int sp = s0 + j * kZChunks;
+        if (sp < splits) q = sp == c ? v[j] : q + v[j];
+      }
+    }
+  }
+  part[c][u] = q;
+  __syncthreads();
+  if (c == 0 && idx < count) {
+    f32x4 zs = part[0][u];
+    for (int k = 1; k < kZChunks && k < splits; ++k) zs += part[k][u];
+    *reinterpret_cast<f32x4*>(z + idx) = zs;
+  }
 }
 
 // The same sums one element per thread (counts or pointers that do not allow
@@ -625,9 +665,13 @@ __global__ void z_reduce1_kernel(const float* __restrict__ zpart, int splits, si
                                  float* __restrict__ z) {
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= count) return;
-  float s = zpart[idx];
-  for (int k = 1; k < splits; ++k) s += zpart[(size_t)k * count + idx];
-  z[idx] = s;
+  float zs = 0.0f;
+  for (int c = 0; c < kZChunks && c < splits; ++c) {
+    float q = zpart[(size_t)c * count + idx];
+    for (int sp = c + kZChunks; sp < splits; sp += kZChunks) q += zpart[(size_t)sp * count + idx];
+    zs = c == 0 ? q : zs + q;
+  }
+  z[idx] = zs;
 }
 
 }  // namespace
@@ -802,8 +846,11 @@ int launch_z_reduce(const float* zpart, int splits, int b, int rank, float* z, v
   // 16-byte accesses when every split's slice and z start 16-byte aligned
   // (the workspace is 256-byte aligned; each slice is count floats)
   const bool vec = count % 4 == 0 && ((uintptr_t)zpart & 15u) == 0 && ((uintptr_t)z & 15u) == 0;
-  if (vec)
+  if (vec && splits <= kZChunks)
     hipLaunchKernelGGL(z_reduce_kernel, dim3((unsigned)((count / 4 + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)stream, zpart, splits, count, z);
+  else if (vec)
+    hipLaunchKernelGGL(z_reduce_chunked_kernel, dim3((unsigned)((count / 4 + 15) / 16)), dim3(256), 0,
                        (hipStream_t)stream, zpart, splits, count, z);
   else
     hipLaunchKernelGGL(z_reduce1_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
