@@ -250,8 +250,9 @@ enum { SVDQ_GEMM_INT4 = 0, SVDQ_GEMM_W8A8 = 1, SVDQ_GEMM_FP4 = 2 };
 /* HOST (queries the current device's CU count; no launch): the schedule the
  * GEMM kernel of `setting` (SVDQ_GEMM_*) would use for an output of b x n with
  * m input channels ([Nunchaku]: one kernel per fused pair; the split of output
- * tiles over workgroups is this library's own).  Writes info[0] = 128 x 128
- * output tiles, info[1] = workgroups launched, info[2] = split workgroups
+ * tiles over workgroups is this library's own).  Writes info[0] = output tiles
+ * (128 x 128; 128 x 64 in the INT4 setting when the 128 x 128 tiles would not
+ * fill one round of workgroups), info[1] = workgroups launched, info[2] = split workgroups
  * (each computes one piece of a tile's channel groups, and a reduction kernel
  * then adds the pieces; 0 when every workgroup computes one whole tile),
  * info[3] = tiles split (info[2] / info[3] pieces each), info[4] = resident

@@ -40,7 +40,8 @@ def test_exports_every_symbol_declared_in_header():
 # workgroups per CU, so a round is 768 tiles.  After full rounds, a last round
 # of R tiles is split into k = min(768 // R, 8, G // 8) pieces per tile when
 # k >= 3; when all T tiles fit in one round, into k = min(768 // T, 16, G // 8)
-# pieces when k >= 2.  NVFP4 tiles are never split.
+# pieces when k >= 2.  NVFP4 tiles are never split.  INT4 tiles are 128 x 64
+# instead of 128 x 128 when the wide tiles would not fill one round.
 SCHEDULES = [
     # (b, n, m, setting, tiles, grid, split workgroups, split tiles, workgroups per CU)
     (4608, 9216, 3072, "int4", 2592, 2592, 0, 0, 3),      # last round 288 tiles: halves are not used
@@ -52,14 +53,14 @@ SCHEDULES = [
     (4608, 9216, 3072, "fp4", 2592, 2592, 0, 0, 3),
     (4608, 3072, 12288, "fp4", 864, 864, 0, 0, 3),        # NVFP4: never split
     (256, 21504, 3072, "fp4", 336, 336, 0, 0, 3),
-    (256, 21504, 3072, "int4", 336, 672, 672, 336, 3),    # one round: 768 // 336 = 2 pieces of 24 groups
-    (256, 3072, 15360, "int4", 48, 768, 768, 48, 3),      # one round: 16 pieces (the cap) of 15 groups
+    (256, 21504, 3072, "int4", 672, 672, 0, 0, 3),        # 336 wide tiles: 672 narrow ones, one per workgroup
+    (256, 3072, 15360, "int4", 96, 768, 768, 96, 3),      # 96 narrow tiles: 8 pieces of 30 groups
     (256, 3072, 15360, "w8a8", 48, 768, 768, 48, 3),
     (4992, 5120, 1536, "int4", 1560, 1608, 72, 24, 3),    # 24 tiles left: 32 pieces, capped at G // 8 = 3
     (4608, 5376, 3072, "int4", 1512, 1512, 0, 0, 3),      # last round 744 tiles: no split
     (4608, 3072, 1024, "int4", 864, 864, 0, 0, 3),        # G = 16: at most 2 pieces after full rounds
-    (256, 3072, 1024, "int4", 48, 96, 96, 48, 3),         # one round, G = 16: 2 pieces of 8 groups
-    (256, 256, 64, "int4", 4, 4, 0, 0, 3),                # one group
+    (256, 3072, 1024, "int4", 96, 192, 192, 96, 3),       # one round, G = 16: 2 pieces of 8 groups
+    (256, 256, 64, "int4", 8, 8, 0, 0, 3),                # one group (narrow tiles)
     (0, 256, 256, "int4", 0, 0, 0, 0, 3),
 ]
 
@@ -67,7 +68,7 @@ SCHEDULES = [
 @pytest.mark.parametrize("b,n,m,setting,tiles,grid,skw,skt,wpc", SCHEDULES)
 def test_gemm_schedule(b, n, m, setting, tiles, grid, skw, skt, wpc):
     _lib_or_skip()
-    if S.svdq_gemm_schedule(128, 128, 64)["grid"] != 1:
+    if S.svdq_gemm_schedule(128, 128, 64, "w8a8")["grid"] != 1:
         pytest.skip("unexpected device")
     got = S.svdq_gemm_schedule(b, n, m, setting)
     assert got == {"tiles": tiles, "grid": grid, "split_workgroups": skw, "split_tiles": skt,

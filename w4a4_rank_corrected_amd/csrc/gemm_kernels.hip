@@ -211,7 +211,7 @@ struct GemmCfg {
   static_assert(WG_PER_CU >= 1 && (WPE * 4) % (NT / 64) == 0, "whole workgroups per CU");
   static_assert(A_BYTES == 4 || A_BYTES == 8 || A_BYTES == 16, "activation staging piece");
   static_assert(B_BYTES == 4 || B_BYTES == 8 || B_BYTES == 16, "weight staging piece");
-  static_assert(NT == TM + TN && TM % 64 == 0, "scale staging: one scale per thread");
+  static_assert(NT >= TM + TN && TM % 64 == 0 && TN % 64 == 0, "scale staging: at most one scale per thread");
   static_assert(BI == 4 && BJ % 2 == 0, "scale reads: one 16-byte row-scale vector, whole fp16 column vectors");
 };
 
@@ -223,6 +223,10 @@ struct GemmCfg {
 // of the library is checked for zero scratch at build time and before its
 // first launch).
 using Cfg = GemmCfg<128, 128, 64, 64, 3, 1>;
+// INT4, narrow tiles for few rows (when the wide tiles would not fill one
+// round of slots): 128 x 64 tiles, 4 waves of 64 x 32, half the work per
+// workgroup and group, twice the workgroups; loads run two groups ahead.
+using CfgN = GemmCfg<128, 64, 64, 32, 3, 2>;
 // 8-bit codes: no per-group VALU work, so a group's compute is short: loads
 // run two groups ahead (140 registers).
 using Cfg8 = GemmCfg<128, 128, 64, 64, 3, 2>;
@@ -494,7 +498,9 @@ __device__ __forceinline__ void gemm_up_body(
           const int pw = TM + ((tid - TM - lw + 4 * BJ * ((lw & 15) >> 2) + 4 * (lw >> 4) + (lw & 3)) >> 1);
           const uint32_t va = __float_as_uint(f16_to_f32((uint16_t)sv) * 0.00390625f);
           const uint32_t vw = (lw & 1) ? (nb | (sv << 16)) : (sv | (nb << 16));
-          reinterpret_cast<uint32_t*>(&Ssc[buf][q * SSC])[act ? pa : pw] = act ? va : vw;
+          // waves past the TM + TN scale threads (narrow tiles) stage none
+          if (TM + TN == NT || wave_u < (TM + TN) / 64)
+            reinterpret_cast<uint32_t*>(&Ssc[buf][q * SSC])[act ? pa : pw] = act ? va : vw;
         }
       }
     };
@@ -748,11 +754,11 @@ __device__ __forceinline__ void gemm_up_body(
       // Slot layout, in 16-byte units: [wave][block k = bi BJ + bj][lane], so
       // each store of a wave writes 1 KB contiguous (the reduction kernel
       // maps units back to outputs the same way); the byte offset
-      // wave*16 KB + k KB + 16 lane is split into a per-lane base, a scalar
+      // wave*BI*BJ KB + k KB + 16 lane is split into a per-lane base, a scalar
       // 4 KB multiple and an instruction immediate below 4 KB.  Slots are
       // piece-major: piece q of split tile t in slot q*T + t.
-      static_assert(BI * BJ == 16 && NT == 256, "partial layout: 16 blocks of 1 KB per wave");
-      const uint32_t part_voff = (uint32_t)(wave * 16384 + lane * 16);
+      static_assert(BI * BJ % 4 == 0 && NT == 256, "partial layout: blocks of 1 KB, 4 per 4 KB");
+      const uint32_t part_voff = (uint32_t)(wave * BI * BJ * 1024 + lane * 16);
       auto partial_offset = [](int q) { return (uint32_t)((q & 3) * 1024); };
       auto partial_soffset = [](int q) { return (q >> 2) * 4096; };
       auto store_slot = [&](int slot, auto&& val) {
@@ -787,7 +793,7 @@ __device__ __forceinline__ void gemm_up_body(
       if (split) {
         const __amdgpu_buffer_rsrc_t rp =
             make_rsrc(sk.partials + ((size_t)sk.k * sk.T + t) * (TM * TN), TM * TN * 4);
-        const uint32_t part_voff = (uint32_t)(wave * 16384 + lane * 16);
+        const uint32_t part_voff = (uint32_t)(wave * BI * BJ * 1024 + lane * 16);
 #pragma unroll
         for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
@@ -847,13 +853,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
     const float* __restrict__ partials, int T, int k, int tiles_m, int tiles_n, int b, int n,
     const uint16_t* __restrict__ ascale, const uint16_t* __restrict__ wscale, int lowrank_slot,
     const uint16_t* __restrict__ bias, void* __restrict__ yout) {
-  static_assert(C::NT == 256 && C::BI * C::BJ == 16 && kMaxPiecesAll <= 16, "unit layout of the slots");
+  static_assert(C::NT == 256 && kMaxPiecesAll <= 16, "unit layout of the slots");
+  constexpr int WU = C::BI * C::BJ * 64;    // units per wave
   static_assert(FMT == kFmtInt4 || FMT == kFmtInt8, "INT4 and 8-bit tiles only");
   constexpr int UNITS = C::TM * C::TN / 4;  // 16-byte units per slot
   const int u = (int)blockIdx.x * 256 + (int)threadIdx.x;
   const int t = u / UNITS, w = u - t * UNITS;
   if (t >= T) return;
-  const int wave = w >> 10, blk = (w >> 6) & 15, lane = w & 63;
+  const int wave = w / WU, blk = (w / 64) % (C::BI * C::BJ), lane = w & 63;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int bi = blk / C::BJ, bj = blk % C::BJ;
   int ti, tj;
@@ -963,7 +970,6 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
     sk.lr = L.rank > 0 ? kLowRankPieceGroups : 0;
     sk.partials = reinterpret_cast<float*>(ws);
   }
-  using CF = std::conditional_t<FMT == kFmtInt8, Cfg8, Cfg>;
 #define SVDQ_GEMM_ARGS qx, ascale, z, L.qw, L.wscale, L.l2, L.bias, b, L.n, plan.G, L.rank, plan.tiles_m, \
                        plan.tiles_n, y, sk, txw
   int st_gemm;
@@ -976,6 +982,10 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
     // register budget of three workgroups per CU)
     if (plan.split) return (int)hipErrorInvalidValue;
     st_gemm = launch_checked(gemm_fp4_up_kernel<CfgF4, OUT_BF16, false>, plan.grid, CfgF4::NT, st, SVDQ_GEMM_ARGS);
+  } else if (plan.tile_n == CfgN::TN) {
+    st_gemm = plan.split
+                  ? launch_checked(gemm_w4a4_up_kernel<CfgN, OUT_BF16, true>, plan.grid, CfgN::NT, st, SVDQ_GEMM_ARGS)
+                  : launch_checked(gemm_w4a4_up_kernel<CfgN, OUT_BF16, false>, plan.grid, CfgN::NT, st, SVDQ_GEMM_ARGS);
   } else {
     st_gemm = plan.split
                   ? launch_checked(gemm_w4a4_up_kernel<Cfg, OUT_BF16, true>, plan.grid, Cfg::NT, st, SVDQ_GEMM_ARGS)
@@ -983,14 +993,20 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
   }
 #undef SVDQ_GEMM_ARGS
   if (st_gemm != 0 || !plan.split) return st_gemm;
-  if constexpr (FMT == kFmtFp4) {
-    return st_gemm;
-  } else {
-    constexpr int UNITS = CF::TM * CF::TN / 4;
-    const int lr_slot = FMT == kFmtInt8 && L.rank > 0 ? 1 : 0;
-    return launch_checked(splitk_reduce_kernel<CF, FMT, OUT_BF16>, (int)(((long long)sk.T * UNITS + 255) / 256),
+  const int lr_slot = FMT == kFmtInt8 && L.rank > 0 ? 1 : 0;
+  auto reduce = [&](auto cfg) {
+    using C = decltype(cfg);
+    constexpr int UNITS = C::TM * C::TN / 4;
+    return launch_checked(splitk_reduce_kernel<C, FMT, OUT_BF16>, (int)(((long long)sk.T * UNITS + 255) / 256),
                           256, st, (const float*)sk.partials, sk.T, sk.k, plan.tiles_m, plan.tiles_n, b, L.n,
                           ascale, L.wscale, lr_slot, L.bias, y);
+  };
+  if constexpr (FMT == kFmtFp4) {
+    return st_gemm;
+  } else if constexpr (FMT == kFmtInt8) {
+    return reduce(Cfg8{});
+  } else {
+    return plan.tile_n == CfgN::TN ? reduce(CfgN{}) : reduce(Cfg{});
   }
 }
 
@@ -998,7 +1014,9 @@ int launch_typed(const uint8_t* qx, const uint16_t* ascale, const float* z, cons
 
 // The launch plan (gemm_plan) is host logic in plan.cpp; the kernel builds
 // here must match the tiling and residencies it plans for.
-static_assert(Cfg::TM == kGemmTileM && Cfg::TN == kGemmTileN, "tile shape");
+static_assert(Cfg::TM == kGemmTileM && Cfg::TN == kGemmTileN && CfgN::TM == kGemmTileM &&
+                  CfgN::TN == kGemmTileNNarrow && CfgN::WG_PER_CU == Cfg::WG_PER_CU,
+              "tile shapes");
 static_assert(Cfg::TM == Cfg8::TM && Cfg::TN == Cfg8::TN && Cfg::TM == CfgF4::TM && Cfg::TN == CfgF4::TN,
               "one tiling for every setting");
 static_assert(Cfg::WG_PER_CU == kGemmWgPerCu[kFmtInt4] && Cfg8::WG_PER_CU == kGemmWgPerCu[kFmtInt8] &&

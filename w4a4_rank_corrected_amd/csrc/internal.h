@@ -133,6 +133,7 @@ struct GemmPlan {
   int pieces;           // pieces per split tile
   int split_grid;       // split workgroups, split_tiles * pieces (dispatched first)
   int wg_per_cu;        // resident workgroups per CU of the kernel planned for
+  int tile_n;           // output columns per tile: kGemmTileN, or kGemmTileNNarrow (INT4, few rows)
   size_t partial_bytes; // partial-sum area at the start of the workspace
   size_t ws_bytes;      // workspace bound for the shape (0 when m has too few groups to split)
 };
@@ -142,6 +143,8 @@ enum GemmFormat { kFmtInt4 = 0, kFmtInt8 = 1, kFmtFp4 = 2 };
 // Output tile of every GEMM build, and the resident workgroups per CU of each
 // format's kernel (the same with and without split tiles).
 constexpr int kGemmTileM = 128, kGemmTileN = 128;
+// INT4 tiles for few rows (the wide tiles would not fill one round of slots)
+constexpr int kGemmTileNNarrow = 64;
 constexpr int kGemmWgPerCu[3] = {3, 3, 3};
 // Split-K: pieces per split tile when full rounds of whole tiles run too
 // (kMinPieces .. kMaxPieces) and when every tile is split (2 ..

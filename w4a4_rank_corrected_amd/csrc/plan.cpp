@@ -32,9 +32,13 @@ GemmPlan gemm_plan(int b, int n, int m, int cus, int fmt) {
   GemmPlan p;
   p.G = m / 64;
   p.tiles_m = (b + kGemmTileM - 1) / kGemmTileM;
-  p.tiles_n = (n + kGemmTileN - 1) / kGemmTileN;
   p.wg_per_cu = kGemmWgPerCu[fmt];
-  const long long T = (long long)p.tiles_m * p.tiles_n, slots = (long long)p.wg_per_cu * ncu;
+  const long long slots = (long long)p.wg_per_cu * ncu;
+  // INT4 tiles narrow to 128 x 64 when the wide ones would not fill a round
+  const long long T128 = (long long)p.tiles_m * ((n + kGemmTileN - 1) / kGemmTileN);  // wide tiles
+  p.tile_n = fmt == kFmtInt4 && T128 < slots ? kGemmTileNNarrow : kGemmTileN;
+  p.tiles_n = (n + p.tile_n - 1) / p.tile_n;
+  const long long T = (long long)p.tiles_m * p.tiles_n;
   const long long full = T / slots, rest = T - full * slots;
   const long long cap = full == 0 ? kMaxPiecesAll : kMaxPieces, kmin = full == 0 ? 2 : kMinPieces;
   const long long k = rest > 0 ? std::min<long long>({slots / rest, cap, p.G / kMinPieceGroups}) : 0;
@@ -49,7 +53,9 @@ GemmPlan gemm_plan(int b, int n, int m, int cus, int fmt) {
   const int max_wg_per_cu = std::max({kGemmWgPerCu[kFmtInt4], kGemmWgPerCu[kFmtInt8], kGemmWgPerCu[kFmtFp4]});
   const long long round = (long long)max_wg_per_cu * kMaxCUs;
   const long long kcap = std::min<long long>(kMaxPiecesAll, p.G / kMinPieceGroups);
-  const long long max_slots = kcap >= 2 ? std::min(round, T * kcap) + std::min(T, round / 2) : 0;
+  // counted in wide tiles of 64 KB: a narrow plan's k * T narrow slots of 32 KB
+  // stay within it, on any device (k * T <= one round, T <= 2 * T128)
+  const long long max_slots = kcap >= 2 ? std::min(round, T128 * kcap) + std::min(T128, round / 2) : 0;
   p.partial_bytes = (size_t)max_slots * kGemmTileM * kGemmTileN * 4;
   p.ws_bytes = p.partial_bytes;
   return p;
