@@ -417,10 +417,10 @@ def test_splitk_deterministic_and_match_oracle(S, b, m, n):
 
 
 def test_splitk_workspace_garbage_and_alternating_shapes(S):
-    """Split-K partial slots and per-tile arrival counters live in the
-    caller's workspace: random initial bytes (any counter value a previous
-    launch or process could leave), two split shapes alternating on one
-    workspace, and repeats must all give the same bits and the oracle's Y."""
+    """Split-K partial slots live in the caller's workspace: random initial
+    bytes (whatever a previous launch or process could leave), two split
+    shapes alternating on one workspace, and repeats must all give the same
+    bits and the oracle's Y."""
     shapes = [(256, 4096, 256), (300, 2368, 520)]
     need = max(S.svdq_linear_workspace_size(b, m, n, 16) for b, m, n in shapes)
     ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda")
