@@ -171,19 +171,29 @@ __device__ __forceinline__ void quant_store(const float (&v)[16], int g, int b, 
     const _Float16 s16 = (_Float16)s32;    // round to nearest even
     const float sf = (float)s16;
     const float rc = sf > 0.0f ? 1.0f / sf : 0.0f;
-    uint32_t w0 = 0u, w1 = 0u;
+    // rb[e]: the bits of q + 1.5 * 2^23, whose low byte is the code in two's
+    // complement (the addition rounds to the nearest integer, ties to even)
+    uint32_t rb[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float pq = v[e] * rc;
       const float rem = __builtin_fmaf(-pq, sf, v[e]);
       const float q1 = __builtin_fmaf(rem, rc, pq);
       const float q = __builtin_amdgcn_fmed3f(q1, -7.0f, 7.0f);
-      const uint32_t nib = __float_as_uint(q + kMagic) & 0xFu;
-      if (e < 8)
-        w0 |= nib << (4 * e);
-      else
-        w1 |= nib << (4 * (e - 8));
+      rb[e] = __float_as_uint(q + kMagic);
     }
+    // Nibble e of a word (bits 4e..4e+3) is code e: byte permutes gather the
+    // even codes' and the odd codes' low bytes into two words, then one
+    // bitfield insert takes the low nibbles of the first and the shifted low
+    // nibbles of the second.
+    auto pack8 = [](const uint32_t* c8) {
+      const uint32_t e01 = __builtin_amdgcn_perm(c8[2], c8[0], 0x0c0c0400u);  // bytes: c0, c2, 0, 0
+      const uint32_t e23 = __builtin_amdgcn_perm(c8[6], c8[4], 0x04000c0cu);  // bytes: 0, 0, c4, c6
+      const uint32_t o01 = __builtin_amdgcn_perm(c8[3], c8[1], 0x0c0c0400u);
+      const uint32_t o23 = __builtin_amdgcn_perm(c8[7], c8[5], 0x04000c0cu);
+      return ((e01 | e23) & 0x0F0F0F0Fu) | (((o01 | o23) << 4) & 0xF0F0F0F0u);
+    };
+    const uint32_t w0 = pack8(rb), w1 = pack8(rb + 8);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qx + (size_t)g * b * 32, (uint32_t)b * 32u);
     __builtin_amdgcn_raw_buffer_store_b32(w0, rq, q_off, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b32(w1, rq, q_off + 16u, 0, 0);
@@ -210,45 +220,64 @@ __global__ __launch_bounds__(256) void act_quant_down_kernel(
   const int g_end = min(G, g_begin + gps);
   const int ng = g_end - g_begin;
 
-  // stage 1/lambda and the L1 slices of groups [cb, ce) in LDS: every thread
-  // issues all of its loads before writing any of them
-  auto stage = [&](int cb, int ce) {
+  // Staging of 1/lambda and the L1 slices of groups [cb, ce) in LDS: each
+  // part's loads all go out before its LDS writes.  A wave's loads complete
+  // in issue order, so the first chunk's staging loads are issued before the
+  // activation loads: the waves then wait only for the staging data before
+  // the barrier, and start on their first group while the rest of the
+  // activations are still arriving.
+  constexpr int SP = TB > 0 ? (chunk * TB * 16 * 8 + 255) / 256 : 1;  // L1 pieces per thread
+  auto inv_load = [&](int cb, int ce) {
+    static_assert(chunk * 16 <= 256, "one 1/lambda piece per thread");
+    const __amdgpu_buffer_rsrc_t ri = make_rsrc(inv + (size_t)cb * 64, (uint32_t)(ce - cb) * 256u);
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ri, (uint32_t)tid * 16u, 0, 0));
+  };
+  auto inv_store = [&](const u32x4& v) {
+    if (tid < chunk * 16) *reinterpret_cast<u32x4*>(lds + (tid >> 4) * GB + 16 * (tid & 15)) = v;
+  };
+  // L1 rows t < 16 TB (zero beyond rank), 8 pieces of 16 B per (group, t)
+  auto l1_load = [&](int cb, int ce, u32x4 (&v)[SP]) {
     const int n = ce - cb;
-    if constexpr (SMOOTH) {
-      static_assert(chunk * 16 <= 256, "one 1/lambda piece per thread");
-      const __amdgpu_buffer_rsrc_t ri = make_rsrc(inv + (size_t)cb * 64, (uint32_t)n * 256u);
-      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ri, (uint32_t)tid * 16u, 0, 0));
-      if (tid < chunk * 16) *reinterpret_cast<u32x4*>(lds + (tid >> 4) * GB + 16 * (tid & 15)) = v;
-    }
-    if constexpr (TB > 0) {
-      // L1 rows t < 16 TB (zero beyond rank), 8 pieces of 16 B per (group, t)
-      constexpr int P = (chunk * TB * 16 * 8 + 255) / 256;
-      const __amdgpu_buffer_rsrc_t rl =
-          make_rsrc(l1t + (size_t)cb * 64, (uint32_t)((rank - 1) * m + n * 64) * 2u);
-      u32x4 v[P];
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(l1t + (size_t)cb * 64, (uint32_t)((rank - 1) * m + n * 64) * 2u);
 #pragma unroll
-      for (int i = 0; i < P; ++i) {
-        const int k = tid + 256 * i;
-        const int q = k & 7, t = (k >> 3) % (TB * 16), j = (k >> 3) / (TB * 16);
-        const uint32_t off = (t < rank && j < n) ? (uint32_t)(t * m + j * 64 + 8 * q) * 2u : 0xFFFFFFF0u;
-        v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, off, 0, 0));
-      }
-#pragma unroll
-      for (int i = 0; i < P; ++i) {
-        const int k = tid + 256 * i;
-        const int q = k & 7, t = (k >> 3) % (TB * 16), j = (k >> 3) / (TB * 16);
-        if (k < chunk * TB * 16 * 8)
-          *reinterpret_cast<u32x4*>(lds + j * GB + 256 + (t * kL1Pitch + 8 * q) * 2) = v[i];
-      }
+    for (int i = 0; i < SP; ++i) {
+      const int k = tid + 256 * i;
+      const int q = k & 7, t = (k >> 3) % (TB * 16), j = (k >> 3) / (TB * 16);
+      const uint32_t off = (t < rank && j < n) ? (uint32_t)(t * m + j * 64 + 8 * q) * 2u : 0xFFFFFFF0u;
+      v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, off, 0, 0));
     }
   };
+  auto l1_store = [&](const u32x4 (&v)[SP]) {
+#pragma unroll
+    for (int i = 0; i < SP; ++i) {
+      const int k = tid + 256 * i;
+      const int q = k & 7, t = (k >> 3) % (TB * 16), j = (k >> 3) / (TB * 16);
+      if (k < chunk * TB * 16 * 8) *reinterpret_cast<u32x4*>(lds + j * GB + 256 + (t * kL1Pitch + 8 * q) * 2) = v[i];
+    }
+  };
+  auto stage = [&](int cb, int ce) {
+    if constexpr (SMOOTH) inv_store(inv_load(cb, ce));
+    if constexpr (TB > 0) {
+      u32x4 v[SP];
+      l1_load(cb, ce, v);
+      l1_store(v);
+    }
+  };
+
+  // Activations D groups ahead in a register ring (below).  Builds with a
+  // one-group ring, for the largest ranks, keep the activation load first and
+  // stage every chunk behind a leading barrier: peeling the first chunk costs
+  // them registers.  Every wave runs the same barrier sequence: the first chunk
+  // (kStageFirst) is staged without a leading barrier, the others with one.
+  constexpr int D = act_depth(TB);
+  constexpr bool kStageFirst = D > 1;
 
   // this wave's strip; a wave past the end only helps stage and takes part in
   // the barriers
   const int row0 = blockIdx.x * 64 + wave * 16;
   if (row0 >= b) {
     for (int cb = g_begin; cb < g_end; cb += chunk) {
-      __syncthreads();
+      if (!kStageFirst || cb != g_begin) __syncthreads();
       stage(cb, min(cb + chunk, g_end));
       __syncthreads();
     }
@@ -325,15 +354,28 @@ __global__ __launch_bounds__(256) void act_quant_down_kernel(
   // x D groups ahead in a register ring: slot u holds the groups g with
   // (g - g_begin) % D == u.  chunk is a multiple of D, so every chunk starts
   // at slot 0 and only the split's last chunk ends early.
-  constexpr int D = act_depth(TB);
   u32x4 xa[D], xb[D];
+  if constexpr (kStageFirst) {
+    const int ce = min(g_begin + chunk, g_end);
+    u32x4 iv = {0u, 0u, 0u, 0u}, lv[SP];
+    if constexpr (SMOOTH) iv = inv_load(g_begin, ce);
+    if constexpr (TB > 0) l1_load(g_begin, ce, lv);
 #pragma unroll
-  for (int u = 0; u < D; ++u) load_x(g_begin + u, xa[u], xb[u]);
+    for (int u = 0; u < D; ++u) load_x(g_begin + u, xa[u], xb[u]);
+    if constexpr (SMOOTH) inv_store(iv);
+    if constexpr (TB > 0) l1_store(lv);
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int u = 0; u < D; ++u) load_x(g_begin + u, xa[u], xb[u]);
+  }
   for (int cb = g_begin; cb < g_end; cb += chunk) {
     const int ce = min(cb + chunk, g_end);
-    __syncthreads();  // every wave is done with the previous chunk
-    stage(cb, ce);
-    __syncthreads();
+    if (!kStageFirst || cb != g_begin) {
+      __syncthreads();  // every wave is done with the previous chunk
+      stage(cb, ce);
+      __syncthreads();
+    }
     int g = cb;
     for (; g + D <= ce; g += D) {
 #pragma unroll
