@@ -32,11 +32,14 @@ void clear_error() { g_err[0] = 0; }
 // load latency (measured slower than the split kernel and its reduction on
 // the FLUX shapes, m >= 3072).  Otherwise workgroups of 64 rows and enough
 // splits of the channel groups to put about 3072 waves on the chip, with at
-// least 3 groups per split (the kernel stages 1/lambda and L1 in LDS
-// act_chunk groups at a time); the splits' partial Z are added in split order
-// by a second kernel.  Depends only on the shape, so every setting's
+// least 3 and at most 8 groups per split (the kernel stages 1/lambda and L1 in
+// LDS act_chunk groups at a time; splits of more groups restage behind their
+// own activation loads, measured 6 % slower on FLUX fc2 and the single-block
+// output projection); the splits' partial Z are added in split order by a
+// second kernel.  Depends only on the shape, so every setting's
 // act-quant kernel, the standalone kernels and the fused layer sum Z in the
 // same order.
+constexpr int kActMaxSplitGroups = 8;
 ActPlan act_plan(int b, int m, int rank) {
   ActPlan p;
   const int G = m / SVDQ_GROUP;
@@ -51,7 +54,8 @@ ActPlan act_plan(int b, int m, int rank) {
   p.strips = (b + 63) / 64;
   int gps = G;
   if (p.strips > 0) {
-    const int splits = std::max(1, (3072 + 4 * p.strips - 1) / (4 * p.strips));
+    const int splits = std::max({1, (3072 + 4 * p.strips - 1) / (4 * p.strips),
+                                 (G + kActMaxSplitGroups - 1) / kActMaxSplitGroups});
     gps = std::max((G + splits - 1) / splits, std::min(3, G));
   }
   p.groups_per_split = gps;

@@ -83,8 +83,11 @@ constexpr int act_blocks(int rank) {
 }
 constexpr int act_lds_group_bytes(int blocks) { return 256 + blocks * 16 * kActL1Pitch * 2; }
 // Groups of activations each wave keeps in flight (a register ring), by the
-// number of Z blocks: deeper for the light kernels.
-constexpr int act_depth(int blocks) { return blocks <= 4 ? 4 : (blocks == 8 ? 2 : 1); }
+// number of Z blocks: deeper for the light kernels, except two for ranks
+// 17..32 (measured faster than four on the FLUX layers: a workgroup's first
+// burst of activation loads delays the staging loads of the workgroups
+// dispatched after it).
+constexpr int act_depth(int blocks) { return blocks == 2 ? 2 : (blocks <= 4 ? 4 : (blocks == 8 ? 2 : 1)); }
 // Groups staged in LDS at a time: the most (a multiple of the depth, at most
 // 8) that fit in about 40 KB.
 constexpr int act_chunk_fit(int blocks) {
