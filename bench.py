@@ -12,7 +12,10 @@ done before timing and is not part of a step.
 Timed region ("cold"): the steps rotate over several independently seeded
 input + weight sets whose footprint exceeds the 256 MB last-level cache, so a
 step does not find its layer's weights or activations cached by the previous
-step.  Also reported: the same steps on one set ("warm"), the low-rank
+step.  Between the warm-up steps and the timed region the layer's own steps
+run untimed for about a quarter second, with no idle gap (``settle_steps``),
+so that the timed steps see the GPU's sustained clock rather than its ramp
+from idle; ``--no-settle`` times from idle instead.  Also reported: the same steps on one set ("warm"), the low-rank
 overhead t(rank r) / t(rank 0, same codes and scales) - 1 from rank-r and
 rank-0 steps interleaved on one set (median HIP-event step times), the
 one-call ``svdq_linear`` entry point, and the GEMM's fractions of the i8 MFMA
@@ -47,6 +50,8 @@ Extra modes (used with rocprofv3 runs):
 from __future__ import annotations
 
 import argparse
+import ctypes
+import functools
 import glob
 import csv
 import hashlib
@@ -74,6 +79,7 @@ GEMM_SOURCES = ["w4a4_rank_corrected_amd/csrc/gemm_kernels.hip",
                 "w4a4_rank_corrected_amd/csrc/internal.h",
                 "w4a4_rank_corrected_amd/csrc/plan.cpp"]
 COPY_BYTES = 256 << 20     # plain copy used to calibrate the byte counters
+SETTLE_OPS = 2.5e14        # work of the clock-settling steps: about 0.25 s at 1 POP/s
 COLD_BYTES = 512 << 20     # rotated footprint of the cold measurement
 
 
@@ -102,6 +108,18 @@ def algorithmic_bytes(b, m, n, r):
     return k1, k2
 
 
+def settle_steps(b, m, n):
+    """Untimed steps of the layer run right before its timed region, with no
+    idle gap, so that the region measures the sustained engine clock.  From
+    idle an MI355X raises its clock over about 40 ms of continuous work (the
+    FLUX QKV GEMM falls from about 255 to 216.5 us per launch over its first
+    150 launches and then holds that), and it drops back after about a second
+    of idling, e.g. while the host prepares a layer.  The count is a function of
+    the shape only (about 0.25 s of work at 1 POP/s, at least 50 steps and at
+    most 5000), so that a kernel trace of the run can find the timed region."""
+    return int(min(5000, max(50, math.ceil(SETTLE_OPS / (2.0 * b * m * n)))))
+
+
 def set_plan(cfg, rank, out):
     """(bytes of one input+weight set, number of sets rotated by the cold timing)."""
     b, m, n = cfg.rows or cfg.b, cfg.m, cfg.n
@@ -128,7 +146,9 @@ def trace_summary(prof_dir, cfg, args, rank):
     f4 = args.fp4 is not None
     cmp_mode = w8 or f4
     _, n_sets = set_plan(cfg, rank, args.out)
-    skip = max(50, args.warmup) if cmp_mode else max(args.warmup, n_sets)
+    b_rows = cfg.rows or cfg.b
+    n_settle = 0 if cmp_mode or args.no_settle else settle_steps(b_rows, cfg.m, cfg.n)
+    skip = max(50, args.warmup) if cmp_mode else max(args.warmup, n_sets) + n_settle
     short = lambda nm: re.sub(r"\(.*", "", nm.replace("svdq::(anonymous namespace)::", "")
                               .replace("void ", "").replace("svdq::", ""))
     rows = list(c.execute("select name, start, end, grid_x, grid_y, workgroup_x, workgroup_y, vgpr_count, "
@@ -147,7 +167,8 @@ def trace_summary(prof_dir, cfg, args, rank):
                   f"all at rank {rank} on one input and weight set (warm).")
         title = f"# Kernel trace, {other} setting against INT4: {cfg.name}"
     else:
-        region = (f"Timed region: {args.steps} steps after {skip} untimed ones, rotating over {n_sets} "
+        region = (f"Timed region: {args.steps} steps after {skip} untimed ones ({max(args.warmup, n_sets)} "
+                  f"warm-up and {n_settle} clock-settling steps), rotating over {n_sets} "
                   f"input+weight sets; the script then times warm steps, rank-r and rank-0 steps interleaved "
                   f"and the one-call entry point, which the all-dispatch columns include.")
         title = f"# Kernel trace: {cfg.name}"
@@ -425,10 +446,14 @@ def fusion_ab(cfg, ranks, args):
 
     def time_pair(ws_f, ws_u):
         """Fused and unfused calls alternate step by step (same clocks and
-        cache state for both), after a warm-up long enough to raise clocks."""
-        for _ in range(max(50, args.warmup)):
+        cache state for both), after at least max(50, warmup) pairs and at
+        least 0.25 s of them (the host preparation before each rank idles the
+        GPU, and its clock needs about 40 ms of work to settle again)."""
+        t0, k = time.perf_counter(), 0
+        while k < max(50, args.warmup) or (not args.no_settle and time.perf_counter() - t0 < 0.25):
             S.svdq_linear(x, layer, out_dtype, y=y, workspace=ws_f, stream=stream)
             S.svdq_linear_unfused(x, layer, out_dtype, y=y, workspace=ws_u, stream=stream)
+            k += 1
         ev = []
         for _ in range(args.steps):
             e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -638,6 +663,8 @@ def main():
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="BLAS threads for the oracle timing (0 = all the process may use)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-settle", action="store_true",
+                    help="time right after the warm-up steps, without the clock-settling steps (from idle)")
     ap.add_argument("--extra-configs", default=EXTRA_CONFIGS,
                     help="further workloads timed by the same method in the same run (comma-separated; "
                          "'' for none)")
@@ -721,7 +748,8 @@ def main():
 
 def measure_layer(cfg, args, distinct_sets, steps, warmup, copy_check=False):
     """Time one layer configuration through the C ABI (one step = the act
-    kernel + its Z reduction, then the GEMM kernel).
+    kernel + its Z reduction, then the GEMM kernel), after the warm-up and the
+    clock-settling steps.
 
     Cold: the steps rotate over enough input + weight sets to exceed the
     last-level cache.  With distinct_sets every set is drawn and prepared from
@@ -783,68 +811,102 @@ def measure_layer(cfg, args, distinct_sets, steps, warmup, copy_check=False):
     gws = torch.empty(max(S.svdq_gemm_workspace_size(b, n, m), 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    # A step's first call on a (set, layer) pair goes through the binding,
+    # which checks every tensor; later calls reuse the C-ABI arguments it was
+    # given (the same tensors), so that the host's per-call checks do not pace
+    # the short layers' steps.
+    from w4a4_rank_corrected_amd import _binding as B
+    marshalled = {}
+
+    def marshal(st, layer):
+        rr = layer.rank
+        lib, P, sp = B.lib(), B._ptr, B._stream(stream)
+        zp = P(z) if rr else None
+        k1 = functools.partial(lib.svdq_quantize_act_lowrank_down, P(st["x"]), b, m, rr, 64, P(layer.smooth_inv),
+                               P(layer.l1), P(qx), P(asc), zp, P(ws), ws.numel(), sp)
+        k2 = functools.partial(lib.svdq_gemm_w4a4_lowrank_up, P(qx), P(asc), zp, ctypes.byref(layer.struct), b,
+                               P(st["y"]), B._out_code(out_dtype), P(gws), gws.numel(), sp)
+        return k1, k2, layer
+
     def step(st, layer=None, ev=None):
         layer = layer or st["layer"]
         rr = layer.rank
+        calls = marshalled.get((id(st), id(layer)))
         if ev is not None:
             ev[0].record(stream)
-        S.svdq_quantize_act_lowrank_down(st["x"], layer.smooth_inv, layer.l1, rr, qx=qx, ascale=asc,
-                                         z=z if rr else None, workspace=ws, stream=stream)
+        if calls is None:
+            S.svdq_quantize_act_lowrank_down(st["x"], layer.smooth_inv, layer.l1, rr, qx=qx, ascale=asc,
+                                             z=z if rr else None, workspace=ws, stream=stream)
+        else:
+            B._check(calls[0]())
         if ev is not None:
             ev[1].record(stream)
-        S.svdq_gemm_w4a4_lowrank_up(qx, asc, z if rr else None, layer, b, out_dtype, y=st["y"],
-                                    workspace=gws, stream=stream)
+        if calls is None:
+            S.svdq_gemm_w4a4_lowrank_up(qx, asc, z if rr else None, layer, b, out_dtype, y=st["y"],
+                                        workspace=gws, stream=stream)
+            marshalled[(id(st), id(layer))] = marshal(st, layer)
+        else:
+            B._check(calls[1]())
         if ev is not None:
             ev[2].record(stream)
 
-    def timed(pick, nsteps, layer_of=None):
-        """Steps bracketed by synchronize on both sides; per-kernel HIP events."""
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nsteps)]
+    l0 = sets[0]["layer"]
+    # the same codes and scales without the low-rank branch
+    layer0 = S.DeviceLayer.from_tensors(m, n, 0, l0.qw, l0.wscale, None, None, l0.smooth_inv, l0.bias)
+    ws_lin = torch.empty(max(S.svdq_linear_workspace_size(b, m, n, r), 1), dtype=torch.uint8, device=dev)
+    n_settle = 0 if args.no_settle else settle_steps(b, m, n)
+    new_events = lambda k: [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(k)]
+    # events only around the first and the last settling steps: thousands of
+    # live timing events slow every later event record on the host
+    n_probe = min(20, n_settle // 2)
+    settle_evs, cold_evs, warm_evs = new_events(2 * n_probe), new_events(steps), new_events(steps)
+    pair = [new_events(2) for _ in range(steps)]
+
+    def timed(pick, evs, layer=None):
+        """Steps bracketed by synchronize on both sides (wall ms per step); the
+        per-kernel HIP events are read after every phase has run, so that the
+        GPU does not idle (and lower its clock) between phases."""
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for k in range(nsteps):
-            st = pick(k)
-            step(st, layer_of(st) if layer_of else None, evs[k])
+        for k, ev in enumerate(evs):
+            step(pick(k), layer, ev)
+        t_issue = time.perf_counter()
         torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) * 1e3 / nsteps
+        k = max(1, len(evs))
+        return (time.perf_counter() - t0) * 1e3 / k, (t_issue - t0) * 1e3 / k
+
+    def kernel_stats(evs, walls):
         k1 = [e[0].elapsed_time(e[1]) for e in evs]
         k2 = [e[1].elapsed_time(e[2]) for e in evs]
-        return {"wall": wall, "k1_mean": float(np.mean(k1)), "k2_mean": float(np.mean(k2)),
+        return {"wall": walls[0], "host_issue": walls[1],
+                "k1_mean": float(np.mean(k1)), "k2_mean": float(np.mean(k2)),
                 "k1_median": float(np.median(k1)), "k2_median": float(np.median(k2)),
                 "step_median": float(np.median([e[0].elapsed_time(e[2]) for e in evs]))}
 
-    # warm-up over every set, then the timed (cold, rotating) region
+    # warm-up over every set, the clock-settling steps, then the timed (cold,
+    # rotating) region
+    rotate = lambda k: sets[k % n_sets]
     for k in range(max(warmup, n_sets)):
-        step(sets[k % n_sets])
+        step(rotate(k))
     torch.cuda.synchronize()
-    log(f"bench: timing {steps} steps rotating over {n_sets} sets")
-    cold = timed(lambda k: sets[k % n_sets], steps)
-
-    log("bench: warm steps, rank-0 steps interleaved with rank-r steps, svdq_linear")
-    warm = timed(lambda k: sets[0], steps)
-    # the same codes and scales without the low-rank branch, interleaved step
-    # by step with the rank-r layer (same clocks and cache state for both)
-    l0 = sets[0]["layer"]
-    layer0 = S.DeviceLayer.from_tensors(m, n, 0, l0.qw, l0.wscale, None, None, l0.smooth_inv, l0.bias)
+    log(f"bench: {n_settle} clock-settling steps, then {steps} timed steps rotating over {n_sets} sets, warm "
+        f"steps, rank-r and rank-0 steps interleaved, svdq_linear")
+    for k in range(n_settle):
+        probe = k - (n_settle - 2 * n_probe) if k >= n_probe else k
+        step(rotate(k), None, settle_evs[probe] if 0 <= probe < 2 * n_probe and (k < n_probe or
+                                                                                   k >= n_settle - n_probe) else None)
+    cold_wall = timed(rotate, cold_evs)
+    warm_wall = timed(lambda k: sets[0], warm_evs)
+    # rank-r and rank-0 steps interleaved step by step on one set (same clocks
+    # and cache state for both)
     for _ in range(3):
         step(sets[0], layer0)
         step(sets[0])
-    pair = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
     for k in range(steps):
         step(sets[0], None, pair[k][0])
         step(sets[0], layer0, pair[k][1])
-    torch.cuda.synchronize()
-    med = lambda f: float(np.median([f(e) for e in pair]))
-    ov = {"ms_rank_r": med(lambda e: e[0][0].elapsed_time(e[0][2])),
-          "ms_rank_0": med(lambda e: e[1][0].elapsed_time(e[1][2])),
-          "k1_ms_rank_r": med(lambda e: e[0][0].elapsed_time(e[0][1])),
-          "k2_ms_rank_r": med(lambda e: e[0][1].elapsed_time(e[0][2])),
-          "k1_ms_rank_0": med(lambda e: e[1][0].elapsed_time(e[1][1])),
-          "k2_ms_rank_0": med(lambda e: e[1][1].elapsed_time(e[1][2]))}
-
     # the one-call entry point (K1 + K2 inside the library), warm
-    ws_lin = torch.empty(max(S.svdq_linear_workspace_size(b, m, n, r), 1), dtype=torch.uint8, device=dev)
     for _ in range(3):
         S.svdq_linear(sets[0]["x"], l0, out_dtype, y=sets[0]["y"], workspace=ws_lin, stream=stream)
     torch.cuda.synchronize()
@@ -853,6 +915,27 @@ def measure_layer(cfg, args, distinct_sets, steps, warmup, copy_check=False):
         S.svdq_linear(sets[0]["x"], l0, out_dtype, y=sets[0]["y"], workspace=ws_lin, stream=stream)
     torch.cuda.synchronize()
     linear_ms = (time.perf_counter() - t1) * 1e3 / steps
+
+    cold = kernel_stats(cold_evs, cold_wall)
+    warm = kernel_stats(warm_evs, warm_wall)
+    med = lambda f: float(np.median([f(e) for e in pair]))
+    ov = {"ms_rank_r": med(lambda e: e[0][0].elapsed_time(e[0][2])),
+          "ms_rank_0": med(lambda e: e[1][0].elapsed_time(e[1][2])),
+          "k1_ms_rank_r": med(lambda e: e[0][0].elapsed_time(e[0][1])),
+          "k2_ms_rank_r": med(lambda e: e[0][1].elapsed_time(e[0][2])),
+          "k1_ms_rank_0": med(lambda e: e[1][0].elapsed_time(e[1][1])),
+          "k2_ms_rank_0": med(lambda e: e[1][1].elapsed_time(e[1][2]))}
+    settle = None
+    if n_probe:
+        k2s = [e[1].elapsed_time(e[2]) for e in settle_evs]
+        settle = {"steps": n_settle,
+                  "ms": round(settle_evs[0][0].elapsed_time(settle_evs[-1][2]), 2),
+                  f"gemm_ms_first_{n_probe}": round(float(np.median(k2s[:n_probe])), 5),
+                  f"gemm_ms_last_{n_probe}": round(float(np.median(k2s[n_probe:])), 5)}
+        log(f"bench: settling took {settle['ms']:.0f} ms; GEMM median {np.median(k2s[:n_probe]) * 1e3:.1f} us "
+            f"over its first {n_probe} steps, {np.median(k2s[n_probe:]) * 1e3:.1f} us over its last; timed "
+            f"{cold['k2_mean'] * 1e3:.1f} us")
+    del settle_evs, cold_evs, warm_evs, pair, marshalled
 
     if copy_check:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
@@ -863,6 +946,7 @@ def measure_layer(cfg, args, distinct_sets, steps, warmup, copy_check=False):
         log(f"bench: copy check of {COPY_BYTES} bytes done")
     return {"cfg": cfg, "b": b, "m": m, "n": n, "r": r, "n_sets": n_sets, "per_set": per_set,
             "cold": cold, "warm": warm, "overhead": ov, "linear_ms": linear_ms, "prep_s": sets[0]["prep_s"],
+            "settle": settle,
             "schedule": S.svdq_gemm_schedule(b, n, m), "inp": sets[0].get("inp"),
             "distinct_sets": distinct_sets, "steps": steps}
 
@@ -892,13 +976,13 @@ def summarize_extra(res):
     f = kernel_fractions(b, m, n, r, c["k1_mean"], c["k2_mean"])
     return {"b": b, "m": m, "n": n, "rank": r,
             "value_TOPs": round(2.0 * b * m * n / (c["wall"] * 1e-3) / 1e12, 2),
-            "ms_per_step": round(c["wall"], 5),
+            "ms_per_step": round(c["wall"], 5), "host_issue_ms_per_step": round(c["host_issue"], 5),
             "act_quant_down_ms": round(c["k1_mean"], 5), "gemm_w4a4_up_ms": round(c["k2_mean"], 5),
             "gemm_frac_i8_peak": round(f["gemm_frac_i8_peak"], 4), "gemm_hbm_frac": round(f["gemm_hbm_frac"], 4),
             "gemm_epilogue_fma_frac": round(f["gemm_epilogue_fma_frac"], 4),
             "act_hbm_frac": round(f["act_hbm_frac"], 4),
             "lowrank_overhead": round(ov["ms_rank_r"] / ov["ms_rank_0"] - 1.0, 4),
-            "schedule": res["schedule"],
+            "schedule": res["schedule"], "clock_settle": res["settle"],
             "timing": f"cold: {res['steps']} steps rotating over {res['n_sets']} copies of one prepared set"}
 
 
@@ -931,6 +1015,7 @@ def headline(res, cfg, args):
                      "unit": "TOP/s", "frac": round(f["gemm_frac_i8_peak"], 4),
                      "traffic": None if traffic is None else round(traffic["traffic_bytes"])},
         "kernels": {"act_quant_down_ms": round(c["k1_mean"], 5), "gemm_w4a4_up_ms": round(c["k2_mean"], 5),
+                    "host_issue_ms_per_step": round(c["host_issue"], 5),
                     "act_quant_down_median_ms": round(c["k1_median"], 5),
                     "gemm_w4a4_up_median_ms": round(c["k2_median"], 5),
                     "act_quant_down_GBs": round(f["act_algorithmic_bytes"] / (c["k1_mean"] * 1e-3) / 1e9, 1),
@@ -952,6 +1037,7 @@ def headline(res, cfg, args):
                              "k1_ms_rank_0": round(ov["k1_ms_rank_0"], 5), "k2_ms_rank_0": round(ov["k2_ms_rank_0"], 5),
                              "method": "rank-r and rank-0 steps interleaved on one set (warm), "
                                        "median of HIP-event step times"},
+        "clock_settle": res["settle"],
         "prep_s": round(res["prep_s"], 2),
     }
 

@@ -35,6 +35,19 @@ def test_cold_plan_rotates_more_than_the_last_level_cache():
         assert n_sets >= 3 and per_set * n_sets >= bench.COLD_BYTES
 
 
+def test_settle_steps_depend_on_the_shape_only():
+    # about 0.25 s of work at 1 POP/s, clamped to [50, 5000]
+    assert bench.settle_steps(4608, 3072, 9216) == 959
+    assert bench.settle_steps(64, 256, 256) == 5000
+    assert bench.settle_steps(10**6, 10**4, 10**4) == 50
+    for name in ("flux_qkv", "flux_fc2", "pixart_fc1", "flux_single_fc_b256", "flux_single_out_b256"):
+        cfg = workloads.CONFIGS[name]
+        k = bench.settle_steps(cfg.rows or cfg.b, cfg.m, cfg.n)
+        assert k == bench.settle_steps(cfg.rows or cfg.b, cfg.m, cfg.n)
+        assert 50 <= k <= 5000
+        assert k == 5000 or k * 2.0 * (cfg.rows or cfg.b) * cfg.m * cfg.n >= bench.SETTLE_OPS
+
+
 def test_algorithmic_bytes_flux_qkv():
     b, m, n, r = 4608, 3072, 9216, 32
     k1, k2 = bench.algorithmic_bytes(b, m, n, r)
