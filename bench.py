@@ -828,60 +828,77 @@ def measure_layer(cfg, args, distinct_sets, steps, warmup, copy_check=False):
                                P(st["y"]), B._out_code(out_dtype), P(gws), gws.numel(), sp)
         return k1, k2, layer
 
-    def step(st, layer=None, ev=None):
+    def step(st, layer=None, marks=None):
+        """One step; marks = (event after the act kernel, event after the
+        GEMM), or None.  Two events per step: each record costs the stream
+        about 3 us, so the act kernel's time is read from the previous step's
+        last event (or the phase's start event) to this step's first."""
         layer = layer or st["layer"]
         rr = layer.rank
         calls = marshalled.get((id(st), id(layer)))
-        if ev is not None:
-            ev[0].record(stream)
         if calls is None:
             S.svdq_quantize_act_lowrank_down(st["x"], layer.smooth_inv, layer.l1, rr, qx=qx, ascale=asc,
                                              z=z if rr else None, workspace=ws, stream=stream)
         else:
             B._check(calls[0]())
-        if ev is not None:
-            ev[1].record(stream)
+        if marks is not None:
+            marks[0].record(stream)
         if calls is None:
             S.svdq_gemm_w4a4_lowrank_up(qx, asc, z if rr else None, layer, b, out_dtype, y=st["y"],
                                         workspace=gws, stream=stream)
             marshalled[(id(st), id(layer))] = marshal(st, layer)
         else:
             B._check(calls[1]())
-        if ev is not None:
-            ev[2].record(stream)
+        if marks is not None:
+            marks[1].record(stream)
 
     l0 = sets[0]["layer"]
     # the same codes and scales without the low-rank branch
     layer0 = S.DeviceLayer.from_tensors(m, n, 0, l0.qw, l0.wscale, None, None, l0.smooth_inv, l0.bias)
     ws_lin = torch.empty(max(S.svdq_linear_workspace_size(b, m, n, r), 1), dtype=torch.uint8, device=dev)
     n_settle = 0 if args.no_settle else settle_steps(b, m, n)
-    new_events = lambda k: [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(k)]
+    event = lambda: torch.cuda.Event(enable_timing=True)
+    # a phase's events: one at its start, then two per step
+    new_chain = lambda k: {"start": event(), "marks": [(event(), event()) for _ in range(k)]}
     # events only around the first and the last settling steps: thousands of
     # live timing events slow every later event record on the host
     n_probe = min(20, n_settle // 2)
-    settle_evs, cold_evs, warm_evs = new_events(2 * n_probe), new_events(steps), new_events(steps)
-    pair = [new_events(2) for _ in range(steps)]
+    settle_a, settle_b = new_chain(n_probe), new_chain(n_probe)
+    cold_ev, warm_ev, pair_ev = new_chain(steps), new_chain(steps), new_chain(2 * steps)
 
-    def timed(pick, evs, layer=None):
-        """Steps bracketed by synchronize on both sides (wall ms per step); the
-        per-kernel HIP events are read after every phase has run, so that the
-        GPU does not idle (and lower its clock) between phases."""
+    def run(pick, chain, layer_of=None):
+        """The chain's steps, issued without synchronising."""
+        chain["start"].record(stream)
+        for k, mk in enumerate(chain["marks"]):
+            st = pick(k)
+            step(st, layer_of(k) if layer_of else None, mk)
+
+    def timed(pick, chain):
+        """Steps bracketed by synchronize on both sides (wall ms per step, and
+        the host's issue time per step); the events are read after every
+        phase has run, so that the GPU does not idle (and lower its clock)
+        between phases."""
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for k, ev in enumerate(evs):
-            step(pick(k), layer, ev)
+        run(pick, chain)
         t_issue = time.perf_counter()
         torch.cuda.synchronize()
-        k = max(1, len(evs))
+        k = max(1, len(chain["marks"]))
         return (time.perf_counter() - t0) * 1e3 / k, (t_issue - t0) * 1e3 / k
 
-    def kernel_stats(evs, walls):
-        k1 = [e[0].elapsed_time(e[1]) for e in evs]
-        k2 = [e[1].elapsed_time(e[2]) for e in evs]
+    def times(chain):
+        """Per step: (act kernel + Z reduction, GEMM, whole step) in ms."""
+        ends = [chain["start"]] + [mk[1] for mk in chain["marks"]]
+        return [(ends[k].elapsed_time(mid), mid.elapsed_time(end), ends[k].elapsed_time(end))
+                for k, (mid, end) in enumerate(chain["marks"])]
+
+    def kernel_stats(chain, walls):
+        t = times(chain)
+        k1, k2 = [v[0] for v in t], [v[1] for v in t]
         return {"wall": walls[0], "host_issue": walls[1],
                 "k1_mean": float(np.mean(k1)), "k2_mean": float(np.mean(k2)),
                 "k1_median": float(np.median(k1)), "k2_median": float(np.median(k2)),
-                "step_median": float(np.median([e[0].elapsed_time(e[2]) for e in evs]))}
+                "step_median": float(np.median([v[2] for v in t]))}
 
     # warm-up over every set, the clock-settling steps, then the timed (cold,
     # rotating) region
@@ -891,21 +908,20 @@ def measure_layer(cfg, args, distinct_sets, steps, warmup, copy_check=False):
     torch.cuda.synchronize()
     log(f"bench: {n_settle} clock-settling steps, then {steps} timed steps rotating over {n_sets} sets, warm "
         f"steps, rank-r and rank-0 steps interleaved, svdq_linear")
-    for k in range(n_settle):
-        probe = k - (n_settle - 2 * n_probe) if k >= n_probe else k
-        step(rotate(k), None, settle_evs[probe] if 0 <= probe < 2 * n_probe and (k < n_probe or
-                                                                                   k >= n_settle - n_probe) else None)
-    cold_wall = timed(rotate, cold_evs)
-    warm_wall = timed(lambda k: sets[0], warm_evs)
-    # rank-r and rank-0 steps interleaved step by step on one set (same clocks
-    # and cache state for both)
+    if n_probe:
+        run(rotate, settle_a)
+    for k in range(n_probe, n_settle - n_probe):
+        step(rotate(k))
+    if n_probe:
+        run(lambda k: rotate(n_settle - n_probe + k), settle_b)
+    cold_wall = timed(rotate, cold_ev)
+    warm_wall = timed(lambda k: sets[0], warm_ev)
+    # rank-r and rank-0 steps alternate on one set (same clocks and cache state
+    # for both)
     for _ in range(3):
         step(sets[0], layer0)
         step(sets[0])
-    torch.cuda.synchronize()
-    for k in range(steps):
-        step(sets[0], None, pair[k][0])
-        step(sets[0], layer0, pair[k][1])
+    run(lambda k: sets[0], pair_ev, lambda k: layer0 if k % 2 else None)
     # the one-call entry point (K1 + K2 inside the library), warm
     for _ in range(3):
         S.svdq_linear(sets[0]["x"], l0, out_dtype, y=sets[0]["y"], workspace=ws_lin, stream=stream)
@@ -916,26 +932,23 @@ def measure_layer(cfg, args, distinct_sets, steps, warmup, copy_check=False):
     torch.cuda.synchronize()
     linear_ms = (time.perf_counter() - t1) * 1e3 / steps
 
-    cold = kernel_stats(cold_evs, cold_wall)
-    warm = kernel_stats(warm_evs, warm_wall)
-    med = lambda f: float(np.median([f(e) for e in pair]))
-    ov = {"ms_rank_r": med(lambda e: e[0][0].elapsed_time(e[0][2])),
-          "ms_rank_0": med(lambda e: e[1][0].elapsed_time(e[1][2])),
-          "k1_ms_rank_r": med(lambda e: e[0][0].elapsed_time(e[0][1])),
-          "k2_ms_rank_r": med(lambda e: e[0][1].elapsed_time(e[0][2])),
-          "k1_ms_rank_0": med(lambda e: e[1][0].elapsed_time(e[1][1])),
-          "k2_ms_rank_0": med(lambda e: e[1][1].elapsed_time(e[1][2]))}
+    cold = kernel_stats(cold_ev, cold_wall)
+    warm = kernel_stats(warm_ev, warm_wall)
+    tp = times(pair_ev)
+    med = lambda i, parity: float(np.median([v[i] for k, v in enumerate(tp) if k % 2 == parity]))
+    ov = {"ms_rank_r": med(2, 0), "ms_rank_0": med(2, 1),
+          "k1_ms_rank_r": med(0, 0), "k2_ms_rank_r": med(1, 0),
+          "k1_ms_rank_0": med(0, 1), "k2_ms_rank_0": med(1, 1)}
     settle = None
     if n_probe:
-        k2s = [e[1].elapsed_time(e[2]) for e in settle_evs]
+        first = float(np.median([v[1] for v in times(settle_a)]))
+        last = float(np.median([v[1] for v in times(settle_b)]))
         settle = {"steps": n_settle,
-                  "ms": round(settle_evs[0][0].elapsed_time(settle_evs[-1][2]), 2),
-                  f"gemm_ms_first_{n_probe}": round(float(np.median(k2s[:n_probe])), 5),
-                  f"gemm_ms_last_{n_probe}": round(float(np.median(k2s[n_probe:])), 5)}
-        log(f"bench: settling took {settle['ms']:.0f} ms; GEMM median {np.median(k2s[:n_probe]) * 1e3:.1f} us "
-            f"over its first {n_probe} steps, {np.median(k2s[n_probe:]) * 1e3:.1f} us over its last; timed "
-            f"{cold['k2_mean'] * 1e3:.1f} us")
-    del settle_evs, cold_evs, warm_evs, pair, marshalled
+                  "ms": round(settle_a["start"].elapsed_time(settle_b["marks"][-1][1]), 2),
+                  f"gemm_ms_first_{n_probe}": round(first, 5), f"gemm_ms_last_{n_probe}": round(last, 5)}
+        log(f"bench: settling took {settle['ms']:.0f} ms; GEMM median {first * 1e3:.1f} us over its first "
+            f"{n_probe} steps, {last * 1e3:.1f} us over its last; timed {cold['k2_mean'] * 1e3:.1f} us")
+    del settle_a, settle_b, cold_ev, warm_ev, pair_ev, marshalled
 
     if copy_check:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
