@@ -120,6 +120,13 @@ def settle_steps(b, m, n):
     return int(min(5000, max(50, math.ceil(SETTLE_OPS / (2.0 * b * m * n)))))
 
 
+def compare_untimed_steps(b, m, n, args):
+    """Untimed steps of the setting comparisons (--w8a8, --fp4): the warm-up,
+    then the clock-settling steps; a step runs both settings' kernels, about
+    twice one layer's work, so half of ``settle_steps``."""
+    return max(50, args.warmup) + (0 if args.no_settle else settle_steps(b, m, n) // 2)
+
+
 def set_plan(cfg, rank, out):
     """(bytes of one input+weight set, number of sets rotated by the cold timing)."""
     b, m, n = cfg.rows or cfg.b, cfg.m, cfg.n
@@ -148,7 +155,7 @@ def trace_summary(prof_dir, cfg, args, rank):
     _, n_sets = set_plan(cfg, rank, args.out)
     b_rows = cfg.rows or cfg.b
     n_settle = 0 if cmp_mode or args.no_settle else settle_steps(b_rows, cfg.m, cfg.n)
-    skip = max(50, args.warmup) if cmp_mode else max(args.warmup, n_sets) + n_settle
+    skip = compare_untimed_steps(b_rows, cfg.m, cfg.n, args) if cmp_mode else max(args.warmup, n_sets) + n_settle
     short = lambda nm: re.sub(r"\(.*", "", nm.replace("svdq::(anonymous namespace)::", "")
                               .replace("void ", "").replace("svdq::", ""))
     rows = list(c.execute("select name, start, end, grid_x, grid_y, workgroup_x, workgroup_y, vgpr_count, "
@@ -539,7 +546,7 @@ def w8a8_compare(cfg, rank, args):
         if ev is not None:
             ev[4].record(stream)
 
-    for _ in range(max(50, args.warmup)):
+    for _ in range(compare_untimed_steps(b, m, n, args)):
         step()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for k in range(args.steps):
@@ -618,7 +625,7 @@ def fp4_compare(cfg, rank, args):
         if ev is not None:
             ev[4].record(stream)
 
-    for _ in range(max(50, args.warmup)):
+    for _ in range(compare_untimed_steps(b, m, n, args)):
         step()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for k in range(args.steps):
