@@ -15,11 +15,12 @@ step does not find its layer's weights or activations cached by the previous
 step.  Between the warm-up steps and the timed region the layer's own steps
 run untimed for about a quarter second, with no idle gap (``settle_steps``),
 so that the timed steps see the GPU's sustained clock rather than its ramp
-from idle; ``--no-settle`` times from idle instead.  Also reported: the same steps on one set ("warm"), the low-rank
-overhead t(rank r) / t(rank 0, same codes and scales) - 1 from rank-r and
-rank-0 steps interleaved on one set (median HIP-event step times), the
-one-call ``svdq_linear`` entry point, and the GEMM's fractions of the i8 MFMA
-peak, of HBM bandwidth and of the fp32 FMA peak its scale epilogue needs.
+from idle; ``--no-settle`` times from idle instead.  Two HIP events per step
+bracket the GEMM kernel.  Also reported: the same steps on one set ("warm"),
+the low-rank overhead t(rank r) / t(rank 0, same codes and scales) - 1 from
+rank-r and rank-0 steps interleaved on one set (median HIP-event step times),
+the one-call ``svdq_linear`` entry point, and the GEMM's fractions of the i8
+MFMA peak, of HBM bandwidth and of the fp32 FMA peak its scale epilogue needs.
 
 Prints ONE JSON line.  Default workload: the FLUX-shaped fused QKV projection
 (b=4608 tokens, m=3072, n=9216, rank 32, group 64).  The other FLUX- and
@@ -829,8 +830,8 @@ def measure_layer(cfg, args, distinct_sets, steps, warmup, copy_check=False):
         rr = layer.rank
         lib, P, sp = B.lib(), B._ptr, B._stream(stream)
         zp = P(z) if rr else None
-        k1 = functools.partial(lib.svdq_quantize_act_lowrank_down, P(st["x"]), b, m, rr, 64, P(layer.smooth_inv),
-                               P(layer.l1), P(qx), P(asc), zp, P(ws), ws.numel(), sp)
+        k1 = functools.partial(lib.svdq_quantize_act_lowrank_down, P(st["x"]), b, m, rr, B.SVDQ_GROUP,
+                               P(layer.smooth_inv), P(layer.l1), P(qx), P(asc), zp, P(ws), ws.numel(), sp)
         k2 = functools.partial(lib.svdq_gemm_w4a4_lowrank_up, P(qx), P(asc), zp, ctypes.byref(layer.struct), b,
                                P(st["y"]), B._out_code(out_dtype), P(gws), gws.numel(), sp)
         return k1, k2, layer
