@@ -834,7 +834,7 @@ def measure_layer(cfg, args, distinct_sets, steps, warmup, copy_check=False):
                                P(layer.smooth_inv), P(layer.l1), P(qx), P(asc), zp, P(ws), ws.numel(), sp)
         k2 = functools.partial(lib.svdq_gemm_w4a4_lowrank_up, P(qx), P(asc), zp, ctypes.byref(layer.struct), b,
                                P(st["y"]), B._out_code(out_dtype), P(gws), gws.numel(), sp)
-        return k1, k2, layer
+        return k1, k2, st, layer  # the set and layer stay referenced, so their ids are not reused
 
     def step(st, layer=None, marks=None):
         """One step; marks = (event after the act kernel, event after the
