@@ -127,3 +127,43 @@ def test_counter_summary_utilisation_and_bandwidth(fake_root):
     assert line[5].strip() == "25.0 %" and line[6].strip() == "0.125" and line[7].strip() == "0.50"
     # 400 MB fetched + 400 MB written in 100 us = 8000 GB/s = 100 % of peak
     assert line[10].strip() == "8000" and line[11].strip() == "100.0 %"
+
+
+def _write_trace(d, dispatches):
+    """A rocpd-like database with the columns trace_summary reads: one row per
+    (name, start, end) dispatch, ns timestamps."""
+    import sqlite3
+    os.makedirs(d, exist_ok=True)
+    c = sqlite3.connect(os.path.join(d, "run_results.db"))
+    c.execute("create table kernels (name text, start integer, end integer, grid_x integer, grid_y integer, "
+              "workgroup_x integer, workgroup_y integer, vgpr_count integer, accum_vgpr_count integer, "
+              "lds_size integer, scratch_size integer)")
+    c.executemany("insert into kernels values (?, ?, ?, 256, 1, 256, 1, 128, 0, 0, 0)", dispatches)
+    c.commit()
+    c.close()
+
+
+@pytest.mark.parametrize("no_settle", [False, True])
+def test_trace_summary_takes_the_timed_steps(fake_root, no_settle):
+    # the GEMM's dispatches: warm-up and settling steps (1 us), the timed steps
+    # (2 us), then the later phases (5 us); the summary's timed-region mean
+    # must be exactly the timed steps'
+    cfg = workloads.CONFIGS["flux_qkv"]
+    args = type("A", (), dict(steps=7, warmup=10, out="bf16", w8a8=None, fp4=None, no_settle=no_settle,
+                              rank=None))()
+    _, n_sets = bench.set_plan(cfg, cfg.rank, "bf16")
+    skip = max(args.warmup, n_sets) + (0 if no_settle else bench.settle_steps(cfg.b, cfg.m, cfg.n))
+    gemm = "void svdq::(anonymous namespace)::gemm_w4a4_up_kernel<GemmCfg<128>, true, false>(...)"
+    durs = [1000] * skip + [2000] * args.steps + [5000] * 40
+    t, rows = 0, []
+    for d in durs:
+        rows.append((gemm, t, t + d))
+        t += d + 100
+    pd = str(fake_root / "prof")
+    _write_trace(pd, rows)
+    bench.trace_summary(pd, cfg, args, cfg.rank)
+    text = open(fake_root / "profiles" / "kernel_trace_flux_qkv.md").read()
+    line = [l for l in text.splitlines() if "gemm_w4a4_up_kernel" in l][0].split("|")
+    assert line[2].strip() == str(len(durs))
+    assert line[3].strip() == "2.00"
+    assert f"after {skip} untimed ones" in text
