@@ -248,7 +248,11 @@ def counter_summary(sq_dir, fetch_dir, write_dir, workload, commands):
     f_fac = COPY_BYTES / (max(_per_dispatch(fr, "FETCH_SIZE", is_copy)) * 1024.0)
     w_fac = COPY_BYTES / (max(_per_dispatch(wr, "WRITE_SIZE", is_copy)) * 1024.0)
     kernels = [("GEMM + up-projection", lambda k: GEMM_KERNEL in k),
-               ("act-quant + down-projection", lambda k: "act_quant_down_kernel" in k and ", 1>" in k)]
+               # the INT4 activation kernel (split or wide) with the low-rank branch: the
+               # rank-0 build (first template argument 0) of the overhead steps is left out
+               ("act-quant + down-projection",
+                lambda k: ("act_quant_down_kernel<" in k or "act_quant_wide_kernel<" in k) and ", 1>" in k
+                and "_kernel<0," not in k)]
     med = lambda v: float(np.median(v)) if v else float("nan")
     out = [f"# Counters: {workload} (one MI355X)", "", "Commands (repository root), then the summary:", "", "```",
            commands, "```", "",
